@@ -1,0 +1,242 @@
+"""Decode-step benchmark of the CSA + HCA layer pair at 128K context, batch 32.
+
+One step = csa_index_topk (lightning-indexer scoring + top-1024) + csa_attend +
+hca_attend for all 32 sequences, caches and queries resident in HBM.  Prints one
+JSON line: queries/s, the step's HBM rate against the 8 TB/s peak, the
+roofline record of the dominant kernel (indexer scoring, timed with HIP events
+on its stream) and the CPU oracle timed on a bounded sample of the same step.
+
+Caches come from the same recipe as the parity tests (x ~ N(0,1), weights
+N(0, 1/fan_in), fp32 projections rounded to bf16, then the library's own
+compressors) with hidden states drawn by torch on the GPU; compression is not
+part of the timed step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--replicas", type=int, default=2, help="cache copies rotated between steps (defeats the MALL)")
+    ap.add_argument("--batch", type=int, default=None, help="override the batch (default 32)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def build_caches(wl, dev, sk, torch, gen):
+    """Caches of every sequence for both layers (GPU-drawn streams, library compressors)."""
+    B = wl.B
+    csa, hca = wl.layers
+    bf = torch.bfloat16
+    Ec, Eh = wl.N // csa.m, wl.N // hca.m
+    c = {"entries": torch.empty(B, Ec, csa.D, device=dev, dtype=bf),
+         "keys": torch.empty(B, Ec, csa.D_I, device=dev, dtype=bf),
+         "win": torch.empty(B, csa.W, csa.D, device=dev, dtype=bf)}
+    h = {"entries": torch.empty(B, Eh, hca.D, device=dev, dtype=bf),
+         "win": torch.empty(B, hca.W, hca.D, device=dev, dtype=bf)}
+    weights = gen.gpu_weights(wl, dev)
+    wc, wh = weights
+    slots = torch.arange(wl.N - csa.W, wl.N, device=dev) % csa.W
+    for b in range(B):
+        st_c, st_h = gen.gpu_sequence_streams(wl, b, weights, dev)
+        kv = sk.Pool(st_c["v"][None], st_c["g"][None], wc["bpos"].contiguous(), c["entries"][b:b + 1])
+        ix = sk.Pool(st_c["vI"][None], st_c["gI"][None], wc["bposI"].contiguous(), c["keys"][b:b + 1])
+        sk.csa_compress(kv, ix, m=csa.m, o=csa.o)
+        sk.hca_compress(sk.Pool(st_h["v"][None], st_h["g"][None], wh["bpos"].contiguous(), h["entries"][b:b + 1]),
+                        m=hca.m, o=hca.o)
+        c["win"][b, slots] = st_c["v"][wl.N - csa.W:]
+        h["win"][b, slots] = st_h["v"][wl.N - hca.W:]
+        del st_c, st_h
+    torch.cuda.synchronize()
+    return c, h
+
+
+def algorithmic_bytes(wl):
+    """Bytes one decode query must move (reads of the data it uses, writes of its results)."""
+    csa, hca = wl.layers
+    t = wl.N - 1
+    ev_c = max(0, (t - csa.W) // csa.m)
+    ev_h = max(0, (t - hca.W) // hca.m)
+    nwin = min(csa.W, t + 1)
+    b16 = 2
+    score = ev_c * csa.D_I * b16 + csa.H_I * csa.D_I * b16 + csa.H_I * 4      # keys + indexer query + weights
+    topk = csa.k * 4                                                           # indices written
+    csa_att = (csa.k * csa.D + nwin * csa.D + csa.H * csa.D) * b16 + csa.k * 4 + csa.H * csa.D * 4
+    hca_att = (ev_h * hca.D + nwin * hca.D + hca.H * hca.D) * b16 + hca.H * hca.D * 4
+    return {"score": score, "topk": topk, "csa_attend": csa_att, "hca_attend": hca_att,
+            "step": score + topk + csa_att + hca_att}
+
+
+def cpu_baseline(wl, budget_s: float):
+    """The oracle (numpy fp64) on one sequence of the same workload, timed on the host."""
+    import numpy as np
+
+    from oracle import method, pipeline
+    from workloads import gen
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    csa, hca = wl.layers
+    t0 = time.time()
+    x = gen.hidden_states(wl, 0)
+    prep = []
+    for li, L in enumerate(wl.layers):
+        w = gen.layer_weights(wl, li)
+        st = gen.layer_streams(wl, li, x, w)
+        q = gen.layer_queries(wl, li, x[wl.N - 1:], w)
+        caches = pipeline.layer_caches(L, st, w, wl.entry_store, wl.key_store)
+        prep.append((L, caches, st["v"], q))
+    del x
+    setup_s = time.time() - t0
+    t = wl.N - 1
+    n = 0
+    t1 = time.time()
+    while True:
+        for L, caches, v, q in prep:
+            if L.kind == "csa":
+                pipeline.decode_row(L, caches, v, q["q"][0], t, q["qI"][0], q["w"][0])
+            else:
+                pipeline.decode_row(L, caches, v, q["q"][0], t)
+        n += 1
+        el = time.time() - t1
+        if el >= budget_s or n >= 50:
+            break
+    return {"value": n / el, "unit": "queries/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n} decode queries of sequence 0 (CSA top-{csa.k} + HCA, fp64 numpy) in {el:.1f} s; "
+                      f"cache preparation {setup_s:.0f} s untimed"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU: the decode path shards by sequence with no exchange, and only the "
+              "single-GPU share is built and measured here; use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import sequence_compressed_kv_amd as sk
+    from workloads import PAIR_DEC_128K_BF16, gen
+
+    wl = PAIR_DEC_128K_BF16 if args.batch is None else PAIR_DEC_128K_BF16.with_sizes(B=args.batch)
+    dev = "cuda:0"
+    sk.load()
+    csa, hca = wl.layers
+    B = wl.B
+    t = wl.N - 1
+    print(f"[bench] building caches: B={B} N={wl.N}", file=sys.stderr, flush=True)
+    tb = time.time()
+    c0, h0 = build_caches(wl, dev, sk, torch, gen)
+    reps = [(c0, h0)] + [({k: v.clone() for k, v in c0.items()}, {k: v.clone() for k, v in h0.items()})
+                         for _ in range(args.replicas - 1)]
+    qc = gen.gpu_queries(wl, 0, B, dev)
+    qh = gen.gpu_queries(wl, 1, B, dev)
+    print(f"[bench] caches ready in {time.time() - tb:.1f} s", file=sys.stderr, flush=True)
+
+    pos = torch.full((B,), t, dtype=torch.int32, device=dev)
+    rows = sk.RowSpec.decode(pos, t)
+    idx = torch.empty(B, csa.k, dtype=torch.int32, device=dev)
+    out_c = torch.empty(B, csa.H, csa.D, device=dev, dtype=torch.float32)
+    out_h = torch.empty(B, hca.H, hca.D, device=dev, dtype=torch.float32)
+    tau = 1.0 / math.sqrt(csa.d_h)
+    ia = sk.index_args(rows, qc["qI"], qc["w"], c0["keys"], idx, m=csa.m, W=csa.W, k=csa.k)
+    L = sk.load()
+    import ctypes as C
+    ws_idx = torch.empty(L.csa_index_topk_workspace_size(C.byref(ia)), dtype=torch.uint8, device=dev)
+    cover = max(0, (t - csa.W) // csa.m)
+    stride = (cover + 63) // 64 * 64
+    scores = ws_idx[: B * stride * 4].view(torch.float32).view(B, stride)
+    ws_sel = ws_idx[B * stride * 4:]
+    ws_c = sk.csa_attend(rows, qc["q"], c0["entries"], idx, c0["win"], out_c, m=csa.m, W=csa.W, softmax_scale=tau)
+    ws_h = sk.hca_attend(rows, qh["q"], h0["entries"], h0["win"], out_h, m=hca.m, W=hca.W, softmax_scale=tau)
+
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        c, h = reps[i % len(reps)]
+        if ev is not None:
+            ev[0].record(stream)
+        sk.csa_index_score(rows, qc["qI"], qc["w"], c["keys"], scores, m=csa.m, W=csa.W, k=csa.k)
+        if ev is not None:
+            ev[1].record(stream)
+        sk.csa_topk_select(rows, scores, idx, keys_meta=(qc["qI"], qc["w"], c["keys"]), m=csa.m, W=csa.W,
+                           k=csa.k, workspace=ws_sel)
+        if ev is not None:
+            ev[2].record(stream)
+        sk.csa_attend(rows, qc["q"], c["entries"], idx, c["win"], out_c, m=csa.m, W=csa.W, softmax_scale=tau,
+                      workspace=ws_c)
+        if ev is not None:
+            ev[3].record(stream)
+        sk.hca_attend(rows, qh["q"], h["entries"], h["win"], out_h, m=hca.m, W=hca.W, softmax_scale=tau,
+                      workspace=ws_h)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # timed region: K whole steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.time()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.time() - w0
+    ms = e0.elapsed_time(e1) / args.steps
+    # per-kernel durations: the same steps with events between the launches
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    parts = {name: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)) / args.steps
+             for j, name in enumerate(["score", "topk", "csa_attend", "hca_attend"])}
+
+    ab = algorithmic_bytes(wl)
+    score_gbps = ab["score"] * B / (parts["score"] * 1e-3) / 1e9
+    step_gbps = ab["step"] * B / (ms * 1e-3) / 1e9
+    rec = {
+        "metric": "CSA+HCA decode attention queries/s at 128K ctx; HBM GB/s as % of peak",
+        "value": B / (ms * 1e-3),
+        "unit": "queries/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "context": wl.N, "layers": "csa+hca", "heads": csa.H,
+                   "latent": csa.D, "indexer": f"{csa.H_I}x{csa.D_I}", "top_k": csa.k, "window": csa.W,
+                   "replicas": args.replicas},
+        "step_hbm_GBps": step_gbps, "step_hbm_frac": step_gbps / PEAK_HBM_GBPS,
+        "step_algorithmic_bytes": ab["step"] * B,
+        "kernel_ms": parts,
+        "roofline": {"bound": "hbm", "kernel": "index_score_decode", "achieved": score_gbps,
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": score_gbps / PEAK_HBM_GBPS,
+                     "traffic": None, "bytes_per_launch": ab["score"] * B},
+        "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,227 @@
+/*
+ * sckv.h -- C ABI of the CSA / HCA compressed-attention hot path (gfx950).
+ *
+ * The method (DeepSeek-V4 hybrid compressed attention):
+ *   - CSA pools the KV sequence about 4:1 with a learned gate over overlapping
+ *     windows, scores the pooled entries with a lightning indexer, keeps a
+ *     per-query top-k and attends to those entries plus a raw recent window
+ *     (knightli.com DeepSeek-V4 KV-cache article, section "CSA: compresión 4x
+ *     más recuperación dispersa"; kongchang.com "DeepSeek V4 Deep Dive",
+ *     "Innovation 1: Hybrid Attention Architecture").
+ *   - HCA pools 128:1 and attends densely to every pooled entry plus the window
+ *     (same article, "HCA: compresión 128x más atención densa"; bayesiansapien
+ *     "DeepSeek-V4: interleaved compressed attention ...", TL;DR).
+ *   - Both concatenate the compressed branch with the sliding-window K/V of the
+ *     most recent raw tokens in one softmax (same article, "Ventana deslizante").
+ *
+ * Formulas (the pages leave them open; the CSA decode workload definition fixes them):
+ *   compressor  c_j[d] = sum_{i in P_j} softmax_i(g_i[d] + Bpos[i - m j + o][d]) * v_i[d],
+ *               P_j = [m j - o, m j + m) restricted to tokens that exist (i >= 0)
+ *   visibility  entry j is usable by the query at position t iff m (j + 1) <= t - W,
+ *               so E_vis(t) = max(0, floor((t - W) / m)) entries are visible
+ *   indexer     s_j = sum_h w_h * max(0, qI_h . kI_j)  over visible j
+ *   top-k       the min(k, E_vis) best j by (s_j descending, j ascending)
+ *   attention   o_h = sum_u softmax_u(scale * q_h . u) u over
+ *               u in {entries kept} U {raw tokens max(0, t-W+1) .. t}; K = V = u
+ *
+ * Conventions for every call
+ *   - All tensor pointers are DEVICE memory owned by the caller, dense row-major
+ *     in the shapes given, 16-byte aligned.  Nothing is allocated, freed or
+ *     synchronised by the library; work is enqueued on `stream` (a hipStream_t,
+ *     NULL = the default stream) and the call returns at once.
+ *   - Arguments are fully validated on the host before any HIP call; a non-OK
+ *     status means nothing was enqueued, and sckv_last_error() (thread-local)
+ *     describes the problem.  Faults inside kernels surface at the caller's
+ *     next synchronisation.
+ *   - Results are deterministic: identical inputs give bitwise identical
+ *     outputs (fixed split counts, fixed reduction order, no float atomics).
+ *   - Storage types: F32, BF16 (round-to-nearest-even), E4M3 (OCP 8-bit
+ *     E4M3 "fn": max 448, saturating round-to-nearest-even).
+ *   - Supported shapes: D in {8,16,32,64,128,256,512} for compression;
+ *     the MFMA paths need bf16 queries, H % 16 == 0 (H <= 128), D in
+ *     {64,128,256,512} for attention and H_I in {32,64}, D_I in {64,128} for
+ *     the indexer; the F32 paths accept H*D <= 4096 and H_I*D_I <= 8192.
+ *     Other shapes return SCKV_ERR_UNSUPPORTED.
+ */
+#ifndef SCKV_H
+#define SCKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SCKV_ABI_VERSION 1
+
+typedef enum { SCKV_F32 = 0, SCKV_BF16 = 1, SCKV_E4M3 = 2 } sckv_dtype;
+
+typedef enum {
+  SCKV_OK = 0,
+  SCKV_ERR_NULL = 1,        /* a required pointer is NULL */
+  SCKV_ERR_SHAPE = 2,       /* a size, count or index argument is out of range */
+  SCKV_ERR_DTYPE = 3,       /* unsupported dtype or dtype combination */
+  SCKV_ERR_UNSUPPORTED = 4, /* shape outside what the kernels implement */
+  SCKV_ERR_ALIGN = 5,       /* a tensor pointer is not 16-byte aligned */
+  SCKV_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than the size query asks for */
+  SCKV_ERR_HIP = 7          /* a kernel launch failed */
+} sckv_status;
+
+/* Query rows of an index or attend call.
+ *   SCKV_ROWS_DECODE: row r belongs to sequence r (R <= B) and sits at position
+ *     pos[r] (device int32 [R]).  pos_max (host) bounds every pos[r]; it sizes the
+ *     grid.  Positions outside [0, pos_max] are clamped into it.
+ *   SCKV_ROWS_CAUSAL: rows are the consecutive positions pos0 .. pos0 + R - 1 of
+ *     sequence seq0 (causal prefill or a chunk of it); pos and pos_max are unused. */
+typedef enum { SCKV_ROWS_DECODE = 0, SCKV_ROWS_CAUSAL = 1 } sckv_rows_kind;
+
+typedef struct {
+  const int32_t* pos; /* DECODE: device [R] positions; CAUSAL: unused (may be NULL) */
+  int32_t kind;       /* sckv_rows_kind */
+  int32_t R;          /* number of query rows, >= 1 */
+  int32_t pos_max;    /* DECODE: host bound on pos[] */
+  int32_t seq0;       /* CAUSAL: sequence of the rows */
+  int32_t pos0;       /* CAUSAL: position of row 0 */
+  int32_t reserved;
+} sckv_rows;
+
+/* ------------------------------------------------------------------ compression
+ * One per-token stream pair pooled into entries (the compressor above).
+ *   val, gate : [B][N][D] values v_i and gate logits g_i (in_dtype F32 or BF16)
+ *   bpos      : [m+o][D] fp32 position bias
+ *   out       : [B][E_cap][D] entries (out_dtype F32, BF16 or E4M3)
+ *   out_scale : E4M3 only.  Non-NULL: [B][E_cap] fp32 per-entry scale, written as
+ *               fp32(max_d |c_j[d]| / 448) (1 for an all-zero entry), codes are
+ *               E4M3(c / scale).  NULL: unscaled E4M3(c) (indexer keys). */
+typedef struct {
+  const void* val;
+  const void* gate;
+  const float* bpos;
+  void* out;
+  float* out_scale;
+  int64_t E_cap;
+  int32_t D;
+  int32_t in_dtype;
+  int32_t out_dtype;
+  int32_t reserved;
+} sckv_pool_stream;
+
+/* csa_compress: pools entries e_begin .. e_begin + e_count - 1 of every sequence
+ * from tokens of a stream holding N tokens per sequence (rows of val/gate are
+ * strided by N).  Entry e needs tokens up to m (e + 1) - 1 < N, and
+ * e_begin + e_count <= E_cap.  `kv` is the shared latent stream; `index_keys`
+ * (may be NULL) is the lightning indexer's own stream, pooled over the same
+ * windows (knightli.com article, CSA section: the indexer scores the pooled
+ * blocks).  CSA uses m = 4, o = 4; the call accepts any m >= 1, 0 <= o. */
+sckv_status csa_compress(int32_t B, int64_t N, int32_t m, int32_t o, int64_t e_begin,
+                         int64_t e_count, const sckv_pool_stream* kv,
+                         const sckv_pool_stream* index_keys, void* stream);
+
+/* hca_compress: as csa_compress for the single HCA stream (128:1 pooling over
+ * non-overlapping blocks: m = 128, o = 0; knightli.com article, HCA section). */
+sckv_status hca_compress(int32_t B, int64_t N, int32_t m, int32_t o, int64_t e_begin,
+                         int64_t e_count, const sckv_pool_stream* kv, void* stream);
+
+/* ------------------------------------------------------------------ lightning indexer + top-k
+ *   q         : [R][H_I][D_I] indexer queries (q_dtype F32 or BF16)
+ *   w         : [R][H_I] fp32 head weights w_h
+ *   keys      : [B][E_cap][D_I] indexer keys (key_dtype F32, BF16 or unscaled E4M3)
+ *   out_idx   : [R][k] int32: the kept entries of each row in ascending order,
+ *               then -1 padding (k' = min(k, E_vis) entries are kept; E_vis = 0
+ *               gives an all -1 row)
+ *   out_score : [R][k] fp32 scores of the kept entries (padding: -inf), or NULL
+ * Only entries 0 .. min(E_vis(t), E_cap) - 1 of each row's sequence are read.
+ * Scores of exactly zero are ranked as +0. */
+typedef struct {
+  sckv_rows rows;
+  const void* q;
+  const float* w;
+  const void* keys;
+  int32_t* out_idx;
+  float* out_score;
+  int64_t E_cap;
+  int32_t B;
+  int32_t H_I;
+  int32_t D_I;
+  int32_t q_dtype;
+  int32_t key_dtype;
+  int32_t m;
+  int32_t W;
+  int32_t k;
+} sckv_index_args;
+
+/* Workspace bytes csa_index_topk needs for these arguments (0 if they are invalid). */
+size_t csa_index_topk_workspace_size(const sckv_index_args* a);
+
+/* csa_index_topk: scores every visible entry of each row and keeps its top-k. */
+sckv_status csa_index_topk(const sckv_index_args* a, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* The two halves of csa_index_topk, for callers that want the scores themselves.
+ * csa_index_score writes s_j for j < min(E_vis, E_cap) of row r to
+ * scores[r * score_stride + j] (score_stride >= the visible count of every row;
+ * entries beyond a row's visible count are left untouched).
+ * csa_topk_select selects from such a score matrix; out_idx / out_score as above. */
+sckv_status csa_index_score(const sckv_index_args* a, float* scores, int64_t score_stride,
+                            void* stream);
+size_t csa_topk_select_workspace_size(const sckv_index_args* a);
+sckv_status csa_topk_select(const sckv_index_args* a, const float* scores, int64_t score_stride,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------ attention
+ *   q           : [R][H][D] queries in the shared latent (q_dtype F32 or BF16); with
+ *                 a latent wider than the head dim the caller passes W_UK^h^T q_h
+ *   entries     : [B][E_cap][D] pooled entries (entry_dtype F32, BF16 or E4M3)
+ *   entry_scale : [B][E_cap] fp32 per-entry scale (E4M3 only, else ignored)
+ *   idx         : csa_attend: [R][k] int32 kept entries (as out_idx above; -1 = none)
+ *   win         : [B][R_w][D] raw per-token latents v_i (win_dtype F32 or BF16);
+ *                 token i of a sequence lives in slot i % R_w (R_w >= W; pass the
+ *                 whole stream with R_w = N for prefill)
+ *   out         : [R][H][D] (out_dtype F32 or BF16), o_h of each row
+ *   lse         : [R][H] fp32 natural-log sum of exp of the scaled logits, or NULL
+ *   softmax_scale : multiplies every logit (1/sqrt(head dim))
+ * csa_attend uses the k listed entries; hca_attend uses entries
+ * 0 .. min(E_vis(t), E_cap) - 1 (dense).  Both add the raw tokens
+ * max(0, t - W + 1) .. t.  The MFMA path computes P.V in fp16: entries and window
+ * values must stay below 65504 in magnitude. */
+typedef struct {
+  sckv_rows rows;
+  const void* q;
+  const void* entries;
+  const float* entry_scale;
+  const int32_t* idx;
+  const void* win;
+  void* out;
+  float* lse;
+  int64_t E_cap;
+  int64_t R_w;
+  int32_t B;
+  int32_t H;
+  int32_t D;
+  int32_t q_dtype;
+  int32_t entry_dtype;
+  int32_t win_dtype;
+  int32_t out_dtype;
+  int32_t m;
+  int32_t W;
+  int32_t k;
+  float softmax_scale;
+  int32_t reserved;
+} sckv_attend_args;
+
+size_t csa_attend_workspace_size(const sckv_attend_args* a);
+size_t hca_attend_workspace_size(const sckv_attend_args* a);
+sckv_status csa_attend(const sckv_attend_args* a, void* workspace, size_t workspace_bytes,
+                       void* stream);
+sckv_status hca_attend(const sckv_attend_args* a, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* ------------------------------------------------------------------ misc */
+const char* sckv_last_error(void); /* thread-local text of the last non-OK status */
+int32_t sckv_abi_version(void);    /* SCKV_ABI_VERSION */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SCKV_H */

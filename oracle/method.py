@@ -49,7 +49,7 @@ def window_positions(t: int, W: int) -> np.ndarray:
 
 
 # ---------------------------------------------------------------- compressor
-def compress(v, g, bpos, m: int, o: int, chunk: int = 2048) -> np.ndarray:
+def compress(v, g, bpos, m: int, o: int, chunk: Optional[int] = None) -> np.ndarray:
     """Gated per-channel softmax pool of one sequence.
 
     v, g : [N][D] values and gate logits per token; bpos : [m+o][D] position bias.
@@ -64,6 +64,8 @@ def compress(v, g, bpos, m: int, o: int, chunk: int = 2048) -> np.ndarray:
     assert bpos.shape == (L, D)
     E = N // m
     out = np.empty((E, D))
+    if chunk is None:                       # bound the [entries][window][D] temporaries
+        chunk = max(1, (1 << 22) // (L * D))
     for j0 in range(0, E, chunk):
         j = np.arange(j0, min(E, j0 + chunk))
         tok = m * j[:, None] - o + np.arange(L)[None, :]          # [J][L]; window slot l = i - m j + o
@@ -160,7 +162,7 @@ def csa_row(t: int, q, qI, w, entries, keys, stream_v, m: int, W: int, k: int, t
     idx = topk(s, k)
     sel = idx[idx >= 0]
     items = np.concatenate([np.asarray(entries, np.float64)[sel],
-                            np.asarray(stream_v, np.float64)[window_positions(t, W)]])
+                            np.asarray(np.asarray(stream_v)[window_positions(t, W)], np.float64)])
     o, lse, p = attend(q, items, tau)
     return {"e_vis": e_vis, "scores": s, "idx": idx, "o": o, "lse": lse, "p": p}
 
@@ -169,7 +171,7 @@ def hca_row(t: int, q, entries, stream_v, m: int, W: int, tau: float):
     """One HCA query at position t: dense over every visible entry plus the window."""
     e_vis = min(entries_visible(t, m, W), entries.shape[0])
     items = np.concatenate([np.asarray(entries, np.float64)[:e_vis],
-                            np.asarray(stream_v, np.float64)[window_positions(t, W)]])
+                            np.asarray(np.asarray(stream_v)[window_positions(t, W)], np.float64)])
     o, lse, p = attend(q, items, tau)
     return {"e_vis": e_vis, "o": o, "lse": lse, "p": p}
 

@@ -1,0 +1,264 @@
+"""ctypes binding of libsckv.so: the same five calls (plus the two indexer halves),
+taking torch device tensors and the current HIP stream.  Argument marshalling
+only: every step runs in the library's HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsckv.so")
+
+F32, BF16, E4M3 = 0, 1, 2
+ROWS_DECODE, ROWS_CAUSAL = 0, 1
+
+STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_DTYPE", 4: "ERR_UNSUPPORTED", 5: "ERR_ALIGN",
+          6: "ERR_WORKSPACE", 7: "ERR_HIP"}
+
+
+class SckvError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+# ---------------------------------------------------------------- C structs (mirror include/sckv.h)
+class Rows(C.Structure):
+    _fields_ = [("pos", C.c_void_p), ("kind", C.c_int32), ("R", C.c_int32), ("pos_max", C.c_int32),
+                ("seq0", C.c_int32), ("pos0", C.c_int32), ("reserved", C.c_int32)]
+
+
+class PoolStream(C.Structure):
+    _fields_ = [("val", C.c_void_p), ("gate", C.c_void_p), ("bpos", C.c_void_p), ("out", C.c_void_p),
+                ("out_scale", C.c_void_p), ("E_cap", C.c_int64), ("D", C.c_int32), ("in_dtype", C.c_int32),
+                ("out_dtype", C.c_int32), ("reserved", C.c_int32)]
+
+
+class IndexArgs(C.Structure):
+    _fields_ = [("rows", Rows), ("q", C.c_void_p), ("w", C.c_void_p), ("keys", C.c_void_p),
+                ("out_idx", C.c_void_p), ("out_score", C.c_void_p), ("E_cap", C.c_int64), ("B", C.c_int32),
+                ("H_I", C.c_int32), ("D_I", C.c_int32), ("q_dtype", C.c_int32), ("key_dtype", C.c_int32),
+                ("m", C.c_int32), ("W", C.c_int32), ("k", C.c_int32)]
+
+
+class AttendArgs(C.Structure):
+    _fields_ = [("rows", Rows), ("q", C.c_void_p), ("entries", C.c_void_p), ("entry_scale", C.c_void_p),
+                ("idx", C.c_void_p), ("win", C.c_void_p), ("out", C.c_void_p), ("lse", C.c_void_p),
+                ("E_cap", C.c_int64), ("R_w", C.c_int64), ("B", C.c_int32), ("H", C.c_int32), ("D", C.c_int32),
+                ("q_dtype", C.c_int32), ("entry_dtype", C.c_int32), ("win_dtype", C.c_int32),
+                ("out_dtype", C.c_int32), ("m", C.c_int32), ("W", C.c_int32), ("k", C.c_int32),
+                ("softmax_scale", C.c_float), ("reserved", C.c_int32)]
+
+
+EXPORTS = ["csa_compress", "hca_compress", "csa_index_topk_workspace_size", "csa_index_topk", "csa_index_score",
+           "csa_topk_select_workspace_size", "csa_topk_select", "csa_attend_workspace_size",
+           "hca_attend_workspace_size", "csa_attend", "hca_attend", "sckv_last_error", "sckv_abi_version"]
+
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load() -> C.CDLL:
+    """Loads libsckv.so (raises if it was not built: there is no fallback path)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with __graft_entry__.build() "
+                          "(python -m sequence_compressed_kv_amd.build)")
+    L = C.CDLL(_LIB_PATH)
+    P, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+    L.csa_compress.argtypes = [i32, i64, i32, i32, i64, i64, C.POINTER(PoolStream), C.POINTER(PoolStream), P]
+    L.hca_compress.argtypes = [i32, i64, i32, i32, i64, i64, C.POINTER(PoolStream), P]
+    L.csa_index_topk_workspace_size.argtypes = [C.POINTER(IndexArgs)]
+    L.csa_index_topk_workspace_size.restype = sz
+    L.csa_index_topk.argtypes = [C.POINTER(IndexArgs), P, sz, P]
+    L.csa_index_score.argtypes = [C.POINTER(IndexArgs), P, i64, P]
+    L.csa_topk_select_workspace_size.argtypes = [C.POINTER(IndexArgs)]
+    L.csa_topk_select_workspace_size.restype = sz
+    L.csa_topk_select.argtypes = [C.POINTER(IndexArgs), P, i64, P, sz, P]
+    for n in ("csa_attend_workspace_size", "hca_attend_workspace_size"):
+        getattr(L, n).argtypes = [C.POINTER(AttendArgs)]
+        getattr(L, n).restype = sz
+    for n in ("csa_attend", "hca_attend"):
+        getattr(L, n).argtypes = [C.POINTER(AttendArgs), P, sz, P]
+    for n in ("csa_compress", "hca_compress", "csa_index_topk", "csa_index_score", "csa_topk_select",
+              "csa_attend", "hca_attend"):
+        getattr(L, n).restype = C.c_int
+    L.sckv_last_error.restype = C.c_char_p
+    L.sckv_abi_version.restype = C.c_int32
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != 0:
+        raise SckvError(status, load().sckv_last_error().decode())
+
+
+# ---------------------------------------------------------------- helpers
+def dtype_code(t: Optional[torch.Tensor]) -> int:
+    if t is None:
+        return -1
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+@dataclass
+class RowSpec:
+    """Query rows: decode (pos: int32 device tensor [R], one row per sequence) or causal
+    (positions pos0 .. pos0 + R - 1 of sequence seq0)."""
+    kind: int
+    R: int
+    pos: Optional[torch.Tensor] = None
+    pos_max: int = 0
+    seq0: int = 0
+    pos0: int = 0
+
+    @staticmethod
+    def decode(pos: torch.Tensor, pos_max: int) -> "RowSpec":
+        return RowSpec(ROWS_DECODE, int(pos.shape[0]), pos, int(pos_max))
+
+    @staticmethod
+    def causal(R: int, pos0: int = 0, seq0: int = 0) -> "RowSpec":
+        return RowSpec(ROWS_CAUSAL, int(R), None, 0, int(seq0), int(pos0))
+
+    def c(self) -> Rows:
+        return Rows(_ptr(self.pos), self.kind, self.R, self.pos_max, self.seq0, self.pos0, 0)
+
+
+@dataclass
+class Pool:
+    """One stream pair to pool: val, gate [B][N][D]; bpos [m+o][D] fp32;
+    out [B][E_cap][D]; out_scale [B][E_cap] fp32 (scaled e4m3 output) or None."""
+    val: torch.Tensor
+    gate: torch.Tensor
+    bpos: torch.Tensor
+    out: torch.Tensor
+    out_scale: Optional[torch.Tensor] = None
+
+    def c(self) -> PoolStream:
+        return PoolStream(_ptr(self.val), _ptr(self.gate), _ptr(self.bpos), _ptr(self.out), _ptr(self.out_scale),
+                          int(self.out.shape[1]), int(self.val.shape[2]), dtype_code(self.val),
+                          dtype_code(self.out), 0)
+
+
+# ---------------------------------------------------------------- calls
+def csa_compress(kv: Pool, index_keys: Optional[Pool] = None, *, m: int = 4, o: int = 4, e_begin: int = 0,
+                 e_count: Optional[int] = None, stream=None):
+    B, N = int(kv.val.shape[0]), int(kv.val.shape[1])
+    e_count = (N // m - e_begin) if e_count is None else e_count
+    a = kv.c()
+    b = index_keys.c() if index_keys is not None else None
+    _check(load().csa_compress(B, N, m, o, e_begin, e_count, C.byref(a), C.byref(b) if b is not None else None,
+                               _stream(stream)))
+
+
+def hca_compress(kv: Pool, *, m: int = 128, o: int = 0, e_begin: int = 0, e_count: Optional[int] = None,
+                 stream=None):
+    B, N = int(kv.val.shape[0]), int(kv.val.shape[1])
+    e_count = (N // m - e_begin) if e_count is None else e_count
+    a = kv.c()
+    _check(load().hca_compress(B, N, m, o, e_begin, e_count, C.byref(a), _stream(stream)))
+
+
+def index_args(rows: RowSpec, q, w, keys, out_idx, *, m: int, W: int, k: int, out_score=None) -> IndexArgs:
+    return IndexArgs(rows.c(), _ptr(q), _ptr(w), _ptr(keys), _ptr(out_idx), _ptr(out_score), int(keys.shape[1]),
+                     int(keys.shape[0]), int(q.shape[1]), int(q.shape[2]), dtype_code(q), dtype_code(keys), m, W, k)
+
+
+def csa_index_topk_workspace_size(a: IndexArgs) -> int:
+    return int(load().csa_index_topk_workspace_size(C.byref(a)))
+
+
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
+    if nbytes == 0:
+        return workspace
+    if workspace is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise SckvError(6, f"workspace of {nbytes} bytes needed")
+    return workspace
+
+
+def csa_index_topk(rows: RowSpec, q, w, keys, out_idx, *, m: int = 4, W: int = 128, k: int, out_score=None,
+                   workspace: Optional[torch.Tensor] = None, stream=None):
+    a = index_args(rows, q, w, keys, out_idx, m=m, W=W, k=k, out_score=out_score)
+    n = csa_index_topk_workspace_size(a)
+    if n == 0:
+        _check(load().csa_index_topk(C.byref(a), None, 0, _stream(stream)))
+    ws = _workspace(n, keys.device, workspace)
+    _check(load().csa_index_topk(C.byref(a), _ptr(ws), n, _stream(stream)))
+    return ws
+
+
+def csa_index_score(rows: RowSpec, q, w, keys, scores, *, m: int = 4, W: int = 128, k: int = 1, stream=None):
+    a = index_args(rows, q, w, keys, None, m=m, W=W, k=k)
+    _check(load().csa_index_score(C.byref(a), _ptr(scores), int(scores.stride(0)), _stream(stream)))
+
+
+def csa_topk_select(rows: RowSpec, scores, out_idx, *, keys_meta, m: int = 4, W: int = 128, k: int,
+                    out_score=None, workspace=None, stream=None):
+    """keys_meta: (q, w, keys) tensors describing the indexer (only shapes/dtypes are read)."""
+    q, w, keys = keys_meta
+    a = index_args(rows, q, w, keys, out_idx, m=m, W=W, k=k, out_score=out_score)
+    n = int(load().csa_topk_select_workspace_size(C.byref(a)))
+    ws = _workspace(n, scores.device, workspace)
+    _check(load().csa_topk_select(C.byref(a), _ptr(scores), int(scores.stride(0)), _ptr(ws), n, _stream(stream)))
+
+
+def attend_args(rows: RowSpec, q, entries, win, out, *, m: int, W: int, softmax_scale: float, entry_scale=None,
+                idx=None, lse=None) -> AttendArgs:
+    k = int(idx.shape[1]) if idx is not None else 0
+    return AttendArgs(rows.c(), _ptr(q), _ptr(entries), _ptr(entry_scale), _ptr(idx), _ptr(win), _ptr(out),
+                      _ptr(lse), int(entries.shape[1]), int(win.shape[1]), int(entries.shape[0]), int(q.shape[1]),
+                      int(q.shape[2]), dtype_code(q), dtype_code(entries), dtype_code(win), dtype_code(out), m, W, k,
+                      float(softmax_scale), 0)
+
+
+def _attend(fn: str, a: AttendArgs, device, workspace, stream):
+    L = load()
+    n = int(getattr(L, fn + "_workspace_size")(C.byref(a)))
+    ws = _workspace(n, device, workspace)
+    _check(getattr(L, fn)(C.byref(a), _ptr(ws), n, _stream(stream)))
+    return ws
+
+
+def csa_attend(rows: RowSpec, q, entries, idx, win, out, *, m: int = 4, W: int = 128, softmax_scale: float,
+               entry_scale=None, lse=None, workspace=None, stream=None):
+    a = attend_args(rows, q, entries, win, out, m=m, W=W, softmax_scale=softmax_scale, entry_scale=entry_scale,
+                    idx=idx, lse=lse)
+    return _attend("csa_attend", a, entries.device, workspace, stream)
+
+
+def hca_attend(rows: RowSpec, q, entries, win, out, *, m: int = 128, W: int = 128, softmax_scale: float,
+               entry_scale=None, lse=None, workspace=None, stream=None):
+    a = attend_args(rows, q, entries, win, out, m=m, W=W, softmax_scale=softmax_scale, entry_scale=entry_scale,
+                    lse=lse)
+    return _attend("hca_attend", a, entries.device, workspace, stream)
+
+
+def abi_version() -> int:
+    return int(load().sckv_abi_version())

@@ -1,0 +1,483 @@
+// Sparse-plus-window (CSA) and dense-plus-window (HCA) attention over a shared
+// latent K = V: o_h = sum_u softmax_u(scale * q_h . u) u, u over the kept entries
+// and the raw tokens max(0, t-W+1) .. t, one softmax for both (knightli.com
+// DeepSeek-V4 KV-cache article, sections "CSA", "HCA" and "Ventana deslizante").
+//
+// MFMA path (bf16 queries; bf16 or e4m3 entries; bf16 window):
+//   block = (split, row); one wave per 16 heads.  Items are staged 32 at a time
+//   into LDS twice: row-major bf16 for Q.K^T and transposed fp16 for P.V.
+//   S^T = items x heads on v_mfma_f32_16x16x32_bf16 (items as M), so each lane
+//   holds one head column; the S accumulator registers are re-used directly as
+//   the A operand of P.V on v_mfma_f32_16x16x32_f16 (the K order of the item
+//   axis is chosen to match), with an online softmax between the two.
+//   fp8 entries keep their exact codes in the MFMA operands; the per-entry scale
+//   multiplies the logit and the probability instead.
+//   Split-K over the item list writes (m, l, unnormalised o) partials that a
+//   second kernel merges in a fixed order.
+// fp32 path: plain VALU, one block per row.
+#include "device_common.h"
+#include "sckv_internal.h"
+
+namespace sckv {
+
+constexpr int kChunk = 32;
+
+struct AttendParams {
+  const uint16_t* q;
+  const void* entries;
+  const float* escale;
+  const int32_t* idx;
+  const void* win;
+  void* out;
+  float* lse;
+  float* ws_o;
+  float* ws_ml;
+  const int32_t* pos;
+  int64_t E_cap, R_w;
+  int32_t kind, pos_max, seq0, pos0;
+  int32_t H, m, W, k;
+  int32_t csa, out_dtype, nsplit, per_split;
+  float scale;
+};
+
+struct RowItems {
+  int64_t seq, t, e_vis, n_list, n_win, win_first, n_items;
+};
+
+__device__ __forceinline__ RowItems row_items(const AttendParams& p, int r) {
+  RowItems ri;
+  if (p.kind == SCKV_ROWS_DECODE) {
+    int32_t t = p.pos[r];
+    ri.t = t < 0 ? 0 : (t > p.pos_max ? p.pos_max : t);
+    ri.seq = r;
+  } else {
+    ri.t = (int64_t)p.pos0 + r;
+    ri.seq = p.seq0;
+  }
+  const int64_t d = ri.t - p.W;
+  int64_t e = d < 0 ? 0 : d / p.m;
+  ri.e_vis = e < p.E_cap ? e : p.E_cap;
+  ri.n_list = p.csa ? p.k : ri.e_vis;
+  ri.n_win = ri.t + 1 < p.W ? ri.t + 1 : p.W;
+  ri.win_first = ri.t - ri.n_win + 1;
+  ri.n_items = ri.n_list + ri.n_win;
+  return ri;
+}
+
+// Where item q of a row lives: entry row (>= 0), window slot (encoded as
+// -2 - slot) or nothing (-1).
+__device__ __forceinline__ int64_t item_source(const AttendParams& p, const RowItems& ri, int r, int64_t q) {
+  if (q >= ri.n_items) return -1;
+  if (q < ri.n_list) {
+    const int64_t j = p.csa ? (int64_t)p.idx[(int64_t)r * p.k + q] : q;
+    return (j >= 0 && j < p.E_cap) ? j : -1;
+  }
+  const int64_t i = ri.win_first + (q - ri.n_list);
+  return -2 - (i % p.R_w);
+}
+
+template <int ENT, int D, int NW>
+struct Stage {
+  static constexpr int NT = NW * kWave;
+  static constexpr int SEGS_PER_ITEM = D / 8;
+  static constexpr int NSEG = kChunk * SEGS_PER_ITEM;
+  static constexpr int SPT = (NSEG + NT - 1) / NT;
+  u32x4 v[SPT];       // 8 bf16 values per segment
+  float sc[SPT];      // item scale (e4m3 entries), 1 otherwise; 0 marks a masked item
+};
+
+template <int ENT, int D, int NW>
+__device__ __forceinline__ void stage_load(const AttendParams& p, const RowItems& ri, int r, int64_t q0,
+                                           Stage<ENT, D, NW>& st) {
+  using S = Stage<ENT, D, NW>;
+#pragma unroll
+  for (int s = 0; s < S::SPT; ++s) {
+    const int seg = threadIdx.x + s * S::NT;
+    st.v[s] = u32x4{0u, 0u, 0u, 0u};
+    st.sc[s] = 0.f;
+    if (seg < S::NSEG) {
+      const int c = seg / S::SEGS_PER_ITEM, part = seg % S::SEGS_PER_ITEM;
+      const int64_t src = item_source(p, ri, r, q0 + c);
+      if (src >= 0) {
+        const int64_t row = ri.seq * p.E_cap + src;
+        if constexpr (ENT == SCKV_E4M3) {
+          const u32x2 raw = *reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(p.entries) + row * D + part * 8);
+          st.v[s] = e4m3x8_to_bf16x8(raw);
+          st.sc[s] = p.escale[row];
+        } else {
+          st.v[s] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.entries) + row * D + part * 8);
+          st.sc[s] = 1.f;
+        }
+      } else if (src <= -2) {
+        const int64_t row = ri.seq * p.R_w + (-2 - src);
+        st.v[s] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.win) + row * D + part * 8);
+        st.sc[s] = 1.f;
+      }
+    }
+  }
+}
+
+template <int D>
+struct Lds {
+  static constexpr int KR_STRIDE = D + 8;        // bf16 elements per item row
+  static constexpr int VT_STRIDE = kChunk + 4;   // fp16 elements per dim row
+  uint16_t kr[kChunk * KR_STRIDE];
+  _Float16 vt[D * VT_STRIDE];
+  float isc[kChunk];
+};
+
+template <int ENT, int D, int NW>
+__device__ __forceinline__ void stage_store(const Stage<ENT, D, NW>& st, Lds<D>& L) {
+  using S = Stage<ENT, D, NW>;
+#pragma unroll
+  for (int s = 0; s < S::SPT; ++s) {
+    const int seg = threadIdx.x + s * S::NT;
+    if (seg < S::NSEG) {
+      const int c = seg / S::SEGS_PER_ITEM, part = seg % S::SEGS_PER_ITEM;
+      *reinterpret_cast<u32x4*>(&L.kr[c * Lds<D>::KR_STRIDE + part * 8]) = st.v[s];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t bits = (st.v[s][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+        L.vt[(part * 8 + e) * Lds<D>::VT_STRIDE + c] = (_Float16)bf16_to_f32(bits);
+      }
+      if (part == 0) L.isc[c] = st.sc[s];
+    }
+  }
+}
+
+template <int ENT, int D, int NW>
+__global__ __launch_bounds__(NW * 64) void attend_mfma(AttendParams p) {
+  constexpr int KSQ = D / 32;      // k-steps of Q.K^T
+  constexpr int ND = D / 16;       // 16-dim output tiles
+  __shared__ Lds<D> L;
+
+  const int r = blockIdx.y, split = blockIdx.x;
+  const RowItems ri = row_items(p, r);
+  const int l = lane_id(), w = wave_id();
+  const int col = l & 15, g = l >> 4;
+  const int head = 16 * w + col;
+
+  const int64_t q_begin = (int64_t)split * p.per_split * kChunk;
+  int64_t q_end = q_begin + (int64_t)p.per_split * kChunk;
+  q_end = q_end < ri.n_items ? q_end : ri.n_items;
+
+  // query fragments (B operand of S^T = items x heads): dims g*D/4 + 8 ks .. +7
+  bf16x8 bq[KSQ];
+  {
+    const u32x4* qp = reinterpret_cast<const u32x4*>(p.q + ((int64_t)r * p.H + head) * D + g * (D / 4));
+#pragma unroll
+    for (int ks = 0; ks < KSQ; ++ks) bq[ks] = bitcast<bf16x8>(qp[ks]);
+  }
+  f32x4 o[ND];
+#pragma unroll
+  for (int nd = 0; nd < ND; ++nd) o[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  Stage<ENT, D, NW> st;
+  if (q_begin < q_end) stage_load<ENT, D, NW>(p, ri, r, q_begin, st);
+  for (int64_t q0 = q_begin; q0 < q_end; q0 += kChunk) {
+    __syncthreads();
+    stage_store<ENT, D, NW>(st, L);
+    __syncthreads();
+    if (q0 + kChunk < q_end) stage_load<ENT, D, NW>(p, ri, r, q0 + kChunk, st);
+
+    // S^T for the chunk: two 16-item tiles
+    f32x4 sacc[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const uint16_t* kr = &L.kr[(16 * mt + col) * Lds<D>::KR_STRIDE + g * (D / 4)];
+#pragma unroll
+      for (int ks = 0; ks < KSQ; ++ks) {
+        const bf16x8 a = bitcast<bf16x8>(*reinterpret_cast<const u32x4*>(kr + 8 * ks));
+        acc = mfma16_bf16(a, bq[ks], acc);
+      }
+      sacc[mt] = acc;
+    }
+    // logits, chunk maximum per head
+    float x[8], isc[8];
+    float cmax = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float sc = L.isc[16 * mt + 4 * g + i];
+        isc[4 * mt + i] = sc;
+        const float v = sc != 0.f ? sacc[mt][i] * (p.scale * sc) : -INFINITY;
+        x[4 * mt + i] = v;
+        cmax = fmaxf(cmax, v);
+      }
+    cmax = fmaxf(cmax, shfl_xor_f(cmax, 16));
+    cmax = fmaxf(cmax, shfl_xor_f(cmax, 32));
+    const float m_new = fmaxf(m_run, cmax);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = m_run == -INFINITY ? 0.f : expf(m_run - m_new);
+    m_run = m_new;
+    f16x8 pa;
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float pe = expf(x[e] - m_use);
+      psum += pe;
+      pa[e] = (_Float16)(ENT == SCKV_E4M3 ? pe * isc[e] : pe);
+    }
+    l_run = l_run * alpha + psum;
+    // rescale rows (heads 4g + i of this wave) by their alpha
+    float al[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i, kWave);
+#pragma unroll
+    for (int nd = 0; nd < ND; ++nd) {
+      const _Float16* vp = &L.vt[(16 * nd + col) * Lds<D>::VT_STRIDE + 4 * g];
+      const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
+      const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 16);
+      const f16x8 bv = bitcast<f16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
+      f32x4 acc = o[nd];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] *= al[i];
+      o[nd] = mfma16_f16(pa, bv, acc);
+    }
+  }
+
+  // per-head totals
+  float l_tot = l_run;
+  l_tot += shfl_xor_f(l_tot, 16);
+  l_tot += shfl_xor_f(l_tot, 32);
+  float lrow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lrow[i] = __shfl(l_tot, 4 * g + i, kWave);
+  const int hbase = 16 * w + 4 * g;
+  if (p.nsplit == 1) {
+#pragma unroll
+    for (int nd = 0; nd < ND; ++nd)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float v = o[nd][i] / lrow[i];
+        const int64_t off = ((int64_t)r * p.H + hbase + i) * D + 16 * nd + col;
+        if (p.out_dtype == SCKV_BF16) static_cast<uint16_t*>(p.out)[off] = (uint16_t)f32_to_bf16_rne(v);
+        else static_cast<float*>(p.out)[off] = v;
+      }
+    if (p.lse && g == 0) p.lse[(int64_t)r * p.H + head] = m_run + logf(l_tot);
+  } else {
+    const int64_t sbase = ((int64_t)r * p.nsplit + split) * p.H;
+#pragma unroll
+    for (int nd = 0; nd < ND; ++nd)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p.ws_o[(sbase + hbase + i) * D + 16 * nd + col] = o[nd][i];
+    if (g == 0) {
+      p.ws_ml[(sbase + head) * 2] = m_run;
+      p.ws_ml[(sbase + head) * 2 + 1] = l_tot;
+    }
+  }
+}
+
+// Merge of split partials: o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s, in split order.
+__global__ __launch_bounds__(128) void attend_combine(const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
+                                                      void* __restrict__ out, float* __restrict__ lse, int H, int D,
+                                                      int nsplit, int out_dtype) {
+  const int r = blockIdx.y, h = blockIdx.x;
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ws_ml[(((int64_t)r * nsplit + s) * H + h) * 2]);
+  float L = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float* ml = &ws_ml[(((int64_t)r * nsplit + s) * H + h) * 2];
+    L += ml[0] == -INFINITY ? 0.f : expf(ml[0] - M) * ml[1];
+  }
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    float acc = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+      const int64_t base = ((int64_t)r * nsplit + s) * H + h;
+      const float ms = ws_ml[base * 2];
+      if (ms != -INFINITY) acc += expf(ms - M) * ws_o[base * D + d];
+    }
+    const float v = acc / L;
+    const int64_t off = ((int64_t)r * H + h) * D + d;
+    if (out_dtype == SCKV_BF16) static_cast<uint16_t*>(out)[off] = (uint16_t)f32_to_bf16_rne(v);
+    else static_cast<float*>(out)[off] = v;
+  }
+  if (lse && threadIdx.x == 0) lse[(int64_t)r * H + h] = M + logf(L);
+}
+
+// fp32 path: one block per row, items 64 at a time through LDS.
+constexpr int kF32Chunk = 64;
+__global__ __launch_bounds__(256) void attend_f32(AttendParams p, int D) {
+  extern __shared__ float sm[];
+  const int H = p.H;
+  float* qs = sm;                              // [H][D]
+  float* it = qs + H * D;                      // [64][D]
+  float* lg = it + kF32Chunk * D;              // [H][64]
+  float* mrun = lg + H * kF32Chunk;            // [H]
+  float* lrun = mrun + H;                      // [H]
+  float* alpha = lrun + H;                     // [H]
+  float* ok = alpha + H;                       // [64]
+  const int r = blockIdx.y;
+  const RowItems ri = row_items(p, r);
+  const float* qg = reinterpret_cast<const float*>(p.q) + (int64_t)r * H * D;
+  for (int i = threadIdx.x; i < H * D; i += 256) qs[i] = qg[i];
+  for (int h = threadIdx.x; h < H; h += 256) { mrun[h] = -INFINITY; lrun[h] = 0.f; }
+  constexpr int MAXP = 16;                     // H * D <= 4096 = 16 * 256
+  float o[MAXP];
+#pragma unroll
+  for (int k = 0; k < MAXP; ++k) o[k] = 0.f;
+  __syncthreads();
+  for (int64_t q0 = 0; q0 < ri.n_items; q0 += kF32Chunk) {
+    for (int c = threadIdx.x; c < kF32Chunk; c += 256) {
+      const int64_t src = item_source(p, ri, r, q0 + c);
+      ok[c] = src == -1 ? 0.f : 1.f;
+    }
+    for (int i = threadIdx.x; i < kF32Chunk * D; i += 256) {
+      const int c = i / D, d = i % D;
+      const int64_t src = item_source(p, ri, r, q0 + c);
+      float v = 0.f;
+      if (src >= 0) v = static_cast<const float*>(p.entries)[(ri.seq * p.E_cap + src) * D + d];
+      else if (src <= -2) v = static_cast<const float*>(p.win)[(ri.seq * p.R_w + (-2 - src)) * D + d];
+      it[i] = v;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < H * kF32Chunk; i += 256) {
+      const int h = i / kF32Chunk, c = i % kF32Chunk;
+      float s = 0.f;
+      for (int d = 0; d < D; ++d) s = fmaf(qs[h * D + d], it[c * D + d], s);
+      lg[i] = ok[c] != 0.f ? s * p.scale : -INFINITY;
+    }
+    __syncthreads();
+    for (int h = threadIdx.x; h < H; h += 256) {
+      float cm = -INFINITY;
+      for (int c = 0; c < kF32Chunk; ++c) cm = fmaxf(cm, lg[h * kF32Chunk + c]);
+      const float mn = fmaxf(mrun[h], cm);
+      const float mu = mn == -INFINITY ? 0.f : mn;
+      const float a = mrun[h] == -INFINITY ? 0.f : expf(mrun[h] - mn);
+      float ps = 0.f;
+      for (int c = 0; c < kF32Chunk; ++c) {
+        const float e = expf(lg[h * kF32Chunk + c] - mu);
+        lg[h * kF32Chunk + c] = e;
+        ps += e;
+      }
+      lrun[h] = lrun[h] * a + ps;
+      mrun[h] = mn;
+      alpha[h] = a;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < MAXP; ++k) {
+      const int i = threadIdx.x + 256 * k;
+      if (i < H * D) {
+        const int h = i / D, d = i % D;
+        float acc = o[k] * alpha[h];
+        for (int c = 0; c < kF32Chunk; ++c) acc = fmaf(lg[h * kF32Chunk + c], it[c * D + d], acc);
+        o[k] = acc;
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int k = 0; k < MAXP; ++k) {
+    const int i = threadIdx.x + 256 * k;
+    if (i < H * D) {
+      const int h = i / D;
+      const float v = o[k] / lrun[h];
+      const int64_t off = (int64_t)r * H * D + i;
+      if (p.out_dtype == SCKV_BF16) static_cast<uint16_t*>(p.out)[off] = (uint16_t)f32_to_bf16_rne(v);
+      else static_cast<float*>(p.out)[off] = v;
+    }
+  }
+  if (p.lse)
+    for (int h = threadIdx.x; h < H; h += 256) p.lse[(int64_t)r * H + h] = mrun[h] + logf(lrun[h]);
+}
+
+AttendPlan plan_attend(const sckv_attend_args& a, bool csa) {
+  AttendPlan pl;
+  const int64_t t = a.rows.kind == SCKV_ROWS_DECODE ? a.rows.pos_max : (int64_t)a.rows.pos0 + a.rows.R - 1;
+  int64_t ev = entries_visible(t, a.m, a.W);
+  ev = ev < a.E_cap ? ev : a.E_cap;
+  pl.items = (csa ? a.k : ev) + a.W;
+  pl.chunks = (pl.items + kChunk - 1) / kChunk;
+  pl.mfma = a.entry_dtype != SCKV_F32;
+  if (!pl.mfma) {
+    pl.nsplit = 1;
+    pl.per_split = pl.chunks;
+    pl.ok = true;
+    return pl;
+  }
+  const int64_t target_blocks = 512;
+  int64_t ns = (target_blocks + a.rows.R - 1) / a.rows.R;
+  ns = ns < 1 ? 1 : (ns > pl.chunks ? pl.chunks : ns);
+  int64_t per = (pl.chunks + ns - 1) / ns;
+  const int64_t min_per = pl.chunks < 8 ? pl.chunks : 8;
+  per = per < min_per ? min_per : per;
+  per = per < 1 ? 1 : per;
+  pl.per_split = per;
+  pl.nsplit = (int32_t)((pl.chunks + per - 1) / per);
+  if (pl.nsplit < 1) pl.nsplit = 1;
+  if (pl.nsplit > 1)
+    pl.ws_bytes = (size_t)a.rows.R * pl.nsplit * a.H * ((size_t)a.D + 2) * sizeof(float) + 256;
+  pl.ok = true;
+  return pl;
+}
+
+template <int ENT, int D>
+static void launch_mfma_d(const AttendParams& p, int H, dim3 grid, hipStream_t s) {
+  switch (H / 16) {
+    case 1: hipLaunchKernelGGL((attend_mfma<ENT, D, 1>), grid, dim3(64), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((attend_mfma<ENT, D, 2>), grid, dim3(128), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((attend_mfma<ENT, D, 4>), grid, dim3(256), 0, s, p); break;
+    default: hipLaunchKernelGGL((attend_mfma<ENT, D, 8>), grid, dim3(512), 0, s, p); break;
+  }
+}
+
+template <int ENT>
+static void launch_mfma_e(const AttendParams& p, int H, int D, dim3 grid, hipStream_t s) {
+  switch (D) {
+    case 64: launch_mfma_d<ENT, 64>(p, H, grid, s); break;
+    case 128: launch_mfma_d<ENT, 128>(p, H, grid, s); break;
+    case 256: launch_mfma_d<ENT, 256>(p, H, grid, s); break;
+    default: launch_mfma_d<ENT, 512>(p, H, grid, s); break;
+  }
+}
+
+hipError_t launch_attend(const sckv_attend_args& a, bool csa, const AttendPlan& pl, void* ws, hipStream_t stream) {
+  AttendParams p{};
+  p.q = static_cast<const uint16_t*>(a.q);
+  p.entries = a.entries;
+  p.escale = a.entry_scale;
+  p.idx = csa ? a.idx : nullptr;
+  p.win = a.win;
+  p.out = a.out;
+  p.lse = a.lse;
+  p.pos = a.rows.pos;
+  p.E_cap = a.E_cap;
+  p.R_w = a.R_w;
+  p.kind = a.rows.kind;
+  p.pos_max = a.rows.pos_max;
+  p.seq0 = a.rows.seq0;
+  p.pos0 = a.rows.pos0;
+  p.H = a.H;
+  p.m = a.m;
+  p.W = a.W;
+  p.k = a.k;
+  p.csa = csa ? 1 : 0;
+  p.out_dtype = a.out_dtype;
+  p.nsplit = pl.nsplit;
+  p.per_split = (int32_t)pl.per_split;
+  p.scale = a.softmax_scale;
+  if (pl.nsplit > 1) {
+    p.ws_o = static_cast<float*>(ws);
+    p.ws_ml = p.ws_o + (size_t)a.rows.R * pl.nsplit * a.H * a.D;
+  }
+  if (!pl.mfma) {
+    const size_t lds = ((size_t)a.H * a.D + (size_t)kF32Chunk * a.D + (size_t)a.H * kF32Chunk + 3 * (size_t)a.H +
+                        kF32Chunk) * sizeof(float);
+    hipLaunchKernelGGL(attend_f32, dim3(1, a.rows.R), dim3(256), lds, stream, p, a.D);
+    return hipGetLastError();
+  }
+  const dim3 grid((unsigned)pl.nsplit, (unsigned)a.rows.R);
+  if (a.entry_dtype == SCKV_E4M3) launch_mfma_e<SCKV_E4M3>(p, a.H, a.D, grid, stream);
+  else launch_mfma_e<SCKV_BF16>(p, a.H, a.D, grid, stream);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || pl.nsplit == 1) return e;
+  hipLaunchKernelGGL(attend_combine, dim3(a.H, a.rows.R), dim3(128), 0, stream, p.ws_o, p.ws_ml, a.out, a.lse,
+                     a.H, a.D, pl.nsplit, a.out_dtype);
+  return hipGetLastError();
+}
+
+}  // namespace sckv

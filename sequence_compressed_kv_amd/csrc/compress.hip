@@ -1,0 +1,140 @@
+// Gated per-channel softmax pooling of per-token streams into compressed entries.
+//
+// c_j[d] = sum_{i in P_j} softmax_i(g_i[d] + Bpos[i - m j + o][d]) v_i[d], with
+// P_j = [m j - o, m j + m) cut to tokens i >= 0 (the CSA decode workload
+// definition's compressor; knightli.com DeepSeek-V4 KV-cache article, sections
+// "CSA" (4:1, learned pool, overlapping windows) and "HCA" (128:1)).
+//
+// HBM streaming: lane groups of D/8 lanes own one entry, each lane 8 channels,
+// so every token row is read as one contiguous D-wide segment.  The softmax is
+// taken online with one exp per (token, channel): the larger of the running
+// maximum and the new logit sets which side is rescaled.
+#include "device_common.h"
+#include "sckv_internal.h"
+
+namespace sckv {
+
+template <int IN>
+__device__ __forceinline__ void load8(const void* base, int64_t elem, float (&x)[8]) {
+  if constexpr (IN == SCKV_BF16) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + elem);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(v[i] << 16);
+      x[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+    }
+  } else {
+    const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + elem);
+    const f32x4 a = p[0], b = p[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { x[i] = a[i]; x[4 + i] = b[i]; }
+  }
+}
+
+template <int IN, int OUT, bool SCALED>
+__global__ __launch_bounds__(256) void compress_kernel(
+    const void* __restrict__ val, const void* __restrict__ gate, const float* __restrict__ bpos,
+    void* __restrict__ out, float* __restrict__ out_scale, int64_t N, int D, int m, int o,
+    int64_t e_begin, int64_t e_count, int64_t E_cap, int G) {
+  const int lane = lane_id();
+  const int epw = kWave / G;
+  const int slot = lane / G, sub = lane % G;
+  const int64_t e_local = (int64_t)blockIdx.x * (4 * epw) + wave_id() * epw + slot;
+  const bool active = e_local < e_count;
+  const int64_t e = e_begin + (active ? e_local : 0);
+  const int64_t b = blockIdx.y;
+  const int ch = sub * 8;
+
+  const int64_t i0 = (int64_t)m * e - o;
+  const int64_t i1 = (int64_t)m * e + m;
+  float mx[8], l[8], acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) { mx[c] = -INFINITY; l[c] = 0.f; acc[c] = 0.f; }
+
+  for (int64_t i = i0 < 0 ? 0 : i0; i < i1; ++i) {
+    float g[8], v[8];
+    const int64_t row = (b * N + i) * D + ch;
+    load8<IN>(gate, row, g);
+    load8<IN>(val, row, v);
+    const f32x4* bp = reinterpret_cast<const f32x4*>(bpos + (i - i0) * D + ch);
+    const f32x4 bp0 = bp[0], bp1 = bp[1];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float a = g[c] + (c < 4 ? bp0[c] : bp1[c - 4]);
+      const float d = a - mx[c];
+      const float x = expf(-fabsf(d));
+      const bool up = d > 0.f;
+      const float sc = up ? x : 1.f;
+      const float p = up ? 1.f : x;
+      l[c] = l[c] * sc + p;
+      acc[c] = acc[c] * sc + p * v[c];
+      mx[c] = fmaxf(mx[c], a);
+    }
+  }
+  float cv[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) cv[c] = acc[c] / l[c];
+
+  const int64_t orow = (b * E_cap + e) * D + ch;
+  if constexpr (OUT == SCKV_F32) {
+    if (active) {
+      f32x4* p = reinterpret_cast<f32x4*>(static_cast<float*>(out) + orow);
+      p[0] = f32x4{cv[0], cv[1], cv[2], cv[3]};
+      p[1] = f32x4{cv[4], cv[5], cv[6], cv[7]};
+    }
+  } else if constexpr (OUT == SCKV_BF16) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = f32_to_bf16_rne(cv[2 * i]) | (f32_to_bf16_rne(cv[2 * i + 1]) << 16);
+    if (active) *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + orow) = r;
+  } else {
+    float scale = 1.f;
+    if constexpr (SCALED) {
+      float amax = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) amax = fmaxf(amax, fabsf(cv[c]));
+      for (int s = 1; s < G; s <<= 1) amax = fmaxf(amax, shfl_xor_f(amax, s));
+      scale = amax > 0.f ? amax / 448.0f : 1.0f;
+    }
+    u32x2 r = {0u, 0u};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint32_t q = f32_to_e4m3_sat(SCALED ? cv[c] / scale : cv[c]);
+      r[c >> 2] |= q << ((c & 3) * 8);
+    }
+    if (active) {
+      *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(out) + orow) = r;
+      if (SCALED && sub == 0) out_scale[b * E_cap + e] = scale;
+    }
+  }
+}
+
+template <int IN>
+static hipError_t launch_in(const sckv_pool_stream& s, int32_t B, int64_t N, int32_t m, int32_t o,
+                            int64_t e_begin, int64_t e_count, hipStream_t stream) {
+  const int G = s.D / 8;
+  const int epw = kWave / G;
+  const dim3 grid((unsigned)((e_count + 4 * epw - 1) / (4 * epw)), (unsigned)B);
+  const dim3 block(256);
+#define SCKV_LAUNCH(OUT, SC)                                                                    \
+  hipLaunchKernelGGL((compress_kernel<IN, OUT, SC>), grid, block, 0, stream, s.val, s.gate,     \
+                     s.bpos, s.out, s.out_scale, N, s.D, m, o, e_begin, e_count, s.E_cap, G)
+  switch (s.out_dtype) {
+    case SCKV_F32: SCKV_LAUNCH(SCKV_F32, false); break;
+    case SCKV_BF16: SCKV_LAUNCH(SCKV_BF16, false); break;
+    default:
+      if (s.out_scale) SCKV_LAUNCH(SCKV_E4M3, true);
+      else SCKV_LAUNCH(SCKV_E4M3, false);
+  }
+#undef SCKV_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_compress(const sckv_pool_stream& s, int32_t B, int64_t N, int32_t m, int32_t o,
+                           int64_t e_begin, int64_t e_count, hipStream_t stream) {
+  if (e_count == 0) return hipSuccess;
+  if (s.in_dtype == SCKV_BF16) return launch_in<SCKV_BF16>(s, B, N, m, o, e_begin, e_count, stream);
+  return launch_in<SCKV_F32>(s, B, N, m, o, e_begin, e_count, stream);
+}
+
+}  // namespace sckv

@@ -1,0 +1,147 @@
+// Device helpers shared by the gfx950 kernels: storage codecs, MFMA wrappers,
+// wavefront reductions and block scans.  Wavefronts are 64 lanes wide.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sckv {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------------ bf16
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 bits (finite inputs; inf/nan keep their class).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u) return (u >> 16) | ((u & 0xffffu) ? 0x40u : 0u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// ------------------------------------------------------------------ OCP e4m3 ("fn")
+// Saturating round-to-nearest-even fp32 -> e4m3 code.  Built from the format
+// definition: 3 mantissa bits, bias 7, subnormal step 2^-9, largest finite 448.
+__device__ __forceinline__ uint32_t f32_to_e4m3_sat(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  float a = fminf(fabsf(x), 448.0f);
+  uint32_t code;
+  if (a < 0.015625f) {                       // below 2^-6: multiples of 2^-9 (q = 8 is 2^-6, code 8)
+    code = (uint32_t)__builtin_rintf(a * 512.0f);
+  } else {
+    int e = (int)((__float_as_uint(a) >> 23) & 0xff) - 127;     // a in [2^e, 2^(e+1))
+    float mant = a * __uint_as_float((uint32_t)(127 - e) << 23);  // exact: a / 2^e in [1, 2)
+    uint32_t q = (uint32_t)__builtin_rintf((mant - 1.0f) * 8.0f);
+    if (q == 8) { q = 0; ++e; }
+    code = ((uint32_t)(e + 7) << 3) | q;
+  }
+  return sign | code;
+}
+
+// e4m3 code -> bf16 bits (exact: every e4m3 value is a bf16 value).
+__device__ __forceinline__ uint32_t e4m3_to_bf16_bits(uint32_t c) {
+  const uint32_t s = (c & 0x80u) << 8;
+  const uint32_t e = (c >> 3) & 15u, mt = c & 7u;
+  if (e) return s | ((e + 120u) << 7) | (mt << 4);
+  // subnormal mt * 2^-9: normalise (mt = 0 is a signed zero)
+  if (mt == 0) return s;
+  const uint32_t lz = (mt >= 4) ? 0u : (mt >= 2 ? 1u : 2u);   // leading position of mt
+  const uint32_t ex = 120u - lz;                                // exponent field of 2^(-7-lz)
+  const uint32_t frac = ((mt << (lz + 1)) & 7u) << 4;           // drop the leading one
+  return s | (ex << 7) | frac;
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) { return bf16_to_f32(e4m3_to_bf16_bits(c)); }
+
+// 8 e4m3 codes (little-endian in two dwords) -> 8 bf16 packed in four dwords.
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(u32x2 v) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = v[i >> 1] >> ((i & 1) * 16);
+    r[i] = e4m3_to_bf16_bits(w & 0xffu) | (e4m3_to_bf16_bits((w >> 8) & 0xffu) << 16);
+  }
+  return r;
+}
+
+// ------------------------------------------------------------------ order-preserving score keys
+// Monotone map fp32 -> uint32 (larger float -> larger key); -0 is ranked as +0.
+__device__ __forceinline__ uint32_t score_key(float s) {
+  uint32_t u = __float_as_uint(s == 0.0f ? 0.0f : s);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_score(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(u);
+}
+
+// ------------------------------------------------------------------ MFMA (gfx950)
+// 16x16x32: A lane l holds row l%16, B lane l holds column l%16, each with 8 K
+// elements of K-group l/16; D lane l holds column l%16, rows 4*(l/16) + i.
+__device__ __forceinline__ f32x4 mfma16_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16_f16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+// 32x32x16: A lane l holds row l%32, B column l%32, 8 K elements of K-group l/32;
+// D lane l holds column l%32, rows 8*(i/4) + 4*(l/32) + i%4 for register i.
+__device__ __forceinline__ f32x16 mfma32_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <typename T, typename S>
+__device__ __forceinline__ T bitcast(const S& s) {
+  static_assert(sizeof(T) == sizeof(S), "size");
+  return __builtin_bit_cast(T, s);
+}
+
+// ------------------------------------------------------------------ wave / block helpers
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+__device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
+
+__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, kWave); }
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    uint32_t t = __shfl_up(v, d, kWave);
+    if (l >= d) v += t;
+  }
+  return v;
+}
+
+// Exclusive prefix sum across the block (blockDim.x = NT threads, NT/64 <= 64 waves).
+// `sh` needs NT/64 + 1 words of LDS.  Returns the thread's exclusive prefix and
+// writes the block total to *total.  Contains barriers: call from every thread.
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, uint32_t* total) {
+  constexpr int NW = NT / kWave;
+  const uint32_t inc = wave_incl_scan(v);
+  const int w = wave_id(), l = lane_id();
+  if (l == kWave - 1) sh[w] = inc;
+  __syncthreads();
+  if (w == 0) {
+    uint32_t x = (l < NW) ? sh[l] : 0u;
+    uint32_t xi = wave_incl_scan(x);
+    if (l < NW) sh[l] = xi - x;
+    if (l == NW - 1) sh[NW] = xi;
+  }
+  __syncthreads();
+  const uint32_t r = sh[w] + inc - v;
+  *total = sh[NW];
+  __syncthreads();
+  return r;
+}
+
+}  // namespace sckv

@@ -1,0 +1,224 @@
+// Lightning-indexer scoring: s_j = sum_h w_h * max(0, qI_h . kI_j) for every
+// visible entry j (knightli.com DeepSeek-V4 KV-cache article, section "CSA":
+// the indexer scores the compressed blocks before the top-k; the score form is
+// fixed by the CSA decode workload definition).
+//
+// MFMA path (bf16 queries; bf16 or e4m3 keys dequantised exactly to bf16): the
+// contraction is [H_I x D_I] . [D_I x 32 keys] per tile on v_mfma_f32_32x32x16_bf16,
+// heads as M, keys as N.  Each lane owns one key column and 16 head rows per
+// 32-head tile, so the ReLU . w head reduction is lane-local plus one exchange
+// between the two half-waves.  The D_I axis is split between the half-waves as
+// two contiguous halves: a lane streams 128 contiguous key bytes per tile.
+//   decode rows : a block takes one row and a 512-key range, 4 waves x 128 keys
+//   causal rows : a block takes 4 consecutive rows (one per wave) and walks every
+//                 visible key tile; blocks with the longest rows start first
+#include "device_common.h"
+#include "sckv_internal.h"
+
+namespace sckv {
+
+struct RowRef {
+  int64_t seq;
+  int64_t t;
+};
+
+__device__ __forceinline__ RowRef row_ref(int kind, const int32_t* pos, int32_t pos_max, int32_t seq0,
+                                          int32_t pos0, int r) {
+  if (kind == SCKV_ROWS_DECODE) {
+    int32_t t = pos[r];
+    t = t < 0 ? 0 : (t > pos_max ? pos_max : t);
+    return {r, t};
+  }
+  return {seq0, (int64_t)pos0 + r};
+}
+
+__device__ __forceinline__ int64_t visible(int64_t t, int m, int W, int64_t E_cap) {
+  const int64_t d = t - W;
+  const int64_t e = d < 0 ? 0 : d / m;
+  return e < E_cap ? e : E_cap;
+}
+
+// Keys of one 32-key tile as MFMA B fragments: lane (n = l%32, half hh = l/32)
+// holds dims hh*DI/2 + 8 ks .. +7 of key n, for ks = 0 .. DI/16 - 1.
+template <int KEY, int DI>
+__device__ __forceinline__ void load_key_tile(const void* keys, int64_t row_elem, bf16x8 (&b)[DI / 16]) {
+  constexpr int KS = DI / 16;
+  if constexpr (KEY == SCKV_BF16) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(keys) + row_elem);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) b[ks] = bitcast<bf16x8>(p[ks]);
+  } else {
+    const u32x2* p = reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(keys) + row_elem);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) b[ks] = bitcast<bf16x8>(e4m3x8_to_bf16x8(p[ks]));
+  }
+}
+
+template <int KEY, int HI, int DI>
+struct ScoreWave {
+  static constexpr int MT = HI / 32;
+  static constexpr int KS = DI / 16;
+  bf16x8 a[MT][KS];
+  float w[MT][16];
+
+  __device__ __forceinline__ void load_query(const uint16_t* q_row, const float* w_row) {
+    const int l = lane_id(), n = l & 31, hh = l >> 5;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const u32x4* p = reinterpret_cast<const u32x4*>(q_row + (int64_t)(32 * mt + n) * DI + hh * (DI / 2));
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) a[mt][ks] = bitcast<bf16x8>(p[ks]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) w[mt][i] = w_row[32 * mt + 8 * (i >> 2) + 4 * hh + (i & 3)];
+    }
+  }
+
+  // Scores of keys [j0, j0 + 32) (keys beyond e_vis are computed on a clamped
+  // row and not stored).
+  __device__ __forceinline__ float tile(const bf16x8 (&b)[KS]) const {
+    float part = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) acc = mfma32_bf16(a[mt][ks], b[ks], acc);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) part += w[mt][i] * fmaxf(acc[i], 0.f);
+    }
+    const float tot = part + shfl_xor_f(part, 32);
+    return tot == 0.f ? 0.f : tot;
+  }
+
+  // Walk tiles [j_begin, j_end) of one row, writing scores of keys < e_vis.
+  __device__ __forceinline__ void run(const void* keys, int64_t key_base_row, int64_t j_begin,
+                                      int64_t j_end, int64_t e_vis, float* srow) const {
+    const int l = lane_id(), n = l & 31, hh = l >> 5;
+    auto row_elem = [&](int64_t j0) {
+      int64_t key = j0 + n;
+      key = key < e_vis ? key : e_vis - 1;
+      return (key_base_row + key) * DI + hh * (DI / 2);
+    };
+    if (j_begin >= j_end) return;
+    bf16x8 cur[KS], nxt[KS];
+    load_key_tile<KEY, DI>(keys, row_elem(j_begin), cur);
+    for (int64_t j0 = j_begin; j0 < j_end; j0 += 32) {
+      const bool more = j0 + 32 < j_end;
+      if (more) load_key_tile<KEY, DI>(keys, row_elem(j0 + 32), nxt);
+      const float s = tile(cur);
+      if (hh == 0 && j0 + n < e_vis) srow[j0 + n] = s;
+      if (more) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) cur[ks] = nxt[ks];
+      }
+    }
+  }
+};
+
+template <int KEY, int HI, int DI>
+__global__ __launch_bounds__(256) void index_score_decode(
+    const uint16_t* __restrict__ q, const float* __restrict__ w, const void* __restrict__ keys,
+    float* __restrict__ scores, int64_t stride, int64_t E_cap, int m, int W, const int32_t* __restrict__ pos,
+    int32_t pos_max, int64_t keys_per_block) {
+  const int r = blockIdx.y;
+  const RowRef rr = row_ref(SCKV_ROWS_DECODE, pos, pos_max, 0, 0, r);
+  const int64_t e_vis = visible(rr.t, m, W, E_cap);
+  const int64_t kpw = keys_per_block / 4;
+  const int64_t j_begin = (int64_t)blockIdx.x * keys_per_block + wave_id() * kpw;
+  if (j_begin >= e_vis) return;
+  int64_t j_end = j_begin + kpw;
+  j_end = j_end < e_vis ? j_end : e_vis;
+  ScoreWave<KEY, HI, DI> sw;
+  sw.load_query(q + (int64_t)r * HI * DI, w + (int64_t)r * HI);
+  sw.run(keys, rr.seq * E_cap, j_begin, j_end, e_vis, scores + (int64_t)r * stride);
+}
+
+template <int KEY, int HI, int DI>
+__global__ __launch_bounds__(256) void index_score_causal(
+    const uint16_t* __restrict__ q, const float* __restrict__ w, const void* __restrict__ keys,
+    float* __restrict__ scores, int64_t stride, int64_t E_cap, int m, int W, int32_t seq0, int32_t pos0,
+    int R) {
+  const int grp = gridDim.x - 1 - blockIdx.x;          // longest rows first
+  const int r = grp * 4 + wave_id();
+  if (r >= R) return;
+  const RowRef rr = row_ref(SCKV_ROWS_CAUSAL, nullptr, 0, seq0, pos0, r);
+  const int64_t e_vis = visible(rr.t, m, W, E_cap);
+  if (e_vis == 0) return;
+  ScoreWave<KEY, HI, DI> sw;
+  sw.load_query(q + (int64_t)r * HI * DI, w + (int64_t)r * HI);
+  sw.run(keys, rr.seq * E_cap, 0, e_vis, e_vis, scores + (int64_t)r * stride);
+}
+
+// fp32 path: one thread per key, query and weights staged in LDS.
+__global__ __launch_bounds__(256) void index_score_f32(
+    const float* __restrict__ q, const float* __restrict__ w, const float* __restrict__ keys,
+    float* __restrict__ scores, int64_t stride, int64_t E_cap, int m, int W, int HI, int DI, int kind,
+    const int32_t* __restrict__ pos, int32_t pos_max, int32_t seq0, int32_t pos0) {
+  extern __shared__ float sq[];                       // [HI*DI] query, then [HI] weights
+  const int r = blockIdx.y;
+  const RowRef rr = row_ref(kind, pos, pos_max, seq0, pos0, r);
+  const int64_t e_vis = visible(rr.t, m, W, E_cap);
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if ((int64_t)blockIdx.x * 256 >= e_vis) return;
+  for (int i = threadIdx.x; i < HI * DI; i += 256) sq[i] = q[(int64_t)r * HI * DI + i];
+  for (int i = threadIdx.x; i < HI; i += 256) sq[HI * DI + i] = w[(int64_t)r * HI + i];
+  __syncthreads();
+  if (j >= e_vis) return;
+  const float* kr = keys + (rr.seq * E_cap + j) * DI;
+  float s = 0.f;
+  for (int h = 0; h < HI; ++h) {
+    float d = 0.f;
+    for (int c = 0; c < DI; ++c) d = fmaf(sq[h * DI + c], kr[c], d);
+    s += sq[HI * DI + h] * fmaxf(d, 0.f);
+  }
+  scores[(int64_t)r * stride + j] = s == 0.f ? 0.f : s;
+}
+
+int64_t index_rows_cover(const sckv_index_args& a) {
+  const int64_t t = a.rows.kind == SCKV_ROWS_DECODE ? a.rows.pos_max : (int64_t)a.rows.pos0 + a.rows.R - 1;
+  const int64_t e = entries_visible(t, a.m, a.W);
+  return e < a.E_cap ? e : a.E_cap;
+}
+
+template <int KEY, int HI, int DI>
+static void launch_mfma(const sckv_index_args& a, float* scores, int64_t stride, int64_t cover,
+                        hipStream_t stream) {
+  const uint16_t* q = static_cast<const uint16_t*>(a.q);
+  if (a.rows.kind == SCKV_ROWS_DECODE) {
+    const int64_t kpb = 512;
+    const dim3 grid((unsigned)((cover + kpb - 1) / kpb), (unsigned)a.rows.R);
+    hipLaunchKernelGGL((index_score_decode<KEY, HI, DI>), grid, dim3(256), 0, stream, q, a.w, a.keys, scores,
+                       stride, a.E_cap, a.m, a.W, a.rows.pos, a.rows.pos_max, kpb);
+  } else {
+    const dim3 grid((unsigned)((a.rows.R + 3) / 4));
+    hipLaunchKernelGGL((index_score_causal<KEY, HI, DI>), grid, dim3(256), 0, stream, q, a.w, a.keys, scores,
+                       stride, a.E_cap, a.m, a.W, a.rows.seq0, a.rows.pos0, a.rows.R);
+  }
+}
+
+template <int KEY>
+static void launch_mfma_key(const sckv_index_args& a, float* scores, int64_t stride, int64_t cover,
+                            hipStream_t stream) {
+  if (a.H_I == 64 && a.D_I == 128) launch_mfma<KEY, 64, 128>(a, scores, stride, cover, stream);
+  else if (a.H_I == 64 && a.D_I == 64) launch_mfma<KEY, 64, 64>(a, scores, stride, cover, stream);
+  else if (a.H_I == 32 && a.D_I == 128) launch_mfma<KEY, 32, 128>(a, scores, stride, cover, stream);
+  else launch_mfma<KEY, 32, 64>(a, scores, stride, cover, stream);
+}
+
+hipError_t launch_index_score(const sckv_index_args& a, float* scores, int64_t stride, int64_t cover,
+                              hipStream_t stream) {
+  if (cover <= 0) return hipSuccess;
+  if (a.key_dtype == SCKV_F32) {
+    const dim3 grid((unsigned)((cover + 255) / 256), (unsigned)a.rows.R);
+    const size_t lds = (size_t)(a.H_I * a.D_I + a.H_I) * sizeof(float);
+    hipLaunchKernelGGL(index_score_f32, grid, dim3(256), lds, stream, static_cast<const float*>(a.q), a.w,
+                       static_cast<const float*>(a.keys), scores, stride, a.E_cap, a.m, a.W, a.H_I, a.D_I,
+                       a.rows.kind, a.rows.pos, a.rows.pos_max, a.rows.seq0, a.rows.pos0);
+  } else if (a.key_dtype == SCKV_BF16) {
+    launch_mfma_key<SCKV_BF16>(a, scores, stride, cover, stream);
+  } else {
+    launch_mfma_key<SCKV_E4M3>(a, scores, stride, cover, stream);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sckv

@@ -59,8 +59,14 @@ def assert_close(g, o, *, rtol=None, atol=None, what=""):
     return err
 
 
-def bf16_code_flips(gpu_vals, ora_raw, ora_rounded, mid_rtol=1e-5):
-    """Count bf16 code mismatches, and those not explained by a near-midpoint value."""
+def bf16_code_flips(gpu_vals, ora_raw, ora_rounded, mid_rtol=1e-5, magnitude=None):
+    """Count bf16 code mismatches, and those not explained by a near-midpoint value.
+
+    A mismatch is explained when the codes are one step apart and the oracle's
+    unrounded value lies within mid_rtol * magnitude of the midpoint between them;
+    `magnitude` is the scale of the rounding error of the value's computation
+    (for a weighted sum sum_i p_i v_i it is sum_i p_i |v_i|), default |value|.
+    """
     from oracle import codecs  # test infrastructure
     g = codecs.bf16_bits(gpu_vals).astype(np.int64)
     o = codecs.bf16_bits(ora_rounded).astype(np.int64)
@@ -68,10 +74,10 @@ def bf16_code_flips(gpu_vals, ora_raw, ora_rounded, mid_rtol=1e-5):
     if not bad.any():
         return 0, 0
     raw = np.asarray(ora_raw, np.float64)[bad]
-    # distance of the unrounded value to the nearest bf16 midpoint
-    _, e = np.frexp(raw)
-    ulp = np.ldexp(1.0, np.maximum(e, -125) - 8)
-    frac = raw / ulp - np.floor(raw / ulp)
-    near_mid = np.abs(frac - 0.5) * ulp <= mid_rtol * np.abs(raw)
+    mag = np.abs(raw) if magnitude is None else np.asarray(magnitude, np.float64)[bad]
+    gv = np.asarray(gpu_vals, np.float64)[bad]
+    ov = np.asarray(ora_rounded, np.float64)[bad]
+    mid = (gv + ov) / 2
+    near_mid = np.abs(raw - mid) <= mid_rtol * mag
     one_step = np.abs(g[bad] - o[bad]) == 1
     return int(bad.sum()), int((~(near_mid & one_step)).sum())

@@ -1,0 +1,146 @@
+"""The C ABI without a GPU: the library loads, exports every declared call, and
+rejects bad arguments on the host before any HIP call."""
+import ctypes as C
+import os
+import re
+
+import pytest
+import torch
+
+import sequence_compressed_kv_amd as sk
+from sequence_compressed_kv_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pytestmark = pytest.mark.skipif(torch.cuda.is_available(),
+                                reason="host-only checks pass fake device pointers; run where no GPU is visible")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(sk.lib_path()):
+        pytest.fail("libsckv.so is not built (run __graft_entry__.build())")
+    return sk.load()
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "sckv.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:sckv_status|size_t|const char\*|int32_t)\s+(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(L):
+    decl = declared_functions()
+    assert set(decl) == set(_lib.EXPORTS), decl
+    for name in decl:
+        assert hasattr(L, name), name
+    assert L.sckv_abi_version() == 1
+
+
+FAKE = 0x10000          # 16-byte aligned, never dereferenced: validation fails first
+FAKE_ODD = 0x10004
+
+
+def pool(**kw):
+    d = dict(val=FAKE, gate=FAKE, bpos=FAKE, out=FAKE, out_scale=None, E_cap=16, D=64, in_dtype=1, out_dtype=1,
+             reserved=0)
+    d.update(kw)
+    return _lib.PoolStream(**d)
+
+
+def err(L):
+    return L.sckv_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(val=None), 1), (dict(out=None), 1), (dict(in_dtype=2), 3), (dict(out_dtype=7), 3),
+    (dict(D=48), 4), (dict(D=1024), 4), (dict(E_cap=3), 2), (dict(val=FAKE_ODD), 5),
+])
+def test_compress_validation(L, kw, status):
+    p = pool(**kw)
+    s = L.csa_compress(1, 64, 4, 4, 0, 16, C.byref(p), None, None)
+    assert s == status, err(L)
+    assert err(L)
+
+
+def test_compress_token_range(L):
+    p = pool()
+    assert L.csa_compress(1, 63, 4, 4, 0, 16, C.byref(p), None, None) == 2     # entry 15 needs 64 tokens
+    assert L.hca_compress(0, 64, 4, 0, 0, 1, C.byref(p), None) == 2             # B = 0
+    assert L.hca_compress(1, 64, 0, 0, 0, 1, C.byref(p), None) == 2             # m = 0
+    assert L.csa_compress(1, 64, 4, -1, 0, 1, C.byref(p), None, None) == 2      # o < 0
+    assert L.csa_compress(1, 64, 4, 4, -1, 1, C.byref(p), None, None) == 2
+    bad = pool(bpos=None)
+    assert L.csa_compress(1, 64, 4, 4, 0, 16, C.byref(p), C.byref(bad), None) == 1
+    assert L.csa_compress(1, 64, 4, 4, 0, 16, None, None, None) == 1
+
+
+def idx_args(**kw):
+    rows = kw.pop("rows", _lib.Rows(FAKE, 0, 2, 4095, 0, 0, 0))
+    d = dict(rows=rows, q=FAKE, w=FAKE, keys=FAKE, out_idx=FAKE, out_score=None, E_cap=1024, B=2, H_I=64, D_I=128,
+             q_dtype=1, key_dtype=1, m=4, W=128, k=64)
+    d.update(kw)
+    return _lib.IndexArgs(**d)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(out_idx=None), 1), (dict(k=0), 2), (dict(m=0), 2), (dict(E_cap=0), 2),
+    (dict(q_dtype=0), 3), (dict(key_dtype=0), 3), (dict(H_I=48), 4), (dict(D_I=96), 4),
+    (dict(q_dtype=0, key_dtype=0, H_I=128, D_I=128), 4), (dict(keys=FAKE_ODD), 5),
+    (dict(rows=_lib.Rows(None, 0, 2, 4095, 0, 0, 0)), 1), (dict(rows=_lib.Rows(FAKE, 0, 3, 4095, 0, 0, 0)), 2),
+    (dict(rows=_lib.Rows(None, 1, 8, 0, 2, 0, 0)), 2), (dict(rows=_lib.Rows(None, 5, 8, 0, 0, 0, 0)), 2),
+])
+def test_index_validation(L, kw, status):
+    a = idx_args(**kw)
+    assert L.csa_index_topk(C.byref(a), FAKE, 1 << 30, None) == status, err(L)
+    if "out_idx" not in kw:                  # the size query does not need the output pointer
+        assert L.csa_index_topk_workspace_size(C.byref(a)) == 0
+
+
+def test_index_workspace(L):
+    a = idx_args()
+    n = L.csa_index_topk_workspace_size(C.byref(a))
+    # scores of 2 rows x 991 visible entries (padded to 1024 floats)
+    assert n >= 2 * 991 * 4
+    assert L.csa_index_topk(C.byref(a), FAKE, n - 1, None) == 6
+    assert L.csa_index_topk(C.byref(a), None, n, None) == 6
+    assert L.csa_index_score(C.byref(a), None, 1024, None) == 1
+    assert L.csa_index_score(C.byref(a), FAKE, 990, None) == 2          # stride below the visible count
+
+
+def test_topk_plan_limits(L):
+    # decode at t = 2^22: 1,048,544 visible entries and k = 4096 exceed the two-stage plan
+    a = idx_args(rows=_lib.Rows(FAKE, 0, 1, 1 << 22, 0, 0, 0), E_cap=1 << 20, k=4096)
+    assert L.csa_index_topk_workspace_size(C.byref(a)) == 0
+    assert L.csa_index_topk(C.byref(a), FAKE, 1 << 40, None) == 4
+
+
+def att_args(**kw):
+    rows = kw.pop("rows", _lib.Rows(FAKE, 0, 4, 131071, 0, 0, 0))
+    d = dict(rows=rows, q=FAKE, entries=FAKE, entry_scale=None, idx=FAKE, win=FAKE, out=FAKE, lse=None,
+             E_cap=32768, R_w=128, B=4, H=64, D=512, q_dtype=1, entry_dtype=1, win_dtype=1, out_dtype=0, m=4,
+             W=128, k=1024, softmax_scale=0.088, reserved=0)
+    d.update(kw)
+    return _lib.AttendArgs(**d)
+
+
+@pytest.mark.parametrize("fn", ["csa_attend", "hca_attend"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(win=None), 1), (dict(entry_dtype=2), 1), (dict(R_w=127), 2), (dict(W=0), 2),
+    (dict(H=40), 4), (dict(D=96), 4), (dict(H=256), 4), (dict(q_dtype=0), 3), (dict(win_dtype=2), 3),
+    (dict(out_dtype=2), 3), (dict(softmax_scale=float("nan")), 2), (dict(out=FAKE_ODD), 5),
+    (dict(q_dtype=0, entry_dtype=0, win_dtype=0, H=64, D=128), 4),
+])
+def test_attend_validation(L, fn, kw, status):
+    a = att_args(**kw)
+    assert getattr(L, fn)(C.byref(a), FAKE, 1 << 30, None) == status, err(L)
+
+
+def test_attend_csa_needs_idx_and_workspace(L):
+    a = att_args(idx=None)
+    assert L.csa_attend(C.byref(a), FAKE, 1 << 30, None) == 1
+    a = att_args()
+    n = L.csa_attend_workspace_size(C.byref(a))
+    assert n > 0                                                          # split partials for 4 rows
+    assert L.csa_attend(C.byref(a), FAKE, n - 1, None) == 6
+    assert L.hca_attend_workspace_size(C.byref(att_args(rows=_lib.Rows(None, 1, 32768, 0, 0, 0, 0), B=1))) == 0

@@ -1,0 +1,296 @@
+"""GPU parity of each HIP call against the oracle on the same seeded inputs.
+
+Sizes span several tiles/blocks and ragged tails; rows cover the edge cases of
+the visibility rule (no visible entry, one entry, short windows at t < W)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import codecs, method
+from tests.compare import assert_close, bf16_code_flips, topk_parity
+from tests.gpu_util import DEV, dev, dev_codes, dev_i32, host, rng_store
+
+pytestmark = pytest.mark.gpu
+
+sk = pytest.importorskip("sequence_compressed_kv_amd")
+
+
+def setup_module(module):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sk.load()
+
+
+# ---------------------------------------------------------------- compression
+def e4m3_flips(gpu_codes, ora_codes, ora_unrounded, magnitude, mid_rtol=1e-5):
+    """Mismatched e4m3 codes not explained by an unrounded value next to a midpoint
+    (within mid_rtol of `magnitude`, the scale of the value's rounding error)."""
+    bad = gpu_codes != ora_codes
+    if not bad.any():
+        return 0, 0
+    g = codecs.e4m3_decode(gpu_codes[bad])
+    o = codecs.e4m3_decode(ora_codes[bad])
+    y = np.asarray(ora_unrounded, np.float64)[bad]
+    mid = (g + o) / 2
+    near = np.abs(y - mid) <= mid_rtol * np.asarray(magnitude, np.float64)[bad]
+    one_step = np.abs(gpu_codes[bad].astype(int) - ora_codes[bad].astype(int)) == 1
+    return int(bad.sum()), int((~(near & one_step)).sum())
+
+
+COMPRESS_CASES = [
+    # m, o, D, in, out, scaled, B, N
+    (4, 4, 64, "f32", "f32", False, 1, 4096),
+    (4, 4, 32, "f32", "f32", False, 1, 4096),
+    (128, 0, 128, "bf16", "bf16", False, 2, 8192),
+    (4, 4, 512, "bf16", "bf16", False, 1, 2048),
+    (4, 4, 512, "bf16", "e4m3", True, 1, 2048),
+    (4, 4, 128, "bf16", "e4m3", False, 2, 1024),
+    (128, 0, 512, "bf16", "e4m3", True, 1, 16384),
+    (4, 4, 8, "bf16", "bf16", False, 3, 203),
+    (2, 6, 16, "f32", "bf16", False, 2, 101),
+]
+
+
+@pytest.mark.parametrize("m,o,D,ins,outs,scaled,B,N", COMPRESS_CASES)
+def test_compress_parity(m, o, D, ins, outs, scaled, B, N):
+    print(f"compress m={m} o={o} D={D} {ins}->{outs} scaled={scaled} B={B} N={N}", flush=True)
+    rng = np.random.default_rng(100 + D + m)
+    v = rng_store(rng, (B, N, D), ins)
+    g = rng_store(rng, (B, N, D), ins, 2.0)
+    bpos = rng.normal(0, 0.5, (m + o, D)).astype(np.float32)
+    E = N // m
+    odt = {"f32": torch.float32, "bf16": torch.bfloat16, "e4m3": torch.float8_e4m3fn}[outs]
+    out = torch.zeros(B, E, D, device=DEV, dtype=odt if outs != "e4m3" else torch.uint8)
+    if outs == "e4m3":
+        out = out.view(torch.float8_e4m3fn)
+    osc = torch.zeros(B, E, device=DEV, dtype=torch.float32) if scaled else None
+    pool = sk.Pool(dev(v, ins), dev(g, ins), dev(bpos), out, osc)
+    if m == 128:
+        sk.hca_compress(pool, m=m, o=o)
+    else:
+        sk.csa_compress(pool, m=m, o=o)
+    torch.cuda.synchronize()
+    for b in range(B):
+        c = method.compress(v[b], g[b], bpos, m, o)
+        # same softmax weights on |v|: the scale of the fp32 rounding error of each pooled sum
+        mag = method.compress(np.abs(v[b]), g[b], bpos, m, o)
+        if outs == "f32":
+            assert_close(host(out[b]), c, rtol=1e-5, what="f32 entries")
+        elif outs == "bf16":
+            st = method.store_entries(c, "bf16")
+            n_bad, n_unexplained = bf16_code_flips(host(out[b]), c, st["values"], magnitude=mag)
+            assert n_unexplained == 0, f"{n_unexplained} of {n_bad} bf16 codes differ"
+        else:
+            st = method.store_entries(c, "e4m3") if scaled else method.store_keys(c, "e4m3")
+            gc = host(out[b])
+            if scaled:
+                gs = osc[b].cpu().numpy().astype(np.float64)
+                np.testing.assert_allclose(gs, st["scale"], rtol=2e-6)
+                y, ymag = c / st["scale"][:, None], mag / st["scale"][:, None]
+            else:
+                y, ymag = c, mag
+            n_bad, n_unexplained = e4m3_flips(gc, st["codes"], y, ymag)
+            assert n_unexplained == 0, f"{n_unexplained} of {n_bad} e4m3 codes differ"
+
+
+def test_compress_appends_only_requested_entries():
+    rng = np.random.default_rng(5)
+    B, N, D = 2, 256, 64
+    v, g = rng_store(rng, (B, N, D), "bf16"), rng_store(rng, (B, N, D), "bf16")
+    bpos = rng.normal(0, 0.5, (8, D)).astype(np.float32)
+    out = torch.full((B, 64, D), 7.0, device=DEV, dtype=torch.bfloat16)
+    sk.csa_compress(sk.Pool(dev(v, "bf16"), dev(g, "bf16"), dev(bpos), out), m=4, o=4, e_begin=5, e_count=9)
+    torch.cuda.synchronize()
+    o = host(out)
+    assert np.all(o[:, :5] == 7.0) and np.all(o[:, 14:] == 7.0)
+    for b in range(B):
+        c = method.compress(v[b], g[b], bpos, 4, 4)[5:14]
+        mag = method.compress(np.abs(v[b]), g[b], bpos, 4, 4)[5:14]
+        n_bad, n_un = bf16_code_flips(o[b, 5:14], c, method.store_entries(c, "bf16")["values"], magnitude=mag)
+        assert n_un == 0
+
+
+# ---------------------------------------------------------------- indexer + top-k (decode rows)
+INDEX_CASES = [
+    # keys, H_I, D_I, E_cap, positions, k
+    ("f32", 4, 32, 1024, [4095], 64),
+    ("bf16", 64, 128, 4096, [16511, 5000, 131, 127, 132, 600], 256),
+    ("e4m3", 64, 128, 4096, [16511, 9000], 1024),
+    ("bf16", 32, 64, 2000, [8127, 4000], 100),
+    ("bf16", 64, 128, 40000, [160127], 1024),
+    ("bf16", 64, 128, 70000, [279999, 200000], 2048),
+    ("e4m3", 64, 128, 70000, [279999], 100),
+]
+
+
+def _index_inputs(rng, keys_s, HI, DI, B, E_cap):
+    qs = "f32" if keys_s == "f32" else "bf16"
+    q = rng_store(rng, (B, HI, DI), qs)
+    w = rng.normal(0, 1, (B, HI)).astype(np.float32)
+    if keys_s == "e4m3":
+        kv = codecs.round_e4m3(rng.normal(0, 1, (B, E_cap, DI)))
+        keys_dev = dev_codes(codecs.e4m3_encode(kv))
+    else:
+        kv = rng_store(rng, (B, E_cap, DI), keys_s)
+        keys_dev = dev(kv, keys_s)
+    return q, w, kv.astype(np.float64), dev(q, qs), dev(w), keys_dev
+
+
+@pytest.mark.parametrize("keys_s,HI,DI,E_cap,positions,k", INDEX_CASES)
+def test_index_topk_decode(keys_s, HI, DI, E_cap, positions, k):
+    print(f"index decode {keys_s} H_I={HI} D_I={DI} E_cap={E_cap} pos={positions} k={k}", flush=True)
+    rng = np.random.default_rng(E_cap + k)
+    B = len(positions)
+    q, w, kv, qd, wd, keysd = _index_inputs(rng, keys_s, HI, DI, B, E_cap)
+    pos = dev_i32(positions)
+    rows = sk.RowSpec.decode(pos, max(positions))
+    out_idx = torch.full((B, k), -7, device=DEV, dtype=torch.int32)
+    out_score = torch.zeros(B, k, device=DEV, dtype=torch.float32)
+    cover = min(method.entries_visible(max(positions), 4, 128), E_cap)
+    scores = torch.full((B, max(cover, 1)), float("nan"), device=DEV, dtype=torch.float32)
+    sk.csa_index_score(rows, qd, wd, keysd, scores, m=4, W=128, k=k)
+    sk.csa_index_topk(rows, qd, wd, keysd, out_idx, m=4, W=128, k=k, out_score=out_score)
+    torch.cuda.synchronize()
+    gi, gsc, gs = host(out_idx), host(out_score), host(scores)
+    for r, t in enumerate(positions):
+        ev = min(method.entries_visible(t, 4, 128), E_cap)
+        s = method.index_scores(q[r], w[r], kv[r, :ev])
+        if ev:
+            assert_close(gs[r, :ev], s, rtol=2e-6, what=f"scores row {r}")
+        ok, msg = topk_parity(gi[r], method.topk(s, k), s)
+        assert ok, f"row {r} (t={t}, E_vis={ev}): {msg}"
+        sel = gi[r][gi[r] >= 0]
+        np.testing.assert_array_equal(gsc[r, :len(sel)], gs[r, sel])
+        assert np.all(np.isneginf(gsc[r, len(sel):]))
+
+
+CAUSAL_CASES = [
+    ("bf16", 64, 128, 800, 3300, 64),
+    ("f32", 4, 32, 300, 1300, 16),
+    ("e4m3", 64, 128, 600, 2500, 128),
+]
+
+
+@pytest.mark.parametrize("keys_s,HI,DI,E_cap,T,k", CAUSAL_CASES)
+def test_index_topk_causal(keys_s, HI, DI, E_cap, T, k):
+    print(f"index causal {keys_s} H_I={HI} D_I={DI} E_cap={E_cap} T={T} k={k}", flush=True)
+    rng = np.random.default_rng(T + k)
+    qs = "f32" if keys_s == "f32" else "bf16"
+    q = rng_store(rng, (T, HI, DI), qs)
+    w = rng.normal(0, 1, (T, HI)).astype(np.float32)
+    _, _, kv, _, _, keysd = _index_inputs(rng, keys_s, HI, DI, 1, E_cap)
+    rows = sk.RowSpec.causal(T)
+    out_idx = torch.full((T, k), -7, device=DEV, dtype=torch.int32)
+    sk.csa_index_topk(rows, dev(q, qs), dev(w), keysd, out_idx, m=4, W=128, k=k)
+    torch.cuda.synchronize()
+    gi = host(out_idx)
+    for t in range(T):
+        ev = min(method.entries_visible(t, 4, 128), E_cap)
+        s = method.index_scores(q[t], w[t], kv[0, :ev])
+        ok, msg = topk_parity(gi[t], method.topk(s, k), s)
+        assert ok, f"row {t} (E_vis={ev}): {msg}"
+
+
+# ---------------------------------------------------------------- attention
+ATTEND_CASES = [
+    # csa, entries, H, D, E_cap, positions, k, out
+    (True, "bf16", 64, 512, 4096, [16511, 300, 50], 1024, "f32"),
+    (False, "bf16", 32, 128, 512, [65535, 20000, 130, 0], 0, "f32"),
+    (False, "bf16", 64, 512, 1024, [131071, 131070], 0, "f32"),
+    (True, "e4m3", 64, 512, 4096, [16511, 9000], 2048, "bf16"),
+    (False, "e4m3", 64, 512, 8192, [1048575], 0, "bf16"),
+    (True, "f32", 8, 64, 1024, [4095, 600, 10], 64, "f32"),
+    (False, "f32", 8, 64, 1024, [4095], 0, "f32"),
+    (True, "bf16", 16, 256, 1000, [4127, 2000], 200, "bf16"),
+]
+
+
+@pytest.mark.parametrize("csa,ent,H,D,E_cap,positions,k,outs", ATTEND_CASES)
+def test_attend_decode(csa, ent, H, D, E_cap, positions, k, outs):
+    print(f"attend decode csa={csa} {ent} H={H} D={D} E_cap={E_cap} pos={positions} k={k} out={outs}", flush=True)
+    rng = np.random.default_rng(H * D + E_cap)
+    B = len(positions)
+    qs = "f32" if ent == "f32" else "bf16"
+    q = rng_store(rng, (B, H, D), qs, 0.3)
+    if ent == "e4m3":
+        st = method.store_entries(rng.normal(0, 1, (B * E_cap, D)), "e4m3")
+        ev_vals = st["values"].reshape(B, E_cap, D)
+        ent_dev = dev_codes(st["codes"].reshape(B, E_cap, D))
+        esc = dev(st["scale"].reshape(B, E_cap))
+    else:
+        ev_vals = rng_store(rng, (B, E_cap, D), ent).astype(np.float64)
+        ent_dev, esc = dev(ev_vals, ent), None
+    R_w = 128
+    win_vals = {}
+    rings = np.zeros((B, R_w, D), np.float32)
+    for b, t in enumerate(positions):
+        wp = method.window_positions(t, 128)          # only the window tokens are ever read
+        win_vals[b] = rng_store(rng, (len(wp), D), qs)
+        rings[b][wp % R_w] = win_vals[b]
+    idx = None
+    idx_np = None
+    if csa:
+        idx_np = np.full((B, k), -1, np.int64)
+        for b, t in enumerate(positions):
+            ev = min(method.entries_visible(t, 4, 128), E_cap)
+            sel = np.sort(rng.choice(ev, size=min(k, ev), replace=False)) if ev else np.zeros(0, np.int64)
+            idx_np[b, :len(sel)] = sel
+        idx = dev_i32(idx_np)
+    odt = torch.float32 if outs == "f32" else torch.bfloat16
+    out = torch.zeros(B, H, D, device=DEV, dtype=odt)
+    lse = torch.zeros(B, H, device=DEV, dtype=torch.float32)
+    rows = sk.RowSpec.decode(dev_i32(positions), max(positions))
+    m = 4 if csa else 128
+    tau = 1.0 / math.sqrt(128 if D >= 128 else D)
+    args = dict(m=m, W=128, softmax_scale=tau, entry_scale=esc, lse=lse)
+    if csa:
+        sk.csa_attend(rows, dev(q, qs), ent_dev, idx, dev(rings, qs), out, **args)
+    else:
+        sk.hca_attend(rows, dev(q, qs), ent_dev, dev(rings, qs), out, **args)
+    torch.cuda.synchronize()
+    go, gl = host(out), host(lse)
+    for b, t in enumerate(positions):
+        if csa:
+            sel = idx_np[b][idx_np[b] >= 0]
+            items = np.concatenate([ev_vals[b][sel], win_vals[b]])
+        else:
+            ev = min(method.entries_visible(t, 128, 128), E_cap)
+            items = np.concatenate([ev_vals[b][:ev], win_vals[b]])
+        o, lse_o, _ = method.attend(q[b], items, tau)
+        if ent == "f32":
+            assert_close(go[b], o, rtol=1e-4, what=f"f32 out row {b}")
+        else:
+            err = assert_close(go[b], o, atol=2e-2, what=f"out row {b}")
+            print(f"  row {b}: max abs err {err:.2e} (max |o| {np.abs(o).max():.2f})")
+        np.testing.assert_allclose(gl[b], lse_o, rtol=1e-5, atol=1e-5)
+
+
+def test_attend_causal_rows_and_determinism():
+    """Prefill-style rows (every position a query) over a whole stream window."""
+    rng = np.random.default_rng(9)
+    T, H, D, E_cap, k = 600, 64, 512, 150, 32
+    q = rng_store(rng, (T, H, D), "bf16", 0.3)
+    ent = rng_store(rng, (1, E_cap, D), "bf16").astype(np.float64)
+    v = rng_store(rng, (1, T, D), "bf16")
+    idx_np = np.full((T, k), -1, np.int64)
+    for t in range(T):
+        ev = min(method.entries_visible(t, 4, 128), E_cap)
+        sel = np.sort(rng.choice(ev, size=min(k, ev), replace=False)) if ev else np.zeros(0, np.int64)
+        idx_np[t, :len(sel)] = sel
+    rows = sk.RowSpec.causal(T)
+    outs = []
+    for _ in range(2):
+        out = torch.zeros(T, H, D, device=DEV, dtype=torch.float32)
+        sk.csa_attend(rows, dev(q, "bf16"), dev(ent, "bf16"), dev_i32(idx_np), dev(v, "bf16"), out, m=4, W=128,
+                      softmax_scale=1 / math.sqrt(128))
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    go = host(outs[0])
+    for t in list(range(0, 140)) + list(range(140, T, 37)) + [T - 1]:
+        sel = idx_np[t][idx_np[t] >= 0]
+        items = np.concatenate([ent[0][sel], v[0][method.window_positions(t, 128)]])
+        o, _, _ = method.attend(q[t], items, 1 / math.sqrt(128))
+        assert_close(go[t], o, atol=2e-2, what=f"row {t}")

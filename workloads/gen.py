@@ -182,34 +182,43 @@ def decode_inputs(wl: Workload, b: int, x: Optional[np.ndarray] = None) -> Dict:
 
 
 # ---------------------------------------------------------------- GPU-side synthesis (same recipe, torch RNG)
-def gpu_streams(wl: Workload, li: int, b: int, device, chunk: int = 65536):
-    """Streams of layer li for sequence b drawn on the GPU with torch's RNG.
-
-    Same distributions as the host recipe (x ~ N(0,1), weights ~ N(0, 1/fan_in),
-    fp32 projections rounded to storage) but other random numbers: used only to
-    fill caches whose outputs are timed, never compared with the oracle.
-    Returns v, g (and vI, gI) as torch tensors [N][D] in storage dtype plus bpos.
-    """
-    L = wl.layers[li]
+def gpu_weights(wl: Workload, device, seed_offset: int = 0):
+    """Per-layer projection weights drawn on the GPU with torch's RNG (fp32)."""
     g = torch.Generator(device=device)
-    g.manual_seed(wl.seed * 1000003 + li * 7919 + b)
+    g.manual_seed(wl.seed * 1000003 + 7919 + seed_offset)
     dm = wl.d_model
+    out = []
+    for L in wl.layers:
+        names = [("v", L.D), ("g", L.D)] + ([("vI", L.D_I), ("gI", L.D_I)] if L.kind == "csa" else [])
+        w = {n: torch.randn(r, dm, device=device, generator=g) * (1.0 / math.sqrt(dm)) for n, r in names}
+        w["bpos"] = torch.randn(L.m + L.o, L.D, device=device, generator=g) * (1.0 / math.sqrt(dm))
+        if L.kind == "csa":
+            w["bposI"] = torch.randn(L.m + L.o, L.D_I, device=device, generator=g) * (1.0 / math.sqrt(dm))
+        out.append(w)
+    return out
+
+
+def gpu_sequence_streams(wl: Workload, b: int, weights, device, chunk: int = 32768):
+    """Streams of every layer for sequence b, from one hidden-state stream drawn on
+    the GPU with torch's RNG (x ~ N(0,1); fp32 projections rounded to storage).
+
+    Same distributions as the host recipe, other random numbers: used to fill
+    caches whose decode steps are timed, never compared with the oracle.
+    Returns a list (per layer) of dicts of torch tensors [N][D] in storage dtype.
+    """
+    g = torch.Generator(device=device)
+    g.manual_seed(wl.seed * 1000003 + 104729 * (b + 1))
     dt = torch_dtype(wl.store)
-
-    def W(rows, fan):
-        return torch.randn(rows, dm, device=device, generator=g) * (1.0 / math.sqrt(fan))
-
-    names = [("v", L.D), ("g", L.D)] + ([("vI", L.D_I), ("gI", L.D_I)] if L.kind == "csa" else [])
-    Ws = {n: W(r, dm) for n, r in names}
-    out = {n: torch.empty(wl.N, r, device=device, dtype=dt) for n, r in names}
+    out = []
+    for L, w in zip(wl.layers, weights):
+        names = ["v", "g"] + (["vI", "gI"] if L.kind == "csa" else [])
+        out.append({n: torch.empty(wl.N, w[n].shape[0], device=device, dtype=dt) for n in names})
     for a in range(0, wl.N, chunk):
         e = min(wl.N, a + chunk)
-        x = torch.randn(e - a, dm, device=device, generator=g)
-        for n, _ in names:
-            out[n][a:e] = (x @ Ws[n].T).to(dt)
-    out["bpos"] = torch.randn(L.m + L.o, L.D, device=device, generator=g) * (1.0 / math.sqrt(dm))
-    if L.kind == "csa":
-        out["bposI"] = torch.randn(L.m + L.o, L.D_I, device=device, generator=g) * (1.0 / math.sqrt(dm))
+        x = torch.randn(e - a, wl.d_model, device=device, generator=g)
+        for st, w in zip(out, weights):
+            for n in st:
+                st[n][a:e] = (x @ w[n].T).to(dt)
     return out
 
 
