@@ -86,11 +86,21 @@ typedef struct {
   int32_t reserved;
 } sckv_rows;
 
+/* ------------------------------------------------------------------ layouts
+ * Entry caches (pooled KV entries, raw window) are row-major: [B][E_cap][D].
+ * Indexer key caches use a tiled layout built for the MFMA scoring kernel, so
+ * that one load instruction of a wavefront reads two contiguous runs of
+ * 32 x 8 elements:  [B][E_cap / 32][D_I / 8][32][8], i.e. entry j, dim d of a
+ * sequence sits at element ((j / 32 * (D_I / 8) + d / 8) * 32 + j % 32) * 8 + d % 8.
+ * E_cap of a key cache must be a multiple of 32. */
+typedef enum { SCKV_LAYOUT_ROWS = 0, SCKV_LAYOUT_KEY_TILES = 1 } sckv_layout;
+
 /* ------------------------------------------------------------------ compression
  * One per-token stream pair pooled into entries (the compressor above).
  *   val, gate : [B][N][D] values v_i and gate logits g_i (in_dtype F32 or BF16)
  *   bpos      : [m+o][D] fp32 position bias
- *   out       : [B][E_cap][D] entries (out_dtype F32, BF16 or E4M3)
+ *   out       : entries (out_dtype F32, BF16 or E4M3) in out_layout:
+ *               SCKV_LAYOUT_ROWS [B][E_cap][D] or SCKV_LAYOUT_KEY_TILES (see above)
  *   out_scale : E4M3 only.  Non-NULL: [B][E_cap] fp32 per-entry scale, written as
  *               fp32(max_d |c_j[d]| / 448) (1 for an all-zero entry), codes are
  *               E4M3(c / scale).  NULL: unscaled E4M3(c) (indexer keys). */
@@ -104,7 +114,7 @@ typedef struct {
   int32_t D;
   int32_t in_dtype;
   int32_t out_dtype;
-  int32_t reserved;
+  int32_t out_layout; /* sckv_layout */
 } sckv_pool_stream;
 
 /* csa_compress: pools entries e_begin .. e_begin + e_count - 1 of every sequence
@@ -113,7 +123,8 @@ typedef struct {
  * e_begin + e_count <= E_cap.  `kv` is the shared latent stream; `index_keys`
  * (may be NULL) is the lightning indexer's own stream, pooled over the same
  * windows (knightli.com article, CSA section: the indexer scores the pooled
- * blocks).  CSA uses m = 4, o = 4; the call accepts any m >= 1, 0 <= o. */
+ * blocks); give it out_layout SCKV_LAYOUT_KEY_TILES to feed csa_index_topk.
+ * CSA uses m = 4, o = 4; the call accepts any m >= 1, 0 <= o. */
 sckv_status csa_compress(int32_t B, int64_t N, int32_t m, int32_t o, int64_t e_begin,
                          int64_t e_count, const sckv_pool_stream* kv,
                          const sckv_pool_stream* index_keys, void* stream);
@@ -126,7 +137,8 @@ sckv_status hca_compress(int32_t B, int64_t N, int32_t m, int32_t o, int64_t e_b
 /* ------------------------------------------------------------------ lightning indexer + top-k
  *   q         : [R][H_I][D_I] indexer queries (q_dtype F32 or BF16)
  *   w         : [R][H_I] fp32 head weights w_h
- *   keys      : [B][E_cap][D_I] indexer keys (key_dtype F32, BF16 or unscaled E4M3)
+ *   keys      : indexer keys in SCKV_LAYOUT_KEY_TILES [B][E_cap/32][D_I/8][32][8]
+ *               (key_dtype F32, BF16 or unscaled E4M3; E_cap a multiple of 32)
  *   out_idx   : [R][k] int32: the kept entries of each row in ascending order,
  *               then -1 padding (k' = min(k, E_vis) entries are kept; E_vis = 0
  *               gives an all -1 row)

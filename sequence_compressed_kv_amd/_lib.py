@@ -15,6 +15,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsckv.so
 
 F32, BF16, E4M3 = 0, 1, 2
 ROWS_DECODE, ROWS_CAUSAL = 0, 1
+LAYOUT_ROWS, LAYOUT_KEY_TILES = 0, 1
 
 STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_DTYPE", 4: "ERR_UNSUPPORTED", 5: "ERR_ALIGN",
           6: "ERR_WORKSPACE", 7: "ERR_HIP"}
@@ -35,7 +36,7 @@ class Rows(C.Structure):
 class PoolStream(C.Structure):
     _fields_ = [("val", C.c_void_p), ("gate", C.c_void_p), ("bpos", C.c_void_p), ("out", C.c_void_p),
                 ("out_scale", C.c_void_p), ("E_cap", C.c_int64), ("D", C.c_int32), ("in_dtype", C.c_int32),
-                ("out_dtype", C.c_int32), ("reserved", C.c_int32)]
+                ("out_dtype", C.c_int32), ("out_layout", C.c_int32)]
 
 
 class IndexArgs(C.Structure):
@@ -152,17 +153,51 @@ class RowSpec:
 @dataclass
 class Pool:
     """One stream pair to pool: val, gate [B][N][D]; bpos [m+o][D] fp32;
-    out [B][E_cap][D]; out_scale [B][E_cap] fp32 (scaled e4m3 output) or None."""
+    out [B][E_cap][D] (rows) or a key-tile cache made by key_tiles_empty();
+    out_scale [B][E_cap] fp32 (scaled e4m3 output) or None."""
     val: torch.Tensor
     gate: torch.Tensor
     bpos: torch.Tensor
     out: torch.Tensor
     out_scale: Optional[torch.Tensor] = None
+    layout: int = LAYOUT_ROWS
 
     def c(self) -> PoolStream:
+        D = int(self.val.shape[2])
+        E_cap = int(self.out.shape[1]) if self.layout == LAYOUT_ROWS else int(self.out.shape[1]) * 32
         return PoolStream(_ptr(self.val), _ptr(self.gate), _ptr(self.bpos), _ptr(self.out), _ptr(self.out_scale),
-                          int(self.out.shape[1]), int(self.val.shape[2]), dtype_code(self.val),
-                          dtype_code(self.out), 0)
+                          E_cap, D, dtype_code(self.val), dtype_code(self.out), self.layout)
+
+
+# ---------------------------------------------------------------- indexer key tiles
+def key_tiles_empty(B: int, E_cap: int, D_I: int, dtype, device) -> torch.Tensor:
+    """An indexer key cache in the tiled layout [B][E_cap/32][D_I/8][32][8]."""
+    if E_cap % 32 or D_I % 8:
+        raise ValueError("key tiles need E_cap % 32 == 0 and D_I % 8 == 0")
+    return torch.empty(B, E_cap // 32, D_I // 8, 32, 8, dtype=dtype, device=device)
+
+
+def to_key_tiles(keys: torch.Tensor) -> torch.Tensor:
+    """[B][E][D_I] row-major keys -> tiled layout (E padded to a multiple of 32)."""
+    f8 = keys.dtype == torch.float8_e4m3fn
+    if f8:
+        keys = keys.view(torch.uint8)
+    B, E, D = keys.shape
+    Ep = (E + 31) // 32 * 32
+    if Ep != E:
+        keys = torch.cat([keys, keys.new_zeros(B, Ep - E, D)], dim=1)
+    t = keys.reshape(B, Ep // 32, 32, D // 8, 8).permute(0, 1, 3, 2, 4).contiguous()
+    return t.view(torch.float8_e4m3fn) if f8 else t
+
+
+def from_key_tiles(tiles: torch.Tensor) -> torch.Tensor:
+    """Tiled keys -> [B][E_cap][D_I] row-major."""
+    f8 = tiles.dtype == torch.float8_e4m3fn
+    if f8:
+        tiles = tiles.view(torch.uint8)
+    B, T, DB, _, _ = tiles.shape
+    r = tiles.permute(0, 1, 3, 2, 4).reshape(B, T * 32, DB * 8)
+    return r.view(torch.float8_e4m3fn) if f8 else r
 
 
 # ---------------------------------------------------------------- calls
@@ -185,8 +220,12 @@ def hca_compress(kv: Pool, *, m: int = 128, o: int = 0, e_begin: int = 0, e_coun
 
 
 def index_args(rows: RowSpec, q, w, keys, out_idx, *, m: int, W: int, k: int, out_score=None) -> IndexArgs:
-    return IndexArgs(rows.c(), _ptr(q), _ptr(w), _ptr(keys), _ptr(out_idx), _ptr(out_score), int(keys.shape[1]),
-                     int(keys.shape[0]), int(q.shape[1]), int(q.shape[2]), dtype_code(q), dtype_code(keys), m, W, k)
+    """keys: a tiled key cache [B][E_cap/32][D_I/8][32][8] (see key_tiles_empty)."""
+    if keys.dim() != 5:
+        raise ValueError("indexer keys must be in the tiled layout [B][E_cap/32][D_I/8][32][8]")
+    return IndexArgs(rows.c(), _ptr(q), _ptr(w), _ptr(keys), _ptr(out_idx), _ptr(out_score),
+                     int(keys.shape[1]) * 32, int(keys.shape[0]), int(q.shape[1]), int(q.shape[2]), dtype_code(q),
+                     dtype_code(keys), m, W, k)
 
 
 def csa_index_topk_workspace_size(a: IndexArgs) -> int:

@@ -21,6 +21,7 @@
 namespace sckv {
 
 constexpr int kChunk = 32;
+constexpr int kSegItems = 1024;   // item sources resolved per segment of a block's range
 
 struct AttendParams {
   const uint16_t* q;
@@ -76,42 +77,62 @@ __device__ __forceinline__ int64_t item_source(const AttendParams& p, const RowI
   return -2 - (i % p.R_w);
 }
 
+// Sources of items [q_begin, q_end) of a row, resolved into LDS ahead of the
+// streaming loop (index-list reads and ring-slot arithmetic off its path).
+__device__ __forceinline__ void block_sources(const AttendParams& p, const RowItems& ri, int r, int64_t q_begin,
+                                              int64_t q_end, int nthreads, int32_t* srcs) {
+  for (int64_t q = q_begin + threadIdx.x; q < q_end; q += nthreads)
+    srcs[q - q_begin] = (int32_t)item_source(p, ri, r, q);
+}
+
+// Staging unit: 4 consecutive items x 8 consecutive dims ("pair" (a, p): items
+// 4a .. 4a+3, dims 8p .. 8p+7).  A thread loads the four row segments into
+// registers one chunk ahead; at store time it writes them row-major for Q.K^T
+// and, transposed in registers, as eight 8-byte cells (one dim, four items) of
+// the P.V operand.  Everything that needs the loaded values (masking, fp8
+// decoding) happens at store time, so issuing the loads never waits on them.
 template <int ENT, int D, int NW>
 struct Stage {
   static constexpr int NT = NW * kWave;
-  static constexpr int SEGS_PER_ITEM = D / 8;
-  static constexpr int NSEG = kChunk * SEGS_PER_ITEM;
-  static constexpr int SPT = (NSEG + NT - 1) / NT;
-  u32x4 v[SPT];       // 8 bf16 values per segment
-  float sc[SPT];      // item scale (e4m3 entries), 1 otherwise; 0 marks a masked item
+  static constexpr int PARTS = D / 8;                 // 8-dim parts per item row
+  static constexpr int NPAIR = (kChunk / 4) * PARTS;  // (item group, part) pairs per chunk
+  static constexpr int PPT = (NPAIR + NT - 1) / NT;   // pairs per thread
+  u32x4 v[PPT][4];                                   // bf16 x 8: entries (BF16) or window rows
+  u32x2 c[ENT == SCKV_E4M3 ? PPT : 1][4];            // e4m3 x 8 entry codes
+  float sc[ENT == SCKV_E4M3 ? PPT : 1][4];           // e4m3 entry scales
+  int32_t src[PPT][4];                               // item sources (entry >= 0, window <= -2, none -1)
 };
 
 template <int ENT, int D, int NW>
-__device__ __forceinline__ void stage_load(const AttendParams& p, const RowItems& ri, int r, int64_t q0,
-                                           Stage<ENT, D, NW>& st) {
+__device__ __forceinline__ void stage_load(const AttendParams& p, gbytes ent, gbytes win, gbytes esc,
+                                           const RowItems& ri, const int32_t* srcs, int64_t q_rel, bool has_ent,
+                                           bool has_win, Stage<ENT, D, NW>& st) {
   using S = Stage<ENT, D, NW>;
 #pragma unroll
-  for (int s = 0; s < S::SPT; ++s) {
-    const int seg = threadIdx.x + s * S::NT;
-    st.v[s] = u32x4{0u, 0u, 0u, 0u};
-    st.sc[s] = 0.f;
-    if (seg < S::NSEG) {
-      const int c = seg / S::SEGS_PER_ITEM, part = seg % S::SEGS_PER_ITEM;
-      const int64_t src = item_source(p, ri, r, q0 + c);
-      if (src >= 0) {
-        const int64_t row = ri.seq * p.E_cap + src;
-        if constexpr (ENT == SCKV_E4M3) {
-          const u32x2 raw = *reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(p.entries) + row * D + part * 8);
-          st.v[s] = e4m3x8_to_bf16x8(raw);
-          st.sc[s] = p.escale[row];
-        } else {
-          st.v[s] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.entries) + row * D + part * 8);
-          st.sc[s] = 1.f;
+  for (int s = 0; s < S::PPT; ++s) {
+    const int pair = threadIdx.x + s * S::NT;
+    const int pr = pair < S::NPAIR ? pair : 0;
+    const int part = pr % S::PARTS, a = pr / S::PARTS;
+    // the four item sources of this pair in one LDS read
+    const int4 src4 = *reinterpret_cast<const int4*>(&srcs[q_rel + 4 * a]);
+    st.src[s][0] = pair < S::NPAIR ? src4.x : -1;
+    st.src[s][1] = pair < S::NPAIR ? src4.y : -1;
+    st.src[s][2] = pair < S::NPAIR ? src4.z : -1;
+    st.src[s][3] = pair < S::NPAIR ? src4.w : -1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int32_t sv = st.src[s][i];
+      const int64_t erow = ri.seq * p.E_cap + (sv >= 0 ? sv : 0);         // masked: row 0, zeroed later
+      const int64_t wrow = ri.seq * p.R_w + (sv <= -2 ? -2 - sv : 0);
+      if constexpr (ENT == SCKV_E4M3) {
+        if (has_ent) {
+          st.c[s][i] = gload<u32x2>(ent, erow * D + part * 8);
+          st.sc[s][i] = gload<float>(esc, erow * 4);
         }
-      } else if (src <= -2) {
-        const int64_t row = ri.seq * p.R_w + (-2 - src);
-        st.v[s] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.win) + row * D + part * 8);
-        st.sc[s] = 1.f;
+        if (has_win) st.v[s][i] = gload<u32x4>(win, (wrow * D + part * 8) * 2);
+      } else {
+        const bool is_win = sv <= -2;
+        st.v[s][i] = gload<u32x4>(is_win ? win : ent, ((is_win ? wrow : erow) * D + part * 8) * 2);
       }
     }
   }
@@ -119,28 +140,57 @@ __device__ __forceinline__ void stage_load(const AttendParams& p, const RowItems
 
 template <int D>
 struct Lds {
-  static constexpr int KR_STRIDE = D + 8;        // bf16 elements per item row
-  static constexpr int VT_STRIDE = kChunk + 4;   // fp16 elements per dim row
+  static constexpr int KR_STRIDE = D + 8;   // bf16 elements per item row
   uint16_t kr[kChunk * KR_STRIDE];
-  _Float16 vt[D * VT_STRIDE];
+  u32x2 vt[D * 8];                          // [dim][8 cells of 4 items] fp16, cells XOR-swizzled
   float isc[kChunk];
 };
+
+// Cell position of items 4a .. 4a+3 in the row of dim d: spreads both the
+// transposed writes (dims 8p + e over lanes p) and the operand reads (dims
+// 16 nd + col over lanes col) over the LDS banks.
+__device__ __forceinline__ int vt_cell(int d, int a) { return d * 8 + (a ^ (((d >> 1) ^ (d >> 4)) & 7)); }
 
 template <int ENT, int D, int NW>
 __device__ __forceinline__ void stage_store(const Stage<ENT, D, NW>& st, Lds<D>& L) {
   using S = Stage<ENT, D, NW>;
 #pragma unroll
-  for (int s = 0; s < S::SPT; ++s) {
-    const int seg = threadIdx.x + s * S::NT;
-    if (seg < S::NSEG) {
-      const int c = seg / S::SEGS_PER_ITEM, part = seg % S::SEGS_PER_ITEM;
-      *reinterpret_cast<u32x4*>(&L.kr[c * Lds<D>::KR_STRIDE + part * 8]) = st.v[s];
+  for (int s = 0; s < S::PPT; ++s) {
+    const int pair = threadIdx.x + s * S::NT;
+    if (pair < S::NPAIR) {
+      const int part = pair % S::PARTS, a = pair / S::PARTS;
+      u32x4 v[4];
+      float sc[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int32_t sv = st.src[s][i];
+        if constexpr (ENT == SCKV_E4M3) {
+          v[i] = sv >= 0 ? e4m3x8_to_bf16x8(st.c[s][i]) : st.v[s][i];
+          sc[i] = sv >= 0 ? st.sc[s][i] : 1.f;
+        } else {
+          v[i] = st.v[s][i];
+          sc[i] = 1.f;
+        }
+        if (sv == -1) {
+          v[i] = u32x4{0u, 0u, 0u, 0u};
+          sc[i] = 0.f;
+        }
+        *reinterpret_cast<u32x4*>(&L.kr[(4 * a + i) * Lds<D>::KR_STRIDE + part * 8]) = v[i];
+      }
+      // fp16 copies, transposed: cell (dim 8 part + e, group a) = items 4a .. 4a+3 of that dim
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t bits = (st.v[s][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-        L.vt[(part * 8 + e) * Lds<D>::VT_STRIDE + c] = (_Float16)bf16_to_f32(bits);
+        float f[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[i] = bf16_to_f32((v[i][e >> 1] >> ((e & 1) * 16)) & 0xffffu);
+        const auto lo = __builtin_amdgcn_cvt_pkrtz(f[0], f[1]);
+        const auto hi = __builtin_amdgcn_cvt_pkrtz(f[2], f[3]);
+        L.vt[vt_cell(part * 8 + e, a)] = u32x2{bitcast<uint32_t>(lo), bitcast<uint32_t>(hi)};
       }
-      if (part == 0) L.isc[c] = st.sc[s];
+      if (part == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) L.isc[4 * a + i] = sc[i];
+      }
     }
   }
 }
@@ -150,6 +200,7 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma(AttendParams p) {
   constexpr int KSQ = D / 32;      // k-steps of Q.K^T
   constexpr int ND = D / 16;       // 16-dim output tiles
   __shared__ Lds<D> L;
+  __shared__ int32_t srcs[kSegItems];
 
   const int r = blockIdx.y, split = blockIdx.x;
   const RowItems ri = row_items(p, r);
@@ -161,25 +212,43 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma(AttendParams p) {
   int64_t q_end = q_begin + (int64_t)p.per_split * kChunk;
   q_end = q_end < ri.n_items ? q_end : ri.n_items;
 
+  const gbytes gent = opaque_global(p.entries), gwin = opaque_global(p.win), gesc = opaque_global(p.escale);
   // query fragments (B operand of S^T = items x heads): dims g*D/4 + 8 ks .. +7
   bf16x8 bq[KSQ];
   {
-    const u32x4* qp = reinterpret_cast<const u32x4*>(p.q + ((int64_t)r * p.H + head) * D + g * (D / 4));
+    const gbytes gq = opaque_global(p.q);
+    const int64_t e0 = ((int64_t)r * p.H + head) * D + g * (D / 4);
 #pragma unroll
-    for (int ks = 0; ks < KSQ; ++ks) bq[ks] = bitcast<bf16x8>(qp[ks]);
+    for (int ks = 0; ks < KSQ; ++ks) bq[ks] = bitcast<bf16x8>(gload<u32x4>(gq, (e0 + 8 * ks) * 2));
+    // the fragments stay in registers for the whole block; redefine them here so no
+    // later instruction is made to wait on these loads
+#pragma unroll
+    for (int ks = 0; ks < KSQ; ++ks) pin(bq[ks]);
   }
   f32x4 o[ND];
 #pragma unroll
   for (int nd = 0; nd < ND; ++nd) o[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;       // running maximum (base-2 logits) and sum
+  const float scale2 = p.scale * 1.4426950408889634f;
 
+  // which kinds of item a chunk starting at q holds (uniform branches in stage_load)
+  auto has_ent = [&](int64_t q) { return q < ri.n_list; };
+  auto has_win = [&](int64_t q) { return q + kChunk > ri.n_list; };
   Stage<ENT, D, NW> st;
-  if (q_begin < q_end) stage_load<ENT, D, NW>(p, ri, r, q_begin, st);
-  for (int64_t q0 = q_begin; q0 < q_end; q0 += kChunk) {
+  for (int64_t s0 = q_begin; s0 < q_end; s0 += kSegItems) {
+    const int64_t s1 = s0 + kSegItems < q_end ? s0 + kSegItems : q_end;
+    // sources of this segment's items, padded with "nothing" to whole chunks
+    __syncthreads();
+    block_sources(p, ri, r, s0, s0 + (s1 - s0 + kChunk - 1) / kChunk * kChunk, NW * kWave, srcs);
+    __syncthreads();
+    stage_load<ENT, D, NW>(p, gent, gwin, gesc, ri, srcs, 0, has_ent(s0), has_win(s0), st);
+  for (int64_t q0 = s0; q0 < s1; q0 += kChunk) {
     __syncthreads();
     stage_store<ENT, D, NW>(st, L);
     __syncthreads();
-    if (q0 + kChunk < q_end) stage_load<ENT, D, NW>(p, ri, r, q0 + kChunk, st);
+    if (q0 + kChunk < s1)
+      stage_load<ENT, D, NW>(p, gent, gwin, gesc, ri, srcs, q0 + kChunk - s0, has_ent(q0 + kChunk),
+                             has_win(q0 + kChunk), st);
 
     // S^T for the chunk: two 16-item tiles
     f32x4 sacc[2];
@@ -194,7 +263,7 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma(AttendParams p) {
       }
       sacc[mt] = acc;
     }
-    // logits, chunk maximum per head
+    // logits in the base-2 domain (scale * log2 e folded in), chunk maximum per head
     float x[8], isc[8];
     float cmax = -INFINITY;
 #pragma unroll
@@ -203,7 +272,7 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma(AttendParams p) {
       for (int i = 0; i < 4; ++i) {
         const float sc = L.isc[16 * mt + 4 * g + i];
         isc[4 * mt + i] = sc;
-        const float v = sc != 0.f ? sacc[mt][i] * (p.scale * sc) : -INFINITY;
+        const float v = sc != 0.f ? sacc[mt][i] * (scale2 * sc) : -INFINITY;
         x[4 * mt + i] = v;
         cmax = fmaxf(cmax, v);
       }
@@ -211,32 +280,37 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma(AttendParams p) {
     cmax = fmaxf(cmax, shfl_xor_f(cmax, 32));
     const float m_new = fmaxf(m_run, cmax);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = m_run == -INFINITY ? 0.f : expf(m_run - m_new);
+    const bool grows = m_new > m_run;                  // this head's running maximum moved
+    const float alpha = grows ? (m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new)) : 1.f;
     m_run = m_new;
     f16x8 pa;
     float psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float pe = expf(x[e] - m_use);
+      const float pe = __builtin_amdgcn_exp2f(x[e] - m_use);
       psum += pe;
       pa[e] = (_Float16)(ENT == SCKV_E4M3 ? pe * isc[e] : pe);
     }
     l_run = l_run * alpha + psum;
-    // rescale rows (heads 4g + i of this wave) by their alpha
-    float al[4];
+    // rescale the output rows (heads 4g + i of this wave) only when some maximum moved
+    if (__any(grows)) {
+      float al[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i, kWave);
+      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i, kWave);
+#pragma unroll
+      for (int nd = 0; nd < ND; ++nd)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[nd][i] *= al[i];
+    }
 #pragma unroll
     for (int nd = 0; nd < ND; ++nd) {
-      const _Float16* vp = &L.vt[(16 * nd + col) * Lds<D>::VT_STRIDE + 4 * g];
-      const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
-      const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 16);
+      const int d = 16 * nd + col;
+      const u32x2 lo = L.vt[vt_cell(d, g)];
+      const u32x2 hi = L.vt[vt_cell(d, 4 + g)];
       const f16x8 bv = bitcast<f16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
-      f32x4 acc = o[nd];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] *= al[i];
-      o[nd] = mfma16_f16(pa, bv, acc);
+      o[nd] = mfma16_f16(pa, bv, o[nd]);
     }
+  }
   }
 
   // per-head totals
@@ -257,7 +331,7 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma(AttendParams p) {
         if (p.out_dtype == SCKV_BF16) static_cast<uint16_t*>(p.out)[off] = (uint16_t)f32_to_bf16_rne(v);
         else static_cast<float*>(p.out)[off] = v;
       }
-    if (p.lse && g == 0) p.lse[(int64_t)r * p.H + head] = m_run + logf(l_tot);
+    if (p.lse && g == 0) p.lse[(int64_t)r * p.H + head] = (m_run + log2f(l_tot)) * 0.6931471805599453f;
   } else {
     const int64_t sbase = ((int64_t)r * p.nsplit + split) * p.H;
 #pragma unroll
@@ -271,7 +345,9 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma(AttendParams p) {
   }
 }
 
-// Merge of split partials: o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s, in split order.
+// Merge of split partials (maxima m_s in base-2 logit units):
+// o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, in split order.
+// One block per (head, row); a thread owns four consecutive dims.
 __global__ __launch_bounds__(128) void attend_combine(const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
                                                       void* __restrict__ out, float* __restrict__ lse, int H, int D,
                                                       int nsplit, int out_dtype) {
@@ -281,21 +357,31 @@ __global__ __launch_bounds__(128) void attend_combine(const float* __restrict__ 
   float L = 0.f;
   for (int s = 0; s < nsplit; ++s) {
     const float* ml = &ws_ml[(((int64_t)r * nsplit + s) * H + h) * 2];
-    L += ml[0] == -INFINITY ? 0.f : expf(ml[0] - M) * ml[1];
+    L += ml[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[0] - M) * ml[1];
   }
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float acc = 0.f;
+  const float inv = 1.f / L;
+  for (int d4 = threadIdx.x; d4 < D / 4; d4 += blockDim.x) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < nsplit; ++s) {
       const int64_t base = ((int64_t)r * nsplit + s) * H + h;
       const float ms = ws_ml[base * 2];
-      if (ms != -INFINITY) acc += expf(ms - M) * ws_o[base * D + d];
+      if (ms != -INFINITY) {
+        const float wgt = __builtin_amdgcn_exp2f(ms - M);
+        const f32x4 v = *reinterpret_cast<const f32x4*>(&ws_o[base * D + 4 * d4]);
+        acc += wgt * v;
+      }
     }
-    const float v = acc / L;
-    const int64_t off = ((int64_t)r * H + h) * D + d;
-    if (out_dtype == SCKV_BF16) static_cast<uint16_t*>(out)[off] = (uint16_t)f32_to_bf16_rne(v);
-    else static_cast<float*>(out)[off] = v;
+    const int64_t off = ((int64_t)r * H + h) * D + 4 * d4;
+    if (out_dtype == SCKV_BF16) {
+      uint16_t* o = static_cast<uint16_t*>(out) + off;
+      const uint32_t lo = f32_to_bf16_rne(acc[0] * inv) | (f32_to_bf16_rne(acc[1] * inv) << 16);
+      const uint32_t hi = f32_to_bf16_rne(acc[2] * inv) | (f32_to_bf16_rne(acc[3] * inv) << 16);
+      *reinterpret_cast<u32x2*>(o) = u32x2{lo, hi};
+    } else {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(out) + off) = acc * inv;
+    }
   }
-  if (lse && threadIdx.x == 0) lse[(int64_t)r * H + h] = M + logf(L);
+  if (lse && threadIdx.x == 0) lse[(int64_t)r * H + h] = (M + log2f(L)) * 0.6931471805599453f;
 }
 
 // fp32 path: one block per row, items 64 at a time through LDS.

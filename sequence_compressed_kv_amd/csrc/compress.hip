@@ -35,7 +35,7 @@ template <int IN, int OUT, bool SCALED>
 __global__ __launch_bounds__(256) void compress_kernel(
     const void* __restrict__ val, const void* __restrict__ gate, const float* __restrict__ bpos,
     void* __restrict__ out, float* __restrict__ out_scale, int64_t N, int D, int m, int o,
-    int64_t e_begin, int64_t e_count, int64_t E_cap, int G) {
+    int64_t e_begin, int64_t e_count, int64_t E_cap, int G, int key_tiles) {
   const int lane = lane_id();
   const int epw = kWave / G;
   const int slot = lane / G, sub = lane % G;
@@ -75,7 +75,9 @@ __global__ __launch_bounds__(256) void compress_kernel(
 #pragma unroll
   for (int c = 0; c < 8; ++c) cv[c] = acc[c] / l[c];
 
-  const int64_t orow = (b * E_cap + e) * D + ch;
+  // rows: [E_cap][D]; key tiles: [E_cap/32][D/8][32][8] (8 channels of 32 entries contiguous)
+  const int64_t orow = key_tiles ? b * E_cap * D + (((e >> 5) * (D >> 3) + (ch >> 3)) * 32 + (e & 31)) * 8
+                                 : (b * E_cap + e) * D + ch;
   if constexpr (OUT == SCKV_F32) {
     if (active) {
       f32x4* p = reinterpret_cast<f32x4*>(static_cast<float*>(out) + orow);
@@ -118,7 +120,8 @@ static hipError_t launch_in(const sckv_pool_stream& s, int32_t B, int64_t N, int
   const dim3 block(256);
 #define SCKV_LAUNCH(OUT, SC)                                                                    \
   hipLaunchKernelGGL((compress_kernel<IN, OUT, SC>), grid, block, 0, stream, s.val, s.gate,     \
-                     s.bpos, s.out, s.out_scale, N, s.D, m, o, e_begin, e_count, s.E_cap, G)
+                     s.bpos, s.out, s.out_scale, N, s.D, m, o, e_begin, e_count, s.E_cap, G,           \
+                     s.out_layout == SCKV_LAYOUT_KEY_TILES ? 1 : 0)
   switch (s.out_dtype) {
     case SCKV_F32: SCKV_LAUNCH(SCKV_F32, false); break;
     case SCKV_BF16: SCKV_LAUNCH(SCKV_BF16, false); break;

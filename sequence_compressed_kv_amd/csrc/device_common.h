@@ -104,6 +104,35 @@ __device__ __forceinline__ T bitcast(const S& s) {
   return __builtin_bit_cast(T, s);
 }
 
+// Global-memory byte pointer whose origin the compiler cannot see.  Loads through
+// it are not known to read memory that stays unchanged during the kernel, so the
+// compiler cannot re-issue them next to their use (rematerialisation): a
+// prefetched value stays in the registers it was loaded into and its load stays
+// where it was issued.  The address space stays global (not flat), so these
+// loads never hold up LDS waits.
+typedef __attribute__((address_space(1))) const uint8_t* gbytes;
+
+__device__ __forceinline__ gbytes opaque_global(const void* p) {
+  asm volatile("" : "+s"(p));
+  return (gbytes)p;
+}
+
+template <typename V>
+__device__ __forceinline__ V gload(gbytes base, int64_t byte_off) {
+  return *reinterpret_cast<__attribute__((address_space(1))) const V*>(base + byte_off);
+}
+
+// Redefines a register value through an empty asm statement (the value must be
+// ready: this waits for its load).  Later uses then carry no dependency on the
+// original load.
+template <typename T>
+__device__ __forceinline__ void pin(T& v) {
+  static_assert(sizeof(T) == 16, "128-bit values");
+  u32x4 x = __builtin_bit_cast(u32x4, v);
+  asm volatile("" : "+v"(x));
+  v = __builtin_bit_cast(T, x);
+}
+
 // ------------------------------------------------------------------ wave / block helpers
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 __device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }

@@ -38,19 +38,26 @@ __device__ __forceinline__ int64_t visible(int64_t t, int m, int W, int64_t E_ca
   return e < E_cap ? e : E_cap;
 }
 
+// Element offset of dims 8 db .. 8 db + 7 of key j in a tiled key cache
+// ([E_cap/32][DI/8][32][8] per sequence, sequence base seq_elem).
+template <int DI>
+__device__ __forceinline__ int64_t key_tile_elem(int64_t seq_elem, int64_t j, int db) {
+  return seq_elem + (((j >> 5) * (DI / 8) + db) * 32 + (j & 31)) * 8;
+}
+
 // Keys of one 32-key tile as MFMA B fragments: lane (n = l%32, half hh = l/32)
-// holds dims hh*DI/2 + 8 ks .. +7 of key n, for ks = 0 .. DI/16 - 1.
+// holds dims hh*DI/2 + 8 ks .. +7 of key n, for ks = 0 .. DI/16 - 1.  In the
+// tiled layout the 32 lanes of a half-wave read one contiguous run of 32 x 8
+// elements per ks (elem0: offset of key n's first dim block of its half).
 template <int KEY, int DI>
-__device__ __forceinline__ void load_key_tile(const void* keys, int64_t row_elem, bf16x8 (&b)[DI / 16]) {
+__device__ __forceinline__ void load_key_tile(gbytes keys, int64_t elem0, bf16x8 (&b)[DI / 16]) {
   constexpr int KS = DI / 16;
   if constexpr (KEY == SCKV_BF16) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(keys) + row_elem);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) b[ks] = bitcast<bf16x8>(p[ks]);
+    for (int ks = 0; ks < KS; ++ks) b[ks] = bitcast<bf16x8>(gload<u32x4>(keys, (elem0 + 256 * ks) * 2));
   } else {
-    const u32x2* p = reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(keys) + row_elem);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) b[ks] = bitcast<bf16x8>(e4m3x8_to_bf16x8(p[ks]));
+    for (int ks = 0; ks < KS; ++ks) b[ks] = bitcast<bf16x8>(e4m3x8_to_bf16x8(gload<u32x2>(keys, elem0 + 256 * ks)));
   }
 }
 
@@ -61,13 +68,13 @@ struct ScoreWave {
   bf16x8 a[MT][KS];
   float w[MT][16];
 
-  __device__ __forceinline__ void load_query(const uint16_t* q_row, const float* w_row) {
+  __device__ __forceinline__ void load_query(gbytes q_row, const float* w_row) {
     const int l = lane_id(), n = l & 31, hh = l >> 5;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const u32x4* p = reinterpret_cast<const u32x4*>(q_row + (int64_t)(32 * mt + n) * DI + hh * (DI / 2));
+      const int64_t e0 = (int64_t)(32 * mt + n) * DI + hh * (DI / 2);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) a[mt][ks] = bitcast<bf16x8>(p[ks]);
+      for (int ks = 0; ks < KS; ++ks) a[mt][ks] = bitcast<bf16x8>(gload<u32x4>(q_row, (e0 + 8 * ks) * 2));
 #pragma unroll
       for (int i = 0; i < 16; ++i) w[mt][i] = w_row[32 * mt + 8 * (i >> 2) + 4 * hh + (i & 3)];
     }
@@ -90,13 +97,13 @@ struct ScoreWave {
   }
 
   // Walk tiles [j_begin, j_end) of one row, writing scores of keys < e_vis.
-  __device__ __forceinline__ void run(const void* keys, int64_t key_base_row, int64_t j_begin,
+  __device__ __forceinline__ void run(gbytes keys, int64_t key_base_row, int64_t j_begin,
                                       int64_t j_end, int64_t e_vis, float* srow) const {
     const int l = lane_id(), n = l & 31, hh = l >> 5;
     auto row_elem = [&](int64_t j0) {
       int64_t key = j0 + n;
       key = key < e_vis ? key : e_vis - 1;
-      return (key_base_row + key) * DI + hh * (DI / 2);
+      return key_tile_elem<DI>(key_base_row * DI, key, hh * (DI / 16));
     };
     if (j_begin >= j_end) return;
     bf16x8 cur[KS], nxt[KS];
@@ -114,22 +121,74 @@ struct ScoreWave {
   }
 };
 
-template <int KEY, int HI, int DI>
+// Decode rows: a block takes one row and 4 consecutive ranges of NT tiles of 32
+// keys (one range per wave).  The row's query sits in LDS (shared by the four
+// waves, rows padded against bank conflicts).  A wave's tile loop is unrolled
+// completely, with two tiles in flight ahead of the one being multiplied: in
+// straight-line code every wait covers exactly the tile it needs.  Loads past
+// the row's last visible tile re-read it; their scores are not stored.
+template <int KEY, int HI, int DI, int NT>
 __global__ __launch_bounds__(256) void index_score_decode(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const void* __restrict__ keys,
     float* __restrict__ scores, int64_t stride, int64_t E_cap, int m, int W, const int32_t* __restrict__ pos,
-    int32_t pos_max, int64_t keys_per_block) {
+    int32_t pos_max) {
+  constexpr int MT = HI / 32, KS = DI / 16, QS = DI + 8;
+  constexpr int64_t KPW = 32 * NT;
+  __shared__ uint16_t qs[HI * QS];
   const int r = blockIdx.y;
   const RowRef rr = row_ref(SCKV_ROWS_DECODE, pos, pos_max, 0, 0, r);
   const int64_t e_vis = visible(rr.t, m, W, E_cap);
-  const int64_t kpw = keys_per_block / 4;
-  const int64_t j_begin = (int64_t)blockIdx.x * keys_per_block + wave_id() * kpw;
+  if ((int64_t)blockIdx.x * 4 * KPW >= e_vis) return;           // whole block past the row
+  for (int i = threadIdx.x; i < HI * DI / 8; i += 256) {
+    const int h = i / (DI / 8), c = i % (DI / 8);
+    *reinterpret_cast<u32x4*>(&qs[h * QS + c * 8]) =
+        *reinterpret_cast<const u32x4*>(q + ((int64_t)r * HI + h) * DI + c * 8);
+  }
+  const int l = lane_id(), n = l & 31, hh = l >> 5;
+  float wr[MT][16];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) wr[mt][i] = w[(int64_t)r * HI + 32 * mt + 8 * (i >> 2) + 4 * hh + (i & 3)];
+  __syncthreads();
+  const int64_t j_begin = ((int64_t)blockIdx.x * 4 + wave_id()) * KPW;
   if (j_begin >= e_vis) return;
-  int64_t j_end = j_begin + kpw;
-  j_end = j_end < e_vis ? j_end : e_vis;
-  ScoreWave<KEY, HI, DI> sw;
-  sw.load_query(q + (int64_t)r * HI * DI, w + (int64_t)r * HI);
-  sw.run(keys, rr.seq * E_cap, j_begin, j_end, e_vis, scores + (int64_t)r * stride);
+  const int64_t j_end = j_begin + KPW < e_vis ? j_begin + KPW : e_vis;
+  const int64_t key_row0 = rr.seq * E_cap;
+  float* srow = scores + (int64_t)r * stride;
+  const gbytes gkeys = opaque_global(keys);
+
+  auto load = [&](int t, bf16x8 (&b)[KS]) {
+    int64_t key = j_begin + 32 * t + n;
+    key = key < e_vis ? key : e_vis - 1;
+    load_key_tile<KEY, DI>(gkeys, key_tile_elem<DI>(key_row0 * DI, key, hh * KS), b);
+  };
+  auto compute = [&](int t, const bf16x8 (&b)[KS]) {
+    float part = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 a = bitcast<bf16x8>(*reinterpret_cast<const u32x4*>(&qs[(32 * mt + n) * QS + hh * (DI / 2) + 8 * ks]));
+        acc = mfma32_bf16(a, b[ks], acc);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) part += wr[mt][i] * fmaxf(acc[i], 0.f);
+    }
+    const float tot = part + shfl_xor_f(part, 32);
+    const int64_t j = j_begin + 32 * t + n;
+    if (hh == 0 && j < j_end) srow[j] = tot == 0.f ? 0.f : tot;
+  };
+
+  bf16x8 buf[3][KS];
+  load(0, buf[0]);
+  if constexpr (NT > 1) load(1, buf[1]);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (t + 2 < NT) load(t + 2, buf[(t + 2) % 3]);
+    compute(t, buf[t % 3]);
+  }
 }
 
 template <int KEY, int HI, int DI>
@@ -144,8 +203,8 @@ __global__ __launch_bounds__(256) void index_score_causal(
   const int64_t e_vis = visible(rr.t, m, W, E_cap);
   if (e_vis == 0) return;
   ScoreWave<KEY, HI, DI> sw;
-  sw.load_query(q + (int64_t)r * HI * DI, w + (int64_t)r * HI);
-  sw.run(keys, rr.seq * E_cap, 0, e_vis, e_vis, scores + (int64_t)r * stride);
+  sw.load_query(opaque_global(q) + (int64_t)r * HI * DI * 2, w + (int64_t)r * HI);
+  sw.run(opaque_global(keys), rr.seq * E_cap, 0, e_vis, e_vis, scores + (int64_t)r * stride);
 }
 
 // fp32 path: one thread per key, query and weights staged in LDS.
@@ -163,11 +222,12 @@ __global__ __launch_bounds__(256) void index_score_f32(
   for (int i = threadIdx.x; i < HI; i += 256) sq[HI * DI + i] = w[(int64_t)r * HI + i];
   __syncthreads();
   if (j >= e_vis) return;
-  const float* kr = keys + (rr.seq * E_cap + j) * DI;
+  // key j in the tiled layout: dims 8 db .. 8 db + 7 at tile_base + db * 256
+  const float* kr = keys + rr.seq * E_cap * DI + ((j >> 5) * (DI / 8) * 32 + (j & 31)) * 8;
   float s = 0.f;
   for (int h = 0; h < HI; ++h) {
     float d = 0.f;
-    for (int c = 0; c < DI; ++c) d = fmaf(sq[h * DI + c], kr[c], d);
+    for (int c = 0; c < DI; ++c) d = fmaf(sq[h * DI + c], kr[(c >> 3) * 256 + (c & 7)], d);
     s += sq[HI * DI + h] * fmaxf(d, 0.f);
   }
   scores[(int64_t)r * stride + j] = s == 0.f ? 0.f : s;
@@ -184,10 +244,18 @@ static void launch_mfma(const sckv_index_args& a, float* scores, int64_t stride,
                         hipStream_t stream) {
   const uint16_t* q = static_cast<const uint16_t*>(a.q);
   if (a.rows.kind == SCKV_ROWS_DECODE) {
-    const int64_t kpb = 512;
+    // tiles per wave: the largest of 16/8/4 that still gives about 2048 waves (8 per CU)
+    const int64_t tiles = (cover + 31) / 32 * a.rows.R;
+    const int nt = tiles >= 2048 * 16 ? 16 : (tiles >= 2048 * 8 ? 8 : 4);
+    const int64_t kpb = 4 * 32 * (int64_t)nt;
     const dim3 grid((unsigned)((cover + kpb - 1) / kpb), (unsigned)a.rows.R);
-    hipLaunchKernelGGL((index_score_decode<KEY, HI, DI>), grid, dim3(256), 0, stream, q, a.w, a.keys, scores,
-                       stride, a.E_cap, a.m, a.W, a.rows.pos, a.rows.pos_max, kpb);
+#define SCKV_DEC(NTT)                                                                                          \
+  hipLaunchKernelGGL((index_score_decode<KEY, HI, DI, NTT>), grid, dim3(256), 0, stream, q, a.w, a.keys, scores, \
+                     stride, a.E_cap, a.m, a.W, a.rows.pos, a.rows.pos_max)
+    if (nt == 16) SCKV_DEC(16);
+    else if (nt == 8) SCKV_DEC(8);
+    else SCKV_DEC(4);
+#undef SCKV_DEC
   } else {
     const dim3 grid((unsigned)((a.rows.R + 3) / 4));
     hipLaunchKernelGGL((index_score_causal<KEY, HI, DI>), grid, dim3(256), 0, stream, q, a.w, a.keys, scores,

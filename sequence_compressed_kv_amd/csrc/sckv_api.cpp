@@ -54,6 +54,10 @@ sckv_status check_pool(const sckv_pool_stream* s, const char* name, int32_t B, i
   if (s->out_dtype != SCKV_F32 && s->out_dtype != SCKV_BF16 && s->out_dtype != SCKV_E4M3)
     return fail(SCKV_ERR_DTYPE, "%s: out_dtype %d not supported", name, s->out_dtype);
   if (!pow2_dim(s->D)) return fail(SCKV_ERR_UNSUPPORTED, "%s: D=%d not in {8,...,512} (powers of two)", name, s->D);
+  if (s->out_layout != SCKV_LAYOUT_ROWS && s->out_layout != SCKV_LAYOUT_KEY_TILES)
+    return fail(SCKV_ERR_SHAPE, "%s: unknown out_layout %d", name, s->out_layout);
+  if (s->out_layout == SCKV_LAYOUT_KEY_TILES && s->E_cap % 32 != 0)
+    return fail(SCKV_ERR_SHAPE, "%s: key-tile caches need E_cap %% 32 == 0 (E_cap=%lld)", name, (long long)s->E_cap);
   if (B < 1 || N < 1 || m < 1 || o < 0) return fail(SCKV_ERR_SHAPE, "%s: need B>=1, N>=1, m>=1, o>=0", name);
   if (e_begin < 0 || e_count < 0) return fail(SCKV_ERR_SHAPE, "%s: e_begin/e_count must be >= 0", name);
   if ((int64_t)m * (e_begin + e_count) > N)
@@ -101,6 +105,9 @@ sckv_status check_index(const sckv_index_args* a, IndexPlan* pl, bool need_out) 
   if (a->k < 1) return fail(SCKV_ERR_SHAPE, "index: k=%d must be >= 1", a->k);
   if (a->m < 1 || a->W < 0 || a->E_cap < 1 || a->H_I < 1 || a->D_I < 1)
     return fail(SCKV_ERR_SHAPE, "index: need m>=1, W>=0, E_cap>=1, H_I>=1, D_I>=1");
+  if (a->E_cap % 32 != 0 || a->D_I % 8 != 0)
+    return fail(SCKV_ERR_SHAPE, "index: tiled keys need E_cap %% 32 == 0 and D_I %% 8 == 0 (got %lld, %d)",
+                (long long)a->E_cap, a->D_I);
   if (a->q_dtype == SCKV_F32 && a->key_dtype == SCKV_F32) {
     if ((int64_t)a->H_I * a->D_I > 8192) return fail(SCKV_ERR_UNSUPPORTED, "index: F32 path needs H_I*D_I <= 8192");
   } else if (a->q_dtype == SCKV_BF16 && (a->key_dtype == SCKV_BF16 || a->key_dtype == SCKV_E4M3)) {

@@ -88,21 +88,55 @@ __device__ __forceinline__ uint32_t radix_threshold(const uint32_t (&key)[V], co
   return prefix;
 }
 
+// Exclusive prefix of per-thread counts c[i] in element order, where a thread
+// holds groups i = 0 .. NI-1 of 4 consecutive elements and element order is
+// (wave, group, lane, element).  Returns per-group offsets and the block total.
+template <int NT, int NI>
+__device__ __forceinline__ void ordered_scan(const uint32_t (&c)[NI], uint32_t (&off)[NI], uint32_t* sh,
+                                             uint32_t* total) {
+  constexpr int NW = NT / kWave;
+  const int w = wave_id(), l = lane_id();
+  uint32_t run = 0;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const uint32_t inc = wave_incl_scan(c[i]);
+    off[i] = run + inc - c[i];
+    run += __shfl(inc, kWave - 1, kWave);
+  }
+  if (l == 0) sh[w] = run;
+  __syncthreads();
+  if (w == 0) {
+    const uint32_t x = l < NW ? sh[l] : 0u;
+    const uint32_t xi = wave_incl_scan(x);
+    if (l < NW) sh[l] = xi - x;
+    if (l == NW - 1) sh[NW] = xi;
+  }
+  __syncthreads();
+  const uint32_t base = sh[w];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) off[i] += base;
+  *total = sh[NW];
+  __syncthreads();
+}
+
 // MODE TOPK_ROW   : scores of row r, elements 0 .. n-1 (n = visible count), out to out_idx.
 // MODE TOPK_SLICE : slice blockIdx.x of row r, local top-k written as candidates.
 // MODE TOPK_MERGE : the candidates of row r (slot q valid iff q % kc < count[r][q / kc]).
+// Wave w owns elements [w*64*V, (w+1)*64*V); its group i is read as one coalesced
+// 1 KB load: lane l takes elements w*64*V + (i*64 + l)*4 .. +3.
 template <int NT, int V, int MODE>
 __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scores, int64_t stride,
                                                   TopkRows rows, int k, int64_t slice, int nslices, int kc,
-                                                  float* __restrict__ cand_s, int32_t* __restrict__ cand_i,
-                                                  int32_t* __restrict__ cand_n, int32_t* __restrict__ out_idx,
-                                                  float* __restrict__ out_score) {
+                                                  int64_t cap, float* __restrict__ cand_s,
+                                                  int32_t* __restrict__ cand_i, int32_t* __restrict__ cand_n,
+                                                  int32_t* __restrict__ out_idx, float* __restrict__ out_score) {
+  constexpr int NI = V / 4;
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t scan_sh[NT / kWave + 1];
   __shared__ uint32_t ctl[2];
   const int r = blockIdx.y;
+  const int w = wave_id(), l = lane_id();
   const int64_t n_row = row_visible(rows, r);
-  const int64_t cap = (int64_t)nslices * kc;
 
   int64_t base = 0, len = 0;
   if (MODE == TOPK_ROW) {
@@ -118,23 +152,35 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
   uint32_t key[V];
   int32_t idx[V];
   bool valid[V];
-  const int64_t e0 = (int64_t)threadIdx.x * V;
+  const float* src = MODE == TOPK_MERGE ? cand_s + (int64_t)r * cap : scores + (int64_t)r * stride + base;
+  const bool vec = ((reinterpret_cast<uintptr_t>(src) & 15u) == 0);
 #pragma unroll
-  for (int v = 0; v < V; ++v) {
-    const int64_t e = e0 + v;
-    bool ok = e < len;
-    float s = 0.f;
-    int32_t id = -1;
-    if (MODE == TOPK_MERGE) {
-      if (ok) ok = (int)(e % kc) < cand_n[(int64_t)r * nslices + e / kc];
-      if (ok) { s = cand_s[(int64_t)r * cap + e]; id = cand_i[(int64_t)r * cap + e]; }
-    } else if (ok) {
-      s = scores[(int64_t)r * stride + base + e];
-      id = (int32_t)(base + e);
+  for (int i = 0; i < NI; ++i) {
+    const int64_t e0 = (int64_t)w * 64 * V + ((int64_t)i * 64 + l) * 4;
+    float s4[4] = {0.f, 0.f, 0.f, 0.f};
+    int32_t i4[4] = {-1, -1, -1, -1};
+    if (vec && e0 + 3 < len) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(src + e0);
+      s4[0] = v[0]; s4[1] = v[1]; s4[2] = v[2]; s4[3] = v[3];
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (e0 + j < len) s4[j] = src[e0 + j];
     }
-    valid[v] = ok;
-    key[v] = ok ? score_key(s) : 0u;
-    idx[v] = id;
+    if (MODE == TOPK_MERGE) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (e0 + j < len) i4[j] = cand_i[(int64_t)r * cap + e0 + j];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t e = e0 + j;
+      bool ok = e < len;
+      if (MODE == TOPK_MERGE && ok) ok = e / kc < nslices && (int)(e % kc) < cand_n[(int64_t)r * nslices + e / kc];
+      valid[4 * i + j] = ok;
+      key[4 * i + j] = ok ? score_key(s4[j]) : 0u;
+      idx[4 * i + j] = MODE == TOPK_MERGE ? i4[j] : (int32_t)(base + e);
+    }
   }
 
   // number of valid elements and how many to keep
@@ -149,16 +195,30 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
   if (kk < n_valid) T = radix_threshold<NT, V>(key, valid, kk, hist, scan_sh, ctl, &need);
 
   // ordered compaction: keys above T, then the first `need` keys equal to T
-  uint32_t n_gt = 0, n_eq = 0;
+  uint32_t ceq[NI], eq_off[NI], tot;
 #pragma unroll
-  for (int v = 0; v < V; ++v) {
-    n_gt += (valid[v] && key[v] > T) ? 1u : 0u;
-    n_eq += (valid[v] && key[v] == T) ? 1u : 0u;
+  for (int i = 0; i < NI; ++i) {
+    ceq[i] = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ceq[i] += (valid[4 * i + j] && key[4 * i + j] == T) ? 1u : 0u;
   }
-  uint32_t tot;
-  const uint32_t eq_before = block_excl_scan<NT>(n_eq, scan_sh, &tot);
-  const uint32_t eq_take = need > eq_before ? (need - eq_before < n_eq ? need - eq_before : n_eq) : 0u;
-  uint32_t off = block_excl_scan<NT>(n_gt + eq_take, scan_sh, &tot);
+  ordered_scan<NT, NI>(ceq, eq_off, scan_sh, &tot);
+  bool sel[V];
+  uint32_t csel[NI], sel_off[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    uint32_t eq_rank = eq_off[i];
+    csel[i] = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int v = 4 * i + j;
+      bool sv = valid[v] && key[v] > T;
+      if (valid[v] && key[v] == T) sv = eq_rank++ < need;
+      sel[v] = sv;
+      csel[i] += sv ? 1u : 0u;
+    }
+  }
+  ordered_scan<NT, NI>(csel, sel_off, scan_sh, &tot);
 
   int32_t* oi;
   float* os;
@@ -170,18 +230,17 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
     oi = out_idx + (int64_t)r * k;
     os = out_score ? out_score + (int64_t)r * k : nullptr;
   }
-  uint32_t eq_seen = 0;
 #pragma unroll
-  for (int v = 0; v < V; ++v) {
-    bool sel = valid[v] && key[v] > T;
-    if (valid[v] && key[v] == T) {
-      sel = eq_seen < eq_take;
-      ++eq_seen;
-    }
-    if (sel) {
-      oi[off] = idx[v];
-      if (os) os[off] = key_score(key[v]);
-      ++off;
+  for (int i = 0; i < NI; ++i) {
+    uint32_t off = sel_off[i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int v = 4 * i + j;
+      if (sel[v]) {
+        oi[off] = idx[v];
+        if (os) os[off] = key_score(key[v]);
+        ++off;
+      }
     }
   }
   if (MODE != TOPK_SLICE) {
@@ -208,7 +267,7 @@ TopkPlan plan_topk(int64_t cover, int32_t k, int32_t R) {
   p.slice = 16384;
   p.nslices = (cover + p.slice - 1) / p.slice;
   const int64_t kc = k < p.slice ? k : p.slice;
-  p.cand = p.nslices * kc;
+  p.cand = (p.nslices * kc + 3) / 4 * 4;
   if (p.cand > 1024 * 64) return p;  // not ok
   p.ws_bytes = (size_t)R * (size_t)p.cand * 8 + (size_t)R * (size_t)p.nslices * 4 + 256;
   p.ok = true;
@@ -217,12 +276,12 @@ TopkPlan plan_topk(int64_t cover, int32_t k, int32_t R) {
 
 template <int MODE>
 static void launch_cfg(int nt, int v, dim3 grid, const float* scores, int64_t stride, const TopkRows& rr,
-                       int k, int64_t slice, int nslices, int kc, float* cs, int32_t* ci, int32_t* cn,
-                       int32_t* oi, float* os, hipStream_t st) {
+                       int k, int64_t slice, int nslices, int kc, int64_t cap, float* cs, int32_t* ci,
+                       int32_t* cn, int32_t* oi, float* os, hipStream_t st) {
 #define SCKV_TK(NT, VV)                                                                                  \
   if (nt == NT && v == VV) {                                                                             \
     hipLaunchKernelGGL((topk_kernel<NT, VV, MODE>), grid, dim3(NT), 0, st, scores, stride, rr, k, slice, \
-                       nslices, kc, cs, ci, cn, oi, os);                                                 \
+                       nslices, kc, cap, cs, ci, cn, oi, os);                                            \
     return;                                                                                              \
   }
   SCKV_TK(256, 4) SCKV_TK(256, 16) SCKV_TK(256, 32) SCKV_TK(1024, 16) SCKV_TK(1024, 32) SCKV_TK(1024, 64)
@@ -234,7 +293,7 @@ hipError_t launch_topk(const sckv_index_args& a, const float* scores, int64_t st
   TopkRows rr{a.rows.kind, a.rows.pos, a.rows.pos_max, a.rows.seq0, a.rows.pos0, a.m, a.W, a.E_cap};
   const int R = a.rows.R;
   if (p.single_nt) {
-    launch_cfg<TOPK_ROW>(p.single_nt, p.single_v, dim3(1, R), scores, stride, rr, a.k, 0, 1, 1, nullptr,
+    launch_cfg<TOPK_ROW>(p.single_nt, p.single_v, dim3(1, R), scores, stride, rr, a.k, 0, 1, 1, 0, nullptr,
                          nullptr, nullptr, a.out_idx, a.out_score, stream);
     return hipGetLastError();
   }
@@ -244,12 +303,12 @@ hipError_t launch_topk(const sckv_index_args& a, const float* scores, int64_t st
   int32_t* ci = reinterpret_cast<int32_t*>(w + (size_t)R * p.cand * 4);
   int32_t* cn = reinterpret_cast<int32_t*>(w + (size_t)R * p.cand * 8);
   launch_cfg<TOPK_SLICE>(1024, 16, dim3((unsigned)p.nslices, R), scores, stride, rr, a.k, p.slice,
-                         (int)p.nslices, kc, cs, ci, cn, nullptr, nullptr, stream);
+                         (int)p.nslices, kc, p.cand, cs, ci, cn, nullptr, nullptr, stream);
   int nt = 1024, v = 64;
   for (auto& c : kCfg)
     if ((int64_t)c[0] * c[1] >= p.cand) { nt = c[0]; v = c[1]; break; }
-  launch_cfg<TOPK_MERGE>(nt, v, dim3(1, R), scores, stride, rr, a.k, p.slice, (int)p.nslices, kc, cs, ci,
-                         cn, a.out_idx, a.out_score, stream);
+  launch_cfg<TOPK_MERGE>(nt, v, dim3(1, R), scores, stride, rr, a.k, p.slice, (int)p.nslices, kc, p.cand, cs,
+                         ci, cn, a.out_idx, a.out_score, stream);
   return hipGetLastError();
 }
 

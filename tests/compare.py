@@ -59,25 +59,33 @@ def assert_close(g, o, *, rtol=None, atol=None, what=""):
     return err
 
 
-def bf16_code_flips(gpu_vals, ora_raw, ora_rounded, mid_rtol=1e-5, magnitude=None):
-    """Count bf16 code mismatches, and those not explained by a near-midpoint value.
+def _spacing(y, sig_bits, min_normal_exp):
+    """Distance between consecutive representable values around y (the larger one at a binade edge)."""
+    _, e = np.frexp(np.asarray(y, np.float64))
+    e = np.maximum(e, min_normal_exp + 1)
+    return np.ldexp(1.0, e - sig_bits)
 
-    A mismatch is explained when the codes are one step apart and the oracle's
-    unrounded value lies within mid_rtol * magnitude of the midpoint between them;
-    `magnitude` is the scale of the rounding error of the value's computation
-    (for a weighted sum sum_i p_i v_i it is sum_i p_i |v_i|), default |value|.
+
+def rounding_mismatches(gpu_vals, ora_raw, ora_rounded, magnitude, fmt="bf16", rtol=1e-5):
+    """Stored values that differ from the oracle's rounding, and how many of those
+    are NOT a correct rounding of some value within rtol * magnitude of the oracle's
+    unrounded value (`magnitude` = scale of the computation's rounding error; for
+    a weighted sum sum_i p_i v_i it is sum_i p_i |v_i|).  Returns (n_diff, n_unexplained).
     """
-    from oracle import codecs  # test infrastructure
-    g = codecs.bf16_bits(gpu_vals).astype(np.int64)
-    o = codecs.bf16_bits(ora_rounded).astype(np.int64)
+    sig, emin = {"bf16": (8, -126), "e4m3": (4, -6)}[fmt]
+    g = np.asarray(gpu_vals, np.float64)
+    o = np.asarray(ora_rounded, np.float64)
     bad = g != o
     if not bad.any():
         return 0, 0
+    gb = g[bad]
     raw = np.asarray(ora_raw, np.float64)[bad]
-    mag = np.abs(raw) if magnitude is None else np.asarray(magnitude, np.float64)[bad]
-    gv = np.asarray(gpu_vals, np.float64)[bad]
-    ov = np.asarray(ora_rounded, np.float64)[bad]
-    mid = (gv + ov) / 2
-    near_mid = np.abs(raw - mid) <= mid_rtol * mag
-    one_step = np.abs(g[bad] - o[bad]) == 1
-    return int(bad.sum()), int((~(near_mid & one_step)).sum())
+    mag = np.asarray(magnitude, np.float64)[bad]
+    ok = np.abs(gb - raw) <= _spacing(gb, sig, emin) / 2 * (1 + 1e-12) + rtol * mag
+    return int(bad.sum()), int((~ok).sum())
+
+
+def bf16_code_flips(gpu_vals, ora_raw, ora_rounded, mid_rtol=1e-5, magnitude=None):
+    """bf16 form of rounding_mismatches (magnitude defaults to |value|)."""
+    mag = np.abs(np.asarray(ora_raw, np.float64)) if magnitude is None else magnitude
+    return rounding_mismatches(gpu_vals, ora_raw, ora_rounded, mag, "bf16", mid_rtol)

@@ -43,7 +43,7 @@ FAKE_ODD = 0x10004
 
 def pool(**kw):
     d = dict(val=FAKE, gate=FAKE, bpos=FAKE, out=FAKE, out_scale=None, E_cap=16, D=64, in_dtype=1, out_dtype=1,
-             reserved=0)
+             out_layout=0)
     d.update(kw)
     return _lib.PoolStream(**d)
 
@@ -55,6 +55,7 @@ def err(L):
 @pytest.mark.parametrize("kw,status", [
     (dict(val=None), 1), (dict(out=None), 1), (dict(in_dtype=2), 3), (dict(out_dtype=7), 3),
     (dict(D=48), 4), (dict(D=1024), 4), (dict(E_cap=3), 2), (dict(val=FAKE_ODD), 5),
+    (dict(out_layout=1, E_cap=48), 2), (dict(out_layout=7), 2),
 ])
 def test_compress_validation(L, kw, status):
     p = pool(**kw)
@@ -86,7 +87,7 @@ def idx_args(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), 1), (dict(out_idx=None), 1), (dict(k=0), 2), (dict(m=0), 2), (dict(E_cap=0), 2),
     (dict(q_dtype=0), 3), (dict(key_dtype=0), 3), (dict(H_I=48), 4), (dict(D_I=96), 4),
-    (dict(q_dtype=0, key_dtype=0, H_I=128, D_I=128), 4), (dict(keys=FAKE_ODD), 5),
+    (dict(q_dtype=0, key_dtype=0, H_I=128, D_I=128), 4), (dict(keys=FAKE_ODD), 5), (dict(E_cap=1000), 2),
     (dict(rows=_lib.Rows(None, 0, 2, 4095, 0, 0, 0)), 1), (dict(rows=_lib.Rows(FAKE, 0, 3, 4095, 0, 0, 0)), 2),
     (dict(rows=_lib.Rows(None, 1, 8, 0, 2, 0, 0)), 2), (dict(rows=_lib.Rows(None, 5, 8, 0, 0, 0, 0)), 2),
 ])

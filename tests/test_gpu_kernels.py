@@ -25,18 +25,11 @@ def setup_module(module):
 
 # ---------------------------------------------------------------- compression
 def e4m3_flips(gpu_codes, ora_codes, ora_unrounded, magnitude, mid_rtol=1e-5):
-    """Mismatched e4m3 codes not explained by an unrounded value next to a midpoint
-    (within mid_rtol of `magnitude`, the scale of the value's rounding error)."""
-    bad = gpu_codes != ora_codes
-    if not bad.any():
-        return 0, 0
-    g = codecs.e4m3_decode(gpu_codes[bad])
-    o = codecs.e4m3_decode(ora_codes[bad])
-    y = np.asarray(ora_unrounded, np.float64)[bad]
-    mid = (g + o) / 2
-    near = np.abs(y - mid) <= mid_rtol * np.asarray(magnitude, np.float64)[bad]
-    one_step = np.abs(gpu_codes[bad].astype(int) - ora_codes[bad].astype(int)) == 1
-    return int(bad.sum()), int((~(near & one_step)).sum())
+    """e4m3 codes that differ from the oracle's, and those not explained by the GPU's
+    fp32 error (within mid_rtol of `magnitude`) moving the value across a rounding boundary."""
+    from tests.compare import rounding_mismatches
+    return rounding_mismatches(codecs.e4m3_decode(gpu_codes), ora_unrounded, codecs.e4m3_decode(ora_codes),
+                               magnitude, "e4m3", mid_rtol)
 
 
 COMPRESS_CASES = [
@@ -51,6 +44,9 @@ COMPRESS_CASES = [
     (4, 4, 8, "bf16", "bf16", False, 3, 203),
     (2, 6, 16, "f32", "bf16", False, 2, 101),
 ]
+# key-tile output (the indexer stream): in, out, D, B, N
+TILED_CASES = [("bf16", "bf16", 128, 2, 4096), ("bf16", "e4m3", 128, 1, 1024), ("f32", "f32", 32, 1, 4096),
+               ("bf16", "bf16", 64, 1, 520)]
 
 
 @pytest.mark.parametrize("m,o,D,ins,outs,scaled,B,N", COMPRESS_CASES)
@@ -95,6 +91,42 @@ def test_compress_parity(m, o, D, ins, outs, scaled, B, N):
             assert n_unexplained == 0, f"{n_unexplained} of {n_bad} e4m3 codes differ"
 
 
+@pytest.mark.parametrize("ins,outs,D,B,N", TILED_CASES)
+def test_compress_key_tiles(ins, outs, D, B, N):
+    """The indexer stream written in the tiled key layout holds the same values as the rows layout."""
+    print(f"compress key tiles {ins}->{outs} D={D} B={B} N={N}", flush=True)
+    rng = np.random.default_rng(7 + D)
+    v, g = rng_store(rng, (B, N, D), ins), rng_store(rng, (B, N, D), ins, 2.0)
+    bpos = rng.normal(0, 0.5, (8, D)).astype(np.float32)
+    E = N // 4
+    Ec = (E + 31) // 32 * 32
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "e4m3": torch.uint8}[outs]
+    rows = torch.zeros(B, Ec, D, device=DEV, dtype=tdt)
+    tiles = torch.zeros(B, Ec // 32, D // 8, 32, 8, device=DEV, dtype=tdt)
+    if outs == "e4m3":
+        rows, tiles = rows.view(torch.float8_e4m3fn), tiles.view(torch.float8_e4m3fn)
+    vd, gd, bd = dev(v, ins), dev(g, ins), dev(bpos)
+    sk.csa_compress(sk.Pool(vd, gd, bd, rows), sk.Pool(vd, gd, bd, tiles, layout=sk.LAYOUT_KEY_TILES), m=4, o=4)
+    torch.cuda.synchronize()
+    back = sk.from_key_tiles(tiles)
+    if outs == "e4m3":
+        assert torch.equal(back.view(torch.uint8), rows.view(torch.uint8))
+    else:
+        assert torch.equal(back, rows)
+    # and the rows themselves follow the oracle
+    for b in range(B):
+        c = method.compress(v[b], g[b], bpos, 4, 4)
+        mag = method.compress(np.abs(v[b]), g[b], bpos, 4, 4)
+        got = host(rows[b])[:E]
+        if outs == "f32":
+            assert_close(got, c, rtol=1e-5, what="f32 keys")
+        elif outs == "bf16":
+            assert bf16_code_flips(got, c, method.store_keys(c, "bf16")["values"], magnitude=mag)[1] == 0
+        else:
+            st = method.store_keys(c, "e4m3")
+            assert e4m3_flips(got, st["codes"], c, mag)[1] == 0
+
+
 def test_compress_appends_only_requested_entries():
     rng = np.random.default_rng(5)
     B, N, D = 2, 256, 64
@@ -135,7 +167,8 @@ def _index_inputs(rng, keys_s, HI, DI, B, E_cap):
     else:
         kv = rng_store(rng, (B, E_cap, DI), keys_s)
         keys_dev = dev(kv, keys_s)
-    return q, w, kv.astype(np.float64), dev(q, qs), dev(w), keys_dev
+    # the indexer reads keys in the tiled layout
+    return q, w, kv.astype(np.float64), dev(q, qs), dev(w), sk.to_key_tiles(keys_dev)
 
 
 @pytest.mark.parametrize("keys_s,HI,DI,E_cap,positions,k", INDEX_CASES)
