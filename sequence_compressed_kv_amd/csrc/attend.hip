@@ -20,7 +20,7 @@
 
 namespace sckv {
 
-constexpr int kChunk = 32;
+constexpr int kPlanChunk = 64;    // split boundaries fall on multiples of this many items
 constexpr int kSegItems = 1024;   // item sources resolved per segment of a block's range
 
 struct AttendParams {
@@ -91,11 +91,11 @@ __device__ __forceinline__ void block_sources(const AttendParams& p, const RowIt
 // and, transposed in registers, as eight 8-byte cells (one dim, four items) of
 // the P.V operand.  Everything that needs the loaded values (masking, fp8
 // decoding) happens at store time, so issuing the loads never waits on them.
-template <int ENT, int D, int NW>
+template <int ENT, int D, int NW, int CH>
 struct Stage {
   static constexpr int NT = NW * kWave;
   static constexpr int PARTS = D / 8;                 // 8-dim parts per item row
-  static constexpr int NPAIR = (kChunk / 4) * PARTS;  // (item group, part) pairs per chunk
+  static constexpr int NPAIR = (CH / 4) * PARTS;      // (item group, part) pairs per chunk
   static constexpr int PPT = (NPAIR + NT - 1) / NT;   // pairs per thread
   u32x4 v[PPT][4];                                   // bf16 x 8: entries (BF16) or window rows
   u32x2 c[ENT == SCKV_E4M3 ? PPT : 1][4];            // e4m3 x 8 entry codes
@@ -103,11 +103,11 @@ struct Stage {
   int32_t src[PPT][4];                               // item sources (entry >= 0, window <= -2, none -1)
 };
 
-template <int ENT, int D, int NW>
+template <int ENT, int D, int NW, int CH>
 __device__ __forceinline__ void stage_load(const AttendParams& p, gbytes ent, gbytes win, gbytes esc,
                                            const RowItems& ri, const int32_t* srcs, int64_t q_rel, bool has_ent,
-                                           bool has_win, Stage<ENT, D, NW>& st) {
-  using S = Stage<ENT, D, NW>;
+                                           bool has_win, Stage<ENT, D, NW, CH>& st) {
+  using S = Stage<ENT, D, NW, CH>;
 #pragma unroll
   for (int s = 0; s < S::PPT; ++s) {
     const int pair = threadIdx.x + s * S::NT;
@@ -138,22 +138,26 @@ __device__ __forceinline__ void stage_load(const AttendParams& p, gbytes ent, gb
   }
 }
 
-template <int D>
+template <int D, int CH>
 struct Lds {
   static constexpr int KR_STRIDE = D + 8;   // bf16 elements per item row
-  uint16_t kr[kChunk * KR_STRIDE];
-  u32x2 vt[D * 8];                          // [dim][8 cells of 4 items] fp16, cells XOR-swizzled
-  float isc[kChunk];
+  static constexpr int CELLS = CH / 4;      // 4-item cells per dim row
+  uint16_t kr[CH * KR_STRIDE];
+  u32x2 vt[D * CELLS];                      // [dim][cells of 4 items] fp16, cells XOR-swizzled
+  float isc[CH];
 };
 
 // Cell position of items 4a .. 4a+3 in the row of dim d: spreads both the
 // transposed writes (dims 8p + e over lanes p) and the operand reads (dims
 // 16 nd + col over lanes col) over the LDS banks.
-__device__ __forceinline__ int vt_cell(int d, int a) { return d * 8 + (a ^ (((d >> 1) ^ (d >> 4)) & 7)); }
+template <int CH>
+__device__ __forceinline__ int vt_cell(int d, int a) {
+  return d * (CH / 4) + (a ^ (((d >> 1) ^ (d >> 4)) & 7));
+}
 
-template <int ENT, int D, int NW>
-__device__ __forceinline__ void stage_store(const Stage<ENT, D, NW>& st, Lds<D>& L) {
-  using S = Stage<ENT, D, NW>;
+template <int ENT, int D, int NW, int CH>
+__device__ __forceinline__ void stage_store(const Stage<ENT, D, NW, CH>& st, Lds<D, CH>& L) {
+  using S = Stage<ENT, D, NW, CH>;
 #pragma unroll
   for (int s = 0; s < S::PPT; ++s) {
     const int pair = threadIdx.x + s * S::NT;
@@ -175,7 +179,7 @@ __device__ __forceinline__ void stage_store(const Stage<ENT, D, NW>& st, Lds<D>&
           v[i] = u32x4{0u, 0u, 0u, 0u};
           sc[i] = 0.f;
         }
-        *reinterpret_cast<u32x4*>(&L.kr[(4 * a + i) * Lds<D>::KR_STRIDE + part * 8]) = v[i];
+        *reinterpret_cast<u32x4*>(&L.kr[(4 * a + i) * Lds<D, CH>::KR_STRIDE + part * 8]) = v[i];
       }
       // fp16 copies, transposed: cell (dim 8 part + e, group a) = items 4a .. 4a+3 of that dim
 #pragma unroll
@@ -185,7 +189,7 @@ __device__ __forceinline__ void stage_store(const Stage<ENT, D, NW>& st, Lds<D>&
         for (int i = 0; i < 4; ++i) f[i] = bf16_to_f32((v[i][e >> 1] >> ((e & 1) * 16)) & 0xffffu);
         const auto lo = __builtin_amdgcn_cvt_pkrtz(f[0], f[1]);
         const auto hi = __builtin_amdgcn_cvt_pkrtz(f[2], f[3]);
-        L.vt[vt_cell(part * 8 + e, a)] = u32x2{bitcast<uint32_t>(lo), bitcast<uint32_t>(hi)};
+        L.vt[vt_cell<CH>(part * 8 + e, a)] = u32x2{bitcast<uint32_t>(lo), bitcast<uint32_t>(hi)};
       }
       if (part == 0) {
 #pragma unroll
@@ -195,11 +199,13 @@ __device__ __forceinline__ void stage_store(const Stage<ENT, D, NW>& st, Lds<D>&
   }
 }
 
-template <int ENT, int D, int NW>
+template <int ENT, int D, int NW, int CH>
 __global__ __launch_bounds__(NW * 64) void attend_mfma(AttendParams p) {
   constexpr int KSQ = D / 32;      // k-steps of Q.K^T
   constexpr int ND = D / 16;       // 16-dim output tiles
-  __shared__ Lds<D> L;
+  constexpr int MT = CH / 16;      // 16-item tiles of a chunk
+  constexpr int KK = CH / 32;      // 32-item k-steps of P.V
+  __shared__ Lds<D, CH> L;
   __shared__ int32_t srcs[kSegItems];
 
   const int r = blockIdx.y, split = blockIdx.x;
@@ -208,8 +214,8 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma(AttendParams p) {
   const int col = l & 15, g = l >> 4;
   const int head = 16 * w + col;
 
-  const int64_t q_begin = (int64_t)split * p.per_split * kChunk;
-  int64_t q_end = q_begin + (int64_t)p.per_split * kChunk;
+  const int64_t q_begin = (int64_t)split * p.per_split;     // per_split: items, a multiple of 64
+  int64_t q_end = q_begin + p.per_split;
   q_end = q_end < ri.n_items ? q_end : ri.n_items;
 
   const gbytes gent = opaque_global(p.entries), gwin = opaque_global(p.win), gesc = opaque_global(p.escale);
@@ -233,29 +239,224 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma(AttendParams p) {
 
   // which kinds of item a chunk starting at q holds (uniform branches in stage_load)
   auto has_ent = [&](int64_t q) { return q < ri.n_list; };
-  auto has_win = [&](int64_t q) { return q + kChunk > ri.n_list; };
-  Stage<ENT, D, NW> st;
+  auto has_win = [&](int64_t q) { return q + CH > ri.n_list; };
+  Stage<ENT, D, NW, CH> st;
   for (int64_t s0 = q_begin; s0 < q_end; s0 += kSegItems) {
     const int64_t s1 = s0 + kSegItems < q_end ? s0 + kSegItems : q_end;
     // sources of this segment's items, padded with "nothing" to whole chunks
     __syncthreads();
-    block_sources(p, ri, r, s0, s0 + (s1 - s0 + kChunk - 1) / kChunk * kChunk, NW * kWave, srcs);
+    block_sources(p, ri, r, s0, s0 + (s1 - s0 + CH - 1) / CH * CH, NW * kWave, srcs);
     __syncthreads();
-    stage_load<ENT, D, NW>(p, gent, gwin, gesc, ri, srcs, 0, has_ent(s0), has_win(s0), st);
-  for (int64_t q0 = s0; q0 < s1; q0 += kChunk) {
-    __syncthreads();
-    stage_store<ENT, D, NW>(st, L);
-    __syncthreads();
-    if (q0 + kChunk < s1)
-      stage_load<ENT, D, NW>(p, gent, gwin, gesc, ri, srcs, q0 + kChunk - s0, has_ent(q0 + kChunk),
-                             has_win(q0 + kChunk), st);
+    stage_load<ENT, D, NW, CH>(p, gent, gwin, gesc, ri, srcs, 0, has_ent(s0), has_win(s0), st);
+    for (int64_t q0 = s0; q0 < s1; q0 += CH) {
+      __syncthreads();
+      stage_store<ENT, D, NW, CH>(st, L);
+      __syncthreads();
+      if (q0 + CH < s1)
+        stage_load<ENT, D, NW, CH>(p, gent, gwin, gesc, ri, srcs, q0 + CH - s0, has_ent(q0 + CH), has_win(q0 + CH),
+                                   st);
 
-    // S^T for the chunk: two 16-item tiles
-    f32x4 sacc[2];
+      // S^T for the chunk: MT tiles of 16 items
+      f32x4 sacc[MT];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const uint16_t* kr = &L.kr[(16 * mt + col) * Lds<D, CH>::KR_STRIDE + g * (D / 4)];
+#pragma unroll
+        for (int ks = 0; ks < KSQ; ++ks) {
+          const bf16x8 a = bitcast<bf16x8>(*reinterpret_cast<const u32x4*>(kr + 8 * ks));
+          acc = mfma16_bf16(a, bq[ks], acc);
+        }
+        sacc[mt] = acc;
+      }
+      // logits in the base-2 domain (scale * log2 e folded in), chunk maximum per head
+      float x[4 * MT], isc[4 * MT];
+      float cmax = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float sc = L.isc[16 * mt + 4 * g + i];
+          isc[4 * mt + i] = sc;
+          const float v = sc != 0.f ? sacc[mt][i] * (scale2 * sc) : -INFINITY;
+          x[4 * mt + i] = v;
+          cmax = fmaxf(cmax, v);
+        }
+      cmax = fmaxf(cmax, shfl_xor_f(cmax, 16));
+      cmax = fmaxf(cmax, shfl_xor_f(cmax, 32));
+      const float m_new = fmaxf(m_run, cmax);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const bool grows = m_new > m_run;                  // this head's running maximum moved
+      const float alpha = grows ? (m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new)) : 1.f;
+      m_run = m_new;
+      // P as the A operand of P.V: k-step kk takes items 32kk + {4g..4g+3} (tile 2kk)
+      // and 32kk + 16 + {4g..4g+3} (tile 2kk+1), the order of the S^T registers
+      f16x8 pa[KK];
+      float psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4 * MT; ++e) {
+        const float pe = __builtin_amdgcn_exp2f(x[e] - m_use);
+        psum += pe;
+        pa[e / 8][e % 8] = (_Float16)(ENT == SCKV_E4M3 ? pe * isc[e] : pe);
+      }
+      l_run = l_run * alpha + psum;
+      // rescale the output rows (heads 4g + i of this wave) only when some maximum moved
+      if (__any(grows)) {
+        float al[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i, kWave);
+#pragma unroll
+        for (int nd = 0; nd < ND; ++nd)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[nd][i] *= al[i];
+      }
+#pragma unroll
+      for (int nd = 0; nd < ND; ++nd) {
+        const int d = 16 * nd + col;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const u32x2 lo = L.vt[vt_cell<CH>(d, 8 * kk + g)];
+          const u32x2 hi = L.vt[vt_cell<CH>(d, 8 * kk + 4 + g)];
+          const f16x8 bv = bitcast<f16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
+          o[nd] = mfma16_f16(pa[kk], bv, o[nd]);
+        }
+      }
+    }
+  }
+
+  // per-head totals
+  float l_tot = l_run;
+  l_tot += shfl_xor_f(l_tot, 16);
+  l_tot += shfl_xor_f(l_tot, 32);
+  float lrow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lrow[i] = __shfl(l_tot, 4 * g + i, kWave);
+  const int hbase = 16 * w + 4 * g;
+  if (p.nsplit == 1) {
+#pragma unroll
+    for (int nd = 0; nd < ND; ++nd)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float v = o[nd][i] / lrow[i];
+        const int64_t off = ((int64_t)r * p.H + hbase + i) * D + 16 * nd + col;
+        if (p.out_dtype == SCKV_BF16) static_cast<uint16_t*>(p.out)[off] = (uint16_t)f32_to_bf16_rne(v);
+        else static_cast<float*>(p.out)[off] = v;
+      }
+    if (p.lse && g == 0) p.lse[(int64_t)r * p.H + head] = (m_run + log2f(l_tot)) * 0.6931471805599453f;
+  } else {
+    const int64_t sbase = ((int64_t)r * p.nsplit + split) * p.H;
+#pragma unroll
+    for (int nd = 0; nd < ND; ++nd)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p.ws_o[(sbase + hbase + i) * D + 16 * nd + col] = o[nd][i];
+    if (g == 0) {
+      p.ws_ml[(sbase + head) * 2] = m_run;
+      p.ws_ml[(sbase + head) * 2 + 1] = l_tot;
+    }
+  }
+}
+
+// bf16 entries and window with D = 512 (the MLA-style latent): items travel
+// global -> LDS by asynchronous copies (one 1 KB row per wavefront instruction)
+// into three 32-item stages, so two chunks are in flight while a third is
+// multiplied, without staging registers.  Waits are explicit: before a chunk is
+// used each wave waits until only the next chunk's copies are outstanding.
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void attend_dma512(AttendParams p) {
+  constexpr int D = 512, CH = 32, KSQ = D / 32, ND = D / 16, MT = 2;
+  constexpr int KRS = D + 8;                 // padded LDS row (bf16 elements)
+  constexpr int NT = NW * kWave;
+  constexpr int RPW = CH / NW;               // rows copied per wave per chunk
+  constexpr int PPT = (8 * 64 + NT - 1) / NT;  // (item group, part) pairs per thread for the transposed copy
+  __shared__ __attribute__((aligned(16))) uint16_t st0[CH * KRS];
+  __shared__ __attribute__((aligned(16))) uint16_t st1[CH * KRS];
+  __shared__ __attribute__((aligned(16))) uint16_t st2[CH * KRS];
+  __shared__ u32x2 vt[D * 8];
+  __shared__ float isc[3][CH];
+  __shared__ int32_t srcs[kSegItems];
+
+  const int r = blockIdx.y, split = blockIdx.x;
+  const RowItems ri = row_items(p, r);
+  const int l = lane_id(), w = wave_id();
+  const int col = l & 15, g = l >> 4;
+  const int head = 16 * w + col;
+
+  const int64_t q_begin = (int64_t)split * p.per_split;
+  int64_t q_end = q_begin + p.per_split;
+  q_end = q_end < ri.n_items ? q_end : ri.n_items;
+
+  const gbytes gent = opaque_global(p.entries), gwin = opaque_global(p.win);
+  bf16x8 bq[KSQ];
+  {
+    const gbytes gq = opaque_global(p.q);
+    const int64_t e0 = ((int64_t)r * p.H + head) * D + g * (D / 4);
+#pragma unroll
+    for (int ks = 0; ks < KSQ; ++ks) bq[ks] = bitcast<bf16x8>(gload<u32x4>(gq, (e0 + 8 * ks) * 2));
+#pragma unroll
+    for (int ks = 0; ks < KSQ; ++ks) pin(bq[ks]);
+  }
+  f32x4 o[ND];
+#pragma unroll
+  for (int nd = 0; nd < ND; ++nd) o[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float scale2 = p.scale * 1.4426950408889634f;
+
+  // copies of chunk q_rel (relative to the segment's sources) into stage S
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  // the sequence's first entry / window row, held in scalar registers
+  gbytes gent_row = gent + ri.seq * p.E_cap * (D * 2), gwin_row = gwin + ri.seq * p.R_w * (D * 2);
+  asm volatile("" : "+s"(gent_row));
+  asm volatile("" : "+s"(gwin_row));
+  auto issue = [&](int64_t q_rel, uint16_t* S, float* iscS) {
+    const int32_t my_src = srcs[q_rel + wu * RPW + (l % RPW)];   // lane i holds row i's source
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int c = wu * RPW + i;
+      const int32_t sv = __builtin_amdgcn_readlane(my_src, i);    // one row per instruction
+      const bool is_win = sv <= -2;
+      const gbytes src = is_win ? gwin_row + (int64_t)(-2 - sv) * (D * 2)
+                                : gent_row + (int64_t)(sv >= 0 ? sv : 0) * (D * 2);
+      copy_to_lds16(src + l * 16, &S[c * KRS]);
+      if (l == 0) iscS[c] = sv == -1 ? 0.f : 1.f;
+    }
+  };
+
+  // one chunk: wait for its copies, build the transposed fp16 operand, multiply
+  auto step = [&](int c, int nch, int64_t q_rel_next2, uint16_t* S, const float* iscS, uint16_t* S2,
+                  float* isc2) {
+    if (c + 1 < nch) wait_vm_lgkm<RPW, 0>();
+    else wait_vm_lgkm<0, 0>();
+    block_barrier();                                           // chunk c visible; stage of c-1 free
+    if (c + 2 < nch) issue(q_rel_next2, S2, isc2);
+#pragma unroll
+    for (int s = 0; s < PPT; ++s) {
+      const int pair = threadIdx.x + s * NT;
+      if (pair < 8 * 64) {
+        const int part = pair % 64, a = pair / 64;
+        u32x4 v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[i] = *reinterpret_cast<const u32x4*>(&S[(4 * a + i) * KRS + part * 8]);
+          if (iscS[4 * a + i] == 0.f) v[i] = u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float f[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) f[i] = bf16_to_f32((v[i][e >> 1] >> ((e & 1) * 16)) & 0xffffu);
+          const auto lo = __builtin_amdgcn_cvt_pkrtz(f[0], f[1]);
+          const auto hi = __builtin_amdgcn_cvt_pkrtz(f[2], f[3]);
+          vt[vt_cell<CH>(part * 8 + e, a)] = u32x2{bitcast<uint32_t>(lo), bitcast<uint32_t>(hi)};
+        }
+      }
+    }
+    wait_vm_lgkm<63, 0>();
+    block_barrier();                                           // transposed operand visible
+    f32x4 sacc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const uint16_t* kr = &L.kr[(16 * mt + col) * Lds<D>::KR_STRIDE + g * (D / 4)];
+      const uint16_t* kr = &S[(16 * mt + col) * KRS + g * (D / 4)];
 #pragma unroll
       for (int ks = 0; ks < KSQ; ++ks) {
         const bf16x8 a = bitcast<bf16x8>(*reinterpret_cast<const u32x4*>(kr + 8 * ks));
@@ -263,16 +464,13 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma(AttendParams p) {
       }
       sacc[mt] = acc;
     }
-    // logits in the base-2 domain (scale * log2 e folded in), chunk maximum per head
-    float x[8], isc[8];
+    float x[8];
     float cmax = -INFINITY;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float sc = L.isc[16 * mt + 4 * g + i];
-        isc[4 * mt + i] = sc;
-        const float v = sc != 0.f ? sacc[mt][i] * (scale2 * sc) : -INFINITY;
+        const float v = iscS[16 * mt + 4 * g + i] != 0.f ? sacc[mt][i] * scale2 : -INFINITY;
         x[4 * mt + i] = v;
         cmax = fmaxf(cmax, v);
       }
@@ -280,7 +478,7 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma(AttendParams p) {
     cmax = fmaxf(cmax, shfl_xor_f(cmax, 32));
     const float m_new = fmaxf(m_run, cmax);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const bool grows = m_new > m_run;                  // this head's running maximum moved
+    const bool grows = m_new > m_run;
     const float alpha = grows ? (m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new)) : 1.f;
     m_run = m_new;
     f16x8 pa;
@@ -289,10 +487,9 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma(AttendParams p) {
     for (int e = 0; e < 8; ++e) {
       const float pe = __builtin_amdgcn_exp2f(x[e] - m_use);
       psum += pe;
-      pa[e] = (_Float16)(ENT == SCKV_E4M3 ? pe * isc[e] : pe);
+      pa[e] = (_Float16)pe;
     }
     l_run = l_run * alpha + psum;
-    // rescale the output rows (heads 4g + i of this wave) only when some maximum moved
     if (__any(grows)) {
       float al[4];
 #pragma unroll
@@ -305,15 +502,27 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma(AttendParams p) {
 #pragma unroll
     for (int nd = 0; nd < ND; ++nd) {
       const int d = 16 * nd + col;
-      const u32x2 lo = L.vt[vt_cell(d, g)];
-      const u32x2 hi = L.vt[vt_cell(d, 4 + g)];
-      const f16x8 bv = bitcast<f16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
-      o[nd] = mfma16_f16(pa, bv, o[nd]);
+      const u32x2 lo = vt[vt_cell<CH>(d, g)];
+      const u32x2 hi = vt[vt_cell<CH>(d, 4 + g)];
+      o[nd] = mfma16_f16(pa, bitcast<f16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]}), o[nd]);
+    }
+  };
+
+  for (int64_t s0 = q_begin; s0 < q_end; s0 += kSegItems) {
+    const int64_t s1 = s0 + kSegItems < q_end ? s0 + kSegItems : q_end;
+    const int nch = (int)((s1 - s0 + CH - 1) / CH);
+    __syncthreads();
+    block_sources(p, ri, r, s0, s0 + (int64_t)nch * CH, NT, srcs);
+    __syncthreads();
+    issue(0, st0, isc[0]);
+    if (nch > 1) issue(CH, st1, isc[1]);
+    for (int c = 0; c < nch; c += 3) {
+      step(c, nch, (int64_t)(c + 2) * CH, st0, isc[0], st2, isc[2]);
+      if (c + 1 < nch) step(c + 1, nch, (int64_t)(c + 3) * CH, st1, isc[1], st0, isc[0]);
+      if (c + 2 < nch) step(c + 2, nch, (int64_t)(c + 4) * CH, st2, isc[2], st1, isc[1]);
     }
   }
-  }
 
-  // per-head totals
   float l_tot = l_run;
   l_tot += shfl_xor_f(l_tot, 16);
   l_tot += shfl_xor_f(l_tot, 32);
@@ -477,7 +686,7 @@ AttendPlan plan_attend(const sckv_attend_args& a, bool csa) {
   int64_t ev = entries_visible(t, a.m, a.W);
   ev = ev < a.E_cap ? ev : a.E_cap;
   pl.items = (csa ? a.k : ev) + a.W;
-  pl.chunks = (pl.items + kChunk - 1) / kChunk;
+  pl.chunks = (pl.items + kPlanChunk - 1) / kPlanChunk;
   pl.mfma = a.entry_dtype != SCKV_F32;
   if (!pl.mfma) {
     pl.nsplit = 1;
@@ -485,14 +694,15 @@ AttendPlan plan_attend(const sckv_attend_args& a, bool csa) {
     pl.ok = true;
     return pl;
   }
-  const int64_t target_blocks = 512;
-  int64_t ns = (target_blocks + a.rows.R - 1) / a.rows.R;
+  // about one block per CU (256): splits per row, each of at least two chunks
+  const int64_t target_blocks = 256;
+  int64_t ns = (target_blocks + a.rows.R / 2) / a.rows.R;
   ns = ns < 1 ? 1 : (ns > pl.chunks ? pl.chunks : ns);
   int64_t per = (pl.chunks + ns - 1) / ns;
-  const int64_t min_per = pl.chunks < 8 ? pl.chunks : 8;
+  const int64_t min_per = pl.chunks < 2 ? pl.chunks : 2;
   per = per < min_per ? min_per : per;
   per = per < 1 ? 1 : per;
-  pl.per_split = per;
+  pl.per_split = per * kPlanChunk;       // in items
   pl.nsplit = (int32_t)((pl.chunks + per - 1) / per);
   if (pl.nsplit < 1) pl.nsplit = 1;
   if (pl.nsplit > 1)
@@ -503,11 +713,22 @@ AttendPlan plan_attend(const sckv_attend_args& a, bool csa) {
 
 template <int ENT, int D>
 static void launch_mfma_d(const AttendParams& p, int H, dim3 grid, hipStream_t s) {
-  switch (H / 16) {
-    case 1: hipLaunchKernelGGL((attend_mfma<ENT, D, 1>), grid, dim3(64), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((attend_mfma<ENT, D, 2>), grid, dim3(128), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((attend_mfma<ENT, D, 4>), grid, dim3(256), 0, s, p); break;
-    default: hipLaunchKernelGGL((attend_mfma<ENT, D, 8>), grid, dim3(512), 0, s, p); break;
+  if constexpr (ENT == SCKV_BF16 && D == 512) {
+    switch (H / 16) {
+      case 1: hipLaunchKernelGGL(attend_dma512<1>, grid, dim3(64), 0, s, p); break;
+      case 2: hipLaunchKernelGGL(attend_dma512<2>, grid, dim3(128), 0, s, p); break;
+      case 4: hipLaunchKernelGGL(attend_dma512<4>, grid, dim3(256), 0, s, p); break;
+      default: hipLaunchKernelGGL(attend_dma512<8>, grid, dim3(512), 0, s, p); break;
+    }
+  } else {
+    // register-staged chunks: 64 items when the latent is narrow, 32 at D = 512
+    constexpr int CH = D <= 256 ? 64 : 32;
+    switch (H / 16) {
+      case 1: hipLaunchKernelGGL((attend_mfma<ENT, D, 1, CH>), grid, dim3(64), 0, s, p); break;
+      case 2: hipLaunchKernelGGL((attend_mfma<ENT, D, 2, CH>), grid, dim3(128), 0, s, p); break;
+      case 4: hipLaunchKernelGGL((attend_mfma<ENT, D, 4, CH>), grid, dim3(256), 0, s, p); break;
+      default: hipLaunchKernelGGL((attend_mfma<ENT, D, 8, CH>), grid, dim3(512), 0, s, p); break;
+    }
   }
 }
 
@@ -544,7 +765,7 @@ hipError_t launch_attend(const sckv_attend_args& a, bool csa, const AttendPlan& 
   p.csa = csa ? 1 : 0;
   p.out_dtype = a.out_dtype;
   p.nsplit = pl.nsplit;
-  p.per_split = (int32_t)pl.per_split;
+  p.per_split = (int32_t)pl.per_split;   // items
   p.scale = a.softmax_scale;
   if (pl.nsplit > 1) {
     p.ws_o = static_cast<float*>(ws);

@@ -133,6 +133,42 @@ __device__ __forceinline__ void pin(T& v) {
   v = __builtin_bit_cast(T, x);
 }
 
+// ------------------------------------------------------------------ asynchronous global -> LDS copies
+// One instruction copies 16 bytes per lane (1 KB per wavefront) from global memory
+// straight into LDS at lds_row + 16 * lane (lds_row must be wave-uniform).  The
+// copy is tracked by the vector-memory counter only: consumers wait with
+// wait_vm_lgkm() and publish with block_barrier().
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+//
+// The copy is written as inline assembly on purpose: the compiler then does not
+// see an asynchronous LDS writer, so it does not make every later LDS read wait
+// for all copies in flight (which would leave nothing in flight during the
+// math).  The caller owns the waits.  lds_row must be wave-uniform.
+__device__ __forceinline__ void copy_to_lds16(gbytes src, void* lds_row) {
+  const uint32_t dst = (uint32_t)reinterpret_cast<uintptr_t>((lds_ptr)lds_row);
+  const uint64_t addr = reinterpret_cast<uint64_t>(src);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(addr), "s"(dst) : "memory", "m0");
+}
+
+// s_waitcnt: at most VM vector-memory operations and LGKM LDS/scalar operations
+// still outstanding (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
+template <int VM, int LGKM>
+__device__ __forceinline__ void wait_vm_lgkm() {
+  static_assert(VM >= 0 && VM < 64 && LGKM >= 0 && LGKM < 16, "counter range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (LGKM << 8) | ((VM >> 4) << 14));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (which would wait
+// for every copy still in flight).  The empty asm statements keep the compiler
+// from moving memory operations across it; the hardware ordering comes from an
+// explicit wait_vm_lgkm() before it.
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ------------------------------------------------------------------ wave / block helpers
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 __device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }

@@ -44,8 +44,8 @@ hipError_t launch_topk(const sckv_index_args& a, const float* scores, int64_t st
 // ---------------------------------------------------------------- attention
 struct AttendPlan {
   int64_t items = 0;        // widest row: listed/visible entries + window
-  int64_t chunks = 0;       // items / 32 rounded up
-  int64_t per_split = 0;    // chunks per split
+  int64_t chunks = 0;       // items / 64 rounded up
+  int64_t per_split = 0;    // items per split (a multiple of 64)
   int32_t nsplit = 1;
   bool mfma = false;
   size_t ws_bytes = 0;      // split partials (0 when nsplit == 1)

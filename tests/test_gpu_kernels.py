@@ -327,3 +327,33 @@ def test_attend_causal_rows_and_determinism():
         items = np.concatenate([ent[0][sel], v[0][method.window_positions(t, 128)]])
         o, _, _ = method.attend(q[t], items, 1 / math.sqrt(128))
         assert_close(go[t], o, atol=2e-2, what=f"row {t}")
+
+
+def test_attend_rows_longer_than_a_segment():
+    """Causal rows whose item lists (k + window) exceed one block's source segment."""
+    rng = np.random.default_rng(10)
+    T, H, D, E_cap, k = 520, 64, 512, 1500, 1100
+    t0 = 5000                                    # rows are positions t0 .. t0 + T - 1
+    q = rng_store(rng, (T, H, D), "bf16", 0.3)
+    ent = rng_store(rng, (1, E_cap, D), "bf16").astype(np.float64)
+    v = rng_store(rng, (1, t0 + T, D), "bf16")
+    idx_np = np.full((T, k), -1, np.int64)
+    for r in range(T):
+        ev = min(method.entries_visible(t0 + r, 4, 128), E_cap)
+        n = min(k - (r % 7) * 50, ev)            # some rows padded with -1
+        sel = np.sort(rng.choice(ev, size=n, replace=False))
+        idx_np[r, :n] = sel
+    rows = sk.RowSpec.causal(T, pos0=t0)
+    out = torch.zeros(T, H, D, device=DEV, dtype=torch.float32)
+    lse = torch.zeros(T, H, device=DEV, dtype=torch.float32)
+    sk.csa_attend(rows, dev(q, "bf16"), dev(ent, "bf16"), dev_i32(idx_np), dev(v, "bf16"), out, m=4, W=128,
+                  softmax_scale=1 / math.sqrt(128), lse=lse)
+    torch.cuda.synchronize()
+    go, gl = host(out), host(lse)
+    for r in [0, 1, 6, 77, 300, T - 1]:
+        t = t0 + r
+        sel = idx_np[r][idx_np[r] >= 0]
+        items = np.concatenate([ent[0][sel], v[0][method.window_positions(t, 128)]])
+        o, lse_o, _ = method.attend(q[r], items, 1 / math.sqrt(128))
+        assert_close(go[r], o, atol=2e-2, what=f"row {r}")
+        np.testing.assert_allclose(gl[r], lse_o, rtol=1e-5, atol=1e-5)
