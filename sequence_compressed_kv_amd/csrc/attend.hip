@@ -361,17 +361,25 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma(AttendParams p) {
 // into three 32-item stages, so two chunks are in flight while a third is
 // multiplied, without staging registers.  Waits are explicit: before a chunk is
 // used each wave waits until only the next chunk's copies are outstanding.
+//
+// Both products read the same staged rows.  Q.K^T takes row fragments (one item,
+// eight dims per lane).  P.V needs the transpose (one dim, eight items per lane):
+// the gfx950 transposing LDS read delivers it directly.  Within each 16-lane
+// group, lane 4r + c receives element c of the 8-byte words addressed by lanes
+// r, r + 4, r + 8 and r + 12 of the group.  So lane a of group g points at item
+// 4g + a/4, dims 4(a%4) .. +3, and lane n of the group comes back holding dim n
+// of items 4g .. 4g + 3, the k-group layout of the P operand.  P is rounded to
+// bf16 for that product; the normaliser (and the log-sum-exp) sums the
+// unrounded fp32 probabilities.
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void attend_dma512(AttendParams p) {
   constexpr int D = 512, CH = 32, KSQ = D / 32, ND = D / 16, MT = 2;
   constexpr int KRS = D + 8;                 // padded LDS row (bf16 elements)
   constexpr int NT = NW * kWave;
   constexpr int RPW = CH / NW;               // rows copied per wave per chunk
-  constexpr int PPT = (8 * 64 + NT - 1) / NT;  // (item group, part) pairs per thread for the transposed copy
   __shared__ __attribute__((aligned(16))) uint16_t st0[CH * KRS];
   __shared__ __attribute__((aligned(16))) uint16_t st1[CH * KRS];
   __shared__ __attribute__((aligned(16))) uint16_t st2[CH * KRS];
-  __shared__ u32x2 vt[D * 8];
   __shared__ float isc[3][CH];
   __shared__ int32_t srcs[kSegItems];
 
@@ -401,68 +409,59 @@ __global__ __launch_bounds__(NW * 64) void attend_dma512(AttendParams p) {
   float m_run = -INFINITY, l_run = 0.f;
   const float scale2 = p.scale * 1.4426950408889634f;
 
-  // copies of chunk q_rel (relative to the segment's sources) into stage S
   const int wu = __builtin_amdgcn_readfirstlane(w);
   // the sequence's first entry / window row, held in scalar registers
   gbytes gent_row = gent + ri.seq * p.E_cap * (D * 2), gwin_row = gwin + ri.seq * p.R_w * (D * 2);
   asm volatile("" : "+s"(gent_row));
   asm volatile("" : "+s"(gwin_row));
-  auto issue = [&](int64_t q_rel, uint16_t* S, float* iscS) {
+  // items without a source copy the row's own token (always present) so that
+  // every staged value is finite; their logits are masked
+  const int32_t t_slot = (int32_t)(ri.t % p.R_w);
+
+  // copies of chunk q_rel (relative to the segment's sources) into stage S
+  auto issue = [&](int64_t q_rel, uint16_t* S, float* iscS) __attribute__((always_inline)) {
     const int32_t my_src = srcs[q_rel + wu * RPW + (l % RPW)];   // lane i holds row i's source
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
       const int c = wu * RPW + i;
       const int32_t sv = __builtin_amdgcn_readlane(my_src, i);    // one row per instruction
-      const bool is_win = sv <= -2;
-      const gbytes src = is_win ? gwin_row + (int64_t)(-2 - sv) * (D * 2)
-                                : gent_row + (int64_t)(sv >= 0 ? sv : 0) * (D * 2);
+      const gbytes src = sv >= 0 ? gent_row + (int64_t)sv * (D * 2)
+                                 : gwin_row + (int64_t)(sv <= -2 ? -2 - sv : t_slot) * (D * 2);
       copy_to_lds16(src + l * 16, &S[c * KRS]);
       if (l == 0) iscS[c] = sv == -1 ? 0.f : 1.f;
     }
   };
 
-  // one chunk: wait for its copies, build the transposed fp16 operand, multiply
+  // one chunk: wait for its copies, multiply
   auto step = [&](int c, int nch, int64_t q_rel_next2, uint16_t* S, const float* iscS, uint16_t* S2,
-                  float* isc2) {
+                  float* isc2) __attribute__((always_inline)) {
     if (c + 1 < nch) wait_vm_lgkm<RPW, 0>();
     else wait_vm_lgkm<0, 0>();
     block_barrier();                                           // chunk c visible; stage of c-1 free
     if (c + 2 < nch) issue(q_rel_next2, S2, isc2);
-#pragma unroll
-    for (int s = 0; s < PPT; ++s) {
-      const int pair = threadIdx.x + s * NT;
-      if (pair < 8 * 64) {
-        const int part = pair % 64, a = pair / 64;
-        u32x4 v[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[i] = *reinterpret_cast<const u32x4*>(&S[(4 * a + i) * KRS + part * 8]);
-          if (iscS[4 * a + i] == 0.f) v[i] = u32x4{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float f[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) f[i] = bf16_to_f32((v[i][e >> 1] >> ((e & 1) * 16)) & 0xffffu);
-          const auto lo = __builtin_amdgcn_cvt_pkrtz(f[0], f[1]);
-          const auto hi = __builtin_amdgcn_cvt_pkrtz(f[2], f[3]);
-          vt[vt_cell<CH>(part * 8 + e, a)] = u32x2{bitcast<uint32_t>(lo), bitcast<uint32_t>(hi)};
-        }
-      }
-    }
-    wait_vm_lgkm<63, 0>();
-    block_barrier();                                           // transposed operand visible
+
+    // S^T = K Q^T: item fragments are read in batches of 8 k-steps, the next
+    // batch in flight while the current one is multiplied
     f32x4 sacc[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const uint16_t* kr = &S[(16 * mt + col) * KRS + g * (D / 4)];
+    for (int mt = 0; mt < MT; ++mt) sacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    constexpr int KB = 8, NB = MT * KSQ / KB;
+    bf16x8 fa[2][KB];
+    auto read_batch = [&](int b, bf16x8 (&f)[KB]) {
+      const int mt = b / (KSQ / KB), k0 = (b % (KSQ / KB)) * KB;
+      const uint16_t* kr = &S[(16 * mt + col) * KRS + g * (D / 4) + 8 * k0];
 #pragma unroll
-      for (int ks = 0; ks < KSQ; ++ks) {
-        const bf16x8 a = bitcast<bf16x8>(*reinterpret_cast<const u32x4*>(kr + 8 * ks));
-        acc = mfma16_bf16(a, bq[ks], acc);
-      }
-      sacc[mt] = acc;
+      for (int j = 0; j < KB; ++j) f[j] = bitcast<bf16x8>(*reinterpret_cast<const u32x4*>(kr + 8 * j));
+    };
+    read_batch(0, fa[0]);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+      for (int j = 0; j < KB; ++j) pin(fa[b & 1][j]);
+      if (b + 1 < NB) read_batch(b + 1, fa[(b + 1) & 1]);
+      const int mt = b / (KSQ / KB), k0 = (b % (KSQ / KB)) * KB;
+#pragma unroll
+      for (int j = 0; j < KB; ++j) sacc[mt] = mfma16_bf16(fa[b & 1][j], bq[k0 + j], sacc[mt]);
     }
     float x[8];
     float cmax = -INFINITY;
@@ -476,18 +475,20 @@ __global__ __launch_bounds__(NW * 64) void attend_dma512(AttendParams p) {
       }
     cmax = fmaxf(cmax, shfl_xor_f(cmax, 16));
     cmax = fmaxf(cmax, shfl_xor_f(cmax, 32));
-    const float m_new = fmaxf(m_run, cmax);
+    // the reference maximum moves only when a logit exceeds it by more than
+    // 2^8 (probabilities then stay below 256): the output is rescaled rarely
+    const bool grows = cmax > m_run + 8.f;
+    const float m_new = grows ? cmax : m_run;
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const bool grows = m_new > m_run;
     const float alpha = grows ? (m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new)) : 1.f;
     m_run = m_new;
-    f16x8 pa;
+    bf16x8 pa;
     float psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float pe = __builtin_amdgcn_exp2f(x[e] - m_use);
       psum += pe;
-      pa[e] = (_Float16)pe;
+      pa[e] = (__bf16)pe;
     }
     l_run = l_run * alpha + psum;
     if (__any(grows)) {
@@ -499,12 +500,14 @@ __global__ __launch_bounds__(NW * 64) void attend_dma512(AttendParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[nd][i] *= al[i];
     }
+    // O += P V: B fragments by transposing reads of the staged rows
+    const lds_ptr v0 = (lds_ptr)&S[(4 * g + (col >> 2)) * KRS + 4 * (col & 3)];
+    const lds_ptr v1 = (lds_ptr)&S[(16 + 4 * g + (col >> 2)) * KRS + 4 * (col & 3)];
 #pragma unroll
     for (int nd = 0; nd < ND; ++nd) {
-      const int d = 16 * nd + col;
-      const u32x2 lo = vt[vt_cell<CH>(d, g)];
-      const u32x2 hi = vt[vt_cell<CH>(d, 4 + g)];
-      o[nd] = mfma16_f16(pa, bitcast<f16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]}), o[nd]);
+      const u32x2 lo = lds_read_tr16(v0, 32 * nd);
+      const u32x2 hi = lds_read_tr16(v1, 32 * nd);
+      o[nd] = mfma16_bf16(pa, bitcast<bf16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]}), o[nd]);
     }
   };
 
@@ -713,13 +716,8 @@ AttendPlan plan_attend(const sckv_attend_args& a, bool csa) {
 
 template <int ENT, int D>
 static void launch_mfma_d(const AttendParams& p, int H, dim3 grid, hipStream_t s) {
-  if constexpr (ENT == SCKV_BF16 && D == 512) {
-    switch (H / 16) {
-      case 1: hipLaunchKernelGGL(attend_dma512<1>, grid, dim3(64), 0, s, p); break;
-      case 2: hipLaunchKernelGGL(attend_dma512<2>, grid, dim3(128), 0, s, p); break;
-      case 4: hipLaunchKernelGGL(attend_dma512<4>, grid, dim3(256), 0, s, p); break;
-      default: hipLaunchKernelGGL(attend_dma512<8>, grid, dim3(512), 0, s, p); break;
-    }
+  if (ENT == SCKV_BF16 && D == 512 && H == 64) {
+    hipLaunchKernelGGL(attend_dma512<4>, grid, dim3(256), 0, s, p);
   } else {
     // register-staged chunks: 64 items when the latent is narrow, 32 at D = 512
     constexpr int CH = D <= 256 ? 64 : 32;

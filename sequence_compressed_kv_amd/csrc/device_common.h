@@ -151,6 +151,17 @@ __device__ __forceinline__ void copy_to_lds16(gbytes src, void* lds_row) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(addr), "s"(dst) : "memory", "m0");
 }
 
+// gfx950 transposing LDS read of four 16-bit values per lane (see the P.V
+// operand in the attention kernel for the lane mapping); byte_off is a
+// compile-time offset added to every lane's address.
+__device__ __forceinline__ u32x2 lds_read_tr16(lds_ptr base, int byte_off) {
+  typedef __attribute__((ext_vector_type(4))) short s16x4;
+  typedef __attribute__((address_space(3))) s16x4* lds_s16x4;
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4)((__attribute__((address_space(3))) uint8_t*)base + byte_off));
+  return __builtin_bit_cast(u32x2, v);
+}
+
 // s_waitcnt: at most VM vector-memory operations and LGKM LDS/scalar operations
 // still outstanding (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
 template <int VM, int LGKM>
