@@ -38,6 +38,7 @@ struct AttendParams {
   int32_t kind, pos_max, seq0, pos0;
   int32_t H, m, W, k;
   int32_t csa, out_dtype, nsplit, per_split;
+  int32_t rows_R;
   float scale;
 };
 
@@ -356,11 +357,49 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma(AttendParams p) {
   }
 }
 
-// bf16 entries and window with D = 512 (the MLA-style latent): items travel
-// global -> LDS by asynchronous copies (one 1 KB row per wavefront instruction)
-// into three 32-item stages, so two chunks are in flight while a third is
-// multiplied, without staging registers.  Waits are explicit: before a chunk is
-// used each wave waits until only the next chunk's copies are outstanding.
+// maximum over the four 16-lane groups (lanes l, l^16, l^32, l^48)
+__device__ __forceinline__ float group_max4(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Sources of items [q_begin, q_end) (at most PER * NT of them) into srcs: every
+// index-list load is issued before any is used, so the whole table costs one
+// memory round trip.  Positions and ring sizes fit 32 bits here.
+template <int PER, int NT>
+__device__ __forceinline__ void block_sources_batched(const AttendParams& p, const RowItems& ri, int r,
+                                                      int64_t q_begin, int64_t q_end, int32_t* srcs) {
+  int32_t j[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int64_t q = q_begin + threadIdx.x + u * NT;
+    const bool listed = q < ri.n_list;
+    j[u] = (int32_t)q;
+    if (p.csa) j[u] = p.idx[(int64_t)r * p.k + (listed ? q : 0)];
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int64_t q = q_begin + threadIdx.x + u * NT;
+    int32_t sv = -1;
+    if (q < ri.n_list) {
+      sv = (j[u] >= 0 && j[u] < p.E_cap) ? j[u] : -1;
+    } else if (q < ri.n_items) {
+      const uint32_t i = (uint32_t)(ri.win_first + (q - ri.n_list));
+      sv = -2 - (int32_t)(i % (uint32_t)p.R_w);
+    }
+    if (q < q_end) srcs[q - q_begin] = sv;
+  }
+}
+
+// bf16 entries and window with D = 512 (the MLA-style latent), 64 heads: items
+// travel global -> LDS by asynchronous copies (one 1 KB row per wavefront
+// instruction) into four 32-item stages, so three chunks are in flight while a
+// fourth is multiplied, without staging registers.  Waits are explicit: before
+// a chunk is used each wave waits until only the later chunks' copies are
+// outstanding, then one barrier publishes the chunk and frees the stage of the
+// chunk before it for the next copy.
 //
 // Both products read the same staged rows.  Q.K^T takes row fragments (one item,
 // eight dims per lane).  P.V needs the transpose (one dim, eight items per lane):
@@ -371,19 +410,35 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma(AttendParams p) {
 // of items 4g .. 4g + 3, the k-group layout of the P operand.  P is rounded to
 // bf16 for that product; the normaliser (and the log-sum-exp) sums the
 // unrounded fp32 probabilities.
-template <int NW>
-__global__ __launch_bounds__(NW * 64) void attend_dma512(AttendParams p) {
-  constexpr int D = 512, CH = 32, KSQ = D / 32, ND = D / 16, MT = 2;
-  constexpr int KRS = D + 8;                 // padded LDS row (bf16 elements)
+//
+// With one wavefront per SIMD every vector instruction costs four cycles of
+// issue, so the loop keeps them few: all LDS addresses are a per-lane base plus
+// an immediate, and item masks are applied only to chunks that contain padding.
+__global__ __launch_bounds__(256) void attend_dma512(AttendParams p) {
+  constexpr int NW = 4, D = 512, CH = 32, KSQ = D / 32, ND = D / 16;
+  constexpr int KRS = D + 8;                 // padded LDS row (bf16 elements): row stride = 4 banks
   constexpr int NT = NW * kWave;
   constexpr int RPW = CH / NW;               // rows copied per wave per chunk
-  __shared__ __attribute__((aligned(16))) uint16_t st0[CH * KRS];
-  __shared__ __attribute__((aligned(16))) uint16_t st1[CH * KRS];
-  __shared__ __attribute__((aligned(16))) uint16_t st2[CH * KRS];
-  __shared__ float isc[3][CH];
+  constexpr int NSTG = 4;
+  constexpr int STG = CH * KRS;              // stage size (bf16 elements)
+  __shared__ __attribute__((aligned(16))) uint16_t stg[NSTG * STG];
   __shared__ int32_t srcs[kSegItems];
 
-  const int r = blockIdx.y, split = blockIdx.x;
+  // one-dimensional grid; with rows in multiples of 8 the splits of a row share
+  // an XCD (blocks are dealt to the 8 XCDs in turn), so its query and index
+  // list are fetched into one L2
+  int r, split;
+  {
+    const int n = blockIdx.x;
+    if ((p.rows_R & 7) == 0) {
+      const int k = n >> 3;
+      r = (n & 7) + 8 * (k / p.nsplit);
+      split = k % p.nsplit;
+    } else {
+      r = n / p.nsplit;
+      split = n % p.nsplit;
+    }
+  }
   const RowItems ri = row_items(p, r);
   const int l = lane_id(), w = wave_id();
   const int col = l & 15, g = l >> 4;
@@ -394,14 +449,13 @@ __global__ __launch_bounds__(NW * 64) void attend_dma512(AttendParams p) {
   q_end = q_end < ri.n_items ? q_end : ri.n_items;
 
   const gbytes gent = opaque_global(p.entries), gwin = opaque_global(p.win);
+  // query fragments: loads issued here, waited for after the first source table
   bf16x8 bq[KSQ];
   {
     const gbytes gq = opaque_global(p.q);
     const int64_t e0 = ((int64_t)r * p.H + head) * D + g * (D / 4);
 #pragma unroll
     for (int ks = 0; ks < KSQ; ++ks) bq[ks] = bitcast<bf16x8>(gload<u32x4>(gq, (e0 + 8 * ks) * 2));
-#pragma unroll
-    for (int ks = 0; ks < KSQ; ++ks) pin(bq[ks]);
   }
   f32x4 o[ND];
 #pragma unroll
@@ -418,8 +472,13 @@ __global__ __launch_bounds__(NW * 64) void attend_dma512(AttendParams p) {
   // every staged value is finite; their logits are masked
   const int32_t t_slot = (int32_t)(ri.t % p.R_w);
 
-  // copies of chunk q_rel (relative to the segment's sources) into stage S
-  auto issue = [&](int64_t q_rel, uint16_t* S, float* iscS) __attribute__((always_inline)) {
+  // per-lane LDS byte offsets within a stage
+  const int qk_base = (col * KRS + g * (D / 4)) * 2;                        // row col, dims g*128 ..
+  const int pv_base = ((4 * g + (col >> 2)) * KRS + 4 * (col & 3)) * 2;      // item 4g + col/4, dims 4(col%4) ..
+  const lds_ptr lds0 = (lds_ptr)stg;
+
+  // copies of chunk q_rel (relative to the segment's sources) into stage st
+  auto issue = [&](int64_t q_rel, int st) __attribute__((always_inline)) {
     const int32_t my_src = srcs[q_rel + wu * RPW + (l % RPW)];   // lane i holds row i's source
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
@@ -427,102 +486,112 @@ __global__ __launch_bounds__(NW * 64) void attend_dma512(AttendParams p) {
       const int32_t sv = __builtin_amdgcn_readlane(my_src, i);    // one row per instruction
       const gbytes src = sv >= 0 ? gent_row + (int64_t)sv * (D * 2)
                                  : gwin_row + (int64_t)(sv <= -2 ? -2 - sv : t_slot) * (D * 2);
-      copy_to_lds16(src + l * 16, &S[c * KRS]);
-      if (l == 0) iscS[c] = sv == -1 ? 0.f : 1.f;
+      copy_to_lds16(src + l * 16, &stg[st * STG + c * KRS]);
     }
   };
 
-  // one chunk: wait for its copies, multiply
-  auto step = [&](int c, int nch, int64_t q_rel_next2, uint16_t* S, const float* iscS, uint16_t* S2,
-                  float* isc2) __attribute__((always_inline)) {
-    if (c + 1 < nch) wait_vm_lgkm<RPW, 0>();
-    else wait_vm_lgkm<0, 0>();
-    block_barrier();                                           // chunk c visible; stage of c-1 free
-    if (c + 2 < nch) issue(q_rel_next2, S2, isc2);
-
-    // S^T = K Q^T: item fragments are read in batches of 8 k-steps, the next
-    // batch in flight while the current one is multiplied
-    f32x4 sacc[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) sacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    constexpr int KB = 8, NB = MT * KSQ / KB;
-    bf16x8 fa[2][KB];
-    auto read_batch = [&](int b, bf16x8 (&f)[KB]) {
-      const int mt = b / (KSQ / KB), k0 = (b % (KSQ / KB)) * KB;
-      const uint16_t* kr = &S[(16 * mt + col) * KRS + g * (D / 4) + 8 * k0];
-#pragma unroll
-      for (int j = 0; j < KB; ++j) f[j] = bitcast<bf16x8>(*reinterpret_cast<const u32x4*>(kr + 8 * j));
-    };
-    read_batch(0, fa[0]);
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-#pragma unroll
-      for (int j = 0; j < KB; ++j) pin(fa[b & 1][j]);
-      if (b + 1 < NB) read_batch(b + 1, fa[(b + 1) & 1]);
-      const int mt = b / (KSQ / KB), k0 = (b % (KSQ / KB)) * KB;
-#pragma unroll
-      for (int j = 0; j < KB; ++j) sacc[mt] = mfma16_bf16(fa[b & 1][j], bq[k0 + j], sacc[mt]);
-    }
-    float x[8];
-    float cmax = -INFINITY;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float v = iscS[16 * mt + 4 * g + i] != 0.f ? sacc[mt][i] * scale2 : -INFINITY;
-        x[4 * mt + i] = v;
-        cmax = fmaxf(cmax, v);
-      }
-    cmax = fmaxf(cmax, shfl_xor_f(cmax, 16));
-    cmax = fmaxf(cmax, shfl_xor_f(cmax, 32));
-    // the reference maximum moves only when a logit exceeds it by more than
-    // 2^8 (probabilities then stay below 256): the output is rescaled rarely
-    const bool grows = cmax > m_run + 8.f;
-    const float m_new = grows ? cmax : m_run;
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = grows ? (m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new)) : 1.f;
-    m_run = m_new;
-    bf16x8 pa;
-    float psum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float pe = __builtin_amdgcn_exp2f(x[e] - m_use);
-      psum += pe;
-      pa[e] = (__bf16)pe;
-    }
-    l_run = l_run * alpha + psum;
-    if (__any(grows)) {
-      float al[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i, kWave);
-#pragma unroll
-      for (int nd = 0; nd < ND; ++nd)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[nd][i] *= al[i];
-    }
-    // O += P V: B fragments by transposing reads of the staged rows
-    const lds_ptr v0 = (lds_ptr)&S[(4 * g + (col >> 2)) * KRS + 4 * (col & 3)];
-    const lds_ptr v1 = (lds_ptr)&S[(16 + 4 * g + (col >> 2)) * KRS + 4 * (col & 3)];
-#pragma unroll
-    for (int nd = 0; nd < ND; ++nd) {
-      const u32x2 lo = lds_read_tr16(v0, 32 * nd);
-      const u32x2 hi = lds_read_tr16(v1, 32 * nd);
-      o[nd] = mfma16_bf16(pa, bitcast<bf16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]}), o[nd]);
-    }
-  };
-
+  bool q_ready = false;
   for (int64_t s0 = q_begin; s0 < q_end; s0 += kSegItems) {
     const int64_t s1 = s0 + kSegItems < q_end ? s0 + kSegItems : q_end;
     const int nch = (int)((s1 - s0 + CH - 1) / CH);
     __syncthreads();
-    block_sources(p, ri, r, s0, s0 + (int64_t)nch * CH, NT, srcs);
+    block_sources_batched<kSegItems / NT, NT>(p, ri, r, s0, s0 + (int64_t)nch * CH, srcs);
     __syncthreads();
-    issue(0, st0, isc[0]);
-    if (nch > 1) issue(CH, st1, isc[1]);
-    for (int c = 0; c < nch; c += 3) {
-      step(c, nch, (int64_t)(c + 2) * CH, st0, isc[0], st2, isc[2]);
-      if (c + 1 < nch) step(c + 1, nch, (int64_t)(c + 3) * CH, st1, isc[1], st0, isc[0]);
-      if (c + 2 < nch) step(c + 2, nch, (int64_t)(c + 4) * CH, st2, isc[2], st1, isc[1]);
+    if (!q_ready) {
+#pragma unroll
+      for (int ks = 0; ks < KSQ; ++ks) pin(bq[ks]);
+      q_ready = true;
+    }
+    for (int c = 0; c < NSTG - 1 && c < nch; ++c) issue((int64_t)c * CH, c);
+
+    for (int c = 0; c < nch; ++c) {
+      const int st = c & (NSTG - 1);
+      // validity of the chunk's 32 items: bit i set when item i has a source
+      const int32_t my_item = srcs[(int64_t)c * CH + (l & 31)];
+      const uint64_t valid = __ballot(l < 32 && my_item != -1);
+      if (c + 2 < nch) wait_vm_lgkm<2 * RPW, 0>();
+      else if (c + 1 < nch) wait_vm_lgkm<RPW, 0>();
+      else wait_vm_lgkm<0, 0>();
+      block_barrier();                                   // chunk c visible; stage of c-1 free
+      if (c + NSTG - 1 < nch) issue((int64_t)(c + NSTG - 1) * CH, (c + NSTG - 1) & (NSTG - 1));
+
+      // S^T = K Q^T in four independent accumulators (2 item tiles x even/odd
+      // k-steps); fragments read in batches of 4 k-steps, one batch ahead
+      const uint8_t* sb = reinterpret_cast<const uint8_t*>(&stg[st * STG]) + qk_base;
+      f32x4 sacc[2][2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sacc[i >> 1][i & 1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      constexpr int KB = 4, NB = KSQ / KB;
+      bf16x8 fa[2][2 * KB];
+      auto read_batch = [&](int b, bf16x8 (&f)[2 * KB]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int j = 0; j < KB; ++j)
+            f[mt * KB + j] = bitcast<bf16x8>(
+                *reinterpret_cast<const u32x4*>(sb + (mt * 16 * KRS + 8 * (KB * b + j)) * 2));
+      };
+      read_batch(0, fa[0]);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+#pragma unroll
+        for (int j = 0; j < 2 * KB; ++j) pin(fa[b & 1][j]);
+        if (b + 1 < NB) read_batch(b + 1, fa[(b + 1) & 1]);
+#pragma unroll
+        for (int j = 0; j < KB; ++j)
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+            sacc[mt][j & 1] = mfma16_bf16(fa[b & 1][mt * KB + j], bq[KB * b + j], sacc[mt][j & 1]);
+      }
+      float x[8];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[4 * mt + i] = (sacc[mt][0][i] + sacc[mt][1][i]) * scale2;
+      if ((uint32_t)valid != 0xffffffffu) {                // padding in this chunk
+        const uint32_t lo = (uint32_t)(valid >> (4 * g)), hi = (uint32_t)(valid >> (16 + 4 * g));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (!((lo >> i) & 1u)) x[i] = -INFINITY;
+          if (!((hi >> i) & 1u)) x[4 + i] = -INFINITY;
+        }
+      }
+      float cmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+      cmax = group_max4(cmax);
+      // the reference maximum moves only when a logit exceeds it by more than
+      // 2^8 (probabilities then stay below 256): the output is rescaled rarely
+      const bool grows = cmax > m_run + 8.f;
+      const bool had = m_run != -INFINITY;       // an earlier chunk contributed
+      const float m_new = grows ? cmax : m_run;
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = grows ? (had ? __builtin_amdgcn_exp2f(m_run - m_new) : 0.f) : 1.f;
+      m_run = m_new;
+      bf16x8 pa;
+      float psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pe = __builtin_amdgcn_exp2f(x[e] - m_use);
+        psum += pe;
+        pa[e] = (__bf16)pe;
+      }
+      l_run = l_run * alpha + psum;
+      if (__any(grows && had)) {                 // nothing to rescale before the first contribution
+        float al[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i, kWave);
+#pragma unroll
+        for (int nd = 0; nd < ND; ++nd)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[nd][i] *= al[i];
+      }
+      // O += P V: B fragments by transposing reads of the staged rows
+      const int vb = st * STG * 2 + pv_base;
+#pragma unroll
+      for (int nd = 0; nd < ND; ++nd) {
+        const u32x2 lo = lds_read_tr16(lds0, vb + 32 * nd);
+        const u32x2 hi = lds_read_tr16(lds0, vb + 32 * nd + 16 * KRS * 2);
+        o[nd] = mfma16_bf16(pa, bitcast<bf16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]}), o[nd]);
+      }
     }
   }
 
@@ -717,7 +786,7 @@ AttendPlan plan_attend(const sckv_attend_args& a, bool csa) {
 template <int ENT, int D>
 static void launch_mfma_d(const AttendParams& p, int H, dim3 grid, hipStream_t s) {
   if (ENT == SCKV_BF16 && D == 512 && H == 64) {
-    hipLaunchKernelGGL(attend_dma512<4>, grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL(attend_dma512, dim3(grid.x * grid.y), dim3(256), 0, s, p);
   } else {
     // register-staged chunks: 64 items when the latent is narrow, 32 at D = 512
     constexpr int CH = D <= 256 ? 64 : 32;
@@ -765,6 +834,7 @@ hipError_t launch_attend(const sckv_attend_args& a, bool csa, const AttendPlan& 
   p.nsplit = pl.nsplit;
   p.per_split = (int32_t)pl.per_split;   // items
   p.scale = a.softmax_scale;
+  p.rows_R = a.rows.R;
   if (pl.nsplit > 1) {
     p.ws_o = static_cast<float*>(ws);
     p.ws_ml = p.ws_o + (size_t)a.rows.R * pl.nsplit * a.H * a.D;
