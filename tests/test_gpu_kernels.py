@@ -154,6 +154,8 @@ INDEX_CASES = [
     ("bf16", 64, 128, 40000, [160127], 1024),
     ("bf16", 64, 128, 70000, [279999, 200000], 2048),
     ("e4m3", 64, 128, 70000, [279999], 100),
+    # 40 rows over a 32K-entry cache: rows cut into 8192-entry slices, ragged row lengths
+    ("bf16", 32, 64, 32768, [131071 - 997 * i for i in range(40)], 512),
 ]
 
 
