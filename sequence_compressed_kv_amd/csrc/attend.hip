@@ -407,9 +407,10 @@ __device__ __forceinline__ void block_sources_batched(const AttendParams& p, con
 // group, lane 4r + c receives element c of the 8-byte words addressed by lanes
 // r, r + 4, r + 8 and r + 12 of the group.  So lane a of group g points at item
 // 4g + a/4, dims 4(a%4) .. +3, and lane n of the group comes back holding dim n
-// of items 4g .. 4g + 3, the k-group layout of the P operand.  P is rounded to
-// bf16 for that product; the normaliser (and the log-sum-exp) sums the
-// unrounded fp32 probabilities.
+// of items 4g .. 4g + 3, the k-group layout of the P operand.  That product
+// runs in bf16, so P enters as the sum of two bf16 parts (a second MFMA per dim
+// tile): a single bf16 P would cost up to 2^-9 of max |v| in the output.  The
+// normaliser (and the log-sum-exp) sums the unrounded fp32 probabilities.
 //
 // With one wavefront per SIMD every vector instruction costs four cycles of
 // issue, so the loop keeps them few: all LDS addresses are a per-lane base plus
@@ -566,13 +567,15 @@ __global__ __launch_bounds__(256) void attend_dma512(AttendParams p) {
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       const float alpha = grows ? (had ? __builtin_amdgcn_exp2f(m_run - m_new) : 0.f) : 1.f;
       m_run = m_new;
-      bf16x8 pa;
+      // P = hi + lo, both bf16 (about 16 significant bits together)
+      bf16x8 pa, pl;
       float psum = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float pe = __builtin_amdgcn_exp2f(x[e] - m_use);
         psum += pe;
         pa[e] = (__bf16)pe;
+        pl[e] = (__bf16)(pe - (float)pa[e]);
       }
       l_run = l_run * alpha + psum;
       if (__any(grows && had)) {                 // nothing to rescale before the first contribution
@@ -590,7 +593,9 @@ __global__ __launch_bounds__(256) void attend_dma512(AttendParams p) {
       for (int nd = 0; nd < ND; ++nd) {
         const u32x2 lo = lds_read_tr16(lds0, vb + 32 * nd);
         const u32x2 hi = lds_read_tr16(lds0, vb + 32 * nd + 16 * KRS * 2);
-        o[nd] = mfma16_bf16(pa, bitcast<bf16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]}), o[nd]);
+        const bf16x8 vb = bitcast<bf16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
+        o[nd] = mfma16_bf16(pa, vb, o[nd]);
+        o[nd] = mfma16_bf16(pl, vb, o[nd]);
       }
     }
   }

@@ -89,3 +89,30 @@ def bf16_code_flips(gpu_vals, ora_raw, ora_rounded, mid_rtol=1e-5, magnitude=Non
     """bf16 form of rounding_mismatches (magnitude defaults to |value|)."""
     mag = np.abs(np.asarray(ora_raw, np.float64)) if magnitude is None else magnitude
     return rounding_mismatches(gpu_vals, ora_raw, ora_rounded, mag, "bf16", mid_rtol)
+
+
+def e4m3_flips(gpu_codes, ora_codes, ora_unrounded, magnitude, mid_rtol=1e-5):
+    """e4m3 codes that differ from the oracle's, and those not explained by the GPU's
+    fp32 error (within mid_rtol of `magnitude`) moving the value across a rounding boundary."""
+    from oracle import codecs
+    return rounding_mismatches(codecs.e4m3_decode(gpu_codes), ora_unrounded, codecs.e4m3_decode(ora_codes),
+                               magnitude, "e4m3", mid_rtol)
+
+
+def blocked_compress(v, g, bpos, m, o, block=16384):
+    """oracle.method.compress over entry blocks: entry j reads only tokens
+    [m j - o, m j + m), so each block runs on its own token slice (bounded host
+    memory at million-token sizes).  Needs o % m == 0."""
+    import numpy as np
+
+    from oracle import method
+    assert o % m == 0
+    N = v.shape[0]
+    E = N // m
+    out = []
+    for j0 in range(0, E, block):
+        j1 = min(E, j0 + block)
+        t0 = max(0, m * j0 - o)
+        c = method.compress(v[t0:m * j1], g[t0:m * j1], bpos, m, o)
+        out.append(c if j0 == 0 else c[o // m:])
+    return np.concatenate(out) if out else np.zeros((0, v.shape[1]))

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 from oracle import codecs, method
-from tests.compare import assert_close, bf16_code_flips, topk_parity
+from tests.compare import assert_close, bf16_code_flips, e4m3_flips, topk_parity
 from tests.gpu_util import DEV, dev, dev_codes, dev_i32, host, rng_store
 
 pytestmark = pytest.mark.gpu
@@ -24,14 +24,6 @@ def setup_module(module):
 
 
 # ---------------------------------------------------------------- compression
-def e4m3_flips(gpu_codes, ora_codes, ora_unrounded, magnitude, mid_rtol=1e-5):
-    """e4m3 codes that differ from the oracle's, and those not explained by the GPU's
-    fp32 error (within mid_rtol of `magnitude`) moving the value across a rounding boundary."""
-    from tests.compare import rounding_mismatches
-    return rounding_mismatches(codecs.e4m3_decode(gpu_codes), ora_unrounded, codecs.e4m3_decode(ora_codes),
-                               magnitude, "e4m3", mid_rtol)
-
-
 COMPRESS_CASES = [
     # m, o, D, in, out, scaled, B, N
     (4, 4, 64, "f32", "f32", False, 1, 4096),

@@ -144,3 +144,13 @@ def test_brute_force_loops_tiny():
             e = [math.exp(x - mx) for x in a]
             ref = sum(ei * v[i, d] for ei, i in zip(e, toks)) / sum(e)
             assert abs(c[j, d] - ref) <= 1e-13 * max(1.0, abs(ref))
+
+
+@pytest.mark.parametrize("m,o,N,block", [(4, 4, 203, 7), (4, 4, 4096, 100), (128, 0, 1300, 3), (2, 6, 101, 5)])
+def test_blocked_compress_equals_whole(m, o, N, block):
+    """The entry-blocked driver used at million-token sizes gives the whole-array result."""
+    from tests.compare import blocked_compress
+    rng = np.random.default_rng(N + block)
+    D = 6
+    v, g, bp = _rand(rng, N, D), _rand(rng, N, D, 2.0), rng.normal(0, 1, (m + o, D))
+    np.testing.assert_array_equal(blocked_compress(v, g, bp, m, o, block=block), method.compress(v, g, bp, m, o))

@@ -198,12 +198,25 @@ def gpu_weights(wl: Workload, device, seed_offset: int = 0):
     return out
 
 
+def _gpu_hidden_chunk(wl: Workload, b: int, g, a: int, e: int, device):
+    """x[a:e] of sequence b drawn with the GPU generator g (consumed in order),
+    with the heavy-token scaling of the host recipe at the same positions."""
+    x = torch.randn(e - a, wl.d_model, device=device, generator=g)
+    hp = heavy_positions(wl, b)
+    hp = hp[(hp >= a) & (hp < e)]
+    if hp.size:
+        x[torch.from_numpy(hp - a).to(device)] *= wl.heavy_scale
+    return x
+
+
 def gpu_sequence_streams(wl: Workload, b: int, weights, device, chunk: int = 32768):
     """Streams of every layer for sequence b, from one hidden-state stream drawn on
-    the GPU with torch's RNG (x ~ N(0,1); fp32 projections rounded to storage).
+    the GPU with torch's RNG (x ~ N(0,1), heavy tokens scaled as in the host
+    recipe; fp32 projections rounded to storage).
 
-    Same distributions as the host recipe, other random numbers: used to fill
-    caches whose decode steps are timed, never compared with the oracle.
+    Same distributions as the host recipe, other random numbers: the inputs of
+    the full-size runs (timed decode steps, and the full-size parity tests, which
+    copy the streams of sampled sequences back to the host for the oracle).
     Returns a list (per layer) of dicts of torch tensors [N][D] in storage dtype.
     """
     g = torch.Generator(device=device)
@@ -215,11 +228,53 @@ def gpu_sequence_streams(wl: Workload, b: int, weights, device, chunk: int = 327
         out.append({n: torch.empty(wl.N, w[n].shape[0], device=device, dtype=dt) for n in names})
     for a in range(0, wl.N, chunk):
         e = min(wl.N, a + chunk)
-        x = torch.randn(e - a, wl.d_model, device=device, generator=g)
+        x = _gpu_hidden_chunk(wl, b, g, a, e, device)
         for st, w in zip(out, weights):
             for n in st:
                 st[n][a:e] = (x @ w[n].T).to(dt)
     return out
+
+
+def gpu_prefill_inputs(wl: Workload, device, chunk: int = 4096):
+    """Prefill inputs of layer 0 for sequence 0 drawn on the GPU: the streams and,
+    from the same hidden state x_t, the query of every row t (causal prefill).
+
+    Returns (weights, streams, queries): streams as gpu_sequence_streams (layer 0),
+    queries {q [N][H][D] (absorbed when D != d_h), qI [N][H_I][D_I]} in storage
+    dtype and w [N][H_I] fp32.
+    """
+    L = wl.layers[0]
+    weights = gpu_weights(wl, device)
+    w0 = weights[0]
+    g = torch.Generator(device=device)
+    g.manual_seed(wl.seed * 1000003 + 15485863)
+    dm = wl.d_model
+    dt = torch_dtype(wl.store)
+    Wq = torch.randn(L.H * L.d_h, dm, device=device, generator=g) / math.sqrt(dm)
+    WUK = (torch.randn(L.H, L.d_h, L.D, device=device, generator=g) / math.sqrt(L.D)) if L.absorbed else None
+    Wiq = torch.randn(L.H_I * L.D_I, dm, device=device, generator=g) / math.sqrt(dm)
+    Ww = torch.randn(L.H_I, dm, device=device, generator=g) / math.sqrt(dm)
+    names = ["v", "g", "vI", "gI"]
+    st = {n: torch.empty(wl.N, w0[n].shape[0], device=device, dtype=dt) for n in names}
+    q = torch.empty(wl.N, L.H, L.D, device=device, dtype=dt)
+    qI = torch.empty(wl.N, L.H_I, L.D_I, device=device, dtype=dt)
+    w = torch.empty(wl.N, L.H_I, device=device, dtype=torch.float32)
+    gx = torch.Generator(device=device)
+    gx.manual_seed(wl.seed * 1000003 + 104729)
+    for a in range(0, wl.N, chunk):
+        e = min(wl.N, a + chunk)
+        x = _gpu_hidden_chunk(wl, 0, gx, a, e, device)
+        for n in names:
+            st[n][a:e] = (x @ w0[n].T).to(dt)
+        qh = (x @ Wq.T).view(e - a, L.H, L.d_h)
+        if WUK is not None:
+            qt = torch.bmm(qh.transpose(0, 1).contiguous(), WUK).transpose(0, 1)
+        else:
+            qt = qh
+        q[a:e] = qt.to(dt)
+        qI[a:e] = (x @ Wiq.T).view(e - a, L.H_I, L.D_I).to(dt)
+        w[a:e] = x @ Ww.T
+    return weights, st, {"q": q, "qI": qI, "w": w}
 
 
 def gpu_queries(wl: Workload, li: int, R: int, device, seed_offset: int = 0):
