@@ -1,15 +1,18 @@
 """Decode-step benchmark of the CSA + HCA layer pair at 128K context, batch 32.
 
-One step = csa_index_topk (lightning-indexer scoring + top-1024) + csa_attend +
-hca_attend for all 32 sequences, caches and queries resident in HBM.  Prints one
-JSON line: queries/s, the step's HBM rate against the 8 TB/s peak, the
-roofline record of the dominant kernel (indexer scoring, timed with HIP events
-on its stream) and the CPU oracle timed on a bounded sample of the same step.
+One step = csa_index_topk (lightning-indexer scoring + top-1024, as its two
+halves csa_index_score and csa_topk_select) + csa_attend + hca_attend for all 32
+sequences, caches and queries resident in HBM.  Prints one JSON line:
+queries/s, the step's HBM rate against the 8 TB/s peak, the roofline record of
+the dominant kernel (indexer scoring: back-to-back launches timed with HIP
+events on its stream; HBM traffic from a committed counter summary while the
+kernel sources match it), the 32K causal prefill indexer rate against the bf16
+MFMA peak, and the CPU oracle timed on a bounded sample of the same step.
 
-Caches come from the same recipe as the parity tests (x ~ N(0,1), weights
-N(0, 1/fan_in), fp32 projections rounded to bf16, then the library's own
-compressors) with hidden states drawn by torch on the GPU; compression is not
-part of the timed step.
+Caches come from the seeded recipe of the full-size parity tests (x ~ N(0,1),
+weights N(0, 1/fan_in), fp32 projections rounded to bf16, then the library's
+own compressors) with hidden states drawn by torch on the GPU; compression is
+not part of the timed step.
 """
 from __future__ import annotations
 
@@ -24,6 +27,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0          # dense bf16 MFMA
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "index_score_decode.pair_decode_128k_bf16.counters.txt")
 
 
 def parse():
@@ -35,7 +40,74 @@ def parse():
     ap.add_argument("--batch", type=int, default=None, help="override the batch (default 32)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill indexer measurement")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 256 MiB device copy (reference for the HBM byte counters)")
     return ap.parse_args()
+
+
+def source_digest() -> str:
+    """sha256 of the sources of the indexer scoring kernel (names the kernel version
+    that a committed counter summary was taken from)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("index.hip", "device_common.h"):
+        with open(os.path.join(ROOT, "sequence_compressed_kv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counter_traffic(path: str):
+    """HBM bytes per launch of the indexer scoring kernel from a committed counter
+    summary (FETCH_SIZE and WRITE_SIZE passes, each scaled by a copy-kernel
+    calibration), or None when the summary is missing or was taken on other
+    kernel sources."""
+    try:
+        with open(path) as f:
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
+    except OSError:
+        return None
+    if kv.get("source_sha256", "").strip() != source_digest():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def prefill_indexer_rate(dev, sk, torch, wl, iters: int = 5):
+    """Indexer scoring of the 32K-token causal prefill (every row scores its visible
+    entries): algorithmic bf16 flops per second on MFMA.  Keys, queries and
+    weights are random with the workload's shapes (the rate does not depend on
+    the values)."""
+    L = wl.layers[0]
+    T, E = wl.N, wl.N // L.m
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.seed)
+    bf = torch.bfloat16
+    keys = sk.to_key_tiles(torch.randn(1, E, L.D_I, device=dev, generator=g).to(bf))
+    qI = torch.randn(T, L.H_I, L.D_I, device=dev, generator=g).to(bf)
+    w = torch.randn(T, L.H_I, device=dev, generator=g)
+    cover = max(0, (T - 1 - L.W) // L.m)
+    scores = torch.empty(T, (cover + 63) // 64 * 64, device=dev)
+    rows = sk.RowSpec.causal(T)
+    pairs = sum(max(0, (t - L.W) // L.m) for t in range(T))
+    flops = 2.0 * pairs * L.H_I * L.D_I
+    for _ in range(2):
+        sk.csa_index_score(rows, qI, w, keys, scores, m=L.m, W=L.W, k=L.k)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(iters):
+        sk.csa_index_score(rows, qI, w, keys, scores, m=L.m, W=L.W, k=L.k)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": wl.name, "kernel": "index_score_causal", "rows": T, "visible_pairs": pairs,
+            "tflop": flops / 1e12, "ms": ms, "achieved_tflops": tf, "peak_tflops": PEAK_BF16_TFLOPS,
+            "frac": tf / PEAK_BF16_TFLOPS}
 
 
 def build_caches(wl, dev, sk, torch, gen):
@@ -133,8 +205,17 @@ def main():
         sys.exit(2)
     import torch
 
+    if args.calibrate_copy:
+        x = torch.empty(256 * 1024 * 1024 // 4, device="cuda:0")
+        y = torch.empty_like(x)
+        for _ in range(5):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": x.numel() * 4, "copy_bytes_written": y.numel() * 4, "launches": 5}))
+        return
+
     import sequence_compressed_kv_amd as sk
-    from workloads import PAIR_DEC_128K_BF16, gen
+    from workloads import CSA_PREFILL_32K_BF16, PAIR_DEC_128K_BF16, gen
 
     wl = PAIR_DEC_128K_BF16 if args.batch is None else PAIR_DEC_128K_BF16.with_sizes(B=args.batch)
     dev = "cuda:0"
@@ -212,8 +293,19 @@ def main():
     parts = {name: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)) / args.steps
              for j, name in enumerate(["score", "topk", "csa_attend", "hca_attend"])}
 
+    # the dominant kernel alone: back-to-back launches on the same stream between
+    # two events (per-launch time without the event/launch gaps of the step)
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record(stream)
+    for i in range(args.steps):
+        c, _ = reps[i % len(reps)]
+        sk.csa_index_score(rows, qc["qI"], qc["w"], c["keys"], scores, m=csa.m, W=csa.W, k=csa.k)
+    s1.record(stream)
+    torch.cuda.synchronize()
+    score_ms = s0.elapsed_time(s1) / args.steps
+
     ab = algorithmic_bytes(wl)
-    score_gbps = ab["score"] * B / (parts["score"] * 1e-3) / 1e9
+    score_gbps = ab["score"] * B / (score_ms * 1e-3) / 1e9
     step_gbps = ab["step"] * B / (ms * 1e-3) / 1e9
     rec = {
         "metric": "CSA+HCA decode attention queries/s at 128K ctx; HBM GB/s as % of peak",
@@ -228,11 +320,16 @@ def main():
         "step_hbm_GBps": step_gbps, "step_hbm_frac": step_gbps / PEAK_HBM_GBPS,
         "step_algorithmic_bytes": ab["step"] * B,
         "kernel_ms": parts,
-        "roofline": {"bound": "hbm", "kernel": "index_score_decode", "achieved": score_gbps,
+        "roofline": {"bound": "hbm", "kernel": "index_score_decode", "launch_ms": score_ms, "achieved": score_gbps,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": score_gbps / PEAK_HBM_GBPS,
-                     "traffic": None, "bytes_per_launch": ab["score"] * B},
+                     "traffic": counter_traffic(TRAFFIC_SUMMARY), "bytes_per_launch": ab["score"] * B},
         "wall_s_timed": wall,
     }
+    if not args.no_prefill:
+        print("[bench] prefill indexer scoring (32K causal rows)", file=sys.stderr, flush=True)
+        del reps, c0, h0
+        torch.cuda.empty_cache()
+        rec["prefill_indexer"] = prefill_indexer_rate(dev, sk, torch, CSA_PREFILL_32K_BF16)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
