@@ -1,8 +1,7 @@
 """Decode-step benchmark of the CSA + HCA layer pair at 128K context, batch 32.
 
-One step = csa_index_topk (lightning-indexer scoring + top-1024, as its two
-halves csa_index_score and csa_topk_select) + csa_attend + hca_attend for all 32
-sequences, caches and queries resident in HBM.  Prints one JSON line:
+One step = csa_index_topk (lightning-indexer scoring + top-1024) + csa_attend +
+hca_attend for all 32 sequences, caches and queries resident in HBM.  Prints one JSON line:
 queries/s, the step's HBM rate against the 8 TB/s peak, the roofline record of
 the dominant kernel (indexer scoring: back-to-back launches timed with HIP
 events on its stream; HBM traffic from a committed counter summary while the
@@ -244,8 +243,7 @@ def main():
     ws_idx = torch.empty(L.csa_index_topk_workspace_size(C.byref(ia)), dtype=torch.uint8, device=dev)
     cover = max(0, (t - csa.W) // csa.m)
     stride = (cover + 63) // 64 * 64
-    scores = ws_idx[: B * stride * 4].view(torch.float32).view(B, stride)
-    ws_sel = ws_idx[B * stride * 4:]
+    scores = torch.empty(B, stride, device=dev)             # for timing the scoring kernel alone
     ws_c = sk.csa_attend(rows, qc["q"], c0["entries"], idx, c0["win"], out_c, m=csa.m, W=csa.W, softmax_scale=tau)
     ws_h = sk.hca_attend(rows, qh["q"], h0["entries"], h0["win"], out_h, m=hca.m, W=hca.W, softmax_scale=tau)
 
@@ -255,21 +253,17 @@ def main():
         c, h = reps[i % len(reps)]
         if ev is not None:
             ev[0].record(stream)
-        sk.csa_index_score(rows, qc["qI"], qc["w"], c["keys"], scores, m=csa.m, W=csa.W, k=csa.k)
+        sk.csa_index_topk(rows, qc["qI"], qc["w"], c["keys"], idx, m=csa.m, W=csa.W, k=csa.k, workspace=ws_idx)
         if ev is not None:
             ev[1].record(stream)
-        sk.csa_topk_select(rows, scores, idx, keys_meta=(qc["qI"], qc["w"], c["keys"]), m=csa.m, W=csa.W,
-                           k=csa.k, workspace=ws_sel)
-        if ev is not None:
-            ev[2].record(stream)
         sk.csa_attend(rows, qc["q"], c["entries"], idx, c["win"], out_c, m=csa.m, W=csa.W, softmax_scale=tau,
                       workspace=ws_c)
         if ev is not None:
-            ev[3].record(stream)
+            ev[2].record(stream)
         sk.hca_attend(rows, qh["q"], h["entries"], h["win"], out_h, m=hca.m, W=hca.W, softmax_scale=tau,
                       workspace=ws_h)
         if ev is not None:
-            ev[4].record(stream)
+            ev[3].record(stream)
 
     for i in range(args.warmup):
         step(i)
@@ -286,12 +280,12 @@ def main():
     wall = time.time() - w0
     ms = e0.elapsed_time(e1) / args.steps
     # per-kernel durations: the same steps with events between the launches
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for i in range(args.steps):
         step(i, evs[i])
     torch.cuda.synchronize()
     parts = {name: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)) / args.steps
-             for j, name in enumerate(["score", "topk", "csa_attend", "hca_attend"])}
+             for j, name in enumerate(["csa_index_topk", "csa_attend", "hca_attend"])}
 
     # the dominant kernel alone: back-to-back launches on the same stream between
     # two events (per-launch time without the event/launch gaps of the step)

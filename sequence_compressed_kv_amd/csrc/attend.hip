@@ -283,8 +283,7 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma(AttendParams p) {
           x[4 * mt + i] = v;
           cmax = fmaxf(cmax, v);
         }
-      cmax = fmaxf(cmax, shfl_xor_f(cmax, 16));
-      cmax = fmaxf(cmax, shfl_xor_f(cmax, 32));
+      cmax = group_max4(cmax);
       const float m_new = fmaxf(m_run, cmax);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       const bool grows = m_new > m_run;                  // this head's running maximum moved
@@ -355,14 +354,6 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma(AttendParams p) {
       p.ws_ml[(sbase + head) * 2 + 1] = l_tot;
     }
   }
-}
-
-// maximum over the four 16-lane groups (lanes l, l^16, l^32, l^48)
-__device__ __forceinline__ float group_max4(float x) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // Sources of items [q_begin, q_end) (at most PER * NT of them) into srcs: every

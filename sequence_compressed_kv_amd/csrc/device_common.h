@@ -186,16 +186,37 @@ __device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, kWave); }
 
+// maximum over the four 16-lane groups (lanes l, l^16, l^32, l^48)
+__device__ __forceinline__ float group_max4(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// v[l] + v[l ^ 32] on every lane, through the gfx950 half-wave swap (no LDS)
+__device__ __forceinline__ float add_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave.
+// Inclusive prefix sum over the 64 lanes with DPP moves (no LDS round trips):
+// shifts by 1, 2, 4 and 8 lanes within each row of 16, then the row totals are
+// carried by row_bcast:15 (lane 15 of a row into the next row, rows 1 and 3)
+// and row_bcast:31 (lane 31 into rows 2 and 3).  Out-of-row sources read 0.
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  const int l = lane_id();
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    uint32_t t = __shfl_up(v, d, kWave);
-    if (l >= d) v += t;
-  }
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return v;
 }
+
+// Value of lane 63 (a wave-uniform result in a scalar register).
+__device__ __forceinline__ uint32_t last_lane(uint32_t v) { return (uint32_t)__builtin_amdgcn_readlane((int)v, 63); }
 
 // Exclusive prefix sum across the block (blockDim.x = NT threads, NT/64 <= 64 waves).
 // `sh` needs NT/64 + 1 words of LDS.  Returns the thread's exclusive prefix and

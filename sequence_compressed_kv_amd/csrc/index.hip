@@ -92,7 +92,7 @@ struct ScoreWave {
 #pragma unroll
       for (int i = 0; i < 16; ++i) part += w[mt][i] * fmaxf(acc[i], 0.f);
     }
-    const float tot = part + shfl_xor_f(part, 32);
+    const float tot = add_xor32(part);
     return tot == 0.f ? 0.f : tot;
   }
 
@@ -176,7 +176,7 @@ __global__ __launch_bounds__(256) void index_score_decode(
 #pragma unroll
       for (int i = 0; i < 16; ++i) part += wr[mt][i] * fmaxf(acc[i], 0.f);
     }
-    const float tot = part + shfl_xor_f(part, 32);
+    const float tot = add_xor32(part);
     const int64_t j = j_begin + 32 * t + n;
     if (hh == 0 && j < j_end) srow[j] = tot == 0.f ? 0.f : tot;
   };

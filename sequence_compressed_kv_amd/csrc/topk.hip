@@ -101,7 +101,7 @@ __device__ __forceinline__ void ordered_scan(const uint32_t (&c)[NI], uint32_t (
   for (int i = 0; i < NI; ++i) {
     const uint32_t inc = wave_incl_scan(c[i]);
     off[i] = run + inc - c[i];
-    run += __shfl(inc, kWave - 1, kWave);
+    run += last_lane(inc);
   }
   if (l == 0) sh[w] = run;
   __syncthreads();

@@ -231,13 +231,10 @@ def test_pair_decode_128k_bf16():
         ora[b] = (vc, vh, sc["values"], sI["values"], sh["values"])
     rows = sk.RowSpec.decode(torch.full((B,), t, dtype=torch.int32, device=DEV), t)
     idx = torch.empty(B, csa.k, dtype=torch.int32, device=DEV)
-    cover = max(0, (t - csa.W) // csa.m)
-    scores = torch.empty(B, (cover + 63) // 64 * 64, device=DEV)
     out_c = torch.empty(B, csa.H, csa.D, device=DEV)
     out_h = torch.empty(B, hca.H, hca.D, device=DEV)
     tau = tau_of(csa)
-    sk.csa_index_score(rows, qc["qI"], qc["w"], c["keys"], scores, m=csa.m, W=csa.W, k=csa.k)
-    sk.csa_topk_select(rows, scores, idx, keys_meta=(qc["qI"], qc["w"], c["keys"]), m=csa.m, W=csa.W, k=csa.k)
+    sk.csa_index_topk(rows, qc["qI"], qc["w"], c["keys"], idx, m=csa.m, W=csa.W, k=csa.k)
     sk.csa_attend(rows, qc["q"], c["entries"], idx, c["win"], out_c, m=csa.m, W=csa.W, softmax_scale=tau)
     sk.hca_attend(rows, qh["q"], h["entries"], h["win"], out_h, m=hca.m, W=hca.W, softmax_scale=tau)
     torch.cuda.synchronize()
