@@ -104,7 +104,7 @@ def prefill_indexer_rate(dev, sk, torch, wl, iters: int = 5):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / iters
     tf = flops / (ms * 1e-3) / 1e12
-    return {"workload": wl.name, "kernel": "index_score_causal", "rows": T, "visible_pairs": pairs,
+    return {"workload": wl.name, "kernel": "index_score_causal_lds", "rows": T, "visible_pairs": pairs,
             "tflop": flops / 1e12, "ms": ms, "achieved_tflops": tf, "peak_tflops": PEAK_BF16_TFLOPS,
             "frac": tf / PEAK_BF16_TFLOPS}
 

@@ -194,6 +194,14 @@ __device__ __forceinline__ float group_max4(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// max(x, 0) in one instruction: on the bit pattern, a signed integer max with 0
+// keeps non-negative floats and maps every negative one (sign bit set) to +0
+// (fmaxf costs a NaN-quieting step besides the max)
+__device__ __forceinline__ float relu(float x) {
+  const int b = __float_as_int(x);
+  return __int_as_float(b > 0 ? b : 0);
+}
+
 // v[l] + v[l ^ 32] on every lane, through the gfx950 half-wave swap (no LDS)
 __device__ __forceinline__ float add_xor32(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);

@@ -9,9 +9,11 @@
 // 32-head tile, so the ReLU . w head reduction is lane-local plus one exchange
 // between the two half-waves.  The D_I axis is split between the half-waves as
 // two contiguous halves: a lane streams 128 contiguous key bytes per tile.
-//   decode rows : a block takes one row and a 512-key range, 4 waves x 128 keys
-//   causal rows : a block takes 4 consecutive rows (one per wave) and walks every
-//                 visible key tile; blocks with the longest rows start first
+//   decode rows : a block takes one row and 4 waves x NT tiles of 32 keys, keys
+//                 streamed from HBM straight into MFMA fragments
+//   causal rows : a block takes 8 consecutive rows (one per wave) and walks every
+//                 visible key tile through LDS (each tile fetched once per block);
+//                 blocks with the longest rows start first
 #include "device_common.h"
 #include "sckv_internal.h"
 
@@ -82,18 +84,46 @@ struct ScoreWave {
 
   // Scores of keys [j0, j0 + 32) (keys beyond e_vis are computed on a clamped
   // row and not stored).
+  // The head tiles' accumulation chains are interleaved k-step by k-step, so
+  // consecutive MFMAs never wait on each other's results.
   __device__ __forceinline__ float tile(const bf16x8 (&b)[KS]) const {
+    f32x16 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma32_bf16(a[mt][ks], b[ks], acc[mt]);
+    return reduce(acc);
+  }
+
+  // sum_h w_h max(0, acc_h) over the lane's heads, then over the two half-waves
+  __device__ __forceinline__ float reduce(const f32x16 (&acc)[MT]) const {
     float part = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      f32x16 acc = {};
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc = mfma32_bf16(a[mt][ks], b[ks], acc);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) part += w[mt][i] * fmaxf(acc[i], 0.f);
-    }
+      for (int i = 0; i < 16; ++i) part += w[mt][i] * relu(acc[mt][i]);
     const float tot = add_xor32(part);
     return tot == 0.f ? 0.f : tot;
+  }
+
+  // Two tiles at once: their 2 MT accumulation chains interleaved, then both
+  // reductions (the second tile's MFMAs still run while the first is reduced).
+  __device__ __forceinline__ void tile2(const bf16x8 (&b0)[KS], const bf16x8 (&b1)[KS], float& s0,
+                                        float& s1) const {
+    f32x16 acc0[MT], acc1[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc0[mt] = acc1[mt] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        acc0[mt] = mfma32_bf16(a[mt][ks], b0[ks], acc0[mt]);
+        acc1[mt] = mfma32_bf16(a[mt][ks], b1[ks], acc1[mt]);
+      }
+    s0 = reduce(acc0);
+    s1 = reduce(acc1);
   }
 
   // Walk tiles [j_begin, j_end) of one row, writing scores of keys < e_vis.
@@ -174,7 +204,7 @@ __global__ __launch_bounds__(256) void index_score_decode(
         acc = mfma32_bf16(a, b[ks], acc);
       }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) part += wr[mt][i] * fmaxf(acc[i], 0.f);
+      for (int i = 0; i < 16; ++i) part += wr[mt][i] * relu(acc[i]);
     }
     const float tot = add_xor32(part);
     const int64_t j = j_begin + 32 * t + n;
@@ -191,20 +221,88 @@ __global__ __launch_bounds__(256) void index_score_decode(
   }
 }
 
+// Causal rows, keys shared through LDS: a block takes 8 consecutive rows (one
+// per wave; their visible counts differ by at most two entries) and walks the
+// key tiles of the widest of them.  Key tiles travel global -> LDS by
+// asynchronous copies (1 KB per wavefront instruction, spread over the waves)
+// into three stages, so each tile is fetched from L2 once per block instead of
+// once per row; every wave reads it from LDS as its MFMA B operand.  The copy
+// counts per wave are uniform (tiles past the row re-read the last one), so the
+// explicit vector-memory waits count exactly the stages still in flight.
 template <int KEY, int HI, int DI>
-__global__ __launch_bounds__(256) void index_score_causal(
+__global__ __launch_bounds__(512) void index_score_causal_lds(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const void* __restrict__ keys,
-    float* __restrict__ scores, int64_t stride, int64_t E_cap, int m, int W, int32_t seq0, int32_t pos0,
-    int R) {
-  const int grp = gridDim.x - 1 - blockIdx.x;          // longest rows first
-  const int r = grp * 4 + wave_id();
-  if (r >= R) return;
-  const RowRef rr = row_ref(SCKV_ROWS_CAUSAL, nullptr, 0, seq0, pos0, r);
-  const int64_t e_vis = visible(rr.t, m, W, E_cap);
-  if (e_vis == 0) return;
+    float* __restrict__ scores, int64_t stride, int64_t E_cap, int m, int W, int32_t seq0, int32_t pos0, int R) {
+  constexpr int NWR = 8, KS = DI / 16;
+  constexpr int ESZ = KEY == SCKV_BF16 ? 2 : 1;
+  constexpr int TB = 32 * DI * ESZ;                                    // bytes per 32-key tile
+  constexpr int TPS = NWR * 1024 / TB > 2 ? NWR * 1024 / TB : 2;       // tiles per stage
+  constexpr int SB = TPS * TB;                                         // bytes per stage
+  constexpr int CPW = SB / 1024 / NWR;                                 // 1 KB copies per wave per stage
+  constexpr int NSTG = 3;
+  static_assert(CPW >= 1 && SB % (1024 * NWR) == 0, "stage must split evenly over the waves");
+  static_assert(TPS % 2 == 0, "tiles are taken in pairs");
+  __shared__ __attribute__((aligned(16))) uint8_t stg[NSTG * SB];
+
+  const int grp = gridDim.x - 1 - blockIdx.x;                          // longest rows first
+  const int r0 = grp * NWR;
+  const int wv = wave_id(), l = lane_id(), n = l & 31, hh = l >> 5;
+  const int r_last = (r0 + NWR < R ? r0 + NWR : R) - 1;
+  const int r = r0 + wv <= r_last ? r0 + wv : r_last;                  // surplus waves shadow the last row
+  const bool own_row = r0 + wv <= r_last;
+  const int64_t ev_max = visible((int64_t)pos0 + r_last, m, W, E_cap);
+  if (ev_max == 0) return;                                             // whole block: nothing visible
+  const int64_t ev = visible((int64_t)pos0 + r, m, W, E_cap);
+  const int64_t ntiles = (ev_max + 31) / 32;
+  const int64_t nstages = (ntiles + TPS - 1) / TPS;
+
   ScoreWave<KEY, HI, DI> sw;
   sw.load_query(opaque_global(q) + (int64_t)r * HI * DI * 2, w + (int64_t)r * HI);
-  sw.run(opaque_global(keys), rr.seq * E_cap, 0, e_vis, e_vis, scores + (int64_t)r * stride);
+  float* srow = scores + (int64_t)r * stride;
+  const gbytes gk = opaque_global(keys) + (int64_t)seq0 * E_cap * DI * ESZ;
+  const int wu = __builtin_amdgcn_readfirstlane(wv);
+
+  auto issue = [&](int64_t sidx) __attribute__((always_inline)) {
+    uint8_t* S = &stg[(sidx % NSTG) * SB];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const int cb = (wu * CPW + c) * 1024;                            // byte offset within the stage
+      int64_t tile = sidx * TPS + cb / TB;
+      tile = tile < ntiles ? tile : ntiles - 1;
+      copy_to_lds16(gk + tile * TB + (cb % TB) + l * 16, S + cb);
+    }
+  };
+
+  for (int64_t s = 0; s < NSTG - 1 && s < nstages; ++s) issue(s);
+  for (int64_t s = 0; s < nstages; ++s) {
+    if (s + 1 < nstages) wait_vm_lgkm<CPW, 0>();
+    else wait_vm_lgkm<0, 0>();
+    block_barrier();                                                   // stage s visible; stage s-1 free
+    if (s + NSTG - 1 < nstages) issue(s + NSTG - 1);
+    const uint8_t* S = &stg[(s % NSTG) * SB];
+    auto frags = [&](int tt, bf16x8 (&b)[KS]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int off = tt * TB + ((hh * KS + ks) * 32 + n) * 8 * ESZ;
+        if constexpr (KEY == SCKV_BF16) b[ks] = bitcast<bf16x8>(*reinterpret_cast<const u32x4*>(S + off));
+        else b[ks] = bitcast<bf16x8>(e4m3x8_to_bf16x8(*reinterpret_cast<const u32x2*>(S + off)));
+      }
+    };
+    // tiles in pairs (tiles past the block's last one are computed on the copy
+    // of the last tile and not stored)
+#pragma unroll
+    for (int tt = 0; tt < TPS; tt += 2) {
+      const int64_t j0 = (s * TPS + tt) * 32;
+      if (j0 >= ev_max) break;                                         // block-uniform
+      bf16x8 b0[KS], b1[KS];
+      frags(tt, b0);
+      frags(tt + 1, b1);
+      float s0, s1;
+      sw.tile2(b0, b1, s0, s1);
+      if (own_row && hh == 0 && j0 + n < ev) srow[j0 + n] = s0;
+      if (own_row && hh == 0 && j0 + 32 + n < ev) srow[j0 + 32 + n] = s1;
+    }
+  }
 }
 
 // fp32 path: one thread per key, query and weights staged in LDS.
@@ -257,8 +355,8 @@ static void launch_mfma(const sckv_index_args& a, float* scores, int64_t stride,
     else SCKV_DEC(4);
 #undef SCKV_DEC
   } else {
-    const dim3 grid((unsigned)((a.rows.R + 3) / 4));
-    hipLaunchKernelGGL((index_score_causal<KEY, HI, DI>), grid, dim3(256), 0, stream, q, a.w, a.keys, scores,
+    const dim3 grid((unsigned)((a.rows.R + 7) / 8));
+    hipLaunchKernelGGL((index_score_causal_lds<KEY, HI, DI>), grid, dim3(512), 0, stream, q, a.w, a.keys, scores,
                        stride, a.E_cap, a.m, a.W, a.rows.seq0, a.rows.pos0, a.rows.R);
   }
 }
