@@ -40,6 +40,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill indexer measurement")
+    ap.add_argument("--no-1m", action="store_true", help="skip the 1M-context fp8 decode measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy (reference for the HBM byte counters)")
     return ap.parse_args()
@@ -136,6 +137,77 @@ def build_caches(wl, dev, sk, torch, gen):
         del st_c, st_h
     torch.cuda.synchronize()
     return c, h
+
+
+def decode_1m_rate(dev, sk, torch, gen, steps: int = 20, replicas: int = 4):
+    """Decode step of the 1M-context pair (batch 1) with fp8 caches: index + top-2048,
+    CSA and HCA attention, bf16 out.  Cache replicas are rotated (the pair cache is
+    smaller than the 256 MiB MALL)."""
+    from workloads import PAIR_DEC_1M_FP8 as wl
+    csa, hca = wl.layers
+    t = wl.N - 1
+    Ec, Eh = wl.N // csa.m, wl.N // hca.m
+    f8, bf = torch.float8_e4m3fn, torch.bfloat16
+    weights = gen.gpu_weights(wl, dev)
+    s_c, s_h = gen.gpu_sequence_streams(wl, 0, weights, dev)
+    c = {"ent": torch.empty(1, Ec, csa.D, device=dev, dtype=torch.uint8).view(f8),
+         "sc": torch.empty(1, Ec, device=dev),
+         "keys": sk.key_tiles_empty(1, Ec, csa.D_I, torch.uint8, dev).view(f8),
+         "win": torch.empty(1, csa.W, csa.D, device=dev, dtype=bf)}
+    h = {"ent": torch.empty(1, Eh, hca.D, device=dev, dtype=torch.uint8).view(f8),
+         "sc": torch.empty(1, Eh, device=dev),
+         "win": torch.empty(1, hca.W, hca.D, device=dev, dtype=bf)}
+    sk.csa_compress(sk.Pool(s_c["v"][None], s_c["g"][None], weights[0]["bpos"].contiguous(), c["ent"], c["sc"]),
+                    sk.Pool(s_c["vI"][None], s_c["gI"][None], weights[0]["bposI"].contiguous(), c["keys"],
+                            layout=sk.LAYOUT_KEY_TILES), m=csa.m, o=csa.o)
+    sk.hca_compress(sk.Pool(s_h["v"][None], s_h["g"][None], weights[1]["bpos"].contiguous(), h["ent"], h["sc"]),
+                    m=hca.m, o=hca.o)
+    slots = torch.arange(wl.N - csa.W, wl.N, device=dev) % csa.W
+    c["win"][0, slots] = s_c["v"][wl.N - csa.W:]
+    h["win"][0, slots] = s_h["v"][wl.N - hca.W:]
+    del s_c, s_h
+    reps = [(c, h)] + [({k: v.clone() for k, v in c.items()}, {k: v.clone() for k, v in h.items()})
+                       for _ in range(replicas - 1)]
+    qc, qh = gen.gpu_queries(wl, 0, 1, dev), gen.gpu_queries(wl, 1, 1, dev)
+    rows = sk.RowSpec.decode(torch.tensor([t], dtype=torch.int32, device=dev), t)
+    idx = torch.empty(1, csa.k, dtype=torch.int32, device=dev)
+    out_c = torch.empty(1, csa.H, csa.D, device=dev, dtype=bf)
+    out_h = torch.empty(1, hca.H, hca.D, device=dev, dtype=bf)
+    tau = 1.0 / math.sqrt(csa.d_h)
+    ws_i = sk.csa_index_topk(rows, qc["qI"], qc["w"], c["keys"], idx, m=csa.m, W=csa.W, k=csa.k)
+    ws_c = sk.csa_attend(rows, qc["q"], c["ent"], idx, c["win"], out_c, m=csa.m, W=csa.W, softmax_scale=tau,
+                         entry_scale=c["sc"])
+    ws_h = sk.hca_attend(rows, qh["q"], h["ent"], h["win"], out_h, m=hca.m, W=hca.W, softmax_scale=tau,
+                         entry_scale=h["sc"])
+
+    def step(i):
+        cc, hh = reps[i % len(reps)]
+        sk.csa_index_topk(rows, qc["qI"], qc["w"], cc["keys"], idx, m=csa.m, W=csa.W, k=csa.k, workspace=ws_i)
+        sk.csa_attend(rows, qc["q"], cc["ent"], idx, cc["win"], out_c, m=csa.m, W=csa.W, softmax_scale=tau,
+                      entry_scale=cc["sc"], workspace=ws_c)
+        sk.hca_attend(rows, qh["q"], hh["ent"], hh["win"], out_h, m=hca.m, W=hca.W, softmax_scale=tau,
+                      entry_scale=hh["sc"], workspace=ws_h)
+
+    for i in range(5):
+        step(i)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    ev_c, ev_h = (t - csa.W) // csa.m, (t - hca.W) // hca.m
+    nwin = csa.W
+    by = (ev_c * csa.D_I + csa.H_I * csa.D_I * 2 + csa.H_I * 4 + csa.k * 4                       # indexer + top-k
+          + csa.k * (csa.D + 4) + nwin * csa.D * 2 + csa.H * csa.D * 2 * 2                       # CSA attention
+          + ev_h * (hca.D + 4) + nwin * hca.D * 2 + hca.H * hca.D * 2 * 2)                       # HCA attention
+    gbps = by / (ms * 1e-3) / 1e9
+    return {"workload": wl.name, "batch": 1, "context": wl.N, "replicas": replicas, "ms_per_step": ms,
+            "queries_per_s": 1.0 / (ms * 1e-3), "algorithmic_bytes": by, "hbm_GBps": gbps,
+            "hbm_frac": gbps / PEAK_HBM_GBPS}
 
 
 def algorithmic_bytes(wl):
@@ -324,6 +396,10 @@ def main():
         del reps, c0, h0
         torch.cuda.empty_cache()
         rec["prefill_indexer"] = prefill_indexer_rate(dev, sk, torch, CSA_PREFILL_32K_BF16)
+    if not args.no_1m:
+        print("[bench] 1M-context fp8 decode step", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+        rec["decode_1m_fp8"] = decode_1m_rate(dev, sk, torch, gen)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

@@ -21,6 +21,7 @@
 namespace sckv {
 
 constexpr int kPlanChunk = 64;    // split boundaries fall on multiples of this many items
+constexpr int kMaxSplits = 256;   // splits per row: about one block per CU when a single row is decoded
 constexpr int kSegItems = 1024;   // item sources resolved per segment of a block's range
 
 struct AttendParams {
@@ -623,31 +624,55 @@ __global__ __launch_bounds__(256) void attend_dma512(AttendParams p) {
 }
 
 // Merge of split partials (maxima m_s in base-2 logit units):
-// o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, in split order.
-// One block per (head, row); a thread owns four consecutive dims.
+// o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
+// One block per (head, row).  The splits' (m_s, l_s) are read once, one thread
+// per split, and reduced across the block; the weights 2^(m_s - M) wait in
+// LDS while each thread accumulates four consecutive dims over the splits, in
+// split order, with eight splits' loads in flight.  The plan keeps the number
+// of splits at or below the target block count, kMaxSplits.
+
 __global__ __launch_bounds__(128) void attend_combine(const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
                                                       void* __restrict__ out, float* __restrict__ lse, int H, int D,
                                                       int nsplit, int out_dtype) {
+  __shared__ float wgt[kMaxSplits];
+  __shared__ float red[2][2];
   const int r = blockIdx.y, h = blockIdx.x;
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ws_ml[(((int64_t)r * nsplit + s) * H + h) * 2]);
-  float L = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float* ml = &ws_ml[(((int64_t)r * nsplit + s) * H + h) * 2];
-    L += ml[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[0] - M) * ml[1];
+  const int l = lane_id(), w = wave_id();
+  const float* ml = ws_ml + ((int64_t)r * nsplit * H + h) * 2;           // split s at + s * 2 H
+  float mloc = -INFINITY;
+  for (int s = threadIdx.x; s < nsplit; s += 128) {
+    wgt[s] = ml[(int64_t)s * 2 * H];
+    mloc = fmaxf(mloc, wgt[s]);
   }
+  mloc = group_max4(mloc);
+  for (int o = 8; o >= 1; o >>= 1) mloc = fmaxf(mloc, shfl_xor_f(mloc, o));
+  if (l == 0) red[0][w] = mloc;
+  __syncthreads();
+  const float M = fmaxf(red[0][0], red[0][1]);
+  float lloc = 0.f;
+  for (int s = threadIdx.x; s < nsplit; s += 128) {
+    const float ms = wgt[s];
+    const float e = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+    lloc += e * ml[(int64_t)s * 2 * H + 1];
+    wgt[s] = e;
+  }
+  for (int o = 32; o >= 1; o >>= 1) lloc += shfl_xor_f(lloc, o);
+  if (l == 0) red[1][w] = lloc;
+  __syncthreads();
+  const float L = red[1][0] + red[1][1];
   const float inv = 1.f / L;
   for (int d4 = threadIdx.x; d4 < D / 4; d4 += blockDim.x) {
+    const float* src = ws_o + ((int64_t)r * nsplit * H + h) * D + 4 * d4;      // split s at + s H D
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < nsplit; ++s) {
-      const int64_t base = ((int64_t)r * nsplit + s) * H + h;
-      const float ms = ws_ml[base * 2];
-      if (ms != -INFINITY) {
-        const float wgt = __builtin_amdgcn_exp2f(ms - M);
-        const f32x4 v = *reinterpret_cast<const f32x4*>(&ws_o[base * D + 4 * d4]);
-        acc += wgt * v;
-      }
+    int s = 0;
+    for (; s + 8 <= nsplit; s += 8) {
+      f32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const f32x4*>(src + (int64_t)(s + u) * H * D);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += wgt[s + u] * v[u];
     }
+    for (; s < nsplit; ++s) acc += wgt[s] * *reinterpret_cast<const f32x4*>(src + (int64_t)s * H * D);
     const int64_t off = ((int64_t)r * H + h) * D + 4 * d4;
     if (out_dtype == SCKV_BF16) {
       uint16_t* o = static_cast<uint16_t*>(out) + off;
@@ -763,7 +788,7 @@ AttendPlan plan_attend(const sckv_attend_args& a, bool csa) {
     return pl;
   }
   // about one block per CU (256): splits per row, each of at least two chunks
-  const int64_t target_blocks = 256;
+  const int64_t target_blocks = kMaxSplits;
   int64_t ns = (target_blocks + a.rows.R / 2) / a.rows.R;
   ns = ns < 1 ? 1 : (ns > pl.chunks ? pl.chunks : ns);
   int64_t per = (pl.chunks + ns - 1) / ns;
@@ -773,6 +798,7 @@ AttendPlan plan_attend(const sckv_attend_args& a, bool csa) {
   pl.per_split = per * kPlanChunk;       // in items
   pl.nsplit = (int32_t)((pl.chunks + per - 1) / per);
   if (pl.nsplit < 1) pl.nsplit = 1;
+  if (pl.nsplit > kMaxSplits) return pl;     // cannot happen: nsplit <= ns <= target_blocks
   if (pl.nsplit > 1)
     pl.ws_bytes = (size_t)a.rows.R * pl.nsplit * a.H * ((size_t)a.D + 2) * sizeof(float) + 256;
   pl.ok = true;

@@ -47,28 +47,16 @@ __device__ __forceinline__ uint32_t f32_to_e4m3_sat(float x) {
 }
 
 // e4m3 code -> bf16 bits (exact: every e4m3 value is a bf16 value).
-__device__ __forceinline__ uint32_t e4m3_to_bf16_bits(uint32_t c) {
-  const uint32_t s = (c & 0x80u) << 8;
-  const uint32_t e = (c >> 3) & 15u, mt = c & 7u;
-  if (e) return s | ((e + 120u) << 7) | (mt << 4);
-  // subnormal mt * 2^-9: normalise (mt = 0 is a signed zero)
-  if (mt == 0) return s;
-  const uint32_t lz = (mt >= 4) ? 0u : (mt >= 2 ? 1u : 2u);   // leading position of mt
-  const uint32_t ex = 120u - lz;                                // exponent field of 2^(-7-lz)
-  const uint32_t frac = ((mt << (lz + 1)) & 7u) << 4;           // drop the leading one
-  return s | (ex << 7) | frac;
-}
-
-__device__ __forceinline__ float e4m3_to_f32(uint32_t c) { return bf16_to_f32(e4m3_to_bf16_bits(c)); }
-
-// 8 e4m3 codes (little-endian in two dwords) -> 8 bf16 packed in four dwords.
+// 8 e4m3 codes (little-endian in two dwords) -> 8 bf16 packed in four dwords,
+// by the gfx950 conversion instruction (two codes per instruction).  Every
+// e4m3 value is exact in bf16; with scale 1 the instruction decodes all finite
+// OCP e4m3 codes (subnormals included) to their exact values.
 __device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(u32x2 v) {
   u32x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t w = v[i >> 1] >> ((i & 1) * 16);
-    r[i] = e4m3_to_bf16_bits(w & 0xffu) | (e4m3_to_bf16_bits((w >> 8) & 0xffu) << 16);
-  }
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)v[0], 1.0f, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)v[0], 1.0f, true));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)v[1], 1.0f, false));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)v[1], 1.0f, true));
   return r;
 }
 
