@@ -4,16 +4,19 @@
 // fixed by the CSA decode workload definition).
 //
 // MFMA path (bf16 queries; bf16 or e4m3 keys dequantised exactly to bf16): the
-// contraction is [H_I x D_I] . [D_I x 32 keys] per tile on v_mfma_f32_32x32x16_bf16,
-// heads as M, keys as N.  Each lane owns one key column and 16 head rows per
-// 32-head tile, so the ReLU . w head reduction is lane-local plus one exchange
-// between the two half-waves.  The D_I axis is split between the half-waves as
-// two contiguous halves: a lane streams 128 contiguous key bytes per tile.
-//   decode rows : a block takes one row and 4 waves x NT tiles of 32 keys, keys
-//                 streamed from HBM straight into MFMA fragments
-//   causal rows : a block takes 8 consecutive rows (one per wave) and walks every
-//                 visible key tile through LDS (each tile fetched once per block);
-//                 blocks with the longest rows start first
+// contraction is [H_I x D_I] . [D_I x 32 keys] per tile, heads as M, keys as N.
+//   decode rows : (HBM-bound) v_mfma_f32_32x32x16_bf16; each lane owns one key
+//                 column and 16 head rows per 32-head tile, so the ReLU . w head
+//                 reduction is lane-local plus one exchange between the two
+//                 half-waves; D_I is split between the half-waves as two
+//                 contiguous halves (a lane streams 128 contiguous key bytes per
+//                 tile).  A block takes one row and 4 waves x NT tiles of 32 keys,
+//                 keys streamed from HBM straight into MFMA fragments.
+//   causal rows : (MFMA-bound) v_mfma_f32_16x16x32_bf16; a block takes 8
+//                 consecutive rows (one per wave) and walks every visible key
+//                 tile through LDS (each tile fetched once per block), each wave
+//                 overlapping one tile's products with the previous tile's
+//                 reduction; blocks with the longest rows start first
 #include "device_common.h"
 #include "sckv_internal.h"
 
@@ -63,91 +66,83 @@ __device__ __forceinline__ void load_key_tile(gbytes keys, int64_t elem0, bf16x8
   }
 }
 
+// Causal-row scoring of one wave on v_mfma_f32_16x16x32_bf16: heads as M in tiles
+// of 16, keys as N in two 16-key halves of a 32-key tile, D_I as K in steps of
+// 32.  (Under this load gfx950 holds a higher clock with this shape than with
+// 32x32x16, which outweighs the extra instructions.)  Lane l
+// holds key (l % 16) of each half and heads 16 mt + 4 (l / 16) + i, so the head
+// reduction is lane-local over MT x 4 values per half, then across the four
+// 16-lane groups: one half-wave swap that also separates the halves (lanes 0-31
+// keep half 0, lanes 32-63 half 1), then one 16-lane swap.
 template <int KEY, int HI, int DI>
 struct ScoreWave {
-  static constexpr int MT = HI / 32;
-  static constexpr int KS = DI / 16;
+  static constexpr int MT = HI / 16;
+  static constexpr int KS = DI / 32;
   bf16x8 a[MT][KS];
-  float w[MT][16];
+  float w[MT][4];
+  using Frag = bf16x8[2][KS];
+  using Acc = f32x4[2][MT];
 
   __device__ __forceinline__ void load_query(gbytes q_row, const float* w_row) {
-    const int l = lane_id(), n = l & 31, hh = l >> 5;
+    const int l = lane_id(), c = l & 15, g = l >> 4;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const int64_t e0 = (int64_t)(32 * mt + n) * DI + hh * (DI / 2);
+      const int64_t e0 = (int64_t)(16 * mt + c) * DI + 8 * g;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) a[mt][ks] = bitcast<bf16x8>(gload<u32x4>(q_row, (e0 + 8 * ks) * 2));
+      for (int ks = 0; ks < KS; ++ks) a[mt][ks] = bitcast<bf16x8>(gload<u32x4>(q_row, (e0 + 32 * ks) * 2));
 #pragma unroll
-      for (int i = 0; i < 16; ++i) w[mt][i] = w_row[32 * mt + 8 * (i >> 2) + 4 * hh + (i & 3)];
+      for (int i = 0; i < 4; ++i) w[mt][i] = w_row[16 * mt + 4 * g + i];
     }
   }
 
-  // Scores of keys [j0, j0 + 32) (keys beyond e_vis are computed on a clamped
-  // row and not stored).
-  // The head tiles' accumulation chains are interleaved k-step by k-step, so
-  // consecutive MFMAs never wait on each other's results.
-  __device__ __forceinline__ float tile(const bf16x8 (&b)[KS]) const {
-    f32x16 acc[MT];
+  // half nh, k-step ks: dims 32 ks + 8 (l / 16) .. +7 of key 16 nh + l % 16
+  __device__ __forceinline__ static void frags(const uint8_t* tile, bf16x8 (&b)[2][KS]) {
+    constexpr int ESZ = KEY == SCKV_BF16 ? 2 : 1;
+    const int l = lane_id(), c = l & 15, g = l >> 4;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{};
+    for (int nh = 0; nh < 2; ++nh)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int off = ((4 * ks + g) * 32 + 16 * nh + c) * 8 * ESZ;
+        if constexpr (KEY == SCKV_BF16) b[nh][ks] = bitcast<bf16x8>(*reinterpret_cast<const u32x4*>(tile + off));
+        else b[nh][ks] = bitcast<bf16x8>(e4m3x8_to_bf16x8(*reinterpret_cast<const u32x2*>(tile + off)));
+      }
+  }
+  __device__ __forceinline__ static int lane_key() { const int l = lane_id(); return (l & 15) | ((l & 32) >> 1); }
+  __device__ __forceinline__ static void zero(f32x4 (&acc)[2][MT]) {
+#pragma unroll
+    for (int nh = 0; nh < 2; ++nh)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[nh][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  __device__ __forceinline__ static bool lane_stores() { return !(lane_id() & 16); }
+
+  __device__ __forceinline__ void mfmas(const bf16x8 (&b)[2][KS], f32x4 (&acc)[2][MT]) const {
+#pragma unroll
+    for (int nh = 0; nh < 2; ++nh)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[nh][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma32_bf16(a[mt][ks], b[ks], acc[mt]);
-    return reduce(acc);
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nh = 0; nh < 2; ++nh) acc[nh][mt] = mfma16_bf16(a[mt][ks], b[nh][ks], acc[nh][mt]);
   }
 
-  // sum_h w_h max(0, acc_h) over the lane's heads, then over the two half-waves
-  __device__ __forceinline__ float reduce(const f32x16 (&acc)[MT]) const {
-    float part = 0.f;
+  __device__ __forceinline__ float reduce(const f32x4 (&acc)[2][MT]) const {
+    float part[2] = {0.f, 0.f};
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int nh = 0; nh < 2; ++nh)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) part += w[mt][i] * relu(acc[mt][i]);
-    const float tot = add_xor32(part);
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part[nh] += w[mt][i] * relu(acc[nh][mt][i]);
+    const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[1]), false, false);
+    const float s = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+    const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+    const float tot = __uint_as_float(y[0]) + __uint_as_float(y[1]);
     return tot == 0.f ? 0.f : tot;
-  }
-
-  // Two tiles at once: their 2 MT accumulation chains interleaved, then both
-  // reductions (the second tile's MFMAs still run while the first is reduced).
-  __device__ __forceinline__ void tile2(const bf16x8 (&b0)[KS], const bf16x8 (&b1)[KS], float& s0,
-                                        float& s1) const {
-    f32x16 acc0[MT], acc1[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc0[mt] = acc1[mt] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        acc0[mt] = mfma32_bf16(a[mt][ks], b0[ks], acc0[mt]);
-        acc1[mt] = mfma32_bf16(a[mt][ks], b1[ks], acc1[mt]);
-      }
-    s0 = reduce(acc0);
-    s1 = reduce(acc1);
-  }
-
-  // Walk tiles [j_begin, j_end) of one row, writing scores of keys < e_vis.
-  __device__ __forceinline__ void run(gbytes keys, int64_t key_base_row, int64_t j_begin,
-                                      int64_t j_end, int64_t e_vis, float* srow) const {
-    const int l = lane_id(), n = l & 31, hh = l >> 5;
-    auto row_elem = [&](int64_t j0) {
-      int64_t key = j0 + n;
-      key = key < e_vis ? key : e_vis - 1;
-      return key_tile_elem<DI>(key_base_row * DI, key, hh * (DI / 16));
-    };
-    if (j_begin >= j_end) return;
-    bf16x8 cur[KS], nxt[KS];
-    load_key_tile<KEY, DI>(keys, row_elem(j_begin), cur);
-    for (int64_t j0 = j_begin; j0 < j_end; j0 += 32) {
-      const bool more = j0 + 32 < j_end;
-      if (more) load_key_tile<KEY, DI>(keys, row_elem(j0 + 32), nxt);
-      const float s = tile(cur);
-      if (hh == 0 && j0 + n < e_vis) srow[j0 + n] = s;
-      if (more) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) cur[ks] = nxt[ks];
-      }
-    }
   }
 };
 
@@ -225,84 +220,108 @@ __global__ __launch_bounds__(256) void index_score_decode(
 // per wave; their visible counts differ by at most two entries) and walks the
 // key tiles of the widest of them.  Key tiles travel global -> LDS by
 // asynchronous copies (1 KB per wavefront instruction, spread over the waves)
-// into three stages, so each tile is fetched from L2 once per block instead of
-// once per row; every wave reads it from LDS as its MFMA B operand.  The copy
-// counts per wave are uniform (tiles past the row re-read the last one), so the
-// explicit vector-memory waits count exactly the stages still in flight.
+// into stages of 64 KB (pairs of tiles A, B; two or three stages), so each tile
+// is fetched from L2 once per block instead of once per row; every wave reads it
+// from LDS as its MFMA B operand.  The copy counts per wave are uniform (tiles past the row
+// re-read the last one), so the explicit vector-memory waits count exactly the
+// stages still in flight (later score stores only make them stricter).
+//
+// Each wave runs a two-tile software pipeline: the MFMAs of one tile are issued
+// next to the ReLU . w reduction of the tile before it (independent work for
+// the matrix core and the vector ALU), and the B fragments of the next tile are
+// read from LDS one step ahead.
 template <int KEY, int HI, int DI>
 __global__ __launch_bounds__(512) void index_score_causal_lds(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const void* __restrict__ keys,
     float* __restrict__ scores, int64_t stride, int64_t E_cap, int m, int W, int32_t seq0, int32_t pos0, int R) {
-  constexpr int NWR = 8, KS = DI / 16;
+  constexpr int NWR = 8;
   constexpr int ESZ = KEY == SCKV_BF16 ? 2 : 1;
   constexpr int TB = 32 * DI * ESZ;                                    // bytes per 32-key tile
-  constexpr int TPS = NWR * 1024 / TB > 2 ? NWR * 1024 / TB : 2;       // tiles per stage
-  constexpr int SB = TPS * TB;                                         // bytes per stage
-  constexpr int CPW = SB / 1024 / NWR;                                 // 1 KB copies per wave per stage
-  constexpr int NSTG = 3;
-  static_assert(CPW >= 1 && SB % (1024 * NWR) == 0, "stage must split evenly over the waves");
-  static_assert(TPS % 2 == 0, "tiles are taken in pairs");
+  constexpr int PPS = 32768 / TB;                                      // tile pairs per stage (64 KB)
+  constexpr int SB = 2 * PPS * TB;                                     // bytes per stage
+  constexpr int NC = SB / 1024;                                        // 1 KB copies per stage
+  constexpr int CPW = NC >= NWR ? NC / NWR : 1;                        // copies per copying wave
+  constexpr int NSTG = 3 * SB <= 96 * 1024 ? 3 : 2;
+  static_assert(NC >= 1 && (NC < NWR ? 1 : NC % NWR == 0), "stage must split evenly over the waves");
   __shared__ __attribute__((aligned(16))) uint8_t stg[NSTG * SB];
 
   const int grp = gridDim.x - 1 - blockIdx.x;                          // longest rows first
   const int r0 = grp * NWR;
-  const int wv = wave_id(), l = lane_id(), n = l & 31, hh = l >> 5;
+  const int wv = wave_id(), l = lane_id();
   const int r_last = (r0 + NWR < R ? r0 + NWR : R) - 1;
   const int r = r0 + wv <= r_last ? r0 + wv : r_last;                  // surplus waves shadow the last row
   const bool own_row = r0 + wv <= r_last;
   const int64_t ev_max = visible((int64_t)pos0 + r_last, m, W, E_cap);
   if (ev_max == 0) return;                                             // whole block: nothing visible
   const int64_t ev = visible((int64_t)pos0 + r, m, W, E_cap);
-  const int64_t ntiles = (ev_max + 31) / 32;
-  const int64_t nstages = (ntiles + TPS - 1) / TPS;
+  const int ntiles = (int)((ev_max + 31) / 32);
+  const int npairs = (ntiles + 1) / 2;
+  const int nst = (npairs + PPS - 1) / PPS;
 
-  ScoreWave<KEY, HI, DI> sw;
+  using SW = ScoreWave<KEY, HI, DI>;
+  SW sw;
   sw.load_query(opaque_global(q) + (int64_t)r * HI * DI * 2, w + (int64_t)r * HI);
   float* srow = scores + (int64_t)r * stride;
   const gbytes gk = opaque_global(keys) + (int64_t)seq0 * E_cap * DI * ESZ;
   const int wu = __builtin_amdgcn_readfirstlane(wv);
+  const bool copier = NC >= NWR || wu < NC;
+  const int lkey = SW::lane_key();
+  const bool lstore = own_row && SW::lane_stores();
 
-  auto issue = [&](int64_t sidx) __attribute__((always_inline)) {
-    uint8_t* S = &stg[(sidx % NSTG) * SB];
+  auto issue = [&](int st, int buf) __attribute__((always_inline)) {
+    if (!copier) return;
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
       const int cb = (wu * CPW + c) * 1024;                            // byte offset within the stage
-      int64_t tile = sidx * TPS + cb / TB;
+      int tile = 2 * PPS * st + cb / TB;
       tile = tile < ntiles ? tile : ntiles - 1;
-      copy_to_lds16(gk + tile * TB + (cb % TB) + l * 16, S + cb);
+      copy_to_lds16(gk + (int64_t)tile * TB + (cb % TB) + l * 16, &stg[buf * SB + cb]);
     }
   };
+  auto store = [&](int tile, float v) __attribute__((always_inline)) {
+    const int64_t j = (int64_t)tile * 32 + lkey;
+    if (lstore && j < ev) srow[j] = v;
+  };
 
-  for (int64_t s = 0; s < NSTG - 1 && s < nstages; ++s) issue(s);
-  for (int64_t s = 0; s < nstages; ++s) {
-    if (s + 1 < nstages) wait_vm_lgkm<CPW, 0>();
-    else wait_vm_lgkm<0, 0>();
-    block_barrier();                                                   // stage s visible; stage s-1 free
-    if (s + NSTG - 1 < nstages) issue(s + NSTG - 1);
-    const uint8_t* S = &stg[(s % NSTG) * SB];
-    auto frags = [&](int tt, bf16x8 (&b)[KS]) __attribute__((always_inline)) {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int off = tt * TB + ((hh * KS + ks) * 32 + n) * 8 * ESZ;
-        if constexpr (KEY == SCKV_BF16) b[ks] = bitcast<bf16x8>(*reinterpret_cast<const u32x4*>(S + off));
-        else b[ks] = bitcast<bf16x8>(e4m3x8_to_bf16x8(*reinterpret_cast<const u32x2*>(S + off)));
+  for (int st = 0; st < NSTG && st < nst; ++st) issue(st, st);
+  if (NSTG == 3 && nst > 2) wait_vm_lgkm<2 * CPW, 0>();
+  else if (nst > 1) wait_vm_lgkm<CPW, 0>();
+  else wait_vm_lgkm<0, 0>();
+  block_barrier();                                                     // stage 0 visible
+
+  typename SW::Frag bA, bB;
+  typename SW::Acc accA, accB;
+  SW::zero(accB);                                                      // reduced (unused) for the first pair
+  SW::frags(&stg[0], bA);
+  int cur = 0, st = 0, gi = 0;                                         // buffer, stage, pair within it
+  for (int g = 0; g < npairs; ++g) {
+    // tile A of pair g on the matrix core, tile B of pair g-1 reduced
+    SW::frags(&stg[cur * SB + (2 * gi + 1) * TB], bB);
+    sw.mfmas(bA, accA);
+    const float sB = sw.reduce(accB);
+    if (g > 0) store(2 * g - 1, sB);
+    int ncur = cur, ngi = gi + 1;
+    if (ngi == PPS) {                                                  // next pair in the next stage
+      if (st + 1 < nst) {
+        if (NSTG == 3 && st + 2 < nst) wait_vm_lgkm<CPW, 0>();
+        else wait_vm_lgkm<0, 0>();
+        block_barrier();                                               // stage st+1 visible; buffer cur free
+        if (st + NSTG < nst) issue(st + NSTG, cur);
       }
-    };
-    // tiles in pairs (tiles past the block's last one are computed on the copy
-    // of the last tile and not stored)
-#pragma unroll
-    for (int tt = 0; tt < TPS; tt += 2) {
-      const int64_t j0 = (s * TPS + tt) * 32;
-      if (j0 >= ev_max) break;                                         // block-uniform
-      bf16x8 b0[KS], b1[KS];
-      frags(tt, b0);
-      frags(tt + 1, b1);
-      float s0, s1;
-      sw.tile2(b0, b1, s0, s1);
-      if (own_row && hh == 0 && j0 + n < ev) srow[j0 + n] = s0;
-      if (own_row && hh == 0 && j0 + 32 + n < ev) srow[j0 + 32 + n] = s1;
+      ncur = cur == NSTG - 1 ? 0 : cur + 1;
+      ngi = 0;
+      ++st;
     }
+    // tile B on the matrix core, tile A reduced; tile A of the next pair read
+    // ahead (after the last pair it reads a settled buffer and is unused)
+    SW::frags(&stg[ncur * SB + 2 * ngi * TB], bA);
+    sw.mfmas(bB, accB);
+    const float sA = sw.reduce(accA);
+    store(2 * g, sA);
+    cur = ncur;
+    gi = ngi;
   }
+  store(2 * npairs - 1, sw.reduce(accB));
 }
 
 // fp32 path: one thread per key, query and weights staged in LDS.

@@ -59,6 +59,23 @@ def assert_close(g, o, *, rtol=None, atol=None, what=""):
     return err
 
 
+def index_term_magnitude(q, w, keys):
+    """Largest sum_h |w_h| max(0, q_h . k_j) over the keys: the size of the terms an
+    indexer score adds up.  fp32 accumulation error scales with it, not with the
+    score, which cancellation between heads of opposite weight can make small."""
+    d = np.maximum(np.asarray(q, np.float64) @ np.asarray(keys, np.float64).T, 0.0)   # [H_I, E]
+    return float(np.max(np.abs(np.asarray(w, np.float64)) @ d)) if d.size else 0.0
+
+
+def assert_scores_close(g, o, q, w, keys, *, rtol, what=""):
+    """Normwise check of indexer scores against the larger of max |score| and the
+    term magnitude (index_term_magnitude)."""
+    err, scale = normwise(g, o)
+    scale = max(scale, index_term_magnitude(q, w, keys))
+    assert err <= rtol * max(scale, 1e-30), f"{what}: max err {err:.3e} > {rtol} * {scale:.3e}"
+    return err
+
+
 def _spacing(y, sig_bits, min_normal_exp):
     """Distance between consecutive representable values around y (the larger one at a binade edge)."""
     _, e = np.frexp(np.asarray(y, np.float64))

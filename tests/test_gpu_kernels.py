@@ -9,7 +9,7 @@ import pytest
 import torch
 
 from oracle import codecs, method
-from tests.compare import assert_close, bf16_code_flips, e4m3_flips, topk_parity
+from tests.compare import assert_close, assert_scores_close, bf16_code_flips, e4m3_flips, topk_parity
 from tests.gpu_util import DEV, dev, dev_codes, dev_i32, host, rng_store
 
 pytestmark = pytest.mark.gpu
@@ -185,7 +185,7 @@ def test_index_topk_decode(keys_s, HI, DI, E_cap, positions, k):
         ev = min(method.entries_visible(t, 4, 128), E_cap)
         s = method.index_scores(q[r], w[r], kv[r, :ev])
         if ev:
-            assert_close(gs[r, :ev], s, rtol=2e-6, what=f"scores row {r}")
+            assert_scores_close(gs[r, :ev], s, q[r], w[r], kv[r, :ev], rtol=2e-6, what=f"scores row {r}")
         ok, msg = topk_parity(gi[r], method.topk(s, k), s)
         assert ok, f"row {r} (t={t}, E_vis={ev}): {msg}"
         sel = gi[r][gi[r] >= 0]
@@ -197,6 +197,8 @@ CAUSAL_CASES = [
     ("bf16", 64, 128, 800, 3300, 64),
     ("f32", 4, 32, 300, 1300, 16),
     ("e4m3", 64, 128, 600, 2500, 128),
+    ("bf16", 32, 64, 700, 2900, 32),
+    ("e4m3", 64, 64, 500, 2123, 64),
 ]
 
 
@@ -210,12 +212,18 @@ def test_index_topk_causal(keys_s, HI, DI, E_cap, T, k):
     _, _, kv, _, _, keysd = _index_inputs(rng, keys_s, HI, DI, 1, E_cap)
     rows = sk.RowSpec.causal(T)
     out_idx = torch.full((T, k), -7, device=DEV, dtype=torch.int32)
+    cover = min(method.entries_visible(T - 1, 4, 128), E_cap)
+    scores = torch.full((T, cover + 5), float("nan"), device=DEV, dtype=torch.float32)
+    sk.csa_index_score(rows, dev(q, qs), dev(w), keysd, scores, m=4, W=128, k=k)
     sk.csa_index_topk(rows, dev(q, qs), dev(w), keysd, out_idx, m=4, W=128, k=k)
     torch.cuda.synchronize()
-    gi = host(out_idx)
+    gi, gs = host(out_idx), host(scores)
     for t in range(T):
         ev = min(method.entries_visible(t, 4, 128), E_cap)
         s = method.index_scores(q[t], w[t], kv[0, :ev])
+        if ev:
+            assert_scores_close(gs[t, :ev], s, q[t], w[t], kv[0, :ev], rtol=2e-6, what=f"scores row {t}")
+        assert np.all(np.isnan(gs[t, ev:])), f"row {t}: scores written past the {ev} visible entries"
         ok, msg = topk_parity(gi[t], method.topk(s, k), s)
         assert ok, f"row {t} (E_vis={ev}): {msg}"
 

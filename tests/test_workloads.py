@@ -1,5 +1,6 @@
 """The seeded generator: determinism, chunk independence, shapes and distributions."""
 import numpy as np
+import pytest
 
 from workloads import ALL, CSA_PREFILL_32K_BF16, PAIR_DEC_128K_BF16, gen
 
@@ -62,3 +63,17 @@ def test_all_workloads_declared():
                 assert (L.m, L.o) == (4, 4) and L.k > 0
             else:
                 assert (L.m, L.o) == (128, 0)
+
+
+def test_index_term_magnitude_and_score_check():
+    """The score check's scale: sum_h |w_h| max(0, q_h . k) of the largest key."""
+    from tests.compare import assert_scores_close, index_term_magnitude
+    q = np.array([[1.0, 2.0], [3.0, -1.0]])          # two heads, D_I = 2
+    w = np.array([-2.0, 0.5])
+    keys = np.array([[1.0, 1.0], [0.0, -1.0]])
+    # key 0: q.k = (3, 2) -> 2*3 + 0.5*2 = 7; key 1: (-2, 1) -> 0 + 0.5*1 = 0.5
+    assert index_term_magnitude(q, w, keys) == 7.0
+    scores = np.array([-2.0 * 3 + 0.5 * 2, 0.5])      # -5, 0.5
+    assert_scores_close(scores + 1e-6, scores, q, w, keys, rtol=2e-6)
+    with pytest.raises(AssertionError):
+        assert_scores_close(scores + 1e-4, scores, q, w, keys, rtol=2e-6)
