@@ -212,7 +212,7 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma(AttendParams p) {
 
   const int r = blockIdx.y, split = blockIdx.x;
   const RowItems ri = row_items(p, r);
-  const int l = lane_id(), w = wave_id();
+  const int l = lane_id(), w = wave_id() + NW * blockIdx.z;  // 16-head group of this wave
   const int col = l & 15, g = l >> 4;
   const int head = 16 * w + col;
 
@@ -773,6 +773,11 @@ __global__ __launch_bounds__(256) void attend_f32(AttendParams p, int D) {
     for (int h = threadIdx.x; h < H; h += 256) p.lse[(int64_t)r * H + h] = mrun[h] + logf(lrun[h]);
 }
 
+// the bf16, D = 512, 64-head shape runs on attend_dma512
+static bool dma512_path(const sckv_attend_args& a) {
+  return a.entry_dtype == SCKV_BF16 && a.D == 512 && a.H == 64;
+}
+
 AttendPlan plan_attend(const sckv_attend_args& a, bool csa) {
   AttendPlan pl;
   const int64_t t = a.rows.kind == SCKV_ROWS_DECODE ? a.rows.pos_max : (int64_t)a.rows.pos0 + a.rows.R - 1;
@@ -787,12 +792,17 @@ AttendPlan plan_attend(const sckv_attend_args& a, bool csa) {
     pl.ok = true;
     return pl;
   }
-  // about one block per CU (256): splits per row, each of at least two chunks
+  // about one block per CU (256): splits per row, each of at least two chunks,
+  // or of single chunks when there are few rows (their partials are small)
   const int64_t target_blocks = kMaxSplits;
-  int64_t ns = (target_blocks + a.rows.R / 2) / a.rows.R;
+  const int waves = a.H / 16;
+  // blocks of 1, 2, 4 or 8 waves: other head counts take one wave per 16-head group
+  if ((waves & (waves - 1)) != 0) pl.hgroups = waves;
+  const int64_t rows_x = (int64_t)a.rows.R * pl.hgroups;
+  int64_t ns = (target_blocks + rows_x / 2) / rows_x;
   ns = ns < 1 ? 1 : (ns > pl.chunks ? pl.chunks : ns);
   int64_t per = (pl.chunks + ns - 1) / ns;
-  const int64_t min_per = pl.chunks < 2 ? pl.chunks : 2;
+  const int64_t min_per = a.rows.R <= 16 ? 1 : (pl.chunks < 2 ? pl.chunks : 2);
   per = per < min_per ? min_per : per;
   per = per < 1 ? 1 : per;
   pl.per_split = per * kPlanChunk;       // in items
@@ -806,28 +816,31 @@ AttendPlan plan_attend(const sckv_attend_args& a, bool csa) {
 }
 
 template <int ENT, int D>
-static void launch_mfma_d(const AttendParams& p, int H, dim3 grid, hipStream_t s) {
-  if (ENT == SCKV_BF16 && D == 512 && H == 64) {
+static void launch_mfma_d(const AttendParams& p, int H, int hgroups, dim3 grid, hipStream_t s) {
+  if (ENT == SCKV_BF16 && D == 512 && H == 64) {         // dma512_path
     hipLaunchKernelGGL(attend_dma512, dim3(grid.x * grid.y), dim3(256), 0, s, p);
   } else {
-    // register-staged chunks: 64 items when the latent is narrow, 32 at D = 512
+    // register-staged chunks: 64 items when the latent is narrow, 32 at D = 512;
+    // grid.z = head groups, each block takes H / 16 / hgroups waves of 16 heads
     constexpr int CH = D <= 256 ? 64 : 32;
-    switch (H / 16) {
+    grid.z = (unsigned)hgroups;
+    switch (H / 16 / hgroups) {    // the plan keeps this in {1, 2, 4, 8}
       case 1: hipLaunchKernelGGL((attend_mfma<ENT, D, 1, CH>), grid, dim3(64), 0, s, p); break;
       case 2: hipLaunchKernelGGL((attend_mfma<ENT, D, 2, CH>), grid, dim3(128), 0, s, p); break;
       case 4: hipLaunchKernelGGL((attend_mfma<ENT, D, 4, CH>), grid, dim3(256), 0, s, p); break;
-      default: hipLaunchKernelGGL((attend_mfma<ENT, D, 8, CH>), grid, dim3(512), 0, s, p); break;
+      case 8: hipLaunchKernelGGL((attend_mfma<ENT, D, 8, CH>), grid, dim3(512), 0, s, p); break;
+      default: break;
     }
   }
 }
 
 template <int ENT>
-static void launch_mfma_e(const AttendParams& p, int H, int D, dim3 grid, hipStream_t s) {
+static void launch_mfma_e(const AttendParams& p, int H, int hgroups, int D, dim3 grid, hipStream_t s) {
   switch (D) {
-    case 64: launch_mfma_d<ENT, 64>(p, H, grid, s); break;
-    case 128: launch_mfma_d<ENT, 128>(p, H, grid, s); break;
-    case 256: launch_mfma_d<ENT, 256>(p, H, grid, s); break;
-    default: launch_mfma_d<ENT, 512>(p, H, grid, s); break;
+    case 64: launch_mfma_d<ENT, 64>(p, H, hgroups, grid, s); break;
+    case 128: launch_mfma_d<ENT, 128>(p, H, hgroups, grid, s); break;
+    case 256: launch_mfma_d<ENT, 256>(p, H, hgroups, grid, s); break;
+    default: launch_mfma_d<ENT, 512>(p, H, hgroups, grid, s); break;
   }
 }
 
@@ -868,8 +881,8 @@ hipError_t launch_attend(const sckv_attend_args& a, bool csa, const AttendPlan& 
     return hipGetLastError();
   }
   const dim3 grid((unsigned)pl.nsplit, (unsigned)a.rows.R);
-  if (a.entry_dtype == SCKV_E4M3) launch_mfma_e<SCKV_E4M3>(p, a.H, a.D, grid, stream);
-  else launch_mfma_e<SCKV_BF16>(p, a.H, a.D, grid, stream);
+  if (a.entry_dtype == SCKV_E4M3) launch_mfma_e<SCKV_E4M3>(p, a.H, pl.hgroups, a.D, grid, stream);
+  else launch_mfma_e<SCKV_BF16>(p, a.H, pl.hgroups, a.D, grid, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.nsplit == 1) return e;
   hipLaunchKernelGGL(attend_combine, dim3(a.H, a.rows.R), dim3(128), 0, stream, p.ws_o, p.ws_ml, a.out, a.lse,

@@ -47,6 +47,7 @@ struct AttendPlan {
   int64_t chunks = 0;       // items / 64 rounded up
   int64_t per_split = 0;    // items per split (a multiple of 64)
   int32_t nsplit = 1;
+  int32_t hgroups = 1;      // blocks per (row, split), each taking H / hgroups heads
   bool mfma = false;
   size_t ws_bytes = 0;      // split partials (0 when nsplit == 1)
   bool ok = false;

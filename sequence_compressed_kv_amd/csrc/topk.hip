@@ -121,14 +121,14 @@ __device__ __forceinline__ void ordered_scan(const uint32_t (&c)[NI], uint32_t (
 
 // MODE TOPK_ROW   : scores of row r, elements 0 .. n-1 (n = visible count), out to out_idx.
 // MODE TOPK_SLICE : slice blockIdx.x of row r, local top-k written as candidates.
-// MODE TOPK_MERGE : the candidates of row r (slot q valid iff q % kc < count[r][q / kc]).
+// MODE TOPK_MERGE : the candidates of row r (nslices x kc slots; unused slots hold index -1).
 // Wave w owns elements [w*64*V, (w+1)*64*V); its group i is read as one coalesced
 // 1 KB load: lane l takes elements w*64*V + (i*64 + l)*4 .. +3.
 template <int NT, int V, int MODE>
 __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scores, int64_t stride,
                                                   TopkRows rows, int k, int64_t slice, int nslices, int kc,
                                                   int64_t cap, float* __restrict__ cand_s,
-                                                  int32_t* __restrict__ cand_i, int32_t* __restrict__ cand_n,
+                                                  int32_t* __restrict__ cand_i,
                                                   int32_t* __restrict__ out_idx, float* __restrict__ out_score) {
   constexpr int NI = V / 4;
   __shared__ uint32_t hist[kBins];
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
     len = n_row - base;
     len = len < 0 ? 0 : (len > slice ? slice : len);
   } else {
-    len = cap;
+    len = (int64_t)nslices * kc;
   }
 
   uint32_t key[V];
@@ -168,15 +168,20 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
         if (e0 + j < len) s4[j] = src[e0 + j];
     }
     if (MODE == TOPK_MERGE) {
+      if (vec && e0 + 3 < len) {
+        const i32x4 v = *reinterpret_cast<const i32x4*>(cand_i + (int64_t)r * cap + e0);
+        i4[0] = v[0]; i4[1] = v[1]; i4[2] = v[2]; i4[3] = v[3];
+      } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (e0 + j < len) i4[j] = cand_i[(int64_t)r * cap + e0 + j];
+        for (int j = 0; j < 4; ++j)
+          if (e0 + j < len) i4[j] = cand_i[(int64_t)r * cap + e0 + j];
+      }
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int64_t e = e0 + j;
       bool ok = e < len;
-      if (MODE == TOPK_MERGE && ok) ok = e / kc < nslices && (int)(e % kc) < cand_n[(int64_t)r * nslices + e / kc];
+      if (MODE == TOPK_MERGE) ok = ok && i4[j] >= 0;           // unused candidate slots hold -1
       valid[4 * i + j] = ok;
       key[4 * i + j] = ok ? score_key(s4[j]) : 0u;
       idx[4 * i + j] = MODE == TOPK_MERGE ? i4[j] : (int32_t)(base + e);
@@ -225,7 +230,6 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
   if (MODE == TOPK_SLICE) {
     oi = cand_i + (int64_t)r * cap + (int64_t)blockIdx.x * kc;
     os = cand_s + (int64_t)r * cap + (int64_t)blockIdx.x * kc;
-    if (threadIdx.x == 0) cand_n[(int64_t)r * nslices + blockIdx.x] = (int32_t)kk;
   } else {
     oi = out_idx + (int64_t)r * k;
     os = out_score ? out_score + (int64_t)r * k : nullptr;
@@ -243,11 +247,11 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
       }
     }
   }
-  if (MODE != TOPK_SLICE) {
-    for (int i = (int)kk + threadIdx.x; i < k; i += NT) {
-      oi[i] = -1;
-      if (os) os[i] = -INFINITY;
-    }
+  // pad to k (a slice pads its kc candidate slots: the merge skips index -1)
+  const int kpad = MODE == TOPK_SLICE ? kc : k;
+  for (int i = (int)kk + threadIdx.x; i < kpad; i += NT) {
+    oi[i] = -1;
+    if (os) os[i] = -INFINITY;
   }
 }
 
@@ -269,7 +273,7 @@ TopkPlan plan_topk(int64_t cover, int32_t k, int32_t R) {
   const int64_t kc = k < p.slice ? k : p.slice;
   p.cand = (p.nslices * kc + 3) / 4 * 4;
   if (p.cand > 1024 * 64) return p;  // not ok
-  p.ws_bytes = (size_t)R * (size_t)p.cand * 8 + (size_t)R * (size_t)p.nslices * 4 + 256;
+  p.ws_bytes = (size_t)R * (size_t)p.cand * 8 + 256;
   p.ok = true;
   return p;
 }
@@ -277,11 +281,11 @@ TopkPlan plan_topk(int64_t cover, int32_t k, int32_t R) {
 template <int MODE>
 static void launch_cfg(int nt, int v, dim3 grid, const float* scores, int64_t stride, const TopkRows& rr,
                        int k, int64_t slice, int nslices, int kc, int64_t cap, float* cs, int32_t* ci,
-                       int32_t* cn, int32_t* oi, float* os, hipStream_t st) {
+                       int32_t* oi, float* os, hipStream_t st) {
 #define SCKV_TK(NT, VV)                                                                                  \
   if (nt == NT && v == VV) {                                                                             \
     hipLaunchKernelGGL((topk_kernel<NT, VV, MODE>), grid, dim3(NT), 0, st, scores, stride, rr, k, slice, \
-                       nslices, kc, cap, cs, ci, cn, oi, os);                                            \
+                       nslices, kc, cap, cs, ci, oi, os);                                                \
     return;                                                                                              \
   }
   SCKV_TK(256, 4) SCKV_TK(256, 16) SCKV_TK(256, 32) SCKV_TK(1024, 16) SCKV_TK(1024, 32) SCKV_TK(1024, 64)
@@ -294,21 +298,20 @@ hipError_t launch_topk(const sckv_index_args& a, const float* scores, int64_t st
   const int R = a.rows.R;
   if (p.single_nt) {
     launch_cfg<TOPK_ROW>(p.single_nt, p.single_v, dim3(1, R), scores, stride, rr, a.k, 0, 1, 1, 0, nullptr,
-                         nullptr, nullptr, a.out_idx, a.out_score, stream);
+                         nullptr, a.out_idx, a.out_score, stream);
     return hipGetLastError();
   }
   const int kc = (int)(a.k < p.slice ? a.k : p.slice);
   char* w = static_cast<char*>(ws);
   float* cs = reinterpret_cast<float*>(w);
   int32_t* ci = reinterpret_cast<int32_t*>(w + (size_t)R * p.cand * 4);
-  int32_t* cn = reinterpret_cast<int32_t*>(w + (size_t)R * p.cand * 8);
   launch_cfg<TOPK_SLICE>(1024, 16, dim3((unsigned)p.nslices, R), scores, stride, rr, a.k, p.slice,
-                         (int)p.nslices, kc, p.cand, cs, ci, cn, nullptr, nullptr, stream);
+                         (int)p.nslices, kc, p.cand, cs, ci, nullptr, nullptr, stream);
   int nt = 1024, v = 64;
   for (auto& c : kCfg)
     if ((int64_t)c[0] * c[1] >= p.cand) { nt = c[0]; v = c[1]; break; }
   launch_cfg<TOPK_MERGE>(nt, v, dim3(1, R), scores, stride, rr, a.k, p.slice, (int)p.nslices, kc, p.cand, cs,
-                         ci, cn, a.out_idx, a.out_score, stream);
+                         ci, a.out_idx, a.out_score, stream);
   return hipGetLastError();
 }
 

@@ -239,6 +239,8 @@ ATTEND_CASES = [
     (True, "f32", 8, 64, 1024, [4095, 600, 10], 64, "f32"),
     (False, "f32", 8, 64, 1024, [4095], 0, "f32"),
     (True, "bf16", 16, 256, 1000, [4127, 2000], 200, "bf16"),
+    (True, "bf16", 48, 128, 2048, [8319, 5000, 129], 300, "f32"),      # three 16-head tiles
+    (False, "e4m3", 112, 64, 1024, [131071, 70000], 0, "f32"),         # seven 16-head tiles
 ]
 
 
@@ -359,3 +361,64 @@ def test_attend_rows_longer_than_a_segment():
         o, lse_o, _ = method.attend(q[r], items, 1 / math.sqrt(128))
         assert_close(go[r], o, atol=2e-2, what=f"row {r}")
         np.testing.assert_allclose(gl[r], lse_o, rtol=1e-5, atol=1e-5)
+
+
+def test_decode_step_replays_as_hip_graph():
+    """A decode step (index + top-k with sliced rows, fp8 CSA attention on the
+    register-staged kernel, bf16 HCA attention on the copy-staged kernel) captured
+    as a HIP graph: every replay, with eager work and synchronizations between
+    replays, reproduces the eager results bit for bit."""
+    print("graph replay of a decode step", flush=True)
+    torch.manual_seed(11)
+    f8, bf = torch.float8_e4m3fn, torch.bfloat16
+    B, E_c, E_h, k, H, D = 2, 40000, 1024, 512, 64, 512
+    pos = [160127, 100000]
+    rows = sk.RowSpec.decode(dev_i32(pos), max(pos))
+    keys = sk.to_key_tiles(torch.randn(B, E_c, 128, device=DEV).to(f8))
+    qI = torch.randn(B, 64, 128, device=DEV).to(bf)
+    w = torch.randn(B, 64, device=DEV)
+    ent_c = torch.randn(B, E_c, D, device=DEV).to(f8)
+    sc_c = torch.rand(B, E_c, device=DEV) + 0.5
+    ent_h = torch.randn(B, E_h, D, device=DEV).to(bf)
+    win = torch.randn(B, 128, D, device=DEV).to(bf)
+    qc = (torch.randn(B, H, D, device=DEV) * 0.3).to(bf)
+    qh = (torch.randn(B, H, D, device=DEV) * 0.3).to(bf)
+    tau = 1 / math.sqrt(128)
+
+    def outputs():
+        return (torch.empty(B, k, device=DEV, dtype=torch.int32), torch.empty(B, H, D, device=DEV, dtype=bf),
+                torch.empty(B, H, D, device=DEV, dtype=bf))
+
+    def step(o, ws=(None, None, None)):
+        idx, oc, oh = o
+        w_i = sk.csa_index_topk(rows, qI, w, keys, idx, m=4, W=128, k=k, workspace=ws[0])
+        w_c = sk.csa_attend(rows, qc, ent_c, idx, win, oc, m=4, W=128, softmax_scale=tau, entry_scale=sc_c,
+                            workspace=ws[1])
+        w_h = sk.hca_attend(rows, qh, ent_h, win, oh, m=128, W=128, softmax_scale=tau, workspace=ws[2])
+        return w_i, w_c, w_h
+
+    eager = outputs()
+    ws = step(eager)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in eager]
+    gout = outputs()
+    step(gout, ws)                                     # warm the captured path once
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            step(gout, ws)
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in gout:
+            t.zero_()
+        step(eager)                                    # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("indices", "csa out", "hca out"), gout, ref):
+            assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager step"
+        for a, b in zip(eager, ref):
+            assert torch.equal(a, b)
