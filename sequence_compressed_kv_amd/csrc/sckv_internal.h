@@ -24,11 +24,13 @@ int64_t index_rows_cover(const sckv_index_args& a);
 hipError_t launch_index_score(const sckv_index_args& a, float* scores, int64_t stride,
                               int64_t cover, hipStream_t stream);
 
-// Top-k plan: one block per row when the visible count fits a block's registers,
-// else a first stage over fixed slices of each row followed by a final stage over
-// the slices' candidates.
+// Top-k plan: one block per row when the visible count fits a block's registers;
+// for a few longer rows, many blocks per row (histogram, filter, final selection
+// over the survivors); else a first stage over fixed slices of each row followed
+// by a final stage over the slices' candidates.
 struct TopkPlan {
   int64_t cover = 0;        // widest row
+  int mb_blocks = 0;        // many-block path: blocks per row (0 = not taken)
   int single_nt = 0;        // threads of the one-stage kernel (0 = two stages)
   int single_v = 0;         // values per thread of the one-stage kernel
   int64_t slice = 0;        // two stages: slice length

@@ -42,45 +42,57 @@ __device__ __forceinline__ int64_t row_visible(const TopkRows& rr, int r) {
   return e < rr.E_cap ? e : rr.E_cap;
 }
 
+// Bin of the kk_rem-th largest element of an LDS histogram (kBins bins, counted
+// from the top): ctl[0] = bin, ctl[1] = kk_rem minus the elements in higher bins.
+// Every thread must call it (block scan, barriers).
+template <int NT>
+__device__ __forceinline__ void find_bin(const uint32_t* hist, uint32_t kk_rem, uint32_t* scan_sh, uint32_t* ctl) {
+  constexpr int BPT = kBins / NT;
+  uint32_t tsum = 0;
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) tsum += hist[threadIdx.x * BPT + i];
+  uint32_t total;
+  const uint32_t below = block_excl_scan<NT>(tsum, scan_sh, &total);
+  const uint32_t above = total - below - tsum;      // elements in higher bins than this chunk
+  if (above < kk_rem && kk_rem <= above + tsum) {
+    uint32_t run = above;
+    for (int i = BPT - 1; i >= 0; --i) {
+      const uint32_t h = hist[threadIdx.x * BPT + i];
+      if (run + h >= kk_rem) {
+        ctl[0] = (uint32_t)(threadIdx.x * BPT + i);
+        ctl[1] = kk_rem - run;
+        break;
+      }
+      run += h;
+    }
+  }
+  __syncthreads();
+}
+
+constexpr int kShift[3] = {20, 8, 0};
+constexpr uint32_t kHMask[3] = {0u, 0xFFF00000u, 0xFFFFFF00u};
+constexpr uint32_t kDMask[3] = {0xFFFu, 0xFFFu, 0xFFu};
+
 // Finds the kk-th largest key among valid elements: returns T and, in *need, how
 // many elements equal to T belong to the selection.  Every thread must call it.
+// A caller that already knows the first digit passes it as prefix (with kk
+// counted from that bin's top) and p0 = 1.
 template <int NT, int V>
 __device__ __forceinline__ uint32_t radix_threshold(const uint32_t (&key)[V], const bool (&valid)[V],
                                                     uint32_t kk, uint32_t* hist, uint32_t* scan_sh,
-                                                    uint32_t* ctl, uint32_t* need) {
-  constexpr int BPT = kBins / NT;
-  uint32_t prefix = 0, kk_rem = kk;
-  const int shifts[3] = {20, 8, 0};
-  const uint32_t hmasks[3] = {0u, 0xFFF00000u, 0xFFFFFF00u};
-  const uint32_t dmasks[3] = {0xFFFu, 0xFFFu, 0xFFu};
+                                                    uint32_t* ctl, uint32_t* need, uint32_t prefix = 0,
+                                                    int p0 = 0) {
+  uint32_t kk_rem = kk;
 #pragma unroll
-  for (int p = 0; p < 3; ++p) {
+  for (int p = p0; p < 3; ++p) {
     for (int i = threadIdx.x; i < kBins; i += NT) hist[i] = 0;
     __syncthreads();
 #pragma unroll
     for (int v = 0; v < V; ++v)
-      if (valid[v] && (key[v] & hmasks[p]) == prefix) atomicAdd(&hist[(key[v] >> shifts[p]) & dmasks[p]], 1u);
+      if (valid[v] && (key[v] & kHMask[p]) == prefix) atomicAdd(&hist[(key[v] >> kShift[p]) & kDMask[p]], 1u);
     __syncthreads();
-    uint32_t tsum = 0;
-#pragma unroll
-    for (int i = 0; i < BPT; ++i) tsum += hist[threadIdx.x * BPT + i];
-    uint32_t total;
-    const uint32_t below = block_excl_scan<NT>(tsum, scan_sh, &total);
-    const uint32_t above = total - below - tsum;      // elements in higher bins than this chunk
-    if (above < kk_rem && kk_rem <= above + tsum) {
-      uint32_t run = above;
-      for (int i = BPT - 1; i >= 0; --i) {
-        const uint32_t h = hist[threadIdx.x * BPT + i];
-        if (run + h >= kk_rem) {
-          ctl[0] = (uint32_t)(threadIdx.x * BPT + i);
-          ctl[1] = kk_rem - run;
-          break;
-        }
-        run += h;
-      }
-    }
-    __syncthreads();
-    prefix |= ctl[0] << shifts[p];
+    find_bin<NT>(hist, kk_rem, scan_sh, ctl);
+    prefix |= ctl[0] << kShift[p];
     kk_rem = ctl[1];
     __syncthreads();
   }
@@ -117,6 +129,68 @@ __device__ __forceinline__ void ordered_scan(const uint32_t (&c)[NI], uint32_t (
   for (int i = 0; i < NI; ++i) off[i] += base;
   *total = sh[NW];
   __syncthreads();
+}
+
+// The kk best of a block's valid elements by (key descending, index ascending),
+// written to oi (and os) in element order, which callers make ascending index
+// order; slots kk .. kpad-1 get index -1.  Elements sit in element order
+// (wave, group, lane, element).  Every thread must call it.
+// A caller that knows the bin b of the first digit holding the kk-th key, and the
+// count `above` of elements in higher bins, passes b1 = b + 1 and above.
+template <int NT, int V>
+__device__ __forceinline__ void select_ordered(const uint32_t (&key)[V], const int32_t (&idx)[V],
+                                               const bool (&valid)[V], uint32_t n_valid, uint32_t kk, int32_t* oi,
+                                               float* os, int kpad, uint32_t* hist, uint32_t* scan_sh, uint32_t* ctl,
+                                               uint32_t b1 = 0, uint32_t above = 0) {
+  constexpr int NI = V / 4;
+  uint32_t T = 0, need = UINT_MAX;
+  if (kk < n_valid) {
+    if (b1) T = radix_threshold<NT, V>(key, valid, kk - above, hist, scan_sh, ctl, &need, (b1 - 1) << 20, 1);
+    else T = radix_threshold<NT, V>(key, valid, kk, hist, scan_sh, ctl, &need);
+  }
+
+  // ordered compaction: keys above T, then the first `need` keys equal to T
+  uint32_t ceq[NI], eq_off[NI], tot;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    ceq[i] = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ceq[i] += (valid[4 * i + j] && key[4 * i + j] == T) ? 1u : 0u;
+  }
+  ordered_scan<NT, NI>(ceq, eq_off, scan_sh, &tot);
+  bool sel[V];
+  uint32_t csel[NI], sel_off[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    uint32_t eq_rank = eq_off[i];
+    csel[i] = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int v = 4 * i + j;
+      bool sv = valid[v] && key[v] > T;
+      if (valid[v] && key[v] == T) sv = eq_rank++ < need;
+      sel[v] = sv;
+      csel[i] += sv ? 1u : 0u;
+    }
+  }
+  ordered_scan<NT, NI>(csel, sel_off, scan_sh, &tot);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    uint32_t off = sel_off[i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int v = 4 * i + j;
+      if (sel[v]) {
+        oi[off] = idx[v];
+        if (os) os[off] = key_score(key[v]);
+        ++off;
+      }
+    }
+  }
+  for (int i = (int)kk + threadIdx.x; i < kpad; i += NT) {
+    oi[i] = -1;
+    if (os) os[i] = -INFINITY;
+  }
 }
 
 // MODE TOPK_ROW   : scores of row r, elements 0 .. n-1 (n = visible count), out to out_idx.
@@ -196,70 +270,371 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
   (void)block_excl_scan<NT>(nv, scan_sh, &n_valid);
   const uint32_t kk = n_valid < (uint32_t)k ? n_valid : (uint32_t)k;
 
-  uint32_t T = 0, need = UINT_MAX;
-  if (kk < n_valid) T = radix_threshold<NT, V>(key, valid, kk, hist, scan_sh, ctl, &need);
-
-  // ordered compaction: keys above T, then the first `need` keys equal to T
-  uint32_t ceq[NI], eq_off[NI], tot;
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    ceq[i] = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) ceq[i] += (valid[4 * i + j] && key[4 * i + j] == T) ? 1u : 0u;
-  }
-  ordered_scan<NT, NI>(ceq, eq_off, scan_sh, &tot);
-  bool sel[V];
-  uint32_t csel[NI], sel_off[NI];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    uint32_t eq_rank = eq_off[i];
-    csel[i] = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int v = 4 * i + j;
-      bool sv = valid[v] && key[v] > T;
-      if (valid[v] && key[v] == T) sv = eq_rank++ < need;
-      sel[v] = sv;
-      csel[i] += sv ? 1u : 0u;
-    }
-  }
-  ordered_scan<NT, NI>(csel, sel_off, scan_sh, &tot);
-
   int32_t* oi;
   float* os;
+  int kpad;                              // a slice pads its kc candidate slots: the merge skips index -1
   if (MODE == TOPK_SLICE) {
     oi = cand_i + (int64_t)r * cap + (int64_t)blockIdx.x * kc;
     os = cand_s + (int64_t)r * cap + (int64_t)blockIdx.x * kc;
+    kpad = kc;
   } else {
     oi = out_idx + (int64_t)r * k;
     os = out_score ? out_score + (int64_t)r * k : nullptr;
+    kpad = k;
   }
+  select_ordered<NT, V>(key, idx, valid, n_valid, kk, oi, os, kpad, hist, scan_sh, ctl);
+}
+
+
+// ------------------------------------------------------------------ many blocks per row
+// For few rows longer than one block's registers hold (long-context decode):
+// every row is cut into blocks of kMbS elements.
+//   zero   : the rows' first-digit histograms are cleared
+//   hist   : each block adds its elements' first-digit (key bits 31:20) counts
+//            into the row's histogram
+//   filter : each block finds, from the full histogram, the bin b holding the
+//            row's kk-th largest key and writes its elements with digit >= b
+//            (every member of the top-kk, plus the rest of bin b) in index order
+//            to its own region of the workspace
+//   final  : one block per row concatenates the regions in block order
+//            (ascending index) and runs the exact selection on those survivors,
+//            from the second digit on.
+// When bin b is too full for one block (heavily tied or clustered scores), the
+// filter writes nothing and the final block streams the whole row instead.
+// (Handing the final step to the last filter block of each row instead would
+// need a device-scope fence in every block, which writes back the L2.)
+constexpr int kMbNT = 256, kMbV = 16, kMbS = kMbNT * kMbV;        // elements per filter block
+constexpr int kFinNT = 1024, kFinV = 16, kFinCap = kFinNT * kFinV;  // survivors the final block holds
+constexpr int kMbMaxBlocks = 1024;                                  // blocks per row
+
+// Elements [base, base + NT*V) of a row (len of them exist) in element order
+// (wave, group, lane, element): wave w owns elements w*64*V .. ; its group i is one
+// coalesced 1 KB load, lane l taking elements (i*64 + l)*4 .. +3.
+template <int NT, int V>
+__device__ __forceinline__ void load_row_part(const float* src, int64_t len, int64_t base, uint32_t (&key)[V],
+                                              int32_t (&idx)[V], bool (&valid)[V]) {
+  constexpr int NI = V / 4;
+  const int w = wave_id(), l = lane_id();
+  const bool vec = ((reinterpret_cast<uintptr_t>(src) & 15u) == 0);
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    uint32_t off = sel_off[i];
+    const int64_t e0 = (int64_t)w * 64 * V + ((int64_t)i * 64 + l) * 4;
+    float s4[4] = {0.f, 0.f, 0.f, 0.f};
+    if (vec && e0 + 3 < len) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(src + e0);
+      s4[0] = v[0]; s4[1] = v[1]; s4[2] = v[2]; s4[3] = v[3];
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (e0 + j < len) s4[j] = src[e0 + j];
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int v = 4 * i + j;
-      if (sel[v]) {
-        oi[off] = idx[v];
-        if (os) os[off] = key_score(key[v]);
-        ++off;
-      }
+      const bool ok = e0 + j < len;
+      valid[4 * i + j] = ok;
+      key[4 * i + j] = ok ? score_key(s4[j]) : 0u;
+      idx[4 * i + j] = (int32_t)(base + e0 + j);
     }
   }
-  // pad to k (a slice pads its kc candidate slots: the merge skips index -1)
-  const int kpad = MODE == TOPK_SLICE ? kc : k;
-  for (int i = (int)kk + threadIdx.x; i < kpad; i += NT) {
-    oi[i] = -1;
-    if (os) os[i] = -INFINITY;
+}
+
+__global__ __launch_bounds__(256) void topk_zero_hist(uint32_t* __restrict__ hist, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) hist[i] = 0u;
+}
+
+__global__ __launch_bounds__(kMbNT) void topk_hist(const float* __restrict__ scores, int64_t stride, TopkRows rows,
+                                                   uint32_t* __restrict__ ghist) {
+  __shared__ uint32_t h[kBins];
+  const int r = blockIdx.y;
+  const int64_t base = (int64_t)blockIdx.x * kMbS;
+  int64_t len = row_visible(rows, r) - base;
+  if (len <= 0) return;
+  len = len > kMbS ? kMbS : len;
+  for (int i = threadIdx.x; i < kBins; i += kMbNT) h[i] = 0u;
+  __syncthreads();
+  uint32_t key[kMbV];
+  int32_t idx[kMbV];
+  bool valid[kMbV];
+  load_row_part<kMbNT, kMbV>(scores + (int64_t)r * stride + base, len, base, key, idx, valid);
+#pragma unroll
+  for (int v = 0; v < kMbV; ++v)
+    if (valid[v]) atomicAdd(&h[key[v] >> 20], 1u);
+  __syncthreads();
+  for (int i = threadIdx.x; i < kBins; i += kMbNT)
+    if (h[i]) atomicAdd(&ghist[(int64_t)r * kBins + i], h[i]);
+}
+
+// From a row's first-digit histogram (global memory): ctl[3] = valid elements,
+// kk = min(k, ctl[3]); ctl[0] = the bin of the kk-th largest key (kBins when kk
+// is 0), ctl[1] = elements in higher bins, ctl[2] = elements in that bin.
+template <int NT>
+__device__ __forceinline__ void row_threshold_bin(const uint32_t* gh, int k, uint32_t* scan_sh, uint32_t* ctl) {
+  constexpr int BPT = kBins / NT;
+  static_assert(BPT % 4 == 0, "bins are read four at a time");
+  uint32_t c[BPT];
+#pragma unroll
+  for (int i = 0; i < BPT; i += 4) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(gh + threadIdx.x * BPT + i);
+    c[i] = v[0]; c[i + 1] = v[1]; c[i + 2] = v[2]; c[i + 3] = v[3];
   }
+  uint32_t tsum = 0;
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) tsum += c[i];
+  uint32_t total;
+  const uint32_t below = block_excl_scan<NT>(tsum, scan_sh, &total);
+  const uint32_t kk = total < (uint32_t)k ? total : (uint32_t)k;
+  const uint32_t above = total - below - tsum;
+  if (threadIdx.x == 0) {
+    ctl[3] = total;
+    if (kk == 0) { ctl[0] = kBins; ctl[1] = 0; ctl[2] = 0; }
+  }
+  if (kk > 0 && above < kk && kk <= above + tsum) {
+    uint32_t run = above;
+#pragma unroll
+    for (int i = BPT - 1; i >= 0; --i) {
+      if (run + c[i] >= kk) {
+        ctl[0] = (uint32_t)(threadIdx.x * BPT + i);
+        ctl[1] = run;
+        ctl[2] = c[i];
+        break;
+      }
+      run += c[i];
+    }
+  }
+  __syncthreads();
+}
+
+// Exact top-kk of a whole row by one block, streamed in chunks of NT*V elements:
+// three radix passes, then an ordered pass that writes the kept indices in order.
+// (The rare path: kept out of line so it does not weigh on the common one.)
+template <int NT, int V>
+__device__ __noinline__ void topk_stream_row(const float* src, int64_t n, uint32_t kk, int32_t* oi, float* os, uint32_t* hist,
+                                uint32_t* scan_sh, uint32_t* ctl) {
+  constexpr int NI = V / 4, CH = NT * V;
+  uint32_t prefix = 0, kk_rem = kk;
+#pragma unroll
+  for (int p = 0; p < 3; ++p) {
+    for (int i = threadIdx.x; i < kBins; i += NT) hist[i] = 0;
+    __syncthreads();
+    for (int64_t c0 = 0; c0 < n; c0 += CH) {
+      uint32_t key[V];
+      int32_t idx[V];
+      bool valid[V];
+      load_row_part<NT, V>(src + c0, n - c0, c0, key, idx, valid);
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+        if (valid[v] && (key[v] & kHMask[p]) == prefix) atomicAdd(&hist[(key[v] >> kShift[p]) & kDMask[p]], 1u);
+    }
+    __syncthreads();
+    find_bin<NT>(hist, kk_rem, scan_sh, ctl);
+    prefix |= ctl[0] << kShift[p];
+    kk_rem = ctl[1];
+    __syncthreads();
+  }
+  const uint32_t T = prefix, need = kk_rem;
+  uint32_t written = 0, eq_seen = 0;                   // block-uniform running totals
+  for (int64_t c0 = 0; c0 < n && written < kk; c0 += CH) {
+    uint32_t key[V];
+    int32_t idx[V];
+    bool valid[V];
+    load_row_part<NT, V>(src + c0, n - c0, c0, key, idx, valid);
+    uint32_t ceq[NI], eq_off[NI], tot_eq;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      ceq[i] = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ceq[i] += (valid[4 * i + j] && key[4 * i + j] == T) ? 1u : 0u;
+    }
+    ordered_scan<NT, NI>(ceq, eq_off, scan_sh, &tot_eq);
+    bool sel[V];
+    uint32_t csel[NI], sel_off[NI], tot_sel;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      uint32_t eq_rank = eq_seen + eq_off[i];
+      csel[i] = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int v = 4 * i + j;
+        bool sv = valid[v] && key[v] > T;
+        if (valid[v] && key[v] == T) sv = eq_rank++ < need;
+        sel[v] = sv;
+        csel[i] += sv ? 1u : 0u;
+      }
+    }
+    ordered_scan<NT, NI>(csel, sel_off, scan_sh, &tot_sel);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      uint32_t off = written + sel_off[i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int v = 4 * i + j;
+        if (sel[v]) {
+          oi[off] = idx[v];
+          if (os) os[off] = key_score(key[v]);
+          ++off;
+        }
+      }
+    }
+    written += tot_sel;
+    eq_seen += tot_eq;
+  }
+}
+
+// The final selection of row r (one block of kFinNT threads).
+__device__ __forceinline__ void topk_row_final(const float* scores, int64_t stride, const TopkRows& rows, int r, int k,
+                                            int nb, const int32_t* cnt, const uint32_t* rkey, const int32_t* ridx,
+                                            uint32_t b, uint32_t above, uint32_t n_valid, int32_t* out_idx,
+                                            float* out_score, uint32_t* hist, uint32_t* scan_sh, uint32_t* ctl,
+                                            int32_t* pre, int32_t* flag) {
+  constexpr int NI = kFinV / 4;
+  const int w = wave_id(), l = lane_id();
+  int32_t* oi = out_idx + (int64_t)r * k;
+  float* os = out_score ? out_score + (int64_t)r * k : nullptr;
+  const uint32_t kk = n_valid < (uint32_t)k ? n_valid : (uint32_t)k;
+  // survivors per block -> exclusive prefix in block order (nb <= kMbMaxBlocks)
+  if (threadIdx.x == 0) *flag = 0;
+  __syncthreads();
+  uint32_t run = 0;
+  for (int j0 = 0; j0 < nb; j0 += kFinNT) {
+    const int j = j0 + threadIdx.x;
+    const int32_t my = j < nb ? cnt[(int64_t)r * nb + j] : 0;
+    if (my < 0) *flag = 1;
+    uint32_t t;
+    const uint32_t ex = block_excl_scan<kFinNT>(my < 0 ? 0u : (uint32_t)my, scan_sh, &t);
+    if (j < nb) pre[j] = (int32_t)(run + ex);
+    run += t;
+  }
+  if (threadIdx.x == 0) pre[nb] = (int32_t)run;
+  __syncthreads();
+  if (*flag) {
+    topk_stream_row<kFinNT, kFinV>(scores + (int64_t)r * stride, row_visible(rows, r), kk, oi, os, hist, scan_sh,
+                                 ctl);
+    for (int i = (int)kk + threadIdx.x; i < k; i += kFinNT) {
+      oi[i] = -1;
+      if (os) os[i] = -INFINITY;
+    }
+    return;
+  }
+  const int tot = pre[nb];
+  // survivor e (concatenation order) lives in region j, pre[j] <= e < pre[j+1]
+  uint32_t key[kFinV];
+  int32_t idx[kFinV];
+  bool valid[kFinV];
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int v = 4 * i + jj;
+      const int e = w * 64 * kFinV + (i * 64 + l) * 4 + jj;
+      valid[v] = e < tot;
+      key[v] = 0u;
+      idx[v] = -1;
+      if (valid[v]) {
+        int lo = 0, hi = nb;                           // largest j with pre[j] <= e
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (pre[mid] <= e) lo = mid;
+          else hi = mid;
+        }
+        const int64_t at = ((int64_t)r * nb + lo) * kMbS + (e - pre[lo]);
+        key[v] = rkey[at];
+        idx[v] = ridx[at];
+      }
+    }
+  select_ordered<kFinNT, kFinV>(key, idx, valid, (uint32_t)tot, kk, oi, os, k, hist, scan_sh, ctl, b + 1, above);
+}
+
+__global__ __launch_bounds__(kMbNT) void topk_filter(const float* __restrict__ scores, int64_t stride,
+                                                     TopkRows rows, int k, int nb,
+                                                     const uint32_t* __restrict__ ghist, int32_t* __restrict__ cnt,
+                                                     uint32_t* __restrict__ rkey, int32_t* __restrict__ ridx) {
+  constexpr int NI = kMbV / 4;
+  __shared__ uint32_t scan_sh[kMbNT / kWave + 1];
+  __shared__ uint32_t ctl[4];
+  const int r = blockIdx.y;
+  const int64_t base = (int64_t)blockIdx.x * kMbS;
+  const int64_t slot = (int64_t)r * nb + blockIdx.x;
+  int64_t len = row_visible(rows, r) - base;
+  len = len < 0 ? 0 : (len > kMbS ? kMbS : len);
+  row_threshold_bin<kMbNT>(ghist + (int64_t)r * kBins, k, scan_sh, ctl);
+  const uint32_t b = ctl[0], above = ctl[1];
+  if (len == 0) {
+    if (threadIdx.x == 0) cnt[slot] = 0;
+  } else if (above + ctl[2] > (uint32_t)kFinCap) {      // too many survivors: the final block streams the row
+    if (threadIdx.x == 0) cnt[slot] = -1;
+  } else {
+    uint32_t key[kMbV];
+    int32_t idx[kMbV];
+    bool valid[kMbV];
+    load_row_part<kMbNT, kMbV>(scores + (int64_t)r * stride + base, len, base, key, idx, valid);
+    bool keep[kMbV];
+    uint32_t c[NI], off[NI], tot;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      c[i] = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int v = 4 * i + j;
+        keep[v] = valid[v] && (key[v] >> 20) >= b;
+        c[i] += keep[v] ? 1u : 0u;
+      }
+    }
+    ordered_scan<kMbNT, NI>(c, off, scan_sh, &tot);
+    uint32_t* ok = rkey + slot * kMbS;
+    int32_t* oi = ridx + slot * kMbS;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      uint32_t o = off[i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int v = 4 * i + j;
+        if (keep[v]) {
+          ok[o] = key[v];
+          oi[o] = idx[v];
+          ++o;
+        }
+      }
+    }
+    if (threadIdx.x == 0) cnt[slot] = (int32_t)tot;
+  }
+}
+
+__global__ __launch_bounds__(kFinNT) void topk_final(const float* __restrict__ scores, int64_t stride, TopkRows rows,
+                                                    int k, int nb, const uint32_t* __restrict__ ghist,
+                                                    const int32_t* __restrict__ cnt, const uint32_t* __restrict__ rkey,
+                                                    const int32_t* __restrict__ ridx, int32_t* __restrict__ out_idx,
+                                                    float* __restrict__ out_score) {
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t scan_sh[kFinNT / kWave + 1];
+  __shared__ uint32_t ctl[4];
+  __shared__ int32_t pre[kMbMaxBlocks + 1];
+  __shared__ int32_t flag;
+  const int r = blockIdx.y;
+  row_threshold_bin<kFinNT>(ghist + (int64_t)r * kBins, k, scan_sh, ctl);
+  const uint32_t b = ctl[0], above = ctl[1], n_valid = ctl[3];
+  topk_row_final(scores, stride, rows, r, k, nb, cnt, rkey, ridx, b, above, n_valid, out_idx, out_score, hist,
+                 scan_sh, ctl, pre, &flag);
 }
 
 static const int kCfg[][2] = {{256, 4}, {256, 16}, {256, 32}, {1024, 16}, {1024, 32}, {1024, 64}};
 
+static size_t align16(size_t n) { return (n + 15) / 16 * 16; }
+// many-block workspace: histograms [R][kBins], then block counts [R][nb], then
+// survivor keys and indices [R][nb][kMbS] each
+static size_t mb_cnt_offset(int R) { return align16((size_t)R * kBins * 4); }
+
 TopkPlan plan_topk(int64_t cover, int32_t k, int32_t R) {
   TopkPlan p;
   p.cover = cover;
+  // few rows too long for one block: spread each row over many blocks
+  const int64_t nb = (cover + kMbS - 1) / kMbS;
+  if (R <= 64 && cover > 1024 * 32 && nb <= kMbMaxBlocks && k <= kFinCap) {
+    p.mb_blocks = (int)nb;
+    p.ws_bytes = mb_cnt_offset(R) + align16((size_t)R * nb * 4) + (size_t)R * nb * kMbS * 8 + 256;
+    p.ok = true;
+    return p;
+  }
   for (auto& c : kCfg) {
     if ((int64_t)c[0] * c[1] >= cover && c[1] <= 32) {
       p.single_nt = c[0];
@@ -296,6 +671,22 @@ hipError_t launch_topk(const sckv_index_args& a, const float* scores, int64_t st
                        void* ws, hipStream_t stream) {
   TopkRows rr{a.rows.kind, a.rows.pos, a.rows.pos_max, a.rows.seq0, a.rows.pos0, a.m, a.W, a.E_cap};
   const int R = a.rows.R;
+  if (p.mb_blocks) {
+    const int nb = p.mb_blocks;
+    char* w = static_cast<char*>(ws);
+    uint32_t* hist = reinterpret_cast<uint32_t*>(w);                    // [R][kBins]
+    int32_t* cnt = reinterpret_cast<int32_t*>(w + mb_cnt_offset(R));
+    uint32_t* rkey = reinterpret_cast<uint32_t*>(w + mb_cnt_offset(R) + align16((size_t)R * nb * 4));
+    int32_t* ridx = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(rkey) + (size_t)R * nb * kMbS * 4);
+    const int64_t nz = (int64_t)R * kBins;
+    hipLaunchKernelGGL(topk_zero_hist, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, stream, hist, nz);
+    hipLaunchKernelGGL(topk_hist, dim3((unsigned)nb, R), dim3(kMbNT), 0, stream, scores, stride, rr, hist);
+    hipLaunchKernelGGL(topk_filter, dim3((unsigned)nb, R), dim3(kMbNT), 0, stream, scores, stride, rr, a.k, nb, hist,
+                       cnt, rkey, ridx);
+    hipLaunchKernelGGL(topk_final, dim3(1, R), dim3(kFinNT), 0, stream, scores, stride, rr, a.k, nb, hist, cnt, rkey,
+                       ridx, a.out_idx, a.out_score);
+    return hipGetLastError();
+  }
   if (p.single_nt) {
     launch_cfg<TOPK_ROW>(p.single_nt, p.single_v, dim3(1, R), scores, stride, rr, a.k, 0, 1, 1, 0, nullptr,
                          nullptr, a.out_idx, a.out_score, stream);

@@ -110,8 +110,12 @@ def test_index_workspace(L):
 
 
 def test_topk_plan_limits(L):
-    # decode at t = 2^22: 1,048,544 visible entries and k = 4096 exceed the two-stage plan
+    # decode at t = 2^22 (1,048,544 visible entries, k = 4096): many blocks per row
     a = idx_args(rows=_lib.Rows(FAKE, 0, 1, 1 << 22, 0, 0, 0), E_cap=1 << 20, k=4096)
+    assert L.csa_index_topk_workspace_size(C.byref(a)) > 1048544 * 4
+    # t = 2^25 with 2^23 entries: more than 1024 blocks of 4096 per row, and slices
+    # whose candidates exceed one block
+    a = idx_args(rows=_lib.Rows(FAKE, 0, 1, 1 << 25, 0, 0, 0), E_cap=1 << 23, k=4096)
     assert L.csa_index_topk_workspace_size(C.byref(a)) == 0
     assert L.csa_index_topk(C.byref(a), FAKE, 1 << 40, None) == 4
 

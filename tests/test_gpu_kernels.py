@@ -422,3 +422,37 @@ def test_decode_step_replays_as_hip_graph():
             assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager step"
         for a, b in zip(eager, ref):
             assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("E,k,tie", [(40000, 512, 7.0), (70016, 2048, 6.0)])
+def test_topk_select_many_blocks_and_ties(E, k, tie):
+    """Selection from given scores on the many-blocks-per-row path (rows longer
+    than one block holds): a row of equal scores (its threshold bin holds every
+    entry, so the final block streams the row), a row with a third of its entries
+    tied at the threshold (k of 40000 keeps the survivors within the final block,
+    k of 70016 does not), rows of distinct and of clustered scores, and a short
+    row."""
+    print(f"topk select many blocks E={E} k={k}", flush=True)
+    rng = np.random.default_rng(E + k)
+    pos = [4 * E + 127, 4 * E + 127, 4 * E + 127, 4 * E + 127, 4 * 900 + 128]
+    R = len(pos)
+    s = rng.normal(0, 3, (R, E)).astype(np.float32)
+    s[0] = 1.5                                             # all tied
+    band = rng.choice(E, size=E // 3, replace=False)       # a third of the row tied near the threshold
+    s[1, band] = np.float32(tie)
+    s[3] = (1000.0 + rng.normal(0, 1e-3, E)).astype(np.float32)   # clustered: few first-digit bins
+    rows = sk.RowSpec.decode(dev_i32(pos), max(pos))
+    out_idx = torch.full((R, k), -7, device=DEV, dtype=torch.int32)
+    out_score = torch.zeros(R, k, device=DEV, dtype=torch.float32)
+    qI = torch.zeros(R, 64, 128, device=DEV, dtype=torch.bfloat16)
+    w = torch.zeros(R, 64, device=DEV)
+    keys = sk.key_tiles_empty(R, E, 128, torch.bfloat16, DEV)
+    sk.csa_topk_select(rows, dev(s), out_idx, keys_meta=(qI, w, keys), m=4, W=128, k=k, out_score=out_score)
+    torch.cuda.synchronize()
+    gi, gs = host(out_idx), host(out_score)
+    for r, t in enumerate(pos):
+        ev = min(method.entries_visible(t, 4, 128), E)
+        ora = method.topk(s[r, :ev], k)
+        np.testing.assert_array_equal(gi[r], ora, err_msg=f"row {r}")
+        sel = gi[r][gi[r] >= 0]
+        np.testing.assert_array_equal(gs[r, :len(sel)], s[r, sel])
