@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill indexer measurement")
     ap.add_argument("--no-1m", action="store_true", help="skip the 1M-context fp8 decode measurement")
+    ap.add_argument("--only", choices=["prefill", "1m"], default=None,
+                    help="run only that side measurement and print its record (for profiling its kernels)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy (reference for the HBM byte counters)")
     return ap.parse_args()
@@ -287,6 +289,13 @@ def main():
 
     import sequence_compressed_kv_amd as sk
     from workloads import CSA_PREFILL_32K_BF16, PAIR_DEC_128K_BF16, gen
+
+    if args.only == "prefill":
+        print(json.dumps({"prefill_indexer": prefill_indexer_rate("cuda:0", sk, torch, CSA_PREFILL_32K_BF16)}))
+        return
+    if args.only == "1m":
+        print(json.dumps({"decode_1m_fp8": decode_1m_rate("cuda:0", sk, torch, gen)}))
+        return
 
     wl = PAIR_DEC_128K_BF16 if args.batch is None else PAIR_DEC_128K_BF16.with_sizes(B=args.batch)
     dev = "cuda:0"
