@@ -134,6 +134,52 @@ sckv_status csa_compress(int32_t B, int64_t N, int32_t m, int32_t o, int64_t e_b
 sckv_status hca_compress(int32_t B, int64_t N, int32_t m, int32_t o, int64_t e_begin,
                          int64_t e_count, const sckv_pool_stream* kv, void* stream);
 
+/* ------------------------------------------------------------------ decode append
+ * The compressor run incrementally in decode: one new token per sequence is
+ * appended to rings of a stream's recent tokens, and where that token completes
+ * an entry (one entry per m tokens; knightli.com article, CSA section: a
+ * compressed entry stands for m tokens; HCA section for m = 128) the entry is
+ * pooled into the cache.
+ *   pos       : device [B] int32 position t of each sequence's new token; a
+ *               sequence with t < 0 appends nothing
+ *   val, gate : [B][D] the new tokens' values and gate logits (in_dtype F32 or BF16)
+ *   val_ring, gate_ring : [B][P][D] (in_dtype) the stream's last P tokens, token i
+ *               at slot i mod P; the call writes token t's slot.  For the shared
+ *               latent stream val_ring may be the attention window ring (P = R_w).
+ *   P         : ring slots, >= m + o (the tokens one entry pools)
+ *   bpos, out, out_scale, E_cap, out_dtype, out_layout : as in sckv_pool_stream.
+ * When (t + 1) % m == 0 and e = (t + 1) / m - 1 < E_cap, entry e is pooled over
+ * tokens [m e - o, m e + m) from the rings and the new token (the rings must hold
+ * the tokens before t), bit for bit as csa_compress / hca_compress would pool it.
+ * Calls on one stream run in order; two calls that share rings must not overlap. */
+typedef struct {
+  const int32_t* pos;
+  const void* val;
+  const void* gate;
+  void* val_ring;
+  void* gate_ring;
+  const float* bpos;
+  void* out;
+  float* out_scale;
+  int64_t E_cap;
+  int32_t D;
+  int32_t P;
+  int32_t in_dtype;
+  int32_t out_dtype;
+  int32_t out_layout; /* sckv_layout */
+  int32_t reserved;
+} sckv_append_stream;
+
+/* csa_append: appends one token per sequence to the latent stream `kv` and to
+ * the indexer stream `index_keys` (may be NULL), with the CSA pool (m = 4, o = 4;
+ * any m >= 1, o >= 0 accepted).  Both streams take the same positions; pass the
+ * same pos pointer in both descriptors. */
+sckv_status csa_append(int32_t B, int32_t m, int32_t o, const sckv_append_stream* kv,
+                       const sckv_append_stream* index_keys, void* stream);
+
+/* hca_append: as csa_append for the single HCA stream (m = 128, o = 0). */
+sckv_status hca_append(int32_t B, int32_t m, int32_t o, const sckv_append_stream* kv, void* stream);
+
 /* ------------------------------------------------------------------ lightning indexer + top-k
  *   q         : [R][H_I][D_I] indexer queries (q_dtype F32 or BF16)
  *   w         : [R][H_I] fp32 head weights w_h

@@ -39,6 +39,13 @@ class PoolStream(C.Structure):
                 ("out_dtype", C.c_int32), ("out_layout", C.c_int32)]
 
 
+class AppendStream(C.Structure):
+    _fields_ = [("pos", C.c_void_p), ("val", C.c_void_p), ("gate", C.c_void_p), ("val_ring", C.c_void_p),
+                ("gate_ring", C.c_void_p), ("bpos", C.c_void_p), ("out", C.c_void_p), ("out_scale", C.c_void_p),
+                ("E_cap", C.c_int64), ("D", C.c_int32), ("P", C.c_int32), ("in_dtype", C.c_int32),
+                ("out_dtype", C.c_int32), ("out_layout", C.c_int32), ("reserved", C.c_int32)]
+
+
 class IndexArgs(C.Structure):
     _fields_ = [("rows", Rows), ("q", C.c_void_p), ("w", C.c_void_p), ("keys", C.c_void_p),
                 ("out_idx", C.c_void_p), ("out_score", C.c_void_p), ("E_cap", C.c_int64), ("B", C.c_int32),
@@ -55,7 +62,7 @@ class AttendArgs(C.Structure):
                 ("softmax_scale", C.c_float), ("reserved", C.c_int32)]
 
 
-EXPORTS = ["csa_compress", "hca_compress", "csa_index_topk_workspace_size", "csa_index_topk", "csa_index_score",
+EXPORTS = ["csa_compress", "hca_compress", "csa_append", "hca_append", "csa_index_topk_workspace_size", "csa_index_topk", "csa_index_score",
            "csa_topk_select_workspace_size", "csa_topk_select", "csa_attend_workspace_size",
            "hca_attend_workspace_size", "csa_attend", "hca_attend", "sckv_last_error", "sckv_abi_version"]
 
@@ -78,6 +85,8 @@ def load() -> C.CDLL:
     P, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
     L.csa_compress.argtypes = [i32, i64, i32, i32, i64, i64, C.POINTER(PoolStream), C.POINTER(PoolStream), P]
     L.hca_compress.argtypes = [i32, i64, i32, i32, i64, i64, C.POINTER(PoolStream), P]
+    L.csa_append.argtypes = [i32, i32, i32, C.POINTER(AppendStream), C.POINTER(AppendStream), P]
+    L.hca_append.argtypes = [i32, i32, i32, C.POINTER(AppendStream), P]
     L.csa_index_topk_workspace_size.argtypes = [C.POINTER(IndexArgs)]
     L.csa_index_topk_workspace_size.restype = sz
     L.csa_index_topk.argtypes = [C.POINTER(IndexArgs), P, sz, P]
@@ -90,8 +99,8 @@ def load() -> C.CDLL:
         getattr(L, n).restype = sz
     for n in ("csa_attend", "hca_attend"):
         getattr(L, n).argtypes = [C.POINTER(AttendArgs), P, sz, P]
-    for n in ("csa_compress", "hca_compress", "csa_index_topk", "csa_index_score", "csa_topk_select",
-              "csa_attend", "hca_attend"):
+    for n in ("csa_compress", "hca_compress", "csa_append", "hca_append", "csa_index_topk", "csa_index_score",
+              "csa_topk_select", "csa_attend", "hca_attend"):
         getattr(L, n).restype = C.c_int
     L.sckv_last_error.restype = C.c_char_p
     L.sckv_abi_version.restype = C.c_int32
@@ -169,6 +178,30 @@ class Pool:
                           E_cap, D, dtype_code(self.val), dtype_code(self.out), self.layout)
 
 
+@dataclass
+class Append:
+    """One stream's decode append: pos [B] int32 positions of the new tokens;
+    val, gate [B][D] the new tokens; val_ring, gate_ring [B][P][D] the last P tokens
+    (slot = position mod P; for the latent stream val_ring may be the window ring);
+    bpos [m+o][D] fp32; out (+ out_scale) the entry cache as in Pool."""
+    pos: torch.Tensor
+    val: torch.Tensor
+    gate: torch.Tensor
+    val_ring: torch.Tensor
+    gate_ring: torch.Tensor
+    bpos: torch.Tensor
+    out: torch.Tensor
+    out_scale: Optional[torch.Tensor] = None
+    layout: int = LAYOUT_ROWS
+
+    def c(self) -> AppendStream:
+        D = int(self.val.shape[1])
+        E_cap = int(self.out.shape[1]) if self.layout == LAYOUT_ROWS else int(self.out.shape[1]) * 32
+        return AppendStream(_ptr(self.pos), _ptr(self.val), _ptr(self.gate), _ptr(self.val_ring),
+                            _ptr(self.gate_ring), _ptr(self.bpos), _ptr(self.out), _ptr(self.out_scale), E_cap, D,
+                            int(self.val_ring.shape[1]), dtype_code(self.val), dtype_code(self.out), self.layout, 0)
+
+
 # ---------------------------------------------------------------- indexer key tiles
 def key_tiles_empty(B: int, E_cap: int, D_I: int, dtype, device) -> torch.Tensor:
     """An indexer key cache in the tiled layout [B][E_cap/32][D_I/8][32][8]."""
@@ -217,6 +250,19 @@ def hca_compress(kv: Pool, *, m: int = 128, o: int = 0, e_begin: int = 0, e_coun
     e_count = (N // m - e_begin) if e_count is None else e_count
     a = kv.c()
     _check(load().hca_compress(B, N, m, o, e_begin, e_count, C.byref(a), _stream(stream)))
+
+
+def csa_append(kv: Append, index_keys: Optional[Append] = None, *, m: int = 4, o: int = 4, stream=None):
+    B = int(kv.val.shape[0])
+    a = kv.c()
+    b = index_keys.c() if index_keys is not None else None
+    _check(load().csa_append(B, m, o, C.byref(a), C.byref(b) if b is not None else None, _stream(stream)))
+
+
+def hca_append(kv: Append, *, m: int = 128, o: int = 0, stream=None):
+    B = int(kv.val.shape[0])
+    a = kv.c()
+    _check(load().hca_append(B, m, o, C.byref(a), _stream(stream)))
 
 
 def index_args(rows: RowSpec, q, w, keys, out_idx, *, m: int, W: int, k: int, out_score=None) -> IndexArgs:

@@ -8,7 +8,9 @@
 // HBM streaming: lane groups of D/8 lanes own one entry, each lane 8 channels,
 // so every token row is read as one contiguous D-wide segment.  The softmax is
 // taken online with one exp per (token, channel): the larger of the running
-// maximum and the new logit sets which side is rescaled.
+// maximum and the new logit sets which side is rescaled.  In decode, one token
+// per sequence is appended to small rings of recent tokens, and the entry it
+// completes (one per m tokens) is pooled by the same code.
 #include "device_common.h"
 #include "sckv_internal.h"
 
@@ -31,33 +33,29 @@ __device__ __forceinline__ void load8(const void* base, int64_t elem, float (&x)
   }
 }
 
-template <int IN, int OUT, bool SCALED>
-__global__ __launch_bounds__(256) void compress_kernel(
-    const void* __restrict__ val, const void* __restrict__ gate, const float* __restrict__ bpos,
-    void* __restrict__ out, float* __restrict__ out_scale, int64_t N, int D, int m, int o,
-    int64_t e_begin, int64_t e_count, int64_t E_cap, int G, int key_tiles) {
-  const int lane = lane_id();
-  const int epw = kWave / G;
-  const int slot = lane / G, sub = lane % G;
-  const int64_t e_local = (int64_t)blockIdx.x * (4 * epw) + wave_id() * epw + slot;
-  const bool active = e_local < e_count;
-  const int64_t e = e_begin + (active ? e_local : 0);
-  const int64_t b = blockIdx.y;
-  const int ch = sub * 8;
-
-  const int64_t i0 = (int64_t)m * e - o;
-  const int64_t i1 = (int64_t)m * e + m;
+// Pools entry e of sequence b from tokens [i0, i1) (cut to i >= 0) and stores it.
+// This lane owns channels ch .. ch+7 of the entry; the entry's G = D/8 lanes are
+// G consecutive lanes of a G-aligned group (the e4m3 scale is reduced over them).
+// tok(i, g, v) loads token i's 8 gate logits and values of this lane's channels.
+// Lanes with active == false take part in the reduction but load and store nothing.
+template <int IN, int OUT, bool SCALED, class Tok>
+__device__ __forceinline__ void pool_and_store(Tok tok, const float* __restrict__ bpos, int64_t i0, int64_t i1,
+                                               int D, int ch, int G, bool active, int sub, int64_t b, int64_t e,
+                                               int64_t E_cap, int key_tiles, void* __restrict__ out,
+                                               float* __restrict__ out_scale) {
   float mx[8], l[8], acc[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) { mx[c] = -INFINITY; l[c] = 0.f; acc[c] = 0.f; }
 
   for (int64_t i = i0 < 0 ? 0 : i0; i < i1; ++i) {
-    float g[8], v[8];
-    const int64_t row = (b * N + i) * D + ch;
-    load8<IN>(gate, row, g);
-    load8<IN>(val, row, v);
-    const f32x4* bp = reinterpret_cast<const f32x4*>(bpos + (i - i0) * D + ch);
-    const f32x4 bp0 = bp[0], bp1 = bp[1];
+    float g[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    f32x4 bp0 = {0.f, 0.f, 0.f, 0.f}, bp1 = {0.f, 0.f, 0.f, 0.f};
+    if (active) {
+      tok(i, g, v);
+      const f32x4* bp = reinterpret_cast<const f32x4*>(bpos + (i - i0) * D + ch);
+      bp0 = bp[0];
+      bp1 = bp[1];
+    }
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const float a = g[c] + (c < 4 ? bp0[c] : bp1[c - 4]);
@@ -111,6 +109,74 @@ __global__ __launch_bounds__(256) void compress_kernel(
   }
 }
 
+template <int IN, int OUT, bool SCALED>
+__global__ __launch_bounds__(256) void compress_kernel(
+    const void* __restrict__ val, const void* __restrict__ gate, const float* __restrict__ bpos,
+    void* __restrict__ out, float* __restrict__ out_scale, int64_t N, int D, int m, int o,
+    int64_t e_begin, int64_t e_count, int64_t E_cap, int G, int key_tiles) {
+  const int lane = lane_id();
+  const int epw = kWave / G;
+  const int slot = lane / G, sub = lane % G;
+  const int64_t e_local = (int64_t)blockIdx.x * (4 * epw) + wave_id() * epw + slot;
+  const bool active = e_local < e_count;
+  const int64_t e = e_begin + (active ? e_local : 0);
+  const int64_t b = blockIdx.y;
+  const int ch = sub * 8;
+  auto tok = [&](int64_t i, float (&g)[8], float (&v)[8]) __attribute__((always_inline)) {
+    const int64_t row = (b * N + i) * D + ch;
+    load8<IN>(gate, row, g);
+    load8<IN>(val, row, v);
+  };
+  pool_and_store<IN, OUT, SCALED>(tok, bpos, (int64_t)m * e - o, (int64_t)m * e + m, D, ch, G, active, sub, b, e,
+                                  E_cap, key_tiles, out, out_scale);
+}
+
+// Decode append: one new token per sequence (one wave per sequence).  The token
+// goes into the value and gate rings at slot t mod P; when it completes entry
+// e = (t + 1) / m - 1, the entry is pooled from the rings (tokens before t) and
+// the new token, by the same code as the bulk compressor.
+template <int IN, int OUT, bool SCALED>
+__global__ __launch_bounds__(64) void append_kernel(const int32_t* __restrict__ pos, const void* __restrict__ val,
+                                                    const void* __restrict__ gate, void* __restrict__ val_ring,
+                                                    void* __restrict__ gate_ring, const float* __restrict__ bpos,
+                                                    void* __restrict__ out, float* __restrict__ out_scale, int D,
+                                                    int P, int m, int o, int64_t E_cap, int key_tiles) {
+  constexpr int ES = IN == SCKV_BF16 ? 2 : 4;
+  const int64_t b = blockIdx.x;
+  const int G = D / 8, lane = lane_id();
+  const bool active = lane < G;
+  const int ch = active ? lane * 8 : 0;
+  const int32_t t = pos[b];
+  if (t < 0) return;                                       // whole wave: nothing to append
+  const int64_t slot_t = t % P;
+  if (active) {
+    const uint8_t* sv = static_cast<const uint8_t*>(val) + (b * D + ch) * ES;
+    const uint8_t* sg = static_cast<const uint8_t*>(gate) + (b * D + ch) * ES;
+    uint8_t* dv = static_cast<uint8_t*>(val_ring) + ((b * P + slot_t) * D + ch) * ES;
+    uint8_t* dg = static_cast<uint8_t*>(gate_ring) + ((b * P + slot_t) * D + ch) * ES;
+#pragma unroll
+    for (int k = 0; k < ES / 2; ++k) {
+      reinterpret_cast<u32x4*>(dv)[k] = reinterpret_cast<const u32x4*>(sv)[k];
+      reinterpret_cast<u32x4*>(dg)[k] = reinterpret_cast<const u32x4*>(sg)[k];
+    }
+  }
+  if ((t + 1) % m != 0) return;                            // uniform: no entry completes
+  const int64_t e = (int64_t)(t + 1) / m - 1;
+  if (e >= E_cap) return;
+  auto tok = [&](int64_t i, float (&g)[8], float (&v)[8]) __attribute__((always_inline)) {
+    if (i == t) {
+      load8<IN>(gate, b * D + ch, g);
+      load8<IN>(val, b * D + ch, v);
+    } else {
+      const int64_t row = (b * P + i % P) * D + ch;
+      load8<IN>(gate_ring, row, g);
+      load8<IN>(val_ring, row, v);
+    }
+  };
+  pool_and_store<IN, OUT, SCALED>(tok, bpos, (int64_t)m * e - o, (int64_t)m * e + m, D, ch, G, active, lane, b, e,
+                                  E_cap, key_tiles, out, out_scale);
+}
+
 template <int IN>
 static hipError_t launch_in(const sckv_pool_stream& s, int32_t B, int64_t N, int32_t m, int32_t o,
                             int64_t e_begin, int64_t e_count, hipStream_t stream) {
@@ -131,6 +197,29 @@ static hipError_t launch_in(const sckv_pool_stream& s, int32_t B, int64_t N, int
   }
 #undef SCKV_LAUNCH
   return hipGetLastError();
+}
+
+template <int IN>
+static hipError_t launch_append_in(const sckv_append_stream& s, int32_t B, int32_t m, int32_t o,
+                                   hipStream_t stream) {
+  const int kt = s.out_layout == SCKV_LAYOUT_KEY_TILES ? 1 : 0;
+#define SCKV_LAUNCH(OUT, SC)                                                                                  \
+  hipLaunchKernelGGL((append_kernel<IN, OUT, SC>), dim3((unsigned)B), dim3(64), 0, stream, s.pos, s.val, s.gate, \
+                     s.val_ring, s.gate_ring, s.bpos, s.out, s.out_scale, s.D, s.P, m, o, s.E_cap, kt)
+  switch (s.out_dtype) {
+    case SCKV_F32: SCKV_LAUNCH(SCKV_F32, false); break;
+    case SCKV_BF16: SCKV_LAUNCH(SCKV_BF16, false); break;
+    default:
+      if (s.out_scale) SCKV_LAUNCH(SCKV_E4M3, true);
+      else SCKV_LAUNCH(SCKV_E4M3, false);
+  }
+#undef SCKV_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const sckv_append_stream& s, int32_t B, int32_t m, int32_t o, hipStream_t stream) {
+  if (s.in_dtype == SCKV_BF16) return launch_append_in<SCKV_BF16>(s, B, m, o, stream);
+  return launch_append_in<SCKV_F32>(s, B, m, o, stream);
 }
 
 hipError_t launch_compress(const sckv_pool_stream& s, int32_t B, int64_t N, int32_t m, int32_t o,

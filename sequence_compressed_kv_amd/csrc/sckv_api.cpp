@@ -72,6 +72,29 @@ sckv_status check_pool(const sckv_pool_stream* s, const char* name, int32_t B, i
   return SCKV_OK;
 }
 
+// ---------------------------------------------------------------- decode append
+sckv_status check_append(const sckv_append_stream* s, const char* name, int32_t B, int32_t m, int32_t o) {
+  if (!s) return fail(SCKV_ERR_NULL, "%s: stream descriptor is NULL", name);
+  if (!s->pos || !s->val || !s->gate || !s->val_ring || !s->gate_ring || !s->bpos || !s->out)
+    return fail(SCKV_ERR_NULL, "%s: pos/val/gate/val_ring/gate_ring/bpos/out must be set", name);
+  if (s->in_dtype != SCKV_F32 && s->in_dtype != SCKV_BF16)
+    return fail(SCKV_ERR_DTYPE, "%s: in_dtype %s not supported (F32, BF16)", name, dtname(s->in_dtype));
+  if (s->out_dtype != SCKV_F32 && s->out_dtype != SCKV_BF16 && s->out_dtype != SCKV_E4M3)
+    return fail(SCKV_ERR_DTYPE, "%s: out_dtype %d not supported", name, s->out_dtype);
+  if (!pow2_dim(s->D)) return fail(SCKV_ERR_UNSUPPORTED, "%s: D=%d not in {8,...,512} (powers of two)", name, s->D);
+  if (s->out_layout != SCKV_LAYOUT_ROWS && s->out_layout != SCKV_LAYOUT_KEY_TILES)
+    return fail(SCKV_ERR_SHAPE, "%s: unknown out_layout %d", name, s->out_layout);
+  if (s->out_layout == SCKV_LAYOUT_KEY_TILES && s->E_cap % 32 != 0)
+    return fail(SCKV_ERR_SHAPE, "%s: key-tile caches need E_cap %% 32 == 0 (E_cap=%lld)", name, (long long)s->E_cap);
+  if (B < 1 || m < 1 || o < 0 || s->E_cap < 1) return fail(SCKV_ERR_SHAPE, "%s: need B>=1, m>=1, o>=0, E_cap>=1", name);
+  if ((int64_t)s->P < (int64_t)m + o)
+    return fail(SCKV_ERR_SHAPE, "%s: P=%d ring slots < m+o=%d tokens of an entry", name, s->P, m + o);
+  if (!aligned16(s->val) || !aligned16(s->gate) || !aligned16(s->val_ring) || !aligned16(s->gate_ring) ||
+      !aligned16(s->bpos) || !aligned16(s->out) || (s->out_scale && !aligned16(s->out_scale)))
+    return fail(SCKV_ERR_ALIGN, "%s: tensors must be 16-byte aligned", name);
+  return SCKV_OK;
+}
+
 // ---------------------------------------------------------------- rows
 sckv_status check_rows(const sckv_rows& r, int32_t B, const char* name) {
   if (r.R < 1) return fail(SCKV_ERR_SHAPE, "%s: rows.R=%d must be >= 1", name, r.R);
@@ -204,6 +227,26 @@ sckv_status hca_compress(int32_t B, int64_t N, int32_t m, int32_t o, int64_t e_b
   if (s != SCKV_OK) return s;
   return hip_status(sckv::launch_compress(*kv, B, N, m, o, e_begin, e_count, static_cast<hipStream_t>(stream)),
                     "hca_compress");
+}
+
+sckv_status csa_append(int32_t B, int32_t m, int32_t o, const sckv_append_stream* kv,
+                       const sckv_append_stream* index_keys, void* stream) {
+  sckv_status s = check_append(kv, "csa_append(kv)", B, m, o);
+  if (s != SCKV_OK) return s;
+  if (index_keys) {
+    s = check_append(index_keys, "csa_append(index_keys)", B, m, o);
+    if (s != SCKV_OK) return s;
+  }
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = sckv::launch_append(*kv, B, m, o, st);
+  if (e == hipSuccess && index_keys) e = sckv::launch_append(*index_keys, B, m, o, st);
+  return hip_status(e, "csa_append");
+}
+
+sckv_status hca_append(int32_t B, int32_t m, int32_t o, const sckv_append_stream* kv, void* stream) {
+  sckv_status s = check_append(kv, "hca_append", B, m, o);
+  if (s != SCKV_OK) return s;
+  return hip_status(sckv::launch_append(*kv, B, m, o, static_cast<hipStream_t>(stream)), "hca_append");
 }
 
 size_t csa_index_topk_workspace_size(const sckv_index_args* a) {

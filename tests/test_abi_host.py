@@ -76,6 +76,36 @@ def test_compress_token_range(L):
     assert L.csa_compress(1, 64, 4, 4, 0, 16, None, None, None) == 1
 
 
+def app(**kw):
+    d = dict(pos=FAKE, val=FAKE, gate=FAKE, val_ring=FAKE, gate_ring=FAKE, bpos=FAKE, out=FAKE, out_scale=None,
+             E_cap=16, D=64, P=8, in_dtype=1, out_dtype=1, out_layout=0, reserved=0)
+    d.update(kw)
+    return _lib.AppendStream(**d)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(pos=None), 1), (dict(gate_ring=None), 1), (dict(val_ring=None), 1), (dict(in_dtype=2), 3),
+    (dict(out_dtype=9), 3), (dict(D=24), 4), (dict(P=7), 2), (dict(E_cap=0), 2),
+    (dict(out_layout=1, E_cap=40), 2), (dict(gate_ring=FAKE_ODD), 5), (dict(out_scale=FAKE_ODD, out_dtype=2), 5),
+])
+def test_append_validation(L, kw, status):
+    a = app(**kw)
+    assert L.csa_append(2, 4, 4, C.byref(a), None, None) == status, err(L)
+    assert err(L)
+
+
+def test_append_pool_and_counts(L):
+    a = app()
+    assert L.csa_append(0, 4, 4, C.byref(a), None, None) == 2                   # B = 0
+    assert L.csa_append(2, 0, 4, C.byref(a), None, None) == 2                   # m = 0
+    assert L.hca_append(2, 128, 0, C.byref(a), None) == 2                      # P = 8 < 128 ring slots
+    bad_idx = app(bpos=None)
+    assert L.csa_append(2, 4, 4, C.byref(a), C.byref(bad_idx), None) == 1       # the index stream is checked too
+    assert L.csa_append(2, 4, 4, None, None, None) == 1
+    assert L.hca_append(2, 128, 0, C.byref(app(P=127)), None) == 2
+    assert L.hca_append(2, 128, 0, C.byref(app(P=128, val=None)), None) == 1
+
+
 def idx_args(**kw):
     rows = kw.pop("rows", _lib.Rows(FAKE, 0, 2, 4095, 0, 0, 0))
     d = dict(rows=rows, q=FAKE, w=FAKE, keys=FAKE, out_idx=FAKE, out_score=None, E_cap=1024, B=2, H_I=64, D_I=128,

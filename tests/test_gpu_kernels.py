@@ -119,6 +119,89 @@ def test_compress_key_tiles(ins, outs, D, B, N):
             assert e4m3_flips(got, st["codes"], c, mag)[1] == 0
 
 
+APPEND_CASES = [
+    # m, o, D, in, out, scaled, key tiles, B, N, ring slots P
+    (4, 4, 64, "bf16", "bf16", False, False, 3, 600, 8),
+    (4, 4, 128, "bf16", "bf16", False, True, 2, 520, 8),          # indexer keys, tiled
+    (4, 4, 128, "bf16", "e4m3", False, True, 2, 300, 8),          # unscaled e4m3 keys, tiled
+    (4, 4, 512, "bf16", "e4m3", True, False, 2, 300, 128),        # latent: the window ring as value ring
+    (128, 0, 64, "f32", "f32", False, False, 2, 700, 128),
+    (128, 0, 512, "bf16", "e4m3", True, False, 1, 520, 128),
+    (2, 6, 16, "f32", "bf16", False, False, 2, 101, 9),
+]
+
+
+@pytest.mark.parametrize("m,o,D,ins,outs,scaled,tiled,B,N,P", APPEND_CASES)
+def test_append_token_by_token(m, o, D, ins, outs, scaled, tiled, B, N, P):
+    """Decode appends, one token per call, with the sequences at different
+    positions: the entries equal the bulk compressor's bit for bit (and follow the
+    oracle in code space), and the rings hold each sequence's last P tokens."""
+    print(f"append m={m} o={o} D={D} {ins}->{outs} scaled={scaled} tiled={tiled} B={B} N={N} P={P}", flush=True)
+    rng = np.random.default_rng(300 + D + m + N)
+    v = rng_store(rng, (B, N, D), ins)
+    g = rng_store(rng, (B, N, D), ins, 2.0)
+    bpos = rng.normal(0, 0.5, (m + o, D)).astype(np.float32)
+    E = N // m
+    E_cap = (E + 31) // 32 * 32 if tiled else E
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "e4m3": torch.uint8}[outs]
+
+    def cache():
+        t = (torch.zeros(B, E_cap // 32, D // 8, 32, 8, device=DEV, dtype=tdt) if tiled
+             else torch.zeros(B, E_cap, D, device=DEV, dtype=tdt))
+        return t.view(torch.float8_e4m3fn) if outs == "e4m3" else t
+
+    out_a, out_b = cache(), cache()
+    sc_a = torch.zeros(B, E_cap, device=DEV) if scaled else None
+    sc_b = torch.zeros(B, E_cap, device=DEV) if scaled else None
+    layout = sk.LAYOUT_KEY_TILES if tiled else sk.LAYOUT_ROWS
+    vd, gd, bd = dev(v, ins), dev(g, ins), dev(bpos)
+    rv = torch.zeros(B, P, D, device=DEV, dtype=vd.dtype)
+    rg = torch.zeros(B, P, D, device=DEV, dtype=vd.dtype)
+    off = [3 * b for b in range(B)]                          # sequence b starts 3b calls late
+    ar = torch.arange(B, device=DEV)
+    for c in range(N + max(off)):
+        p_host = [c - off[b] if 0 <= c - off[b] < N else -1 for b in range(B)]
+        pos = dev_i32(p_host)
+        pc = pos.clamp(min=0).long()
+        a = sk.Append(pos, vd[ar, pc].contiguous(), gd[ar, pc].contiguous(), rv, rg, bd, out_a, sc_a, layout)
+        if m == 128:
+            sk.hca_append(a, m=m, o=o)
+        else:
+            sk.csa_append(a, m=m, o=o)
+    bulk = sk.Pool(vd, gd, bd, out_b, sc_b, layout)
+    if m == 128:
+        sk.hca_compress(bulk, m=m, o=o)
+    else:
+        sk.csa_compress(bulk, m=m, o=o)
+    torch.cuda.synchronize()
+    raw = (lambda t: t.view(torch.uint8)) if outs == "e4m3" else (lambda t: t)
+    assert torch.equal(raw(out_a), raw(out_b)), "appended entries differ from the bulk compressor's"
+    if scaled:
+        assert torch.equal(sc_a, sc_b)
+    for b in range(B):                                       # the rings: the last P tokens, slot = position mod P
+        last = np.arange(N - P, N)
+        np.testing.assert_array_equal(host(rv[b])[last % P], v[b][last])
+        np.testing.assert_array_equal(host(rg[b])[last % P], g[b][last])
+    # the oracle, in code space, for sequence 0
+    c = method.compress(v[0], g[0], bpos, m, o)
+    mag = method.compress(np.abs(v[0]), g[0], bpos, m, o)
+    got = host(sk.from_key_tiles(out_a) if tiled else out_a)[0][:E]
+    if outs == "f32":
+        assert_close(got, c, rtol=1e-5, what="f32 entries")
+    elif outs == "bf16":
+        st = method.store_keys(c, "bf16") if tiled else method.store_entries(c, "bf16")
+        assert bf16_code_flips(got, c, st["values"], magnitude=mag)[1] == 0
+    else:
+        st = method.store_entries(c, "e4m3") if scaled else method.store_keys(c, "e4m3")
+        if scaled:
+            gs = sc_a[0].cpu().numpy().astype(np.float64)[:E]
+            np.testing.assert_allclose(gs, st["scale"], rtol=2e-6)
+            y, ymag = c / st["scale"][:, None], mag / st["scale"][:, None]
+        else:
+            y, ymag = c, mag
+        assert e4m3_flips(got, st["codes"], y, ymag)[1] == 0
+
+
 def test_compress_appends_only_requested_entries():
     rng = np.random.default_rng(5)
     B, N, D = 2, 256, 64
