@@ -41,6 +41,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill indexer measurement")
     ap.add_argument("--no-1m", action="store_true", help="skip the 1M-context fp8 decode measurement")
+    ap.add_argument("--no-append", action="store_true", help="skip the steady-state decode-with-appends measurement")
     ap.add_argument("--only", choices=["prefill", "1m"], default=None,
                     help="run only that side measurement and print its record (for profiling its kernels)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -112,8 +113,10 @@ def prefill_indexer_rate(dev, sk, torch, wl, iters: int = 5):
             "frac": tf / PEAK_BF16_TFLOPS}
 
 
-def build_caches(wl, dev, sk, torch, gen):
-    """Caches of every sequence for both layers (GPU-drawn streams, library compressors)."""
+def build_caches(wl, dev, sk, torch, gen, tail: int = 0):
+    """Caches of every sequence for both layers (GPU-drawn streams, library compressors).
+    With tail > 0 the last `tail` tokens of every stream are returned too (third
+    value: per layer, a dict of [B][tail][D] tensors) for decode appends."""
     B = wl.B
     csa, hca = wl.layers
     bf = torch.bfloat16
@@ -126,8 +129,16 @@ def build_caches(wl, dev, sk, torch, gen):
     weights = gen.gpu_weights(wl, dev)
     wc, wh = weights
     slots = torch.arange(wl.N - csa.W, wl.N, device=dev) % csa.W
+    tails = None
+    if tail:
+        tails = [{n: torch.empty(B, tail, wc[n].shape[0], device=dev, dtype=bf) for n in ("v", "g", "vI", "gI")},
+                 {n: torch.empty(B, tail, wh[n].shape[0], device=dev, dtype=bf) for n in ("v", "g")}]
     for b in range(B):
         st_c, st_h = gen.gpu_sequence_streams(wl, b, weights, dev)
+        if tail:
+            for st, tl in zip((st_c, st_h), tails):
+                for n in tl:
+                    tl[n][b] = st[n][wl.N - tail:]
         kv = sk.Pool(st_c["v"][None], st_c["g"][None], wc["bpos"].contiguous(), c["entries"][b:b + 1])
         ix = sk.Pool(st_c["vI"][None], st_c["gI"][None], wc["bposI"].contiguous(), c["keys"][b:b + 1],
                      layout=sk.LAYOUT_KEY_TILES)
@@ -138,7 +149,115 @@ def build_caches(wl, dev, sk, torch, gen):
         h["win"][b, slots] = st_h["v"][wl.N - hca.W:]
         del st_c, st_h
     torch.cuda.synchronize()
+    if tail:
+        return c, h, tails, weights
     return c, h
+
+
+def decode_append_rate(dev, sk, torch, wl, c, h, tails, weights, qc, qh, steps: int = 128, replays: int = 5):
+    """Steady-state decode of the pair: `steps` consecutive tokens (the last ones
+    of every sequence, re-appended at their own positions) each appended to the
+    rings and caches (csa_append for the latent and indexer streams, hca_append)
+    before the step's index, top-k and attention.  Timed eagerly and as one HIP
+    graph of all the steps; the caches after the appends must equal the ones the
+    bulk compressors built."""
+    csa, hca = wl.layers
+    B, N = wl.B, wl.N
+    t0 = N - steps
+    bf = torch.bfloat16
+    wc, wh = weights
+    P_lat = csa.W                                          # the window ring doubles as the value ring
+    before = {k: v.clone() for k, v in c.items()}, {k: v.clone() for k, v in h.items()}
+    tl_c, tl_h = tails
+    T = tl_c["v"].shape[1]
+    # rings as of position t0 - 1 (slot = position mod P)
+    pos_r = torch.arange(t0 - P_lat, t0, device=dev)
+    ring0 = {"win_c": torch.empty_like(c["win"]), "win_h": torch.empty_like(h["win"]),
+             "g_c": torch.empty(B, P_lat, csa.D, device=dev, dtype=bf),
+             "g_h": torch.empty(B, hca.m, hca.D, device=dev, dtype=bf),
+             "vI": torch.empty(B, csa.m + csa.o, csa.D_I, device=dev, dtype=bf),
+             "gI": torch.empty(B, csa.m + csa.o, csa.D_I, device=dev, dtype=bf)}
+    src = pos_r - (N - T)
+    ring0["win_c"][:, pos_r % P_lat] = tl_c["v"][:, src]
+    ring0["g_c"][:, pos_r % P_lat] = tl_c["g"][:, src]
+    ring0["win_h"][:, pos_r % hca.W] = tl_h["v"][:, src]
+    ring0["g_h"][:, pos_r % hca.m] = tl_h["g"][:, src]
+    pi = torch.arange(t0 - (csa.m + csa.o), t0, device=dev)
+    ring0["vI"][:, pi % (csa.m + csa.o)] = tl_c["vI"][:, pi - (N - T)]
+    ring0["gI"][:, pi % (csa.m + csa.o)] = tl_c["gI"][:, pi - (N - T)]
+    rings = {k: v.clone() for k, v in ring0.items()}
+    rings["win_c"], rings["win_h"] = c["win"], h["win"]    # the attention reads the live window rings
+    pos = [torch.full((B,), t, dtype=torch.int32, device=dev) for t in range(t0, N)]
+    idx = torch.empty(B, csa.k, dtype=torch.int32, device=dev)
+    out_c = torch.empty(B, csa.H, csa.D, device=dev)
+    out_h = torch.empty(B, hca.H, hca.D, device=dev)
+    tau = 1.0 / math.sqrt(csa.d_h)
+    rows0 = sk.RowSpec.decode(pos[-1], N - 1)
+    ws_i = sk.csa_index_topk(rows0, qc["qI"], qc["w"], c["keys"], idx, m=csa.m, W=csa.W, k=csa.k)
+    ws_c = sk.csa_attend(rows0, qc["q"], c["entries"], idx, c["win"], out_c, m=csa.m, W=csa.W, softmax_scale=tau)
+    ws_h = sk.hca_attend(rows0, qh["q"], h["entries"], h["win"], out_h, m=hca.m, W=hca.W, softmax_scale=tau)
+    new = [{n: tl_c[n][:, t - (N - T)].contiguous() for n in tl_c} | {"vh": tl_h["v"][:, t - (N - T)].contiguous(),
+           "gh": tl_h["g"][:, t - (N - T)].contiguous()} for t in range(t0, N)]
+
+    def reset():
+        for k in ("win_c", "win_h", "g_c", "g_h", "vI", "gI"):
+            rings[k].copy_(ring0[k])
+
+    def step(s):
+        p, x = pos[s], new[s]
+        sk.csa_append(sk.Append(p, x["v"], x["g"], rings["win_c"], rings["g_c"], wc["bpos"], c["entries"]),
+                      sk.Append(p, x["vI"], x["gI"], rings["vI"], rings["gI"], wc["bposI"], c["keys"],
+                                layout=sk.LAYOUT_KEY_TILES), m=csa.m, o=csa.o)
+        sk.hca_append(sk.Append(p, x["vh"], x["gh"], rings["win_h"], rings["g_h"], wh["bpos"], h["entries"]),
+                      m=hca.m, o=hca.o)
+        rows = sk.RowSpec.decode(p, N - 1)
+        sk.csa_index_topk(rows, qc["qI"], qc["w"], c["keys"], idx, m=csa.m, W=csa.W, k=csa.k, workspace=ws_i)
+        sk.csa_attend(rows, qc["q"], c["entries"], idx, c["win"], out_c, m=csa.m, W=csa.W, softmax_scale=tau,
+                      workspace=ws_c)
+        sk.hca_attend(rows, qh["q"], h["entries"], h["win"], out_h, m=hca.m, W=hca.W, softmax_scale=tau,
+                      workspace=ws_h)
+
+    def run():
+        reset()
+        for s_ in range(steps):
+            step(s_)
+
+    stream = torch.cuda.current_stream()
+    run()
+    torch.cuda.synchronize()
+    same_caches = all(torch.equal(before[0][k], c[k]) for k in c) and all(torch.equal(before[1][k], h[k]) for k in h)
+    ref_c, ref_h = out_c.clone(), out_h.clone()
+
+    def timed(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n / steps
+
+    ms_eager = timed(run, replays)
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            run()
+    stream.wait_stream(cap)
+    torch.cuda.synchronize()
+    out_c.zero_()
+    out_h.zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    same_graph = bool(torch.equal(out_c, ref_c) and torch.equal(out_h, ref_h))
+    ms_graph = timed(g.replay, replays)
+    by_append = (3 * csa.D * 2 + 2 * csa.D_I * 2 + 2 * hca.D * 2) * B       # new tokens in, ring slots out
+    return {"workload": wl.name, "steps": steps, "positions": [t0, N - 1], "ms_per_step_eager": ms_eager,
+            "ms_per_step_graph": ms_graph, "queries_per_s_graph": B / (ms_graph * 1e-3),
+            "caches_equal_bulk_compress": same_caches, "graph_matches_eager": same_graph,
+            "append_bytes_per_step": by_append}
 
 
 def decode_1m_rate(dev, sk, torch, gen, steps: int = 20, replicas: int = 4):
@@ -305,7 +424,7 @@ def main():
     t = wl.N - 1
     print(f"[bench] building caches: B={B} N={wl.N}", file=sys.stderr, flush=True)
     tb = time.time()
-    c0, h0 = build_caches(wl, dev, sk, torch, gen)
+    c0, h0, tails, weights = build_caches(wl, dev, sk, torch, gen, tail=256)
     reps = [(c0, h0)] + [({k: v.clone() for k, v in c0.items()}, {k: v.clone() for k, v in h0.items()})
                          for _ in range(args.replicas - 1)]
     qc = gen.gpu_queries(wl, 0, B, dev)
@@ -400,6 +519,10 @@ def main():
                      "traffic": counter_traffic(TRAFFIC_SUMMARY), "bytes_per_launch": ab["score"] * B},
         "wall_s_timed": wall,
     }
+    if not args.no_append:
+        print("[bench] steady-state decode with appends", file=sys.stderr, flush=True)
+        rec["decode_append"] = decode_append_rate(dev, sk, torch, wl, c0, h0, tails, weights, qc, qh)
+    del tails
     if not args.no_prefill:
         print("[bench] prefill indexer scoring (32K causal rows)", file=sys.stderr, flush=True)
         del reps, c0, h0
