@@ -131,29 +131,42 @@ __global__ __launch_bounds__(256) void compress_kernel(
                                   E_cap, key_tiles, out, out_scale);
 }
 
-// Decode append: one new token per sequence (one wave per sequence).  The token
+// One stream of a decode append, as the kernel sees it.
+struct AppendK {
+  const int32_t* pos;
+  const void* val;
+  const void* gate;
+  void* val_ring;
+  void* gate_ring;
+  const float* bpos;
+  void* out;
+  float* out_scale;
+  int64_t E_cap;
+  int D, P, key_tiles;
+};
+
+// Decode append: one new token per sequence (one wave per sequence; blockIdx.y
+// picks one of up to two streams that share the pool and the dtypes).  The token
 // goes into the value and gate rings at slot t mod P; when it completes entry
 // e = (t + 1) / m - 1, the entry is pooled from the rings (tokens before t) and
 // the new token, by the same code as the bulk compressor.
 template <int IN, int OUT, bool SCALED>
-__global__ __launch_bounds__(64) void append_kernel(const int32_t* __restrict__ pos, const void* __restrict__ val,
-                                                    const void* __restrict__ gate, void* __restrict__ val_ring,
-                                                    void* __restrict__ gate_ring, const float* __restrict__ bpos,
-                                                    void* __restrict__ out, float* __restrict__ out_scale, int D,
-                                                    int P, int m, int o, int64_t E_cap, int key_tiles) {
+__global__ __launch_bounds__(64) void append_kernel(AppendK s0, AppendK s1, int m, int o) {
   constexpr int ES = IN == SCKV_BF16 ? 2 : 4;
+  const AppendK& s = blockIdx.y == 0 ? s0 : s1;
   const int64_t b = blockIdx.x;
+  const int D = s.D, P = s.P;
   const int G = D / 8, lane = lane_id();
   const bool active = lane < G;
   const int ch = active ? lane * 8 : 0;
-  const int32_t t = pos[b];
+  const int32_t t = s.pos[b];
   if (t < 0) return;                                       // whole wave: nothing to append
   const int64_t slot_t = t % P;
   if (active) {
-    const uint8_t* sv = static_cast<const uint8_t*>(val) + (b * D + ch) * ES;
-    const uint8_t* sg = static_cast<const uint8_t*>(gate) + (b * D + ch) * ES;
-    uint8_t* dv = static_cast<uint8_t*>(val_ring) + ((b * P + slot_t) * D + ch) * ES;
-    uint8_t* dg = static_cast<uint8_t*>(gate_ring) + ((b * P + slot_t) * D + ch) * ES;
+    const uint8_t* sv = static_cast<const uint8_t*>(s.val) + (b * D + ch) * ES;
+    const uint8_t* sg = static_cast<const uint8_t*>(s.gate) + (b * D + ch) * ES;
+    uint8_t* dv = static_cast<uint8_t*>(s.val_ring) + ((b * P + slot_t) * D + ch) * ES;
+    uint8_t* dg = static_cast<uint8_t*>(s.gate_ring) + ((b * P + slot_t) * D + ch) * ES;
 #pragma unroll
     for (int k = 0; k < ES / 2; ++k) {
       reinterpret_cast<u32x4*>(dv)[k] = reinterpret_cast<const u32x4*>(sv)[k];
@@ -162,19 +175,19 @@ __global__ __launch_bounds__(64) void append_kernel(const int32_t* __restrict__ 
   }
   if ((t + 1) % m != 0) return;                            // uniform: no entry completes
   const int64_t e = (int64_t)(t + 1) / m - 1;
-  if (e >= E_cap) return;
+  if (e >= s.E_cap) return;
   auto tok = [&](int64_t i, float (&g)[8], float (&v)[8]) __attribute__((always_inline)) {
     if (i == t) {
-      load8<IN>(gate, b * D + ch, g);
-      load8<IN>(val, b * D + ch, v);
+      load8<IN>(s.gate, b * D + ch, g);
+      load8<IN>(s.val, b * D + ch, v);
     } else {
       const int64_t row = (b * P + i % P) * D + ch;
-      load8<IN>(gate_ring, row, g);
-      load8<IN>(val_ring, row, v);
+      load8<IN>(s.gate_ring, row, g);
+      load8<IN>(s.val_ring, row, v);
     }
   };
-  pool_and_store<IN, OUT, SCALED>(tok, bpos, (int64_t)m * e - o, (int64_t)m * e + m, D, ch, G, active, lane, b, e,
-                                  E_cap, key_tiles, out, out_scale);
+  pool_and_store<IN, OUT, SCALED>(tok, s.bpos, (int64_t)m * e - o, (int64_t)m * e + m, D, ch, G, active, lane, b, e,
+                                  s.E_cap, s.key_tiles, s.out, s.out_scale);
 }
 
 template <int IN>
@@ -199,27 +212,46 @@ static hipError_t launch_in(const sckv_pool_stream& s, int32_t B, int64_t N, int
   return hipGetLastError();
 }
 
+static AppendK append_k(const sckv_append_stream& s) {
+  return AppendK{s.pos,       s.val, s.gate, s.val_ring, s.gate_ring, s.bpos, s.out, s.out_scale,
+                 s.E_cap,     s.D,   s.P,    s.out_layout == SCKV_LAYOUT_KEY_TILES ? 1 : 0};
+}
+
 template <int IN>
-static hipError_t launch_append_in(const sckv_append_stream& s, int32_t B, int32_t m, int32_t o,
-                                   hipStream_t stream) {
-  const int kt = s.out_layout == SCKV_LAYOUT_KEY_TILES ? 1 : 0;
-#define SCKV_LAUNCH(OUT, SC)                                                                                  \
-  hipLaunchKernelGGL((append_kernel<IN, OUT, SC>), dim3((unsigned)B), dim3(64), 0, stream, s.pos, s.val, s.gate, \
-                     s.val_ring, s.gate_ring, s.bpos, s.out, s.out_scale, s.D, s.P, m, o, s.E_cap, kt)
-  switch (s.out_dtype) {
+static hipError_t launch_append_in(const AppendK& k0, const AppendK& k1, int nstreams, int out_dtype, bool scaled,
+                                   int32_t B, int32_t m, int32_t o, hipStream_t stream) {
+  const dim3 grid((unsigned)B, (unsigned)nstreams);
+#define SCKV_LAUNCH(OUT, SC) \
+  hipLaunchKernelGGL((append_kernel<IN, OUT, SC>), grid, dim3(64), 0, stream, k0, k1, m, o)
+  switch (out_dtype) {
     case SCKV_F32: SCKV_LAUNCH(SCKV_F32, false); break;
     case SCKV_BF16: SCKV_LAUNCH(SCKV_BF16, false); break;
     default:
-      if (s.out_scale) SCKV_LAUNCH(SCKV_E4M3, true);
+      if (scaled) SCKV_LAUNCH(SCKV_E4M3, true);
       else SCKV_LAUNCH(SCKV_E4M3, false);
   }
 #undef SCKV_LAUNCH
   return hipGetLastError();
 }
 
-hipError_t launch_append(const sckv_append_stream& s, int32_t B, int32_t m, int32_t o, hipStream_t stream) {
-  if (s.in_dtype == SCKV_BF16) return launch_append_in<SCKV_BF16>(s, B, m, o, stream);
-  return launch_append_in<SCKV_F32>(s, B, m, o, stream);
+static hipError_t launch_append_group(const sckv_append_stream& s, const sckv_append_stream* s2, int32_t B,
+                                      int32_t m, int32_t o, hipStream_t stream) {
+  const AppendK k0 = append_k(s), k1 = s2 ? append_k(*s2) : k0;
+  const int n = s2 ? 2 : 1;
+  if (s.in_dtype == SCKV_BF16)
+    return launch_append_in<SCKV_BF16>(k0, k1, n, s.out_dtype, s.out_scale != nullptr, B, m, o, stream);
+  return launch_append_in<SCKV_F32>(k0, k1, n, s.out_dtype, s.out_scale != nullptr, B, m, o, stream);
+}
+
+// Streams with the same input dtype, output dtype and scaling share one launch.
+hipError_t launch_append(const sckv_append_stream& s, const sckv_append_stream* s2, int32_t B, int32_t m, int32_t o,
+                         hipStream_t stream) {
+  if (s2 && s2->in_dtype == s.in_dtype && s2->out_dtype == s.out_dtype &&
+      (s2->out_scale != nullptr) == (s.out_scale != nullptr))
+    return launch_append_group(s, s2, B, m, o, stream);
+  hipError_t e = launch_append_group(s, nullptr, B, m, o, stream);
+  if (e == hipSuccess && s2) e = launch_append_group(*s2, nullptr, B, m, o, stream);
+  return e;
 }
 
 hipError_t launch_compress(const sckv_pool_stream& s, int32_t B, int64_t N, int32_t m, int32_t o,

@@ -237,16 +237,13 @@ sckv_status csa_append(int32_t B, int32_t m, int32_t o, const sckv_append_stream
     s = check_append(index_keys, "csa_append(index_keys)", B, m, o);
     if (s != SCKV_OK) return s;
   }
-  const hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = sckv::launch_append(*kv, B, m, o, st);
-  if (e == hipSuccess && index_keys) e = sckv::launch_append(*index_keys, B, m, o, st);
-  return hip_status(e, "csa_append");
+  return hip_status(sckv::launch_append(*kv, index_keys, B, m, o, static_cast<hipStream_t>(stream)), "csa_append");
 }
 
 sckv_status hca_append(int32_t B, int32_t m, int32_t o, const sckv_append_stream* kv, void* stream) {
   sckv_status s = check_append(kv, "hca_append", B, m, o);
   if (s != SCKV_OK) return s;
-  return hip_status(sckv::launch_append(*kv, B, m, o, static_cast<hipStream_t>(stream)), "hca_append");
+  return hip_status(sckv::launch_append(*kv, nullptr, B, m, o, static_cast<hipStream_t>(stream)), "hca_append");
 }
 
 size_t csa_index_topk_workspace_size(const sckv_index_args* a) {

@@ -17,7 +17,9 @@ inline int64_t entries_visible(int64_t t, int64_t m, int64_t W) {
 // ---------------------------------------------------------------- compression
 hipError_t launch_compress(const sckv_pool_stream& s, int32_t B, int64_t N, int32_t m, int32_t o,
                            int64_t e_begin, int64_t e_count, hipStream_t stream);
-hipError_t launch_append(const sckv_append_stream& s, int32_t B, int32_t m, int32_t o, hipStream_t stream);
+// Decode append of one stream, or of two streams (s2 non-NULL) over the same positions.
+hipError_t launch_append(const sckv_append_stream& s, const sckv_append_stream* s2, int32_t B, int32_t m, int32_t o,
+                         hipStream_t stream);
 
 // ---------------------------------------------------------------- indexer
 // Largest visible-entry count over the rows (the score matrix width needed).

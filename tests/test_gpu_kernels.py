@@ -202,6 +202,44 @@ def test_append_token_by_token(m, o, D, ins, outs, scaled, tiled, B, N, P):
         assert e4m3_flips(got, st["codes"], y, ymag)[1] == 0
 
 
+@pytest.mark.parametrize("kv_out,scaled", [("bf16", False), ("e4m3", True)])
+def test_csa_append_two_streams(kv_out, scaled):
+    """csa_append with the latent and the indexer stream (one launch when their
+    dtypes agree, two otherwise) equals csa_compress of both streams bit for bit."""
+    print(f"csa append, two streams: kv -> {kv_out} scaled={scaled}", flush=True)
+    rng = np.random.default_rng(41)
+    B, N, D, DI, P = 2, 264, 512, 128, 128
+    v, g = rng_store(rng, (B, N, D), "bf16"), rng_store(rng, (B, N, D), "bf16", 2.0)
+    vI, gI = rng_store(rng, (B, N, DI), "bf16"), rng_store(rng, (B, N, DI), "bf16", 2.0)
+    bp, bpI = rng.normal(0, 0.5, (8, D)).astype(np.float32), rng.normal(0, 0.5, (8, DI)).astype(np.float32)
+    E = N // 4
+    Ec = (E + 31) // 32 * 32
+    kdt = torch.bfloat16 if kv_out == "bf16" else torch.uint8
+
+    def caches():
+        ent = torch.zeros(B, E, D, device=DEV, dtype=kdt)
+        ent = ent.view(torch.float8_e4m3fn) if kv_out == "e4m3" else ent
+        scale = torch.zeros(B, E, device=DEV) if scaled else None
+        return ent, scale, sk.key_tiles_empty(B, Ec, DI, torch.bfloat16, DEV).zero_()
+
+    (ea, sa, ka), (eb, sb, kb) = caches(), caches()
+    vd, gd, vId, gId, bd, bId = dev(v, "bf16"), dev(g, "bf16"), dev(vI, "bf16"), dev(gI, "bf16"), dev(bp), dev(bpI)
+    rv, rg = (torch.zeros(B, P, D, device=DEV, dtype=torch.bfloat16) for _ in range(2))
+    rvI, rgI = (torch.zeros(B, 8, DI, device=DEV, dtype=torch.bfloat16) for _ in range(2))
+    for t in range(N):
+        pos = dev_i32([t] * B)
+        sk.csa_append(sk.Append(pos, vd[:, t].contiguous(), gd[:, t].contiguous(), rv, rg, bd, ea, sa),
+                      sk.Append(pos, vId[:, t].contiguous(), gId[:, t].contiguous(), rvI, rgI, bId, ka,
+                                layout=sk.LAYOUT_KEY_TILES), m=4, o=4)
+    sk.csa_compress(sk.Pool(vd, gd, bd, eb, sb), sk.Pool(vId, gId, bId, kb, layout=sk.LAYOUT_KEY_TILES), m=4, o=4)
+    torch.cuda.synchronize()
+    raw = (lambda x: x.view(torch.uint8)) if kv_out == "e4m3" else (lambda x: x)
+    assert torch.equal(raw(ea), raw(eb))
+    assert torch.equal(ka, kb)
+    if scaled:
+        assert torch.equal(sa, sb)
+
+
 def test_compress_appends_only_requested_entries():
     rng = np.random.default_rng(5)
     B, N, D = 2, 256, 64
