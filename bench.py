@@ -113,6 +113,46 @@ def prefill_indexer_rate(dev, sk, torch, wl, iters: int = 5):
             "frac": tf / PEAK_BF16_TFLOPS}
 
 
+def prefill_attend_rate(dev, sk, torch, wl, iters: int = 3):
+    """CSA attention of the 32K-token causal prefill: every row t attends to its
+    min(k, E_vis(t)) selected entries (spread evenly over the visible ones) plus
+    its window.  Algorithmic flops on MFMA: (Q.K^T + P.V) x 2 per (row, item,
+    head, latent dim); queries, entries and the stream are random with the
+    workload's shapes (the rate does not depend on the values)."""
+    L = wl.layers[0]
+    T, E = wl.N, wl.N // L.m
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.seed + 17)
+    bf = torch.bfloat16
+    q = (torch.randn(T, L.H, L.D, device=dev, generator=g) * 0.3).to(bf)
+    ent = torch.randn(1, E, L.D, device=dev, generator=g).to(bf)
+    stream_v = torch.randn(1, T, L.D, device=dev, generator=g).to(bf)
+    t = torch.arange(T, device=dev)
+    ev = torch.clamp(torch.div(t - L.W, L.m, rounding_mode="floor"), min=0).clamp(max=E)
+    kk = torch.clamp(ev, max=L.k)
+    i = torch.arange(L.k, device=dev)
+    idx = torch.div(i[None, :] * ev[:, None], kk.clamp(min=1)[:, None], rounding_mode="floor")
+    idx = torch.where(i[None, :] < kk[:, None], idx, torch.full_like(idx, -1)).to(torch.int32).contiguous()
+    items = int(kk.sum().item()) + sum(min(L.W, int(x) + 1) for x in range(T))
+    flops = 4.0 * items * L.H * L.D
+    out = torch.empty(T, L.H, L.D, device=dev)
+    rows = sk.RowSpec.causal(T)
+    tau = 1.0 / math.sqrt(L.d_h)
+    ws = sk.csa_attend(rows, q, ent, idx, stream_v, out, m=L.m, W=L.W, softmax_scale=tau)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(iters):
+        sk.csa_attend(rows, q, ent, idx, stream_v, out, m=L.m, W=L.W, softmax_scale=tau, workspace=ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": wl.name, "kernel": "attend_dma512", "rows": T, "row_items": items, "tflop": flops / 1e12,
+            "ms": ms, "achieved_tflops": tf, "peak_tflops": PEAK_BF16_TFLOPS, "frac": tf / PEAK_BF16_TFLOPS}
+
+
 def build_caches(wl, dev, sk, torch, gen, tail: int = 0):
     """Caches of every sequence for both layers (GPU-drawn streams, library compressors).
     With tail > 0 the last `tail` tokens of every stream are returned too (third
@@ -410,7 +450,8 @@ def main():
     from workloads import CSA_PREFILL_32K_BF16, PAIR_DEC_128K_BF16, gen
 
     if args.only == "prefill":
-        print(json.dumps({"prefill_indexer": prefill_indexer_rate("cuda:0", sk, torch, CSA_PREFILL_32K_BF16)}))
+        print(json.dumps({"prefill_indexer": prefill_indexer_rate("cuda:0", sk, torch, CSA_PREFILL_32K_BF16),
+                          "prefill_attend": prefill_attend_rate("cuda:0", sk, torch, CSA_PREFILL_32K_BF16)}))
         return
     if args.only == "1m":
         print(json.dumps({"decode_1m_fp8": decode_1m_rate("cuda:0", sk, torch, gen)}))
@@ -528,6 +569,8 @@ def main():
         del reps, c0, h0
         torch.cuda.empty_cache()
         rec["prefill_indexer"] = prefill_indexer_rate(dev, sk, torch, CSA_PREFILL_32K_BF16)
+        torch.cuda.empty_cache()
+        rec["prefill_attend"] = prefill_attend_rate(dev, sk, torch, CSA_PREFILL_32K_BF16)
     if not args.no_1m:
         print("[bench] 1M-context fp8 decode step", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
