@@ -393,6 +393,13 @@ __device__ __forceinline__ void block_sources_batched(const AttendParams& p, con
 // outstanding, then one barrier publishes the chunk and frees the stage of the
 // chunk before it for the next copy.
 //
+// Eight waves: wave w takes the 16 heads 16 (w % 4) .. and the latent half
+// h = w / 4 (dims 256 h .. 256 h + 255).  Q.K^T is split the same way: each
+// wave multiplies its half of the dims, the two halves of a head group meet
+// through LDS (both waves add the same two partial sums, so they hold the same
+// logits and take the same softmax), and each wave accumulates P.V for its own
+// half of the output.  Two waves per SIMD then hide each other's latencies.
+//
 // Both products read the same staged rows.  Q.K^T takes row fragments (one item,
 // eight dims per lane).  P.V needs the transpose (one dim, eight items per lane):
 // the gfx950 transposing LDS read delivers it directly.  Within each 16-lane
@@ -403,12 +410,8 @@ __device__ __forceinline__ void block_sources_batched(const AttendParams& p, con
 // runs in bf16, so P enters as the sum of two bf16 parts (a second MFMA per dim
 // tile): a single bf16 P would cost up to 2^-9 of max |v| in the output.  The
 // normaliser (and the log-sum-exp) sums the unrounded fp32 probabilities.
-//
-// With one wavefront per SIMD every vector instruction costs four cycles of
-// issue, so the loop keeps them few: all LDS addresses are a per-lane base plus
-// an immediate, and item masks are applied only to chunks that contain padding.
-__global__ __launch_bounds__(256) void attend_dma512(AttendParams p) {
-  constexpr int NW = 4, D = 512, CH = 32, KSQ = D / 32, ND = D / 16;
+__global__ __launch_bounds__(512) void attend_dma512(AttendParams p) {
+  constexpr int NW = 8, D = 512, DH = D / 2, CH = 32, KSQ = DH / 32, ND = DH / 16;
   constexpr int KRS = D + 8;                 // padded LDS row (bf16 elements): row stride = 4 banks
   constexpr int NT = NW * kWave;
   constexpr int RPW = CH / NW;               // rows copied per wave per chunk
@@ -416,6 +419,7 @@ __global__ __launch_bounds__(256) void attend_dma512(AttendParams p) {
   constexpr int STG = CH * KRS;              // stage size (bf16 elements)
   __shared__ __attribute__((aligned(16))) uint16_t stg[NSTG * STG];
   __shared__ int32_t srcs[kSegItems];
+  __shared__ f32x4 xs[NW][2][kWave];         // partial logits of each wave, exchanged per chunk
 
   // one-dimensional grid; with rows in multiples of 8 the splits of a row share
   // an XCD (blocks are dealt to the 8 XCDs in turn), so its query and index
@@ -434,19 +438,21 @@ __global__ __launch_bounds__(256) void attend_dma512(AttendParams p) {
   }
   const RowItems ri = row_items(p, r);
   const int l = lane_id(), w = wave_id();
+  const int hg = w & 3, dh = w >> 2;         // head group, latent half
   const int col = l & 15, g = l >> 4;
-  const int head = 16 * w + col;
+  const int head = 16 * hg + col;
 
   const int64_t q_begin = (int64_t)split * p.per_split;
   int64_t q_end = q_begin + p.per_split;
   q_end = q_end < ri.n_items ? q_end : ri.n_items;
 
   const gbytes gent = opaque_global(p.entries), gwin = opaque_global(p.win);
-  // query fragments: loads issued here, waited for after the first source table
+  // query fragments of this wave's latent half: loads issued here, waited for
+  // after the first source table
   bf16x8 bq[KSQ];
   {
     const gbytes gq = opaque_global(p.q);
-    const int64_t e0 = ((int64_t)r * p.H + head) * D + g * (D / 4);
+    const int64_t e0 = ((int64_t)r * p.H + head) * D + DH * dh + g * (DH / 4);
 #pragma unroll
     for (int ks = 0; ks < KSQ; ++ks) bq[ks] = bitcast<bf16x8>(gload<u32x4>(gq, (e0 + 8 * ks) * 2));
   }
@@ -466,8 +472,8 @@ __global__ __launch_bounds__(256) void attend_dma512(AttendParams p) {
   const int32_t t_slot = (int32_t)(ri.t % p.R_w);
 
   // per-lane LDS byte offsets within a stage
-  const int qk_base = (col * KRS + g * (D / 4)) * 2;                        // row col, dims g*128 ..
-  const int pv_base = ((4 * g + (col >> 2)) * KRS + 4 * (col & 3)) * 2;      // item 4g + col/4, dims 4(col%4) ..
+  const int qk_base = (col * KRS + DH * dh + g * (DH / 4)) * 2;             // row col, dims of this half
+  const int pv_base = ((4 * g + (col >> 2)) * KRS + DH * dh + 4 * (col & 3)) * 2;  // item 4g + col/4
   const lds_ptr lds0 = (lds_ptr)stg;
 
   // copies of chunk q_rel (relative to the segment's sources) into stage st
@@ -508,8 +514,9 @@ __global__ __launch_bounds__(256) void attend_dma512(AttendParams p) {
       block_barrier();                                   // chunk c visible; stage of c-1 free
       if (c + NSTG - 1 < nch) issue((int64_t)(c + NSTG - 1) * CH, (c + NSTG - 1) & (NSTG - 1));
 
-      // S^T = K Q^T in four independent accumulators (2 item tiles x even/odd
-      // k-steps); fragments read in batches of 4 k-steps, one batch ahead
+      // S^T = K Q^T over this wave's latent half, in four independent
+      // accumulators (2 item tiles x even/odd k-steps); fragments read in
+      // batches of 4 k-steps, one batch ahead
       const uint8_t* sb = reinterpret_cast<const uint8_t*>(&stg[st * STG]) + qk_base;
       f32x4 sacc[2][2];
 #pragma unroll
@@ -536,11 +543,21 @@ __global__ __launch_bounds__(256) void attend_dma512(AttendParams p) {
           for (int mt = 0; mt < 2; ++mt)
             sacc[mt][j & 1] = mfma16_bf16(fa[b & 1][mt * KB + j], bq[KB * b + j], sacc[mt][j & 1]);
       }
+      // the two halves of the head group meet: each wave adds its own and its
+      // partner's partial sums (the same two values, so the same logits)
+      f32x4 part[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) part[mt] = sacc[mt][0] + sacc[mt][1];
+      xs[w][0][l] = part[0];
+      xs[w][1][l] = part[1];
+      block_barrier();
+      const f32x4 other0 = xs[w ^ 4][0][l], other1 = xs[w ^ 4][1][l];
       float x[8];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[4 * mt + i] = (sacc[mt][0][i] + sacc[mt][1][i]) * scale2;
+      for (int i = 0; i < 4; ++i) {
+        x[i] = (part[0][i] + other0[i]) * scale2;
+        x[4 + i] = (part[1][i] + other1[i]) * scale2;
+      }
       if ((uint32_t)valid != 0xffffffffu) {                // padding in this chunk
         const uint32_t lo = (uint32_t)(valid >> (4 * g)), hi = (uint32_t)(valid >> (16 + 4 * g));
 #pragma unroll
@@ -579,7 +596,7 @@ __global__ __launch_bounds__(256) void attend_dma512(AttendParams p) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) o[nd][i] *= al[i];
       }
-      // O += P V: B fragments by transposing reads of the staged rows
+      // O += P V over this wave's latent half: B fragments by transposing reads
       const int vb = st * STG * 2 + pv_base;
 #pragma unroll
       for (int nd = 0; nd < ND; ++nd) {
@@ -598,25 +615,26 @@ __global__ __launch_bounds__(256) void attend_dma512(AttendParams p) {
   float lrow[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) lrow[i] = __shfl(l_tot, 4 * g + i, kWave);
-  const int hbase = 16 * w + 4 * g;
+  const int hbase = 16 * hg + 4 * g;
+  const int dbase = DH * dh + col;
   if (p.nsplit == 1) {
 #pragma unroll
     for (int nd = 0; nd < ND; ++nd)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float v = o[nd][i] / lrow[i];
-        const int64_t off = ((int64_t)r * p.H + hbase + i) * D + 16 * nd + col;
+        const int64_t off = ((int64_t)r * p.H + hbase + i) * D + dbase + 16 * nd;
         if (p.out_dtype == SCKV_BF16) static_cast<uint16_t*>(p.out)[off] = (uint16_t)f32_to_bf16_rne(v);
         else static_cast<float*>(p.out)[off] = v;
       }
-    if (p.lse && g == 0) p.lse[(int64_t)r * p.H + head] = (m_run + log2f(l_tot)) * 0.6931471805599453f;
+    if (p.lse && g == 0 && dh == 0) p.lse[(int64_t)r * p.H + head] = (m_run + log2f(l_tot)) * 0.6931471805599453f;
   } else {
     const int64_t sbase = ((int64_t)r * p.nsplit + split) * p.H;
 #pragma unroll
     for (int nd = 0; nd < ND; ++nd)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p.ws_o[(sbase + hbase + i) * D + 16 * nd + col] = o[nd][i];
-    if (g == 0) {
+      for (int i = 0; i < 4; ++i) p.ws_o[(sbase + hbase + i) * D + dbase + 16 * nd] = o[nd][i];
+    if (g == 0 && dh == 0) {
       p.ws_ml[(sbase + head) * 2] = m_run;
       p.ws_ml[(sbase + head) * 2 + 1] = l_tot;
     }
@@ -818,7 +836,7 @@ AttendPlan plan_attend(const sckv_attend_args& a, bool csa) {
 template <int ENT, int D>
 static void launch_mfma_d(const AttendParams& p, int H, int hgroups, dim3 grid, hipStream_t s) {
   if (ENT == SCKV_BF16 && D == 512 && H == 64) {         // dma512_path
-    hipLaunchKernelGGL(attend_dma512, dim3(grid.x * grid.y), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(attend_dma512, dim3(grid.x * grid.y), dim3(512), 0, s, p);
   } else {
     // register-staged chunks: 64 items when the latent is narrow, 32 at D = 512;
     // grid.z = head groups, each block takes H / 16 / hgroups waves of 16 heads
