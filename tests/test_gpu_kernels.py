@@ -454,6 +454,35 @@ def test_attend_causal_rows_and_determinism():
         assert_close(go[t], o, atol=2e-2, what=f"row {t}")
 
 
+@pytest.mark.parametrize("H,D,T,E_cap", [(64, 512, 3000, 32), (32, 128, 2900, 16)])
+def test_hca_attend_causal_rows(H, D, T, E_cap):
+    """HCA prefill: every position a query over all its visible 128:1 entries plus
+    its window (rows before the first entry, rows within it, a capped E_cap)."""
+    print(f"hca causal rows H={H} D={D} T={T} E_cap={E_cap}", flush=True)
+    rng = np.random.default_rng(H + D + T)
+    q = rng_store(rng, (T, H, D), "bf16", 0.3)
+    ent = rng_store(rng, (1, E_cap, D), "bf16").astype(np.float64)
+    v = rng_store(rng, (1, T, D), "bf16")
+    rows = sk.RowSpec.causal(T)
+    tau = 1 / math.sqrt(128 if D >= 128 else D)
+    outs = []
+    for _ in range(2):
+        out = torch.zeros(T, H, D, device=DEV, dtype=torch.float32)
+        lse = torch.zeros(T, H, device=DEV, dtype=torch.float32)
+        sk.hca_attend(rows, dev(q, "bf16"), dev(ent, "bf16"), dev(v, "bf16"), out, m=128, W=128, softmax_scale=tau,
+                      lse=lse)
+        outs.append((out, lse))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0])
+    go, gl = host(outs[0][0]), host(outs[0][1])
+    for t in [0, 1, 127, 128, 255, 256, 257, 383, 384, 1000, 2047, 2176, T - 1]:
+        ev = min(method.entries_visible(t, 128, 128), E_cap)
+        items = np.concatenate([ent[0][:ev], v[0][method.window_positions(t, 128)]])
+        o, lse_o, _ = method.attend(q[t], items, tau)
+        assert_close(go[t], o, atol=2e-2, what=f"row {t} (E_vis={ev})")
+        np.testing.assert_allclose(gl[t], lse_o, rtol=1e-5, atol=1e-5)
+
+
 def test_attend_rows_longer_than_a_segment():
     """Causal rows whose item lists (k + window) exceed one block's source segment."""
     rng = np.random.default_rng(10)
