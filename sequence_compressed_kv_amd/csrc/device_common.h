@@ -133,11 +133,13 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 // The copy is written as inline assembly on purpose: the compiler then does not
 // see an asynchronous LDS writer, so it does not make every later LDS read wait
 // for all copies in flight (which would leave nothing in flight during the
-// math).  The caller owns the waits.  lds_row must be wave-uniform.
+// math).  The caller owns the waits.  lds_row must be wave-uniform: it is
+// handed to the instruction in M0, which the compiler loads itself (the {m0}
+// operand), so it never holds a value of its own there across the copy.
 __device__ __forceinline__ void copy_to_lds16(gbytes src, void* lds_row) {
   const uint32_t dst = (uint32_t)reinterpret_cast<uintptr_t>((lds_ptr)lds_row);
   const uint64_t addr = reinterpret_cast<uint64_t>(src);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(addr), "s"(dst) : "memory", "m0");
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(addr), "{m0}"(dst) : "memory");
 }
 
 // gfx950 transposing LDS read of four 16-bit values per lane (see the P.V
