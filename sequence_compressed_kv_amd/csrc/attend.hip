@@ -791,11 +791,6 @@ __global__ __launch_bounds__(256) void attend_f32(AttendParams p, int D) {
     for (int h = threadIdx.x; h < H; h += 256) p.lse[(int64_t)r * H + h] = mrun[h] + logf(lrun[h]);
 }
 
-// the bf16, D = 512, 64-head shape runs on attend_dma512
-static bool dma512_path(const sckv_attend_args& a) {
-  return a.entry_dtype == SCKV_BF16 && a.D == 512 && a.H == 64;
-}
-
 AttendPlan plan_attend(const sckv_attend_args& a, bool csa) {
   AttendPlan pl;
   const int64_t t = a.rows.kind == SCKV_ROWS_DECODE ? a.rows.pos_max : (int64_t)a.rows.pos0 + a.rows.R - 1;
@@ -835,7 +830,7 @@ AttendPlan plan_attend(const sckv_attend_args& a, bool csa) {
 
 template <int ENT, int D>
 static void launch_mfma_d(const AttendParams& p, int H, int hgroups, dim3 grid, hipStream_t s) {
-  if (ENT == SCKV_BF16 && D == 512 && H == 64) {         // dma512_path
+  if (ENT == SCKV_BF16 && D == 512 && H == 64) {
     hipLaunchKernelGGL(attend_dma512, dim3(grid.x * grid.y), dim3(512), 0, s, p);
   } else {
     // register-staged chunks: 64 items when the latent is narrow, 32 at D = 512;
