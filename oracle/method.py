@@ -176,6 +176,24 @@ def hca_row(t: int, q, entries, stream_v, m: int, W: int, tau: float):
     return {"e_vis": e_vis, "o": o, "lse": lse, "p": p}
 
 
+# ---------------------------------------------------------------- projections of the hidden state
+def project(x, W) -> np.ndarray:
+    """A linear map of the rows of x: y = x W^T (x : [R][K], W : [N][K])."""
+    return np.asarray(x, np.float64) @ np.asarray(W, np.float64).T
+
+
+def absorb_queries(q_heads, W_UK) -> np.ndarray:
+    """Queries against the shared latent: q~_h = (W_UK^h)^T q_h for every row and
+    head (q_heads : [R][H][d_h], W_UK : [H][d_h][D] -> [R][H][D]); then
+    q~_h . c = q_h . (W_UK^h c) for every latent c (MLA absorption)."""
+    q_heads = np.asarray(q_heads, np.float64)
+    W_UK = np.asarray(W_UK, np.float64)
+    out = np.zeros((q_heads.shape[0], W_UK.shape[0], W_UK.shape[2]))
+    for h in range(W_UK.shape[0]):
+        out[:, h, :] = q_heads[:, h, :] @ W_UK[h]
+    return out
+
+
 # ---------------------------------------------------------------- heads back to the model width
 def layer_output(o_latent, W_o, W_UV=None) -> np.ndarray:
     """y = W_o . concat_h(o_h) with o_h = W_UV^h o~_h when the latent is wider than
