@@ -275,6 +275,95 @@ sckv_status csa_attend(const sckv_attend_args* a, void* workspace, size_t worksp
 sckv_status hca_attend(const sckv_attend_args* a, void* workspace, size_t workspace_bytes,
                        void* stream);
 
+/* ------------------------------------------------------------------ projections
+ * Decode rows enter and leave the attention path through dense projections of
+ * their hidden state x (the CSA decode workload definition: per-head queries,
+ * attention against the shared latent, then the output projection W_o; MLA keeps
+ * one compressed latent per token and absorbs the head projections into the
+ * queries: knightli.com DeepSeek-V4 KV-cache article, section on the successive
+ * KV-cache optimisations).  Every weight is bf16, row-major [N][K] as a linear
+ * layer stores it (y = x W^T), and every product accumulates in fp32 on the
+ * matrix cores.  The rows are few (R <= 64), so each call streams its weights
+ * from HBM once.  Every reduction length (d_model, and D or H * d_h on the output
+ * side) must be a multiple of 128.
+ *
+ * layer_queries -- the query side of one layer:
+ *   x     : [R][d_model] bf16 hidden states of the query rows
+ *   W_q   : [H * d_h][d_model]; q_h = rows h d_h .. (h+1) d_h - 1 of W_q x
+ *   W_UK  : [H][d_h][D] or NULL.  Non-NULL: q = W_UK^h^T q_h (the head queries are
+ *           kept in fp32 in the workspace and absorbed in fp32; D % 128 == 0,
+ *           D <= 4096, d_h % 16 == 0, d_h <= 256).  NULL: q = q_h, and D must equal d_h.
+ *   q     : [R][H][D] (q_dtype F32 or BF16), the attention queries
+ *   W_iq  : [H_I * D_I][d_model] or NULL; qI : [R][H_I][D_I] (q_dtype), indexer queries
+ *   W_w   : [H_I][d_model] or NULL; w : [R][H_I] fp32, indexer head weights
+ * layer_streams -- the per-token streams the compressors pool (rows may be the
+ *   newest token of each sequence, as csa_append / hca_append take them):
+ *   W_c, W_g : [D][d_model] -> v, g : [R][D]; W_cI, W_gI : [D_I][d_model] -> vI, gI :
+ *   [R][D_I] (each pair member may be NULL, then its output is not written);
+ *   outputs in out_dtype (F32 or BF16).
+ * layer_output -- back to the model width:
+ *   o     : [R][H][D] bf16 attention outputs against the latent
+ *   W_UV  : [H][d_h][D] or NULL.  Non-NULL: o_h = W_UV^h o~_h (rounded to bf16 in
+ *           the workspace; D % 128 == 0).  NULL: o_h = o~_h (D == d_h).
+ *   W_o   : [d_model][H * d_h]; y = W_o [o_1 .. o_H] : [R][d_model] (y_dtype F32 or
+ *           BF16); H * d_h % 128 == 0.
+ * The workspace size queries return 0 when no workspace is needed. */
+typedef struct {
+  const void* x;
+  const void* W_q;
+  const void* W_UK;
+  const void* W_iq;
+  const void* W_w;
+  void* q;
+  void* qI;
+  float* w;
+  int32_t R;
+  int32_t d_model;
+  int32_t H;
+  int32_t d_h;
+  int32_t D;
+  int32_t H_I;
+  int32_t D_I;
+  int32_t q_dtype;
+} sckv_query_args;
+
+typedef struct {
+  const void* x;
+  const void* W_c;
+  const void* W_g;
+  const void* W_cI;
+  const void* W_gI;
+  void* v;
+  void* g;
+  void* vI;
+  void* gI;
+  int32_t R;
+  int32_t d_model;
+  int32_t D;
+  int32_t D_I;
+  int32_t out_dtype;
+  int32_t reserved;
+} sckv_stream_args;
+
+typedef struct {
+  const void* o;
+  const void* W_UV;
+  const void* W_o;
+  void* y;
+  int32_t R;
+  int32_t d_model;
+  int32_t H;
+  int32_t d_h;
+  int32_t D;
+  int32_t y_dtype;
+} sckv_output_args;
+
+size_t layer_queries_workspace_size(const sckv_query_args* a);
+sckv_status layer_queries(const sckv_query_args* a, void* workspace, size_t workspace_bytes, void* stream);
+sckv_status layer_streams(const sckv_stream_args* a, void* stream);
+size_t layer_output_workspace_size(const sckv_output_args* a);
+sckv_status layer_output(const sckv_output_args* a, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------ misc */
 const char* sckv_last_error(void); /* thread-local text of the last non-OK status */
 int32_t sckv_abi_version(void);    /* SCKV_ABI_VERSION */

@@ -62,9 +62,30 @@ class AttendArgs(C.Structure):
                 ("softmax_scale", C.c_float), ("reserved", C.c_int32)]
 
 
+class QueryArgs(C.Structure):
+    _fields_ = [("x", C.c_void_p), ("W_q", C.c_void_p), ("W_UK", C.c_void_p), ("W_iq", C.c_void_p),
+                ("W_w", C.c_void_p), ("q", C.c_void_p), ("qI", C.c_void_p), ("w", C.c_void_p), ("R", C.c_int32),
+                ("d_model", C.c_int32), ("H", C.c_int32), ("d_h", C.c_int32), ("D", C.c_int32), ("H_I", C.c_int32),
+                ("D_I", C.c_int32), ("q_dtype", C.c_int32)]
+
+
+class StreamArgs(C.Structure):
+    _fields_ = [("x", C.c_void_p), ("W_c", C.c_void_p), ("W_g", C.c_void_p), ("W_cI", C.c_void_p),
+                ("W_gI", C.c_void_p), ("v", C.c_void_p), ("g", C.c_void_p), ("vI", C.c_void_p), ("gI", C.c_void_p),
+                ("R", C.c_int32), ("d_model", C.c_int32), ("D", C.c_int32), ("D_I", C.c_int32),
+                ("out_dtype", C.c_int32), ("reserved", C.c_int32)]
+
+
+class OutputArgs(C.Structure):
+    _fields_ = [("o", C.c_void_p), ("W_UV", C.c_void_p), ("W_o", C.c_void_p), ("y", C.c_void_p), ("R", C.c_int32),
+                ("d_model", C.c_int32), ("H", C.c_int32), ("d_h", C.c_int32), ("D", C.c_int32),
+                ("y_dtype", C.c_int32)]
+
+
 EXPORTS = ["csa_compress", "hca_compress", "csa_append", "hca_append", "csa_index_topk_workspace_size", "csa_index_topk", "csa_index_score",
            "csa_topk_select_workspace_size", "csa_topk_select", "csa_attend_workspace_size",
-           "hca_attend_workspace_size", "csa_attend", "hca_attend", "sckv_last_error", "sckv_abi_version"]
+           "hca_attend_workspace_size", "csa_attend", "hca_attend", "layer_queries_workspace_size", "layer_queries",
+           "layer_streams", "layer_output_workspace_size", "layer_output", "sckv_last_error", "sckv_abi_version"]
 
 _lib = None
 
@@ -99,8 +120,15 @@ def load() -> C.CDLL:
         getattr(L, n).restype = sz
     for n in ("csa_attend", "hca_attend"):
         getattr(L, n).argtypes = [C.POINTER(AttendArgs), P, sz, P]
+    L.layer_queries_workspace_size.argtypes = [C.POINTER(QueryArgs)]
+    L.layer_queries_workspace_size.restype = sz
+    L.layer_queries.argtypes = [C.POINTER(QueryArgs), P, sz, P]
+    L.layer_streams.argtypes = [C.POINTER(StreamArgs), P]
+    L.layer_output_workspace_size.argtypes = [C.POINTER(OutputArgs)]
+    L.layer_output_workspace_size.restype = sz
+    L.layer_output.argtypes = [C.POINTER(OutputArgs), P, sz, P]
     for n in ("csa_compress", "hca_compress", "csa_append", "hca_append", "csa_index_topk", "csa_index_score",
-              "csa_topk_select", "csa_attend", "hca_attend"):
+              "csa_topk_select", "csa_attend", "hca_attend", "layer_queries", "layer_streams", "layer_output"):
         getattr(L, n).restype = C.c_int
     L.sckv_last_error.restype = C.c_char_p
     L.sckv_abi_version.restype = C.c_int32
@@ -343,6 +371,55 @@ def hca_attend(rows: RowSpec, q, entries, win, out, *, m: int = 128, W: int = 12
     a = attend_args(rows, q, entries, win, out, m=m, W=W, softmax_scale=softmax_scale, entry_scale=entry_scale,
                     lse=lse)
     return _attend("hca_attend", a, entries.device, workspace, stream)
+
+
+# ---------------------------------------------------------------- projections
+def query_args(x, W_q, q, *, W_UK=None, W_iq=None, qI=None, W_w=None, w=None) -> QueryArgs:
+    """x [R][d_model], W_q [H*d_h][d_model], q [R][H][D]; W_UK [H][d_h][D] (absorption) or None;
+    W_iq [H_I*D_I][d_model] -> qI [R][H_I][D_I]; W_w [H_I][d_model] -> w [R][H_I] (fp32)."""
+    R, dm = int(x.shape[0]), int(x.shape[1])
+    H, D = int(q.shape[1]), int(q.shape[2])
+    d_h = int(W_q.shape[0]) // H
+    H_I = int(qI.shape[1]) if qI is not None else (int(W_w.shape[0]) if W_w is not None else 0)
+    D_I = int(qI.shape[2]) if qI is not None else (1 if W_w is not None else 0)
+    return QueryArgs(_ptr(x), _ptr(W_q), _ptr(W_UK), _ptr(W_iq), _ptr(W_w), _ptr(q), _ptr(qI), _ptr(w), R, dm, H,
+                     d_h, D, H_I, D_I, dtype_code(q))
+
+
+def layer_queries(x, W_q, q, *, W_UK=None, W_iq=None, qI=None, W_w=None, w=None, workspace=None, stream=None):
+    a = query_args(x, W_q, q, W_UK=W_UK, W_iq=W_iq, qI=qI, W_w=W_w, w=w)
+    L = load()
+    n = int(L.layer_queries_workspace_size(C.byref(a)))
+    ws = _workspace(n, x.device, workspace)
+    _check(L.layer_queries(C.byref(a), _ptr(ws), n, _stream(stream)))
+    return ws
+
+
+def layer_streams(x, *, W_c=None, v=None, W_g=None, g=None, W_cI=None, vI=None, W_gI=None, gI=None, stream=None):
+    """x [R][d_model]; each given weight [n][d_model] writes its output [R][n] (v, g: n = D; vI, gI: n = D_I)."""
+    R, dm = int(x.shape[0]), int(x.shape[1])
+    D = int((W_c if W_c is not None else W_g).shape[0]) if (W_c is not None or W_g is not None) else 0
+    D_I = int((W_cI if W_cI is not None else W_gI).shape[0]) if (W_cI is not None or W_gI is not None) else 0
+    outs = [t for t in (v, g, vI, gI) if t is not None]
+    a = StreamArgs(_ptr(x), _ptr(W_c), _ptr(W_g), _ptr(W_cI), _ptr(W_gI), _ptr(v), _ptr(g), _ptr(vI), _ptr(gI), R,
+                   dm, D, D_I, dtype_code(outs[0]) if outs else F32, 0)
+    _check(load().layer_streams(C.byref(a), _stream(stream)))
+
+
+def output_args(o, W_o, y, *, W_UV=None) -> OutputArgs:
+    """o [R][H][D] bf16, W_o [d_model][H*d_h], y [R][d_model]; W_UV [H][d_h][D] or None."""
+    R, H, D = int(o.shape[0]), int(o.shape[1]), int(o.shape[2])
+    return OutputArgs(_ptr(o), _ptr(W_UV), _ptr(W_o), _ptr(y), R, int(W_o.shape[0]), H, int(W_o.shape[1]) // H, D,
+                      dtype_code(y))
+
+
+def layer_output(o, W_o, y, *, W_UV=None, workspace=None, stream=None):
+    a = output_args(o, W_o, y, W_UV=W_UV)
+    L = load()
+    n = int(L.layer_output_workspace_size(C.byref(a)))
+    ws = _workspace(n, o.device, workspace)
+    _check(L.layer_output(C.byref(a), _ptr(ws), n, _stream(stream)))
+    return ws
 
 
 def abi_version() -> int:

@@ -23,7 +23,7 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          # keep hipcc from emitting packed fp32 arithmetic
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", INCLUDE, "-I", CSRC]
-SOURCES = ["sckv_api.cpp", "compress.hip", "index.hip", "topk.hip", "attend.hip"]
+SOURCES = ["sckv_api.cpp", "compress.hip", "index.hip", "topk.hip", "attend.hip", "project.hip"]
 
 
 def _compile(src: str) -> str:

@@ -203,6 +203,96 @@ sckv_status attend_common(const sckv_attend_args* a, bool csa, void* ws, size_t 
                     csa ? "csa_attend" : "hca_attend");
 }
 
+// ---------------------------------------------------------------- projections
+bool out_dtype_ok(int32_t d) { return d == SCKV_F32 || d == SCKV_BF16; }
+
+sckv_status check_reduce_len(int64_t K, const char* name, const char* what) {
+  if (K < 128 || K % 128) return fail(SCKV_ERR_UNSUPPORTED, "%s: %s=%lld must be a positive multiple of 128", name, what,
+                                      (long long)K);
+  if (K > (1 << 20)) return fail(SCKV_ERR_UNSUPPORTED, "%s: %s=%lld exceeds 2^20", name, what, (long long)K);
+  return SCKV_OK;
+}
+
+sckv_status check_queries(const sckv_query_args* a, size_t* ws) {
+  const char* name = "layer_queries";
+  if (!a) return fail(SCKV_ERR_NULL, "%s: args is NULL", name);
+  if (!a->x || !a->W_q || !a->q) return fail(SCKV_ERR_NULL, "%s: x, W_q and q must be set", name);
+  if ((a->W_iq && !a->qI) || (a->W_w && !a->w)) return fail(SCKV_ERR_NULL, "%s: W_iq needs qI and W_w needs w", name);
+  if (a->R < 1 || a->R > 64) return fail(SCKV_ERR_SHAPE, "%s: R=%d outside [1,64]", name, a->R);
+  if (a->H < 1 || a->d_h < 1 || a->D < 1) return fail(SCKV_ERR_SHAPE, "%s: need H, d_h, D >= 1", name);
+  if ((int64_t)a->H * a->d_h > (1 << 20)) return fail(SCKV_ERR_UNSUPPORTED, "%s: H*d_h exceeds 2^20", name);
+  if ((a->W_iq || a->W_w) && (a->H_I < 1 || a->D_I < 1 || (int64_t)a->H_I * a->D_I > (1 << 20)))
+    return fail(SCKV_ERR_SHAPE, "%s: indexer needs 1 <= H_I, D_I and H_I*D_I <= 2^20", name);
+  sckv_status s = check_reduce_len(a->d_model, name, "d_model");
+  if (s != SCKV_OK) return s;
+  if (!out_dtype_ok(a->q_dtype)) return fail(SCKV_ERR_DTYPE, "%s: q_dtype %s not supported (F32, BF16)", name,
+                                             dtname(a->q_dtype));
+  if (a->W_UK) {
+    if (a->D % 128 || a->D > 4096 || a->d_h % 16 || a->d_h > 256)
+      return fail(SCKV_ERR_UNSUPPORTED,
+                  "%s: absorption needs D %% 128 == 0 (D <= 4096), d_h %% 16 == 0 and d_h <= 256 (got %d, %d)", name,
+                  a->D, a->d_h);
+  } else if (a->D != a->d_h) {
+    return fail(SCKV_ERR_SHAPE, "%s: without W_UK the latent D=%d must equal d_h=%d", name, a->D, a->d_h);
+  }
+  if (!aligned16(a->x) || !aligned16(a->W_q) || !aligned16(a->q) || (a->W_UK && !aligned16(a->W_UK)) ||
+      (a->W_iq && (!aligned16(a->W_iq) || !aligned16(a->qI))) || (a->W_w && (!aligned16(a->W_w) || !aligned16(a->w))))
+    return fail(SCKV_ERR_ALIGN, "%s: tensors must be 16-byte aligned", name);
+  *ws = a->W_UK ? (size_t)a->R * a->H * a->d_h * sizeof(float) : 0;
+  return ok();
+}
+
+sckv_status check_streams(const sckv_stream_args* a) {
+  const char* name = "layer_streams";
+  if (!a) return fail(SCKV_ERR_NULL, "%s: args is NULL", name);
+  if (!a->x) return fail(SCKV_ERR_NULL, "%s: x must be set", name);
+  if ((a->W_c && !a->v) || (a->W_g && !a->g) || (a->W_cI && !a->vI) || (a->W_gI && !a->gI))
+    return fail(SCKV_ERR_NULL, "%s: every weight given needs its output", name);
+  if (a->R < 1 || a->R > 64) return fail(SCKV_ERR_SHAPE, "%s: R=%d outside [1,64]", name, a->R);
+  if ((a->W_c || a->W_g) && (a->D < 1 || a->D > (1 << 20))) return fail(SCKV_ERR_SHAPE, "%s: D=%d", name, a->D);
+  if ((a->W_cI || a->W_gI) && (a->D_I < 1 || a->D_I > (1 << 20)))
+    return fail(SCKV_ERR_SHAPE, "%s: D_I=%d", name, a->D_I);
+  sckv_status s = check_reduce_len(a->d_model, name, "d_model");
+  if (s != SCKV_OK) return s;
+  if (!out_dtype_ok(a->out_dtype))
+    return fail(SCKV_ERR_DTYPE, "%s: out_dtype %s not supported (F32, BF16)", name, dtname(a->out_dtype));
+  const void* p[9] = {a->x, a->W_c, a->W_g, a->W_cI, a->W_gI, a->v, a->g, a->vI, a->gI};
+  for (const void* q : p)
+    if (q && !aligned16(q)) return fail(SCKV_ERR_ALIGN, "%s: tensors must be 16-byte aligned", name);
+  return ok();
+}
+
+sckv_status check_output(const sckv_output_args* a, size_t* ws) {
+  const char* name = "layer_output";
+  if (!a) return fail(SCKV_ERR_NULL, "%s: args is NULL", name);
+  if (!a->o || !a->W_o || !a->y) return fail(SCKV_ERR_NULL, "%s: o, W_o and y must be set", name);
+  if (a->R < 1 || a->R > 64) return fail(SCKV_ERR_SHAPE, "%s: R=%d outside [1,64]", name, a->R);
+  if (a->H < 1 || a->d_h < 1 || a->D < 1 || a->d_model < 1 || a->d_model > (1 << 20))
+    return fail(SCKV_ERR_SHAPE, "%s: need H, d_h, D, d_model >= 1 (d_model <= 2^20)", name);
+  sckv_status s = check_reduce_len((int64_t)a->H * a->d_h, name, "H*d_h");
+  if (s != SCKV_OK) return s;
+  if (a->W_UV) {
+    s = check_reduce_len(a->D, name, "D");
+    if (s != SCKV_OK) return s;
+  } else if (a->D != a->d_h) {
+    return fail(SCKV_ERR_SHAPE, "%s: without W_UV the latent D=%d must equal d_h=%d", name, a->D, a->d_h);
+  }
+  if (!out_dtype_ok(a->y_dtype))
+    return fail(SCKV_ERR_DTYPE, "%s: y_dtype %s not supported (F32, BF16)", name, dtname(a->y_dtype));
+  if (!aligned16(a->o) || !aligned16(a->W_o) || !aligned16(a->y) || (a->W_UV && !aligned16(a->W_UV)))
+    return fail(SCKV_ERR_ALIGN, "%s: tensors must be 16-byte aligned", name);
+  *ws = a->W_UV ? (size_t)a->R * a->H * a->d_h * sizeof(uint16_t) : 0;
+  return ok();
+}
+
+sckv_status check_ws(const char* name, size_t need, const void* ws, size_t ws_bytes) {
+  if (need && (!ws || ws_bytes < need))
+    return fail(SCKV_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", name, need,
+                ws ? ws_bytes : (size_t)0);
+  if (ws && !aligned16(ws)) return fail(SCKV_ERR_ALIGN, "%s: workspace must be 16-byte aligned", name);
+  return SCKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -321,6 +411,38 @@ sckv_status csa_attend(const sckv_attend_args* a, void* ws, size_t ws_bytes, voi
 
 sckv_status hca_attend(const sckv_attend_args* a, void* ws, size_t ws_bytes, void* stream) {
   return attend_common(a, false, ws, ws_bytes, stream);
+}
+
+size_t layer_queries_workspace_size(const sckv_query_args* a) {
+  size_t ws = 0;
+  return check_queries(a, &ws) == SCKV_OK ? ws : 0;
+}
+
+sckv_status layer_queries(const sckv_query_args* a, void* ws, size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  sckv_status s = check_queries(a, &need);
+  if (s == SCKV_OK) s = check_ws("layer_queries", need, ws, ws_bytes);
+  if (s != SCKV_OK) return s;
+  return hip_status(sckv::launch_layer_queries(*a, ws, static_cast<hipStream_t>(stream)), "layer_queries");
+}
+
+sckv_status layer_streams(const sckv_stream_args* a, void* stream) {
+  sckv_status s = check_streams(a);
+  if (s != SCKV_OK) return s;
+  return hip_status(sckv::launch_layer_streams(*a, static_cast<hipStream_t>(stream)), "layer_streams");
+}
+
+size_t layer_output_workspace_size(const sckv_output_args* a) {
+  size_t ws = 0;
+  return check_output(a, &ws) == SCKV_OK ? ws : 0;
+}
+
+sckv_status layer_output(const sckv_output_args* a, void* ws, size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  sckv_status s = check_output(a, &need);
+  if (s == SCKV_OK) s = check_ws("layer_output", need, ws, ws_bytes);
+  if (s != SCKV_OK) return s;
+  return hip_status(sckv::launch_layer_output(*a, ws, static_cast<hipStream_t>(stream)), "layer_output");
 }
 
 const char* sckv_last_error(void) { return g_err; }

@@ -61,4 +61,11 @@ AttendPlan plan_attend(const sckv_attend_args& a, bool csa);
 hipError_t launch_attend(const sckv_attend_args& a, bool csa, const AttendPlan& p, void* ws,
                          hipStream_t stream);
 
+// ---------------------------------------------------------------- projections
+// Arguments are validated; ws holds R * H * d_h fp32 (queries, when absorbed) or
+// bf16 (output heads, when W_UV is given).
+hipError_t launch_layer_queries(const sckv_query_args& a, void* ws, hipStream_t stream);
+hipError_t launch_layer_streams(const sckv_stream_args& a, hipStream_t stream);
+hipError_t launch_layer_output(const sckv_output_args& a, void* ws, hipStream_t stream);
+
 }  // namespace sckv

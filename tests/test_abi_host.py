@@ -179,3 +179,68 @@ def test_attend_csa_needs_idx_and_workspace(L):
     assert n > 0                                                          # split partials for 4 rows
     assert L.csa_attend(C.byref(a), FAKE, n - 1, None) == 6
     assert L.hca_attend_workspace_size(C.byref(att_args(rows=_lib.Rows(None, 1, 32768, 0, 0, 0, 0), B=1))) == 0
+
+
+def qargs(**kw):
+    d = dict(x=FAKE, W_q=FAKE, W_UK=FAKE, W_iq=FAKE, W_w=FAKE, q=FAKE, qI=FAKE, w=FAKE, R=32, d_model=4096, H=64,
+             d_h=128, D=512, H_I=64, D_I=128, q_dtype=1)
+    d.update(kw)
+    return _lib.QueryArgs(**d)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), 1), (dict(q=None), 1), (dict(qI=None), 1), (dict(w=None), 1), (dict(R=0), 2), (dict(R=65), 2),
+    (dict(d_model=4000), 4), (dict(d_model=0), 4), (dict(q_dtype=2), 3), (dict(D=576), 4), (dict(D=8192), 4),
+    (dict(d_h=120), 4),
+    (dict(d_h=512), 4), (dict(W_UK=None), 2), (dict(W_q=FAKE_ODD), 5), (dict(w=FAKE_ODD), 5), (dict(H=0), 2),
+])
+def test_queries_validation(L, kw, status):
+    a = qargs(**kw)
+    assert L.layer_queries(C.byref(a), FAKE, 1 << 30, None) == status, err(L)
+
+
+def test_queries_workspace(L):
+    a = qargs()
+    n = L.layer_queries_workspace_size(C.byref(a))
+    assert n == 32 * 64 * 128 * 4                                   # fp32 head queries before absorption
+    assert L.layer_queries(C.byref(a), FAKE, n - 1, None) == 6
+    assert L.layer_queries(C.byref(a), None, 0, None) == 6
+    assert L.layer_queries_workspace_size(C.byref(qargs(W_UK=None, D=128))) == 0
+    assert L.layer_queries_workspace_size(C.byref(qargs(R=0))) == 0
+
+
+def sargs(**kw):
+    d = dict(x=FAKE, W_c=FAKE, W_g=FAKE, W_cI=FAKE, W_gI=FAKE, v=FAKE, g=FAKE, vI=FAKE, gI=FAKE, R=32, d_model=4096,
+             D=512, D_I=128, out_dtype=1, reserved=0)
+    d.update(kw)
+    return _lib.StreamArgs(**d)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), 1), (dict(v=None), 1), (dict(gI=None), 1), (dict(R=65), 2), (dict(D=0), 2),
+    (dict(D_I=0), 2), (dict(d_model=100), 4), (dict(out_dtype=2), 3), (dict(vI=FAKE_ODD), 5),
+])
+def test_streams_validation(L, kw, status):
+    assert L.layer_streams(C.byref(sargs(**kw)), None) == status, err(L)
+
+
+def oargs(**kw):
+    d = dict(o=FAKE, W_UV=FAKE, W_o=FAKE, y=FAKE, R=32, d_model=4096, H=64, d_h=128, D=512, y_dtype=1)
+    d.update(kw)
+    return _lib.OutputArgs(**d)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(o=None), 1), (dict(W_o=None), 1), (dict(y=None), 1), (dict(R=0), 2), (dict(d_model=0), 2),
+    (dict(H=1, d_h=64), 4), (dict(D=192), 4), (dict(W_UV=None), 2), (dict(y_dtype=2), 3), (dict(y=FAKE_ODD), 5),
+])
+def test_output_validation(L, kw, status):
+    assert L.layer_output(C.byref(oargs(**kw)), FAKE, 1 << 30, None) == status, err(L)
+
+
+def test_output_workspace(L):
+    a = oargs()
+    n = L.layer_output_workspace_size(C.byref(a))
+    assert n == 32 * 64 * 128 * 2                                   # bf16 heads o_h = W_UV^h o~_h
+    assert L.layer_output(C.byref(a), FAKE, n - 1, None) == 6
+    assert L.layer_output_workspace_size(C.byref(oargs(W_UV=None, D=128))) == 0

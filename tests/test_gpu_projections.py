@@ -1,0 +1,238 @@
+"""GPU parity of the decode projections (layer_queries, layer_streams,
+layer_output) against oracle.method.project / absorb_queries / layer_output.
+
+Hidden states, weights and attention outputs are bf16 on both sides; the oracle
+runs on the same values in fp64.  Error bounds, element by element:
+  * a sum of K products of bf16 values (each exact in fp32) accumulated in fp32
+    in any order errs by at most K u sum_k |x_k w_k|; u is taken as 2^-23 (twice
+    fp32's unit roundoff) so that the bound holds whatever rounding the matrix
+    cores apply inside one instruction;
+  * a product fed by an inexact operand adds sum_k |w_k| err_k;
+  * a bf16 rounding (to nearest even) adds at most 2^-8 of the magnitude.
+Intermediate results the library keeps in its workspace (the fp32 head queries
+before absorption, the bf16 heads o_h = W_UV^h o~_h) are checked against the
+oracle's own intermediate values with the same bounds."""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import method
+from tests.gpu_util import DEV, host
+from workloads import configs, gen
+
+pytestmark = pytest.mark.gpu
+
+sk = pytest.importorskip("sequence_compressed_kv_amd")
+
+U32 = 2.0 ** -23
+U16 = 2.0 ** -8
+
+
+def setup_module(module):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sk.load()
+
+
+def bf16(a):
+    """float32 values rounded to bf16 (float32 array holding the exact values)."""
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16).float().numpy()
+
+
+def up(a, dtype=torch.bfloat16):
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(DEV).to(dtype).contiguous()
+
+
+@functools.lru_cache(maxsize=None)
+def weights(name: str, li: int):
+    wl = configs.BY_NAME[name]
+    return {k: bf16(v) for k, v in gen.layer_weights(wl, li).items() if k != "bpos" and k != "bposI"}
+
+
+def hidden_rows(R: int, d_model: int, seed: int):
+    """Decode rows: N(0, 1) hidden states with every 7th row scaled by 8 (heavy tokens)."""
+    x = np.random.default_rng(seed).standard_normal((R, d_model)).astype(np.float32)
+    x[::7] *= 8.0
+    return bf16(x)
+
+
+def dot_bound(x, W, K=None):
+    """fp32 accumulation bound of x @ W.T (x [R][K], W [N][K])."""
+    K = x.shape[1] if K is None else K
+    return K * U32 * (np.abs(x) @ np.abs(W).T)
+
+
+def check(g, o, bound, rounded: bool, what: str):
+    g = np.asarray(g, np.float64)
+    o = np.asarray(o, np.float64)
+    lim = bound + (U16 * (np.abs(o) + bound) if rounded else 0.0)
+    err = np.abs(g - o)
+    bad = err > lim
+    print(f"{what}: max err {err.max():.3e}, max err/limit {np.max(err / np.maximum(lim, 1e-300)):.3f}", flush=True)
+    assert not bad.any(), f"{what}: {int(bad.sum())} of {bad.size} outside the bound, first at " \
+                          f"{np.argwhere(bad)[0].tolist()}: {g[bad][0]!r} vs {o[bad][0]!r} (limit {lim[bad][0]:.3e})"
+
+
+# ---------------------------------------------------------------- queries
+QUERY_CASES = [
+    # workload, layer, R, q dtype
+    ("pair_decode_128k_bf16", 0, 32, "bf16"),
+    ("pair_decode_128k_bf16", 0, 1, "f32"),
+    ("pair_decode_128k_bf16", 0, 64, "bf16"),
+    ("pair_decode_128k_bf16", 0, 17, "f32"),
+    ("pair_decode_1m_fp8", 1, 1, "bf16"),
+    ("csa_decode_4k_f32", 0, 1, "f32"),
+    ("csa_decode_4k_f32", 0, 50, "bf16"),
+    ("hca_decode_64k_bf16", 0, 4, "bf16"),
+]
+
+
+@pytest.mark.parametrize("name,li,R,qd", QUERY_CASES)
+def test_layer_queries_parity(name, li, R, qd):
+    print(f"layer_queries {name} layer {li} R={R} q={qd}", flush=True)
+    wl = configs.BY_NAME[name]
+    L = wl.layers[li]
+    w = weights(name, li)
+    x = hidden_rows(R, wl.d_model, 11 + R)
+    tq = torch.float32 if qd == "f32" else torch.bfloat16
+    q = torch.full((R, L.H, L.D), float("nan"), device=DEV, dtype=tq)
+    csa = L.kind == "csa"
+    qI = torch.full((R, L.H_I, L.D_I), float("nan"), device=DEV, dtype=tq) if csa else None
+    hw = torch.full((R, L.H_I), float("nan"), device=DEV) if csa else None
+    ws = sk.layer_queries(up(x), up(w["W_q"]), q, W_UK=up(w["W_UK"]) if L.absorbed else None,
+                          W_iq=up(w["W_iq"]) if csa else None, qI=qI, W_w=up(w["W_w"]) if csa else None, w=hw)
+    torch.cuda.synchronize()
+    rounded = qd == "bf16"
+    qh = method.project(x, w["W_q"]).reshape(R, L.H, L.d_h)
+    bqh = dot_bound(x, w["W_q"]).reshape(R, L.H, L.d_h)
+    if L.absorbed:
+        # the fp32 head queries the library keeps before absorbing them
+        qh_gpu = ws[:R * L.H * L.d_h * 4].view(torch.float32).view(R, L.H, L.d_h)
+        check(host(qh_gpu), qh, bqh, False, "q_heads")
+        q_ora = method.absorb_queries(qh, w["W_UK"])
+        WUK = np.abs(w["W_UK"])                                          # [H][d_h][D]
+        bq = np.empty_like(q_ora)
+        for h in range(L.H):
+            carried = bqh[:, h, :] @ WUK[h]
+            fresh = L.d_h * U32 * ((np.abs(qh[:, h, :]) + bqh[:, h, :]) @ WUK[h])
+            bq[:, h, :] = carried + fresh
+        check(host(q), q_ora, bq, rounded, "q (absorbed)")
+    else:
+        check(host(q), qh, bqh, rounded, "q")
+    if csa:
+        check(host(qI), method.project(x, w["W_iq"]).reshape(R, L.H_I, L.D_I),
+              dot_bound(x, w["W_iq"]).reshape(R, L.H_I, L.D_I), rounded, "qI")
+        check(host(hw), method.project(x, w["W_w"]), dot_bound(x, w["W_w"]), False, "w")
+
+
+# ---------------------------------------------------------------- streams
+STREAM_CASES = [
+    ("pair_decode_128k_bf16", 0, 32, "bf16"),
+    ("pair_decode_128k_bf16", 1, 32, "f32"),
+    ("pair_decode_128k_bf16", 0, 3, "f32"),
+    ("csa_decode_4k_f32", 0, 1, "f32"),
+    ("hca_decode_64k_bf16", 0, 4, "bf16"),
+]
+
+
+@pytest.mark.parametrize("name,li,R,od", STREAM_CASES)
+def test_layer_streams_parity(name, li, R, od):
+    print(f"layer_streams {name} layer {li} R={R} out={od}", flush=True)
+    wl = configs.BY_NAME[name]
+    L = wl.layers[li]
+    w = weights(name, li)
+    x = hidden_rows(R, wl.d_model, 31 + R)
+    td = torch.float32 if od == "f32" else torch.bfloat16
+    outs = {"v": ("W_c", L.D), "g": ("W_g", L.D)}
+    if L.kind == "csa":
+        outs.update({"vI": ("W_cI", L.D_I), "gI": ("W_gI", L.D_I)})
+    t = {k: torch.full((R, n), float("nan"), device=DEV, dtype=td) for k, (_, n) in outs.items()}
+    kw = {}
+    for k, (wn, _) in outs.items():
+        kw[wn] = up(w[wn])
+        kw[k] = t[k]
+    sk.layer_streams(up(x), **kw)
+    torch.cuda.synchronize()
+    for k, (wn, _) in outs.items():
+        check(host(t[k]), method.project(x, w[wn]), dot_bound(x, w[wn]), od == "bf16", k)
+
+
+def test_layer_streams_partial():
+    """Only the indexer pair: the other outputs stay untouched."""
+    wl = configs.PAIR_DEC_128K_BF16
+    w = weights(wl.name, 0)
+    x = hidden_rows(5, wl.d_model, 77)
+    vI = torch.zeros(5, 128, device=DEV)
+    gI = torch.zeros(5, 128, device=DEV)
+    sk.layer_streams(up(x), W_cI=up(w["W_cI"]), vI=vI, W_gI=up(w["W_gI"]), gI=gI)
+    torch.cuda.synchronize()
+    check(host(vI), method.project(x, w["W_cI"]), dot_bound(x, w["W_cI"]), False, "vI")
+    check(host(gI), method.project(x, w["W_gI"]), dot_bound(x, w["W_gI"]), False, "gI")
+
+
+# ---------------------------------------------------------------- output
+def head_outputs(o, W_UV):
+    """o_h = W_UV^h o~_h for every row and head, by the oracle's projection."""
+    return np.stack([method.project(o[:, h, :], W_UV[h]) for h in range(W_UV.shape[0])], axis=1)
+
+
+OUTPUT_CASES = [
+    ("pair_decode_128k_bf16", 1, 32, "f32"),
+    ("pair_decode_128k_bf16", 0, 32, "bf16"),
+    ("pair_decode_128k_bf16", 1, 5, "bf16"),
+    ("pair_decode_1m_fp8", 0, 1, "bf16"),
+    ("hca_decode_64k_bf16", 0, 4, "f32"),
+    ("csa_decode_4k_f32", 0, 1, "f32"),
+    ("csa_decode_4k_f32", 0, 64, "bf16"),
+]
+
+
+@pytest.mark.parametrize("name,li,R,yd", OUTPUT_CASES)
+def test_layer_output_parity(name, li, R, yd):
+    print(f"layer_output {name} layer {li} R={R} y={yd}", flush=True)
+    wl = configs.BY_NAME[name]
+    L = wl.layers[li]
+    w = weights(name, li)
+    # attention outputs against the latent: convex mixes of latents, |o| ~ 1
+    o = bf16(np.random.default_rng(51 + R).standard_normal((R, L.H, L.D)).astype(np.float32) * 0.5)
+    td = torch.float32 if yd == "f32" else torch.bfloat16
+    y = torch.full((R, wl.d_model), float("nan"), device=DEV, dtype=td)
+    ws = sk.layer_output(up(o), up(w["W_o"]), y, W_UV=up(w["W_UV"]) if L.absorbed else None)
+    torch.cuda.synchronize()
+    HD = L.H * L.d_h
+    Wo = w["W_o"]
+    if L.absorbed:
+        heads = head_outputs(o, w["W_UV"])                              # o_h = W_UV^h o~_h (fp64)
+        b1 = L.D * U32 * np.einsum("hkd,rhd->rhk", np.abs(w["W_UV"]), np.abs(o))
+        e1 = b1 + U16 * (np.abs(heads) + b1)                            # rounded to bf16 in the workspace
+        heads_gpu = host(ws[:R * HD * 2].view(torch.bfloat16).view(R, L.H, L.d_h))
+        check(heads_gpu, heads, b1, True, "heads")
+        hflat, eflat = heads.reshape(R, HD), e1.reshape(R, HD)
+        bound = eflat @ np.abs(Wo).T + HD * U32 * ((np.abs(hflat) + eflat) @ np.abs(Wo).T)
+    else:
+        hflat = o.reshape(R, HD)
+        bound = dot_bound(hflat, Wo)
+    y_ora = np.stack([method.layer_output(o[r], Wo, w["W_UV"] if L.absorbed else None) for r in range(R)])
+    check(host(y), y_ora, bound, yd == "bf16", "y")
+
+
+def test_layer_output_consecutive_calls_reuse_workspace():
+    """Two calls in a row through one caller-owned workspace, the second smaller."""
+    wl = configs.PAIR_DEC_128K_BF16
+    L = wl.layers[1]
+    w = weights(wl.name, 1)
+    Wo, WUV = up(w["W_o"]), up(w["W_UV"])
+    ws = torch.empty(64 * L.H * L.d_h * 2, dtype=torch.uint8, device=DEV)
+    for R in (40, 9):
+        o = bf16(np.random.default_rng(R).standard_normal((R, L.H, L.D)).astype(np.float32) * 0.5)
+        y = torch.full((R, wl.d_model), float("nan"), device=DEV)
+        sk.layer_output(up(o), Wo, y, W_UV=WUV, workspace=ws)
+        torch.cuda.synchronize()
+        heads = head_outputs(o, w["W_UV"])
+        y_ora = np.stack([method.layer_output(o[r], w["W_o"], w["W_UV"]) for r in range(R)])
+        b1 = L.D * U32 * np.einsum("hkd,rhd->rhk", np.abs(w["W_UV"]), np.abs(o))
+        e1 = (b1 + U16 * (np.abs(heads) + b1)).reshape(R, -1)
+        bound = e1 @ np.abs(w["W_o"]).T + L.H * L.d_h * U32 * ((np.abs(heads).reshape(R, -1) + e1) @ np.abs(w["W_o"]).T)
+        check(host(y), y_ora, bound, False, f"y R={R}")
