@@ -292,7 +292,7 @@ sckv_status hca_attend(const sckv_attend_args* a, void* workspace, size_t worksp
  *   W_q   : [H * d_h][d_model]; q_h = rows h d_h .. (h+1) d_h - 1 of W_q x
  *   W_UK  : [H][d_h][D] or NULL.  Non-NULL: q = W_UK^h^T q_h (the head queries are
  *           kept in fp32 in the workspace and absorbed in fp32; D % 128 == 0,
- *           D <= 4096, d_h % 16 == 0, d_h <= 256).  NULL: q = q_h, and D must equal d_h.
+ *           D <= 4096, d_h in {64, 128, 256}).  NULL: q = q_h, and D must equal d_h.
  *   q     : [R][H][D] (q_dtype F32 or BF16), the attention queries
  *   W_iq  : [H_I * D_I][d_model] or NULL; qI : [R][H_I][D_I] (q_dtype), indexer queries
  *   W_w   : [H_I][d_model] or NULL; w : [R][H_I] fp32, indexer head weights
@@ -301,13 +301,19 @@ sckv_status hca_attend(const sckv_attend_args* a, void* workspace, size_t worksp
  *   W_c, W_g : [D][d_model] -> v, g : [R][D]; W_cI, W_gI : [D_I][d_model] -> vI, gI :
  *   [R][D_I] (each pair member may be NULL, then its output is not written);
  *   outputs in out_dtype (F32 or BF16).
+ * layer_inputs -- layer_queries and layer_streams of the same rows (one x, R and
+ *   d_model) in one launch: the decode step's new token both queries and joins
+ *   the streams.  Outputs and workspace as the two calls.
  * layer_output -- back to the model width:
  *   o     : [R][H][D] bf16 attention outputs against the latent
  *   W_UV  : [H][d_h][D] or NULL.  Non-NULL: o_h = W_UV^h o~_h (rounded to bf16 in
  *           the workspace; D % 128 == 0).  NULL: o_h = o~_h (D == d_h).
  *   W_o   : [d_model][H * d_h]; y = W_o [o_1 .. o_H] : [R][d_model] (y_dtype F32 or
  *           BF16); H * d_h % 128 == 0.
- * The workspace size queries return 0 when no workspace is needed. */
+ * Workspaces hold the fp32 head queries before absorption, the bf16 heads o_h, and
+ * the fp32 partial sums of launches that cut the reduction across blocks (small
+ * products); the size queries return 0 when none is needed (or the arguments are
+ * invalid). */
 typedef struct {
   const void* x;
   const void* W_q;
@@ -360,7 +366,11 @@ typedef struct {
 
 size_t layer_queries_workspace_size(const sckv_query_args* a);
 sckv_status layer_queries(const sckv_query_args* a, void* workspace, size_t workspace_bytes, void* stream);
-sckv_status layer_streams(const sckv_stream_args* a, void* stream);
+size_t layer_streams_workspace_size(const sckv_stream_args* a);
+sckv_status layer_streams(const sckv_stream_args* a, void* workspace, size_t workspace_bytes, void* stream);
+size_t layer_inputs_workspace_size(const sckv_query_args* q, const sckv_stream_args* s);
+sckv_status layer_inputs(const sckv_query_args* q, const sckv_stream_args* s, void* workspace, size_t workspace_bytes,
+                         void* stream);
 size_t layer_output_workspace_size(const sckv_output_args* a);
 sckv_status layer_output(const sckv_output_args* a, void* workspace, size_t workspace_bytes, void* stream);
 

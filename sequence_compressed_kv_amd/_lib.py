@@ -85,7 +85,9 @@ class OutputArgs(C.Structure):
 EXPORTS = ["csa_compress", "hca_compress", "csa_append", "hca_append", "csa_index_topk_workspace_size", "csa_index_topk", "csa_index_score",
            "csa_topk_select_workspace_size", "csa_topk_select", "csa_attend_workspace_size",
            "hca_attend_workspace_size", "csa_attend", "hca_attend", "layer_queries_workspace_size", "layer_queries",
-           "layer_streams", "layer_output_workspace_size", "layer_output", "sckv_last_error", "sckv_abi_version"]
+           "layer_streams_workspace_size", "layer_streams", "layer_inputs_workspace_size", "layer_inputs",
+           "layer_output_workspace_size", "layer_output",
+           "sckv_last_error", "sckv_abi_version"]
 
 _lib = None
 
@@ -123,12 +125,17 @@ def load() -> C.CDLL:
     L.layer_queries_workspace_size.argtypes = [C.POINTER(QueryArgs)]
     L.layer_queries_workspace_size.restype = sz
     L.layer_queries.argtypes = [C.POINTER(QueryArgs), P, sz, P]
-    L.layer_streams.argtypes = [C.POINTER(StreamArgs), P]
+    L.layer_streams_workspace_size.argtypes = [C.POINTER(StreamArgs)]
+    L.layer_streams_workspace_size.restype = sz
+    L.layer_streams.argtypes = [C.POINTER(StreamArgs), P, sz, P]
+    L.layer_inputs_workspace_size.argtypes = [C.POINTER(QueryArgs), C.POINTER(StreamArgs)]
+    L.layer_inputs_workspace_size.restype = sz
+    L.layer_inputs.argtypes = [C.POINTER(QueryArgs), C.POINTER(StreamArgs), P, sz, P]
     L.layer_output_workspace_size.argtypes = [C.POINTER(OutputArgs)]
     L.layer_output_workspace_size.restype = sz
     L.layer_output.argtypes = [C.POINTER(OutputArgs), P, sz, P]
     for n in ("csa_compress", "hca_compress", "csa_append", "hca_append", "csa_index_topk", "csa_index_score",
-              "csa_topk_select", "csa_attend", "hca_attend", "layer_queries", "layer_streams", "layer_output"):
+              "csa_topk_select", "csa_attend", "hca_attend", "layer_queries", "layer_streams", "layer_inputs", "layer_output"):
         getattr(L, n).restype = C.c_int
     L.sckv_last_error.restype = C.c_char_p
     L.sckv_abi_version.restype = C.c_int32
@@ -395,15 +402,36 @@ def layer_queries(x, W_q, q, *, W_UK=None, W_iq=None, qI=None, W_w=None, w=None,
     return ws
 
 
-def layer_streams(x, *, W_c=None, v=None, W_g=None, g=None, W_cI=None, vI=None, W_gI=None, gI=None, stream=None):
-    """x [R][d_model]; each given weight [n][d_model] writes its output [R][n] (v, g: n = D; vI, gI: n = D_I)."""
+def stream_args(x, *, W_c=None, v=None, W_g=None, g=None, W_cI=None, vI=None, W_gI=None, gI=None) -> StreamArgs:
     R, dm = int(x.shape[0]), int(x.shape[1])
     D = int((W_c if W_c is not None else W_g).shape[0]) if (W_c is not None or W_g is not None) else 0
     D_I = int((W_cI if W_cI is not None else W_gI).shape[0]) if (W_cI is not None or W_gI is not None) else 0
     outs = [t for t in (v, g, vI, gI) if t is not None]
-    a = StreamArgs(_ptr(x), _ptr(W_c), _ptr(W_g), _ptr(W_cI), _ptr(W_gI), _ptr(v), _ptr(g), _ptr(vI), _ptr(gI), R,
-                   dm, D, D_I, dtype_code(outs[0]) if outs else F32, 0)
-    _check(load().layer_streams(C.byref(a), _stream(stream)))
+    return StreamArgs(_ptr(x), _ptr(W_c), _ptr(W_g), _ptr(W_cI), _ptr(W_gI), _ptr(v), _ptr(g), _ptr(vI), _ptr(gI), R,
+                      dm, D, D_I, dtype_code(outs[0]) if outs else F32, 0)
+
+
+def layer_inputs(x, W_q, q, *, W_UK=None, W_iq=None, qI=None, W_w=None, w=None, W_c=None, v=None, W_g=None, g=None,
+                 W_cI=None, vI=None, W_gI=None, gI=None, workspace=None, stream=None):
+    """layer_queries and layer_streams of the same rows x in one launch."""
+    a = query_args(x, W_q, q, W_UK=W_UK, W_iq=W_iq, qI=qI, W_w=W_w, w=w)
+    b = stream_args(x, W_c=W_c, v=v, W_g=W_g, g=g, W_cI=W_cI, vI=vI, W_gI=W_gI, gI=gI)
+    L = load()
+    n = int(L.layer_inputs_workspace_size(C.byref(a), C.byref(b)))
+    ws = _workspace(n, x.device, workspace)
+    _check(L.layer_inputs(C.byref(a), C.byref(b), _ptr(ws), n, _stream(stream)))
+    return ws
+
+
+def layer_streams(x, *, W_c=None, v=None, W_g=None, g=None, W_cI=None, vI=None, W_gI=None, gI=None, workspace=None,
+                  stream=None):
+    """x [R][d_model]; each given weight [n][d_model] writes its output [R][n] (v, g: n = D; vI, gI: n = D_I)."""
+    a = stream_args(x, W_c=W_c, v=v, W_g=W_g, g=g, W_cI=W_cI, vI=vI, W_gI=W_gI, gI=gI)
+    L = load()
+    n = int(L.layer_streams_workspace_size(C.byref(a)))
+    ws = _workspace(n, x.device, workspace)
+    _check(L.layer_streams(C.byref(a), _ptr(ws), n, _stream(stream)))
+    return ws
 
 
 def output_args(o, W_o, y, *, W_UV=None) -> OutputArgs:

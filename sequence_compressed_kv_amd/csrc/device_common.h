@@ -81,6 +81,11 @@ __device__ __forceinline__ f32x4 mfma16_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
 __device__ __forceinline__ f32x4 mfma16_f16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
+// 16x16x4 fp32: A lane l holds row l%16, B lane l column l%16, each the K element
+// l/16; D as for 16x16x32.
+__device__ __forceinline__ f32x4 mfma16_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
 // 32x32x16: A lane l holds row l%32, B column l%32, 8 K elements of K-group l/32;
 // D lane l holds column l%32, rows 8*(i/4) + 4*(l/32) + i%4 for register i.
 __device__ __forceinline__ f32x16 mfma32_bf16(bf16x8 a, bf16x8 b, f32x16 c) {

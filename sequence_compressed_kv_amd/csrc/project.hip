@@ -18,43 +18,55 @@
 
 namespace sckv {
 
-// One product of a grouped launch: y = x W^T over N columns, tiles of the launch
-// numbered from tile0.  Batch item b (blockIdx.y) adds b * w_bs to W and b * y_bs to y.
+// One product of a grouped launch: y = x W^T over N columns.  Its blocks are
+// numbered from blk0: tiles of 16 NT columns times `splits` equal parts of K.  A
+// product with several parts writes fp32 partial sums [splits][nbatch][R][N] at
+// part_off (floats) of the launch's partial buffer; its results are elements
+// e0 .. e0 + nbatch R N - 1 of the sum kernel.  Batch item b (blockIdx.y) adds
+// b * w_bs to W and b * y_bs to y.
 struct LinearSeg {
   const uint16_t* W;  // [N][K]
   void* y;            // row r, column n at y + r * y_rs + n
   int64_t w_bs, y_bs, y_rs;
-  int N, tile0, out;  // out: SCKV_F32 or SCKV_BF16
-  int pad;
+  int64_t part_off, e0;
+  int N, blk0, splits, out;  // out: SCKV_F32 or SCKV_BF16
 };
 
-constexpr int kMaxSegs = 4;
+constexpr int kMaxSegs = 8;
 
 struct LinearParams {
   const uint16_t* x;  // batch item b, row r at x + b * x_bs + r * x_rs (K contiguous)
   int64_t x_bs, x_rs;
   LinearSeg seg[kMaxSegs];
-  int nseg, R, K, pad;
+  float* part;
+  int nseg, R, K, nbatch;
 };
 
-// Up to 16 MT rows against 16 NT columns per block; the block's NW = blockDim / 64
-// waves split K evenly and walk their share U k-steps of 32 at a time, the loads
-// of the next U steps issued before the products of the current ones.  The
-// waves' partial sums meet in LDS (dynamic, NW * MT * NT * 1 KiB) and are added
-// in wave order.  Eight tiles per wave (MT * NT == 8) allow at most 8 waves.
+__device__ __forceinline__ void store_out(const LinearSeg& sg, int64_t off, float v) {
+  if (sg.out == SCKV_BF16) static_cast<uint16_t*>(sg.y)[off] = (uint16_t)f32_to_bf16_rne(v);
+  else static_cast<float*>(sg.y)[off] = v;
+}
+
+// Up to 16 MT rows against 16 NT columns per block, over one part of K.  The
+// block's NW = blockDim / 64 waves split that part evenly and walk their share U
+// k-steps of 32 at a time, the loads of the next U steps issued before the
+// products of the current ones.  The waves' partial sums meet in LDS (dynamic,
+// NW * MT * NT KiB) and are added in wave order.
 template <int MT, int NT, int U>
-__global__ __launch_bounds__(MT * NT >= 8 ? 512 : 1024) void linear_rows(LinearParams p) {
+__global__ __launch_bounds__(MT * NT >= 8 ? 256 : 512) void linear_rows(LinearParams p) {
   extern __shared__ f32x4 red[];
   const int NW = blockDim.x / kWave;
-  int s = 0;
+  int si = 0;
 #pragma unroll
   for (int i = 1; i < kMaxSegs; ++i)
-    if (i < p.nseg && (int)blockIdx.x >= p.seg[i].tile0) s = i;
-  const LinearSeg& sg = p.seg[s];
+    if (i < p.nseg && (int)blockIdx.x >= p.seg[i].blk0) si = i;
+  const LinearSeg& sg = p.seg[si];
+  const int j = (int)blockIdx.x - sg.blk0, ntile = (sg.N + 16 * NT - 1) / (16 * NT);
+  const int tile = j % ntile, part = j / ntile;
   const int64_t b = blockIdx.y;
-  const int N = sg.N, n0 = ((int)blockIdx.x - sg.tile0) * 16 * NT;
+  const int N = sg.N, n0 = tile * 16 * NT;
   const int l = lane_id(), w = wave_id(), c = l & 15, g = l >> 4;
-  const int KW = p.K / NW, k0 = w * KW;
+  const int KS = p.K / sg.splits, KW = KS / NW, k0 = part * KS + w * KW;
   const gbytes xb = opaque_global(p.x + b * p.x_bs), wb = opaque_global(sg.W + b * sg.w_bs);
   int64_t xr[MT], wr[NT];
 #pragma unroll
@@ -106,9 +118,10 @@ __global__ __launch_bounds__(MT * NT >= 8 ? 512 : 1024) void linear_rows(LinearP
 #pragma unroll
   for (int i = 0; i < T; ++i) red[(w * T + i) * kWave + l] = acc[i / NT][i % NT];
   __syncthreads();
+  const bool split = sg.splits > 1;
   for (int i = w; i < T; i += NW) {
     f32x4 v = red[i * kWave + l];
-    for (int j = 1; j < NW; ++j) v += red[(j * T + i) * kWave + l];
+    for (int jw = 1; jw < NW; ++jw) v += red[(jw * T + i) * kWave + l];
     const int mt = i / NT, nt = i % NT;
     const int n = n0 + 16 * nt + c;
     if (n >= N) continue;
@@ -116,19 +129,98 @@ __global__ __launch_bounds__(MT * NT >= 8 ? 512 : 1024) void linear_rows(LinearP
     for (int e = 0; e < 4; ++e) {
       const int row = 16 * mt + 4 * g + e;
       if (row >= p.R) continue;
-      const int64_t off = b * sg.y_bs + (int64_t)row * sg.y_rs + n;
-      if (sg.out == SCKV_BF16) static_cast<uint16_t*>(sg.y)[off] = (uint16_t)f32_to_bf16_rne(v[e]);
-      else static_cast<float*>(sg.y)[off] = v[e];
+      if (split)
+        p.part[sg.part_off + (((int64_t)part * p.nbatch + b) * p.R + row) * N + n] = v[e];
+      else
+        store_out(sg, b * sg.y_bs + (int64_t)row * sg.y_rs + n, v[e]);
     }
   }
 }
 
+// Sum, in part order, of the partial results of the products whose K was split.
+__global__ __launch_bounds__(256) void linear_reduce(LinearParams p, int64_t total) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  int si = 0;
+#pragma unroll
+  for (int j = 1; j < kMaxSegs; ++j)
+    if (j < p.nseg && p.seg[j].splits > 1 && i >= p.seg[j].e0) si = j;
+  const LinearSeg& sg = p.seg[si];
+  const int64_t e = i - sg.e0, count = (int64_t)p.nbatch * p.R * sg.N;
+  const int n = (int)(e % sg.N);
+  const int64_t br = e / sg.N;
+  const int r = (int)(br % p.R);
+  const int64_t b = br / p.R;
+  const float* src = p.part + sg.part_off + e;
+  // the loads of 8 parts are issued before their sums (the parts sit in other
+  // XCDs' caches or in HBM: one wait instead of eight)
+  float v = 0.f;
+  for (int k0 = 0; k0 < sg.splits; k0 += 8) {
+    float t[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t[j] = k0 + j < sg.splits ? src[(k0 + j) * count] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (k0 + j < sg.splits) v = k0 + j == 0 ? t[j] : v + t[j];
+  }
+  store_out(sg, b * sg.y_bs + (int64_t)r * sg.y_rs + n, v);
+}
+
 template <int MT, int NT>
-static void launch_lr(const LinearParams& p, dim3 grid, int nw, hipStream_t s) {
-  const int kw = p.K / nw;
-  const size_t lds = (size_t)nw * MT * NT * kWave * sizeof(f32x4);
-  if (kw % 64 == 0) hipLaunchKernelGGL((linear_rows<MT, NT, 2>), grid, dim3(nw * kWave), lds, s, p);
-  else hipLaunchKernelGGL((linear_rows<MT, NT, 1>), grid, dim3(nw * kWave), lds, s, p);
+static void launch_lr(const LinearParams& p, const LinearPlan& pl, dim3 grid, hipStream_t s) {
+  const size_t lds = (size_t)pl.nw * MT * NT * kWave * sizeof(f32x4);
+  if (pl.u == 2) hipLaunchKernelGGL((linear_rows<MT, NT, 2>), grid, dim3(pl.nw * kWave), lds, s, p);
+  else hipLaunchKernelGGL((linear_rows<MT, NT, 1>), grid, dim3(pl.nw * kWave), lds, s, p);
+}
+
+// One block per CU streams weights at what the CU's memory path sustains, so the
+// plan aims at blocks that fill all 256 CUs once, none doubled up:
+//  - column tiles of 64 (each x fragment serves four weight fragments); tiles of
+//    32 when that alone reaches 256 blocks and 64 would not;
+//  - with fewer blocks than that, every product's K is cut into equal parts;
+//  - with enough, a product much smaller than the launch is cut into 16 parts, so
+//    that its blocks are short wherever they land.
+LinearPlan plan_linear(int R, int K, const int* N, int np, int nbatch) {
+  LinearPlan pl;
+  pl.np = np;
+  pl.mt = R <= 16 ? 1 : (R <= 32 ? 2 : 4);
+  auto count_tiles = [&](int nt) {
+    int64_t t = 0;
+    for (int i = 0; i < np; ++i) t += (N[i] + 16 * nt - 1) / (16 * nt);
+    return t * nbatch;
+  };
+  pl.nt = (count_tiles(4) < 256 && count_tiles(2) >= 256) ? 2 : 4;
+  pl.nw = pl.mt * pl.nt >= 8 ? 4 : 8;
+  if (K % (pl.nw * 32)) pl.nw = 4;
+  const int64_t tiles = count_tiles(pl.nt);
+  auto fits = [&](int s) { return K % s == 0 && (K / s) % (pl.nw * 32) == 0; };
+  int uniform = 1;
+  if (tiles < 256)
+    while (tiles * uniform < 256 && fits(2 * uniform)) uniform *= 2;
+  int64_t blocks = 0, part = 0, elems = 0;
+  bool u2 = pl.mt * pl.nt < 16;
+  for (int i = 0; i < np; ++i) {
+    const int64_t ti = (N[i] + 16 * pl.nt - 1) / (16 * pl.nt);
+    int s = uniform;
+    if (tiles >= 256 && ti * nbatch * 16 <= tiles)  // keep two k-steps per wave trip
+      while (s < 16 && fits(2 * s) && (K / (2 * s) / pl.nw) % 64 == 0) s *= 2;
+    pl.splits[i] = s;
+    pl.blk0[i] = (int)blocks;
+    blocks += ti * s;
+    if (s > 1) {
+      const int64_t count = (int64_t)nbatch * R * N[i];
+      pl.part_off[i] = part;
+      pl.e0[i] = elems;
+      part += count * s;
+      elems += count;
+    }
+    if ((K / s / pl.nw) % 64) u2 = false;
+  }
+  pl.u = u2 ? 2 : 1;
+  pl.blocks = (int)blocks;
+  pl.reduce_elems = elems;
+  pl.part_bytes = (size_t)part * sizeof(float);
+  return pl;
 }
 
 struct Product {
@@ -138,25 +230,26 @@ struct Product {
   int N, out;
 };
 
-// Products sharing the rows x [R][K] (R <= 64, K % 128 == 0), one launch.  Small
-// launches take 16-column tiles and 16 waves per block so that the K stream is
-// cut into more, shorter pieces.
+static LinearPlan plan_products(int R, int K, const Product* pr, int np, int nbatch) {
+  int N[kMaxSegs];
+  for (int i = 0; i < np; ++i) N[i] = pr[i].N;
+  return plan_linear(R, K, N, np, nbatch);
+}
+
+// Products sharing the rows x [R][K] (R <= 64, K % 128 == 0) in one launch; `part`
+// holds the plan's partial sums when it splits K.
 static hipError_t linear(const void* x, int64_t x_bs, int64_t x_rs, int R, int K, const Product* pr, int np,
-                         int nbatch, hipStream_t s) {
-  int64_t cols32 = 0;
-  for (int i = 0; i < np; ++i) cols32 += (pr[i].N + 31) / 32;
-  const int nt = cols32 * nbatch >= 256 ? 2 : 1;
-  const int mt = R <= 16 ? 1 : (R <= 32 ? 2 : 4);
-  int nw = (nt == 2 && cols32 * nbatch >= 512) ? 8 : 16;
-  while (nw > 4 && (K % (nw * 32) != 0 || (size_t)nw * mt * nt * 1024 > 65536)) nw /= 2;
+                         int nbatch, float* part, hipStream_t s) {
+  const LinearPlan pl = plan_products(R, K, pr, np, nbatch);
   LinearParams p{};
   p.x = static_cast<const uint16_t*>(x);
   p.x_bs = x_bs;
   p.x_rs = x_rs;
+  p.part = part;
   p.nseg = np;
   p.R = R;
   p.K = K;
-  int tiles = 0;
+  p.nbatch = nbatch;
   for (int i = 0; i < np; ++i) {
     LinearSeg& g = p.seg[i];
     g.W = static_cast<const uint16_t*>(pr[i].W);
@@ -166,120 +259,222 @@ static hipError_t linear(const void* x, int64_t x_bs, int64_t x_rs, int R, int K
     g.y_rs = pr[i].y_rs;
     g.N = pr[i].N;
     g.out = pr[i].out;
-    g.tile0 = tiles;
-    tiles += (pr[i].N + 16 * nt - 1) / (16 * nt);
+    g.blk0 = pl.blk0[i];
+    g.splits = pl.splits[i];
+    g.part_off = pl.part_off[i];
+    g.e0 = pl.e0[i];
   }
-  const dim3 grid((unsigned)tiles, (unsigned)nbatch);
-  if (nt == 2) {
-    if (mt == 1) launch_lr<1, 2>(p, grid, nw, s);
-    else if (mt == 2) launch_lr<2, 2>(p, grid, nw, s);
-    else launch_lr<4, 2>(p, grid, nw, s);
+  const dim3 grid((unsigned)pl.blocks, (unsigned)nbatch);
+  if (pl.nt == 2) {
+    if (pl.mt == 1) launch_lr<1, 2>(p, pl, grid, s);
+    else if (pl.mt == 2) launch_lr<2, 2>(p, pl, grid, s);
+    else launch_lr<4, 2>(p, pl, grid, s);
   } else {
-    if (mt == 1) launch_lr<1, 1>(p, grid, nw, s);
-    else if (mt == 2) launch_lr<2, 1>(p, grid, nw, s);
-    else launch_lr<4, 1>(p, grid, nw, s);
+    if (pl.mt == 1) launch_lr<1, 4>(p, pl, grid, s);
+    else if (pl.mt == 2) launch_lr<2, 4>(p, pl, grid, s);
+    else launch_lr<4, 4>(p, pl, grid, s);
   }
+  if (pl.reduce_elems)
+    hipLaunchKernelGGL(linear_reduce, dim3((unsigned)((pl.reduce_elems + 255) / 256)), dim3(256), 0, s, p,
+                       pl.reduce_elems);
   return hipGetLastError();
 }
 
-// q[r][h][d] = sum_k qh[r][h][k] W_UK[h][k][d] in fp32.  Block (head, 128 latent
-// columns, 16 rows), 4 waves taking a quarter of k each; a lane owns two adjacent
-// columns and keeps its W_UK values in registers; the rows' head queries sit in
-// LDS; the quarters are added in wave order.
-template <int OUT>
+// q[r][h][d] = sum_k qh[r][h][k] W_UK[h][k][d], fp32 products on the matrix
+// cores (16x16x4 fp32).  Block (128 latent columns, head, 16 MT rows); its 4 waves
+// take a quarter of k each (KG groups of 16) and add up in LDS in wave order.
+// A lane loads 8 adjacent columns of one W_UK row (16 bytes), which serve as the
+// B operands of 8 products whose 16 output columns are 8 apart: product e of
+// lane column c holds latent column 8 c + e.  Within a group of 16 k, step ss
+// (0..3) gives K slot g the value k = 16 q + 4 g + ss, so a lane's four A values
+// of a group are 4 adjacent head-query elements (one 16-byte load).
+template <int OUT, int MT, int KG>
 __global__ __launch_bounds__(256) void absorb_kernel(const float* __restrict__ qh, const uint16_t* __restrict__ WUK,
-                                                     void* __restrict__ q, int R, int H, int dh, int D) {
-  __shared__ float qs[16][256];
-  __shared__ float part[4][16][128];
-  const int h = blockIdx.x, c0 = blockIdx.y * 128, r0 = blockIdx.z * 16;
-  const int l = lane_id(), w = wave_id();
-  const int nr = R - r0 < 16 ? R - r0 : 16;
-  for (int i = threadIdx.x; i < 16 * dh; i += blockDim.x) {
-    const int rr = i / dh, k = i % dh;
-    qs[rr][k] = rr < nr ? qh[((int64_t)(r0 + rr) * H + h) * dh + k] : 0.f;
-  }
-  __syncthreads();
-  const int KQ = dh / 4, k0 = w * KQ;
-  const uint32_t* wp = reinterpret_cast<const uint32_t*>(WUK + ((int64_t)h * dh + k0) * D + c0) + l;
-  float acc[16][2];
+                                                     void* __restrict__ q, int R, int H, int D) {
+  constexpr int dh = 64 * KG;
+  __shared__ f32x4 red[4][8 * MT][kWave];
+  const int nb = blockIdx.x * 128, h = blockIdx.y, r0 = blockIdx.z * 16 * MT;
+  const int l = lane_id(), w = wave_id(), c = l & 15, g = l >> 4;
+  const int kw0 = w * 16 * KG;  // first k of the wave
+  const gbytes qb = opaque_global(qh), wb = opaque_global(WUK + (int64_t)h * dh * D + nb);
+  f32x4 a[KG][MT];
+  u32x4 bw[KG][4];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i][0] = acc[i][1] = 0.f;
-  for (int k = 0; k < KQ; k += 4) {
-    uint32_t wv[4];
+  for (int kg = 0; kg < KG; ++kg) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) wv[j] = wp[(int64_t)(k + j) * (D / 2)];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float wa = bf16_to_f32(wv[j] & 0xffffu), wb = bf16_to_f32(wv[j] >> 16);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float qv = qs[i][k0 + k + j];
-        acc[i][0] = fmaf(qv, wa, acc[i][0]);
-        acc[i][1] = fmaf(qv, wb, acc[i][1]);
-      }
+    for (int mt = 0; mt < MT; ++mt) {
+      int row = r0 + 16 * mt + c;
+      row = row < R ? row : R - 1;  // rows past R repeat the last (not stored)
+      a[kg][mt] = gload<f32x4>(qb, (((int64_t)row * H + h) * dh + kw0 + 16 * kg + 4 * g) * 4);
     }
-  }
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    part[w][i][2 * l] = acc[i][0];
-    part[w][i][2 * l + 1] = acc[i][1];
+    for (int ss = 0; ss < 4; ++ss)
+      bw[kg][ss] = gload<u32x4>(wb, ((int64_t)(kw0 + 16 * kg + 4 * g + ss) * D + 8 * c) * 2);
   }
+  f32x4 acc[MT][8];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[mt][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kg = 0; kg < KG; ++kg)
+#pragma unroll
+    for (int ss = 0; ss < 4; ++ss)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t word = bw[kg][ss][e >> 1];
+        const float b = bf16_to_f32((e & 1) ? word >> 16 : word & 0xffffu);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt][e] = mfma16_f32(a[kg][mt][ss], b, acc[mt][e]);
+      }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[w][mt * 8 + e][l] = acc[mt][e];
   __syncthreads();
-  for (int i = threadIdx.x; i < 16 * 128; i += blockDim.x) {
-    const int rr = i / 128, col = i % 128;
-    if (rr >= nr) break;
-    const float v = ((part[0][rr][col] + part[1][rr][col]) + part[2][rr][col]) + part[3][rr][col];
-    const int64_t off = ((int64_t)(r0 + rr) * H + h) * D + c0 + col;
-    if constexpr (OUT == SCKV_BF16) static_cast<uint16_t*>(q)[off] = (uint16_t)f32_to_bf16_rne(v);
-    else static_cast<float*>(q)[off] = v;
+  for (int t = w; t < 8 * MT; t += 4) {
+    const f32x4 v = ((red[0][t][l] + red[1][t][l]) + red[2][t][l]) + red[3][t][l];
+    const int mt = t / 8, e = t % 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = r0 + 16 * mt + 4 * g + i;
+      if (row >= R) continue;
+      const int64_t off = ((int64_t)row * H + h) * D + nb + 8 * c + e;
+      if constexpr (OUT == SCKV_BF16) static_cast<uint16_t*>(q)[off] = (uint16_t)f32_to_bf16_rne(v[i]);
+      else static_cast<float*>(q)[off] = v[i];
+    }
   }
 }
 
-hipError_t launch_layer_queries(const sckv_query_args& a, void* ws, hipStream_t s) {
+template <int OUT, int MT>
+static void launch_absorb_mt(const sckv_query_args& a, const float* qh, hipStream_t s) {
+  const dim3 grid((unsigned)(a.D / 128), (unsigned)a.H, (unsigned)((a.R + 16 * MT - 1) / (16 * MT)));
+  const uint16_t* W = static_cast<const uint16_t*>(a.W_UK);
+  if (a.d_h == 64) hipLaunchKernelGGL((absorb_kernel<OUT, MT, 1>), grid, dim3(256), 0, s, qh, W, a.q, a.R, a.H, a.D);
+  else if (a.d_h == 128) hipLaunchKernelGGL((absorb_kernel<OUT, MT, 2>), grid, dim3(256), 0, s, qh, W, a.q, a.R, a.H, a.D);
+  else hipLaunchKernelGGL((absorb_kernel<OUT, MT, 4>), grid, dim3(256), 0, s, qh, W, a.q, a.R, a.H, a.D);
+}
+
+template <int OUT>
+static void launch_absorb(const sckv_query_args& a, const float* qh, hipStream_t s) {
+  if (a.R <= 16) launch_absorb_mt<OUT, 1>(a, qh, s);
+  else launch_absorb_mt<OUT, 2>(a, qh, s);
+}
+
+static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+static int query_products(const sckv_query_args& a, void* ws, Product* pr) {
   const int HD = a.H * a.d_h;
   const bool absorb = a.W_UK != nullptr;
-  Product pr[3];
   int np = 0;
   // head queries: into the workspace (fp32) when they are absorbed, else straight to q
   pr[np++] = Product{a.W_q, absorb ? ws : a.q, 0, 0, HD, HD, absorb ? SCKV_F32 : a.q_dtype};
   if (a.W_iq) pr[np++] = Product{a.W_iq, a.qI, 0, 0, (int64_t)a.H_I * a.D_I, a.H_I * a.D_I, a.q_dtype};
   if (a.W_w) pr[np++] = Product{a.W_w, a.w, 0, 0, a.H_I, a.H_I, SCKV_F32};
-  hipError_t e = linear(a.x, 0, a.d_model, a.R, a.d_model, pr, np, 1, s);
-  if (e != hipSuccess || !absorb) return e;
-  const dim3 grid((unsigned)a.H, (unsigned)(a.D / 128), (unsigned)((a.R + 15) / 16));
-  if (a.q_dtype == SCKV_BF16)
-    hipLaunchKernelGGL(absorb_kernel<SCKV_BF16>, grid, dim3(256), 0, s, static_cast<const float*>(ws),
-                       static_cast<const uint16_t*>(a.W_UK), a.q, a.R, a.H, a.d_h, a.D);
-  else
-    hipLaunchKernelGGL(absorb_kernel<SCKV_F32>, grid, dim3(256), 0, s, static_cast<const float*>(ws),
-                       static_cast<const uint16_t*>(a.W_UK), a.q, a.R, a.H, a.d_h, a.D);
+  return np;
+}
+
+static size_t query_heads_bytes(const sckv_query_args& a) {
+  return a.W_UK ? align256((size_t)a.R * a.H * a.d_h * sizeof(float)) : 0;
+}
+
+size_t queries_workspace(const sckv_query_args& a) {
+  Product pr[3];
+  const int np = query_products(a, nullptr, pr);
+  return query_heads_bytes(a) + plan_products(a.R, a.d_model, pr, np, 1).part_bytes;
+}
+
+hipError_t launch_layer_queries(const sckv_query_args& a, void* ws, hipStream_t s) {
+  Product pr[3];
+  const int np = query_products(a, ws, pr);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + query_heads_bytes(a));
+  hipError_t e = linear(a.x, 0, a.d_model, a.R, a.d_model, pr, np, 1, part, s);
+  if (e != hipSuccess || !a.W_UK) return e;
+  if (a.q_dtype == SCKV_BF16) launch_absorb<SCKV_BF16>(a, static_cast<const float*>(ws), s);
+  else launch_absorb<SCKV_F32>(a, static_cast<const float*>(ws), s);
   return hipGetLastError();
 }
 
-hipError_t launch_layer_streams(const sckv_stream_args& a, hipStream_t s) {
+static int stream_products(const sckv_stream_args& a, Product* pr) {
   const void* W[4] = {a.W_c, a.W_g, a.W_cI, a.W_gI};
   void* out[4] = {a.v, a.g, a.vI, a.gI};
   const int N[4] = {a.D, a.D, a.D_I, a.D_I};
-  Product pr[4];
   int np = 0;
   for (int i = 0; i < 4; ++i)
     if (W[i]) pr[np++] = Product{W[i], out[i], 0, 0, N[i], N[i], a.out_dtype};
+  return np;
+}
+
+size_t streams_workspace(const sckv_stream_args& a) {
+  Product pr[4];
+  const int np = stream_products(a, pr);
+  return np ? plan_products(a.R, a.d_model, pr, np, 1).part_bytes : 0;
+}
+
+hipError_t launch_layer_streams(const sckv_stream_args& a, void* ws, hipStream_t s) {
+  Product pr[4];
+  const int np = stream_products(a, pr);
   if (np == 0) return hipSuccess;
-  return linear(a.x, 0, a.d_model, a.R, a.d_model, pr, np, 1, s);
+  return linear(a.x, 0, a.d_model, a.R, a.d_model, pr, np, 1, static_cast<float*>(ws), s);
+}
+
+// Queries and streams of the same rows in one launch.
+size_t inputs_workspace(const sckv_query_args& a, const sckv_stream_args& st) {
+  Product pr[kMaxSegs];
+  int np = query_products(a, nullptr, pr);
+  np += stream_products(st, pr + np);
+  return query_heads_bytes(a) + plan_products(a.R, a.d_model, pr, np, 1).part_bytes;
+}
+
+hipError_t launch_layer_inputs(const sckv_query_args& a, const sckv_stream_args& st, void* ws, hipStream_t s) {
+  Product pr[kMaxSegs];
+  int np = query_products(a, ws, pr);
+  np += stream_products(st, pr + np);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + query_heads_bytes(a));
+  hipError_t e = linear(a.x, 0, a.d_model, a.R, a.d_model, pr, np, 1, part, s);
+  if (e != hipSuccess || !a.W_UK) return e;
+  if (a.q_dtype == SCKV_BF16) launch_absorb<SCKV_BF16>(a, static_cast<const float*>(ws), s);
+  else launch_absorb<SCKV_F32>(a, static_cast<const float*>(ws), s);
+  return hipGetLastError();
+}
+
+// o_h = W_UV^h o~_h for every head (a batch of H products), rounded to bf16 into
+// the workspace; then y = W_o [o_1 .. o_H].
+static Product heads_product(const sckv_output_args& a, void* ws) {
+  return Product{a.W_UV, ws, (int64_t)a.d_h * a.D, a.d_h, (int64_t)a.H * a.d_h, a.d_h, SCKV_BF16};
+}
+
+static Product out_product(const sckv_output_args& a) {
+  return Product{a.W_o, a.y, 0, 0, a.d_model, a.d_model, a.y_dtype};
+}
+
+static size_t output_heads_bytes(const sckv_output_args& a) {
+  return a.W_UV ? align256((size_t)a.R * a.H * a.d_h * sizeof(uint16_t)) : 0;
+}
+
+size_t output_workspace(const sckv_output_args& a) {
+  const Product po = out_product(a);
+  size_t part = plan_products(a.R, a.H * a.d_h, &po, 1, 1).part_bytes;
+  if (a.W_UV) {
+    const Product ph = heads_product(a, nullptr);
+    const size_t p1 = plan_products(a.R, a.D, &ph, 1, a.H).part_bytes;
+    part = p1 > part ? p1 : part;
+  }
+  return output_heads_bytes(a) + part;
 }
 
 hipError_t launch_layer_output(const sckv_output_args& a, void* ws, hipStream_t s) {
   const int HD = a.H * a.d_h;
+  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + output_heads_bytes(a));
   const void* heads = a.o;
   if (a.W_UV) {
-    // o_h = W_UV^h o~_h for every head (a batch of H products), rounded to bf16
-    const Product pr{a.W_UV, ws, (int64_t)a.d_h * a.D, a.d_h, HD, a.d_h, SCKV_BF16};
-    hipError_t e = linear(a.o, a.D, (int64_t)a.H * a.D, a.R, a.D, &pr, 1, a.H, s);
+    const Product ph = heads_product(a, ws);
+    hipError_t e = linear(a.o, a.D, (int64_t)a.H * a.D, a.R, a.D, &ph, 1, a.H, part, s);
     if (e != hipSuccess) return e;
     heads = ws;
   }
-  const Product pr{a.W_o, a.y, 0, 0, a.d_model, a.d_model, a.y_dtype};
-  return linear(heads, 0, HD, a.R, HD, &pr, 1, 1, s);
+  const Product po = out_product(a);
+  return linear(heads, 0, HD, a.R, HD, &po, 1, 1, part, s);
 }
 
 }  // namespace sckv

@@ -228,21 +228,21 @@ sckv_status check_queries(const sckv_query_args* a, size_t* ws) {
   if (!out_dtype_ok(a->q_dtype)) return fail(SCKV_ERR_DTYPE, "%s: q_dtype %s not supported (F32, BF16)", name,
                                              dtname(a->q_dtype));
   if (a->W_UK) {
-    if (a->D % 128 || a->D > 4096 || a->d_h % 16 || a->d_h > 256)
+    if (a->D % 128 || a->D > 4096 || (a->d_h != 64 && a->d_h != 128 && a->d_h != 256))
       return fail(SCKV_ERR_UNSUPPORTED,
-                  "%s: absorption needs D %% 128 == 0 (D <= 4096), d_h %% 16 == 0 and d_h <= 256 (got %d, %d)", name,
-                  a->D, a->d_h);
+                  "%s: absorption needs D %% 128 == 0 (D <= 4096) and d_h in {64, 128, 256} (got %d, %d)", name, a->D,
+                  a->d_h);
   } else if (a->D != a->d_h) {
     return fail(SCKV_ERR_SHAPE, "%s: without W_UK the latent D=%d must equal d_h=%d", name, a->D, a->d_h);
   }
   if (!aligned16(a->x) || !aligned16(a->W_q) || !aligned16(a->q) || (a->W_UK && !aligned16(a->W_UK)) ||
       (a->W_iq && (!aligned16(a->W_iq) || !aligned16(a->qI))) || (a->W_w && (!aligned16(a->W_w) || !aligned16(a->w))))
     return fail(SCKV_ERR_ALIGN, "%s: tensors must be 16-byte aligned", name);
-  *ws = a->W_UK ? (size_t)a->R * a->H * a->d_h * sizeof(float) : 0;
+  *ws = sckv::queries_workspace(*a);
   return ok();
 }
 
-sckv_status check_streams(const sckv_stream_args* a) {
+sckv_status check_streams(const sckv_stream_args* a, size_t* ws) {
   const char* name = "layer_streams";
   if (!a) return fail(SCKV_ERR_NULL, "%s: args is NULL", name);
   if (!a->x) return fail(SCKV_ERR_NULL, "%s: x must be set", name);
@@ -259,6 +259,7 @@ sckv_status check_streams(const sckv_stream_args* a) {
   const void* p[9] = {a->x, a->W_c, a->W_g, a->W_cI, a->W_gI, a->v, a->g, a->vI, a->gI};
   for (const void* q : p)
     if (q && !aligned16(q)) return fail(SCKV_ERR_ALIGN, "%s: tensors must be 16-byte aligned", name);
+  *ws = sckv::streams_workspace(*a);
   return ok();
 }
 
@@ -281,7 +282,18 @@ sckv_status check_output(const sckv_output_args* a, size_t* ws) {
     return fail(SCKV_ERR_DTYPE, "%s: y_dtype %s not supported (F32, BF16)", name, dtname(a->y_dtype));
   if (!aligned16(a->o) || !aligned16(a->W_o) || !aligned16(a->y) || (a->W_UV && !aligned16(a->W_UV)))
     return fail(SCKV_ERR_ALIGN, "%s: tensors must be 16-byte aligned", name);
-  *ws = a->W_UV ? (size_t)a->R * a->H * a->d_h * sizeof(uint16_t) : 0;
+  *ws = sckv::output_workspace(*a);
+  return ok();
+}
+
+sckv_status check_inputs(const sckv_query_args* q, const sckv_stream_args* st, size_t* ws) {
+  size_t w1 = 0, w2 = 0;
+  sckv_status s = check_queries(q, &w1);
+  if (s == SCKV_OK) s = check_streams(st, &w2);
+  if (s != SCKV_OK) return s;
+  if (q->x != st->x || q->R != st->R || q->d_model != st->d_model)
+    return fail(SCKV_ERR_SHAPE, "layer_inputs: queries and streams must share x, R and d_model");
+  *ws = sckv::inputs_workspace(*q, *st);
   return ok();
 }
 
@@ -426,10 +438,31 @@ sckv_status layer_queries(const sckv_query_args* a, void* ws, size_t ws_bytes, v
   return hip_status(sckv::launch_layer_queries(*a, ws, static_cast<hipStream_t>(stream)), "layer_queries");
 }
 
-sckv_status layer_streams(const sckv_stream_args* a, void* stream) {
-  sckv_status s = check_streams(a);
+size_t layer_streams_workspace_size(const sckv_stream_args* a) {
+  size_t ws = 0;
+  return check_streams(a, &ws) == SCKV_OK ? ws : 0;
+}
+
+sckv_status layer_streams(const sckv_stream_args* a, void* ws, size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  sckv_status s = check_streams(a, &need);
+  if (s == SCKV_OK) s = check_ws("layer_streams", need, ws, ws_bytes);
   if (s != SCKV_OK) return s;
-  return hip_status(sckv::launch_layer_streams(*a, static_cast<hipStream_t>(stream)), "layer_streams");
+  return hip_status(sckv::launch_layer_streams(*a, ws, static_cast<hipStream_t>(stream)), "layer_streams");
+}
+
+size_t layer_inputs_workspace_size(const sckv_query_args* q, const sckv_stream_args* st) {
+  size_t ws = 0;
+  return check_inputs(q, st, &ws) == SCKV_OK ? ws : 0;
+}
+
+sckv_status layer_inputs(const sckv_query_args* q, const sckv_stream_args* st, void* ws, size_t ws_bytes,
+                         void* stream) {
+  size_t need = 0;
+  sckv_status s = check_inputs(q, st, &need);
+  if (s == SCKV_OK) s = check_ws("layer_inputs", need, ws, ws_bytes);
+  if (s != SCKV_OK) return s;
+  return hip_status(sckv::launch_layer_inputs(*q, *st, ws, static_cast<hipStream_t>(stream)), "layer_inputs");
 }
 
 size_t layer_output_workspace_size(const sckv_output_args* a) {

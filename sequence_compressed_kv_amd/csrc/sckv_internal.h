@@ -62,10 +62,29 @@ hipError_t launch_attend(const sckv_attend_args& a, bool csa, const AttendPlan& 
                          hipStream_t stream);
 
 // ---------------------------------------------------------------- projections
-// Arguments are validated; ws holds R * H * d_h fp32 (queries, when absorbed) or
-// bf16 (output heads, when W_UV is given).
+// Plan of one grouped launch of up to 8 products sharing rows x [R][K]: row tiles
+// of 16 mt, column tiles of 16 nt, nw waves per block; product i takes blocks
+// blk0[i] .. and cuts K in splits[i] parts, whose fp32 partial sums (at part_off[i]
+// floats of a buffer of part_bytes) a second kernel adds up.
+struct LinearPlan {
+  int np = 0, mt = 0, nt = 0, nw = 0, u = 1, blocks = 0;
+  int splits[8] = {1, 1, 1, 1, 1, 1, 1, 1};
+  int blk0[8] = {};
+  int64_t part_off[8] = {};
+  int64_t e0[8] = {};
+  int64_t reduce_elems = 0;
+  size_t part_bytes = 0;
+};
+LinearPlan plan_linear(int R, int K, const int* N, int np, int nbatch);
+// Arguments are validated.  Workspaces: the fp32 head queries before absorption
+// (or the bf16 heads o_h on the output side) and the partial sums of split launches.
+size_t queries_workspace(const sckv_query_args& a);
+size_t streams_workspace(const sckv_stream_args& a);
+size_t output_workspace(const sckv_output_args& a);
+size_t inputs_workspace(const sckv_query_args& a, const sckv_stream_args& st);
+hipError_t launch_layer_inputs(const sckv_query_args& a, const sckv_stream_args& st, void* ws, hipStream_t stream);
 hipError_t launch_layer_queries(const sckv_query_args& a, void* ws, hipStream_t stream);
-hipError_t launch_layer_streams(const sckv_stream_args& a, hipStream_t stream);
+hipError_t launch_layer_streams(const sckv_stream_args& a, void* ws, hipStream_t stream);
 hipError_t launch_layer_output(const sckv_output_args& a, void* ws, hipStream_t stream);
 
 }  // namespace sckv

@@ -202,10 +202,13 @@ def test_queries_validation(L, kw, status):
 def test_queries_workspace(L):
     a = qargs()
     n = L.layer_queries_workspace_size(C.byref(a))
-    assert n == 32 * 64 * 128 * 4                                   # fp32 head queries before absorption
+    # fp32 head queries before absorption, then the partial sums of W_w, whose
+    # single column tile is cut in 16 parts of K beside the 256 tiles of W_q and W_iq
+    assert n == 32 * 64 * 128 * 4 + 16 * 32 * 64 * 4
     assert L.layer_queries(C.byref(a), FAKE, n - 1, None) == 6
     assert L.layer_queries(C.byref(a), None, 0, None) == 6
-    assert L.layer_queries_workspace_size(C.byref(qargs(W_UK=None, D=128))) == 0
+    assert L.layer_queries_workspace_size(C.byref(qargs(W_UK=None, D=128))) == 16 * 32 * 64 * 4
+    assert L.layer_queries_workspace_size(C.byref(qargs(W_UK=None, D=128, W_w=None))) == 0
     assert L.layer_queries_workspace_size(C.byref(qargs(R=0))) == 0
 
 
@@ -221,7 +224,16 @@ def sargs(**kw):
     (dict(D_I=0), 2), (dict(d_model=100), 4), (dict(out_dtype=2), 3), (dict(vI=FAKE_ODD), 5),
 ])
 def test_streams_validation(L, kw, status):
-    assert L.layer_streams(C.byref(sargs(**kw)), None) == status, err(L)
+    assert L.layer_streams(C.byref(sargs(**kw)), FAKE, 1 << 30, None) == status, err(L)
+
+
+def test_streams_workspace(L):
+    a = sargs()
+    n = L.layer_streams_workspace_size(C.byref(a))
+    # 1280 columns make 20 tiles of 64: K is cut in 16 parts, fp32 partial sums per part
+    assert n == 16 * 32 * 1280 * 4
+    assert L.layer_streams(C.byref(a), FAKE, n - 1, None) == 6
+    assert L.layer_streams_workspace_size(C.byref(sargs(R=65))) == 0
 
 
 def oargs(**kw):
@@ -241,6 +253,21 @@ def test_output_validation(L, kw, status):
 def test_output_workspace(L):
     a = oargs()
     n = L.layer_output_workspace_size(C.byref(a))
-    assert n == 32 * 64 * 128 * 2                                   # bf16 heads o_h = W_UV^h o~_h
+    heads = 32 * 64 * 128 * 2                                       # bf16 heads o_h = W_UV^h o~_h
+    part = 4 * 32 * 4096 * 4                                        # W_o: 64 column tiles, K cut in 4 parts
+    assert n == heads + part
     assert L.layer_output(C.byref(a), FAKE, n - 1, None) == 6
-    assert L.layer_output_workspace_size(C.byref(oargs(W_UV=None, D=128))) == 0
+    assert L.layer_output_workspace_size(C.byref(oargs(W_UV=None, D=128))) == part
+
+
+def test_inputs_validation_and_workspace(L):
+    q, st = qargs(), sargs()
+    n = L.layer_inputs_workspace_size(C.byref(q), C.byref(st))
+    # fp32 head queries, then the partial sums of the products cut in 16 parts of K
+    # beside the 256 column tiles of W_q and W_iq: W_w (64 columns) and the four streams
+    assert n == 32 * 64 * 128 * 4 + 16 * 32 * (64 + 512 + 512 + 128 + 128) * 4
+    assert L.layer_inputs(C.byref(q), C.byref(st), FAKE, n - 1, None) == 6
+    assert L.layer_inputs(C.byref(q), C.byref(sargs(x=FAKE + 16)), FAKE, 1 << 30, None) == 2
+    assert L.layer_inputs(C.byref(q), C.byref(sargs(R=31)), FAKE, 1 << 30, None) == 2
+    assert L.layer_inputs(C.byref(qargs(q=None)), C.byref(st), FAKE, 1 << 30, None) == 1
+    assert L.layer_inputs(C.byref(q), C.byref(sargs(out_dtype=2)), FAKE, 1 << 30, None) == 3

@@ -12,6 +12,7 @@ runs on the same values in fp64.  Error bounds, element by element:
 Intermediate results the library keeps in its workspace (the fp32 head queries
 before absorption, the bf16 heads o_h = W_UV^h o~_h) are checked against the
 oracle's own intermediate values with the same bounds."""
+import ctypes
 import functools
 
 import numpy as np
@@ -127,6 +128,27 @@ def test_layer_queries_parity(name, li, R, qd):
         check(host(hw), method.project(x, w["W_w"]), dot_bound(x, w["W_w"]), False, "w")
 
 
+@pytest.mark.parametrize("d_h,D,H,R", [(64, 256, 8, 3), (256, 512, 4, 20), (128, 128, 16, 33)])
+def test_layer_queries_absorb_head_dims(d_h, D, H, R):
+    """Absorption for the other head widths the library takes (synthetic weights)."""
+    print(f"layer_queries absorb d_h={d_h} D={D} H={H} R={R}", flush=True)
+    rng = np.random.default_rng(d_h + D)
+    dm = 1024
+    Wq = bf16(rng.standard_normal((H * d_h, dm)).astype(np.float32) / np.sqrt(dm))
+    WUK = bf16(rng.standard_normal((H, d_h, D)).astype(np.float32) / np.sqrt(D))
+    x = hidden_rows(R, dm, 5)
+    q = torch.full((R, H, D), float("nan"), device=DEV)
+    ws = sk.layer_queries(up(x), up(Wq), q, W_UK=up(WUK))
+    torch.cuda.synchronize()
+    qh = method.project(x, Wq).reshape(R, H, d_h)
+    bqh = dot_bound(x, Wq).reshape(R, H, d_h)
+    check(host(ws[:R * H * d_h * 4].view(torch.float32).view(R, H, d_h)), qh, bqh, False, "q_heads")
+    q_ora = method.absorb_queries(qh, WUK)
+    bq = np.stack([bqh[:, h, :] @ np.abs(WUK[h]) + d_h * U32 * ((np.abs(qh[:, h, :]) + bqh[:, h, :]) @ np.abs(WUK[h]))
+                   for h in range(H)], axis=1)
+    check(host(q), q_ora, bq, False, "q (absorbed)")
+
+
 # ---------------------------------------------------------------- streams
 STREAM_CASES = [
     ("pair_decode_128k_bf16", 0, 32, "bf16"),
@@ -170,6 +192,48 @@ def test_layer_streams_partial():
     torch.cuda.synchronize()
     check(host(vI), method.project(x, w["W_cI"]), dot_bound(x, w["W_cI"]), False, "vI")
     check(host(gI), method.project(x, w["W_gI"]), dot_bound(x, w["W_gI"]), False, "gI")
+
+
+@pytest.mark.parametrize("name,li,R", [("pair_decode_128k_bf16", 0, 32), ("pair_decode_128k_bf16", 1, 32),
+                                       ("csa_decode_4k_f32", 0, 1), ("pair_decode_1m_fp8", 0, 1)])
+def test_layer_inputs_parity(name, li, R):
+    """Queries and streams of the same rows in one launch."""
+    print(f"layer_inputs {name} layer {li} R={R}", flush=True)
+    wl = configs.BY_NAME[name]
+    L = wl.layers[li]
+    w = weights(name, li)
+    x = hidden_rows(R, wl.d_model, 91 + R)
+    csa = L.kind == "csa"
+    nan = float("nan")
+    q = torch.full((R, L.H, L.D), nan, device=DEV, dtype=torch.bfloat16)
+    qI = torch.full((R, L.H_I, L.D_I), nan, device=DEV, dtype=torch.bfloat16) if csa else None
+    hw = torch.full((R, L.H_I), nan, device=DEV) if csa else None
+    st = {"v": ("W_c", L.D), "g": ("W_g", L.D)}
+    if csa:
+        st.update({"vI": ("W_cI", L.D_I), "gI": ("W_gI", L.D_I)})
+    out = {k: torch.full((R, n), nan, device=DEV, dtype=torch.bfloat16) for k, (_, n) in st.items()}
+    kw = {}
+    for k, (wn, _) in st.items():
+        kw[wn] = up(w[wn])
+        kw[k] = out[k]
+    sk.layer_inputs(up(x), up(w["W_q"]), q, W_UK=up(w["W_UK"]) if L.absorbed else None,
+                    W_iq=up(w["W_iq"]) if csa else None, qI=qI, W_w=up(w["W_w"]) if csa else None, w=hw, **kw)
+    torch.cuda.synchronize()
+    qh = method.project(x, w["W_q"]).reshape(R, L.H, L.d_h)
+    bqh = dot_bound(x, w["W_q"]).reshape(R, L.H, L.d_h)
+    if L.absorbed:
+        q_ora = method.absorb_queries(qh, w["W_UK"])
+        bq = np.stack([bqh[:, h, :] @ np.abs(w["W_UK"][h]) + L.d_h * U32 *
+                       ((np.abs(qh[:, h, :]) + bqh[:, h, :]) @ np.abs(w["W_UK"][h])) for h in range(L.H)], axis=1)
+        check(host(q), q_ora, bq, True, "q (absorbed)")
+    else:
+        check(host(q), qh, bqh, True, "q")
+    if csa:
+        check(host(qI), method.project(x, w["W_iq"]).reshape(R, L.H_I, L.D_I),
+              dot_bound(x, w["W_iq"]).reshape(R, L.H_I, L.D_I), True, "qI")
+        check(host(hw), method.project(x, w["W_w"]), dot_bound(x, w["W_w"]), False, "w")
+    for k, (wn, _) in st.items():
+        check(host(out[k]), method.project(x, w[wn]), dot_bound(x, w[wn]), True, k)
 
 
 # ---------------------------------------------------------------- output
@@ -224,7 +288,10 @@ def test_layer_output_consecutive_calls_reuse_workspace():
     L = wl.layers[1]
     w = weights(wl.name, 1)
     Wo, WUV = up(w["W_o"]), up(w["W_UV"])
-    ws = torch.empty(64 * L.H * L.d_h * 2, dtype=torch.uint8, device=DEV)
+    o40 = torch.zeros(40, L.H, L.D, device=DEV, dtype=torch.bfloat16)
+    y40 = torch.zeros(40, wl.d_model, device=DEV)
+    a = sk.output_args(o40, Wo, y40, W_UV=WUV)
+    ws = torch.empty(sk.load().layer_output_workspace_size(ctypes.byref(a)), dtype=torch.uint8, device=DEV)
     for R in (40, 9):
         o = bf16(np.random.default_rng(R).standard_normal((R, L.H, L.D)).astype(np.float32) * 0.5)
         y = torch.full((R, wl.d_model), float("nan"), device=DEV)
