@@ -42,7 +42,8 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill indexer measurement")
     ap.add_argument("--no-1m", action="store_true", help="skip the 1M-context fp8 decode measurement")
     ap.add_argument("--no-append", action="store_true", help="skip the steady-state decode-with-appends measurement")
-    ap.add_argument("--only", choices=["prefill", "1m"], default=None,
+    ap.add_argument("--no-layer", action="store_true", help="skip the whole-layer decode step (projections) measurement")
+    ap.add_argument("--only", choices=["prefill", "1m", "layer"], default=None,
                     help="run only that side measurement and print its record (for profiling its kernels)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy (reference for the HBM byte counters)")
@@ -300,6 +301,131 @@ def decode_append_rate(dev, sk, torch, wl, c, h, tails, weights, qc, qh, steps: 
             "append_bytes_per_step": by_append}
 
 
+def decode_layer_rate(dev, sk, torch, wl, c, h, weights, steps: int = 32, replays: int = 5):
+    """The whole decode step of the layer pair, hidden rows x_t in, layer outputs y out:
+    per layer layer_inputs (queries, absorbed into the latent, and the token's
+    streams in one launch), the append of the token, index + top-k (CSA), attention
+    (bf16 out) and layer_output (W_UV heads, W_o).  Both layers take the same
+    hidden rows (norms, residuals and the MLP between layers are not part of the
+    path).  Every step appends at t = N - 1, so each emits a CSA and an HCA entry.
+    Timed eagerly and as a HIP graph of `steps` steps; the projection calls are
+    also timed alone, against the bytes of the weights they stream."""
+    csa, hca = wl.layers
+    B, N, dm = wl.B, wl.N, wl.d_model
+    bf = torch.bfloat16
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.seed * 7919 + 17)
+
+    def rnd(*shape, fan_in):
+        return (torch.randn(*shape, device=dev, generator=g) / math.sqrt(fan_in)).to(bf)
+
+    wc, wh = weights
+    Wc = {"W_q": rnd(csa.H * csa.d_h, dm, fan_in=dm), "W_UK": rnd(csa.H, csa.d_h, csa.D, fan_in=csa.D),
+          "W_UV": rnd(csa.H, csa.d_h, csa.D, fan_in=csa.D), "W_o": rnd(dm, csa.H * csa.d_h, fan_in=csa.H * csa.d_h),
+          "W_iq": rnd(csa.H_I * csa.D_I, dm, fan_in=dm), "W_w": rnd(csa.H_I, dm, fan_in=dm),
+          "W_c": wc["v"].to(bf), "W_g": wc["g"].to(bf), "W_cI": wc["vI"].to(bf), "W_gI": wc["gI"].to(bf)}
+    Wh = {"W_q": rnd(hca.H * hca.d_h, dm, fan_in=dm), "W_UK": rnd(hca.H, hca.d_h, hca.D, fan_in=hca.D),
+          "W_UV": rnd(hca.H, hca.d_h, hca.D, fan_in=hca.D), "W_o": rnd(dm, hca.H * hca.d_h, fan_in=hca.H * hca.d_h),
+          "W_c": wh["v"].to(bf), "W_g": wh["g"].to(bf)}
+    wbytes = sum(t.numel() * 2 for t in Wc.values()) + sum(t.numel() * 2 for t in Wh.values())
+    x = torch.randn(B, dm, device=dev, generator=g).to(bf)
+    pos = torch.full((B,), N - 1, dtype=torch.int32, device=dev)
+    rows = sk.RowSpec.decode(pos, N - 1)
+    e = lambda *s, dt=bf: torch.zeros(*s, device=dev, dtype=dt)
+    t_c = {"q": e(B, csa.H, csa.D), "qI": e(B, csa.H_I, csa.D_I), "w": e(B, csa.H_I, dt=torch.float32),
+           "v": e(B, csa.D), "g": e(B, csa.D), "vI": e(B, csa.D_I), "gI": e(B, csa.D_I), "o": e(B, csa.H, csa.D),
+           "y": e(B, dm), "g_ring": e(B, csa.W, csa.D), "vI_ring": e(B, csa.m + csa.o, csa.D_I),
+           "gI_ring": e(B, csa.m + csa.o, csa.D_I), "idx": e(B, csa.k, dt=torch.int32)}
+    t_h = {"q": e(B, hca.H, hca.D), "v": e(B, hca.D), "g": e(B, hca.D), "o": e(B, hca.H, hca.D), "y": e(B, dm),
+           "g_ring": e(B, hca.m + hca.o, hca.D)}
+    tau = 1.0 / math.sqrt(csa.d_h)
+
+    def inputs_c(ws=None):
+        return sk.layer_inputs(x, Wc["W_q"], t_c["q"], W_UK=Wc["W_UK"], W_iq=Wc["W_iq"], qI=t_c["qI"], W_w=Wc["W_w"],
+                               w=t_c["w"], W_c=Wc["W_c"], v=t_c["v"], W_g=Wc["W_g"], g=t_c["g"], W_cI=Wc["W_cI"],
+                               vI=t_c["vI"], W_gI=Wc["W_gI"], gI=t_c["gI"], workspace=ws)
+
+    def inputs_h(ws=None):
+        return sk.layer_inputs(x, Wh["W_q"], t_h["q"], W_UK=Wh["W_UK"], W_c=Wh["W_c"], v=t_h["v"], W_g=Wh["W_g"],
+                               g=t_h["g"], workspace=ws)
+
+    def output_c(ws=None):
+        return sk.layer_output(t_c["o"], Wc["W_o"], t_c["y"], W_UV=Wc["W_UV"], workspace=ws)
+
+    def output_h(ws=None):
+        return sk.layer_output(t_h["o"], Wh["W_o"], t_h["y"], W_UV=Wh["W_UV"], workspace=ws)
+
+    ws = {"in_c": inputs_c(), "in_h": inputs_h(), "out_c": output_c(), "out_h": output_h()}
+    ws["idx"] = sk.csa_index_topk(rows, t_c["qI"], t_c["w"], c["keys"], t_c["idx"], m=csa.m, W=csa.W, k=csa.k)
+    ws["att_c"] = sk.csa_attend(rows, t_c["q"], c["entries"], t_c["idx"], c["win"], t_c["o"], m=csa.m, W=csa.W,
+                                softmax_scale=tau)
+    ws["att_h"] = sk.hca_attend(rows, t_h["q"], h["entries"], h["win"], t_h["o"], m=hca.m, W=hca.W, softmax_scale=tau)
+
+    def projections():
+        inputs_c(ws["in_c"])
+        output_c(ws["out_c"])
+        inputs_h(ws["in_h"])
+        output_h(ws["out_h"])
+
+    def step():
+        inputs_c(ws["in_c"])
+        sk.csa_append(sk.Append(pos, t_c["v"], t_c["g"], c["win"], t_c["g_ring"], wc["bpos"], c["entries"]),
+                      sk.Append(pos, t_c["vI"], t_c["gI"], t_c["vI_ring"], t_c["gI_ring"], wc["bposI"], c["keys"],
+                                layout=sk.LAYOUT_KEY_TILES), m=csa.m, o=csa.o)
+        sk.csa_index_topk(rows, t_c["qI"], t_c["w"], c["keys"], t_c["idx"], m=csa.m, W=csa.W, k=csa.k,
+                          workspace=ws["idx"])
+        sk.csa_attend(rows, t_c["q"], c["entries"], t_c["idx"], c["win"], t_c["o"], m=csa.m, W=csa.W,
+                      softmax_scale=tau, workspace=ws["att_c"])
+        output_c(ws["out_c"])
+        inputs_h(ws["in_h"])
+        sk.hca_append(sk.Append(pos, t_h["v"], t_h["g"], h["win"], t_h["g_ring"], wh["bpos"], h["entries"]),
+                      m=hca.m, o=hca.o)
+        sk.hca_attend(rows, t_h["q"], h["entries"], h["win"], t_h["o"], m=hca.m, W=hca.W, softmax_scale=tau,
+                      workspace=ws["att_h"])
+        output_h(ws["out_h"])
+
+    def run():
+        for _ in range(steps):
+            step()
+
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n, per):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n / per
+
+    run()
+    torch.cuda.synchronize()
+    ref = (t_c["y"].clone(), t_h["y"].clone())
+    finite = bool(torch.isfinite(ref[0].float()).all() and torch.isfinite(ref[1].float()).all())
+    ms_eager = timed(run, replays, steps)
+    ms_proj = timed(projections, replays * steps, 1)
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(gr, stream=cap):
+            run()
+    stream.wait_stream(cap)
+    torch.cuda.synchronize()
+    t_c["y"].zero_()
+    t_h["y"].zero_()
+    gr.replay()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(t_c["y"], ref[0]) and torch.equal(t_h["y"], ref[1]))
+    ms_graph = timed(gr.replay, replays, steps)
+    return {"workload": wl.name, "steps": steps, "ms_per_step_eager": ms_eager, "ms_per_step_graph": ms_graph,
+            "tokens_per_s_graph": B / (ms_graph * 1e-3), "graph_matches_eager": same, "outputs_finite": finite,
+            "projections_ms_eager": ms_proj, "projection_weight_bytes": wbytes,
+            "projection_weight_GBps": wbytes / (ms_proj * 1e-3) / 1e9}
+
+
 def decode_1m_rate(dev, sk, torch, gen, steps: int = 20, replicas: int = 4):
     """Decode step of the 1M-context pair (batch 1) with fp8 caches: index + top-2048,
     CSA and HCA attention, bf16 out.  Cache replicas are rotated (the pair cache is
@@ -471,6 +597,9 @@ def main():
     qc = gen.gpu_queries(wl, 0, B, dev)
     qh = gen.gpu_queries(wl, 1, B, dev)
     print(f"[bench] caches ready in {time.time() - tb:.1f} s", file=sys.stderr, flush=True)
+    if args.only == "layer":
+        print(json.dumps({"decode_layer": decode_layer_rate(dev, sk, torch, wl, c0, h0, weights)}), flush=True)
+        return
 
     pos = torch.full((B,), t, dtype=torch.int32, device=dev)
     rows = sk.RowSpec.decode(pos, t)
@@ -564,6 +693,9 @@ def main():
         print("[bench] steady-state decode with appends", file=sys.stderr, flush=True)
         rec["decode_append"] = decode_append_rate(dev, sk, torch, wl, c0, h0, tails, weights, qc, qh)
     del tails
+    if not args.no_layer:
+        print("[bench] whole decode layer step (projections in and out)", file=sys.stderr, flush=True)
+        rec["decode_layer"] = decode_layer_rate(dev, sk, torch, wl, c0, h0, weights)
     if not args.no_prefill:
         print("[bench] prefill indexer scoring (32K causal rows)", file=sys.stderr, flush=True)
         del reps, c0, h0

@@ -8,9 +8,11 @@
 // HBM streaming: lane groups of D/8 lanes own one entry, each lane 8 channels,
 // so every token row is read as one contiguous D-wide segment.  The softmax is
 // taken online with one exp per (token, channel): the larger of the running
-// maximum and the new logit sets which side is rescaled.  In decode, one token
-// per sequence is appended to small rings of recent tokens, and the entry it
-// completes (one per m tokens) is pooled by the same code.
+// maximum and the new logit sets which side is rescaled.  An entry's window is
+// pooled in 4 parts whose states are folded in order.  In decode, one token per
+// sequence is appended to small rings of recent tokens, and the entry it
+// completes (one per m tokens) is pooled with the same arithmetic, its 4 parts on
+// 4 waves.
 #include "device_common.h"
 #include "sckv_internal.h"
 
@@ -33,45 +35,105 @@ __device__ __forceinline__ void load8(const void* base, int64_t elem, float (&x)
   }
 }
 
-// Pools entry e of sequence b from tokens [i0, i1) (cut to i >= 0) and stores it.
-// This lane owns channels ch .. ch+7 of the entry; the entry's G = D/8 lanes are
-// G consecutive lanes of a G-aligned group (the e4m3 scale is reduced over them).
-// tok(i, g, v) loads token i's 8 gate logits and values of this lane's channels.
-// Lanes with active == false take part in the reduction but load and store nothing.
-template <int IN, int OUT, bool SCALED, class Tok>
-__device__ __forceinline__ void pool_and_store(Tok tok, const float* __restrict__ bpos, int64_t i0, int64_t i1,
-                                               int D, int ch, int G, bool active, int sub, int64_t b, int64_t e,
-                                               int64_t E_cap, int key_tiles, void* __restrict__ out,
-                                               float* __restrict__ out_scale) {
+// Online-softmax state of one lane's 8 channels over some tokens: running maximum
+// of the logits, sum of exp(logit - max) and the matching weighted sum of values.
+struct PoolState {
   float mx[8], l[8], acc[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) { mx[c] = -INFINITY; l[c] = 0.f; acc[c] = 0.f; }
+};
 
-  for (int64_t i = i0 < 0 ? 0 : i0; i < i1; ++i) {
-    float g[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    f32x4 bp0 = {0.f, 0.f, 0.f, 0.f}, bp1 = {0.f, 0.f, 0.f, 0.f};
-    if (active) {
-      tok(i, g, v);
-      const f32x4* bp = reinterpret_cast<const f32x4*>(bpos + (i - i0) * D + ch);
-      bp0 = bp[0];
-      bp1 = bp[1];
-    }
+// Adds tokens [ia, ib) (ia >= 0) to st in token order; the bias row of token i is
+// i - i0.  With AHEAD == 2 the loads of two tokens are issued before their
+// updates (for few waves in flight; the arithmetic is the same).  The larger of
+// the running maximum and the new logit decides which side is rescaled, so each
+// (token, channel) costs one exp.
+template <int AHEAD, class Tok>
+__device__ __forceinline__ void pool_range(Tok tok, const float* __restrict__ bpos, int64_t i0, int64_t ia,
+                                           int64_t ib, int D, int ch, bool active, PoolState& st) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) { st.mx[c] = -INFINITY; st.l[c] = 0.f; st.acc[c] = 0.f; }
+  auto update = [&](const float (&g)[8], const float (&v)[8], f32x4 bp0, f32x4 bp1) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const float a = g[c] + (c < 4 ? bp0[c] : bp1[c - 4]);
-      const float d = a - mx[c];
+      const float a = __fadd_rn(g[c], c < 4 ? bp0[c] : bp1[c - 4]);
+      const float d = __fsub_rn(a, st.mx[c]);
       const float x = expf(-fabsf(d));
       const bool up = d > 0.f;
       const float sc = up ? x : 1.f;
       const float p = up ? 1.f : x;
-      l[c] = l[c] * sc + p;
-      acc[c] = acc[c] * sc + p * v[c];
-      mx[c] = fmaxf(mx[c], a);
+      st.l[c] = fmaf(st.l[c], sc, p);
+      st.acc[c] = fmaf(st.acc[c], sc, __fmul_rn(p, v[c]));
+      st.mx[c] = fmaxf(st.mx[c], a);
     }
+  };
+  for (int64_t i = ia; i < ib; i += AHEAD) {
+    const bool two = AHEAD == 2 && i + 1 < ib;
+    float g0[8] = {}, v0[8] = {}, g1[8] = {}, v1[8] = {};
+    f32x4 b00 = {}, b01 = {}, b10 = {}, b11 = {};
+    if (active) {
+      tok(i, g0, v0);
+      const f32x4* bp = reinterpret_cast<const f32x4*>(bpos + (i - i0) * D + ch);
+      b00 = bp[0];
+      b01 = bp[1];
+      if (two) {
+        tok(i + 1, g1, v1);
+        b10 = bp[D / 4];
+        b11 = bp[D / 4 + 1];
+      }
+    }
+    update(g0, v0, b00, b01);
+    if (two) update(g1, v1, b10, b11);
   }
+}
+
+// Folds the state of a later part of the window into r (an empty part, with a
+// maximum of -inf, changes nothing).  Here and in the token update every rounding
+// is spelled out (no contraction left to the compiler), so that the bulk and the
+// decode kernels produce the same bits.
+__device__ __forceinline__ void fold_state(PoolState& r, const PoolState& q) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const bool qe = q.mx[c] == -INFINITY, re = r.mx[c] == -INFINITY;
+    const float M = fmaxf(r.mx[c], q.mx[c]);
+    const float sa = re ? 0.f : expf(__fsub_rn(r.mx[c], M));
+    const float sb = qe ? 0.f : expf(__fsub_rn(q.mx[c], M));
+    const float l = qe ? r.l[c] : (re ? q.l[c] : fmaf(r.l[c], sa, __fmul_rn(q.l[c], sb)));
+    const float acc = qe ? r.acc[c] : (re ? q.acc[c] : fmaf(r.acc[c], sa, __fmul_rn(q.acc[c], sb)));
+    r.l[c] = l;
+    r.acc[c] = acc;
+    r.mx[c] = M;
+  }
+}
+
+// A pooling window [i0, i1) of 64 tokens or more is cut into 4 parts of
+// ceil((i1 - i0) / 4) tokens; each part is pooled on its own and the parts are
+// folded in order.  The bulk compressor runs the parts one after another, the
+// decode append on four waves, with identical arithmetic.  Shorter windows are
+// pooled in one pass.
+constexpr int kParts = 4;
+
+__device__ __forceinline__ int window_parts(int64_t i0, int64_t i1) { return i1 - i0 >= 64 ? kParts : 1; }
+
+__device__ __forceinline__ void part_range(int64_t i0, int64_t i1, int q, int64_t& ia, int64_t& ib) {
+  const int np = window_parts(i0, i1);
+  const int64_t len = (i1 - i0 + np - 1) / np;
+  int64_t a = i0 + q * len, b = a + len;
+  b = b < i1 ? b : i1;
+  a = a < 0 ? 0 : a;
+  ia = a;
+  ib = b > a ? b : a;
+}
+
+// Stores entry e of sequence b from its pooled state.  This lane owns channels
+// ch .. ch+7; the entry's G = D/8 lanes are G consecutive lanes of a G-aligned
+// group (the e4m3 scale is reduced over them).  Lanes with active == false take
+// part in the reduction but store nothing.
+template <int OUT, bool SCALED>
+__device__ __forceinline__ void store_entry(const PoolState& st, int ch, int G, bool active, int sub, int64_t b,
+                                            int64_t e, int D, int64_t E_cap, int key_tiles, void* __restrict__ out,
+                                            float* __restrict__ out_scale) {
   float cv[8];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) cv[c] = acc[c] / l[c];
+  for (int c = 0; c < 8; ++c) cv[c] = st.acc[c] / st.l[c];
 
   // rows: [E_cap][D]; key tiles: [E_cap/32][D/8][32][8] (8 channels of 32 entries contiguous)
   const int64_t orow = key_tiles ? b * E_cap * D + (((e >> 5) * (D >> 3) + (ch >> 3)) * 32 + (e & 31)) * 8
@@ -109,7 +171,9 @@ __device__ __forceinline__ void pool_and_store(Tok tok, const float* __restrict_
   }
 }
 
-template <int IN, int OUT, bool SCALED>
+// MULTI: the window has 64 tokens or more (pooled in parts; chosen on the host by
+// the same rule as window_parts).
+template <int IN, int OUT, bool SCALED, bool MULTI>
 __global__ __launch_bounds__(256) void compress_kernel(
     const void* __restrict__ val, const void* __restrict__ gate, const float* __restrict__ bpos,
     void* __restrict__ out, float* __restrict__ out_scale, int64_t N, int D, int m, int o,
@@ -127,8 +191,21 @@ __global__ __launch_bounds__(256) void compress_kernel(
     load8<IN>(gate, row, g);
     load8<IN>(val, row, v);
   };
-  pool_and_store<IN, OUT, SCALED>(tok, bpos, (int64_t)m * e - o, (int64_t)m * e + m, D, ch, G, active, sub, b, e,
-                                  E_cap, key_tiles, out, out_scale);
+  const int64_t i0 = (int64_t)m * e - o, i1 = (int64_t)m * e + m;
+  PoolState r;
+  int64_t ia, ib;
+  part_range(i0, i1, 0, ia, ib);
+  pool_range<1>(tok, bpos, i0, ia, ib, D, ch, active, r);
+  if constexpr (MULTI) {
+    PoolState q;
+#pragma unroll 1
+    for (int p = 1; p < kParts; ++p) {
+      part_range(i0, i1, p, ia, ib);
+      pool_range<1>(tok, bpos, i0, ia, ib, D, ch, active, q);
+      fold_state(r, q);
+    }
+  }
+  store_entry<OUT, SCALED>(r, ch, G, active, sub, b, e, D, E_cap, key_tiles, out, out_scale);
 }
 
 // One stream of a decode append, as the kernel sees it.
@@ -145,24 +222,27 @@ struct AppendK {
   int D, P, key_tiles;
 };
 
-// Decode append: one new token per sequence (one wave per sequence; blockIdx.y
-// picks one of up to two streams that share the pool and the dtypes).  The token
-// goes into the value and gate rings at slot t mod P; when it completes entry
-// e = (t + 1) / m - 1, the entry is pooled from the rings (tokens before t) and
-// the new token, by the same code as the bulk compressor.
+// Decode append: one new token per sequence (one block of 4 waves per sequence;
+// blockIdx.y picks one of up to two streams that share the pool and the dtypes).
+// The token goes into the value and gate rings at slot t mod P; when it completes
+// entry e = (t + 1) / m - 1, the entry is pooled from the rings (tokens before t)
+// and the new token: wave q pools part q of the window (wave 0 alone for a short
+// window), and wave 0 folds the parts in order and stores the entry (the bulk
+// compressor's arithmetic, bit for bit).
 template <int IN, int OUT, bool SCALED>
-__global__ __launch_bounds__(64) void append_kernel(AppendK s0, AppendK s1, int m, int o) {
+__global__ __launch_bounds__(256) void append_kernel(AppendK s0, AppendK s1, int m, int o) {
   constexpr int ES = IN == SCKV_BF16 ? 2 : 4;
+  __shared__ PoolState parts[kParts - 1][kWave];
   const AppendK& s = blockIdx.y == 0 ? s0 : s1;
   const int64_t b = blockIdx.x;
   const int D = s.D, P = s.P;
-  const int G = D / 8, lane = lane_id();
+  const int G = D / 8, lane = lane_id(), w = wave_id();
   const bool active = lane < G;
   const int ch = active ? lane * 8 : 0;
   const int32_t t = s.pos[b];
-  if (t < 0) return;                                       // whole wave: nothing to append
+  if (t < 0) return;                                       // whole block: nothing to append
   const int64_t slot_t = t % P;
-  if (active) {
+  if (w == 0 && active) {
     const uint8_t* sv = static_cast<const uint8_t*>(s.val) + (b * D + ch) * ES;
     const uint8_t* sg = static_cast<const uint8_t*>(s.gate) + (b * D + ch) * ES;
     uint8_t* dv = static_cast<uint8_t*>(s.val_ring) + ((b * P + slot_t) * D + ch) * ES;
@@ -186,8 +266,20 @@ __global__ __launch_bounds__(64) void append_kernel(AppendK s0, AppendK s1, int 
       load8<IN>(s.val_ring, row, v);
     }
   };
-  pool_and_store<IN, OUT, SCALED>(tok, s.bpos, (int64_t)m * e - o, (int64_t)m * e + m, D, ch, G, active, lane, b, e,
-                                  s.E_cap, s.key_tiles, s.out, s.out_scale);
+  const int64_t i0 = (int64_t)m * e - o, i1 = (int64_t)m * e + m;
+  const int np = window_parts(i0, i1);                     // uniform
+  PoolState st;
+  if (w < np) {
+    int64_t ia, ib;
+    part_range(i0, i1, w, ia, ib);
+    pool_range<2>(tok, s.bpos, i0, ia, ib, D, ch, active, st);
+    if (w > 0) parts[w - 1][lane] = st;
+  }
+  __syncthreads();
+  if (w != 0) return;
+#pragma unroll 1
+  for (int p = 1; p < np; ++p) fold_state(st, parts[p - 1][lane]);
+  store_entry<OUT, SCALED>(st, ch, G, active, lane, b, e, D, s.E_cap, s.key_tiles, s.out, s.out_scale);
 }
 
 template <int IN>
@@ -197,10 +289,15 @@ static hipError_t launch_in(const sckv_pool_stream& s, int32_t B, int64_t N, int
   const int epw = kWave / G;
   const dim3 grid((unsigned)((e_count + 4 * epw - 1) / (4 * epw)), (unsigned)B);
   const dim3 block(256);
-#define SCKV_LAUNCH(OUT, SC)                                                                    \
-  hipLaunchKernelGGL((compress_kernel<IN, OUT, SC>), grid, block, 0, stream, s.val, s.gate,     \
-                     s.bpos, s.out, s.out_scale, N, s.D, m, o, e_begin, e_count, s.E_cap, G,           \
-                     s.out_layout == SCKV_LAYOUT_KEY_TILES ? 1 : 0)
+#define SCKV_LAUNCH(OUT, SC)                                                                                   \
+  if (m + o >= 64)                                                                                             \
+    hipLaunchKernelGGL((compress_kernel<IN, OUT, SC, true>), grid, block, 0, stream, s.val, s.gate, s.bpos,    \
+                       s.out, s.out_scale, N, s.D, m, o, e_begin, e_count, s.E_cap, G,                         \
+                       s.out_layout == SCKV_LAYOUT_KEY_TILES ? 1 : 0);                                         \
+  else                                                                                                         \
+    hipLaunchKernelGGL((compress_kernel<IN, OUT, SC, false>), grid, block, 0, stream, s.val, s.gate, s.bpos,   \
+                       s.out, s.out_scale, N, s.D, m, o, e_begin, e_count, s.E_cap, G,                         \
+                       s.out_layout == SCKV_LAYOUT_KEY_TILES ? 1 : 0)
   switch (s.out_dtype) {
     case SCKV_F32: SCKV_LAUNCH(SCKV_F32, false); break;
     case SCKV_BF16: SCKV_LAUNCH(SCKV_BF16, false); break;
@@ -222,7 +319,7 @@ static hipError_t launch_append_in(const AppendK& k0, const AppendK& k1, int nst
                                    int32_t B, int32_t m, int32_t o, hipStream_t stream) {
   const dim3 grid((unsigned)B, (unsigned)nstreams);
 #define SCKV_LAUNCH(OUT, SC) \
-  hipLaunchKernelGGL((append_kernel<IN, OUT, SC>), grid, dim3(64), 0, stream, k0, k1, m, o)
+  hipLaunchKernelGGL((append_kernel<IN, OUT, SC>), grid, dim3(kParts * kWave), 0, stream, k0, k1, m, o)
   switch (out_dtype) {
     case SCKV_F32: SCKV_LAUNCH(SCKV_F32, false); break;
     case SCKV_BF16: SCKV_LAUNCH(SCKV_BF16, false); break;
