@@ -283,9 +283,9 @@ sckv_status hca_attend(const sckv_attend_args* a, void* workspace, size_t worksp
  * queries: knightli.com DeepSeek-V4 KV-cache article, section on the successive
  * KV-cache optimisations).  Every weight is bf16, row-major [N][K] as a linear
  * layer stores it (y = x W^T), and every product accumulates in fp32 on the
- * matrix cores.  The rows are few (R <= 64), so each call streams its weights
- * from HBM once.  Every reduction length (d_model, and D or H * d_h on the output
- * side) must be a multiple of 128.
+ * matrix cores.  1 <= R <= 2^21 rows; up to 64 rows (decode) a call streams its
+ * weights from HBM once, more rows are taken in blocks of 64.  Every reduction
+ * length (d_model, and D or H * d_h on the output side) must be a multiple of 128.
  *
  * layer_queries -- the query side of one layer:
  *   x     : [R][d_model] bf16 hidden states of the query rows

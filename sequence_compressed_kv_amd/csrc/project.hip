@@ -33,6 +33,7 @@ struct LinearSeg {
 };
 
 constexpr int kMaxSegs = 8;
+constexpr int kGemmRows = 512;  // from this many rows on, products run as tiled GEMMs
 
 struct LinearParams {
   const uint16_t* x;  // batch item b, row r at x + b * x_bs + r * x_rs (K contiguous)
@@ -47,7 +48,8 @@ __device__ __forceinline__ void store_out(const LinearSeg& sg, int64_t off, floa
   else static_cast<float*>(sg.y)[off] = v;
 }
 
-// Up to 16 MT rows against 16 NT columns per block, over one part of K.  The
+// Rows r0 .. r0 + 16 MT - 1 (r0 = blockIdx.z * 16 MT) against 16 NT columns per
+// block, over one part of K.  The
 // block's NW = blockDim / 64 waves split that part evenly and walk their share U
 // k-steps of 32 at a time, the loads of the next U steps issued before the
 // products of the current ones.  The waves' partial sums meet in LDS (dynamic,
@@ -64,6 +66,7 @@ __global__ __launch_bounds__(MT * NT >= 8 ? 256 : 512) void linear_rows(LinearPa
   const int j = (int)blockIdx.x - sg.blk0, ntile = (sg.N + 16 * NT - 1) / (16 * NT);
   const int tile = j % ntile, part = j / ntile;
   const int64_t b = blockIdx.y;
+  const int r0 = (int)blockIdx.z * 16 * MT;  // row block
   const int N = sg.N, n0 = tile * 16 * NT;
   const int l = lane_id(), w = wave_id(), c = l & 15, g = l >> 4;
   const int KS = p.K / sg.splits, KW = KS / NW, k0 = part * KS + w * KW;
@@ -71,8 +74,8 @@ __global__ __launch_bounds__(MT * NT >= 8 ? 256 : 512) void linear_rows(LinearPa
   int64_t xr[MT], wr[NT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const int row = 16 * mt + c;
-    xr[mt] = ((int64_t)(row < p.R ? row : 0) * p.x_rs + k0 + 8 * g) * 2;   // rows past R read row 0 (not stored)
+    const int row = r0 + 16 * mt + c;
+    xr[mt] = ((int64_t)(row < p.R ? row : r0) * p.x_rs + k0 + 8 * g) * 2;  // rows past R read row r0 (not stored)
   }
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -127,7 +130,7 @@ __global__ __launch_bounds__(MT * NT >= 8 ? 256 : 512) void linear_rows(LinearPa
     if (n >= N) continue;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int row = 16 * mt + 4 * g + e;
+      const int row = r0 + 16 * mt + 4 * g + e;
       if (row >= p.R) continue;
       if (split)
         p.part[sg.part_off + (((int64_t)part * p.nbatch + b) * p.R + row) * N + n] = v[e];
@@ -166,6 +169,117 @@ __global__ __launch_bounds__(256) void linear_reduce(LinearParams p, int64_t tot
   store_out(sg, b * sg.y_bs + (int64_t)r * sg.y_rs + n, v);
 }
 
+// ---------------------------------------------------------------- many rows
+// y = x W^T for many rows (prefill): block tiles of 256 rows x 256 columns over
+// K chunks of 32.  Both operand tiles of a chunk go global -> LDS by direct
+// copies (16 bytes per lane) into 4 stages (three chunks in flight while one is
+// multiplied).  A tile row is 64 bytes = 4 chunks of 8 elements; chunk j of row r
+// sits at position j ^ ((r >> 2) & 3), so the 16 lanes of a fragment read hit 16
+// different 4-bank groups.  8 waves, each 128 rows x 64 columns: MFMA 32x32x16
+// bf16, 4 x 2 tiles of fp32 accumulators.
+struct GemmParams {
+  const uint16_t* x;  // batch item b (blockIdx.z): rows at x + b * x_bs + r * x_rs
+  int64_t x_bs, x_rs;
+  const uint16_t* W;  // [N][K] at W + b * w_bs
+  int64_t w_bs;
+  void* y;            // row r, column n at y + b * y_bs + r * y_rs + n
+  int64_t y_bs, y_rs;
+  int R, N, K, out;
+  int split;          // > 0: column n = h split + k goes to y as two bf16 parts, hi = bf16(v) at
+                      // h 2 split + k and lo = bf16(v - hi) at h 2 split + split + k
+};
+
+constexpr int kGM = 256, kGN = 256, kGK = 32, kGStg = 4;
+constexpr int kGTile = kGM * kGK * 2;  // bytes of one operand's chunk tile
+constexpr int kGCopies = 4;            // copy instructions per wave per chunk
+
+__global__ __launch_bounds__(512) void gemm_rows(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t stg[kGStg][2][kGTile];
+  const int l = lane_id(), w = wave_id();
+  const int bn = (int)blockIdx.x * kGN, bm = (int)blockIdx.y * kGM;
+  const int64_t b = blockIdx.z;
+  const gbytes xa = opaque_global(p.x + b * p.x_bs), wa = opaque_global(p.W + b * p.w_bs);
+  // copies: wave w fills tile rows 32 w .. 32 w + 31 of both operands, 16 rows per
+  // instruction; lane l writes row 32 w + 16 i + l / 4, position l % 4
+  int64_t asrc[2], bsrc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 32 * w + 16 * i + (l >> 2);
+    const int j = (l & 3) ^ ((r >> 2) & 3);
+    const int ar = bm + r < p.R ? bm + r : p.R - 1;  // rows past R repeat the last (not stored)
+    const int br = bn + r < p.N ? bn + r : p.N - 1;  // columns past N likewise
+    asrc[i] = ((int64_t)ar * p.x_rs + 8 * j) * 2;
+    bsrc[i] = ((int64_t)br * p.K + 8 * j) * 2;
+  }
+  auto issue = [&](int kc, int buf) {
+    const int64_t koff = (int64_t)kc * kGK * 2;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) copy_to_lds16(xa + asrc[i] + koff, &stg[buf][0][(32 * w + 16 * i) * 64]);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) copy_to_lds16(wa + bsrc[i] + koff, &stg[buf][1][(32 * w + 16 * i) * 64]);
+  };
+  const int wm = w & 1, wn = w >> 1, c = l & 31, g = l >> 5;
+  const int swz = (c >> 2) & 3;
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jn = 0; jn < 2; ++jn)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][jn][e] = 0.f;
+  const int nk = p.K / kGK;
+  for (int s0 = 0; s0 < kGStg - 1 && s0 < nk; ++s0) issue(s0, s0);
+  for (int kc = 0; kc < nk; ++kc) {
+    const int ahead = nk - 1 - kc < kGStg - 2 ? nk - 1 - kc : kGStg - 2;  // chunks issued after kc
+    if (ahead >= 2) wait_vm_lgkm<2 * kGCopies, 0>();
+    else if (ahead == 1) wait_vm_lgkm<kGCopies, 0>();
+    else wait_vm_lgkm<0, 0>();
+    block_barrier();  // chunk kc visible to all waves; buffer (kc - 1) % kGStg read by all
+    if (kc + kGStg - 1 < nk) issue(kc + kGStg - 1, (kc + kGStg - 1) % kGStg);
+    const uint8_t* at = stg[kc % kGStg][0];
+    const uint8_t* bt = stg[kc % kGStg][1];
+#pragma unroll
+    for (int st = 0; st < kGK / 16; ++st) {
+      const int pos = (2 * st + g) ^ swz;
+      bf16x8 af[4], bf[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        af[i] = *reinterpret_cast<const bf16x8*>(at + (wm * 128 + 32 * i + c) * 64 + pos * 16);
+#pragma unroll
+      for (int jn = 0; jn < 2; ++jn)
+        bf[jn] = *reinterpret_cast<const bf16x8*>(bt + (wn * 64 + 32 * jn + c) * 64 + pos * 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jn = 0; jn < 2; ++jn) acc[i][jn] = mfma32_bf16(af[i], bf[jn], acc[i][jn]);
+    }
+  }
+  // D lane l: column l % 32, rows 8 (e / 4) + 4 (l / 32) + e % 4
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jn = 0; jn < 2; ++jn) {
+      const int col = bn + wn * 64 + 32 * jn + c;
+      if (col >= p.N) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = bm + wm * 128 + 32 * i + 8 * (e >> 2) + 4 * g + (e & 3);
+        if (row >= p.R) continue;
+        const float v = acc[i][jn][e];
+        if (p.split) {
+          const int64_t off = b * p.y_bs + (int64_t)row * p.y_rs + (col / p.split) * 2 * p.split + col % p.split;
+          const uint32_t hi = f32_to_bf16_rne(v);
+          static_cast<uint16_t*>(p.y)[off] = (uint16_t)hi;
+          static_cast<uint16_t*>(p.y)[off + p.split] = (uint16_t)f32_to_bf16_rne(v - bf16_to_f32(hi));
+          continue;
+        }
+        const int64_t off = b * p.y_bs + (int64_t)row * p.y_rs + col;
+        if (p.out == SCKV_BF16) static_cast<uint16_t*>(p.y)[off] = (uint16_t)f32_to_bf16_rne(v);
+        else static_cast<float*>(p.y)[off] = v;
+      }
+    }
+}
+
 template <int MT, int NT>
 static void launch_lr(const LinearParams& p, const LinearPlan& pl, dim3 grid, hipStream_t s) {
   const size_t lds = (size_t)pl.nw * MT * NT * kWave * sizeof(f32x4);
@@ -183,11 +297,16 @@ static void launch_lr(const LinearParams& p, const LinearPlan& pl, dim3 grid, hi
 LinearPlan plan_linear(int R, int K, const int* N, int np, int nbatch) {
   LinearPlan pl;
   pl.np = np;
+  if (R >= kGemmRows) {  // one tiled GEMM per product, no partial sums
+    pl.gemm = true;
+    return pl;
+  }
   pl.mt = R <= 16 ? 1 : (R <= 32 ? 2 : 4);
+  pl.row_blocks = (R + 16 * pl.mt - 1) / (16 * pl.mt);
   auto count_tiles = [&](int nt) {
     int64_t t = 0;
     for (int i = 0; i < np; ++i) t += (N[i] + 16 * nt - 1) / (16 * nt);
-    return t * nbatch;
+    return t * nbatch * pl.row_blocks;
   };
   pl.nt = (count_tiles(4) < 256 && count_tiles(2) >= 256) ? 2 : 4;
   pl.nw = pl.mt * pl.nt >= 8 ? 4 : 8;
@@ -202,7 +321,7 @@ LinearPlan plan_linear(int R, int K, const int* N, int np, int nbatch) {
   for (int i = 0; i < np; ++i) {
     const int64_t ti = (N[i] + 16 * pl.nt - 1) / (16 * pl.nt);
     int s = uniform;
-    if (tiles >= 256 && ti * nbatch * 16 <= tiles)  // keep two k-steps per wave trip
+    if (tiles >= 256 && ti * nbatch * pl.row_blocks * 16 <= tiles)  // keep two k-steps per wave trip
       while (s < 16 && fits(2 * s) && (K / (2 * s) / pl.nw) % 64 == 0) s *= 2;
     pl.splits[i] = s;
     pl.blk0[i] = (int)blocks;
@@ -228,6 +347,7 @@ struct Product {
   void* y;
   int64_t w_bs, y_bs, y_rs;
   int N, out;
+  int split;  // tiled GEMM only: write bf16 hi and lo parts per block of `split` columns
 };
 
 static LinearPlan plan_products(int R, int K, const Product* pr, int np, int nbatch) {
@@ -236,11 +356,32 @@ static LinearPlan plan_products(int R, int K, const Product* pr, int np, int nba
   return plan_linear(R, K, N, np, nbatch);
 }
 
-// Products sharing the rows x [R][K] (R <= 64, K % 128 == 0) in one launch; `part`
+// Products sharing the rows x [R][K] (K % 128 == 0) in one launch; `part`
 // holds the plan's partial sums when it splits K.
 static hipError_t linear(const void* x, int64_t x_bs, int64_t x_rs, int R, int K, const Product* pr, int np,
                          int nbatch, float* part, hipStream_t s) {
   const LinearPlan pl = plan_products(R, K, pr, np, nbatch);
+  if (pl.gemm) {
+    for (int i = 0; i < np; ++i) {
+      GemmParams g{};
+      g.x = static_cast<const uint16_t*>(x);
+      g.x_bs = x_bs;
+      g.x_rs = x_rs;
+      g.W = static_cast<const uint16_t*>(pr[i].W);
+      g.w_bs = pr[i].w_bs;
+      g.y = pr[i].y;
+      g.y_bs = pr[i].y_bs;
+      g.y_rs = pr[i].y_rs;
+      g.R = R;
+      g.N = pr[i].N;
+      g.K = K;
+      g.out = pr[i].out;
+      g.split = pr[i].split;
+      const dim3 grid((unsigned)((pr[i].N + kGN - 1) / kGN), (unsigned)((R + kGM - 1) / kGM), (unsigned)nbatch);
+      hipLaunchKernelGGL(gemm_rows, grid, dim3(512), 0, s, g);
+    }
+    return hipGetLastError();
+  }
   LinearParams p{};
   p.x = static_cast<const uint16_t*>(x);
   p.x_bs = x_bs;
@@ -264,7 +405,7 @@ static hipError_t linear(const void* x, int64_t x_bs, int64_t x_rs, int R, int K
     g.part_off = pl.part_off[i];
     g.e0 = pl.e0[i];
   }
-  const dim3 grid((unsigned)pl.blocks, (unsigned)nbatch);
+  const dim3 grid((unsigned)pl.blocks, (unsigned)nbatch, (unsigned)pl.row_blocks);
   if (pl.nt == 2) {
     if (pl.mt == 1) launch_lr<1, 2>(p, pl, grid, s);
     else if (pl.mt == 2) launch_lr<2, 2>(p, pl, grid, s);
@@ -361,21 +502,67 @@ static void launch_absorb(const sckv_query_args& a, const float* qh, hipStream_t
   else launch_absorb_mt<OUT, 2>(a, qh, s);
 }
 
+// W_UK [H][dh][D] -> T [H][D][2 dh] with T[h][n][k] = T[h][n][dh + k] = W_UK[h][k][n]:
+// the absorption's weights as a GEMM operand over the two bf16 parts of the head
+// queries.  64 x 64 tiles through LDS.
+__global__ __launch_bounds__(256) void dup_transpose(const uint16_t* __restrict__ WUK, uint16_t* __restrict__ T,
+                                                     int dh, int D) {
+  __shared__ uint16_t t[64][65];
+  const int h = blockIdx.z, n0 = blockIdx.x * 64, k0 = blockIdx.y * 64;
+  const uint16_t* src = WUK + (int64_t)h * dh * D;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int kk = i / 64, nn = i % 64;
+    t[kk][nn] = src[(int64_t)(k0 + kk) * D + n0 + nn];
+  }
+  __syncthreads();
+  uint16_t* dst = T + (int64_t)h * D * 2 * dh;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int nn = i / 64, kk = i % 64;
+    const uint16_t v = t[kk][nn];
+    dst[(int64_t)(n0 + nn) * 2 * dh + k0 + kk] = v;
+    dst[(int64_t)(n0 + nn) * 2 * dh + dh + k0 + kk] = v;
+  }
+}
+
 static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Absorption of many rows runs on the bf16 GEMM: W_q writes each head query as two
+// bf16 parts (hi, lo: the same bytes as fp32) and the GEMM multiplies [hi | lo]
+// by [W_UK^T | W_UK^T] (the duplicated transpose, after the head queries).
+static bool absorb_by_gemm(const sckv_query_args& a) { return a.W_UK && a.R >= kGemmRows; }
 
 static int query_products(const sckv_query_args& a, void* ws, Product* pr) {
   const int HD = a.H * a.d_h;
   const bool absorb = a.W_UK != nullptr;
   int np = 0;
-  // head queries: into the workspace (fp32) when they are absorbed, else straight to q
-  pr[np++] = Product{a.W_q, absorb ? ws : a.q, 0, 0, HD, HD, absorb ? SCKV_F32 : a.q_dtype};
-  if (a.W_iq) pr[np++] = Product{a.W_iq, a.qI, 0, 0, (int64_t)a.H_I * a.D_I, a.H_I * a.D_I, a.q_dtype};
-  if (a.W_w) pr[np++] = Product{a.W_w, a.w, 0, 0, a.H_I, a.H_I, SCKV_F32};
+  // head queries: into the workspace when they are absorbed (fp32, or two bf16
+  // parts for the GEMM absorption), else straight to q
+  if (absorb_by_gemm(a)) pr[np++] = Product{a.W_q, ws, 0, 0, 2 * (int64_t)HD, HD, SCKV_BF16, a.d_h};
+  else pr[np++] = Product{a.W_q, absorb ? ws : a.q, 0, 0, HD, HD, absorb ? SCKV_F32 : a.q_dtype, 0};
+  if (a.W_iq) pr[np++] = Product{a.W_iq, a.qI, 0, 0, (int64_t)a.H_I * a.D_I, a.H_I * a.D_I, a.q_dtype, 0};
+  if (a.W_w) pr[np++] = Product{a.W_w, a.w, 0, 0, a.H_I, a.H_I, SCKV_F32, 0};
   return np;
 }
 
 static size_t query_heads_bytes(const sckv_query_args& a) {
-  return a.W_UK ? align256((size_t)a.R * a.H * a.d_h * sizeof(float)) : 0;
+  if (!a.W_UK) return 0;
+  const size_t heads = align256((size_t)a.R * a.H * a.d_h * sizeof(float));
+  return absorb_by_gemm(a) ? heads + align256((size_t)a.H * a.D * 2 * a.d_h * sizeof(uint16_t)) : heads;
+}
+
+static hipError_t absorb(const sckv_query_args& a, void* ws, hipStream_t s) {
+  if (absorb_by_gemm(a)) {
+    uint16_t* T = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) +
+                                              align256((size_t)a.R * a.H * a.d_h * sizeof(float)));
+    hipLaunchKernelGGL(dup_transpose, dim3((unsigned)(a.D / 64), (unsigned)(a.d_h / 64), (unsigned)a.H), dim3(256), 0,
+                       s, static_cast<const uint16_t*>(a.W_UK), T, a.d_h, a.D);
+    // batch item h: x = [hi | lo] of head h (2 d_h columns), W = T[h] [D][2 d_h], y = q[:, h, :]
+    const Product pr{T, a.q, (int64_t)a.D * 2 * a.d_h, a.D, (int64_t)a.H * a.D, a.D, a.q_dtype, 0};
+    return linear(ws, 2 * a.d_h, (int64_t)a.H * 2 * a.d_h, a.R, 2 * a.d_h, &pr, 1, a.H, nullptr, s);
+  }
+  if (a.q_dtype == SCKV_BF16) launch_absorb<SCKV_BF16>(a, static_cast<const float*>(ws), s);
+  else launch_absorb<SCKV_F32>(a, static_cast<const float*>(ws), s);
+  return hipGetLastError();
 }
 
 size_t queries_workspace(const sckv_query_args& a) {
@@ -390,9 +577,7 @@ hipError_t launch_layer_queries(const sckv_query_args& a, void* ws, hipStream_t 
   float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + query_heads_bytes(a));
   hipError_t e = linear(a.x, 0, a.d_model, a.R, a.d_model, pr, np, 1, part, s);
   if (e != hipSuccess || !a.W_UK) return e;
-  if (a.q_dtype == SCKV_BF16) launch_absorb<SCKV_BF16>(a, static_cast<const float*>(ws), s);
-  else launch_absorb<SCKV_F32>(a, static_cast<const float*>(ws), s);
-  return hipGetLastError();
+  return absorb(a, ws, s);
 }
 
 static int stream_products(const sckv_stream_args& a, Product* pr) {
@@ -401,7 +586,7 @@ static int stream_products(const sckv_stream_args& a, Product* pr) {
   const int N[4] = {a.D, a.D, a.D_I, a.D_I};
   int np = 0;
   for (int i = 0; i < 4; ++i)
-    if (W[i]) pr[np++] = Product{W[i], out[i], 0, 0, N[i], N[i], a.out_dtype};
+    if (W[i]) pr[np++] = Product{W[i], out[i], 0, 0, N[i], N[i], a.out_dtype, 0};
   return np;
 }
 
@@ -433,19 +618,17 @@ hipError_t launch_layer_inputs(const sckv_query_args& a, const sckv_stream_args&
   float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + query_heads_bytes(a));
   hipError_t e = linear(a.x, 0, a.d_model, a.R, a.d_model, pr, np, 1, part, s);
   if (e != hipSuccess || !a.W_UK) return e;
-  if (a.q_dtype == SCKV_BF16) launch_absorb<SCKV_BF16>(a, static_cast<const float*>(ws), s);
-  else launch_absorb<SCKV_F32>(a, static_cast<const float*>(ws), s);
-  return hipGetLastError();
+  return absorb(a, ws, s);
 }
 
 // o_h = W_UV^h o~_h for every head (a batch of H products), rounded to bf16 into
 // the workspace; then y = W_o [o_1 .. o_H].
 static Product heads_product(const sckv_output_args& a, void* ws) {
-  return Product{a.W_UV, ws, (int64_t)a.d_h * a.D, a.d_h, (int64_t)a.H * a.d_h, a.d_h, SCKV_BF16};
+  return Product{a.W_UV, ws, (int64_t)a.d_h * a.D, a.d_h, (int64_t)a.H * a.d_h, a.d_h, SCKV_BF16, 0};
 }
 
 static Product out_product(const sckv_output_args& a) {
-  return Product{a.W_o, a.y, 0, 0, a.d_model, a.d_model, a.y_dtype};
+  return Product{a.W_o, a.y, 0, 0, a.d_model, a.d_model, a.y_dtype, 0};
 }
 
 static size_t output_heads_bytes(const sckv_output_args& a) {

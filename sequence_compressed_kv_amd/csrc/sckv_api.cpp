@@ -218,7 +218,7 @@ sckv_status check_queries(const sckv_query_args* a, size_t* ws) {
   if (!a) return fail(SCKV_ERR_NULL, "%s: args is NULL", name);
   if (!a->x || !a->W_q || !a->q) return fail(SCKV_ERR_NULL, "%s: x, W_q and q must be set", name);
   if ((a->W_iq && !a->qI) || (a->W_w && !a->w)) return fail(SCKV_ERR_NULL, "%s: W_iq needs qI and W_w needs w", name);
-  if (a->R < 1 || a->R > 64) return fail(SCKV_ERR_SHAPE, "%s: R=%d outside [1,64]", name, a->R);
+  if (a->R < 1 || a->R > (1 << 21)) return fail(SCKV_ERR_SHAPE, "%s: R=%d outside [1,2^21]", name, a->R);
   if (a->H < 1 || a->d_h < 1 || a->D < 1) return fail(SCKV_ERR_SHAPE, "%s: need H, d_h, D >= 1", name);
   if ((int64_t)a->H * a->d_h > (1 << 20)) return fail(SCKV_ERR_UNSUPPORTED, "%s: H*d_h exceeds 2^20", name);
   if ((a->W_iq || a->W_w) && (a->H_I < 1 || a->D_I < 1 || (int64_t)a->H_I * a->D_I > (1 << 20)))
@@ -248,7 +248,7 @@ sckv_status check_streams(const sckv_stream_args* a, size_t* ws) {
   if (!a->x) return fail(SCKV_ERR_NULL, "%s: x must be set", name);
   if ((a->W_c && !a->v) || (a->W_g && !a->g) || (a->W_cI && !a->vI) || (a->W_gI && !a->gI))
     return fail(SCKV_ERR_NULL, "%s: every weight given needs its output", name);
-  if (a->R < 1 || a->R > 64) return fail(SCKV_ERR_SHAPE, "%s: R=%d outside [1,64]", name, a->R);
+  if (a->R < 1 || a->R > (1 << 21)) return fail(SCKV_ERR_SHAPE, "%s: R=%d outside [1,2^21]", name, a->R);
   if ((a->W_c || a->W_g) && (a->D < 1 || a->D > (1 << 20))) return fail(SCKV_ERR_SHAPE, "%s: D=%d", name, a->D);
   if ((a->W_cI || a->W_gI) && (a->D_I < 1 || a->D_I > (1 << 20)))
     return fail(SCKV_ERR_SHAPE, "%s: D_I=%d", name, a->D_I);
@@ -267,7 +267,7 @@ sckv_status check_output(const sckv_output_args* a, size_t* ws) {
   const char* name = "layer_output";
   if (!a) return fail(SCKV_ERR_NULL, "%s: args is NULL", name);
   if (!a->o || !a->W_o || !a->y) return fail(SCKV_ERR_NULL, "%s: o, W_o and y must be set", name);
-  if (a->R < 1 || a->R > 64) return fail(SCKV_ERR_SHAPE, "%s: R=%d outside [1,64]", name, a->R);
+  if (a->R < 1 || a->R > (1 << 21)) return fail(SCKV_ERR_SHAPE, "%s: R=%d outside [1,2^21]", name, a->R);
   if (a->H < 1 || a->d_h < 1 || a->D < 1 || a->d_model < 1 || a->d_model > (1 << 20))
     return fail(SCKV_ERR_SHAPE, "%s: need H, d_h, D, d_model >= 1 (d_model <= 2^20)", name);
   sckv_status s = check_reduce_len((int64_t)a->H * a->d_h, name, "H*d_h");

@@ -62,12 +62,13 @@ hipError_t launch_attend(const sckv_attend_args& a, bool csa, const AttendPlan& 
                          hipStream_t stream);
 
 // ---------------------------------------------------------------- projections
-// Plan of one grouped launch of up to 8 products sharing rows x [R][K]: row tiles
-// of 16 mt, column tiles of 16 nt, nw waves per block; product i takes blocks
+// Plan of one grouped launch of up to 8 products sharing rows x [R][K]: row blocks
+// of 16 mt rows, column tiles of 16 nt, nw waves per block; product i takes blocks
 // blk0[i] .. and cuts K in splits[i] parts, whose fp32 partial sums (at part_off[i]
 // floats of a buffer of part_bytes) a second kernel adds up.
 struct LinearPlan {
-  int np = 0, mt = 0, nt = 0, nw = 0, u = 1, blocks = 0;
+  bool gemm = false;  // many rows: one tiled GEMM launch per product instead
+  int np = 0, mt = 0, nt = 0, nw = 0, u = 1, blocks = 0, row_blocks = 1;
   int splits[8] = {1, 1, 1, 1, 1, 1, 1, 1};
   int blk0[8] = {};
   int64_t part_off[8] = {};

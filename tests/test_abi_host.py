@@ -189,7 +189,8 @@ def qargs(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(x=None), 1), (dict(q=None), 1), (dict(qI=None), 1), (dict(w=None), 1), (dict(R=0), 2), (dict(R=65), 2),
+    (dict(x=None), 1), (dict(q=None), 1), (dict(qI=None), 1), (dict(w=None), 1), (dict(R=0), 2),
+    (dict(R=(1 << 21) + 1), 2),
     (dict(d_model=4000), 4), (dict(d_model=0), 4), (dict(q_dtype=2), 3), (dict(D=576), 4), (dict(D=8192), 4),
     (dict(d_h=120), 4),
     (dict(d_h=512), 4), (dict(W_UK=None), 2), (dict(W_q=FAKE_ODD), 5), (dict(w=FAKE_ODD), 5), (dict(H=0), 2),
@@ -220,7 +221,7 @@ def sargs(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(x=None), 1), (dict(v=None), 1), (dict(gI=None), 1), (dict(R=65), 2), (dict(D=0), 2),
+    (dict(x=None), 1), (dict(v=None), 1), (dict(gI=None), 1), (dict(R=(1 << 21) + 1), 2), (dict(D=0), 2),
     (dict(D_I=0), 2), (dict(d_model=100), 4), (dict(out_dtype=2), 3), (dict(vI=FAKE_ODD), 5),
 ])
 def test_streams_validation(L, kw, status):
@@ -233,7 +234,7 @@ def test_streams_workspace(L):
     # 1280 columns make 20 tiles of 64: K is cut in 16 parts, fp32 partial sums per part
     assert n == 16 * 32 * 1280 * 4
     assert L.layer_streams(C.byref(a), FAKE, n - 1, None) == 6
-    assert L.layer_streams_workspace_size(C.byref(sargs(R=65))) == 0
+    assert L.layer_streams_workspace_size(C.byref(sargs(R=0))) == 0
 
 
 def oargs(**kw):

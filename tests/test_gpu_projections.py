@@ -11,7 +11,10 @@ runs on the same values in fp64.  Error bounds, element by element:
   * a bf16 rounding (to nearest even) adds at most 2^-8 of the magnitude.
 Intermediate results the library keeps in its workspace (the fp32 head queries
 before absorption, the bf16 heads o_h = W_UV^h o~_h) are checked against the
-oracle's own intermediate values with the same bounds."""
+oracle's own intermediate values with the same bounds.  The absorption of many
+rows multiplies the head queries as two bf16 parts (hi = bf16(q), lo =
+bf16(q - hi), together within 2^-18 |q|), 2 d_h products per output: its bound,
+used for every row count, counts 2 d_h terms and adds 2^-18 of the magnitude."""
 import ctypes
 import functools
 
@@ -65,6 +68,15 @@ def dot_bound(x, W, K=None):
     return K * U32 * (np.abs(x) @ np.abs(W).T)
 
 
+def absorbed_bound(qh, bqh, WUK):
+    """Bound of the absorbed queries: the head queries' own bound carried through
+    |W_UK|, plus the absorption's (2 d_h fp32 terms of the two-part split, and the
+    split's 2^-18)."""
+    d_h = WUK.shape[1]
+    return np.stack([bqh[:, h, :] @ np.abs(WUK[h]) + (2 * d_h * U32 * 1.01 + 2.0 ** -18) *
+                     ((np.abs(qh[:, h, :]) + bqh[:, h, :]) @ np.abs(WUK[h])) for h in range(WUK.shape[0])], axis=1)
+
+
 def check(g, o, bound, rounded: bool, what: str):
     g = np.asarray(g, np.float64)
     o = np.asarray(o, np.float64)
@@ -113,13 +125,7 @@ def test_layer_queries_parity(name, li, R, qd):
         qh_gpu = ws[:R * L.H * L.d_h * 4].view(torch.float32).view(R, L.H, L.d_h)
         check(host(qh_gpu), qh, bqh, False, "q_heads")
         q_ora = method.absorb_queries(qh, w["W_UK"])
-        WUK = np.abs(w["W_UK"])                                          # [H][d_h][D]
-        bq = np.empty_like(q_ora)
-        for h in range(L.H):
-            carried = bqh[:, h, :] @ WUK[h]
-            fresh = L.d_h * U32 * ((np.abs(qh[:, h, :]) + bqh[:, h, :]) @ WUK[h])
-            bq[:, h, :] = carried + fresh
-        check(host(q), q_ora, bq, rounded, "q (absorbed)")
+        check(host(q), q_ora, absorbed_bound(qh, bqh, w["W_UK"]), rounded, "q (absorbed)")
     else:
         check(host(q), qh, bqh, rounded, "q")
     if csa:
@@ -128,7 +134,8 @@ def test_layer_queries_parity(name, li, R, qd):
         check(host(hw), method.project(x, w["W_w"]), dot_bound(x, w["W_w"]), False, "w")
 
 
-@pytest.mark.parametrize("d_h,D,H,R", [(64, 256, 8, 3), (256, 512, 4, 20), (128, 128, 16, 33)])
+@pytest.mark.parametrize("d_h,D,H,R", [(64, 256, 8, 3), (256, 512, 4, 20), (128, 128, 16, 33), (64, 256, 8, 520),
+                                     (256, 512, 4, 700)])
 def test_layer_queries_absorb_head_dims(d_h, D, H, R):
     """Absorption for the other head widths the library takes (synthetic weights)."""
     print(f"layer_queries absorb d_h={d_h} D={D} H={H} R={R}", flush=True)
@@ -142,11 +149,14 @@ def test_layer_queries_absorb_head_dims(d_h, D, H, R):
     torch.cuda.synchronize()
     qh = method.project(x, Wq).reshape(R, H, d_h)
     bqh = dot_bound(x, Wq).reshape(R, H, d_h)
-    check(host(ws[:R * H * d_h * 4].view(torch.float32).view(R, H, d_h)), qh, bqh, False, "q_heads")
+    if R >= 512:
+        # many rows: the head queries as two bf16 parts [R][H][hi | lo]
+        parts = host(ws[:R * H * d_h * 4].view(torch.bfloat16).view(R, H, 2, d_h))
+        check(parts[:, :, 0] + parts[:, :, 1], qh, bqh + 2.0 ** -18 * (np.abs(qh) + bqh), False, "q_heads (hi + lo)")
+    else:
+        check(host(ws[:R * H * d_h * 4].view(torch.float32).view(R, H, d_h)), qh, bqh, False, "q_heads")
     q_ora = method.absorb_queries(qh, WUK)
-    bq = np.stack([bqh[:, h, :] @ np.abs(WUK[h]) + d_h * U32 * ((np.abs(qh[:, h, :]) + bqh[:, h, :]) @ np.abs(WUK[h]))
-                   for h in range(H)], axis=1)
-    check(host(q), q_ora, bq, False, "q (absorbed)")
+    check(host(q), q_ora, absorbed_bound(qh, bqh, WUK), False, "q (absorbed)")
 
 
 # ---------------------------------------------------------------- streams
@@ -223,9 +233,7 @@ def test_layer_inputs_parity(name, li, R):
     bqh = dot_bound(x, w["W_q"]).reshape(R, L.H, L.d_h)
     if L.absorbed:
         q_ora = method.absorb_queries(qh, w["W_UK"])
-        bq = np.stack([bqh[:, h, :] @ np.abs(w["W_UK"][h]) + L.d_h * U32 *
-                       ((np.abs(qh[:, h, :]) + bqh[:, h, :]) @ np.abs(w["W_UK"][h])) for h in range(L.H)], axis=1)
-        check(host(q), q_ora, bq, True, "q (absorbed)")
+        check(host(q), q_ora, absorbed_bound(qh, bqh, w["W_UK"]), True, "q (absorbed)")
     else:
         check(host(q), qh, bqh, True, "q")
     if csa:
@@ -303,3 +311,74 @@ def test_layer_output_consecutive_calls_reuse_workspace():
         e1 = (b1 + U16 * (np.abs(heads) + b1)).reshape(R, -1)
         bound = e1 @ np.abs(w["W_o"]).T + L.H * L.d_h * U32 * ((np.abs(heads).reshape(R, -1) + e1) @ np.abs(w["W_o"]).T)
         check(host(y), y_ora, bound, False, f"y R={R}")
+
+
+# ---------------------------------------------------------------- many rows (prefill)
+@pytest.mark.parametrize("R", [65, 333, 600])
+def test_layer_inputs_many_rows(R):
+    """Rows in blocks (64 rows, or 256-row GEMM tiles from 512 rows on) with a ragged
+    last block: queries (absorbed, indexer) and streams of the 32K prefill layer's
+    shapes."""
+    print(f"layer_inputs many rows R={R}", flush=True)
+    wl = configs.CSA_PREFILL_32K_BF16
+    L = wl.layers[0]
+    w = weights(wl.name, 0)
+    x = hidden_rows(R, wl.d_model, 7 + R)
+    q = torch.full((R, L.H, L.D), float("nan"), device=DEV, dtype=torch.bfloat16)
+    qI = torch.full((R, L.H_I, L.D_I), float("nan"), device=DEV, dtype=torch.bfloat16)
+    hw = torch.full((R, L.H_I), float("nan"), device=DEV)
+    v = torch.full((R, L.D), float("nan"), device=DEV)
+    gI = torch.full((R, L.D_I), float("nan"), device=DEV)
+    sk.layer_inputs(up(x), up(w["W_q"]), q, W_UK=up(w["W_UK"]), W_iq=up(w["W_iq"]), qI=qI, W_w=up(w["W_w"]), w=hw,
+                    W_c=up(w["W_c"]), v=v, W_gI=up(w["W_gI"]), gI=gI)
+    torch.cuda.synchronize()
+    qh = method.project(x, w["W_q"]).reshape(R, L.H, L.d_h)
+    bqh = dot_bound(x, w["W_q"]).reshape(R, L.H, L.d_h)
+    q_ora = method.absorb_queries(qh, w["W_UK"])
+    check(host(q), q_ora, absorbed_bound(qh, bqh, w["W_UK"]), True, "q (absorbed)")
+    check(host(qI), method.project(x, w["W_iq"]).reshape(R, L.H_I, L.D_I),
+          dot_bound(x, w["W_iq"]).reshape(R, L.H_I, L.D_I), True, "qI")
+    check(host(hw), method.project(x, w["W_w"]), dot_bound(x, w["W_w"]), False, "w")
+    check(host(v), method.project(x, w["W_c"]), dot_bound(x, w["W_c"]), False, "v")
+    check(host(gI), method.project(x, w["W_gI"]), dot_bound(x, w["W_gI"]), False, "gI")
+
+
+@pytest.mark.parametrize("R", [130, 700])
+def test_layer_output_many_rows(R):
+    wl = configs.CSA_PREFILL_32K_BF16
+    L = wl.layers[0]
+    w = weights(wl.name, 0)
+    o = bf16(np.random.default_rng(3).standard_normal((R, L.H, L.D)).astype(np.float32) * 0.5)
+    y = torch.full((R, wl.d_model), float("nan"), device=DEV)
+    ws = sk.layer_output(up(o), up(w["W_o"]), y, W_UV=up(w["W_UV"]))
+    torch.cuda.synchronize()
+    heads = head_outputs(o, w["W_UV"])
+    b1 = L.D * U32 * np.einsum("hkd,rhd->rhk", np.abs(w["W_UV"]), np.abs(o))
+    check(host(ws[:R * L.H * L.d_h * 2].view(torch.bfloat16).view(R, L.H, L.d_h)), heads, b1, True, "heads")
+    e1 = (b1 + U16 * (np.abs(heads) + b1)).reshape(R, -1)
+    Wo = w["W_o"]
+    bound = e1 @ np.abs(Wo).T + L.H * L.d_h * U32 * ((np.abs(heads).reshape(R, -1) + e1) @ np.abs(Wo).T)
+    y_ora = np.stack([method.layer_output(o[r], Wo, w["W_UV"]) for r in range(R)])
+    check(host(y), y_ora, bound, False, "y")
+
+
+def test_prefill_streams_full_size_sampled():
+    """The 32K prefill layer's four stream products over all 32768 rows in one
+    launch; 48 rows (both ends, row-block edges, random) against the oracle."""
+    wl = configs.CSA_PREFILL_32K_BF16
+    w = weights(wl.name, 0)
+    R = wl.N
+    x = hidden_rows(R, wl.d_model, 123)
+    xd = up(x)
+    outs = {k: torch.full((R, n), float("nan"), device=DEV, dtype=torch.bfloat16)
+            for k, n in (("v", 512), ("g", 512), ("vI", 128), ("gI", 128))}
+    sk.layer_streams(xd, W_c=up(w["W_c"]), v=outs["v"], W_g=up(w["W_g"]), g=outs["g"], W_cI=up(w["W_cI"]),
+                     vI=outs["vI"], W_gI=up(w["W_gI"]), gI=outs["gI"])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 65, 127, 128, R // 2, R - 65, R - 64, R - 2, R - 1],
+                                     rng.integers(0, R, 36)]))
+    xs = x[rows]
+    for k, wn in (("v", "W_c"), ("g", "W_g"), ("vI", "W_cI"), ("gI", "W_gI")):
+        assert torch.isfinite(outs[k].float()).all(), k
+        check(host(outs[k][torch.from_numpy(rows).to(DEV)]), method.project(xs, w[wn]), dot_bound(xs, w[wn]), True, k)
