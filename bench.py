@@ -154,6 +154,65 @@ def prefill_attend_rate(dev, sk, torch, wl, iters: int = 3):
             "ms": ms, "achieved_tflops": tf, "peak_tflops": PEAK_BF16_TFLOPS, "frac": tf / PEAK_BF16_TFLOPS}
 
 
+def prefill_projection_rate(dev, sk, torch, wl, iters: int = 3):
+    """The projections of the 32K-token causal prefill layer: layer_inputs (W_q with
+    the absorption into the latent, W_iq, W_w and the four stream weights) and
+    layer_output (W_UV, W_o) over all 32768 rows, on the tiled bf16 GEMM.
+    Algorithmic flops: 2 x rows x (in x out) of every product; the absorption
+    counts its d_h x D product once (its two-part split runs it twice)."""
+    L = wl.layers[0]
+    T, dm = wl.N, wl.d_model
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.seed + 29)
+    bf = torch.bfloat16
+
+    def rnd(*shape, fan_in):
+        return (torch.randn(*shape, device=dev, generator=g) / math.sqrt(fan_in)).to(bf)
+
+    x = torch.randn(T, dm, device=dev, generator=g).to(bf)
+    Wq, WUK, WUV = rnd(L.H * L.d_h, dm, fan_in=dm), rnd(L.H, L.d_h, L.D, fan_in=L.D), rnd(L.H, L.d_h, L.D, fan_in=L.D)
+    Wo, Wiq, Ww = rnd(dm, L.H * L.d_h, fan_in=L.H * L.d_h), rnd(L.H_I * L.D_I, dm, fan_in=dm), rnd(L.H_I, dm, fan_in=dm)
+    Wc, Wg, WcI, WgI = (rnd(L.D, dm, fan_in=dm), rnd(L.D, dm, fan_in=dm), rnd(L.D_I, dm, fan_in=dm),
+                        rnd(L.D_I, dm, fan_in=dm))
+    q = torch.empty(T, L.H, L.D, device=dev, dtype=bf)
+    qI = torch.empty(T, L.H_I, L.D_I, device=dev, dtype=bf)
+    w = torch.empty(T, L.H_I, device=dev)
+    v, gg = torch.empty(T, L.D, device=dev, dtype=bf), torch.empty(T, L.D, device=dev, dtype=bf)
+    vI, gI = torch.empty(T, L.D_I, device=dev, dtype=bf), torch.empty(T, L.D_I, device=dev, dtype=bf)
+    o = (torch.randn(T, L.H, L.D, device=dev, generator=g) * 0.5).to(bf)
+    y = torch.empty(T, dm, device=dev, dtype=bf)
+
+    def inputs(ws=None):
+        return sk.layer_inputs(x, Wq, q, W_UK=WUK, W_iq=Wiq, qI=qI, W_w=Ww, w=w, W_c=Wc, v=v, W_g=Wg, g=gg,
+                               W_cI=WcI, vI=vI, W_gI=WgI, gI=gI, workspace=ws)
+
+    def output(ws=None):
+        return sk.layer_output(o, Wo, y, W_UV=WUV, workspace=ws)
+
+    ws_in, ws_out = inputs(), output()
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(iters):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+    ms_in = timed(lambda: inputs(ws_in))
+    ms_out = timed(lambda: output(ws_out))
+    HD = L.H * L.d_h
+    fl_in = 2.0 * T * (dm * (HD + L.H_I * L.D_I + L.H_I + 2 * L.D + 2 * L.D_I) + HD * L.D)
+    fl_out = 2.0 * T * (HD * L.D + HD * dm)
+    tf = (fl_in + fl_out) / ((ms_in + ms_out) * 1e-3) / 1e12
+    return {"workload": wl.name, "kernel": "gemm_rows", "rows": T, "tflop": (fl_in + fl_out) / 1e12,
+            "ms_layer_inputs": ms_in, "ms_layer_output": ms_out, "achieved_tflops": tf,
+            "peak_tflops": PEAK_BF16_TFLOPS, "frac": tf / PEAK_BF16_TFLOPS}
+
+
 def build_caches(wl, dev, sk, torch, gen, tail: int = 0):
     """Caches of every sequence for both layers (GPU-drawn streams, library compressors).
     With tail > 0 the last `tail` tokens of every stream are returned too (third
@@ -577,7 +636,9 @@ def main():
 
     if args.only == "prefill":
         print(json.dumps({"prefill_indexer": prefill_indexer_rate("cuda:0", sk, torch, CSA_PREFILL_32K_BF16),
-                          "prefill_attend": prefill_attend_rate("cuda:0", sk, torch, CSA_PREFILL_32K_BF16)}))
+                          "prefill_attend": prefill_attend_rate("cuda:0", sk, torch, CSA_PREFILL_32K_BF16),
+                          "prefill_projections": prefill_projection_rate("cuda:0", sk, torch,
+                                                                         CSA_PREFILL_32K_BF16)}))
         return
     if args.only == "1m":
         print(json.dumps({"decode_1m_fp8": decode_1m_rate("cuda:0", sk, torch, gen)}))
@@ -703,6 +764,8 @@ def main():
         rec["prefill_indexer"] = prefill_indexer_rate(dev, sk, torch, CSA_PREFILL_32K_BF16)
         torch.cuda.empty_cache()
         rec["prefill_attend"] = prefill_attend_rate(dev, sk, torch, CSA_PREFILL_32K_BF16)
+        torch.cuda.empty_cache()
+        rec["prefill_projections"] = prefill_projection_rate(dev, sk, torch, CSA_PREFILL_32K_BF16)
     if not args.no_1m:
         print("[bench] 1M-context fp8 decode step", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()

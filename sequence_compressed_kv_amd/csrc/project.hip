@@ -422,18 +422,20 @@ static hipError_t linear(const void* x, int64_t x_bs, int64_t x_rs, int R, int K
 }
 
 // q[r][h][d] = sum_k qh[r][h][k] W_UK[h][k][d], fp32 products on the matrix
-// cores (16x16x4 fp32).  Block (128 latent columns, head, 16 MT rows); its 4 waves
-// take a quarter of k each (KG groups of 16) and add up in LDS in wave order.
+// cores (16x16x4 fp32).  Block (128 latent columns, head, 16 MT rows); its NWV
+// waves take equal shares of k (KG groups of 16 each) and add up in LDS in wave
+// order.
 // A lane loads 8 adjacent columns of one W_UK row (16 bytes), which serve as the
 // B operands of 8 products whose 16 output columns are 8 apart: product e of
 // lane column c holds latent column 8 c + e.  Within a group of 16 k, step ss
 // (0..3) gives K slot g the value k = 16 q + 4 g + ss, so a lane's four A values
 // of a group are 4 adjacent head-query elements (one 16-byte load).
-template <int OUT, int MT, int KG>
-__global__ __launch_bounds__(256) void absorb_kernel(const float* __restrict__ qh, const uint16_t* __restrict__ WUK,
-                                                     void* __restrict__ q, int R, int H, int D) {
-  constexpr int dh = 64 * KG;
-  __shared__ f32x4 red[4][8 * MT][kWave];
+template <int OUT, int MT, int KG, int NWV>
+__global__ __launch_bounds__(NWV * 64) void absorb_kernel(const float* __restrict__ qh,
+                                                          const uint16_t* __restrict__ WUK, void* __restrict__ q, int R,
+                                                          int H, int D) {
+  constexpr int dh = 16 * KG * NWV;
+  __shared__ f32x4 red[NWV][8 * MT][kWave];
   const int nb = blockIdx.x * 128, h = blockIdx.y, r0 = blockIdx.z * 16 * MT;
   const int l = lane_id(), w = wave_id(), c = l & 15, g = l >> 4;
   const int kw0 = w * 16 * KG;  // first k of the wave
@@ -473,8 +475,10 @@ __global__ __launch_bounds__(256) void absorb_kernel(const float* __restrict__ q
 #pragma unroll
     for (int e = 0; e < 8; ++e) red[w][mt * 8 + e][l] = acc[mt][e];
   __syncthreads();
-  for (int t = w; t < 8 * MT; t += 4) {
-    const f32x4 v = ((red[0][t][l] + red[1][t][l]) + red[2][t][l]) + red[3][t][l];
+  for (int t = w; t < 8 * MT; t += NWV) {
+    f32x4 v = red[0][t][l];
+#pragma unroll
+    for (int j = 1; j < NWV; ++j) v += red[j][t][l];
     const int mt = t / 8, e = t % 8;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -487,19 +491,18 @@ __global__ __launch_bounds__(256) void absorb_kernel(const float* __restrict__ q
   }
 }
 
-template <int OUT, int MT>
-static void launch_absorb_mt(const sckv_query_args& a, const float* qh, hipStream_t s) {
-  const dim3 grid((unsigned)(a.D / 128), (unsigned)a.H, (unsigned)((a.R + 16 * MT - 1) / (16 * MT)));
-  const uint16_t* W = static_cast<const uint16_t*>(a.W_UK);
-  if (a.d_h == 64) hipLaunchKernelGGL((absorb_kernel<OUT, MT, 1>), grid, dim3(256), 0, s, qh, W, a.q, a.R, a.H, a.D);
-  else if (a.d_h == 128) hipLaunchKernelGGL((absorb_kernel<OUT, MT, 2>), grid, dim3(256), 0, s, qh, W, a.q, a.R, a.H, a.D);
-  else hipLaunchKernelGGL((absorb_kernel<OUT, MT, 4>), grid, dim3(256), 0, s, qh, W, a.q, a.R, a.H, a.D);
-}
-
+// Blocks of 16 rows; d_h = 64 on 4 waves, 128 and 256 on 8 (one or two groups of
+// 16 k per wave).
 template <int OUT>
 static void launch_absorb(const sckv_query_args& a, const float* qh, hipStream_t s) {
-  if (a.R <= 16) launch_absorb_mt<OUT, 1>(a, qh, s);
-  else launch_absorb_mt<OUT, 2>(a, qh, s);
+  const dim3 grid((unsigned)(a.D / 128), (unsigned)a.H, (unsigned)((a.R + 15) / 16));
+  const uint16_t* W = static_cast<const uint16_t*>(a.W_UK);
+  if (a.d_h == 64)
+    hipLaunchKernelGGL((absorb_kernel<OUT, 1, 1, 4>), grid, dim3(256), 0, s, qh, W, a.q, a.R, a.H, a.D);
+  else if (a.d_h == 128)
+    hipLaunchKernelGGL((absorb_kernel<OUT, 1, 1, 8>), grid, dim3(512), 0, s, qh, W, a.q, a.R, a.H, a.D);
+  else
+    hipLaunchKernelGGL((absorb_kernel<OUT, 1, 2, 8>), grid, dim3(512), 0, s, qh, W, a.q, a.R, a.H, a.D);
 }
 
 // W_UK [H][dh][D] -> T [H][D][2 dh] with T[h][n][k] = T[h][n][dh + k] = W_UK[h][k][n]:
