@@ -43,7 +43,8 @@ def parse():
     ap.add_argument("--no-1m", action="store_true", help="skip the 1M-context fp8 decode measurement")
     ap.add_argument("--no-append", action="store_true", help="skip the steady-state decode-with-appends measurement")
     ap.add_argument("--no-layer", action="store_true", help="skip the whole-layer decode step (projections) measurement")
-    ap.add_argument("--only", choices=["prefill", "1m", "layer"], default=None,
+    ap.add_argument("--no-stack", action="store_true", help="skip the HCA prefill and the layer-stack measurements")
+    ap.add_argument("--only", choices=["prefill", "1m", "layer", "stack"], default=None,
                     help="run only that side measurement and print its record (for profiling its kernels)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy (reference for the HBM byte counters)")
@@ -211,6 +212,160 @@ def prefill_projection_rate(dev, sk, torch, wl, iters: int = 3):
     return {"workload": wl.name, "kernel": "gemm_rows", "rows": T, "tflop": (fl_in + fl_out) / 1e12,
             "ms_layer_inputs": ms_in, "ms_layer_output": ms_out, "achieved_tflops": tf,
             "peak_tflops": PEAK_BF16_TFLOPS, "frac": tf / PEAK_BF16_TFLOPS}
+
+
+def prefill_hca_attend_rate(dev, sk, torch, wl, iters: int = 3):
+    """HCA attention of a 32K-token causal prefill with the 128K pair's HCA shapes
+    (64 heads, latent 512, 128:1 pooling, window 128): row t attends densely to
+    its E_vis(t) entries plus its window.  Flops as for the CSA prefill."""
+    L = wl.layers[1]
+    T = 32768
+    E = T // L.m
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.seed + 23)
+    bf = torch.bfloat16
+    q = (torch.randn(T, L.H, L.D, device=dev, generator=g) * 0.3).to(bf)
+    ent = torch.randn(1, E, L.D, device=dev, generator=g).to(bf)
+    stream_v = torch.randn(1, T, L.D, device=dev, generator=g).to(bf)
+    items = sum(min(E, max(0, (t - L.W) // L.m)) + min(L.W, t + 1) for t in range(T))
+    flops = 4.0 * items * L.H * L.D
+    out = torch.empty(T, L.H, L.D, device=dev, dtype=bf)
+    rows = sk.RowSpec.causal(T)
+    tau = 1.0 / math.sqrt(L.d_h)
+    ws = sk.hca_attend(rows, q, ent, stream_v, out, m=L.m, W=L.W, softmax_scale=tau)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(iters):
+        sk.hca_attend(rows, q, ent, stream_v, out, m=L.m, W=L.W, softmax_scale=tau, workspace=ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"rows": T, "row_items": items, "tflop": flops / 1e12, "ms": ms, "achieved_tflops": tf,
+            "peak_tflops": PEAK_BF16_TFLOPS, "frac": tf / PEAK_BF16_TFLOPS}
+
+
+def stack_weights(stk, layers, d_model, dev, torch, seed):
+    """Random weights of every layer, N(0, 1/fan_in), drawn by torch on the GPU."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    out = []
+    for L in layers:
+        w = {}
+        for name, shape in stk.layer_weight_shapes(L, d_model).items():
+            fan_in = d_model if name.startswith("bpos") else shape[-1]
+            t = torch.randn(*shape, device=dev, generator=g) / math.sqrt(fan_in)
+            w[name] = t if name.startswith("bpos") else t.to(torch.bfloat16)
+        out.append(w)
+    return out
+
+
+def stack_decode_rate(dev, sk, torch, n_layers: int = 8, B: int = 32, N: int = 131072, steps: int = 16,
+                      replays: int = 5):
+    """Decode through a random-weight stack of the hybrid schedule (HCA, HCA, then
+    CSA / HCA alternating) with the 128K pair's layer shapes, batch 32: `steps`
+    consecutive tokens, every layer appending, indexing (CSA) and attending.  The
+    caches hold random bf16 values (the step's cost does not depend on them;
+    filling 8 layers x 32 sequences x 128K tokens through the stack is a prefill of
+    its own).  Timed eagerly and as one HIP graph of the steps; each run restores
+    the rings first (about 100 MB of copies per 16 steps, inside the timing)."""
+    from sequence_compressed_kv_amd import stack as stk
+    from workloads import PAIR_DEC_128K_BF16
+
+    c_, h_ = PAIR_DEC_128K_BF16.layers
+    csa = stk.StackLayer("csa", c_.m, c_.o, c_.D, c_.H, c_.d_h, c_.W, c_.H_I, c_.D_I, c_.k)
+    hca = stk.StackLayer("hca", h_.m, h_.o, h_.D, h_.H, h_.d_h, h_.W)
+    layers = stk.hybrid_schedule(n_layers, csa, hca)
+    dm = PAIR_DEC_128K_BF16.d_model
+    st = stk.Stack(layers, stack_weights(stk, layers, dm, dev, torch, 101), dm, B, N_max=N)
+    g = torch.Generator(device=dev)
+    g.manual_seed(102)
+    for c in st.caches:
+        for t in c.values():
+            for b in range(B):
+                t[b].copy_(torch.randn(t[b].shape, device=dev, generator=g))
+    xs = [torch.randn(B, dm, device=dev, generator=g).to(torch.bfloat16) for _ in range(steps)]
+    pos = [torch.full((B,), N - steps + i, dtype=torch.int32, device=dev) for i in range(steps)]
+    # the rings as of position N - steps - 1: each run starts from them (a run's later
+    # tokens overwrite the window slots its earlier steps read); the entry caches
+    # need no reset, as re-appending the same tokens rewrites the same entries
+    ring_names = ("win", "g_ring", "vI_ring", "gI_ring")
+    rings0 = [{k: c[k].clone() for k in ring_names if k in c} for c in st.caches]
+
+    def run():
+        for c, r0 in zip(st.caches, rings0):
+            for k, v in r0.items():
+                c[k].copy_(v)
+        for i in range(steps):
+            st.decode(xs[i], pos[i])
+
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n / steps
+
+    run()
+    torch.cuda.synchronize()
+    ref = st._decode_ws[-1]["y"].clone()
+    ms_eager = timed(run, replays)
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(gr, stream=cap):
+            run()
+    stream.wait_stream(cap)
+    torch.cuda.synchronize()
+    gr.replay()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(st._decode_ws[-1]["y"], ref))
+    ms_graph = timed(gr.replay, replays)
+    return {"layers": [L.kind for L in layers], "batch": B, "context": N, "steps": steps,
+            "cache_arena_bytes": st.arena.size, "ms_per_step_eager": ms_eager, "ms_per_step_graph": ms_graph,
+            "tokens_per_s_graph": B / (ms_graph * 1e-3), "graph_matches_eager": same}
+
+
+def stack_prefill_rate(dev, sk, torch, n_layers: int = 4, N: int = 32768, iters: int = 2):
+    """Prefill of one 32K-token sequence through a random-weight stack (HCA, HCA, CSA,
+    HCA) with the 32K prefill layer's shapes (CSA top-512): every layer's
+    projections (tiled GEMM), compression, causal indexing and top-k (CSA),
+    causal attention and output projections."""
+    from sequence_compressed_kv_amd import stack as stk
+    from workloads import CSA_PREFILL_32K_BF16, PAIR_DEC_128K_BF16
+
+    c_ = CSA_PREFILL_32K_BF16.layers[0]
+    h_ = PAIR_DEC_128K_BF16.layers[1]
+    csa = stk.StackLayer("csa", c_.m, c_.o, c_.D, c_.H, c_.d_h, c_.W, c_.H_I, c_.D_I, c_.k)
+    hca = stk.StackLayer("hca", h_.m, h_.o, h_.D, h_.H, h_.d_h, h_.W)
+    layers = stk.hybrid_schedule(n_layers, csa, hca)
+    dm = CSA_PREFILL_32K_BF16.d_model
+    st = stk.Stack(layers, stack_weights(stk, layers, dm, dev, torch, 103), dm, 1, N_max=N)
+    g = torch.Generator(device=dev)
+    g.manual_seed(104)
+    x = torch.randn(1, N, dm, device=dev, generator=g).to(torch.bfloat16)
+    outs = st.prefill(x)
+    torch.cuda.synchronize()
+    finite = bool(torch.isfinite(outs[-1].float()).all())
+    del outs
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(iters):
+        st.prefill(x)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    return {"layers": [L.kind for L in layers], "tokens": N, "ms": ms, "tokens_per_s": N / (ms * 1e-3),
+            "outputs_finite": finite}
 
 
 def build_caches(wl, dev, sk, torch, gen, tail: int = 0):
@@ -643,6 +798,11 @@ def main():
     if args.only == "1m":
         print(json.dumps({"decode_1m_fp8": decode_1m_rate("cuda:0", sk, torch, gen)}))
         return
+    if args.only == "stack":
+        print(json.dumps({"prefill_hca_attend": prefill_hca_attend_rate("cuda:0", sk, torch, PAIR_DEC_128K_BF16),
+                          "stack_prefill": stack_prefill_rate("cuda:0", sk, torch),
+                          "stack_decode": stack_decode_rate("cuda:0", sk, torch)}))
+        return
 
     wl = PAIR_DEC_128K_BF16 if args.batch is None else PAIR_DEC_128K_BF16.with_sizes(B=args.batch)
     dev = "cuda:0"
@@ -766,6 +926,14 @@ def main():
         rec["prefill_attend"] = prefill_attend_rate(dev, sk, torch, CSA_PREFILL_32K_BF16)
         torch.cuda.empty_cache()
         rec["prefill_projections"] = prefill_projection_rate(dev, sk, torch, CSA_PREFILL_32K_BF16)
+    if not args.no_stack:
+        print("[bench] HCA prefill attention and the layer stack (prefill, decode)", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+        rec["prefill_hca_attend"] = prefill_hca_attend_rate(dev, sk, torch, wl)
+        torch.cuda.empty_cache()
+        rec["stack_prefill"] = stack_prefill_rate(dev, sk, torch)
+        torch.cuda.empty_cache()
+        rec["stack_decode"] = stack_decode_rate(dev, sk, torch)
     if not args.no_1m:
         print("[bench] 1M-context fp8 decode step", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
