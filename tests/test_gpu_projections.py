@@ -382,3 +382,35 @@ def test_prefill_streams_full_size_sampled():
     for k, wn in (("v", "W_c"), ("g", "W_g"), ("vI", "W_cI"), ("gI", "W_gI")):
         assert torch.isfinite(outs[k].float()).all(), k
         check(host(outs[k][torch.from_numpy(rows).to(DEV)]), method.project(xs, w[wn]), dot_bound(xs, w[wn]), True, k)
+
+
+@pytest.mark.parametrize("R", [1, 3, 40])
+def test_projections_smallest_shapes(R):
+    """d_model = 128 (one k-step per wave, four-wave blocks) and a 128-dim latent
+    with W_UV over 128: the smallest reduction lengths the library takes."""
+    rng = np.random.default_rng(R)
+    dm, H, d_h, D = 128, 2, 64, 128
+    Wq = bf16(rng.standard_normal((H * d_h, dm)).astype(np.float32) / np.sqrt(dm))
+    WUK = bf16(rng.standard_normal((H, d_h, D)).astype(np.float32) / np.sqrt(D))
+    Wc = bf16(rng.standard_normal((D, dm)).astype(np.float32) / np.sqrt(dm))
+    WUV = bf16(rng.standard_normal((H, d_h, D)).astype(np.float32) / np.sqrt(D))
+    Wo = bf16(rng.standard_normal((dm, H * d_h)).astype(np.float32) / np.sqrt(H * d_h))
+    x = hidden_rows(R, dm, 9)
+    q = torch.full((R, H, D), float("nan"), device=DEV)
+    v = torch.full((R, D), float("nan"), device=DEV)
+    sk.layer_inputs(up(x), up(Wq), q, W_UK=up(WUK), W_c=up(Wc), v=v)
+    torch.cuda.synchronize()
+    qh = method.project(x, Wq).reshape(R, H, d_h)
+    bqh = dot_bound(x, Wq).reshape(R, H, d_h)
+    check(host(q), method.absorb_queries(qh, WUK), absorbed_bound(qh, bqh, WUK), False, "q")
+    check(host(v), method.project(x, Wc), dot_bound(x, Wc), False, "v")
+    o = bf16(rng.standard_normal((R, H, D)).astype(np.float32) * 0.5)
+    y = torch.full((R, dm), float("nan"), device=DEV)
+    sk.layer_output(up(o), up(Wo), y, W_UV=up(WUV))
+    torch.cuda.synchronize()
+    heads = head_outputs(o, WUV)
+    b1 = D * U32 * np.einsum("hkd,rhd->rhk", np.abs(WUV), np.abs(o))
+    e1 = (b1 + U16 * (np.abs(heads) + b1)).reshape(R, -1)
+    bound = e1 @ np.abs(Wo).T + H * d_h * U32 * ((np.abs(heads).reshape(R, -1) + e1) @ np.abs(Wo).T)
+    y_ora = np.stack([method.layer_output(o[r], Wo, WUV) for r in range(R)])
+    check(host(y), y_ora, bound, False, "y")
