@@ -727,17 +727,58 @@ def algorithmic_bytes(wl):
             "step": score + topk + csa_att + hca_att}
 
 
+def hbm_read_reference(torch, dev, gib: int = 2, iters: int = 10):
+    """Plain streaming references on the same GPU, timed with HIP events: torch's sum
+    over a bf16 tensor of `gib` GiB (each byte read once) and a device copy of that
+    tensor (each byte read once and written once).  `GBps` is the faster of the two."""
+    x = torch.ones(gib * (1 << 30) // 2, dtype=torch.bfloat16, device=dev)
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+
+    def rate(fn, nbytes):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(iters):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return nbytes / (e0.elapsed_time(e1) / iters * 1e-3) / 1e9
+
+    nb = x.numel() * 2
+    read = rate(lambda: x.sum(), nb)
+    copy = rate(lambda: y.copy_(x), 2 * nb)
+    del x, y
+    return {"sum_read_GBps": read, "copy_GBps": copy, "bytes": nb, "GBps": max(read, copy)}
+
+
+def host_cpu():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    return {"cpu_count": os.cpu_count(), "model": model}
+
+
 def cpu_baseline(wl, budget_s: float):
-    """The oracle (numpy fp64) on one sequence of the same workload, timed on the host."""
+    """The oracle (numpy fp64) on one sequence of the same workload, timed on the host
+    with all BLAS threads and with one."""
     import numpy as np
 
     from oracle import method, pipeline
     from workloads import gen
 
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
+        threadpool_limits = None
         cores = os.cpu_count()
     csa, hca = wl.layers
     t0 = time.time()
@@ -764,9 +805,26 @@ def cpu_baseline(wl, budget_s: float):
         el = time.time() - t1
         if el >= budget_s:
             break
+    one = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            n1, t2 = 0, time.time()
+            while True:
+                for L, caches, v, q in prep:
+                    if L.kind == "csa":
+                        pipeline.decode_row(L, caches, v, q["q"][0], t, q["qI"][0], q["w"][0])
+                    else:
+                        pipeline.decode_row(L, caches, v, q["q"][0], t)
+                n1 += 1
+                el1 = time.time() - t2
+                if el1 >= budget_s / 2:
+                    break
+        one = n1 / el1
     return {"value": n / el, "unit": "queries/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{n} decode queries of sequence 0 (CSA top-{csa.k} + HCA, fp64 numpy) in {el:.1f} s; "
-                      f"cache preparation {setup_s:.0f} s untimed"}
+            "value_1thread": one, "host": host_cpu(),
+            "sample": f"{n} decode queries of sequence 0 (CSA top-{csa.k} + HCA, fp64 numpy) in {el:.1f} s with "
+                      f"{int(cores)} threads (and {budget_s / 2:.0f} s on one thread); cache preparation "
+                      f"{setup_s:.0f} s untimed"}
 
 
 def main():
@@ -910,6 +968,10 @@ def main():
                      "traffic": counter_traffic(TRAFFIC_SUMMARY), "bytes_per_launch": ab["score"] * B},
         "wall_s_timed": wall,
     }
+    rd = hbm_read_reference(torch, dev)
+    rec["hbm_read_reference"] = rd
+    rec["step_frac_of_read"] = step_gbps / rd["GBps"]
+    rec["roofline"]["frac_of_read"] = score_gbps / rd["GBps"]
     if not args.no_append:
         print("[bench] steady-state decode with appends", file=sys.stderr, flush=True)
         rec["decode_append"] = decode_append_rate(dev, sk, torch, wl, c0, h0, tails, weights, qc, qh)
