@@ -385,6 +385,14 @@ __device__ __forceinline__ void block_sources_batched(const AttendParams& p, con
   }
 }
 
+// Chunk permutation of a staged row (row index within the stage, low four
+// bits): bits 0 and 1 of the row go to chunk bits 1 and 2, bit 2 to chunk bit 3,
+// and bit 2 xor bit 3 to chunk bit 0.  It stays within aligned groups of 16
+// chunks, so a row's copy still reads whole 256-byte segments.
+__device__ __forceinline__ int chunk_swizzle(int r) {
+  return (((r >> 2) ^ (r >> 3)) & 1) | ((r & 3) << 1) | (((r >> 2) & 1) << 3);
+}
+
 // bf16 entries and window with D = 512 (the MLA-style latent), 64 heads: items
 // travel global -> LDS by asynchronous copies (one 1 KB row per wavefront
 // instruction) into four 32-item stages, so three chunks are in flight while a
@@ -412,7 +420,7 @@ __device__ __forceinline__ void block_sources_batched(const AttendParams& p, con
 // normaliser (and the log-sum-exp) sums the unrounded fp32 probabilities.
 __global__ __launch_bounds__(512) void attend_dma512(AttendParams p) {
   constexpr int NW = 8, D = 512, DH = D / 2, CH = 32, KSQ = DH / 32, ND = DH / 16;
-  constexpr int KRS = D + 8;                 // padded LDS row (bf16 elements): row stride = 4 banks
+  constexpr int KRS = D;                     // LDS row (bf16 elements), 16-byte chunks swizzled per row
   constexpr int NT = NW * kWave;
   constexpr int RPW = CH / NW;               // rows copied per wave per chunk
   constexpr int NSTG = 4;
@@ -471,9 +479,18 @@ __global__ __launch_bounds__(512) void attend_dma512(AttendParams p) {
   // every staged value is finite; their logits are masked
   const int32_t t_slot = (int32_t)(ri.t % p.R_w);
 
-  // per-lane LDS byte offsets within a stage
-  const int qk_base = (col * KRS + DH * dh + g * (DH / 4)) * 2;             // row col, dims of this half
-  const int pv_base = ((4 * g + (col >> 2)) * KRS + DH * dh + 4 * (col & 3)) * 2;  // item 4g + col/4
+  // Staged rows keep their 16-byte chunks permuted: logical chunk c of row r
+  // sits at chunk c ^ chunk_swizzle(r).  Eight consecutive rows then start in
+  // eight different bank groups (the Q.K^T reads, one chunk of 16 rows per
+  // instruction) and the four or eight rows of a transposing read group take
+  // disjoint 32-byte bank spans (P.V, two chunks per row), with 32 or 64 banks.
+  // Per-lane LDS byte offsets within a stage:
+  const int fq = chunk_swizzle(col);                                        // Q.K^T: row col (+16)
+  const int qk_row = col * KRS * 2 + (32 * dh + 16 * (g >> 1) + (8 * (g & 1) ^ (fq & 8))) * 16;
+  const int pv_r = 4 * g + (col >> 2);                                      // P.V: item 4g + col/4 (+16)
+  const int fv = chunk_swizzle(pv_r);
+  const int pv_row = pv_r * KRS * 2 + 32 * dh * 16 + 8 * (col & 1);
+  const int pv_h = (col >> 1) & 1;                                          // second chunk of the 32-byte span
   const lds_ptr lds0 = (lds_ptr)stg;
 
   // copies of chunk q_rel (relative to the segment's sources) into stage st
@@ -485,7 +502,7 @@ __global__ __launch_bounds__(512) void attend_dma512(AttendParams p) {
       const int32_t sv = __builtin_amdgcn_readlane(my_src, i);    // one row per instruction
       const gbytes src = sv >= 0 ? gent_row + (int64_t)sv * (D * 2)
                                  : gwin_row + (int64_t)(sv <= -2 ? -2 - sv : t_slot) * (D * 2);
-      copy_to_lds16(src + l * 16, &stg[st * STG + c * KRS]);
+      copy_to_lds16(src + ((l ^ chunk_swizzle(c)) << 4), &stg[st * STG + c * KRS]);
     }
   };
 
@@ -517,7 +534,7 @@ __global__ __launch_bounds__(512) void attend_dma512(AttendParams p) {
       // S^T = K Q^T over this wave's latent half, in four independent
       // accumulators (2 item tiles x even/odd k-steps); fragments read in
       // batches of 4 k-steps, one batch ahead
-      const uint8_t* sb = reinterpret_cast<const uint8_t*>(&stg[st * STG]) + qk_base;
+      const uint8_t* sb = reinterpret_cast<const uint8_t*>(&stg[st * STG]) + qk_row;
       f32x4 sacc[2][2];
 #pragma unroll
       for (int i = 0; i < 4; ++i) sacc[i >> 1][i & 1] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -529,7 +546,7 @@ __global__ __launch_bounds__(512) void attend_dma512(AttendParams p) {
 #pragma unroll
           for (int j = 0; j < KB; ++j)
             f[mt * KB + j] = bitcast<bf16x8>(
-                *reinterpret_cast<const u32x4*>(sb + (mt * 16 * KRS + 8 * (KB * b + j)) * 2));
+                *reinterpret_cast<const u32x4*>(sb + mt * 16 * KRS * 2 + (((KB * b + j) ^ (fq & 7)) << 4)));
       };
       read_batch(0, fa[0]);
 #pragma unroll
@@ -597,11 +614,12 @@ __global__ __launch_bounds__(512) void attend_dma512(AttendParams p) {
           for (int i = 0; i < 4; ++i) o[nd][i] *= al[i];
       }
       // O += P V over this wave's latent half: B fragments by transposing reads
-      const int vb = st * STG * 2 + pv_base;
+      const int vb = st * STG * 2 + pv_row;
 #pragma unroll
       for (int nd = 0; nd < ND; ++nd) {
-        const u32x2 lo = lds_read_tr16(lds0, vb + 32 * nd);
-        const u32x2 hi = lds_read_tr16(lds0, vb + 32 * nd + 16 * KRS * 2);
+        const int off = vb + ((16 * (nd >> 3) + ((2 * (nd & 7) + pv_h) ^ fv)) << 4);
+        const u32x2 lo = lds_read_tr16(lds0, off);
+        const u32x2 hi = lds_read_tr16(lds0, off + 16 * KRS * 2);
         const bf16x8 vb = bitcast<bf16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
         o[nd] = mfma16_bf16(pa, vb, o[nd]);
         o[nd] = mfma16_bf16(pl, vb, o[nd]);
