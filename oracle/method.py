@@ -102,10 +102,17 @@ def store_entries(c, store: str) -> Dict[str, Optional[np.ndarray]]:
 
 
 def store_keys(c, store: str) -> Dict[str, Optional[np.ndarray]]:
-    """Indexer keys: like entries, but e4m3 keys carry no scale (saturating RNE of c)."""
+    """Indexer keys: like entries, but e4m3 keys carry no scale (saturating RNE of c),
+    and "mxfp4" stores FP4 blocks of 32 channels with one power-of-two scale each
+    (the indexer's FP4 keys: knightli.com DeepSeek-V4 KV-cache article, section
+    "FP8 y FP4 reducen aun mas el costo de cache"; block format as in codecs).
+    mxfp4 returns scale = the uint8 scale bytes [n][D/32]."""
     if store == "e4m3":
         r = codecs.round_e4m3(c)
         return {"values": r, "codes": codecs.e4m3_encode(r), "scale": None}
+    if store == "mxfp4":
+        values, codes, scale = codecs.mxfp4_quantize(c)
+        return {"values": values, "codes": codes, "scale": scale}
     return store_entries(c, store)
 
 
