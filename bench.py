@@ -44,7 +44,8 @@ def parse():
     ap.add_argument("--no-append", action="store_true", help="skip the steady-state decode-with-appends measurement")
     ap.add_argument("--no-layer", action="store_true", help="skip the whole-layer decode step (projections) measurement")
     ap.add_argument("--no-stack", action="store_true", help="skip the HCA prefill and the layer-stack measurements")
-    ap.add_argument("--only", choices=["prefill", "1m", "layer", "stack"], default=None,
+    ap.add_argument("--no-fp4", action="store_true", help="skip the decode step with MXFP4 indexer keys")
+    ap.add_argument("--only", choices=["prefill", "1m", "layer", "stack", "fp4"], default=None,
                     help="run only that side measurement and print its record (for profiling its kernels)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy (reference for the HBM byte counters)")
@@ -368,10 +369,11 @@ def stack_prefill_rate(dev, sk, torch, n_layers: int = 4, N: int = 32768, iters:
             "outputs_finite": finite}
 
 
-def build_caches(wl, dev, sk, torch, gen, tail: int = 0):
+def build_caches(wl, dev, sk, torch, gen, tail: int = 0, fp4_keys: bool = False):
     """Caches of every sequence for both layers (GPU-drawn streams, library compressors).
     With tail > 0 the last `tail` tokens of every stream are returned too (third
-    value: per layer, a dict of [B][tail][D] tensors) for decode appends."""
+    value: per layer, a dict of [B][tail][D] tensors) for decode appends.  With
+    fp4_keys the indexer stream is also pooled into MXFP4 key tiles (c["keys_fp4"])."""
     B = wl.B
     csa, hca = wl.layers
     bf = torch.bfloat16
@@ -381,6 +383,8 @@ def build_caches(wl, dev, sk, torch, gen, tail: int = 0):
          "win": torch.empty(B, csa.W, csa.D, device=dev, dtype=bf)}
     h = {"entries": torch.empty(B, Eh, hca.D, device=dev, dtype=bf),
          "win": torch.empty(B, hca.W, hca.D, device=dev, dtype=bf)}
+    if fp4_keys:
+        c["keys_fp4"] = sk.Mxfp4Keys.empty(B, Ec, csa.D_I, dev)
     weights = gen.gpu_weights(wl, dev)
     wc, wh = weights
     slots = torch.arange(wl.N - csa.W, wl.N, device=dev) % csa.W
@@ -398,6 +402,10 @@ def build_caches(wl, dev, sk, torch, gen, tail: int = 0):
         ix = sk.Pool(st_c["vI"][None], st_c["gI"][None], wc["bposI"].contiguous(), c["keys"][b:b + 1],
                      layout=sk.LAYOUT_KEY_TILES)
         sk.csa_compress(kv, ix, m=csa.m, o=csa.o)
+        if fp4_keys:
+            k4 = sk.Mxfp4Keys(c["keys_fp4"].tiles[b:b + 1], csa.D_I)
+            sk.csa_compress(sk.Pool(st_c["vI"][None], st_c["gI"][None], wc["bposI"].contiguous(), k4,
+                                    layout=sk.LAYOUT_KEY_TILES), m=csa.m, o=csa.o)
         sk.hca_compress(sk.Pool(st_h["v"][None], st_h["g"][None], wh["bpos"].contiguous(), h["entries"][b:b + 1]),
                         m=hca.m, o=hca.o)
         c["win"][b, slots] = st_c["v"][wl.N - csa.W:]
@@ -711,6 +719,77 @@ def decode_1m_rate(dev, sk, torch, gen, steps: int = 20, replicas: int = 4):
             "hbm_frac": gbps / PEAK_HBM_GBPS}
 
 
+def decode_fp4_rate(dev, sk, torch, wl, c, h, qc, qh, steps: int = 50, replicas: int = 2):
+    """The 128K-context decode step with the lightning indexer's keys in MXFP4 (FP4
+    e2m1 codes in blocks of 32 channels with a power-of-two scale byte: 68 bytes per
+    128-dim key against 256 in bf16); attention caches as in the bf16 step.  Key
+    replicas are rotated as in the main step."""
+    csa, hca = wl.layers
+    B = wl.B
+    t = wl.N - 1
+    keys = [c["keys_fp4"]] + [sk.Mxfp4Keys(c["keys_fp4"].tiles.clone(), csa.D_I) for _ in range(replicas - 1)]
+    pos = torch.full((B,), t, dtype=torch.int32, device=dev)
+    rows = sk.RowSpec.decode(pos, t)
+    idx = torch.empty(B, csa.k, dtype=torch.int32, device=dev)
+    out_c = torch.empty(B, csa.H, csa.D, device=dev, dtype=torch.float32)
+    out_h = torch.empty(B, hca.H, hca.D, device=dev, dtype=torch.float32)
+    tau = 1.0 / math.sqrt(csa.d_h)
+    ws_i = sk.csa_index_topk(rows, qc["qI"], qc["w"], keys[0], idx, m=csa.m, W=csa.W, k=csa.k)
+    ws_c = sk.csa_attend(rows, qc["q"], c["entries"], idx, c["win"], out_c, m=csa.m, W=csa.W, softmax_scale=tau)
+    ws_h = sk.hca_attend(rows, qh["q"], h["entries"], h["win"], out_h, m=hca.m, W=hca.W, softmax_scale=tau)
+    cover = max(0, (t - csa.W) // csa.m)
+    scores = torch.empty(B, (cover + 63) // 64 * 64, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        sk.csa_index_topk(rows, qc["qI"], qc["w"], keys[i % len(keys)], idx, m=csa.m, W=csa.W, k=csa.k,
+                          workspace=ws_i)
+        if ev is not None:
+            ev[1].record(stream)
+        sk.csa_attend(rows, qc["q"], c["entries"], idx, c["win"], out_c, m=csa.m, W=csa.W, softmax_scale=tau,
+                      workspace=ws_c)
+        sk.hca_attend(rows, qh["q"], h["entries"], h["win"], out_h, m=hca.m, W=hca.W, softmax_scale=tau,
+                      workspace=ws_h)
+
+    for i in range(10):
+        step(i)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    topk_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record(stream)
+    for i in range(steps):
+        sk.csa_index_score(rows, qc["qI"], qc["w"], keys[i % len(keys)], scores, m=csa.m, W=csa.W, k=csa.k)
+    s1.record(stream)
+    torch.cuda.synchronize()
+    score_ms = s0.elapsed_time(s1) / steps
+    ab = algorithmic_bytes(wl)
+    key_bytes = csa.D_I // 2 + csa.D_I // 32                   # e2m1 codes + one scale byte per 32 channels
+    score_by = (cover * key_bytes + csa.H_I * csa.D_I * 2 + csa.H_I * 4) * B
+    step_by = (ab["step"] - ab["score"]) * B + score_by
+    score_gbps = score_by / (score_ms * 1e-3) / 1e9
+    step_gbps = step_by / (ms * 1e-3) / 1e9
+    return {"workload": wl.name + "_mxfp4_keys", "batch": B, "context": wl.N, "key_bytes": key_bytes,
+            "replicas": replicas, "ms_per_step": ms, "queries_per_s": B / (ms * 1e-3),
+            "index_topk_ms": topk_ms, "step_algorithmic_bytes": step_by, "step_hbm_GBps": step_gbps,
+            "step_hbm_frac": step_gbps / PEAK_HBM_GBPS,
+            "index_score": {"kernel": "index_score_decode (MXFP4 keys)", "launch_ms": score_ms,
+                            "bytes_per_launch": score_by, "achieved_GBps": score_gbps,
+                            "frac": score_gbps / PEAK_HBM_GBPS}}
+
+
 def algorithmic_bytes(wl):
     """Bytes one decode query must move (reads of the data it uses, writes of its results)."""
     csa, hca = wl.layers
@@ -870,14 +949,18 @@ def main():
     t = wl.N - 1
     print(f"[bench] building caches: B={B} N={wl.N}", file=sys.stderr, flush=True)
     tb = time.time()
-    c0, h0, tails, weights = build_caches(wl, dev, sk, torch, gen, tail=256)
-    reps = [(c0, h0)] + [({k: v.clone() for k, v in c0.items()}, {k: v.clone() for k, v in h0.items()})
-                         for _ in range(args.replicas - 1)]
+    fp4 = (not args.no_fp4 and args.only is None) or args.only == "fp4"
+    c0, h0, tails, weights = build_caches(wl, dev, sk, torch, gen, tail=256, fp4_keys=fp4)
+    reps = [(c0, h0)] + [({k: v.clone() for k, v in c0.items() if k != "keys_fp4"},
+                          {k: v.clone() for k, v in h0.items()}) for _ in range(args.replicas - 1)]
     qc = gen.gpu_queries(wl, 0, B, dev)
     qh = gen.gpu_queries(wl, 1, B, dev)
     print(f"[bench] caches ready in {time.time() - tb:.1f} s", file=sys.stderr, flush=True)
     if args.only == "layer":
         print(json.dumps({"decode_layer": decode_layer_rate(dev, sk, torch, wl, c0, h0, weights)}), flush=True)
+        return
+    if args.only == "fp4":
+        print(json.dumps({"decode_fp4_keys": decode_fp4_rate(dev, sk, torch, wl, c0, h0, qc, qh)}), flush=True)
         return
 
     pos = torch.full((B,), t, dtype=torch.int32, device=dev)
@@ -976,6 +1059,9 @@ def main():
         print("[bench] steady-state decode with appends", file=sys.stderr, flush=True)
         rec["decode_append"] = decode_append_rate(dev, sk, torch, wl, c0, h0, tails, weights, qc, qh)
     del tails
+    if fp4:
+        print("[bench] decode step with MXFP4 indexer keys", file=sys.stderr, flush=True)
+        rec["decode_fp4_keys"] = decode_fp4_rate(dev, sk, torch, wl, c0, h0, qc, qh)
     if not args.no_layer:
         print("[bench] whole decode layer step (projections in and out)", file=sys.stderr, flush=True)
         rec["decode_layer"] = decode_layer_rate(dev, sk, torch, wl, c0, h0, weights)

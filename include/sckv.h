@@ -55,7 +55,15 @@ extern "C" {
 
 #define SCKV_ABI_VERSION 1
 
-typedef enum { SCKV_F32 = 0, SCKV_BF16 = 1, SCKV_E4M3 = 2 } sckv_dtype;
+/* SCKV_MXFP4: FP4 indexer keys.  The pages say only that the CSA lightning
+ * indexer uses FP4 (knightli.com DeepSeek-V4 KV-cache article, section "FP8 y FP4
+ * reducen aun mas el costo de cache"); the format taken is OCP MXFP4: e2m1
+ * elements (values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives) in blocks of
+ * 32 consecutive channels sharing one E8M0 scale byte s (scale 2^(s - 127)).
+ * The compressor sets s - 127 = floor(log2 max|c|) - 2 over the block, clamped to
+ * [-127, 127] (-127 for an all-zero block), and rounds c / 2^(s - 127) to e2m1 to
+ * nearest, ties to even, saturating at 6.  Layout: see the key tiles below. */
+typedef enum { SCKV_F32 = 0, SCKV_BF16 = 1, SCKV_E4M3 = 2, SCKV_MXFP4 = 3 } sckv_dtype;
 
 typedef enum {
   SCKV_OK = 0,
@@ -92,7 +100,13 @@ typedef struct {
  * that one load instruction of a wavefront reads two contiguous runs of
  * 32 x 8 elements:  [B][E_cap / 32][D_I / 8][32][8], i.e. entry j, dim d of a
  * sequence sits at element ((j / 32 * (D_I / 8) + d / 8) * 32 + j % 32) * 8 + d % 8.
- * E_cap of a key cache must be a multiple of 32. */
+ * E_cap of a key cache must be a multiple of 32.
+ * MXFP4 key caches (D_I a multiple of 32) use tiles of their own: per sequence
+ * E_cap / 32 tiles of 17 * D_I bytes, each holding the codes [D_I/32][32][16]
+ * (block b of key n as 16 bytes: its 32 codes two per byte, the even channel in
+ * the low nibble) followed by the scales [32][D_I/32] (one byte per block), i.e.
+ * code byte (j/32) * 17 D_I + ((d/32) * 32 + j%32) * 16 + (d%32)/2 and scale byte
+ * (j/32) * 17 D_I + 16 D_I + (j%32) * (D_I/32) + d/32. */
 typedef enum { SCKV_LAYOUT_ROWS = 0, SCKV_LAYOUT_KEY_TILES = 1 } sckv_layout;
 
 /* ------------------------------------------------------------------ compression
@@ -103,7 +117,9 @@ typedef enum { SCKV_LAYOUT_ROWS = 0, SCKV_LAYOUT_KEY_TILES = 1 } sckv_layout;
  *               SCKV_LAYOUT_ROWS [B][E_cap][D] or SCKV_LAYOUT_KEY_TILES (see above)
  *   out_scale : E4M3 only.  Non-NULL: [B][E_cap] fp32 per-entry scale, written as
  *               fp32(max_d |c_j[d]| / 448) (1 for an all-zero entry), codes are
- *               E4M3(c / scale).  NULL: unscaled E4M3(c) (indexer keys). */
+ *               E4M3(c / scale).  NULL: unscaled E4M3(c) (indexer keys).
+ *   out_dtype SCKV_MXFP4 (indexer keys) needs SCKV_LAYOUT_KEY_TILES, D >= 32 and
+ *               out_scale NULL: the block scales sit inside the tiles. */
 typedef struct {
   const void* val;
   const void* gate;
@@ -184,7 +200,9 @@ sckv_status hca_append(int32_t B, int32_t m, int32_t o, const sckv_append_stream
  *   q         : [R][H_I][D_I] indexer queries (q_dtype F32 or BF16)
  *   w         : [R][H_I] fp32 head weights w_h
  *   keys      : indexer keys in SCKV_LAYOUT_KEY_TILES [B][E_cap/32][D_I/8][32][8]
- *               (key_dtype F32, BF16 or unscaled E4M3; E_cap a multiple of 32)
+ *               (key_dtype F32, BF16 or unscaled E4M3; E_cap a multiple of 32), or
+ *               MXFP4 tiles (key_dtype SCKV_MXFP4, BF16 queries, decode rows only:
+ *               each key is dequantised exactly to bf16 and scored as bf16 keys are)
  *   out_idx   : [R][k] int32: the kept entries of each row in ascending order,
  *               then -1 padding (k' = min(k, E_vis) entries are kept; E_vis = 0
  *               gives an all -1 row)

@@ -13,7 +13,7 @@ import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsckv.so")
 
-F32, BF16, E4M3 = 0, 1, 2
+F32, BF16, E4M3, MXFP4 = 0, 1, 2, 3
 ROWS_DECODE, ROWS_CAUSAL = 0, 1
 LAYOUT_ROWS, LAYOUT_KEY_TILES = 0, 1
 
@@ -195,6 +195,62 @@ class RowSpec:
 
 
 @dataclass
+class Mxfp4Keys:
+    """An MXFP4 indexer key cache: tiles uint8 [B][E_cap/32][17 * D_I], per tile of 32
+    keys the codes [D_I/32][32][16 bytes] (two e2m1 codes per byte, the even channel
+    in the low nibble) then the E8M0 scale bytes [32][D_I/32]."""
+    tiles: torch.Tensor
+    D_I: int
+
+    @staticmethod
+    def empty(B: int, E_cap: int, D_I: int, device) -> "Mxfp4Keys":
+        if E_cap % 32 or D_I % 32:
+            raise ValueError("MXFP4 key tiles need E_cap % 32 == 0 and D_I % 32 == 0")
+        return Mxfp4Keys(torch.empty(B, E_cap // 32, 17 * D_I, dtype=torch.uint8, device=device), D_I)
+
+    @property
+    def device(self):
+        return self.tiles.device
+
+    @property
+    def E_cap(self) -> int:
+        return int(self.tiles.shape[1]) * 32
+
+
+def mxfp4_pack(codes: torch.Tensor, scale: torch.Tensor) -> Mxfp4Keys:
+    """Row-major e2m1 codes [B][E][D] (uint8 0..15) and scale bytes [B][E][D/32] ->
+    MXFP4 key tiles (E padded with zero keys to a multiple of 32).  Byte layout only."""
+    B, E, D = codes.shape
+    Ep = (E + 31) // 32 * 32
+    if Ep != E:
+        codes = torch.cat([codes, codes.new_zeros(B, Ep - E, D)], dim=1)
+        scale = torch.cat([scale, scale.new_zeros(B, Ep - E, D // 32)], dim=1)
+    T = Ep // 32
+    c = codes.to(torch.uint8).reshape(B, T, 32, D // 32, 16, 2)
+    byte = (c[..., 0] | (c[..., 1] << 4)).permute(0, 1, 3, 2, 4).reshape(B, T, 16 * D)
+    sc = scale.to(torch.uint8).reshape(B, T, D)
+    return Mxfp4Keys(torch.cat([byte, sc], dim=2).contiguous(), D)
+
+
+def mxfp4_unpack(keys: Mxfp4Keys):
+    """MXFP4 key tiles -> (codes [B][E_cap][D] uint8 0..15, scale bytes [B][E_cap][D/32])."""
+    t, D = keys.tiles, keys.D_I
+    B, T, _ = t.shape
+    byte = t[:, :, :16 * D].reshape(B, T, D // 32, 32, 16).permute(0, 1, 3, 2, 4)    # [B][T][n][blk][16]
+    codes = torch.stack([byte & 15, byte >> 4], dim=-1).reshape(B, T * 32, D)
+    scale = t[:, :, 16 * D:].reshape(B, T * 32, D // 32)
+    return codes, scale
+
+
+def _out_code(out) -> int:
+    return MXFP4 if isinstance(out, Mxfp4Keys) else dtype_code(out)
+
+
+def _out_tensor(out) -> torch.Tensor:
+    return out.tiles if isinstance(out, Mxfp4Keys) else out
+
+
+@dataclass
 class Pool:
     """One stream pair to pool: val, gate [B][N][D]; bpos [m+o][D] fp32;
     out [B][E_cap][D] (rows) or a key-tile cache made by key_tiles_empty();
@@ -208,9 +264,10 @@ class Pool:
 
     def c(self) -> PoolStream:
         D = int(self.val.shape[2])
-        E_cap = int(self.out.shape[1]) if self.layout == LAYOUT_ROWS else int(self.out.shape[1]) * 32
-        return PoolStream(_ptr(self.val), _ptr(self.gate), _ptr(self.bpos), _ptr(self.out), _ptr(self.out_scale),
-                          E_cap, D, dtype_code(self.val), dtype_code(self.out), self.layout)
+        out = _out_tensor(self.out)
+        E_cap = int(out.shape[1]) if self.layout == LAYOUT_ROWS else int(out.shape[1]) * 32
+        return PoolStream(_ptr(self.val), _ptr(self.gate), _ptr(self.bpos), _ptr(out), _ptr(self.out_scale),
+                          E_cap, D, dtype_code(self.val), _out_code(self.out), self.layout)
 
 
 @dataclass
@@ -231,10 +288,11 @@ class Append:
 
     def c(self) -> AppendStream:
         D = int(self.val.shape[1])
-        E_cap = int(self.out.shape[1]) if self.layout == LAYOUT_ROWS else int(self.out.shape[1]) * 32
+        out = _out_tensor(self.out)
+        E_cap = int(out.shape[1]) if self.layout == LAYOUT_ROWS else int(out.shape[1]) * 32
         return AppendStream(_ptr(self.pos), _ptr(self.val), _ptr(self.gate), _ptr(self.val_ring),
-                            _ptr(self.gate_ring), _ptr(self.bpos), _ptr(self.out), _ptr(self.out_scale), E_cap, D,
-                            int(self.val_ring.shape[1]), dtype_code(self.val), dtype_code(self.out), self.layout, 0)
+                            _ptr(self.gate_ring), _ptr(self.bpos), _ptr(out), _ptr(self.out_scale), E_cap, D,
+                            int(self.val_ring.shape[1]), dtype_code(self.val), _out_code(self.out), self.layout, 0)
 
 
 # ---------------------------------------------------------------- indexer key tiles
@@ -301,7 +359,10 @@ def hca_append(kv: Append, *, m: int = 128, o: int = 0, stream=None):
 
 
 def index_args(rows: RowSpec, q, w, keys, out_idx, *, m: int, W: int, k: int, out_score=None) -> IndexArgs:
-    """keys: a tiled key cache [B][E_cap/32][D_I/8][32][8] (see key_tiles_empty)."""
+    """keys: a tiled key cache [B][E_cap/32][D_I/8][32][8] (see key_tiles_empty) or Mxfp4Keys."""
+    if isinstance(keys, Mxfp4Keys):
+        return IndexArgs(rows.c(), _ptr(q), _ptr(w), _ptr(keys.tiles), _ptr(out_idx), _ptr(out_score), keys.E_cap,
+                         int(keys.tiles.shape[0]), int(q.shape[1]), int(q.shape[2]), dtype_code(q), MXFP4, m, W, k)
     if keys.dim() != 5:
         raise ValueError("indexer keys must be in the tiled layout [B][E_cap/32][D_I/8][32][8]")
     return IndexArgs(rows.c(), _ptr(q), _ptr(w), _ptr(keys), _ptr(out_idx), _ptr(out_score),

@@ -149,6 +149,37 @@ __device__ __forceinline__ void store_entry(const PoolState& st, int ch, int G, 
 #pragma unroll
     for (int i = 0; i < 4; ++i) r[i] = f32_to_bf16_rne(cv[2 * i]) | (f32_to_bf16_rne(cv[2 * i + 1]) << 16);
     if (active) *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + orow) = r;
+  } else if constexpr (OUT == SCKV_MXFP4) {
+    // OCP MX block of 32 channels = the 4 lanes sub = 4i .. 4i + 3 of this entry.
+    // Shared scale 2^X with X = floor(log2 max|c|) - 2 clamped to [-127, 127]
+    // (the biased fp32 exponent of the block maximum gives floor(log2); a zero or
+    // subnormal maximum gives -127).
+    float amax = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) amax = fmaxf(amax, fabsf(cv[c]));
+    amax = fmaxf(amax, shfl_xor_f(amax, 1));
+    amax = fmaxf(amax, shfl_xor_f(amax, 2));
+    int X = (int)((__float_as_uint(amax) >> 23) & 255u) - 127 - 2;
+    X = X < -127 ? -127 : (X > 127 ? 127 : X);
+    // e2m1 code of c / 2^X (exact power-of-two scaling), to nearest with ties to
+    // the even mantissa bit, saturating at 6: the count of rounding midpoints
+    // 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5 that |x| passes (a tie passes the
+    // midpoints below the even neighbours 1, 2, 4 and not those below 0.5, 1.5, 3, 6)
+    uint32_t word = 0;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float a = fabsf(ldexpf(cv[c], -X));
+      uint32_t code = (a > 0.25f ? 1u : 0u) + (a >= 0.75f ? 1u : 0u) + (a > 1.25f ? 1u : 0u) +
+                      (a >= 1.75f ? 1u : 0u) + (a > 2.5f ? 1u : 0u) + (a >= 3.5f ? 1u : 0u) + (a > 5.0f ? 1u : 0u);
+      code |= (__float_as_uint(cv[c]) >> 31) << 3;
+      word |= code << (4 * c);
+    }
+    if (active) {
+      // tile of 32 entries: codes [D/32][32][16 B], then scales [32][D/32] B
+      uint8_t* tile = static_cast<uint8_t*>(out) + (b * (E_cap >> 5) + (e >> 5)) * (17 * (int64_t)D);
+      *reinterpret_cast<uint32_t*>(tile + ((ch >> 5) * 32 + (e & 31)) * 16 + 4 * ((ch >> 3) & 3)) = word;
+      if ((ch & 31) == 0) tile[16 * D + (e & 31) * (D >> 5) + (ch >> 5)] = (uint8_t)(X + 127);
+    }
   } else {
     float scale = 1.f;
     if constexpr (SCALED) {
@@ -301,6 +332,7 @@ static hipError_t launch_in(const sckv_pool_stream& s, int32_t B, int64_t N, int
   switch (s.out_dtype) {
     case SCKV_F32: SCKV_LAUNCH(SCKV_F32, false); break;
     case SCKV_BF16: SCKV_LAUNCH(SCKV_BF16, false); break;
+    case SCKV_MXFP4: SCKV_LAUNCH(SCKV_MXFP4, false); break;
     default:
       if (s.out_scale) SCKV_LAUNCH(SCKV_E4M3, true);
       else SCKV_LAUNCH(SCKV_E4M3, false);
@@ -323,6 +355,7 @@ static hipError_t launch_append_in(const AppendK& k0, const AppendK& k1, int nst
   switch (out_dtype) {
     case SCKV_F32: SCKV_LAUNCH(SCKV_F32, false); break;
     case SCKV_BF16: SCKV_LAUNCH(SCKV_BF16, false); break;
+    case SCKV_MXFP4: SCKV_LAUNCH(SCKV_MXFP4, false); break;
     default:
       if (scaled) SCKV_LAUNCH(SCKV_E4M3, true);
       else SCKV_LAUNCH(SCKV_E4M3, false);

@@ -3,7 +3,7 @@
 // the indexer scores the compressed blocks before the top-k; the score form is
 // fixed by the CSA decode workload definition).
 //
-// MFMA path (bf16 queries; bf16 or e4m3 keys dequantised exactly to bf16): the
+// MFMA path (bf16 queries; bf16, e4m3 or MXFP4 keys dequantised exactly to bf16): the
 // contraction is [H_I x D_I] . [D_I x 32 keys] per tile, heads as M, keys as N.
 //   decode rows : (HBM-bound) v_mfma_f32_32x32x16_bf16; each lane owns one key
 //                 column and 16 head rows per 32-head tile, so the ReLU . w head
@@ -63,6 +63,41 @@ __device__ __forceinline__ void load_key_tile(gbytes keys, int64_t elem0, bf16x8
   } else {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) b[ks] = bitcast<bf16x8>(e4m3x8_to_bf16x8(gload<u32x2>(keys, elem0 + 256 * ks)));
+  }
+}
+
+// MXFP4 keys (tiles of 17 DI bytes per 32 keys: codes [DI/32][32][16 B], then
+// scales [32][DI/32] B): the same fragments as load_key_tile, dequantised exactly
+// to bf16 by the gfx950 scaled FP4 conversion (two codes per instruction, the
+// low nibble first; the block scale byte s enters as the float 2^(s - 127)).
+// Lane (n, hh) reads the 16-byte blocks DI/64 hh .. of key n and its scale bytes.
+__device__ __forceinline__ float e8m0_scale(uint32_t s) {
+  return s ? __uint_as_float(s << 23) : __uint_as_float(0x00400000u);    // 2^(s - 127); s = 0: 2^-127
+}
+
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t v, float scale) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 0));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 1));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 2));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 3));
+  return bitcast<bf16x8>(r);
+}
+
+template <int DI>
+__device__ __forceinline__ void load_fp4_tile(gbytes keys, int64_t tile_byte, int n, int hh, bf16x8 (&b)[DI / 16]) {
+  constexpr int NB = DI / 64;                  // 32-channel blocks per half of a key
+  uint32_t sc;
+  if constexpr (DI == 128) sc = gload<uint32_t>(keys, tile_byte + 16 * DI + 4 * n);
+  else sc = gload<uint16_t>(keys, tile_byte + 16 * DI + 2 * n);
+  u32x4 c[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) c[i] = gload<u32x4>(keys, tile_byte + ((NB * hh + i) * 32 + n) * 16);
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const float f = e8m0_scale((sc >> (8 * (NB * hh + i))) & 255u);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) b[4 * i + q] = fp4x8_to_bf16x8(c[i][q], f);
   }
 }
 
@@ -186,7 +221,8 @@ __global__ __launch_bounds__(256) void index_score_decode(
   auto load = [&](int t, bf16x8 (&b)[KS]) {
     int64_t key = j_begin + 32 * t + n;
     key = key < e_vis ? key : e_vis - 1;
-    load_key_tile<KEY, DI>(gkeys, key_tile_elem<DI>(key_row0 * DI, key, hh * KS), b);
+    if constexpr (KEY == SCKV_MXFP4) load_fp4_tile<DI>(gkeys, (key_row0 + (key & ~(int64_t)31)) / 32 * (17 * DI), n, hh, b);
+    else load_key_tile<KEY, DI>(gkeys, key_tile_elem<DI>(key_row0 * DI, key, hh * KS), b);
   };
   auto compute = [&](int t, const bf16x8 (&b)[KS]) {
     float part = 0.f;
@@ -373,7 +409,7 @@ static void launch_mfma(const sckv_index_args& a, float* scores, int64_t stride,
     else if (nt == 8) SCKV_DEC(8);
     else SCKV_DEC(4);
 #undef SCKV_DEC
-  } else {
+  } else if constexpr (KEY != SCKV_MXFP4) {      // MXFP4 keys: decode rows only (checked on the host)
     const dim3 grid((unsigned)((a.rows.R + 7) / 8));
     hipLaunchKernelGGL((index_score_causal_lds<KEY, HI, DI>), grid, dim3(512), 0, stream, q, a.w, a.keys, scores,
                        stride, a.E_cap, a.m, a.W, a.rows.seq0, a.rows.pos0, a.rows.R);
@@ -400,6 +436,8 @@ hipError_t launch_index_score(const sckv_index_args& a, float* scores, int64_t s
                        a.rows.kind, a.rows.pos, a.rows.pos_max, a.rows.seq0, a.rows.pos0);
   } else if (a.key_dtype == SCKV_BF16) {
     launch_mfma_key<SCKV_BF16>(a, scores, stride, cover, stream);
+  } else if (a.key_dtype == SCKV_MXFP4) {
+    launch_mfma_key<SCKV_MXFP4>(a, scores, stride, cover, stream);
   } else {
     launch_mfma_key<SCKV_E4M3>(a, scores, stride, cover, stream);
   }

@@ -35,6 +35,7 @@ const char* dtname(int32_t d) {
     case SCKV_F32: return "F32";
     case SCKV_BF16: return "BF16";
     case SCKV_E4M3: return "E4M3";
+    case SCKV_MXFP4: return "MXFP4";
     default: return "?";
   }
 }
@@ -51,13 +52,16 @@ sckv_status check_pool(const sckv_pool_stream* s, const char* name, int32_t B, i
   if (!s->val || !s->gate || !s->bpos || !s->out) return fail(SCKV_ERR_NULL, "%s: val/gate/bpos/out must be set", name);
   if (s->in_dtype != SCKV_F32 && s->in_dtype != SCKV_BF16)
     return fail(SCKV_ERR_DTYPE, "%s: in_dtype %s not supported (F32, BF16)", name, dtname(s->in_dtype));
-  if (s->out_dtype != SCKV_F32 && s->out_dtype != SCKV_BF16 && s->out_dtype != SCKV_E4M3)
+  if (s->out_dtype != SCKV_F32 && s->out_dtype != SCKV_BF16 && s->out_dtype != SCKV_E4M3 &&
+      s->out_dtype != SCKV_MXFP4)
     return fail(SCKV_ERR_DTYPE, "%s: out_dtype %d not supported", name, s->out_dtype);
   if (!pow2_dim(s->D)) return fail(SCKV_ERR_UNSUPPORTED, "%s: D=%d not in {8,...,512} (powers of two)", name, s->D);
   if (s->out_layout != SCKV_LAYOUT_ROWS && s->out_layout != SCKV_LAYOUT_KEY_TILES)
     return fail(SCKV_ERR_SHAPE, "%s: unknown out_layout %d", name, s->out_layout);
   if (s->out_layout == SCKV_LAYOUT_KEY_TILES && s->E_cap % 32 != 0)
     return fail(SCKV_ERR_SHAPE, "%s: key-tile caches need E_cap %% 32 == 0 (E_cap=%lld)", name, (long long)s->E_cap);
+  if (s->out_dtype == SCKV_MXFP4 && (s->out_layout != SCKV_LAYOUT_KEY_TILES || s->D < 32 || s->out_scale))
+    return fail(SCKV_ERR_UNSUPPORTED, "%s: MXFP4 keys need the key-tile layout, D >= 32 and no out_scale", name);
   if (B < 1 || N < 1 || m < 1 || o < 0) return fail(SCKV_ERR_SHAPE, "%s: need B>=1, N>=1, m>=1, o>=0", name);
   if (e_begin < 0 || e_count < 0) return fail(SCKV_ERR_SHAPE, "%s: e_begin/e_count must be >= 0", name);
   if ((int64_t)m * (e_begin + e_count) > N)
@@ -79,13 +83,16 @@ sckv_status check_append(const sckv_append_stream* s, const char* name, int32_t 
     return fail(SCKV_ERR_NULL, "%s: pos/val/gate/val_ring/gate_ring/bpos/out must be set", name);
   if (s->in_dtype != SCKV_F32 && s->in_dtype != SCKV_BF16)
     return fail(SCKV_ERR_DTYPE, "%s: in_dtype %s not supported (F32, BF16)", name, dtname(s->in_dtype));
-  if (s->out_dtype != SCKV_F32 && s->out_dtype != SCKV_BF16 && s->out_dtype != SCKV_E4M3)
+  if (s->out_dtype != SCKV_F32 && s->out_dtype != SCKV_BF16 && s->out_dtype != SCKV_E4M3 &&
+      s->out_dtype != SCKV_MXFP4)
     return fail(SCKV_ERR_DTYPE, "%s: out_dtype %d not supported", name, s->out_dtype);
   if (!pow2_dim(s->D)) return fail(SCKV_ERR_UNSUPPORTED, "%s: D=%d not in {8,...,512} (powers of two)", name, s->D);
   if (s->out_layout != SCKV_LAYOUT_ROWS && s->out_layout != SCKV_LAYOUT_KEY_TILES)
     return fail(SCKV_ERR_SHAPE, "%s: unknown out_layout %d", name, s->out_layout);
   if (s->out_layout == SCKV_LAYOUT_KEY_TILES && s->E_cap % 32 != 0)
     return fail(SCKV_ERR_SHAPE, "%s: key-tile caches need E_cap %% 32 == 0 (E_cap=%lld)", name, (long long)s->E_cap);
+  if (s->out_dtype == SCKV_MXFP4 && (s->out_layout != SCKV_LAYOUT_KEY_TILES || s->D < 32 || s->out_scale))
+    return fail(SCKV_ERR_UNSUPPORTED, "%s: MXFP4 keys need the key-tile layout, D >= 32 and no out_scale", name);
   if (B < 1 || m < 1 || o < 0 || s->E_cap < 1) return fail(SCKV_ERR_SHAPE, "%s: need B>=1, m>=1, o>=0, E_cap>=1", name);
   if ((int64_t)s->P < (int64_t)m + o)
     return fail(SCKV_ERR_SHAPE, "%s: P=%d ring slots < m+o=%d tokens of an entry", name, s->P, m + o);
@@ -133,12 +140,15 @@ sckv_status check_index(const sckv_index_args* a, IndexPlan* pl, bool need_out) 
                 (long long)a->E_cap, a->D_I);
   if (a->q_dtype == SCKV_F32 && a->key_dtype == SCKV_F32) {
     if ((int64_t)a->H_I * a->D_I > 8192) return fail(SCKV_ERR_UNSUPPORTED, "index: F32 path needs H_I*D_I <= 8192");
-  } else if (a->q_dtype == SCKV_BF16 && (a->key_dtype == SCKV_BF16 || a->key_dtype == SCKV_E4M3)) {
+  } else if (a->q_dtype == SCKV_BF16 &&
+             (a->key_dtype == SCKV_BF16 || a->key_dtype == SCKV_E4M3 || a->key_dtype == SCKV_MXFP4)) {
     if (!(a->H_I == 32 || a->H_I == 64) || !(a->D_I == 64 || a->D_I == 128))
       return fail(SCKV_ERR_UNSUPPORTED, "index: MFMA path needs H_I in {32,64} and D_I in {64,128} (got %d, %d)",
                   a->H_I, a->D_I);
+    if (a->key_dtype == SCKV_MXFP4 && a->rows.kind != SCKV_ROWS_DECODE)
+      return fail(SCKV_ERR_UNSUPPORTED, "index: MXFP4 keys are scored for decode rows only");
   } else {
-    return fail(SCKV_ERR_DTYPE, "index: q %s with keys %s not supported (F32/F32, BF16/BF16, BF16/E4M3)",
+    return fail(SCKV_ERR_DTYPE, "index: q %s with keys %s not supported (F32/F32, BF16/BF16, BF16/E4M3, BF16/MXFP4)",
                 dtname(a->q_dtype), dtname(a->key_dtype));
   }
   if (!aligned16(a->q) || !aligned16(a->w) || !aligned16(a->keys) || (a->out_idx && !aligned16(a->out_idx)) ||

@@ -133,3 +133,41 @@ def blocked_compress(v, g, bpos, m, o, block=16384):
         c = method.compress(v[t0:m * j1], g[t0:m * j1], bpos, m, o)
         out.append(c if j0 == 0 else c[o // m:])
     return np.concatenate(out) if out else np.zeros((0, v.shape[1]))
+
+
+def mxfp4_flips(gpu_codes, gpu_scale, ora_unrounded, magnitude, rtol=1e-5):
+    """MXFP4 blocks stored by the GPU against the oracle's rounding of the unrounded
+    values c [n][D] (magnitude [n][D]: scale of the GPU's fp32 error in c).  A block
+    scale is explained when it is the oracle's scale rule applied to some block
+    maximum within rtol * (block's largest magnitude) of the oracle's; an element
+    is explained when, under the GPU's scale, it lies between the roundings of
+    c - rtol * mag and c + rtol * mag (rounding is monotone).  Returns
+    (elements or scales that differ from the oracle's, how many are unexplained)."""
+    from oracle import codecs
+    c = np.asarray(ora_unrounded, np.float64)
+    mag = np.asarray(magnitude, np.float64)
+    n, D = c.shape
+    _, o_codes, o_scale = codecs.mxfp4_quantize(c)
+    gc = np.asarray(gpu_codes).astype(np.int64)
+    gs = np.asarray(gpu_scale).astype(np.int64)
+    nb = D // codecs.MX_BLOCK
+    cb = c.reshape(n, nb, codecs.MX_BLOCK)
+    d = rtol * mag.reshape(n, nb, codecs.MX_BLOCK)
+
+    def rule(amax):
+        _, e = np.frexp(np.where(amax > 0, amax, 1.0))
+        return np.clip(np.where(amax > 0, e - 3, -127), -127, 127) + 127
+
+    amax = np.abs(cb).max(axis=2)
+    slack = d.max(axis=2)
+    lo_s, hi_s = rule(np.maximum(amax - slack, 0.0)), rule(amax + slack)
+    scale_diff = gs != o_scale
+    scale_bad = (gs < lo_s) | (gs > hi_s)
+    X = np.ldexp(1.0, gs - 127)[:, :, None]
+    g_val = codecs.e2m1_decode(gc).reshape(n, nb, codecs.MX_BLOCK)
+    lo = codecs.round_e2m1((cb - d) / X)
+    hi = codecs.round_e2m1((cb + d) / X)
+    elem_diff = (gc != o_codes.astype(np.int64)).reshape(n, nb, codecs.MX_BLOCK) & \
+        ~((g_val == 0) & (codecs.e2m1_decode(o_codes).reshape(n, nb, codecs.MX_BLOCK) == 0) & ~scale_diff[:, :, None])
+    elem_bad = elem_diff & ((g_val < lo) | (g_val > hi))
+    return int(scale_diff.sum() + elem_diff.sum()), int(scale_bad.sum() + elem_bad.sum())

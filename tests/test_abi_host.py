@@ -4,6 +4,7 @@ import ctypes as C
 import os
 import re
 
+import numpy as np
 import pytest
 import torch
 
@@ -57,6 +58,9 @@ def err(L):
     (dict(val=None), 1), (dict(out=None), 1), (dict(in_dtype=2), 3), (dict(out_dtype=7), 3),
     (dict(D=48), 4), (dict(D=1024), 4), (dict(E_cap=3), 2), (dict(val=FAKE_ODD), 5),
     (dict(out_layout=1, E_cap=48), 2), (dict(out_layout=7), 2),
+    # MXFP4 keys: tiles only, D >= 32, no out_scale (the scales sit in the tiles)
+    (dict(out_dtype=3), 4), (dict(out_dtype=3, out_layout=1, E_cap=32, out_scale=FAKE), 4),
+    (dict(out_dtype=3, out_layout=1, E_cap=32, D=16), 4),
 ])
 def test_compress_validation(L, kw, status):
     p = pool(**kw)
@@ -88,6 +92,7 @@ def app(**kw):
     (dict(pos=None), 1), (dict(gate_ring=None), 1), (dict(val_ring=None), 1), (dict(in_dtype=2), 3),
     (dict(out_dtype=9), 3), (dict(D=24), 4), (dict(P=7), 2), (dict(E_cap=0), 2),
     (dict(out_layout=1, E_cap=40), 2), (dict(gate_ring=FAKE_ODD), 5), (dict(out_scale=FAKE_ODD, out_dtype=2), 5),
+    (dict(out_dtype=3), 4),
 ])
 def test_append_validation(L, kw, status):
     a = app(**kw)
@@ -121,6 +126,9 @@ def idx_args(**kw):
     (dict(q_dtype=0, key_dtype=0, H_I=128, D_I=128), 4), (dict(keys=FAKE_ODD), 5), (dict(E_cap=1000), 2),
     (dict(rows=_lib.Rows(None, 0, 2, 4095, 0, 0, 0)), 1), (dict(rows=_lib.Rows(FAKE, 0, 3, 4095, 0, 0, 0)), 2),
     (dict(rows=_lib.Rows(None, 1, 8, 0, 2, 0, 0)), 2), (dict(rows=_lib.Rows(None, 5, 8, 0, 0, 0, 0)), 2),
+    # MXFP4 keys: bf16 queries and decode rows only
+    (dict(key_dtype=3, q_dtype=0), 3), (dict(key_dtype=3, rows=_lib.Rows(None, 1, 8, 0, 0, 0, 0)), 4),
+    (dict(key_dtype=3, D_I=96), 4),
 ])
 def test_index_validation(L, kw, status):
     a = idx_args(**kw)
@@ -273,3 +281,27 @@ def test_inputs_validation_and_workspace(L):
     assert L.layer_inputs(C.byref(q), C.byref(sargs(R=31)), FAKE, 1 << 30, None) == 2
     assert L.layer_inputs(C.byref(qargs(q=None)), C.byref(st), FAKE, 1 << 30, None) == 1
     assert L.layer_inputs(C.byref(q), C.byref(sargs(out_dtype=2)), FAKE, 1 << 30, None) == 3
+
+
+def test_mxfp4_key_tiles_layout():
+    """mxfp4_pack / mxfp4_unpack follow the byte layout the header states: code byte
+    (j/32) * 17 D + ((d/32) * 32 + j%32) * 16 + (d%32)/2 (even channel in the low
+    nibble), scale byte (j/32) * 17 D + 16 D + (j%32) * (D/32) + d/32."""
+    import torch
+    rng = np.random.default_rng(5)
+    for B, E, D in [(2, 70, 64), (1, 32, 128), (1, 5, 32)]:
+        codes = rng.integers(0, 16, size=(B, E, D), dtype=np.uint8)
+        scale = rng.integers(0, 255, size=(B, E, D // 32), dtype=np.uint8)
+        keys = _lib.mxfp4_pack(torch.from_numpy(codes), torch.from_numpy(scale))
+        t = keys.tiles.numpy()
+        assert t.shape == (B, (E + 31) // 32, 17 * D) and keys.E_cap == (E + 31) // 32 * 32
+        for b in range(B):
+            for j in range(E):
+                base = t[b, j // 32]
+                for d in range(D):
+                    byte = base[((d // 32) * 32 + j % 32) * 16 + (d % 32) // 2]
+                    assert ((byte >> 4) if d % 2 else (byte & 15)) == codes[b, j, d]
+                for blk in range(D // 32):
+                    assert base[16 * D + (j % 32) * (D // 32) + blk] == scale[b, j, blk]
+        c2, s2 = _lib.mxfp4_unpack(keys)
+        assert np.array_equal(c2.numpy()[:, :E], codes) and np.array_equal(s2.numpy()[:, :E], scale)

@@ -23,7 +23,7 @@ import pytest
 import torch
 
 from oracle import method
-from tests.compare import assert_close, bf16_code_flips, blocked_compress, e4m3_flips, topk_parity
+from tests.compare import assert_close, bf16_code_flips, blocked_compress, e4m3_flips, mxfp4_flips, topk_parity
 from tests.gpu_util import DEV, dev, dev_codes, dev_i32, host
 from workloads import (CSA_DEC_4K_F32, CSA_PREFILL_32K_BF16, HCA_DEC_64K_BF16, PAIR_DEC_1M_FP8,
                        PAIR_DEC_128K_BF16, gen)
@@ -249,6 +249,57 @@ def test_pair_decode_128k_bf16():
         rh = method.hca_row(t, f32(qh["q"][b]), ent_h, vh, hca.m, hca.W, tau)
         eh = assert_close(host(out_h[b]), rh["o"], atol=2e-2, what=f"HCA output seq {b}")
         print(f"  seq {b}: CSA max abs err {ec:.2e}, HCA {eh:.2e}", flush=True)
+
+
+# ---------------------------------------------------------------- the same step with MXFP4 indexer keys
+def test_pair_decode_128k_mxfp4_keys():
+    """The 128K batch-32 step with the indexer keys pooled into MXFP4 tiles by the
+    timed step's builder: stored blocks against the oracle's (scales and codes, flips
+    only where the fp32 pooling error explains them), then the step's top-k and CSA
+    output against the oracle on the oracle's keys."""
+    import bench
+    wl = PAIR_DEC_128K_BF16
+    csa, hca = wl.layers
+    B, t = wl.B, wl.N - 1
+    print(f"{wl.name} with MXFP4 indexer keys: B={B} N={wl.N}", flush=True)
+    c, h = bench.build_caches(wl, DEV, sk, torch, gen, fp4_keys=True)
+    keys = c["keys_fp4"]
+    weights = gen.gpu_weights(wl, DEV)
+    qc = gen.gpu_queries(wl, 0, B, DEV)
+    sampled = [0, B - 1]
+    ora = {}
+    codes_all, scale_all = sk.mxfp4_unpack(keys)
+    for b in sampled:
+        s_c, _ = gen.gpu_sequence_streams(wl, b, weights, DEV)
+        vc = f32(s_c["v"])
+        cI = blocked_compress(f32(s_c["vI"]), f32(s_c["gI"]), f32(weights[0]["bposI"]), csa.m, csa.o)
+        magI = blocked_compress(np.abs(f32(s_c["vI"])), f32(s_c["gI"]), f32(weights[0]["bposI"]), csa.m, csa.o)
+        del s_c
+        E = cI.shape[0]
+        n_diff, n_un = mxfp4_flips(codes_all[b, :E].cpu().numpy(), scale_all[b, :E].cpu().numpy(), cI, magI)
+        assert n_un == 0, f"seq {b}: {n_un} of {n_diff} MXFP4 scales/codes unexplained"
+        print(f"  seq {b}: {n_diff} MXFP4 flips explained by the fp32 pooling error", flush=True)
+        st = method.store_keys(cI, "mxfp4")
+        keys.tiles[b:b + 1] = sk.mxfp4_pack(torch.from_numpy(st["codes"])[None],
+                                            torch.from_numpy(st["scale"])[None]).tiles.to(DEV)
+        ent = c["entries"][b].float().cpu().numpy().astype(np.float64)
+        ora[b] = (vc, ent, st["values"])
+    rows = sk.RowSpec.decode(torch.full((B,), t, dtype=torch.int32, device=DEV), t)
+    idx = torch.empty(B, csa.k, dtype=torch.int32, device=DEV)
+    out_c = torch.empty(B, csa.H, csa.D, device=DEV)
+    tau = tau_of(csa)
+    sk.csa_index_topk(rows, qc["qI"], qc["w"], keys, idx, m=csa.m, W=csa.W, k=csa.k)
+    sk.csa_attend(rows, qc["q"], c["entries"], idx, c["win"], out_c, m=csa.m, W=csa.W, softmax_scale=tau)
+    torch.cuda.synchronize()
+    gi = host(idx)
+    for b in sampled:
+        vc, ent_c, keys_c = ora[b]
+        r = method.csa_row(t, f32(qc["q"][b]), f32(qc["qI"][b]), qc["w"][b].cpu().numpy(), ent_c, keys_c, vc,
+                           csa.m, csa.W, csa.k, tau)
+        ok, msg = topk_parity(gi[b], r["idx"], r["scores"])
+        assert ok, f"seq {b}: {msg}"
+        ec = assert_close(host(out_c[b]), r["o"], atol=2e-2, what=f"CSA output seq {b}")
+        print(f"  seq {b}: top-k matches, CSA max abs err {ec:.2e}", flush=True)
 
 
 # ---------------------------------------------------------------- CSA+HCA pair decode at 1M, fp8 caches

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 from oracle import codecs, method
-from tests.compare import assert_close, assert_scores_close, bf16_code_flips, e4m3_flips, topk_parity
+from tests.compare import assert_close, assert_scores_close, bf16_code_flips, e4m3_flips, mxfp4_flips, topk_parity
 from tests.gpu_util import DEV, dev, dev_codes, dev_i32, host, rng_store
 
 pytestmark = pytest.mark.gpu
@@ -119,6 +119,33 @@ def test_compress_key_tiles(ins, outs, D, B, N):
             assert e4m3_flips(got, st["codes"], c, mag)[1] == 0
 
 
+@pytest.mark.parametrize("ins,D,B,N", [("bf16", 128, 2, 4096), ("f32", 64, 1, 1030), ("bf16", 32, 1, 600)])
+def test_compress_mxfp4_keys(ins, D, B, N):
+    """FP4 indexer keys: the GPU's MXFP4 blocks against the oracle's, block scales and
+    e2m1 codes, with flips only where the fp32 pooling error can cross a rounding
+    boundary or a power of two."""
+    print(f"compress mxfp4 keys {ins} D={D} B={B} N={N}", flush=True)
+    rng = np.random.default_rng(17 + D + N)
+    v, g = rng_store(rng, (B, N, D), ins), rng_store(rng, (B, N, D), ins, 2.0)
+    v[:, :8] = 0.0                                   # zero tokens: the first entry's blocks are all zero
+    bpos = rng.normal(0, 0.5, (8, D)).astype(np.float32)
+    E = N // 4
+    keys = sk.Mxfp4Keys.empty(B, (E + 31) // 32 * 32, D, DEV)
+    keys.tiles.fill_(0x5A)
+    vd, gd, bd = dev(v, ins), dev(g, ins), dev(bpos)
+    sk.csa_compress(sk.Pool(vd, gd, bd, keys, layout=sk.LAYOUT_KEY_TILES), m=4, o=4)
+    torch.cuda.synchronize()
+    codes, scale = (t.cpu().numpy() for t in sk.mxfp4_unpack(keys))
+    for b in range(B):
+        c = method.compress(v[b], g[b], bpos, 4, 4)
+        mag = method.compress(np.abs(v[b]), g[b], bpos, 4, 4)
+        n_diff, n_un = mxfp4_flips(codes[b, :E], scale[b, :E], c, mag)
+        assert n_un == 0, f"seq {b}: {n_un} of {n_diff} MXFP4 scales/codes unexplained"
+        assert n_diff <= 1e-3 * E * D, f"seq {b}: {n_diff} flips"
+        st = method.store_keys(c, "mxfp4")
+        assert np.all(scale[b, 0] == 0) and np.all(st["scale"][0] == 0)          # the all-zero entry
+
+
 APPEND_CASES = [
     # m, o, D, in, out, scaled, key tiles, B, N, ring slots P
     (4, 4, 64, "bf16", "bf16", False, False, 3, 600, 8),
@@ -202,6 +229,32 @@ def test_append_token_by_token(m, o, D, ins, outs, scaled, tiled, B, N, P):
         assert e4m3_flips(got, st["codes"], y, ymag)[1] == 0
 
 
+def test_append_mxfp4_keys_match_bulk():
+    """MXFP4 indexer keys appended token by token equal the bulk compressor's tiles
+    byte for byte (entries whose window is complete)."""
+    B, N, D, P = 2, 300, 128, 8
+    print(f"append mxfp4 B={B} N={N} D={D}", flush=True)
+    rng = np.random.default_rng(41)
+    v, g = rng_store(rng, (B, N, D), "bf16"), rng_store(rng, (B, N, D), "bf16", 2.0)
+    bpos = rng.normal(0, 0.5, (8, D)).astype(np.float32)
+    E = N // 4
+    E_cap = (E + 31) // 32 * 32
+    vd, gd, bd = dev(v, "bf16"), dev(g, "bf16"), dev(bpos)
+    ka, kb = sk.Mxfp4Keys.empty(B, E_cap, D, DEV), sk.Mxfp4Keys.empty(B, E_cap, D, DEV)
+    ka.tiles.zero_()
+    kb.tiles.zero_()
+    rv = torch.zeros(B, P, D, device=DEV, dtype=vd.dtype)
+    rg = torch.zeros(B, P, D, device=DEV, dtype=vd.dtype)
+    ar = torch.arange(B, device=DEV)
+    for t in range(N):
+        pos = dev_i32([t] * B)
+        sk.csa_append(sk.Append(pos, vd[ar, t].contiguous(), gd[ar, t].contiguous(), rv, rg, bd, ka,
+                                layout=sk.LAYOUT_KEY_TILES), m=4, o=4)
+    sk.csa_compress(sk.Pool(vd, gd, bd, kb, layout=sk.LAYOUT_KEY_TILES), m=4, o=4)
+    torch.cuda.synchronize()
+    assert torch.equal(ka.tiles, kb.tiles)
+
+
 @pytest.mark.parametrize("kv_out,scaled", [("bf16", False), ("e4m3", True)])
 def test_csa_append_two_streams(kv_out, scaled):
     """csa_append with the latent and the indexer stream (one launch when their
@@ -267,6 +320,9 @@ INDEX_CASES = [
     ("bf16", 64, 128, 40000, [160127], 1024),
     ("bf16", 64, 128, 70000, [279999, 200000], 2048),
     ("e4m3", 64, 128, 70000, [279999], 100),
+    ("mxfp4", 64, 128, 4096, [16511, 9000, 131, 600], 1024),
+    ("mxfp4", 32, 64, 2000, [8127, 4000], 100),
+    ("mxfp4", 64, 128, 70000, [279999], 2048),
     # 40 rows over a 32K-entry cache: rows cut into 8192-entry slices, ragged row lengths
     ("bf16", 32, 64, 32768, [131071 - 997 * i for i in range(40)], 512),
 ]
@@ -276,6 +332,14 @@ def _index_inputs(rng, keys_s, HI, DI, B, E_cap):
     qs = "f32" if keys_s == "f32" else "bf16"
     q = rng_store(rng, (B, HI, DI), qs)
     w = rng.normal(0, 1, (B, HI)).astype(np.float32)
+    if keys_s == "mxfp4":
+        # per-key magnitudes spread over a few binades, so blocks take different scales
+        raw = rng.normal(0, 1, (B * E_cap, DI)) * np.ldexp(1.0, rng.integers(-3, 4, size=(B * E_cap, 1)))
+        vals, codes, scale = codecs.mxfp4_quantize(raw)
+        kv = vals.reshape(B, E_cap, DI)
+        keys = sk.mxfp4_pack(torch.from_numpy(codes.reshape(B, E_cap, DI)),
+                             torch.from_numpy(scale.reshape(B, E_cap, DI // 32)))
+        return q, w, kv, dev(q, qs), dev(w), sk.Mxfp4Keys(keys.tiles.to(DEV), DI)
     if keys_s == "e4m3":
         kv = codecs.round_e4m3(rng.normal(0, 1, (B, E_cap, DI)))
         keys_dev = dev_codes(codecs.e4m3_encode(kv))
