@@ -430,7 +430,7 @@ def decode_append_rate(dev, sk, torch, wl, c, h, tails, weights, qc, qh, steps: 
     bf = torch.bfloat16
     wc, wh = weights
     P_lat = csa.W                                          # the window ring doubles as the value ring
-    before = {k: v.clone() for k, v in c.items()}, {k: v.clone() for k, v in h.items()}
+    before = {k: v.clone() for k, v in c.items() if k != "keys_fp4"}, {k: v.clone() for k, v in h.items()}
     tl_c, tl_h = tails
     T = tl_c["v"].shape[1]
     # rings as of position t0 - 1 (slot = position mod P)
@@ -488,7 +488,7 @@ def decode_append_rate(dev, sk, torch, wl, c, h, tails, weights, qc, qh, steps: 
     stream = torch.cuda.current_stream()
     run()
     torch.cuda.synchronize()
-    same_caches = all(torch.equal(before[0][k], c[k]) for k in c) and all(torch.equal(before[1][k], h[k]) for k in h)
+    same_caches = all(torch.equal(before[0][k], c[k]) for k in before[0]) and all(torch.equal(before[1][k], h[k]) for k in h)
     ref_c, ref_h = out_c.clone(), out_h.clone()
 
     def timed(fn, n):
