@@ -81,17 +81,23 @@ def counter_traffic(path: str):
         return None
 
 
-def prefill_indexer_rate(dev, sk, torch, wl, iters: int = 5):
+def prefill_indexer_rate(dev, sk, torch, wl, iters: int = 5, fp4: bool = False):
     """Indexer scoring of the 32K-token causal prefill (every row scores its visible
     entries): algorithmic bf16 flops per second on MFMA.  Keys, queries and
     weights are random with the workload's shapes (the rate does not depend on
-    the values)."""
+    the values).  fp4: the keys are MXFP4 tiles (random codes, scale bytes near
+    2^0), dequantised to bf16 inside the kernel."""
     L = wl.layers[0]
     T, E = wl.N, wl.N // L.m
     g = torch.Generator(device=dev)
     g.manual_seed(wl.seed)
     bf = torch.bfloat16
-    keys = sk.to_key_tiles(torch.randn(1, E, L.D_I, device=dev, generator=g).to(bf))
+    if fp4:
+        codes = torch.randint(0, 16, (1, E, L.D_I), device=dev, generator=g, dtype=torch.uint8)
+        scale = torch.randint(124, 130, (1, E, L.D_I // 32), device=dev, generator=g, dtype=torch.uint8)
+        keys = sk.mxfp4_pack(codes, scale)
+    else:
+        keys = sk.to_key_tiles(torch.randn(1, E, L.D_I, device=dev, generator=g).to(bf))
     qI = torch.randn(T, L.H_I, L.D_I, device=dev, generator=g).to(bf)
     w = torch.randn(T, L.H_I, device=dev, generator=g)
     cover = max(0, (T - 1 - L.W) // L.m)
@@ -111,9 +117,9 @@ def prefill_indexer_rate(dev, sk, torch, wl, iters: int = 5):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / iters
     tf = flops / (ms * 1e-3) / 1e12
-    return {"workload": wl.name, "kernel": "index_score_causal_lds", "rows": T, "visible_pairs": pairs,
-            "tflop": flops / 1e12, "ms": ms, "achieved_tflops": tf, "peak_tflops": PEAK_BF16_TFLOPS,
-            "frac": tf / PEAK_BF16_TFLOPS}
+    return {"workload": wl.name + ("_mxfp4_keys" if fp4 else ""), "kernel": "index_score_causal_lds", "rows": T,
+            "visible_pairs": pairs, "tflop": flops / 1e12, "ms": ms, "achieved_tflops": tf,
+            "peak_tflops": PEAK_BF16_TFLOPS, "frac": tf / PEAK_BF16_TFLOPS}
 
 
 def prefill_attend_rate(dev, sk, torch, wl, iters: int = 3):
@@ -928,6 +934,8 @@ def main():
 
     if args.only == "prefill":
         print(json.dumps({"prefill_indexer": prefill_indexer_rate("cuda:0", sk, torch, CSA_PREFILL_32K_BF16),
+                          "prefill_indexer_fp4": prefill_indexer_rate("cuda:0", sk, torch, CSA_PREFILL_32K_BF16,
+                                                                      fp4=True),
                           "prefill_attend": prefill_attend_rate("cuda:0", sk, torch, CSA_PREFILL_32K_BF16),
                           "prefill_projections": prefill_projection_rate("cuda:0", sk, torch,
                                                                          CSA_PREFILL_32K_BF16)}))
@@ -1070,6 +1078,8 @@ def main():
         del reps, c0, h0
         torch.cuda.empty_cache()
         rec["prefill_indexer"] = prefill_indexer_rate(dev, sk, torch, CSA_PREFILL_32K_BF16)
+        torch.cuda.empty_cache()
+        rec["prefill_indexer_fp4"] = prefill_indexer_rate(dev, sk, torch, CSA_PREFILL_32K_BF16, fp4=True)
         torch.cuda.empty_cache()
         rec["prefill_attend"] = prefill_attend_rate(dev, sk, torch, CSA_PREFILL_32K_BF16)
         torch.cuda.empty_cache()

@@ -201,8 +201,8 @@ sckv_status hca_append(int32_t B, int32_t m, int32_t o, const sckv_append_stream
  *   w         : [R][H_I] fp32 head weights w_h
  *   keys      : indexer keys in SCKV_LAYOUT_KEY_TILES [B][E_cap/32][D_I/8][32][8]
  *               (key_dtype F32, BF16 or unscaled E4M3; E_cap a multiple of 32), or
- *               MXFP4 tiles (key_dtype SCKV_MXFP4, BF16 queries, decode rows only:
- *               each key is dequantised exactly to bf16 and scored as bf16 keys are)
+ *               MXFP4 tiles (key_dtype SCKV_MXFP4 with BF16 queries: each key is
+ *               dequantised exactly to bf16 and scored as bf16 keys are)
  *   out_idx   : [R][k] int32: the kept entries of each row in ascending order,
  *               then -1 padding (k' = min(k, E_vis) entries are kept; E_vis = 0
  *               gives an all -1 row)

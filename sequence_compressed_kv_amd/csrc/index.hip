@@ -134,6 +134,23 @@ struct ScoreWave {
   __device__ __forceinline__ static void frags(const uint8_t* tile, bf16x8 (&b)[2][KS]) {
     constexpr int ESZ = KEY == SCKV_BF16 ? 2 : 1;
     const int l = lane_id(), c = l & 15, g = l >> 4;
+    if constexpr (KEY == SCKV_MXFP4) {
+      // MXFP4 tile: k-step ks is 32-channel block ks; the lane's 8 codes are 4
+      // bytes of the key's 16-byte block, its scale one of the key's scale bytes
+#pragma unroll
+      for (int nh = 0; nh < 2; ++nh) {
+        const int key = 16 * nh + c;
+        uint32_t sc;
+        if constexpr (DI == 128) sc = *reinterpret_cast<const uint32_t*>(tile + 16 * DI + 4 * key);
+        else sc = *reinterpret_cast<const uint16_t*>(tile + 16 * DI + 2 * key);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const uint32_t v = *reinterpret_cast<const uint32_t*>(tile + (ks * 32 + key) * 16 + 4 * g);
+          b[nh][ks] = fp4x8_to_bf16x8(v, e8m0_scale((sc >> (8 * ks)) & 255u));
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int nh = 0; nh < 2; ++nh)
 #pragma unroll
@@ -271,10 +288,13 @@ __global__ __launch_bounds__(512) void index_score_causal_lds(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const void* __restrict__ keys,
     float* __restrict__ scores, int64_t stride, int64_t E_cap, int m, int W, int32_t seq0, int32_t pos0, int R) {
   constexpr int NWR = 8;
+  constexpr bool FP4 = KEY == SCKV_MXFP4;
   constexpr int ESZ = KEY == SCKV_BF16 ? 2 : 1;
-  constexpr int TB = 32 * DI * ESZ;                                    // bytes per 32-key tile
+  constexpr int TB = FP4 ? 17 * DI : 32 * DI * ESZ;                    // bytes per 32-key tile
   constexpr int PPS = 32768 / TB;                                      // tile pairs per stage (64 KB)
-  constexpr int SB = 2 * PPS * TB;                                     // bytes per stage
+  // bytes per stage: whole tiles; MXFP4 tiles (17 DI bytes) are copied as one
+  // linear run rounded up to 1 KB per wave (the bytes past the last tile are not read)
+  constexpr int SB = FP4 ? (2 * PPS * TB + NWR * 1024 - 1) / (NWR * 1024) * (NWR * 1024) : 2 * PPS * TB;
   constexpr int NC = SB / 1024;                                        // 1 KB copies per stage
   constexpr int CPW = NC >= NWR ? NC / NWR : 1;                        // copies per copying wave
   constexpr int NSTG = 3 * SB <= 96 * 1024 ? 3 : 2;
@@ -298,7 +318,7 @@ __global__ __launch_bounds__(512) void index_score_causal_lds(
   SW sw;
   sw.load_query(opaque_global(q) + (int64_t)r * HI * DI * 2, w + (int64_t)r * HI);
   float* srow = scores + (int64_t)r * stride;
-  const gbytes gk = opaque_global(keys) + (int64_t)seq0 * E_cap * DI * ESZ;
+  const gbytes gk = opaque_global(keys) + (int64_t)seq0 * (E_cap / 32) * TB;
   const int wu = __builtin_amdgcn_readfirstlane(wv);
   const bool copier = NC >= NWR || wu < NC;
   const int lkey = SW::lane_key();
@@ -309,9 +329,19 @@ __global__ __launch_bounds__(512) void index_score_causal_lds(
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
       const int cb = (wu * CPW + c) * 1024;                            // byte offset within the stage
-      int tile = 2 * PPS * st + cb / TB;
-      tile = tile < ntiles ? tile : ntiles - 1;
-      copy_to_lds16(gk + (int64_t)tile * TB + (cb % TB) + l * 16, &stg[buf * SB + cb]);
+      if constexpr (FP4) {
+        // the stage's tiles as one run; a lane whose 16 bytes would pass the end of
+        // the sequence's cache re-reads its last 16 bytes (landing past every tile
+        // the block scores)
+        int64_t off = (int64_t)2 * PPS * st * TB + cb + l * 16;
+        const int64_t last = (E_cap / 32) * TB - 16;
+        off = off < last ? off : last;
+        copy_to_lds16(gk + off, &stg[buf * SB + cb]);
+      } else {
+        int tile = 2 * PPS * st + cb / TB;
+        tile = tile < ntiles ? tile : ntiles - 1;
+        copy_to_lds16(gk + (int64_t)tile * TB + (cb % TB) + l * 16, &stg[buf * SB + cb]);
+      }
     }
   };
   auto store = [&](int tile, float v) __attribute__((always_inline)) {
@@ -409,7 +439,7 @@ static void launch_mfma(const sckv_index_args& a, float* scores, int64_t stride,
     else if (nt == 8) SCKV_DEC(8);
     else SCKV_DEC(4);
 #undef SCKV_DEC
-  } else if constexpr (KEY != SCKV_MXFP4) {      // MXFP4 keys: decode rows only (checked on the host)
+  } else {
     const dim3 grid((unsigned)((a.rows.R + 7) / 8));
     hipLaunchKernelGGL((index_score_causal_lds<KEY, HI, DI>), grid, dim3(512), 0, stream, q, a.w, a.keys, scores,
                        stride, a.E_cap, a.m, a.W, a.rows.seq0, a.rows.pos0, a.rows.R);

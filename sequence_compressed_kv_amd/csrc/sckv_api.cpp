@@ -145,8 +145,6 @@ sckv_status check_index(const sckv_index_args* a, IndexPlan* pl, bool need_out) 
     if (!(a->H_I == 32 || a->H_I == 64) || !(a->D_I == 64 || a->D_I == 128))
       return fail(SCKV_ERR_UNSUPPORTED, "index: MFMA path needs H_I in {32,64} and D_I in {64,128} (got %d, %d)",
                   a->H_I, a->D_I);
-    if (a->key_dtype == SCKV_MXFP4 && a->rows.kind != SCKV_ROWS_DECODE)
-      return fail(SCKV_ERR_UNSUPPORTED, "index: MXFP4 keys are scored for decode rows only");
   } else {
     return fail(SCKV_ERR_DTYPE, "index: q %s with keys %s not supported (F32/F32, BF16/BF16, BF16/E4M3, BF16/MXFP4)",
                 dtname(a->q_dtype), dtname(a->key_dtype));

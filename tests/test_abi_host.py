@@ -127,14 +127,20 @@ def idx_args(**kw):
     (dict(rows=_lib.Rows(None, 0, 2, 4095, 0, 0, 0)), 1), (dict(rows=_lib.Rows(FAKE, 0, 3, 4095, 0, 0, 0)), 2),
     (dict(rows=_lib.Rows(None, 1, 8, 0, 2, 0, 0)), 2), (dict(rows=_lib.Rows(None, 5, 8, 0, 0, 0, 0)), 2),
     # MXFP4 keys: bf16 queries and decode rows only
-    (dict(key_dtype=3, q_dtype=0), 3), (dict(key_dtype=3, rows=_lib.Rows(None, 1, 8, 0, 0, 0, 0)), 4),
-    (dict(key_dtype=3, D_I=96), 4),
+    (dict(key_dtype=3, q_dtype=0), 3), (dict(key_dtype=3, D_I=96), 4),
 ])
 def test_index_validation(L, kw, status):
     a = idx_args(**kw)
     assert L.csa_index_topk(C.byref(a), FAKE, 1 << 30, None) == status, err(L)
     if "out_idx" not in kw:                  # the size query does not need the output pointer
         assert L.csa_index_topk_workspace_size(C.byref(a)) == 0
+
+
+def test_index_mxfp4_rows_accepted(L):
+    """MXFP4 keys with bf16 queries pass validation for decode and causal rows."""
+    for rows in (_lib.Rows(FAKE, 0, 2, 4095, 0, 0, 0), _lib.Rows(None, 1, 8, 0, 0, 100, 0)):
+        a = idx_args(key_dtype=3, rows=rows)
+        assert L.csa_index_topk_workspace_size(C.byref(a)) > 0, err(L)
 
 
 def test_index_workspace(L):

@@ -384,6 +384,8 @@ CAUSAL_CASES = [
     ("e4m3", 64, 128, 600, 2500, 128),
     ("bf16", 32, 64, 700, 2900, 32),
     ("e4m3", 64, 64, 500, 2123, 64),
+    ("mxfp4", 64, 128, 800, 3300, 64),
+    ("mxfp4", 32, 64, 700, 2900, 32),
 ]
 
 
@@ -410,6 +412,35 @@ def test_index_topk_causal(keys_s, HI, DI, E_cap, T, k):
             assert_scores_close(gs[t, :ev], s, q[t], w[t], kv[0, :ev], rtol=2e-6, what=f"scores row {t}")
         assert np.all(np.isnan(gs[t, ev:])), f"row {t}: scores written past the {ev} visible entries"
         ok, msg = topk_parity(gi[t], method.topk(s, k), s)
+        assert ok, f"row {t} (E_vis={ev}): {msg}"
+
+
+def test_index_causal_mxfp4_many_stages():
+    """Causal rows late in a long sequence over MXFP4 keys: the key tiles pass
+    through five LDS stages, and the last stage's copy runs past the end of the
+    cache (those lanes re-read its last bytes; nothing past the visible tiles is
+    stored)."""
+    HI, DI, E_cap, R, pos0, k = 64, 128, 4096, 24, 16000, 256
+    print(f"index causal mxfp4 many stages R={R} pos0={pos0} E_cap={E_cap}", flush=True)
+    rng = np.random.default_rng(77)
+    q = rng_store(rng, (R, HI, DI), "bf16")
+    w = rng.normal(0, 1, (R, HI)).astype(np.float32)
+    _, _, kv, _, _, keysd = _index_inputs(rng, "mxfp4", HI, DI, 1, E_cap)
+    rows = sk.RowSpec.causal(R, pos0=pos0)
+    cover = min(method.entries_visible(pos0 + R - 1, 4, 128), E_cap)
+    scores = torch.full((R, cover + 3), float("nan"), device=DEV, dtype=torch.float32)
+    out_idx = torch.full((R, k), -7, device=DEV, dtype=torch.int32)
+    sk.csa_index_score(rows, dev(q, "bf16"), dev(w), keysd, scores, m=4, W=128, k=k)
+    sk.csa_index_topk(rows, dev(q, "bf16"), dev(w), keysd, out_idx, m=4, W=128, k=k)
+    torch.cuda.synchronize()
+    gi, gs = host(out_idx), host(scores)
+    for i in range(R):
+        t = pos0 + i
+        ev = min(method.entries_visible(t, 4, 128), E_cap)
+        s = method.index_scores(q[i], w[i], kv[0, :ev])
+        assert_scores_close(gs[i, :ev], s, q[i], w[i], kv[0, :ev], rtol=2e-6, what=f"scores row {t}")
+        assert np.all(np.isnan(gs[i, ev:])), f"row {t}: scores written past the {ev} visible entries"
+        ok, msg = topk_parity(gi[i], method.topk(s, k), s)
         assert ok, f"row {t} (E_vis={ev}): {msg}"
 
 
