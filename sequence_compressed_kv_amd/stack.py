@@ -35,6 +35,7 @@ class StackLayer:
     H_I: int = 0     # indexer heads (CSA)
     D_I: int = 0     # indexer dim (CSA)
     k: int = 0       # top-k (CSA)
+    keys: str = "bf16"   # indexer key storage (CSA): "bf16" key tiles or "mxfp4" FP4 blocks
 
 
 def hybrid_schedule(n_layers: int, csa: StackLayer, hca: StackLayer) -> List[StackLayer]:
@@ -100,13 +101,21 @@ class Stack:
                   "g_ring": arena.reserve(f"{li}.gate_ring", (B, L.W, L.D), bf)}
             if L.kind == "csa":
                 E_t = (E_cap + 31) // 32 * 32
-                sl["keys"] = arena.reserve(f"{li}.index_keys", (B, E_t // 32, L.D_I // 8, 32, 8), bf)
+                if L.keys == "mxfp4":
+                    sl["keys"] = arena.reserve(f"{li}.index_keys", (B, E_t // 32, 17 * L.D_I), torch.uint8)
+                elif L.keys == "bf16":
+                    sl["keys"] = arena.reserve(f"{li}.index_keys", (B, E_t // 32, L.D_I // 8, 32, 8), bf)
+                else:
+                    raise ValueError(f"layer {li}: unknown key storage {L.keys!r}")
                 sl["vI_ring"] = arena.reserve(f"{li}.index_value_ring", (B, L.m + L.o, L.D_I), bf)
                 sl["gI_ring"] = arena.reserve(f"{li}.index_gate_ring", (B, L.m + L.o, L.D_I), bf)
             self._slots.append(sl)
         arena.allocate()
         self.arena = arena
         self.caches = [{k: arena.view(i) for k, i in sl.items()} for sl in self._slots]
+        for L, c in zip(self.layers, self.caches):
+            if L.kind == "csa" and L.keys == "mxfp4":
+                c["keys"] = sk.Mxfp4Keys(c["keys"], L.D_I)
         self._decode_ws: Optional[List[Dict]] = None
 
     @property

@@ -61,7 +61,7 @@ def oracle_layer(L, w, x):
     if L.kind == "csa":
         st["vI"] = bf16(method.project(x, w["W_cI"]))
         st["gI"] = bf16(method.project(x, w["W_gI"]))
-    caches = pipeline.layer_caches(L, st, w, "bf16", "bf16")
+    caches = pipeline.layer_caches(L, st, w, "bf16", L.keys if L.kind == "csa" else "bf16")
     qh = method.project(x, w["W_q"]).reshape(n, L.H, L.d_h)
     q = bf16(method.absorb_queries(qh, w["W_UK"]) if L.D != L.d_h else qh)
     qI = bf16(method.project(x, w["W_iq"]).reshape(n, L.H_I, L.D_I)) if L.kind == "csa" else None
@@ -99,13 +99,17 @@ def normwise(g, o):
 TOL = 3e-2
 
 
-def test_stack_prefill_and_decode():
-    layers = stk.hybrid_schedule(4, CSA, HCA)
+@pytest.mark.parametrize("keys", ["bf16", "mxfp4"])
+def test_stack_prefill_and_decode(keys):
+    """keys: the CSA layer's indexer key storage (MXFP4: FP4 blocks of 32 channels
+    with a power-of-two scale; the oracle stores its keys the same way)."""
+    import dataclasses
+    layers = stk.hybrid_schedule(4, dataclasses.replace(CSA, keys=keys), HCA)
     assert [L.kind for L in layers] == ["hca", "hca", "csa", "hca"]
     w_host = make_weights(layers)
     rng = np.random.default_rng(1)
     x = bf16(rng.standard_normal((B, N, D_MODEL)).astype(np.float32))
-    print(f"stack prefill B={B} N={N} layers={[L.kind for L in layers]}", flush=True)
+    print(f"stack prefill B={B} N={N} layers={[L.kind for L in layers]} keys={keys}", flush=True)
     st = stk.Stack(layers, [to_dev(w) for w in w_host], D_MODEL, B, N_max=N + 100)
     names = [n for n, _, _ in st.plan]
     assert len(names) == len(set(names)) and all(off % 256 == 0 for _, off, _ in st.plan)

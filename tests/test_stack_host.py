@@ -46,3 +46,19 @@ def test_window_ring_must_hold_a_pooling_window():
     bad = stk.StackLayer("hca", m=128, o=0, D=512, H=64, d_h=128, W=64)
     with pytest.raises(ValueError):
         stk.Stack([bad], [{}], 4096, B=1, N_max=512, device="cpu")
+
+
+def test_arena_mxfp4_keys():
+    """A CSA layer with MXFP4 keys reserves 17 D_I bytes per 32 entries and hands the
+    calls an Mxfp4Keys view of them."""
+    import dataclasses
+    from sequence_compressed_kv_amd import _lib
+    csa4 = dataclasses.replace(CSA, keys="mxfp4")
+    st = stk.Stack(stk.hybrid_schedule(3, csa4, HCA), [{} for _ in range(3)], 4096, B=2, N_max=1000, device="cpu")
+    k = st.caches[2]["keys"]
+    assert isinstance(k, _lib.Mxfp4Keys) and k.D_I == 128 and k.E_cap == 256
+    assert k.tiles.shape == (2, 8, 17 * 128) and k.tiles.dtype == torch.uint8
+    (name, off, nb), = [p for p in st.plan if p[0] == "2.index_keys"]
+    assert nb == 2 * 8 * 17 * 128 and off % 256 == 0
+    with pytest.raises(ValueError):
+        stk.Stack([dataclasses.replace(CSA, keys="e2m1")], [{}], 4096, B=1, N_max=512, device="cpu")
