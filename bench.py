@@ -654,10 +654,11 @@ def decode_layer_rate(dev, sk, torch, wl, c, h, weights, steps: int = 32, replay
             "projection_weight_GBps": wbytes / (ms_proj * 1e-3) / 1e9}
 
 
-def decode_1m_rate(dev, sk, torch, gen, steps: int = 20, replicas: int = 4):
+def decode_1m_rate(dev, sk, torch, gen, steps: int = 20, replicas: int = 4, fp4: bool = False):
     """Decode step of the 1M-context pair (batch 1) with fp8 caches: index + top-2048,
     CSA and HCA attention, bf16 out.  Cache replicas are rotated (the pair cache is
-    smaller than the 256 MiB MALL)."""
+    smaller than the 256 MiB MALL).  fp4: the indexer keys are MXFP4 tiles (68
+    bytes per key) instead of unscaled e4m3 (128 bytes)."""
     from workloads import PAIR_DEC_1M_FP8 as wl
     csa, hca = wl.layers
     t = wl.N - 1
@@ -667,7 +668,8 @@ def decode_1m_rate(dev, sk, torch, gen, steps: int = 20, replicas: int = 4):
     s_c, s_h = gen.gpu_sequence_streams(wl, 0, weights, dev)
     c = {"ent": torch.empty(1, Ec, csa.D, device=dev, dtype=torch.uint8).view(f8),
          "sc": torch.empty(1, Ec, device=dev),
-         "keys": sk.key_tiles_empty(1, Ec, csa.D_I, torch.uint8, dev).view(f8),
+         "keys": (sk.Mxfp4Keys.empty(1, Ec, csa.D_I, dev) if fp4
+                  else sk.key_tiles_empty(1, Ec, csa.D_I, torch.uint8, dev).view(f8)),
          "win": torch.empty(1, csa.W, csa.D, device=dev, dtype=bf)}
     h = {"ent": torch.empty(1, Eh, hca.D, device=dev, dtype=torch.uint8).view(f8),
          "sc": torch.empty(1, Eh, device=dev),
@@ -716,11 +718,13 @@ def decode_1m_rate(dev, sk, torch, gen, steps: int = 20, replicas: int = 4):
     ms = e0.elapsed_time(e1) / steps
     ev_c, ev_h = (t - csa.W) // csa.m, (t - hca.W) // hca.m
     nwin = csa.W
-    by = (ev_c * csa.D_I + csa.H_I * csa.D_I * 2 + csa.H_I * 4 + csa.k * 4                       # indexer + top-k
+    key_bytes = csa.D_I // 2 + csa.D_I // 32 if fp4 else csa.D_I
+    by = (ev_c * key_bytes + csa.H_I * csa.D_I * 2 + csa.H_I * 4 + csa.k * 4                     # indexer + top-k
           + csa.k * (csa.D + 4) + nwin * csa.D * 2 + csa.H * csa.D * 2 * 2                       # CSA attention
           + ev_h * (hca.D + 4) + nwin * hca.D * 2 + hca.H * hca.D * 2 * 2)                       # HCA attention
     gbps = by / (ms * 1e-3) / 1e9
-    return {"workload": wl.name, "batch": 1, "context": wl.N, "replicas": replicas, "ms_per_step": ms,
+    return {"workload": wl.name + ("_mxfp4_keys" if fp4 else ""), "batch": 1, "context": wl.N,
+            "key_bytes": key_bytes, "replicas": replicas, "ms_per_step": ms,
             "queries_per_s": 1.0 / (ms * 1e-3), "algorithmic_bytes": by, "hbm_GBps": gbps,
             "hbm_frac": gbps / PEAK_HBM_GBPS}
 
@@ -941,7 +945,8 @@ def main():
                                                                          CSA_PREFILL_32K_BF16)}))
         return
     if args.only == "1m":
-        print(json.dumps({"decode_1m_fp8": decode_1m_rate("cuda:0", sk, torch, gen)}))
+        print(json.dumps({"decode_1m_fp8": decode_1m_rate("cuda:0", sk, torch, gen),
+                          "decode_1m_fp8_mxfp4_keys": decode_1m_rate("cuda:0", sk, torch, gen, fp4=True)}))
         return
     if args.only == "stack":
         print(json.dumps({"prefill_hca_attend": prefill_hca_attend_rate("cuda:0", sk, torch, PAIR_DEC_128K_BF16),
@@ -1096,6 +1101,8 @@ def main():
         print("[bench] 1M-context fp8 decode step", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
         rec["decode_1m_fp8"] = decode_1m_rate(dev, sk, torch, gen)
+        torch.cuda.empty_cache()
+        rec["decode_1m_fp8_mxfp4_keys"] = decode_1m_rate(dev, sk, torch, gen, fp4=True)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

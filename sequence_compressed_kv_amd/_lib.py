@@ -212,6 +212,9 @@ class Mxfp4Keys:
     def device(self):
         return self.tiles.device
 
+    def clone(self) -> "Mxfp4Keys":
+        return Mxfp4Keys(self.tiles.clone(), self.D_I)
+
     @property
     def E_cap(self) -> int:
         return int(self.tiles.shape[1]) * 32

@@ -304,17 +304,21 @@ def test_pair_decode_128k_mxfp4_keys():
 
 # ---------------------------------------------------------------- CSA+HCA pair decode at 1M, fp8 caches
 @pytest.mark.slow
-def test_pair_decode_1m_fp8():
+@pytest.mark.parametrize("keys_s", ["e4m3", "mxfp4"])
+def test_pair_decode_1m_fp8(keys_s):
+    """keys_s: the indexer keys' storage, unscaled e4m3 or MXFP4 (FP4 blocks of 32
+    channels with a power-of-two scale: the pages' FP4 indexer at 1M context)."""
     wl = PAIR_DEC_1M_FP8
     csa, hca = wl.layers
     t = wl.N - 1
-    print(f"{wl.name}: B={wl.B} N={wl.N}", flush=True)
+    print(f"{wl.name}: B={wl.B} N={wl.N} indexer keys {keys_s}", flush=True)
     weights = gen.gpu_weights(wl, DEV)
     Ec, Eh = wl.N // csa.m, wl.N // hca.m
     f8, bf = torch.float8_e4m3fn, torch.bfloat16
     ent_c = torch.empty(1, Ec, csa.D, device=DEV, dtype=torch.uint8).view(f8)
     sc_c = torch.empty(1, Ec, device=DEV)
-    keys = sk.key_tiles_empty(1, Ec, csa.D_I, torch.uint8, DEV).view(f8)
+    keys = (sk.Mxfp4Keys.empty(1, Ec, csa.D_I, DEV) if keys_s == "mxfp4"
+            else sk.key_tiles_empty(1, Ec, csa.D_I, torch.uint8, DEV).view(f8))
     ent_h = torch.empty(1, Eh, hca.D, device=DEV, dtype=torch.uint8).view(f8)
     sc_h = torch.empty(1, Eh, device=DEV)
     win_c = torch.empty(1, csa.W, csa.D, device=DEV, dtype=bf)
@@ -331,17 +335,26 @@ def test_pair_decode_1m_fp8():
     torch.cuda.synchronize()
     vc, vh = f32(s_c["v"]), f32(s_h["v"])
     cc, magc, stc = oracle_pool(vc, f32(s_c["g"]), f32(weights[0]["bpos"]), csa.m, csa.o, "e4m3")
-    cI, magI, stI = oracle_pool(f32(s_c["vI"]), f32(s_c["gI"]), f32(weights[0]["bposI"]), csa.m, csa.o, "e4m3",
+    cI, magI, stI = oracle_pool(f32(s_c["vI"]), f32(s_c["gI"]), f32(weights[0]["bposI"]), csa.m, csa.o, keys_s,
                                 keys=True)
     ch, magh, sth = oracle_pool(vh, f32(s_h["g"]), f32(weights[1]["bpos"]), hca.m, hca.o, "e4m3")
     del s_c, s_h
     check_codes("CSA entries", "e4m3", ent_c[0], cc, magc, stc, got_scale=sc_c[0])
-    check_codes("CSA keys", "e4m3", sk.from_key_tiles(keys)[0], cI, magI, stI, keys=True)
+    if keys_s == "mxfp4":
+        gcodes, gscale = (x[0, :Ec].cpu().numpy() for x in sk.mxfp4_unpack(keys))
+        n_diff, n_un = mxfp4_flips(gcodes, gscale, cI, magI)
+        assert n_un == 0, f"CSA keys: {n_un} of {n_diff} MXFP4 scales/codes unexplained"
+    else:
+        check_codes("CSA keys", "e4m3", sk.from_key_tiles(keys)[0], cI, magI, stI, keys=True)
     check_codes("HCA entries", "e4m3", ent_h[0], ch, magh, sth, got_scale=sc_h[0])
     del cc, magc, cI, magI, ch, magh
     ent_c[0] = dev_codes(stc["codes"])
     sc_c[0] = dev(stc["scale"])
-    keys.copy_(sk.to_key_tiles(dev_codes(stI["codes"])[None]))
+    if keys_s == "mxfp4":
+        keys.tiles.copy_(sk.mxfp4_pack(torch.from_numpy(stI["codes"])[None],
+                                       torch.from_numpy(stI["scale"])[None]).tiles.to(DEV))
+    else:
+        keys.copy_(sk.to_key_tiles(dev_codes(stI["codes"])[None]))
     ent_h[0] = dev_codes(sth["codes"])
     sc_h[0] = dev(sth["scale"])
     qc = gen.gpu_queries(wl, 0, 1, DEV)
