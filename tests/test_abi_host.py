@@ -126,7 +126,7 @@ def idx_args(**kw):
     (dict(q_dtype=0, key_dtype=0, H_I=128, D_I=128), 4), (dict(keys=FAKE_ODD), 5), (dict(E_cap=1000), 2),
     (dict(rows=_lib.Rows(None, 0, 2, 4095, 0, 0, 0)), 1), (dict(rows=_lib.Rows(FAKE, 0, 3, 4095, 0, 0, 0)), 2),
     (dict(rows=_lib.Rows(None, 1, 8, 0, 2, 0, 0)), 2), (dict(rows=_lib.Rows(None, 5, 8, 0, 0, 0, 0)), 2),
-    # MXFP4 keys: bf16 queries and decode rows only
+    # MXFP4 keys need bf16 queries and the MFMA shapes
     (dict(key_dtype=3, q_dtype=0), 3), (dict(key_dtype=3, D_I=96), 4),
 ])
 def test_index_validation(L, kw, status):
