@@ -119,7 +119,8 @@ def test_compress_key_tiles(ins, outs, D, B, N):
             assert e4m3_flips(got, st["codes"], c, mag)[1] == 0
 
 
-@pytest.mark.parametrize("ins,D,B,N", [("bf16", 128, 2, 4096), ("f32", 64, 1, 1030), ("bf16", 32, 1, 600)])
+@pytest.mark.parametrize("ins,D,B,N", [("bf16", 128, 2, 4096), ("f32", 64, 1, 1030), ("bf16", 32, 1, 600),
+                                       ("bf16", 256, 1, 700), ("f32", 512, 1, 520)])
 def test_compress_mxfp4_keys(ins, D, B, N):
     """FP4 indexer keys: the GPU's MXFP4 blocks against the oracle's, block scales and
     e2m1 codes, with flips only where the fp32 pooling error can cross a rounding
