@@ -609,18 +609,24 @@ def test_attend_rows_longer_than_a_segment():
         np.testing.assert_allclose(gl[r], lse_o, rtol=1e-5, atol=1e-5)
 
 
-def test_decode_step_replays_as_hip_graph():
+@pytest.mark.parametrize("keys_s", ["e4m3", "mxfp4"])
+def test_decode_step_replays_as_hip_graph(keys_s):
     """A decode step (index + top-k with sliced rows, fp8 CSA attention on the
     register-staged kernel, bf16 HCA attention on the copy-staged kernel) captured
     as a HIP graph: every replay, with eager work and synchronizations between
-    replays, reproduces the eager results bit for bit."""
-    print("graph replay of a decode step", flush=True)
+    replays, reproduces the eager results bit for bit.  keys_s: the indexer keys'
+    storage (unscaled e4m3 or MXFP4 tiles)."""
+    print(f"graph replay of a decode step, {keys_s} indexer keys", flush=True)
     torch.manual_seed(11)
     f8, bf = torch.float8_e4m3fn, torch.bfloat16
     B, E_c, E_h, k, H, D = 2, 40000, 1024, 512, 64, 512
     pos = [160127, 100000]
     rows = sk.RowSpec.decode(dev_i32(pos), max(pos))
-    keys = sk.to_key_tiles(torch.randn(B, E_c, 128, device=DEV).to(f8))
+    if keys_s == "mxfp4":
+        keys = sk.mxfp4_pack(torch.randint(0, 16, (B, E_c, 128), device=DEV, dtype=torch.uint8),
+                             torch.randint(120, 134, (B, E_c, 4), device=DEV, dtype=torch.uint8))
+    else:
+        keys = sk.to_key_tiles(torch.randn(B, E_c, 128, device=DEV).to(f8))
     qI = torch.randn(B, 64, 128, device=DEV).to(bf)
     w = torch.randn(B, 64, device=DEV)
     ent_c = torch.randn(B, E_c, D, device=DEV).to(f8)
