@@ -165,6 +165,46 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else t.data_ptr()
 
 
+def _fail(msg: str):
+    raise SckvError(2, msg)
+
+
+def _dense(device, **named):
+    """Every named tensor (None skipped) must be contiguous and on `device`: the
+    C ABI sees bare pointers, so a strided view or a tensor on another device
+    would be read or written out of bounds."""
+    for name, t in named.items():
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor):
+            _fail(f"{name}: expected a tensor, got {type(t).__name__}")
+        if not t.is_contiguous():
+            _fail(f"{name}: tensor must be contiguous (shape {tuple(t.shape)}, strides {t.stride()})")
+        if device is not None and t.device != device:
+            _fail(f"{name}: on {t.device}, expected {device}")
+
+
+def _shape(name: str, t: Optional[torch.Tensor], want):
+    """t.shape must equal want (None entries match any size)."""
+    if t is None:
+        return
+    got = tuple(int(x) for x in t.shape)
+    if len(got) != len(want) or any(w is not None and g != w for g, w in zip(got, want)):
+        _fail(f"{name}: shape {got}, expected {tuple('*' if w is None else w for w in want)}")
+
+
+def _int32(name: str, t: Optional[torch.Tensor]):
+    if t is not None and t.dtype != torch.int32:
+        _fail(f"{name}: dtype {t.dtype}, expected torch.int32")
+
+
+def _rows_check(rows: "RowSpec", device):
+    if rows.kind == ROWS_DECODE and rows.pos is not None:
+        _dense(device, pos=rows.pos)
+        _int32("pos", rows.pos)
+        _shape("pos", rows.pos, (rows.R,))
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
@@ -266,9 +306,19 @@ class Pool:
     layout: int = LAYOUT_ROWS
 
     def c(self) -> PoolStream:
-        D = int(self.val.shape[2])
         out = _out_tensor(self.out)
+        _dense(self.val.device, val=self.val, gate=self.gate, bpos=self.bpos, out=out, out_scale=self.out_scale)
+        if self.val.dim() != 3:
+            _fail(f"val: shape {tuple(self.val.shape)}, expected [B][N][D]")
+        B, N, D = (int(x) for x in self.val.shape)
+        _shape("gate", self.gate, (B, N, D))
+        _shape("bpos", self.bpos, (None, D))
         E_cap = int(out.shape[1]) if self.layout == LAYOUT_ROWS else int(out.shape[1]) * 32
+        if int(out.shape[0]) != B:
+            _fail(f"out: batch {int(out.shape[0])}, expected {B}")
+        if self.layout == LAYOUT_ROWS:
+            _shape("out", out, (B, E_cap, D))
+        _shape("out_scale", self.out_scale, (B, E_cap))
         return PoolStream(_ptr(self.val), _ptr(self.gate), _ptr(self.bpos), _ptr(out), _ptr(self.out_scale),
                           E_cap, D, dtype_code(self.val), _out_code(self.out), self.layout)
 
@@ -290,9 +340,24 @@ class Append:
     layout: int = LAYOUT_ROWS
 
     def c(self) -> AppendStream:
-        D = int(self.val.shape[1])
         out = _out_tensor(self.out)
+        _dense(self.val.device, pos=self.pos, val=self.val, gate=self.gate, val_ring=self.val_ring,
+               gate_ring=self.gate_ring, bpos=self.bpos, out=out, out_scale=self.out_scale)
+        if self.val.dim() != 2:
+            _fail(f"val: shape {tuple(self.val.shape)}, expected [B][D]")
+        B, D = (int(x) for x in self.val.shape)
+        _int32("pos", self.pos)
+        _shape("pos", self.pos, (B,))
+        _shape("gate", self.gate, (B, D))
+        _shape("val_ring", self.val_ring, (B, None, D))
+        _shape("gate_ring", self.gate_ring, (B, int(self.val_ring.shape[1]), D))
+        _shape("bpos", self.bpos, (None, D))
         E_cap = int(out.shape[1]) if self.layout == LAYOUT_ROWS else int(out.shape[1]) * 32
+        if int(out.shape[0]) != B:
+            _fail(f"out: batch {int(out.shape[0])}, expected {B}")
+        if self.layout == LAYOUT_ROWS:
+            _shape("out", out, (B, E_cap, D))
+        _shape("out_scale", self.out_scale, (B, E_cap))
         return AppendStream(_ptr(self.pos), _ptr(self.val), _ptr(self.gate), _ptr(self.val_ring),
                             _ptr(self.gate_ring), _ptr(self.bpos), _ptr(out), _ptr(self.out_scale), E_cap, D,
                             int(self.val_ring.shape[1]), dtype_code(self.val), _out_code(self.out), self.layout, 0)
@@ -363,14 +428,35 @@ def hca_append(kv: Append, *, m: int = 128, o: int = 0, stream=None):
 
 def index_args(rows: RowSpec, q, w, keys, out_idx, *, m: int, W: int, k: int, out_score=None) -> IndexArgs:
     """keys: a tiled key cache [B][E_cap/32][D_I/8][32][8] (see key_tiles_empty) or Mxfp4Keys."""
+    kt = keys.tiles if isinstance(keys, Mxfp4Keys) else keys
+    _dense(kt.device, q=q, w=w, keys=kt, out_idx=out_idx, out_score=out_score)
+    _rows_check(rows, kt.device)
+    if q.dim() != 3:
+        _fail(f"q: shape {tuple(q.shape)}, expected [R][H_I][D_I]")
+    _shape("q", q, (rows.R, None, None))
+    _shape("w", w, (rows.R, int(q.shape[1])))
+    _int32("out_idx", out_idx)
+    _shape("out_idx", out_idx, (rows.R, k))
+    _shape("out_score", out_score, (rows.R, k))
     if isinstance(keys, Mxfp4Keys):
+        _shape("keys", kt, (None, None, 17 * int(q.shape[2])))
         return IndexArgs(rows.c(), _ptr(q), _ptr(w), _ptr(keys.tiles), _ptr(out_idx), _ptr(out_score), keys.E_cap,
                          int(keys.tiles.shape[0]), int(q.shape[1]), int(q.shape[2]), dtype_code(q), MXFP4, m, W, k)
     if keys.dim() != 5:
         raise ValueError("indexer keys must be in the tiled layout [B][E_cap/32][D_I/8][32][8]")
+    _shape("keys", keys, (None, None, int(q.shape[2]) // 8, 32, 8))
     return IndexArgs(rows.c(), _ptr(q), _ptr(w), _ptr(keys), _ptr(out_idx), _ptr(out_score),
                      int(keys.shape[1]) * 32, int(keys.shape[0]), int(q.shape[1]), int(q.shape[2]), dtype_code(q),
                      dtype_code(keys), m, W, k)
+
+
+def _scores_check(scores, rows: RowSpec, keys):
+    """A score matrix [R][stride] with unit stride along a row."""
+    dev = (keys.tiles if isinstance(keys, Mxfp4Keys) else keys).device
+    if scores.dim() != 2 or int(scores.shape[0]) != rows.R or scores.stride(1) != 1:
+        _fail(f"scores: shape {tuple(scores.shape)} strides {scores.stride()}, expected [R][n] with unit row stride")
+    if scores.device != dev or scores.dtype != torch.float32:
+        _fail(f"scores: {scores.dtype} on {scores.device}, expected torch.float32 on {dev}")
 
 
 def csa_index_topk_workspace_size(a: IndexArgs) -> int:
@@ -393,6 +479,7 @@ def csa_index_topk(rows: RowSpec, q, w, keys, out_idx, *, m: int = 4, W: int = 1
     n = csa_index_topk_workspace_size(a)
     if n == 0:
         _check(load().csa_index_topk(C.byref(a), None, 0, _stream(stream)))
+        return None
     ws = _workspace(n, keys.device, workspace)
     _check(load().csa_index_topk(C.byref(a), _ptr(ws), n, _stream(stream)))
     return ws
@@ -400,6 +487,7 @@ def csa_index_topk(rows: RowSpec, q, w, keys, out_idx, *, m: int = 4, W: int = 1
 
 def csa_index_score(rows: RowSpec, q, w, keys, scores, *, m: int = 4, W: int = 128, k: int = 1, stream=None):
     a = index_args(rows, q, w, keys, None, m=m, W=W, k=k)
+    _scores_check(scores, rows, keys)
     _check(load().csa_index_score(C.byref(a), _ptr(scores), int(scores.stride(0)), _stream(stream)))
 
 
@@ -408,6 +496,7 @@ def csa_topk_select(rows: RowSpec, scores, out_idx, *, keys_meta, m: int = 4, W:
     """keys_meta: (q, w, keys) tensors describing the indexer (only shapes/dtypes are read)."""
     q, w, keys = keys_meta
     a = index_args(rows, q, w, keys, out_idx, m=m, W=W, k=k, out_score=out_score)
+    _scores_check(scores, rows, keys)
     n = int(load().csa_topk_select_workspace_size(C.byref(a)))
     ws = _workspace(n, scores.device, workspace)
     _check(load().csa_topk_select(C.byref(a), _ptr(scores), int(scores.stride(0)), _ptr(ws), n, _stream(stream)))
@@ -415,6 +504,21 @@ def csa_topk_select(rows: RowSpec, scores, out_idx, *, keys_meta, m: int = 4, W:
 
 def attend_args(rows: RowSpec, q, entries, win, out, *, m: int, W: int, softmax_scale: float, entry_scale=None,
                 idx=None, lse=None) -> AttendArgs:
+    _dense(entries.device, q=q, entries=entries, win=win, out=out, entry_scale=entry_scale, idx=idx, lse=lse)
+    _rows_check(rows, entries.device)
+    if q.dim() != 3 or entries.dim() != 3 or win.dim() != 3:
+        _fail("q [R][H][D], entries [B][E_cap][D] and win [B][R_w][D] must be 3-dimensional")
+    H, D = int(q.shape[1]), int(q.shape[2])
+    B, E_cap = int(entries.shape[0]), int(entries.shape[1])
+    _shape("q", q, (rows.R, H, D))
+    _shape("entries", entries, (B, E_cap, D))
+    _shape("win", win, (B, None, D))
+    _shape("out", out, (rows.R, H, D))
+    _shape("lse", lse, (rows.R, H))
+    _shape("entry_scale", entry_scale, (B, E_cap))
+    _int32("idx", idx)
+    if idx is not None:
+        _shape("idx", idx, (rows.R, None))
     k = int(idx.shape[1]) if idx is not None else 0
     return AttendArgs(rows.c(), _ptr(q), _ptr(entries), _ptr(entry_scale), _ptr(idx), _ptr(win), _ptr(out),
                       _ptr(lse), int(entries.shape[1]), int(win.shape[1]), int(entries.shape[0]), int(q.shape[1]),

@@ -311,3 +311,91 @@ def test_mxfp4_key_tiles_layout():
                     assert base[16 * D + (j % 32) * (D // 32) + blk] == scale[b, j, blk]
         c2, s2 = _lib.mxfp4_unpack(keys)
         assert np.array_equal(c2.numpy()[:, :E], codes) and np.array_equal(s2.numpy()[:, :E], scale)
+
+
+# ---------------------------------------------------------------- the binding's own checks
+# The C ABI sees bare pointers, so the Python binding refuses strided views, tensors on
+# another device and shapes that disagree with the row count, head count or k before
+# anything reaches the library (CPU tensors: the checks raise before any C call).
+def _attend_inputs(R=2, H=16, D=64, B=2, E=32, Rw=128, k=8):
+    q = torch.zeros(R, H, D, dtype=torch.bfloat16)
+    ent = torch.zeros(B, E, D, dtype=torch.bfloat16)
+    idx = torch.zeros(R, k, dtype=torch.int32)
+    win = torch.zeros(B, Rw, D, dtype=torch.bfloat16)
+    out = torch.zeros(R, H, D)
+    pos = torch.full((R,), 200, dtype=torch.int32)
+    return sk.RowSpec.decode(pos, 200), q, ent, idx, win, out
+
+
+@pytest.mark.parametrize("bad", ["q_strided", "out_rows", "idx_dtype", "idx_rows", "win_dim", "lse_shape",
+                                 "pos_rows", "ent_D"])
+def test_binding_rejects_attend_tensors(bad):
+    rows, q, ent, idx, win, out = _attend_inputs()
+    lse = None
+    if bad == "q_strided":
+        q = torch.zeros(2, 16, 128, dtype=torch.bfloat16)[:, :, ::2]
+    elif bad == "out_rows":
+        out = torch.zeros(3, 16, 64)
+    elif bad == "idx_dtype":
+        idx = idx.to(torch.int64)
+    elif bad == "idx_rows":
+        idx = torch.zeros(1, 8, dtype=torch.int32)
+    elif bad == "win_dim":
+        win = torch.zeros(2, 128, 32, dtype=torch.bfloat16)
+    elif bad == "lse_shape":
+        lse = torch.zeros(2, 8)
+    elif bad == "pos_rows":
+        rows = sk.RowSpec(sk.ROWS_DECODE, 2, torch.zeros(3, dtype=torch.int32), 200)
+    elif bad == "ent_D":
+        ent = torch.zeros(2, 32, 128, dtype=torch.bfloat16)
+    with pytest.raises(sk.SckvError):
+        _lib.attend_args(rows, q, ent, win, out, m=4, W=128, softmax_scale=0.125, idx=idx, lse=lse)
+
+
+@pytest.mark.parametrize("bad", ["w_shape", "q_strided", "out_k", "keys_tiles", "scores_rows"])
+def test_binding_rejects_index_tensors(bad):
+    R, HI, DI, B, E, k = 2, 32, 64, 2, 64, 16
+    rows = sk.RowSpec.decode(torch.full((R,), 300, dtype=torch.int32), 300)
+    q = torch.zeros(R, HI, DI, dtype=torch.bfloat16)
+    w = torch.zeros(R, HI)
+    keys = sk.key_tiles_empty(B, E, DI, torch.bfloat16, "cpu")
+    out = torch.zeros(R, k, dtype=torch.int32)
+    if bad == "w_shape":
+        w = torch.zeros(R, HI + 1)
+    elif bad == "q_strided":
+        q = torch.zeros(R, DI, HI, dtype=torch.bfloat16).transpose(1, 2)
+    elif bad == "out_k":
+        out = torch.zeros(R, k + 1, dtype=torch.int32)
+    elif bad == "keys_tiles":
+        keys = torch.zeros(B, E // 32, DI // 8, 16, 16, dtype=torch.bfloat16)
+    with pytest.raises(sk.SckvError):
+        if bad == "scores_rows":
+            sk.csa_index_score(rows, q, w, keys, torch.zeros(R + 1, 64), m=4, W=128, k=k)
+        else:
+            _lib.index_args(rows, q, w, keys, out, m=4, W=128, k=k)
+
+
+@pytest.mark.parametrize("bad", ["gate_shape", "out_batch", "scale_shape", "ring_shape"])
+def test_binding_rejects_pool_tensors(bad):
+    B, N, D, E = 2, 64, 64, 16
+    v = torch.zeros(B, N, D, dtype=torch.bfloat16)
+    g = torch.zeros(B, N, D, dtype=torch.bfloat16)
+    bp = torch.zeros(8, D)
+    out = torch.zeros(B, E, D, dtype=torch.bfloat16)
+    with pytest.raises(sk.SckvError):
+        if bad == "gate_shape":
+            sk.Pool(v, g[:, :32].contiguous(), bp, out).c()
+        elif bad == "out_batch":
+            sk.Pool(v, g, bp, torch.zeros(B + 1, E, D, dtype=torch.bfloat16)).c()
+        elif bad == "scale_shape":
+            sk.Pool(v, g, bp, out.to(torch.uint8), out_scale=torch.zeros(B, E + 1)).c()
+        else:
+            pos = torch.zeros(B, dtype=torch.int32)
+            sk.Append(pos, v[:, 0].contiguous(), g[:, 0].contiguous(), torch.zeros(B, 16, D, dtype=torch.bfloat16),
+                      torch.zeros(B, 8, D, dtype=torch.bfloat16), bp, out).c()
+
+
+def test_binding_accepts_consistent_tensors():
+    rows, q, ent, idx, win, out = _attend_inputs()
+    a = _lib.attend_args(rows, q, ent, win, out, m=4, W=128, softmax_scale=0.125, idx=idx, lse=torch.zeros(2, 16))
+    assert a.H == 16 and a.D == 64 and a.k == 8 and a.R_w == 128
