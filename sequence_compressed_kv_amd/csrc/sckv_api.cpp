@@ -176,6 +176,9 @@ sckv_status check_attend(const sckv_attend_args* a, bool csa, sckv::AttendPlan* 
   if (a->H < 1 || a->D < 1 || a->m < 1 || a->W < 1 || a->E_cap < 1 || a->R_w < a->W)
     return fail(SCKV_ERR_SHAPE, "%s: need H,D,m,W,E_cap >= 1 and R_w >= W", name);
   if (!std::isfinite(a->softmax_scale)) return fail(SCKV_ERR_SHAPE, "%s: softmax_scale must be finite", name);
+  if (a->R_w > INT32_MAX || a->E_cap > INT32_MAX)
+    return fail(SCKV_ERR_UNSUPPORTED, "%s: R_w and E_cap must fit 31 bits (got %lld, %lld)", name,
+                (long long)a->R_w, (long long)a->E_cap);
   if (a->out_dtype != SCKV_F32 && a->out_dtype != SCKV_BF16)
     return fail(SCKV_ERR_DTYPE, "%s: out_dtype %s not supported", name, dtname(a->out_dtype));
   if (a->q_dtype == SCKV_F32 && a->entry_dtype == SCKV_F32 && a->win_dtype == SCKV_F32) {
