@@ -234,6 +234,22 @@ size_t csa_index_topk_workspace_size(const sckv_index_args* a);
 sckv_status csa_index_topk(const sckv_index_args* a, void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/* csa_index_topk_noalloc: csa_index_topk without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The scores and the selection's
+ * workspace live in a static device array of SCKV_NOALLOC_SCRATCH_BYTES that
+ * the library holds on every device it runs on until the process ends; the
+ * call allocates nothing.  Arguments, results and kernels are those of
+ * csa_index_topk.  Returns SCKV_ERR_WORKSPACE (nothing enqueued) when the rows
+ * need more scratch than the array holds (csa_index_topk_workspace_size above
+ * it), SCKV_ERR_UNSUPPORTED when `stream` belongs to another device than the
+ * current one.  Every call on a device shares that device's array: calls that
+ * overlap on one device (two streams, two threads) race and may return wrong
+ * indices; calls in order on one stream are safe.  The first call on a device
+ * looks the array's address up (thread-safe). */
+#define SCKV_NOALLOC_SCRATCH_BYTES (16u << 20)
+sckv_status csa_index_topk_noalloc(const sckv_index_args* a, void* stream);
+
 /* The two halves of csa_index_topk, for callers that want the scores themselves.
  * csa_index_score writes s_j for j < min(E_vis, E_cap) of row r to
  * scores[r * score_stride + j] (score_stride >= the visible count of every row;

@@ -8,12 +8,12 @@ layer_output); this package binds them for torch device tensors.
 """
 from ._lib import (BF16, E4M3, F32, LAYOUT_KEY_TILES, LAYOUT_ROWS, MXFP4, ROWS_CAUSAL, ROWS_DECODE, Append,
                    Mxfp4Keys, Pool, RowSpec, SckvError, abi_version, attend_args, csa_append, csa_attend, csa_compress, csa_index_score,
-                   csa_index_topk, csa_topk_select, from_key_tiles, hca_append, hca_attend, hca_compress, index_args,
+                   csa_index_topk, csa_index_topk_noalloc, csa_topk_select, from_key_tiles, hca_append, hca_attend, hca_compress, index_args,
                    key_tiles_empty, layer_inputs, layer_output, layer_queries, layer_streams, lib_path, load,
                    mxfp4_pack, mxfp4_unpack, output_args, query_args, stream_args, to_key_tiles)
 
 __all__ = ["BF16", "E4M3", "F32", "LAYOUT_KEY_TILES", "LAYOUT_ROWS", "MXFP4", "ROWS_CAUSAL", "ROWS_DECODE", "Append",
            "Mxfp4Keys", "Pool", "RowSpec", "SckvError", "abi_version", "attend_args", "csa_append", "csa_attend", "csa_compress",
-           "csa_index_score", "csa_index_topk", "csa_topk_select", "from_key_tiles", "hca_append", "hca_attend",
+           "csa_index_score", "csa_index_topk", "csa_index_topk_noalloc", "csa_topk_select", "from_key_tiles", "hca_append", "hca_attend",
            "hca_compress", "index_args", "key_tiles_empty", "layer_inputs", "layer_output", "layer_queries",
            "layer_streams", "lib_path", "load", "mxfp4_pack", "mxfp4_unpack", "output_args", "query_args", "stream_args", "to_key_tiles"]

@@ -82,7 +82,8 @@ class OutputArgs(C.Structure):
                 ("y_dtype", C.c_int32)]
 
 
-EXPORTS = ["csa_compress", "hca_compress", "csa_append", "hca_append", "csa_index_topk_workspace_size", "csa_index_topk", "csa_index_score",
+EXPORTS = ["csa_compress", "hca_compress", "csa_append", "hca_append", "csa_index_topk_workspace_size", "csa_index_topk",
+           "csa_index_topk_noalloc", "csa_index_score",
            "csa_topk_select_workspace_size", "csa_topk_select", "csa_attend_workspace_size",
            "hca_attend_workspace_size", "csa_attend", "hca_attend", "layer_queries_workspace_size", "layer_queries",
            "layer_streams_workspace_size", "layer_streams", "layer_inputs_workspace_size", "layer_inputs",
@@ -113,6 +114,7 @@ def load() -> C.CDLL:
     L.csa_index_topk_workspace_size.argtypes = [C.POINTER(IndexArgs)]
     L.csa_index_topk_workspace_size.restype = sz
     L.csa_index_topk.argtypes = [C.POINTER(IndexArgs), P, sz, P]
+    L.csa_index_topk_noalloc.argtypes = [C.POINTER(IndexArgs), P]
     L.csa_index_score.argtypes = [C.POINTER(IndexArgs), P, i64, P]
     L.csa_topk_select_workspace_size.argtypes = [C.POINTER(IndexArgs)]
     L.csa_topk_select_workspace_size.restype = sz
@@ -134,7 +136,8 @@ def load() -> C.CDLL:
     L.layer_output_workspace_size.argtypes = [C.POINTER(OutputArgs)]
     L.layer_output_workspace_size.restype = sz
     L.layer_output.argtypes = [C.POINTER(OutputArgs), P, sz, P]
-    for n in ("csa_compress", "hca_compress", "csa_append", "hca_append", "csa_index_topk", "csa_index_score",
+    for n in ("csa_compress", "hca_compress", "csa_append", "hca_append", "csa_index_topk", "csa_index_topk_noalloc",
+              "csa_index_score",
               "csa_topk_select", "csa_attend", "hca_attend", "layer_queries", "layer_streams", "layer_inputs", "layer_output"):
         getattr(L, n).restype = C.c_int
     L.sckv_last_error.restype = C.c_char_p
@@ -483,6 +486,17 @@ def csa_index_topk(rows: RowSpec, q, w, keys, out_idx, *, m: int = 4, W: int = 1
     ws = _workspace(n, keys.device, workspace)
     _check(load().csa_index_topk(C.byref(a), _ptr(ws), n, _stream(stream)))
     return ws
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def csa_index_topk_noalloc(rows: RowSpec, q, w, keys, out_idx, *, m: int = 4, W: int = 128, k: int, out_score=None,
+                           stream=None):
+    """csa_index_topk with the library's static device scratch instead of a workspace
+    (for callers that cannot allocate); calls that overlap on one device race."""
+    a = index_args(rows, q, w, keys, out_idx, m=m, W=W, k=k, out_score=out_score)
+    _check(load().csa_index_topk_noalloc(C.byref(a), _stream(stream)))
 
 
 def csa_index_score(rows: RowSpec, q, w, keys, scores, *, m: int = 4, W: int = 128, k: int = 1, stream=None):

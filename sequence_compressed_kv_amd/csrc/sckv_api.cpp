@@ -1,11 +1,20 @@
 // C ABI entry points: validation, workspace sizing and kernel dispatch.
 // Every argument is checked before the first HIP call, so a failing status
 // never leaves work enqueued (and the checks run on machines without a GPU).
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 
 #include "sckv_internal.h"
+
+// Scratch of csa_index_topk_noalloc: the score matrix and the top-k workspace of
+// one call, held for the life of the process on every device the library runs
+// on.  In host code `scratch` names a host-side stand-in, never the device
+// memory: host code only uses the address hipGetSymbolAddress returns for the
+// current device.
+static __device__ __align__(256) uint8_t scratch[SCKV_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -43,6 +52,26 @@ const char* dtname(int32_t d) {
 sckv_status hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(SCKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return ok();
+}
+
+// Device address of `scratch` on the current device, looked up once per device
+// (each device holds its own copy of the array).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_address(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 // ---------------------------------------------------------------- compression
@@ -385,6 +414,36 @@ sckv_status csa_index_topk(const sckv_index_args* a, void* ws, size_t ws_bytes, 
   if (e == hipSuccess)
     e = sckv::launch_topk(*a, scores, pl.stride, pl.topk, static_cast<char*>(ws) + pl.ws_scores, st);
   return hip_status(e, "csa_index_topk");
+}
+
+sckv_status csa_index_topk_noalloc(const sckv_index_args* a, void* stream) {
+  IndexPlan pl;
+  sckv_status s = check_index(a, &pl, true);
+  if (s != SCKV_OK) return s;
+  if (pl.ws_total > (size_t)SCKV_NOALLOC_SCRATCH_BYTES)
+    return fail(SCKV_ERR_WORKSPACE,
+                "csa_index_topk_noalloc: these rows need %zu bytes of scratch, the static buffer holds %zu; "
+                "call csa_index_topk with a workspace instead", pl.ws_total, (size_t)SCKV_NOALLOC_SCRATCH_BYTES);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "csa_index_topk_noalloc");
+  if (st) {
+    hipDevice_t sdev = 0;
+    e = hipStreamGetDevice(st, &sdev);
+    if (e != hipSuccess) return hip_status(e, "csa_index_topk_noalloc");
+    if ((int)sdev != dev)
+      return fail(SCKV_ERR_UNSUPPORTED, "csa_index_topk_noalloc: the stream belongs to device %d, current device is %d",
+                  (int)sdev, dev);
+  }
+  void* ws = nullptr;
+  e = scratch_address(dev, &ws);
+  if (e != hipSuccess) return hip_status(e, "csa_index_topk_noalloc (scratch address)");
+  float* scores = static_cast<float*>(ws);
+  e = sckv::launch_index_score(*a, scores, pl.stride, pl.cover, st);
+  if (e == hipSuccess)
+    e = sckv::launch_topk(*a, scores, pl.stride, pl.topk, static_cast<char*>(ws) + pl.ws_scores, st);
+  return hip_status(e, "csa_index_topk_noalloc");
 }
 
 sckv_status csa_index_score(const sckv_index_args* a, float* scores, int64_t score_stride, void* stream) {

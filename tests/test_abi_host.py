@@ -399,3 +399,17 @@ def test_binding_accepts_consistent_tensors():
     rows, q, ent, idx, win, out = _attend_inputs()
     a = _lib.attend_args(rows, q, ent, win, out, m=4, W=128, softmax_scale=0.125, idx=idx, lse=torch.zeros(2, 16))
     assert a.H == 16 and a.D == 64 and a.k == 8 and a.R_w == 128
+
+
+def test_noalloc_index_rejects_rows_beyond_its_scratch(L):
+    """csa_index_topk_noalloc refuses, before any HIP call, rows whose scores and
+    selection need more than the static scratch holds."""
+    # 4096 causal rows over 8192 visible entries: 4096 x 8192 fp32 scores = 128 MiB
+    a = idx_args(rows=_lib.Rows(None, 1, 4096, 0, 0, 32900, 0), E_cap=8192, k=512)
+    need = L.csa_index_topk_workspace_size(C.byref(a))
+    assert need > _lib.NOALLOC_SCRATCH_BYTES
+    assert L.csa_index_topk_noalloc(C.byref(a), None) == 6, err(L)
+    assert "scratch" in err(L)
+    # invalid arguments keep their own status
+    bad = idx_args(k=0)
+    assert L.csa_index_topk_noalloc(C.byref(bad), None) == 2
