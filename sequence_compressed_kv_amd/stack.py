@@ -145,10 +145,13 @@ class Stack:
         return 1.0 / math.sqrt(L.d_h)
 
     # ------------------------------------------------------------ prefill
-    def prefill(self, x: torch.Tensor, out_dtype=torch.bfloat16) -> List[torch.Tensor]:
+    def prefill(self, x: torch.Tensor, out_dtype=torch.bfloat16, record: Optional[list] = None) -> List[torch.Tensor]:
         """x [B][N][d_model] bf16, N <= N_max: every token of every sequence through
         the stack (causal rows).  Fills every layer's caches and rings; returns each
-        layer's output rows [B][N][d_model]."""
+        layer's output rows [B][N][d_model].  With a list as `record`, each layer
+        appends its intermediates: the projections' outputs ("t": q, v, g and for CSA
+        qI, w, vI, gI, rows b * N + position), the selections ("idx": per sequence
+        [N][k], CSA) and the attention outputs ("o" [B * N][H][D])."""
         B, N, dm = x.shape
         assert B == self.B and N <= self.N_max and dm == self.d_model
         outs = []
@@ -165,6 +168,7 @@ class Stack:
                 sk.hca_compress(kv, m=L.m, o=L.o)
             self._fill_rings(li, t, B, N)
             o = torch.empty(B * N, L.H, L.D, device=self.device, dtype=torch.bfloat16)
+            kept = []
             for b in range(B):
                 rows = sk.RowSpec.causal(N, seq0=b)
                 r = slice(b * N, (b + 1) * N)
@@ -173,11 +177,14 @@ class Stack:
                     sk.csa_index_topk(rows, t["qI"][r], t["w"][r], c["keys"], idx, m=L.m, W=L.W, k=L.k)
                     sk.csa_attend(rows, t["q"][r], c["entries"], idx, v, o[r], m=L.m, W=L.W,
                                   softmax_scale=self._tau(L))
+                    kept.append(idx)
                 else:
                     sk.hca_attend(rows, t["q"][r], c["entries"], v, o[r], m=L.m, W=L.W, softmax_scale=self._tau(L))
             y = torch.empty(B * N, dm, device=self.device, dtype=out_dtype)
             sk.layer_output(o, w["W_o"], y, W_UV=w.get("W_UV"))
             outs.append(y.view(B, N, dm))
+            if record is not None:
+                record.append({"t": t, "idx": kept, "o": o})
             h = y if out_dtype == torch.bfloat16 else y.to(torch.bfloat16)
         return outs
 

@@ -82,6 +82,11 @@ def tau_of(L):
     return 1.0 / math.sqrt(L.d_h)
 
 
+# sequences of the batch-32 step compared in full: one for each residue modulo 8 (the
+# attention kernel deals a row's blocks to the XCD of that residue), spread over the batch
+SEQ_SAMPLE = [0, 9, 18, 27, 4, 13, 22, 31]
+
+
 # ---------------------------------------------------------------- small CSA decode, fp32 (host recipe)
 def test_csa_decode_4k_f32():
     wl = CSA_DEC_4K_F32
@@ -187,17 +192,28 @@ def test_csa_prefill_32k_bf16():
     sk.csa_attend(rows, qs["q"], ent, idx, st["v"][None], out, m=L.m, W=L.W, softmax_scale=tau_of(L))
     torch.cuda.synchronize()
     heavy = gen.heavy_positions(wl, 0)
-    sample = sorted({0, 1, 127, 131, 132, 133, 200, 1000, 2179, 2180, 2500, 5000, 12345, 20000, T - 1,
-                     *[int(h) for h in heavy[[3, 150, 300]]], *[int(h) + 5 for h in heavy[[3, 150]]]})
+    # rows compared: every 16th; edge rows; a full block of 8 consecutive rows (the
+    # causal scoring kernel's unit) around every boundary of its 256-key LDS stages
+    # (visible count 256 s: position 1024 s + 128); each heavy token and the two
+    # rows after it (queries whose window holds it)
+    edges = {0, 1, 127, 128, 131, 132, 133, 200, 1000, 2179, 2180, 2500, T - 2, T - 1}
+    blocks = {8 * ((1024 * s_ + 128) // 8) + i for s_ in range(T // 1024) for i in range(-8, 8)}
+    near_heavy = {int(h) + d for h in heavy for d in (0, 1, 2)}
+    sample = sorted(x for x in set(range(0, T, 16)) | edges | blocks | near_heavy if 0 <= x < T)
+    print(f"  comparing {len(sample)} of {T} rows", flush=True)
     gi = host(idx)
-    for t in sample:
-        r = method.csa_row(t, f32(qs["q"][t]), f32(qs["qI"][t]), qs["w"][t].cpu().numpy(), se["values"],
-                           sI["values"], v, L.m, L.W, L.k, tau_of(L))
+    sel = torch.tensor(sample, device=DEV)
+    go = host(out[sel])
+    tau = tau_of(L)
+    qh, qIh, wh = f32(qs["q"][sel]), f32(qs["qI"][sel]), qs["w"][sel].cpu().numpy()
+    worst = 0.0
+    for i, t in enumerate(sample):
+        r = method.csa_row(t, qh[i], qIh[i], wh[i], se["values"], sI["values"], v, L.m, L.W, L.k, tau)
         ok, msg = topk_parity(gi[t], r["idx"], r["scores"])
         assert ok, f"row {t} (E_vis={r['e_vis']}): {msg}"
-        err = assert_close(host(out[t]), r["o"], atol=2e-2, what=f"row {t}")
-        print(f"  row {t}: E_vis={r['e_vis']} max abs err {err:.2e} (max |o| {np.abs(r['o']).max():.2f})",
-              flush=True)
+        err = assert_close(go[i], r["o"], atol=2e-2, what=f"row {t}")
+        worst = max(worst, err)
+    print(f"  {len(sample)} rows: top-k match, max abs err {worst:.2e}", flush=True)
 
 
 # ---------------------------------------------------------------- CSA+HCA pair decode, bf16, batch 32 at 128K
@@ -212,7 +228,8 @@ def test_pair_decode_128k_bf16():
     weights = gen.gpu_weights(wl, DEV)
     qc = gen.gpu_queries(wl, 0, B, DEV)
     qh = gen.gpu_queries(wl, 1, B, DEV)
-    sampled = [0, B - 1]
+    sampled = SEQ_SAMPLE
+    tau = tau_of(csa)
     ora = {}
     for b in sampled:
         s_c, s_h = gen.gpu_sequence_streams(wl, b, weights, DEV)
@@ -228,26 +245,27 @@ def test_pair_decode_128k_bf16():
         c["entries"][b] = upload_store(sc, "bf16", c["entries"])
         c["keys"][b:b + 1] = sk.to_key_tiles(dev(sI["values"], "bf16")[None])
         h["entries"][b] = upload_store(sh, "bf16", h["entries"])
-        ora[b] = (vc, vh, sc["values"], sI["values"], sh["values"])
+        # the oracle's rows now (they need only host data), keeping the big arrays short-lived
+        r = method.csa_row(t, f32(qc["q"][b]), f32(qc["qI"][b]), qc["w"][b].cpu().numpy(), sc["values"],
+                           sI["values"], vc, csa.m, csa.W, csa.k, tau)
+        rh = method.hca_row(t, f32(qh["q"][b]), sh["values"], vh, hca.m, hca.W, tau)
+        ora[b] = (r["idx"], r["scores"], r["o"], rh["o"])
+        del vc, vh, cc, magc, sc, cI, magI, sI, ch, magh, sh, r, rh
     rows = sk.RowSpec.decode(torch.full((B,), t, dtype=torch.int32, device=DEV), t)
     idx = torch.empty(B, csa.k, dtype=torch.int32, device=DEV)
     out_c = torch.empty(B, csa.H, csa.D, device=DEV)
     out_h = torch.empty(B, hca.H, hca.D, device=DEV)
-    tau = tau_of(csa)
     sk.csa_index_topk(rows, qc["qI"], qc["w"], c["keys"], idx, m=csa.m, W=csa.W, k=csa.k)
     sk.csa_attend(rows, qc["q"], c["entries"], idx, c["win"], out_c, m=csa.m, W=csa.W, softmax_scale=tau)
     sk.hca_attend(rows, qh["q"], h["entries"], h["win"], out_h, m=hca.m, W=hca.W, softmax_scale=tau)
     torch.cuda.synchronize()
     gi = host(idx)
     for b in sampled:
-        vc, vh, ent_c, keys_c, ent_h = ora[b]
-        r = method.csa_row(t, f32(qc["q"][b]), f32(qc["qI"][b]), qc["w"][b].cpu().numpy(), ent_c, keys_c, vc,
-                           csa.m, csa.W, csa.k, tau)
-        ok, msg = topk_parity(gi[b], r["idx"], r["scores"])
+        r_idx, r_scores, r_o, rh_o = ora[b]
+        ok, msg = topk_parity(gi[b], r_idx, r_scores)
         assert ok, f"seq {b}: {msg}"
-        ec = assert_close(host(out_c[b]), r["o"], atol=2e-2, what=f"CSA output seq {b}")
-        rh = method.hca_row(t, f32(qh["q"][b]), ent_h, vh, hca.m, hca.W, tau)
-        eh = assert_close(host(out_h[b]), rh["o"], atol=2e-2, what=f"HCA output seq {b}")
+        ec = assert_close(host(out_c[b]), r_o, atol=2e-2, what=f"CSA output seq {b}")
+        eh = assert_close(host(out_h[b]), rh_o, atol=2e-2, what=f"HCA output seq {b}")
         print(f"  seq {b}: CSA max abs err {ec:.2e}, HCA {eh:.2e}", flush=True)
 
 
@@ -266,7 +284,8 @@ def test_pair_decode_128k_mxfp4_keys():
     keys = c["keys_fp4"]
     weights = gen.gpu_weights(wl, DEV)
     qc = gen.gpu_queries(wl, 0, B, DEV)
-    sampled = [0, B - 1]
+    sampled = SEQ_SAMPLE
+    tau = tau_of(csa)
     ora = {}
     codes_all, scale_all = sk.mxfp4_unpack(keys)
     for b in sampled:
@@ -283,22 +302,22 @@ def test_pair_decode_128k_mxfp4_keys():
         keys.tiles[b:b + 1] = sk.mxfp4_pack(torch.from_numpy(st["codes"])[None],
                                             torch.from_numpy(st["scale"])[None]).tiles.to(DEV)
         ent = c["entries"][b].float().cpu().numpy().astype(np.float64)
-        ora[b] = (vc, ent, st["values"])
+        r = method.csa_row(t, f32(qc["q"][b]), f32(qc["qI"][b]), qc["w"][b].cpu().numpy(), ent, st["values"], vc,
+                           csa.m, csa.W, csa.k, tau)
+        ora[b] = (r["idx"], r["scores"], r["o"])
+        del vc, cI, magI, ent, r
     rows = sk.RowSpec.decode(torch.full((B,), t, dtype=torch.int32, device=DEV), t)
     idx = torch.empty(B, csa.k, dtype=torch.int32, device=DEV)
     out_c = torch.empty(B, csa.H, csa.D, device=DEV)
-    tau = tau_of(csa)
     sk.csa_index_topk(rows, qc["qI"], qc["w"], keys, idx, m=csa.m, W=csa.W, k=csa.k)
     sk.csa_attend(rows, qc["q"], c["entries"], idx, c["win"], out_c, m=csa.m, W=csa.W, softmax_scale=tau)
     torch.cuda.synchronize()
     gi = host(idx)
     for b in sampled:
-        vc, ent_c, keys_c = ora[b]
-        r = method.csa_row(t, f32(qc["q"][b]), f32(qc["qI"][b]), qc["w"][b].cpu().numpy(), ent_c, keys_c, vc,
-                           csa.m, csa.W, csa.k, tau)
-        ok, msg = topk_parity(gi[b], r["idx"], r["scores"])
+        r_idx, r_scores, r_o = ora[b]
+        ok, msg = topk_parity(gi[b], r_idx, r_scores)
         assert ok, f"seq {b}: {msg}"
-        ec = assert_close(host(out_c[b]), r["o"], atol=2e-2, what=f"CSA output seq {b}")
+        ec = assert_close(host(out_c[b]), r_o, atol=2e-2, what=f"CSA output seq {b}")
         print(f"  seq {b}: top-k matches, CSA max abs err {ec:.2e}", flush=True)
 
 

@@ -379,6 +379,55 @@ def test_index_topk_decode(keys_s, HI, DI, E_cap, positions, k):
         assert np.all(np.isneginf(gsc[r, len(sel):]))
 
 
+@pytest.mark.parametrize("case", ["all_tied", "zeros", "hot_region", "band_tied", "mixed_rows"])
+def test_index_topk_decode_hint_edges(case):
+    """Decode rows long enough for the selection to filter by the scoring kernel's
+    per-wave hint, with scores set exactly: a unit query on key dimension 0 and
+    one head weight make s_j = ReLU(k_j[0]).  Every score tied (the survivors
+    overflow the final block, which streams the row), mostly zeros (ties at 0), a
+    region of high scores (many survivors from one part of the row), a band tied
+    near the threshold, and rows whose waves hold too few keys for the bound (a
+    short row, an empty row, a row with k above its visible count)."""
+    print(f"index decode hint edge case {case}", flush=True)
+    rng = np.random.default_rng(abs(hash(case)) % 2**32)
+    E_cap, HI, DI, k = 70016, 64, 128, 2048
+    pos = [4 * 70000 + 131] * 3
+    if case == "mixed_rows":
+        pos = [4 * 70000 + 131, 4 * 1500 + 131, 100, 4 * 1800 + 131]
+    B = len(pos)
+    x0 = rng.normal(0, 1, (B, E_cap))
+    if case == "all_tied":
+        x0[:] = 1.5
+    elif case == "zeros":
+        x0[:] = -1.0
+        x0[:, rng.choice(E_cap, size=500, replace=False)] = rng.uniform(0.5, 2.0, (B, 500))
+    elif case == "hot_region":
+        x0[:, 30000:38192] += 5.0
+    elif case == "band_tied":
+        x0[:, rng.choice(E_cap, size=E_cap // 3, replace=False)] = 1.875
+    kv = rng_store(rng, (B, E_cap, DI), "bf16")
+    kv[:, :, 0] = torch.from_numpy(x0.astype(np.float32)).to(torch.bfloat16).float().numpy()
+    q = np.zeros((B, HI, DI), np.float32)
+    q[:, 0, 0] = 1.0
+    w = np.zeros((B, HI), np.float32)
+    w[:, 0] = 1.0
+    rows = sk.RowSpec.decode(dev_i32(pos), max(pos))
+    out_idx = torch.full((B, k), -7, device=DEV, dtype=torch.int32)
+    out_score = torch.zeros(B, k, device=DEV, dtype=torch.float32)
+    keys = sk.to_key_tiles(dev(kv, "bf16"))
+    sk.csa_index_topk(rows, dev(q, "bf16"), dev(w), keys, out_idx, m=4, W=128, k=k, out_score=out_score)
+    torch.cuda.synchronize()
+    gi, gsc = host(out_idx), host(out_score)
+    for r, t in enumerate(pos):
+        ev = min(method.entries_visible(t, 4, 128), E_cap)
+        s = method.index_scores(q[r], w[r], kv[r, :ev].astype(np.float64))
+        np.testing.assert_array_equal(s, np.maximum(kv[r, :ev, 0].astype(np.float64), 0.0))
+        ora = method.topk(s, k)
+        np.testing.assert_array_equal(gi[r], ora, err_msg=f"{case} row {r} (t={t}, E_vis={ev})")
+        sel = gi[r][gi[r] >= 0]
+        np.testing.assert_array_equal(gsc[r, :len(sel)], s[sel].astype(np.float32))
+
+
 CAUSAL_CASES = [
     ("bf16", 64, 128, 800, 3300, 64),
     ("f32", 4, 32, 300, 1300, 16),

@@ -166,3 +166,73 @@ def test_stack_decode_steps_replay_as_graph():
         graphs[i].replay()
         torch.cuda.synchronize()
         assert torch.equal(st._decode_ws[-1]["y"], eager[i]), f"step {i}"
+
+
+def test_stack_layer_by_layer_with_selection_cut():
+    """The CSA layer keeps 64 of up to 242 visible entries (k < E_vis), and every
+    layer is checked against the oracle on the GPU's own inputs to that step, so
+    no difference is carried from layer to layer: the stored entries and keys
+    against the oracle's pool of the GPU's streams (code space); the selection of
+    every row under the swap rule, with the oracle's scores over the GPU's keys
+    and indexer queries; every row's attention over the GPU's caches, queries and
+    selection within 2e-2 absolute; and the output projection of the GPU's
+    attention outputs (bf16 output: 1e-2 of the largest magnitude)."""
+    import dataclasses
+    from tests.compare import bf16_code_flips, topk_parity
+    csa = dataclasses.replace(CSA, k=64)
+    layers = stk.hybrid_schedule(4, csa, HCA)
+    w_host = make_weights(layers, seed=7)
+    rng = np.random.default_rng(8)
+    n = N
+    x = bf16(rng.standard_normal((B, n, D_MODEL)).astype(np.float32))
+    print(f"stack layer by layer B={B} N={n} layers={[L.kind for L in layers]} k={csa.k}", flush=True)
+    st = stk.Stack(layers, [to_dev(w) for w in w_host], D_MODEL, B, N_max=n + 8)
+    rec = []
+    outs = st.prefill(torch.from_numpy(x).to(DEV).to(torch.bfloat16), record=rec)
+    torch.cuda.synchronize()
+    cut_rows = 0
+    for li, L in enumerate(layers):
+        w, t = w_host[li], rec[li]["t"]
+        tau = 1.0 / np.sqrt(L.d_h)
+        o_gpu = host(rec[li]["o"]).reshape(B, n, L.H, L.D)
+        y_gpu = host(outs[li])
+        worst = 0.0
+        for b in range(B):
+            r = slice(b * n, (b + 1) * n)
+            v, g = host(t["v"][r]), host(t["g"][r])
+            c = method.compress(v, g, w["bpos"], L.m, L.o)
+            se = method.store_entries(c, "bf16")
+            E = c.shape[0]
+            ent = host(st.caches[li]["entries"][b])[:E]
+            _, unexp = bf16_code_flips(ent, c, se["values"], magnitude=method.compress(np.abs(v), g, w["bpos"], L.m, L.o))
+            assert unexp == 0, f"layer {li} seq {b}: {unexp} entry codes unexplained"
+            q = host(t["q"][r])
+            if L.kind == "csa":
+                vI, gI = host(t["vI"][r]), host(t["gI"][r])
+                cI = method.compress(vI, gI, w["bposI"], L.m, L.o)
+                sI = method.store_keys(cI, "bf16")
+                keys = host(sk.from_key_tiles(st.caches[li]["keys"][b:b + 1])[0])[:E]
+                _, unexp = bf16_code_flips(keys, cI, sI["values"],
+                                           magnitude=method.compress(np.abs(vI), gI, w["bposI"], L.m, L.o))
+                assert unexp == 0, f"layer {li} seq {b}: {unexp} key codes unexplained"
+                qI, wI, gidx = host(t["qI"][r]), host(t["w"][r]), host(rec[li]["idx"][b])
+            for p in range(n):
+                ev = min(method.entries_visible(p, L.m, L.W), E)
+                if L.kind == "csa":
+                    s = method.index_scores(qI[p], wI[p], keys[:ev])
+                    ok, msg = topk_parity(gidx[p], method.topk(s, L.k), s)
+                    assert ok, f"layer {li} seq {b} row {p} (E_vis={ev}): {msg}"
+                    sel = gidx[p][gidx[p] >= 0]
+                    cut_rows += int(len(sel) < ev)
+                    items = np.concatenate([ent[sel], v[method.window_positions(p, L.W)]])
+                else:
+                    items = np.concatenate([ent[:ev], v[method.window_positions(p, L.W)]])
+                oo, _, _ = method.attend(q[p], items, tau)
+                err = float(np.max(np.abs(o_gpu[b, p] - oo)))
+                worst = max(worst, err)
+                assert err <= 2e-2, f"layer {li} seq {b} row {p}: attention error {err:.3e}"
+            yo = np.stack([method.layer_output(o_gpu[b, p], w["W_o"], w.get("W_UV")) for p in range(n)])
+            ey = normwise(y_gpu[b], yo)
+            assert ey <= 1e-2, f"layer {li} seq {b}: output projection error {ey:.3e}"
+        print(f"  layer {li} ({L.kind}): attention max abs err {worst:.2e}", flush=True)
+    assert cut_rows > 1000, f"only {cut_rows} rows had more visible entries than k"
