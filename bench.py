@@ -45,7 +45,8 @@ def parse():
     ap.add_argument("--no-layer", action="store_true", help="skip the whole-layer decode step (projections) measurement")
     ap.add_argument("--no-stack", action="store_true", help="skip the HCA prefill and the layer-stack measurements")
     ap.add_argument("--no-fp4", action="store_true", help="skip the decode step with MXFP4 indexer keys")
-    ap.add_argument("--only", choices=["prefill", "1m", "layer", "stack", "fp4"], default=None,
+    ap.add_argument("--no-compress", action="store_true", help="skip the bulk compressor measurement")
+    ap.add_argument("--only", choices=["prefill", "1m", "layer", "stack", "fp4", "compress"], default=None,
                     help="run only that side measurement and print its record (for profiling its kernels)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy (reference for the HBM byte counters)")
@@ -729,6 +730,64 @@ def decode_1m_rate(dev, sk, torch, gen, steps: int = 20, replicas: int = 4, fp4:
             "hbm_frac": gbps / PEAK_HBM_GBPS}
 
 
+def compress_rates(dev, sk, torch, gen, iters: int = 5):
+    """The bulk compressors on one sequence's streams, as the caches are built: the
+    128K pair's (CSA latent and indexer streams into bf16 entries and key tiles in
+    one call, the HCA stream into bf16 entries) and the 1M pair's pre-population
+    (e4m3 entries with per-entry scales and unscaled e4m3 keys).  Algorithmic bytes
+    per call: each stream's values and gate logits read once, the entries (and
+    scales) written."""
+    from workloads import PAIR_DEC_128K_BF16, PAIR_DEC_1M_FP8
+    out = {}
+    stream = torch.cuda.current_stream()
+    for wl, f8 in ((PAIR_DEC_128K_BF16, False), (PAIR_DEC_1M_FP8, True)):
+        csa, hca = wl.layers
+        N = wl.N
+        Ec, Eh = N // csa.m, N // hca.m
+        weights = gen.gpu_weights(wl, dev)
+        s_c, s_h = gen.gpu_sequence_streams(wl, 0, weights, dev)
+        if f8:
+            u8, f8t = torch.uint8, torch.float8_e4m3fn
+            ent_c = torch.empty(1, Ec, csa.D, device=dev, dtype=u8).view(f8t)
+            keys = sk.key_tiles_empty(1, Ec, csa.D_I, u8, dev).view(f8t)
+            ent_h = torch.empty(1, Eh, hca.D, device=dev, dtype=u8).view(f8t)
+            sc_c, sc_h = torch.empty(1, Ec, device=dev), torch.empty(1, Eh, device=dev)
+            esz = 1
+        else:
+            bf = torch.bfloat16
+            ent_c = torch.empty(1, Ec, csa.D, device=dev, dtype=bf)
+            keys = sk.key_tiles_empty(1, Ec, csa.D_I, bf, dev)
+            ent_h = torch.empty(1, Eh, hca.D, device=dev, dtype=bf)
+            sc_c = sc_h = None
+            esz = 2
+        kv = sk.Pool(s_c["v"][None], s_c["g"][None], weights[0]["bpos"].contiguous(), ent_c, sc_c)
+        ix = sk.Pool(s_c["vI"][None], s_c["gI"][None], weights[0]["bposI"].contiguous(), keys,
+                     layout=sk.LAYOUT_KEY_TILES)
+        hk = sk.Pool(s_h["v"][None], s_h["g"][None], weights[1]["bpos"].contiguous(), ent_h, sc_h)
+        scale_b = 4 if f8 else 0
+        calls = {
+            "csa": (lambda: sk.csa_compress(kv, ix, m=csa.m, o=csa.o),
+                    2 * N * (csa.D + csa.D_I) * 2 + Ec * (csa.D * esz + scale_b + csa.D_I * esz)),
+            "hca": (lambda: sk.hca_compress(hk, m=hca.m, o=hca.o), 2 * N * hca.D * 2 + Eh * (hca.D * esz + scale_b)),
+        }
+        for name, (fn, nbytes) in calls.items():
+            fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(iters):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / iters
+            gbps = nbytes / (ms * 1e-3) / 1e9
+            out[f"{name}_{wl.name}"] = {"tokens": N, "entries": Ec if name == "csa" else Eh, "ms": ms,
+                                        "algorithmic_bytes": nbytes, "GBps": gbps, "frac": gbps / PEAK_HBM_GBPS}
+        del s_c, s_h, kv, ix, hk, ent_c, ent_h, keys
+        torch.cuda.empty_cache()
+    return out
+
+
 def decode_fp4_rate(dev, sk, torch, wl, c, h, qc, qh, steps: int = 50, replicas: int = 2):
     """The 128K-context decode step with the lightning indexer's keys in MXFP4 (FP4
     e2m1 codes in blocks of 32 channels with a power-of-two scale byte: 68 bytes per
@@ -817,12 +876,24 @@ def algorithmic_bytes(wl):
 
 
 def hbm_read_reference(torch, dev, gib: int = 2, iters: int = 10):
-    """Plain streaming references on the same GPU, timed with HIP events: torch's sum
-    over a bf16 tensor of `gib` GiB (each byte read once) and a device copy of that
-    tensor (each byte read once and written once).  `GBps` is the faster of the two."""
+    """Plain streaming references on the same GPU, timed with HIP events: the
+    hand-written streaming read (libsckv_bench.so: every byte of `gib` GiB read once
+    with 16-byte loads, 2048 blocks of 256 threads), torch's sum over the same bf16
+    tensor and a device copy of it (each byte read once and written once).  `GBps`
+    is the hand-written read's rate."""
+    import ctypes as C
     x = torch.ones(gib * (1 << 30) // 2, dtype=torch.bfloat16, device=dev)
     y = torch.empty_like(x)
     stream = torch.cuda.current_stream()
+    blib = C.CDLL(os.path.join(ROOT, "sequence_compressed_kv_amd", "libsckv_bench.so"))
+    blib.sckv_bench_stream_read.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int, C.c_void_p]
+    blib.sckv_bench_stream_read.restype = C.c_int
+    sink = torch.empty(2048, dtype=torch.int32, device=dev)
+
+    def kernel_read():
+        e = blib.sckv_bench_stream_read(x.data_ptr(), x.numel() * 2, sink.data_ptr(), 2048, stream.cuda_stream)
+        if e != 0:
+            raise RuntimeError(f"streaming-read reference failed: hipError {e}")
 
     def rate(fn, nbytes):
         fn()
@@ -836,10 +907,11 @@ def hbm_read_reference(torch, dev, gib: int = 2, iters: int = 10):
         return nbytes / (e0.elapsed_time(e1) / iters * 1e-3) / 1e9
 
     nb = x.numel() * 2
+    kread = rate(kernel_read, nb)
     read = rate(lambda: x.sum(), nb)
     copy = rate(lambda: y.copy_(x), 2 * nb)
     del x, y
-    return {"sum_read_GBps": read, "copy_GBps": copy, "bytes": nb, "GBps": max(read, copy)}
+    return {"stream_read_kernel_GBps": kread, "sum_read_GBps": read, "copy_GBps": copy, "bytes": nb, "GBps": kread}
 
 
 def host_cpu():
@@ -947,6 +1019,9 @@ def main():
     if args.only == "1m":
         print(json.dumps({"decode_1m_fp8": decode_1m_rate("cuda:0", sk, torch, gen),
                           "decode_1m_fp8_mxfp4_keys": decode_1m_rate("cuda:0", sk, torch, gen, fp4=True)}))
+        return
+    if args.only == "compress":
+        print(json.dumps({"compress": compress_rates("cuda:0", sk, torch, gen)}))
         return
     if args.only == "stack":
         print(json.dumps({"prefill_hca_attend": prefill_hca_attend_rate("cuda:0", sk, torch, PAIR_DEC_128K_BF16),
@@ -1068,6 +1143,9 @@ def main():
     rec["hbm_read_reference"] = rd
     rec["step_frac_of_read"] = step_gbps / rd["GBps"]
     rec["roofline"]["frac_of_read"] = score_gbps / rd["GBps"]
+    if not args.no_compress:
+        print("[bench] bulk compressors (128K and 1M sequences)", file=sys.stderr, flush=True)
+        rec["compress"] = compress_rates(dev, sk, torch, gen)
     if not args.no_append:
         print("[bench] steady-state decode with appends", file=sys.stderr, flush=True)
         rec["decode_append"] = decode_append_rate(dev, sk, torch, wl, c0, h0, tails, weights, qc, qh)

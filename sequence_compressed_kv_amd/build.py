@@ -16,6 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsckv.so")
+BENCH_LIB = os.path.join(PKG, "libsckv_bench.so")
+BENCH_SOURCE = "bench_read.hip"
 
 ARCH = os.environ.get("SCKV_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -45,8 +47,15 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    # the benchmark's streaming-read reference, a library of its own
+    bobj = _compile(BENCH_SOURCE)
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", bobj, "-o", BENCH_LIB + ".tmp"],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(BENCH_LIB + ".tmp", BENCH_LIB)
     if verbose:
-        print(f"built {LIB}", file=sys.stderr)
+        print(f"built {LIB} and {BENCH_LIB}", file=sys.stderr)
     return LIB
 
 

@@ -8,8 +8,8 @@
 // HBM streaming: lane groups of D/8 lanes own one entry, each lane 8 channels,
 // so every token row is read as one contiguous D-wide segment.  The softmax is
 // taken online with one exp per (token, channel): the larger of the running
-// maximum and the new logit sets which side is rescaled.  An entry's window is
-// pooled in 4 parts whose states are folded in order.  In decode, one token per
+// maximum and the new logit sets which side is rescaled.  A window of 64 tokens
+// or more is pooled in 4 parts (on 4 waves) whose states are folded in order.  In decode, one token per
 // sequence is appended to small rings of recent tokens, and the entry it
 // completes (one per m tokens) is pooled with the same arithmetic, its 4 parts on
 // 4 waves.
@@ -42,46 +42,62 @@ struct PoolState {
 };
 
 // Adds tokens [ia, ib) (ia >= 0) to st in token order; the bias row of token i is
-// i - i0.  With AHEAD == 2 the loads of two tokens are issued before their
-// updates (for few waves in flight; the arithmetic is the same).  The larger of
-// the running maximum and the new logit decides which side is rescaled, so each
+// i - i0.  The loads of AHEAD tokens are issued before their updates (the
+// arithmetic and its order do not depend on AHEAD).  The larger of the running
+// maximum and the new logit decides which side is rescaled, so each
 // (token, channel) costs one exp.
+// exp(-|d|) as the hardware base-2 exponential of -|d| log2(e): relative error
+// about |d| 2^-24 from rounding the product, below 1e-6 for every difference of
+// logits that still weighs in the sum (exp(-|d|) underflows past |d| ~ 87)
+__device__ __forceinline__ float pool_exp(float d) {
+  return __builtin_amdgcn_exp2f(__fmul_rn(-fabsf(d), 1.4426950408889634f));
+}
+
+__device__ __forceinline__ void pool_init(PoolState& st) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) { st.mx[c] = -INFINITY; st.l[c] = 0.f; st.acc[c] = 0.f; }
+}
+
+// One token into the state: gate logits g (bias bp0, bp1 added) and values v.
+__device__ __forceinline__ void pool_token(PoolState& st, const float (&g)[8], const float (&v)[8], f32x4 bp0,
+                                           f32x4 bp1) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const float a = __fadd_rn(g[c], c < 4 ? bp0[c] : bp1[c - 4]);
+    const float d = __fsub_rn(a, st.mx[c]);
+    const float x = pool_exp(d);
+    const bool up = d > 0.f;
+    const float sc = up ? x : 1.f;
+    const float p = up ? 1.f : x;
+    st.l[c] = fmaf(st.l[c], sc, p);
+    st.acc[c] = fmaf(st.acc[c], sc, __fmul_rn(p, v[c]));
+    st.mx[c] = fmaxf(st.mx[c], a);
+  }
+}
+
 template <int AHEAD, class Tok>
 __device__ __forceinline__ void pool_range(Tok tok, const float* __restrict__ bpos, int64_t i0, int64_t ia,
                                            int64_t ib, int D, int ch, bool active, PoolState& st) {
-#pragma unroll
-  for (int c = 0; c < 8; ++c) { st.mx[c] = -INFINITY; st.l[c] = 0.f; st.acc[c] = 0.f; }
-  auto update = [&](const float (&g)[8], const float (&v)[8], f32x4 bp0, f32x4 bp1) __attribute__((always_inline)) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const float a = __fadd_rn(g[c], c < 4 ? bp0[c] : bp1[c - 4]);
-      const float d = __fsub_rn(a, st.mx[c]);
-      const float x = expf(-fabsf(d));
-      const bool up = d > 0.f;
-      const float sc = up ? x : 1.f;
-      const float p = up ? 1.f : x;
-      st.l[c] = fmaf(st.l[c], sc, p);
-      st.acc[c] = fmaf(st.acc[c], sc, __fmul_rn(p, v[c]));
-      st.mx[c] = fmaxf(st.mx[c], a);
-    }
-  };
+  pool_init(st);
   for (int64_t i = ia; i < ib; i += AHEAD) {
-    const bool two = AHEAD == 2 && i + 1 < ib;
-    float g0[8] = {}, v0[8] = {}, g1[8] = {}, v1[8] = {};
-    f32x4 b00 = {}, b01 = {}, b10 = {}, b11 = {};
-    if (active) {
-      tok(i, g0, v0);
-      const f32x4* bp = reinterpret_cast<const f32x4*>(bpos + (i - i0) * D + ch);
-      b00 = bp[0];
-      b01 = bp[1];
-      if (two) {
-        tok(i + 1, g1, v1);
-        b10 = bp[D / 4];
-        b11 = bp[D / 4 + 1];
+    float g[AHEAD][8], v[AHEAD][8];
+    f32x4 b0[AHEAD], b1[AHEAD];
+#pragma unroll
+    for (int u = 0; u < AHEAD; ++u) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) { g[u][c] = 0.f; v[u][c] = 0.f; }
+      b0[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      b1[u] = b0[u];
+      if (active && i + u < ib) {
+        tok(i + u, g[u], v[u]);
+        const f32x4* bp = reinterpret_cast<const f32x4*>(bpos + (i + u - i0) * D + ch);
+        b0[u] = bp[0];
+        b1[u] = bp[1];
       }
     }
-    update(g0, v0, b00, b01);
-    if (two) update(g1, v1, b10, b11);
+#pragma unroll
+    for (int u = 0; u < AHEAD; ++u)
+      if (i + u < ib) pool_token(st, g[u], v[u], b0[u], b1[u]);
   }
 }
 
@@ -94,8 +110,8 @@ __device__ __forceinline__ void fold_state(PoolState& r, const PoolState& q) {
   for (int c = 0; c < 8; ++c) {
     const bool qe = q.mx[c] == -INFINITY, re = r.mx[c] == -INFINITY;
     const float M = fmaxf(r.mx[c], q.mx[c]);
-    const float sa = re ? 0.f : expf(__fsub_rn(r.mx[c], M));
-    const float sb = qe ? 0.f : expf(__fsub_rn(q.mx[c], M));
+    const float sa = re ? 0.f : pool_exp(__fsub_rn(r.mx[c], M));
+    const float sb = qe ? 0.f : pool_exp(__fsub_rn(q.mx[c], M));
     const float l = qe ? r.l[c] : (re ? q.l[c] : fmaf(r.l[c], sa, __fmul_rn(q.l[c], sb)));
     const float acc = qe ? r.acc[c] : (re ? q.acc[c] : fmaf(r.acc[c], sa, __fmul_rn(q.acc[c], sb)));
     r.l[c] = l;
@@ -202,9 +218,9 @@ __device__ __forceinline__ void store_entry(const PoolState& st, int ch, int G, 
   }
 }
 
-// MULTI: the window has 64 tokens or more (pooled in parts; chosen on the host by
-// the same rule as window_parts).
-template <int IN, int OUT, bool SCALED, bool MULTI>
+// Windows shorter than 64 tokens, pooled in one pass by D/8 lanes per entry, the
+// loads of two tokens in flight (windows of 64 or more: compress_parts_kernel).
+template <int IN, int OUT, bool SCALED>
 __global__ __launch_bounds__(256) void compress_kernel(
     const void* __restrict__ val, const void* __restrict__ gate, const float* __restrict__ bpos,
     void* __restrict__ out, float* __restrict__ out_scale, int64_t N, int D, int m, int o,
@@ -226,17 +242,44 @@ __global__ __launch_bounds__(256) void compress_kernel(
   PoolState r;
   int64_t ia, ib;
   part_range(i0, i1, 0, ia, ib);
-  pool_range<1>(tok, bpos, i0, ia, ib, D, ch, active, r);
-  if constexpr (MULTI) {
-    PoolState q;
-#pragma unroll 1
-    for (int p = 1; p < kParts; ++p) {
-      part_range(i0, i1, p, ia, ib);
-      pool_range<1>(tok, bpos, i0, ia, ib, D, ch, active, q);
-      fold_state(r, q);
-    }
-  }
+  pool_range<2>(tok, bpos, i0, ia, ib, D, ch, active, r);
   store_entry<OUT, SCALED>(r, ch, G, active, sub, b, e, D, E_cap, key_tiles, out, out_scale);
+}
+
+// Windows of 64 tokens or more (HCA): the 4 parts of each window on the 4 waves
+// of a block (wave q pools part q of the block's entries), folded in order by
+// wave 0 through LDS, the arithmetic of the decode append, with two tokens'
+// loads in flight per wave.
+template <int IN, int OUT, bool SCALED>
+__global__ __launch_bounds__(256) void compress_parts_kernel(
+    const void* __restrict__ val, const void* __restrict__ gate, const float* __restrict__ bpos,
+    void* __restrict__ out, float* __restrict__ out_scale, int64_t N, int D, int m, int o,
+    int64_t e_begin, int64_t e_count, int64_t E_cap, int G, int key_tiles) {
+  __shared__ PoolState parts[kParts - 1][kWave];
+  const int lane = lane_id(), w = wave_id();
+  const int epw = kWave / G;
+  const int slot = lane / G, sub = lane % G;
+  const int64_t e_local = (int64_t)blockIdx.x * epw + slot;
+  const bool active = e_local < e_count;
+  const int64_t e = e_begin + (active ? e_local : 0);
+  const int64_t b = blockIdx.y;
+  const int ch = sub * 8;
+  auto tok = [&](int64_t i, float (&g)[8], float (&v)[8]) __attribute__((always_inline)) {
+    const int64_t row = (b * N + i) * D + ch;
+    load8<IN>(gate, row, g);
+    load8<IN>(val, row, v);
+  };
+  const int64_t i0 = (int64_t)m * e - o, i1 = (int64_t)m * e + m;
+  PoolState st;
+  int64_t ia, ib;
+  part_range(i0, i1, w, ia, ib);
+  pool_range<2>(tok, bpos, i0, ia, ib, D, ch, active, st);
+  if (w > 0) parts[w - 1][lane] = st;
+  __syncthreads();
+  if (w != 0) return;
+#pragma unroll 1
+  for (int p = 1; p < kParts; ++p) fold_state(st, parts[p - 1][lane]);
+  store_entry<OUT, SCALED>(st, ch, G, active, sub, b, e, D, E_cap, key_tiles, out, out_scale);
 }
 
 // One stream of a decode append, as the kernel sees it.
@@ -320,15 +363,15 @@ static hipError_t launch_in(const sckv_pool_stream& s, int32_t B, int64_t N, int
   const int epw = kWave / G;
   const dim3 grid((unsigned)((e_count + 4 * epw - 1) / (4 * epw)), (unsigned)B);
   const dim3 block(256);
+  const int tiles = s.out_layout == SCKV_LAYOUT_KEY_TILES ? 1 : 0;
+  const dim3 grid_parts((unsigned)((e_count + epw - 1) / epw), (unsigned)B);
 #define SCKV_LAUNCH(OUT, SC)                                                                                   \
   if (m + o >= 64)                                                                                             \
-    hipLaunchKernelGGL((compress_kernel<IN, OUT, SC, true>), grid, block, 0, stream, s.val, s.gate, s.bpos,    \
-                       s.out, s.out_scale, N, s.D, m, o, e_begin, e_count, s.E_cap, G,                         \
-                       s.out_layout == SCKV_LAYOUT_KEY_TILES ? 1 : 0);                                         \
+    hipLaunchKernelGGL((compress_parts_kernel<IN, OUT, SC>), grid_parts, block, 0, stream, s.val, s.gate,      \
+                       s.bpos, s.out, s.out_scale, N, s.D, m, o, e_begin, e_count, s.E_cap, G, tiles);          \
   else                                                                                                         \
-    hipLaunchKernelGGL((compress_kernel<IN, OUT, SC, false>), grid, block, 0, stream, s.val, s.gate, s.bpos,   \
-                       s.out, s.out_scale, N, s.D, m, o, e_begin, e_count, s.E_cap, G,                         \
-                       s.out_layout == SCKV_LAYOUT_KEY_TILES ? 1 : 0)
+    hipLaunchKernelGGL((compress_kernel<IN, OUT, SC>), grid, block, 0, stream, s.val, s.gate, s.bpos,          \
+                       s.out, s.out_scale, N, s.D, m, o, e_begin, e_count, s.E_cap, G, tiles)
   switch (s.out_dtype) {
     case SCKV_F32: SCKV_LAUNCH(SCKV_F32, false); break;
     case SCKV_BF16: SCKV_LAUNCH(SCKV_BF16, false); break;
