@@ -27,7 +27,11 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0          # dense bf16 MFMA
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "index_score_decode.pair_decode_128k_bf16.counters.txt")
+PROFILES = os.path.join(ROOT, "profiles")
+STEP_COUNTERS = "pair_decode_128k_bf16.step_kernels.counters.txt"
+STEP_1M_COUNTERS = "pair_decode_1m_fp8.step_kernels.counters.txt"
+COMPRESS_COUNTERS = "compressors_128k_bf16_1m_fp8.counters.txt"
+PREFILL_COUNTERS = "csa_prefill_32k_bf16.kernels.counters.txt"
 
 
 def parse():
@@ -53,33 +57,43 @@ def parse():
     return ap.parse_args()
 
 
-def source_digest() -> str:
-    """sha256 of the sources of the indexer scoring kernel (names the kernel version
-    that a committed counter summary was taken from)."""
+def family_digest(family: str) -> str:
+    """sha256 of a kernel family's sources (csrc/<family>.hip + device_common.h +
+    sckv_internal.h): names the kernel version a committed counter summary was taken on."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("index.hip", "device_common.h"):
+    for f in (family + ".hip", "device_common.h", "sckv_internal.h"):
         with open(os.path.join(ROOT, "sequence_compressed_kv_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def counter_traffic(path: str):
-    """HBM bytes per launch of the indexer scoring kernel from a committed counter
-    summary (FETCH_SIZE and WRITE_SIZE passes, each scaled by a copy-kernel
-    calibration), or None when the summary is missing or was taken on other
-    kernel sources."""
+def kernel_counters(name: str) -> dict:
+    """Per-kernel HBM bytes per launch from a committed counter summary under
+    profiles/ (FETCH_SIZE and WRITE_SIZE passes, each scaled by a copy-kernel
+    calibration): {kernel: {"traffic_B", "fetch_B", "write_B", "alg_B", "ratio",
+    "profiled_us"}}.  A kernel whose sources no longer hash to the summary's digest
+    reports traffic null ("stale": true): its counters describe other code."""
+    out = {}
     try:
-        with open(path) as f:
-            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
+        with open(os.path.join(PROFILES, name)) as f:
+            lines = [ln.split(None, 1)[1] for ln in f if ln.startswith("counter: ")]
     except OSError:
-        return None
-    if kv.get("source_sha256", "").strip() != source_digest():
-        return None
-    try:
-        return float(kv["traffic_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+        return out
+    digests = {}
+    for ln in lines:
+        label, *fields = ln.split()
+        kv = dict(x.split("=", 1) for x in fields)
+        fam = kv["family"]
+        if fam not in digests:
+            digests[fam] = family_digest(fam)
+        fresh = kv["sha256"] == digests[fam]
+        fe, wr, alg = float(kv["fetch_B"]), float(kv["write_B"]), float(kv["alg_B"])
+        out[label] = {"traffic_B": fe + wr if fresh else None, "fetch_B": fe if fresh else None,
+                      "write_B": wr if fresh else None, "alg_B": alg,
+                      "ratio": (fe + wr) / alg if fresh else None, "profiled_us": float(kv["avg_us"]),
+                      "stale": not fresh}
+    return out
 
 
 def prefill_indexer_rate(dev, sk, torch, wl, iters: int = 5, fp4: bool = False):
@@ -120,7 +134,9 @@ def prefill_indexer_rate(dev, sk, torch, wl, iters: int = 5, fp4: bool = False):
     tf = flops / (ms * 1e-3) / 1e12
     return {"workload": wl.name + ("_mxfp4_keys" if fp4 else ""), "kernel": "index_score_causal_lds", "rows": T,
             "visible_pairs": pairs, "tflop": flops / 1e12, "ms": ms, "achieved_tflops": tf,
-            "peak_tflops": PEAK_BF16_TFLOPS, "frac": tf / PEAK_BF16_TFLOPS}
+            "peak_tflops": PEAK_BF16_TFLOPS, "frac": tf / PEAK_BF16_TFLOPS,
+            "traffic_B": kernel_counters(PREFILL_COUNTERS).get(
+                "index_score_causal_lds_" + ("mxfp4" if fp4 else "bf16") + "_keys", {}).get("traffic_B")}
 
 
 def prefill_attend_rate(dev, sk, torch, wl, iters: int = 3):
@@ -160,7 +176,8 @@ def prefill_attend_rate(dev, sk, torch, wl, iters: int = 3):
     ms = e0.elapsed_time(e1) / iters
     tf = flops / (ms * 1e-3) / 1e12
     return {"workload": wl.name, "kernel": "attend_dma512", "rows": T, "row_items": items, "tflop": flops / 1e12,
-            "ms": ms, "achieved_tflops": tf, "peak_tflops": PEAK_BF16_TFLOPS, "frac": tf / PEAK_BF16_TFLOPS}
+            "ms": ms, "achieved_tflops": tf, "peak_tflops": PEAK_BF16_TFLOPS, "frac": tf / PEAK_BF16_TFLOPS,
+            "traffic_B": kernel_counters(PREFILL_COUNTERS).get("attend_dma512_prefill", {}).get("traffic_B")}
 
 
 def prefill_projection_rate(dev, sk, torch, wl, iters: int = 3):
@@ -727,7 +744,7 @@ def decode_1m_rate(dev, sk, torch, gen, steps: int = 20, replicas: int = 4, fp4:
     return {"workload": wl.name + ("_mxfp4_keys" if fp4 else ""), "batch": 1, "context": wl.N,
             "key_bytes": key_bytes, "replicas": replicas, "ms_per_step": ms,
             "queries_per_s": 1.0 / (ms * 1e-3), "algorithmic_bytes": by, "hbm_GBps": gbps,
-            "hbm_frac": gbps / PEAK_HBM_GBPS}
+            "hbm_frac": gbps / PEAK_HBM_GBPS, "kernel_traffic": kernel_counters(STEP_1M_COUNTERS)}
 
 
 def compress_rates(dev, sk, torch, gen, iters: int = 5):
@@ -785,6 +802,7 @@ def compress_rates(dev, sk, torch, gen, iters: int = 5):
                                         "algorithmic_bytes": nbytes, "GBps": gbps, "frac": gbps / PEAK_HBM_GBPS}
         del s_c, s_h, kv, ix, hk, ent_c, ent_h, keys
         torch.cuda.empty_cache()
+    out["kernel_traffic"] = kernel_counters(COMPRESS_COUNTERS)
     return out
 
 
@@ -1119,6 +1137,7 @@ def main():
     score_ms = s0.elapsed_time(s1) / args.steps
 
     ab = algorithmic_bytes(wl)
+    ctr = kernel_counters(STEP_COUNTERS)
     score_gbps = ab["score"] * B / (score_ms * 1e-3) / 1e9
     step_gbps = ab["step"] * B / (ms * 1e-3) / 1e9
     rec = {
@@ -1136,7 +1155,9 @@ def main():
         "kernel_ms": parts,
         "roofline": {"bound": "hbm", "kernel": "index_score_decode", "launch_ms": score_ms, "achieved": score_gbps,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": score_gbps / PEAK_HBM_GBPS,
-                     "traffic": counter_traffic(TRAFFIC_SUMMARY), "bytes_per_launch": ab["score"] * B},
+                     "traffic": ctr.get("index_score_decode", {}).get("traffic_B"),
+                     "bytes_per_launch": ab["score"] * B},
+        "kernel_traffic": ctr,
         "wall_s_timed": wall,
     }
     rd = hbm_read_reference(torch, dev)

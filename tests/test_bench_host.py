@@ -33,3 +33,29 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, cwd=ROOT, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_committed_counter_summaries_parse():
+    """Every committed per-kernel counter summary names its kernels with calibrated
+    bytes, algorithmic bytes and a source digest."""
+    for name in (bench.STEP_COUNTERS, bench.STEP_1M_COUNTERS, bench.COMPRESS_COUNTERS, bench.PREFILL_COUNTERS):
+        c = bench.kernel_counters(name)
+        assert c, name
+        for label, v in c.items():
+            assert v["alg_B"] > 0 and v["profiled_us"] > 0, (name, label)
+            if not v["stale"]:
+                assert v["traffic_B"] == v["fetch_B"] + v["write_B"]
+    assert "index_score_decode" in bench.kernel_counters(bench.STEP_COUNTERS)
+
+
+def test_counter_summary_on_other_sources_reports_no_traffic(tmp_path, monkeypatch):
+    src = os.path.join(bench.PROFILES, bench.STEP_COUNTERS)
+    with open(src) as f:
+        text = f.read()
+    lines = [ln if not ln.startswith("counter: topk_kernel ") else ln.rsplit("sha256=", 1)[0] + "sha256=" + "0" * 64
+             for ln in text.splitlines()]
+    (tmp_path / "s.txt").write_text("\n".join(lines) + "\n")
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    c = bench.kernel_counters("s.txt")
+    assert c["topk_kernel"]["stale"] and c["topk_kernel"]["traffic_B"] is None
+    assert bench.kernel_counters("missing.txt") == {}
