@@ -661,32 +661,37 @@ __global__ __launch_bounds__(512) void attend_dma512(AttendParams p) {
 
 // Merge of split partials (maxima m_s in base-2 logit units):
 // o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
-// One block per (head, row).  The splits' (m_s, l_s) are read once, one thread
-// per split, and reduced across the block; the weights 2^(m_s - M) wait in
-// LDS while each thread accumulates four consecutive dims over the splits, in
-// split order, with eight splits' loads in flight.  The plan keeps the number
-// of splits at or below the target block count, kMaxSplits.
-
-__global__ __launch_bounds__(128) void attend_combine(const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
+// One block per (head, row, latent slice of `dslice` dims).  The splits' (m_s, l_s)
+// are read once, one thread per split, and reduced across the block; the weights
+// 2^(m_s - M) wait in LDS.  Each thread accumulates four consecutive dims over a
+// run of splits in split order, eight splits' loads in flight.  With SG = 1 one
+// thread takes all the splits (many rows: the grid alone fills the chip); with
+// SG > 1 (a few rows with many splits) SG thread groups take consecutive runs of
+// splits and their sums are added in run order through LDS.  The plan keeps the
+// number of splits at or below kMaxSplits.
+template <int SG>
+__global__ __launch_bounds__(256) void attend_combine(const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
                                                       void* __restrict__ out, float* __restrict__ lse, int H, int D,
-                                                      int nsplit, int out_dtype) {
+                                                      int nsplit, int out_dtype, int dslice) {
   __shared__ float wgt[kMaxSplits];
-  __shared__ float red[2][2];
+  __shared__ float red[2][4];
+  __shared__ f32x4 part[SG][SG > 1 ? 64 : 1];
   const int r = blockIdx.y, h = blockIdx.x;
+  const int nt = blockDim.x, nw = (nt + kWave - 1) / kWave;
   const int l = lane_id(), w = wave_id();
   const float* ml = ws_ml + ((int64_t)r * nsplit * H + h) * 2;           // split s at + s * 2 H
   float mloc = -INFINITY;
-  for (int s = threadIdx.x; s < nsplit; s += 128) {
+  for (int s = threadIdx.x; s < nsplit; s += nt) {
     wgt[s] = ml[(int64_t)s * 2 * H];
     mloc = fmaxf(mloc, wgt[s]);
   }
-  mloc = group_max4(mloc);
-  for (int o = 8; o >= 1; o >>= 1) mloc = fmaxf(mloc, shfl_xor_f(mloc, o));
+  for (int o = 32; o >= 1; o >>= 1) mloc = fmaxf(mloc, shfl_xor_f(mloc, o));
   if (l == 0) red[0][w] = mloc;
   __syncthreads();
-  const float M = fmaxf(red[0][0], red[0][1]);
+  float M = red[0][0];
+  for (int i = 1; i < nw; ++i) M = fmaxf(M, red[0][i]);
   float lloc = 0.f;
-  for (int s = threadIdx.x; s < nsplit; s += 128) {
+  for (int s = threadIdx.x; s < nsplit; s += nt) {
     const float ms = wgt[s];
     const float e = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
     lloc += e * ml[(int64_t)s * 2 * H + 1];
@@ -695,21 +700,34 @@ __global__ __launch_bounds__(128) void attend_combine(const float* __restrict__ 
   for (int o = 32; o >= 1; o >>= 1) lloc += shfl_xor_f(lloc, o);
   if (l == 0) red[1][w] = lloc;
   __syncthreads();
-  const float L = red[1][0] + red[1][1];
+  float L = red[1][0];
+  for (int i = 1; i < nw; ++i) L += red[1][i];
   const float inv = 1.f / L;
-  for (int d4 = threadIdx.x; d4 < D / 4; d4 += blockDim.x) {
-    const float* src = ws_o + ((int64_t)r * nsplit * H + h) * D + 4 * d4;      // split s at + s H D
+  const int td_n = nt / SG, td = threadIdx.x % td_n, sg = threadIdx.x / td_n;
+  const int per = (nsplit + SG - 1) / SG;
+  const int s_begin = sg * per, s_end = s_begin + per < nsplit ? s_begin + per : nsplit;
+  const int d_first = blockIdx.z * dslice;
+  // SG > 1: td_n == dslice / 4, so every thread makes exactly one pass (the barrier below)
+  for (int d4 = td; d4 < dslice / 4; d4 += td_n) {
+    const int dd = d_first + 4 * d4;
+    const float* src = ws_o + ((int64_t)r * nsplit * H + h) * D + dd;      // split s at + s H D
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    int s = 0;
-    for (; s + 8 <= nsplit; s += 8) {
+    int s = s_begin;
+    for (; s + 8 <= s_end; s += 8) {
       f32x4 v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const f32x4*>(src + (int64_t)(s + u) * H * D);
 #pragma unroll
       for (int u = 0; u < 8; ++u) acc += wgt[s + u] * v[u];
     }
-    for (; s < nsplit; ++s) acc += wgt[s] * *reinterpret_cast<const f32x4*>(src + (int64_t)s * H * D);
-    const int64_t off = ((int64_t)r * H + h) * D + 4 * d4;
+    for (; s < s_end; ++s) acc += wgt[s] * *reinterpret_cast<const f32x4*>(src + (int64_t)s * H * D);
+    if (SG > 1) {
+      part[sg][td] = acc;
+      __syncthreads();
+      if (sg != 0) break;
+      for (int g = 1; g < SG; ++g) acc += part[g][td];
+    }
+    const int64_t off = ((int64_t)r * H + h) * D + dd;
     if (out_dtype == SCKV_BF16) {
       uint16_t* o = static_cast<uint16_t*>(out) + off;
       const uint32_t lo = f32_to_bf16_rne(acc[0] * inv) | (f32_to_bf16_rne(acc[1] * inv) << 16);
@@ -719,7 +737,7 @@ __global__ __launch_bounds__(128) void attend_combine(const float* __restrict__ 
       *reinterpret_cast<f32x4*>(static_cast<float*>(out) + off) = acc * inv;
     }
   }
-  if (lse && threadIdx.x == 0) lse[(int64_t)r * H + h] = (M + log2f(L)) * 0.6931471805599453f;
+  if (lse && threadIdx.x == 0 && blockIdx.z == 0) lse[(int64_t)r * H + h] = (M + log2f(L)) * 0.6931471805599453f;
 }
 
 // fp32 path: one block per row, items 64 at a time through LDS.
@@ -916,8 +934,17 @@ hipError_t launch_attend(const sckv_attend_args& a, bool csa, const AttendPlan& 
   else launch_mfma_e<SCKV_BF16>(p, a.H, pl.hgroups, a.D, grid, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.nsplit == 1) return e;
-  hipLaunchKernelGGL(attend_combine, dim3(a.H, a.rows.R), dim3(128), 0, stream, p.ws_o, p.ws_ml, a.out, a.lse,
-                     a.H, a.D, pl.nsplit, a.out_dtype);
+  // a few rows with many splits: latent slices of 128 dims and 8 groups of splits
+  // per block, so the merge runs on about one block per CU; otherwise one block per
+  // (head, row) with each thread taking all the splits
+  if ((int64_t)a.rows.R * a.H < 512 && pl.nsplit >= 16) {
+    const int dslice = a.D < 128 ? a.D : 128;
+    hipLaunchKernelGGL(attend_combine<8>, dim3(a.H, a.rows.R, a.D / dslice), dim3(dslice / 4 * 8), 0, stream,
+                       p.ws_o, p.ws_ml, a.out, a.lse, a.H, a.D, pl.nsplit, a.out_dtype, dslice);
+  } else {
+    hipLaunchKernelGGL(attend_combine<1>, dim3(a.H, a.rows.R, 1), dim3(128), 0, stream, p.ws_o, p.ws_ml, a.out,
+                       a.lse, a.H, a.D, pl.nsplit, a.out_dtype, a.D);
+  }
   return hipGetLastError();
 }
 
