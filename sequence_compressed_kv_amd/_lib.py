@@ -11,7 +11,9 @@ from typing import Optional
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsckv.so")
+# SCKV_LIB_PATH names another build of the same library (the sanitized host build
+# the host checks run against); by default the library next to this file
+_LIB_PATH = os.environ.get("SCKV_LIB_PATH") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsckv.so")
 
 F32, BF16, E4M3, MXFP4 = 0, 1, 2, 3
 ROWS_DECODE, ROWS_CAUSAL = 0, 1

@@ -413,3 +413,25 @@ def test_noalloc_index_rejects_rows_beyond_its_scratch(L):
     # invalid arguments keep their own status
     bad = idx_args(k=0)
     assert L.csa_index_topk_noalloc(C.byref(bad), None) == 2
+
+
+@pytest.mark.skipif(bool(os.environ.get("SCKV_LIB_PATH")), reason="this run already loads another build")
+def test_host_checks_under_address_and_undefined_behaviour_sanitizers():
+    """Every check above again, in a child process, against a host-only build of the
+    library with AddressSanitizer and UndefinedBehaviorSanitizer (the runtime
+    preloaded): the argument checks, plan arithmetic and error paths must neither
+    touch memory they do not own nor hit undefined behaviour."""
+    import subprocess
+    import sys
+
+    import sanitized_build
+    lib = sanitized_build.build()
+    env = dict(os.environ, LD_PRELOAD=sanitized_build.runtime(), SCKV_LIB_PATH=lib,
+               ASAN_OPTIONS="detect_leaks=0:halt_on_error=1:abort_on_error=0",
+               UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
+    r = subprocess.run([sys.executable, "-m", "pytest", os.path.abspath(__file__), "-q", "-x", "-m", "not gpu",
+                        "-p", "no:cacheprovider"], env=env, capture_output=True, text=True, cwd=ROOT, timeout=900)
+    out = r.stdout + r.stderr
+    assert r.returncode == 0, out[-4000:]
+    assert "AddressSanitizer" not in out and "runtime error" not in out, out[-4000:]
+    assert " passed" in r.stdout
