@@ -6,17 +6,34 @@
 // "CSA" (4:1, learned pool, overlapping windows) and "HCA" (128:1)).
 //
 // HBM streaming: lane groups of D/8 lanes own one entry, each lane 8 channels,
-// so every token row is read as one contiguous D-wide segment.  The softmax is
-// taken online with one exp per (token, channel): the larger of the running
-// maximum and the new logit sets which side is rescaled.  A window of 64 tokens
-// or more is pooled in 4 parts (on 4 waves) whose states are folded in order.  In decode, one token per
-// sequence is appended to small rings of recent tokens, and the entry it
-// completes (one per m tokens) is pooled with the same arithmetic, its 4 parts on
-// 4 waves.
+// so every token row is read as one contiguous D-wide segment.
+//  - 4:1 windows with overlap 4 (CSA): every 4-token block belongs to two
+//    windows; a lane group walks a run of consecutive entries, reads each block
+//    once and pools it once into two half-window sums with one exp per (token,
+//    channel) (the softmax factored per block, below).
+//  - Other windows: the softmax is taken online with one exp per (token,
+//    channel), the larger of the running maximum and the new logit setting which
+//    side is rescaled; a window of 64 tokens or more (HCA) is pooled in 4 parts
+//    (on 4 waves) whose states are folded in order.
+// In decode, one token per sequence is appended to small rings of recent tokens,
+// and the entry it completes (one per m tokens) is pooled with the bulk kernel's
+// arithmetic, so appends and bulk pooling store the same bits.
 #include "device_common.h"
 #include "sckv_internal.h"
 
+// Every rounding in this file is written out: a product or sum is rounded on its
+// own and fused multiply-adds are explicit fmaf calls.  Contraction is switched
+// off for the file, and the rounded operations below are defined here (HIP's
+// __fmul_rn / __fadd_rn are plain operators compiled under the header's own
+// contraction setting), so the bulk and decode kernels round alike and store the
+// same bits.
+#pragma clang fp contract(off)
+
 namespace sckv {
+
+__device__ __forceinline__ float rmul(float a, float b) { return a * b; }
+__device__ __forceinline__ float radd(float a, float b) { return a + b; }
+__device__ __forceinline__ float rsub(float a, float b) { return a - b; }
 
 template <int IN>
 __device__ __forceinline__ void load8(const void* base, int64_t elem, float (&x)[8]) {
@@ -50,7 +67,7 @@ struct PoolState {
 // about |d| 2^-24 from rounding the product, below 1e-6 for every difference of
 // logits that still weighs in the sum (exp(-|d|) underflows past |d| ~ 87)
 __device__ __forceinline__ float pool_exp(float d) {
-  return __builtin_amdgcn_exp2f(__fmul_rn(-fabsf(d), 1.4426950408889634f));
+  return __builtin_amdgcn_exp2f(rmul(-fabsf(d), 1.4426950408889634f));
 }
 
 __device__ __forceinline__ void pool_init(PoolState& st) {
@@ -63,14 +80,14 @@ __device__ __forceinline__ void pool_token(PoolState& st, const float (&g)[8], c
                                            f32x4 bp1) {
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
-    const float a = __fadd_rn(g[c], c < 4 ? bp0[c] : bp1[c - 4]);
-    const float d = __fsub_rn(a, st.mx[c]);
+    const float a = radd(g[c], c < 4 ? bp0[c] : bp1[c - 4]);
+    const float d = rsub(a, st.mx[c]);
     const float x = pool_exp(d);
     const bool up = d > 0.f;
     const float sc = up ? x : 1.f;
     const float p = up ? 1.f : x;
     st.l[c] = fmaf(st.l[c], sc, p);
-    st.acc[c] = fmaf(st.acc[c], sc, __fmul_rn(p, v[c]));
+    st.acc[c] = fmaf(st.acc[c], sc, rmul(p, v[c]));
     st.mx[c] = fmaxf(st.mx[c], a);
   }
 }
@@ -110,10 +127,10 @@ __device__ __forceinline__ void fold_state(PoolState& r, const PoolState& q) {
   for (int c = 0; c < 8; ++c) {
     const bool qe = q.mx[c] == -INFINITY, re = r.mx[c] == -INFINITY;
     const float M = fmaxf(r.mx[c], q.mx[c]);
-    const float sa = re ? 0.f : pool_exp(__fsub_rn(r.mx[c], M));
-    const float sb = qe ? 0.f : pool_exp(__fsub_rn(q.mx[c], M));
-    const float l = qe ? r.l[c] : (re ? q.l[c] : fmaf(r.l[c], sa, __fmul_rn(q.l[c], sb)));
-    const float acc = qe ? r.acc[c] : (re ? q.acc[c] : fmaf(r.acc[c], sa, __fmul_rn(q.acc[c], sb)));
+    const float sa = re ? 0.f : pool_exp(rsub(r.mx[c], M));
+    const float sb = qe ? 0.f : pool_exp(rsub(q.mx[c], M));
+    const float l = qe ? r.l[c] : (re ? q.l[c] : fmaf(r.l[c], sa, rmul(q.l[c], sb)));
+    const float acc = qe ? r.acc[c] : (re ? q.acc[c] : fmaf(r.acc[c], sa, rmul(q.acc[c], sb)));
     r.l[c] = l;
     r.acc[c] = acc;
     r.mx[c] = M;
@@ -144,12 +161,9 @@ __device__ __forceinline__ void part_range(int64_t i0, int64_t i1, int q, int64_
 // group (the e4m3 scale is reduced over them).  Lanes with active == false take
 // part in the reduction but store nothing.
 template <int OUT, bool SCALED>
-__device__ __forceinline__ void store_entry(const PoolState& st, int ch, int G, bool active, int sub, int64_t b,
-                                            int64_t e, int D, int64_t E_cap, int key_tiles, void* __restrict__ out,
-                                            float* __restrict__ out_scale) {
-  float cv[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) cv[c] = st.acc[c] / st.l[c];
+__device__ __forceinline__ void store_values(const float (&cv)[8], int ch, int G, bool active, int sub, int64_t b,
+                                             int64_t e, int D, int64_t E_cap, int key_tiles, void* __restrict__ out,
+                                             float* __restrict__ out_scale) {
 
   // rows: [E_cap][D]; key tiles: [E_cap/32][D/8][32][8] (8 channels of 32 entries contiguous)
   const int64_t orow = key_tiles ? b * E_cap * D + (((e >> 5) * (D >> 3) + (ch >> 3)) * 32 + (e & 31)) * 8
@@ -205,10 +219,11 @@ __device__ __forceinline__ void store_entry(const PoolState& st, int ch, int G, 
       for (int s = 1; s < G; s <<= 1) amax = fmaxf(amax, shfl_xor_f(amax, s));
       scale = amax > 0.f ? amax / 448.0f : 1.0f;
     }
+    const float rscale = 1.0f / scale;
     u32x2 r = {0u, 0u};
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const uint32_t q = f32_to_e4m3_sat(SCALED ? cv[c] / scale : cv[c]);
+      const uint32_t q = f32_to_e4m3_sat(SCALED ? rmul(cv[c], rscale) : cv[c]);
       r[c >> 2] |= q << ((c & 3) * 8);
     }
     if (active) {
@@ -216,6 +231,177 @@ __device__ __forceinline__ void store_entry(const PoolState& st, int ch, int G, 
       if (SCALED && sub == 0) out_scale[b * E_cap + e] = scale;
     }
   }
+}
+
+// Stores the entry of an online-softmax state (the pooled value of each channel is
+// its weighted sum over its normaliser).
+template <int OUT, bool SCALED>
+__device__ __forceinline__ void store_entry(const PoolState& st, int ch, int G, bool active, int sub, int64_t b,
+                                            int64_t e, int D, int64_t E_cap, int key_tiles, void* __restrict__ out,
+                                            float* __restrict__ out_scale) {
+  float cv[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) cv[c] = st.acc[c] / st.l[c];
+  store_values<OUT, SCALED>(cv, ch, G, active, sub, b, e, D, E_cap, key_tiles, out, out_scale);
+}
+
+// ------------------------------------------------------------------ overlapping 4:1 windows
+// CSA pooling (m = 4, overlap o = 4): entry e pools tokens [4e - 4, 4e + 4), token
+// blocks e - 1 and e (block k = tokens 4k .. 4k+3), with the bias rows 0..3 on
+// block e - 1 and 4..7 on block e, so every block belongs to two windows.  The
+// softmax is factored per block: with s_k the block's largest gate logit (per
+// channel) and u_p = exp(Bpos[p] - max_p Bpos[p]),
+//   exp(g_i + Bpos[p] - const) = exp(g_i - s_k) u_p exp(s_k - S),  S = max(s_{e-1}, s_e),
+// so one exp per (token, channel) serves both windows: each block keeps two
+// half-window sums (sum of w and of w v, w = exp(g_i - s_k) u_p) for its two bias
+// halves, and an entry joins the previous block's first-half sums to its own
+// block's second-half sums with the factors exp(s_k - S), then divides.  The
+// common factor cancels in the quotient.  Exact in real arithmetic; in fp32 a
+// weight below 2^-126 of the window's largest is lost, which needs a spread of
+// the bias rows of more than about 60 (the largest weight is at least
+// exp(-spread)): such channels take the online path.  The bulk kernel and the
+// decode append share these functions, so both store the same bits.
+constexpr int kOvM = 4;                       // tokens per block (m = o = 4)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kMaxBiasSpread = 60.0f;
+constexpr int kOvMaxD = 512;                  // widest latent the bulk kernel's factor table holds
+
+// Block maximum and per-token factors exp(g_t - s) (base 2, log2 e folded in).
+__device__ __forceinline__ void ov_block(const float (&g)[kOvM][8], float (&s)[8], float (&E)[kOvM][8]) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    s[c] = fmaxf(fmaxf(g[0][c], g[1][c]), fmaxf(g[2][c], g[3][c]));
+    const float sl = rmul(s[c], kLog2e);
+#pragma unroll
+    for (int t = 0; t < kOvM; ++t) E[t][c] = __builtin_amdgcn_exp2f(fmaf(g[t][c], kLog2e, -sl));
+  }
+}
+
+// Half-window sums of one block for the bias rows u[0..3] (token order).
+__device__ __forceinline__ void ov_half(const float (&E)[kOvM][8], const float (&v)[kOvM][8],
+                                        const float (&u)[kOvM][8], float (&l)[8], float (&acc)[8]) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    float w = rmul(E[0][c], u[0][c]);
+    float ls = w, as = rmul(w, v[0][c]);
+#pragma unroll
+    for (int t = 1; t < kOvM; ++t) {
+      w = rmul(E[t][c], u[t][c]);
+      ls = radd(ls, w);
+      as = fmaf(w, v[t][c], as);
+    }
+    l[c] = ls;
+    acc[c] = as;
+  }
+}
+
+// Entry from the first half (previous block: max sp, sums lp, ap) and the second
+// half (this block: s, l, a).  A missing previous block has sp = -inf, lp = ap = 0.
+__device__ __forceinline__ void ov_entry(const float (&sp)[8], const float (&lp)[8], const float (&ap)[8],
+                                         const float (&s)[8], const float (&l)[8], const float (&a)[8],
+                                         float (&cv)[8]) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    // the half with the larger maximum keeps factor 1, the other exp(-|difference|)
+    // (a missing previous block: exp2(-inf) = 0)
+    const float d = rsub(sp[c], s[c]);
+    const float f = __builtin_amdgcn_exp2f(rmul(-fabsf(d), kLog2e));
+    const bool prev_up = d > 0.f;
+    const float f1 = prev_up ? 1.f : f;
+    const float f2 = prev_up ? f : 1.f;
+    const float lt = fmaf(lp[c], f1, rmul(l[c], f2));
+    const float at = fmaf(ap[c], f1, rmul(a[c], f2));
+    cv[c] = rmul(at, __builtin_amdgcn_rcpf(lt));
+  }
+}
+
+// Bias factors u[p] = exp(Bpos[p][c] - max_p Bpos[p][c]) of one channel c (rows
+// 0 .. 7), and whether the rows spread by at most kMaxBiasSpread.
+__device__ __forceinline__ bool ov_bias_channel(const float* __restrict__ bpos, int D, int c, float (&u)[2 * kOvM]) {
+  float b[2 * kOvM];
+#pragma unroll
+  for (int p = 0; p < 2 * kOvM; ++p) b[p] = bpos[(int64_t)p * D + c];
+  float hi = b[0], lo = b[0];
+#pragma unroll
+  for (int p = 1; p < 2 * kOvM; ++p) { hi = fmaxf(hi, b[p]); lo = fminf(lo, b[p]); }
+  const float hl = rmul(hi, kLog2e);
+#pragma unroll
+  for (int p = 0; p < 2 * kOvM; ++p) u[p] = __builtin_amdgcn_exp2f(fmaf(b[p], kLog2e, -hl));
+  return rsub(hi, lo) <= kMaxBiasSpread;
+}
+
+// The factors of this lane's channels ch .. ch+7, and whether every one of the
+// entry's D channels (G lanes from group lane 0) stays within the spread.
+__device__ __forceinline__ bool ov_bias(const float* __restrict__ bpos, int D, int ch, int G,
+                                        float (&u)[2 * kOvM][8]) {
+  bool ok = true;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    float uc[2 * kOvM];
+    ok = ov_bias_channel(bpos, D, ch + c, uc) && ok;
+#pragma unroll
+    for (int p = 0; p < 2 * kOvM; ++p) u[p][c] = uc[p];
+  }
+  // all lanes of the entry's group agree (G is a power of two, the group G-aligned)
+  int okall = ok ? 1 : 0;
+  for (int sft = 1; sft < G; sft <<= 1) okall &= __shfl_xor(okall, sft, kWave);
+  return okall != 0;
+}
+
+// A block's gate and value rows for one lane's 8 channels as loaded (bf16 pairs
+// or fp32), unpacked only when used, so a prefetched block costs few registers.
+template <int IN>
+struct RawBlock {
+  static constexpr int W = IN == SCKV_BF16 ? 1 : 2;   // 16-byte words per 8 channels
+  u32x4 g[kOvM][W], v[kOvM][W];
+};
+
+template <int IN>
+__device__ __forceinline__ void raw_load(const void* base, int64_t elem, u32x4 (&w)[RawBlock<IN>::W]) {
+  if constexpr (IN == SCKV_BF16) {
+    w[0] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + elem);
+  } else {
+    const u32x4* q = reinterpret_cast<const u32x4*>(static_cast<const float*>(base) + elem);
+    w[0] = q[0];
+    w[1] = q[1];
+  }
+}
+
+template <int IN>
+__device__ __forceinline__ void raw_unpack(const u32x4 (&w)[RawBlock<IN>::W], float (&x)[8]) {
+  if constexpr (IN == SCKV_BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[0][i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[0][i] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { x[i] = __uint_as_float(w[0][i]); x[4 + i] = __uint_as_float(w[1][i]); }
+  }
+}
+
+template <int IN>
+__device__ __forceinline__ void raw_block_load(const void* gate, const void* val, int64_t row0, int D,
+                                               RawBlock<IN>& rb) {
+#pragma unroll
+  for (int t = 0; t < kOvM; ++t) {
+    raw_load<IN>(gate, row0 + (int64_t)t * D, rb.g[t]);
+    raw_load<IN>(val, row0 + (int64_t)t * D, rb.v[t]);
+  }
+}
+
+template <int IN>
+__device__ __forceinline__ void raw_block_unpack(const RawBlock<IN>& rb, float (&g)[kOvM][8], float (&v)[kOvM][8]) {
+#pragma unroll
+  for (int t = 0; t < kOvM; ++t) {
+    raw_unpack<IN>(rb.g[t], g[t]);
+    raw_unpack<IN>(rb.v[t], v[t]);
+  }
+}
+
+__device__ __forceinline__ const float (&ov_rows(const float (&u)[2 * kOvM][8], int half))[kOvM][8] {
+  return *reinterpret_cast<const float(*)[kOvM][8]>(&u[kOvM * half]);
 }
 
 // Windows shorter than 64 tokens, pooled in one pass by D/8 lanes per entry, the
@@ -244,6 +430,134 @@ __global__ __launch_bounds__(256) void compress_kernel(
   part_range(i0, i1, 0, ia, ib);
   pool_range<2>(tok, bpos, i0, ia, ib, D, ch, active, r);
   store_entry<OUT, SCALED>(r, ch, G, active, sub, b, e, D, E_cap, key_tiles, out, out_scale);
+}
+
+// Both half-window sums of one block straight from its loaded rows: the block
+// maximum first, then token by token the factor exp(g - s) and its two weighted
+// terms, with the bias factors of rows 4..7 (second half: la, aa) and rows 0..3
+// (first half of the next entry: lb, ab) read from the table in LDS.  The same
+// operations in the same order as ov_block and ov_half, so the same bits, with
+// far fewer values live at once.
+template <int IN>
+__device__ __forceinline__ void ov_block_sums(const RawBlock<IN>& rb, const float* u_sh, int D, int ch,
+                                              float (&s)[8], float (&la)[8], float (&aa)[8], float (&lb)[8],
+                                              float (&ab)[8]) {
+  {
+    float x[8];
+    raw_unpack<IN>(rb.g[0], x);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) s[c] = x[c];
+#pragma unroll
+    for (int t = 1; t < kOvM; ++t) {
+      raw_unpack<IN>(rb.g[t], x);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) s[c] = fmaxf(s[c], x[c]);
+    }
+  }
+  float sl[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) sl[c] = rmul(s[c], kLog2e);
+#pragma unroll
+  for (int t = 0; t < kOvM; ++t) {
+    float g[8], v[8], ua[8], ub[8];
+    raw_unpack<IN>(rb.g[t], g);
+    raw_unpack<IN>(rb.v[t], v);
+    {
+      const f32x4* qa = reinterpret_cast<const f32x4*>(&u_sh[(kOvM + t) * D + ch]);
+      const f32x4* qb = reinterpret_cast<const f32x4*>(&u_sh[t * D + ch]);
+      const f32x4 a0 = qa[0], a1 = qa[1], b0 = qb[0], b1 = qb[1];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) { ua[c] = a0[c]; ua[4 + c] = a1[c]; ub[c] = b0[c]; ub[4 + c] = b1[c]; }
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float E = __builtin_amdgcn_exp2f(fmaf(g[c], kLog2e, -sl[c]));
+      const float wa = rmul(E, ua[c]), wb = rmul(E, ub[c]);
+      if (t == 0) {
+        la[c] = wa;
+        aa[c] = rmul(wa, v[c]);
+        lb[c] = wb;
+        ab[c] = rmul(wb, v[c]);
+      } else {
+        la[c] = radd(la[c], wa);
+        aa[c] = fmaf(wa, v[c], aa[c]);
+        lb[c] = radd(lb[c], wb);
+        ab[c] = fmaf(wb, v[c], ab[c]);
+      }
+    }
+  }
+}
+
+// Overlapping 4:1 windows (m = o = 4) by the factored softmax: a slot of G = D/8
+// lanes pools a run of J consecutive entries, loading each token block once (the
+// next block's loads in flight while the current one is pooled) and carrying the
+// block's first-half sums into the next entry.  Channels whose bias rows spread
+// too far take the online path entry by entry.
+template <int IN, int OUT, bool SCALED>
+__global__ __launch_bounds__(256) void compress_overlap_kernel(
+    const void* __restrict__ val, const void* __restrict__ gate, const float* __restrict__ bpos,
+    void* __restrict__ out, float* __restrict__ out_scale, int64_t N, int D, int64_t e_begin, int64_t e_count,
+    int64_t E_cap, int G, int key_tiles, int J) {
+  const int lane = lane_id();
+  const int epw = kWave / G;
+  const int slot = lane / G, sub = lane % G;
+  const int64_t first = ((int64_t)blockIdx.x * (4 * epw) + wave_id() * epw + slot) * J;   // first local entry
+  const int64_t b = blockIdx.y;
+  const int ch = sub * 8;
+  // the bias factors of all D channels, [row][channel], shared by the block's slots
+  __shared__ __attribute__((aligned(16))) float u_sh[2 * kOvM * kOvMaxD];
+  bool ok = true;
+  for (int c = threadIdx.x; c < D; c += blockDim.x) {
+    float uc[2 * kOvM];
+    ok = ov_bias_channel(bpos, D, c, uc) && ok;
+#pragma unroll
+    for (int p = 0; p < 2 * kOvM; ++p) u_sh[p * D + c] = uc[p];
+  }
+  const bool fast = __syncthreads_and(ok ? 1 : 0) != 0;
+  if (first >= e_count) return;
+  if (!fast) {
+    auto tok = [&](int64_t i, float (&g)[8], float (&v)[8]) __attribute__((always_inline)) {
+      const int64_t row = (b * N + i) * D + ch;
+      load8<IN>(gate, row, g);
+      load8<IN>(val, row, v);
+    };
+    for (int j = 0; j < J && first + j < e_count; ++j) {
+      const int64_t e = e_begin + first + j;
+      const int64_t i0 = (int64_t)kOvM * e - kOvM, i1 = (int64_t)kOvM * e + kOvM;
+      PoolState r;
+      int64_t ia, ib;
+      part_range(i0, i1, 0, ia, ib);
+      pool_range<2>(tok, bpos, i0, ia, ib, D, ch, true, r);
+      store_entry<OUT, SCALED>(r, ch, G, true, sub, b, e, D, E_cap, key_tiles, out, out_scale);
+    }
+    return;
+  }
+  const int64_t e0 = e_begin + first;
+  const int64_t row_b = b * N * D + ch;            // token i's channels at row_b + i * D
+  float sp[8], lp[8], ap[8];                       // first-half state carried into the next entry
+  RawBlock<IN> rb;
+  if (e0 > 0) {
+    raw_block_load<IN>(gate, val, row_b + (e0 - 1) * kOvM * D, D, rb);
+    float la[8], aa[8];
+    ov_block_sums<IN>(rb, u_sh, D, ch, sp, la, aa, lp, ap);
+  } else {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) { sp[c] = -INFINITY; lp[c] = 0.f; ap[c] = 0.f; }
+  }
+  raw_block_load<IN>(gate, val, row_b + e0 * kOvM * D, D, rb);
+  for (int j = 0; j < J; ++j) {
+    const int64_t el = first + j;
+    if (el >= e_count) break;
+    const int64_t e = e_begin + el;
+    RawBlock<IN> cur = rb;
+    if (j + 1 < J && el + 1 < e_count) raw_block_load<IN>(gate, val, row_b + (e + 1) * kOvM * D, D, rb);
+    float s[8], la[8], aa[8], lb[8], ab[8], cv[8];
+    ov_block_sums<IN>(cur, u_sh, D, ch, s, la, aa, lb, ab);
+    ov_entry(sp, lp, ap, s, la, aa, cv);
+    store_values<OUT, SCALED>(cv, ch, G, true, sub, b, e, D, E_cap, key_tiles, out, out_scale);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) { sp[c] = s[c]; lp[c] = lb[c]; ap[c] = ab[c]; }
+  }
 }
 
 // Windows of 64 tokens or more (HCA): the 4 parts of each window on the 4 waves
@@ -340,6 +654,32 @@ __global__ __launch_bounds__(256) void append_kernel(AppendK s0, AppendK s1, int
       load8<IN>(s.val_ring, row, v);
     }
   };
+  if (m == kOvM && o == kOvM) {
+    // overlapping 4:1 windows: the bulk kernel's factored softmax on wave 0, with
+    // the bulk kernel's choice of path (the same bits either way)
+    if (w != 0) return;
+    float u[2 * kOvM][8];
+    if (ov_bias(s.bpos, D, ch, G, u)) {
+      float sp[8], lp[8], ap[8], g[kOvM][8], v[kOvM][8], E[kOvM][8];
+      if (e > 0) {
+#pragma unroll
+        for (int q = 0; q < kOvM; ++q) tok(kOvM * (e - 1) + q, g[q], v[q]);
+        ov_block(g, sp, E);
+        ov_half(E, v, ov_rows(u, 0), lp, ap);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) { sp[c] = -INFINITY; lp[c] = 0.f; ap[c] = 0.f; }
+      }
+#pragma unroll
+      for (int q = 0; q < kOvM; ++q) tok(kOvM * e + q, g[q], v[q]);
+      float sb[8], la[8], aa[8], cv[8];
+      ov_block(g, sb, E);
+      ov_half(E, v, ov_rows(u, 1), la, aa);
+      ov_entry(sp, lp, ap, sb, la, aa, cv);
+      store_values<OUT, SCALED>(cv, ch, G, active, lane, b, e, D, s.E_cap, s.key_tiles, s.out, s.out_scale);
+      return;
+    }
+  }
   const int64_t i0 = (int64_t)m * e - o, i1 = (int64_t)m * e + m;
   const int np = window_parts(i0, i1);                     // uniform
   PoolState st;
@@ -365,8 +705,17 @@ static hipError_t launch_in(const sckv_pool_stream& s, int32_t B, int64_t N, int
   const dim3 block(256);
   const int tiles = s.out_layout == SCKV_LAYOUT_KEY_TILES ? 1 : 0;
   const dim3 grid_parts((unsigned)((e_count + epw - 1) / epw), (unsigned)B);
+  // overlapping 4:1 windows: runs of J entries per slot (each run loads one block
+  // twice), J as large as keeps 2048 blocks in the grid
+  int J = 16;
+  auto ov_blocks = [&](int j) { return ((e_count + (int64_t)j * 4 * epw - 1) / ((int64_t)j * 4 * epw)) * B; };
+  while (J > 2 && ov_blocks(J) < 2048) J /= 2;
+  const dim3 grid_ov((unsigned)((e_count + (int64_t)J * 4 * epw - 1) / ((int64_t)J * 4 * epw)), (unsigned)B);
 #define SCKV_LAUNCH(OUT, SC)                                                                                   \
-  if (m + o >= 64)                                                                                             \
+  if (m == kOvM && o == kOvM)                                                                                  \
+    hipLaunchKernelGGL((compress_overlap_kernel<IN, OUT, SC>), grid_ov, block, 0, stream, s.val, s.gate,       \
+                       s.bpos, s.out, s.out_scale, N, s.D, e_begin, e_count, s.E_cap, G, tiles, J);             \
+  else if (m + o >= 64)                                                                                        \
     hipLaunchKernelGGL((compress_parts_kernel<IN, OUT, SC>), grid_parts, block, 0, stream, s.val, s.gate,      \
                        s.bpos, s.out, s.out_scale, N, s.D, m, o, e_begin, e_count, s.E_cap, G, tiles);          \
   else                                                                                                         \

@@ -31,27 +31,18 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 // ------------------------------------------------------------------ OCP e4m3 ("fn")
 // Saturating round-to-nearest-even fp32 -> e4m3 code.  Built from the format
 // definition: 3 mantissa bits, bias 7, subnormal step 2^-9, largest finite 448.
+// Normal range (|x| >= 2^-6): the fp32 bits rounded to nearest even at bit 20
+// (a carry moves into the exponent), exponent rebased from bias 127 to 7; below
+// 2^-6 the code is the count of 2^-9 steps.  Branch-free.
 __device__ __forceinline__ uint32_t f32_to_e4m3_sat(float x) {
   const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
-  float a = fminf(fabsf(x), 448.0f);
-  uint32_t code;
-  if (a < 0.015625f) {                       // below 2^-6: multiples of 2^-9 (q = 8 is 2^-6, code 8)
-    code = (uint32_t)__builtin_rintf(a * 512.0f);
-  } else {
-    int e = (int)((__float_as_uint(a) >> 23) & 0xff) - 127;     // a in [2^e, 2^(e+1))
-    float mant = a * __uint_as_float((uint32_t)(127 - e) << 23);  // exact: a / 2^e in [1, 2)
-    uint32_t q = (uint32_t)__builtin_rintf((mant - 1.0f) * 8.0f);
-    if (q == 8) { q = 0; ++e; }
-    code = ((uint32_t)(e + 7) << 3) | q;
-  }
-  return sign | code;
+  const float a = fminf(fabsf(x), 448.0f);
+  const uint32_t u = __float_as_uint(a);
+  const uint32_t normal = ((u + 0x7ffffu + ((u >> 20) & 1u)) >> 20) - (120u << 3);
+  const uint32_t sub = (uint32_t)__builtin_rintf(a * 512.0f);
+  return sign | (a < 0.015625f ? sub : normal);
 }
 
-// e4m3 code -> bf16 bits (exact: every e4m3 value is a bf16 value).
-// 8 e4m3 codes (little-endian in two dwords) -> 8 bf16 packed in four dwords,
-// by the gfx950 conversion instruction (two codes per instruction).  Every
-// e4m3 value is exact in bf16; with scale 1 the instruction decodes all finite
-// OCP e4m3 codes (subnormals included) to their exact values.
 __device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(u32x2 v) {
   u32x4 r;
   r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)v[0], 1.0f, false));

@@ -294,6 +294,54 @@ def test_csa_append_two_streams(kv_out, scaled):
         assert torch.equal(sa, sb)
 
 
+@pytest.mark.parametrize("D,outs,scaled", [(64, "bf16", False), (512, "e4m3", True)])
+def test_overlap_windows_with_wide_bias_spread(D, outs, scaled):
+    """4:1 overlapping windows whose position biases spread by more than 60 in some
+    channels (those entries take the online softmax): bulk and token-by-token
+    appends store the same bits, and both follow the oracle in code space."""
+    print(f"wide bias spread D={D} {outs} scaled={scaled}", flush=True)
+    rng = np.random.default_rng(41 + D)
+    B, N, P, m, o = 2, 160, 8, 4, 4
+    v = rng_store(rng, (B, N, D), "bf16")
+    g = rng_store(rng, (B, N, D), "bf16", 2.0)
+    bpos = rng.normal(0, 0.5, (m + o, D)).astype(np.float32)
+    bpos[0, 3], bpos[7, 3] = 33.0, -33.0                       # channel 3: spread 66
+    if D > 64:
+        bpos[2, D - 5], bpos[5, D - 5] = -40.0, 25.0           # a channel in the last lane group
+    E = N // m
+    tdt = torch.uint8 if outs == "e4m3" else torch.bfloat16
+    mk = (lambda: torch.zeros(B, E, D, device=DEV, dtype=tdt).view(torch.float8_e4m3fn)) if outs == "e4m3" else \
+        (lambda: torch.zeros(B, E, D, device=DEV, dtype=tdt))
+    out_a, out_b = mk(), mk()
+    sc_a = torch.zeros(B, E, device=DEV) if scaled else None
+    sc_b = torch.zeros(B, E, device=DEV) if scaled else None
+    vd, gd, bd = dev(v, "bf16"), dev(g, "bf16"), dev(bpos)
+    rv = torch.zeros(B, P, D, device=DEV, dtype=vd.dtype)
+    rg = torch.zeros(B, P, D, device=DEV, dtype=vd.dtype)
+    ar = torch.arange(B, device=DEV)
+    for c in range(N):
+        pos = dev_i32([c] * B)
+        a = sk.Append(pos, vd[ar, pos.long()].contiguous(), gd[ar, pos.long()].contiguous(), rv, rg, bd, out_a, sc_a)
+        sk.csa_append(a, m=m, o=o)
+    sk.csa_compress(sk.Pool(vd, gd, bd, out_b, sc_b), m=m, o=o)
+    torch.cuda.synchronize()
+    raw = (lambda t: t.view(torch.uint8)) if outs == "e4m3" else (lambda t: t)
+    assert torch.equal(raw(out_a), raw(out_b)), "appended entries differ from the bulk compressor's"
+    if scaled:
+        assert torch.equal(sc_a, sc_b)
+    for b in range(B):
+        c = method.compress(v[b], g[b], bpos, m, o)
+        mag = method.compress(np.abs(v[b]), g[b], bpos, m, o)
+        got = host(out_b[b])
+        if outs == "bf16":
+            st = method.store_entries(c, "bf16")
+            assert bf16_code_flips(got, c, st["values"], magnitude=mag)[1] == 0
+        else:
+            st = method.store_entries(c, "e4m3")
+            np.testing.assert_allclose(sc_b[b].cpu().numpy().astype(np.float64), st["scale"], rtol=2e-6)
+            assert e4m3_flips(got, st["codes"], c / st["scale"][:, None], mag / st["scale"][:, None])[1] == 0
+
+
 def test_compress_appends_only_requested_entries():
     rng = np.random.default_rng(5)
     B, N, D = 2, 256, 64
