@@ -96,6 +96,61 @@ def kernel_counters(name: str) -> dict:
     return out
 
 
+def step_graphs(torch, step, nvar: int, steps: int, per_graph: int = 10):
+    """HIP graphs that together run step(0) .. step(steps - 1) when replayed in
+    order: graphs of `chunk` consecutive steps (a multiple of nvar, the number of
+    input variants step(i) cycles through, so every chunk starts at variant 0),
+    then one of the remaining steps.  The library's kernels on preallocated
+    workspaces (no allocation or memset inside); captured after an eager pass on a
+    side stream of default priority.  Returns [(graph, n_steps), ...]."""
+    chunk = max(nvar, (per_graph // nvar) * nvar)
+    chunk = min(chunk, (steps // nvar) * nvar) or nvar
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(nvar):
+            step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    def capture(n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                step(i)
+        return g
+
+    full = capture(chunk) if steps >= chunk else None
+    plan = [(full, chunk)] * (steps // chunk) if full is not None else []
+    rest = steps - chunk * len(plan)
+    if rest:
+        plan.append((capture(rest), rest))
+    torch.cuda.synchronize()
+    return plan
+
+
+def replay_matches_eager(torch, step, nvar: int, plan, outputs) -> bool:
+    """The first graph of the plan against the same steps run eagerly: the outputs
+    after it (its last step) must agree bit for bit."""
+    g, n = plan[0]
+    for i in range(n):
+        step(i)
+    torch.cuda.synchronize()
+    want = [t.clone() for t in outputs]
+    for t in outputs:
+        t.fill_(7)
+    g.replay()
+    torch.cuda.synchronize()
+    return all(torch.equal(a.view(torch.uint8) if a.dtype == torch.float8_e4m3fn else a,
+                           b.view(torch.uint8) if b.dtype == torch.float8_e4m3fn else b)
+               for a, b in zip(outputs, want))
+
+
+def replay(plan):
+    for g, _ in plan:
+        g.replay()
+
+
 def prefill_indexer_rate(dev, sk, torch, wl, iters: int = 5, fp4: bool = False):
     """Indexer scoring of the 32K-token causal prefill (every row scores its visible
     entries): algorithmic bf16 flops per second on MFMA.  Keys, queries and
@@ -733,6 +788,15 @@ def decode_1m_rate(dev, sk, torch, gen, steps: int = 20, replicas: int = 4, fp4:
         step(i)
     e1.record(stream)
     torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / steps
+    plan = step_graphs(torch, step, len(reps), steps)
+    graph_ok = replay_matches_eager(torch, step, len(reps), plan, [idx, out_c, out_h])
+    replay(plan)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    replay(plan)
+    e1.record(stream)
+    torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     ev_c, ev_h = (t - csa.W) // csa.m, (t - hca.W) // hca.m
     nwin = csa.W
@@ -744,7 +808,9 @@ def decode_1m_rate(dev, sk, torch, gen, steps: int = 20, replicas: int = 4, fp4:
     return {"workload": wl.name + ("_mxfp4_keys" if fp4 else ""), "batch": 1, "context": wl.N,
             "key_bytes": key_bytes, "replicas": replicas, "ms_per_step": ms,
             "queries_per_s": 1.0 / (ms * 1e-3), "algorithmic_bytes": by, "hbm_GBps": gbps,
-            "hbm_frac": gbps / PEAK_HBM_GBPS, "kernel_traffic": kernel_counters(STEP_1M_COUNTERS)}
+            "hbm_frac": gbps / PEAK_HBM_GBPS, "step_launch": "hip_graph_replay",
+            "graph_replay_equals_eager": graph_ok, "eager_ms_per_step": eager_ms,
+            "kernel_traffic": kernel_counters(STEP_1M_COUNTERS)}
 
 
 def compress_rates(dev, sk, torch, gen, iters: int = 5):
@@ -849,7 +915,7 @@ def decode_fp4_rate(dev, sk, torch, wl, c, h, qc, qh, steps: int = 50, replicas:
         step(i)
     e1.record(stream)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    eager_ms = e0.elapsed_time(e1) / steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     for i in range(steps):
         step(i, evs[i])
@@ -862,6 +928,15 @@ def decode_fp4_rate(dev, sk, torch, wl, c, h, qc, qh, steps: int = 50, replicas:
     s1.record(stream)
     torch.cuda.synchronize()
     score_ms = s0.elapsed_time(s1) / steps
+    plan = step_graphs(torch, step, len(keys), steps)
+    graph_ok = replay_matches_eager(torch, step, len(keys), plan, [idx, out_c, out_h])
+    replay(plan)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    replay(plan)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
     ab = algorithmic_bytes(wl)
     key_bytes = csa.D_I // 2 + csa.D_I // 32                   # e2m1 codes + one scale byte per 32 channels
     score_by = (cover * key_bytes + csa.H_I * csa.D_I * 2 + csa.H_I * 4) * B
@@ -870,6 +945,7 @@ def decode_fp4_rate(dev, sk, torch, wl, c, h, qc, qh, steps: int = 50, replicas:
     step_gbps = step_by / (ms * 1e-3) / 1e9
     return {"workload": wl.name + "_mxfp4_keys", "batch": B, "context": wl.N, "key_bytes": key_bytes,
             "replicas": replicas, "ms_per_step": ms, "queries_per_s": B / (ms * 1e-3),
+            "step_launch": "hip_graph_replay", "graph_replay_equals_eager": graph_ok, "eager_ms_per_step": eager_ms,
             "index_topk_ms": topk_ms, "step_algorithmic_bytes": step_by, "step_hbm_GBps": step_gbps,
             "step_hbm_frac": step_gbps / PEAK_HBM_GBPS,
             "index_score": {"kernel": "index_score_decode (MXFP4 keys)", "launch_ms": score_ms,
@@ -1106,17 +1182,14 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    # timed region: K whole steps
+    # eager steps (each call marshals its arguments in Python)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    w0 = time.time()
     e0.record(stream)
     for i in range(args.steps):
         step(i)
     e1.record(stream)
     torch.cuda.synchronize()
-    wall = time.time() - w0
-    ms = e0.elapsed_time(e1) / args.steps
+    eager_ms = e0.elapsed_time(e1) / args.steps
     # per-kernel durations: the same steps with events between the launches
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for i in range(args.steps):
@@ -1135,6 +1208,19 @@ def main():
     s1.record(stream)
     torch.cuda.synchronize()
     score_ms = s0.elapsed_time(s1) / args.steps
+    # timed region: K whole steps, each a replay of the step's HIP graph (the way a
+    # serving loop launches it: no host work between the kernels)
+    plan = step_graphs(torch, step, len(reps), args.steps)
+    graph_ok = replay_matches_eager(torch, step, len(reps), plan, [idx, out_c, out_h])
+    replay(plan)
+    torch.cuda.synchronize()
+    w0 = time.time()
+    e0.record(stream)
+    replay(plan)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.time() - w0
+    ms = e0.elapsed_time(e1) / args.steps
 
     ab = algorithmic_bytes(wl)
     ctr = kernel_counters(STEP_COUNTERS)
@@ -1151,6 +1237,7 @@ def main():
                    "latent": csa.D, "indexer": f"{csa.H_I}x{csa.D_I}", "top_k": csa.k, "window": csa.W,
                    "replicas": args.replicas},
         "step_hbm_GBps": step_gbps, "step_hbm_frac": step_gbps / PEAK_HBM_GBPS,
+        "step_launch": "hip_graph_replay", "graph_replay_equals_eager": graph_ok, "eager_ms_per_step": eager_ms,
         "step_algorithmic_bytes": ab["step"] * B,
         "kernel_ms": parts,
         "roofline": {"bound": "hbm", "kernel": "index_score_decode", "launch_ms": score_ms, "achieved": score_gbps,

@@ -193,9 +193,15 @@ def _shape(name: str, t: Optional[torch.Tensor], want):
     """t.shape must equal want (None entries match any size)."""
     if t is None:
         return
-    got = tuple(int(x) for x in t.shape)
-    if len(got) != len(want) or any(w is not None and g != w for g, w in zip(got, want)):
-        _fail(f"{name}: shape {got}, expected {tuple('*' if w is None else w for w in want)}")
+    got = t.shape
+    ok = len(got) == len(want)
+    if ok:
+        for g, w in zip(got, want):
+            if w is not None and g != w:
+                ok = False
+                break
+    if not ok:
+        _fail(f"{name}: shape {tuple(got)}, expected {tuple('*' if w is None else w for w in want)}")
 
 
 def _int32(name: str, t: Optional[torch.Tensor]):
@@ -210,9 +216,15 @@ def _rows_check(rows: "RowSpec", device):
         _shape("pos", rows.pos, (rows.R,))
 
 
+_HAVE_GPU: Optional[bool] = None
+
+
 def _stream(stream) -> Optional[int]:
+    global _HAVE_GPU
     if stream is None:
-        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+        if _HAVE_GPU is None:
+            _HAVE_GPU = torch.cuda.is_available()
+        return torch.cuda.current_stream().cuda_stream if _HAVE_GPU else None
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
 
 

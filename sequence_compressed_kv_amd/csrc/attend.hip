@@ -222,16 +222,13 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma(AttendParams p) {
 
   const gbytes gent = opaque_global(p.entries), gwin = opaque_global(p.win), gesc = opaque_global(p.escale);
   // query fragments (B operand of S^T = items x heads): dims g*D/4 + 8 ks .. +7
+  // loads issued here, waited for once the first chunk's loads are also in flight
   bf16x8 bq[KSQ];
   {
     const gbytes gq = opaque_global(p.q);
     const int64_t e0 = ((int64_t)r * p.H + head) * D + g * (D / 4);
 #pragma unroll
     for (int ks = 0; ks < KSQ; ++ks) bq[ks] = bitcast<bf16x8>(gload<u32x4>(gq, (e0 + 8 * ks) * 2));
-    // the fragments stay in registers for the whole block; redefine them here so no
-    // later instruction is made to wait on these loads
-#pragma unroll
-    for (int ks = 0; ks < KSQ; ++ks) pin(bq[ks]);
   }
   f32x4 o[ND];
 #pragma unroll
@@ -250,6 +247,12 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma(AttendParams p) {
     block_sources(p, ri, r, s0, s0 + (s1 - s0 + CH - 1) / CH * CH, NW * kWave, srcs);
     __syncthreads();
     stage_load<ENT, D, NW, CH>(p, gent, gwin, gesc, ri, srcs, 0, has_ent(s0), has_win(s0), st);
+    if (s0 == q_begin) {
+      // the query fragments stay in registers for the whole block; redefine them
+      // here (their loads were issued first) so no later instruction waits on them
+#pragma unroll
+      for (int ks = 0; ks < KSQ; ++ks) pin(bq[ks]);
+    }
     for (int64_t q0 = s0; q0 < s1; q0 += CH) {
       __syncthreads();
       stage_store<ENT, D, NW, CH>(st, L);
