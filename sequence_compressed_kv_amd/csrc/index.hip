@@ -208,11 +208,15 @@ template <int KEY, int HI, int DI, int NT>
 __global__ __launch_bounds__(256) void index_score_decode(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const void* __restrict__ keys,
     float* __restrict__ scores, int64_t stride, int64_t E_cap, int m, int W, const int32_t* __restrict__ pos,
-    int32_t pos_max) {
+    int32_t pos_max, uint32_t* __restrict__ zero_hist, int zero_words) {
   constexpr int MT = HI / 32, KS = DI / 16, QS = DI + 8;
   constexpr int64_t KPW = 32 * NT;
   __shared__ uint16_t qs[HI * QS];
   const int r = blockIdx.y;
+  if (zero_hist != nullptr && blockIdx.x == 0) {                 // the row's top-k histogram, cleared
+    uint32_t* h = zero_hist + (int64_t)r * zero_words;
+    for (int i = 4 * threadIdx.x; i < zero_words; i += 4 * 256) *reinterpret_cast<u32x4*>(h + i) = u32x4{0u, 0u, 0u, 0u};
+  }
   const RowRef rr = row_ref(SCKV_ROWS_DECODE, pos, pos_max, 0, 0, r);
   const int64_t e_vis = visible(rr.t, m, W, E_cap);
   if ((int64_t)blockIdx.x * 4 * KPW >= e_vis) return;           // whole block past the row
@@ -424,7 +428,7 @@ int64_t index_rows_cover(const sckv_index_args& a) {
 
 template <int KEY, int HI, int DI>
 static void launch_mfma(const sckv_index_args& a, float* scores, int64_t stride, int64_t cover,
-                        hipStream_t stream) {
+                        hipStream_t stream, uint32_t* zero_hist, int zero_words, bool* zeroed) {
   const uint16_t* q = static_cast<const uint16_t*>(a.q);
   if (a.rows.kind == SCKV_ROWS_DECODE) {
     // tiles per wave: the largest of 16/8/4 that still gives about 2048 waves (8 per CU)
@@ -434,11 +438,12 @@ static void launch_mfma(const sckv_index_args& a, float* scores, int64_t stride,
     const dim3 grid((unsigned)((cover + kpb - 1) / kpb), (unsigned)a.rows.R);
 #define SCKV_DEC(NTT)                                                                                          \
   hipLaunchKernelGGL((index_score_decode<KEY, HI, DI, NTT>), grid, dim3(256), 0, stream, q, a.w, a.keys, scores, \
-                     stride, a.E_cap, a.m, a.W, a.rows.pos, a.rows.pos_max)
+                     stride, a.E_cap, a.m, a.W, a.rows.pos, a.rows.pos_max, zero_hist, zero_words)
     if (nt == 16) SCKV_DEC(16);
     else if (nt == 8) SCKV_DEC(8);
     else SCKV_DEC(4);
 #undef SCKV_DEC
+    if (zeroed) *zeroed = zero_hist != nullptr;
   } else {
     const dim3 grid((unsigned)((a.rows.R + 7) / 8));
     hipLaunchKernelGGL((index_score_causal_lds<KEY, HI, DI>), grid, dim3(512), 0, stream, q, a.w, a.keys, scores,
@@ -448,15 +453,17 @@ static void launch_mfma(const sckv_index_args& a, float* scores, int64_t stride,
 
 template <int KEY>
 static void launch_mfma_key(const sckv_index_args& a, float* scores, int64_t stride, int64_t cover,
-                            hipStream_t stream) {
-  if (a.H_I == 64 && a.D_I == 128) launch_mfma<KEY, 64, 128>(a, scores, stride, cover, stream);
-  else if (a.H_I == 64 && a.D_I == 64) launch_mfma<KEY, 64, 64>(a, scores, stride, cover, stream);
-  else if (a.H_I == 32 && a.D_I == 128) launch_mfma<KEY, 32, 128>(a, scores, stride, cover, stream);
-  else launch_mfma<KEY, 32, 64>(a, scores, stride, cover, stream);
+                            hipStream_t stream, uint32_t* zh, int zw, bool* zeroed) {
+  if (a.H_I == 64 && a.D_I == 128) launch_mfma<KEY, 64, 128>(a, scores, stride, cover, stream, zh, zw, zeroed);
+  else if (a.H_I == 64 && a.D_I == 64) launch_mfma<KEY, 64, 64>(a, scores, stride, cover, stream, zh, zw, zeroed);
+  else if (a.H_I == 32 && a.D_I == 128) launch_mfma<KEY, 32, 128>(a, scores, stride, cover, stream, zh, zw, zeroed);
+  else launch_mfma<KEY, 32, 64>(a, scores, stride, cover, stream, zh, zw, zeroed);
 }
 
 hipError_t launch_index_score(const sckv_index_args& a, float* scores, int64_t stride, int64_t cover,
-                              hipStream_t stream) {
+                              hipStream_t stream, uint32_t* zh, int zw, bool* zeroed) {
+  if (zeroed) *zeroed = false;
+  if (zw <= 0 || zw % 4) zh = nullptr;
   if (cover <= 0) return hipSuccess;
   if (a.key_dtype == SCKV_F32) {
     const dim3 grid((unsigned)((cover + 255) / 256), (unsigned)a.rows.R);
@@ -465,11 +472,11 @@ hipError_t launch_index_score(const sckv_index_args& a, float* scores, int64_t s
                        static_cast<const float*>(a.keys), scores, stride, a.E_cap, a.m, a.W, a.H_I, a.D_I,
                        a.rows.kind, a.rows.pos, a.rows.pos_max, a.rows.seq0, a.rows.pos0);
   } else if (a.key_dtype == SCKV_BF16) {
-    launch_mfma_key<SCKV_BF16>(a, scores, stride, cover, stream);
+    launch_mfma_key<SCKV_BF16>(a, scores, stride, cover, stream, zh, zw, zeroed);
   } else if (a.key_dtype == SCKV_MXFP4) {
-    launch_mfma_key<SCKV_MXFP4>(a, scores, stride, cover, stream);
+    launch_mfma_key<SCKV_MXFP4>(a, scores, stride, cover, stream, zh, zw, zeroed);
   } else {
-    launch_mfma_key<SCKV_E4M3>(a, scores, stride, cover, stream);
+    launch_mfma_key<SCKV_E4M3>(a, scores, stride, cover, stream, zh, zw, zeroed);
   }
   return hipGetLastError();
 }

@@ -400,6 +400,18 @@ size_t csa_topk_select_workspace_size(const sckv_index_args* a) {
   return pl.topk.ws_bytes;
 }
 
+// Scores into the workspace, then the top-k; the scoring kernel clears the
+// many-block top-k's histograms on its way (one launch fewer).
+static hipError_t index_then_topk(const sckv_index_args& a, const IndexPlan& pl, void* ws, hipStream_t st) {
+  float* scores = static_cast<float*>(ws);
+  void* tws = static_cast<char*>(ws) + pl.ws_scores;
+  bool zeroed = false;
+  hipError_t e = sckv::launch_index_score(a, scores, pl.stride, pl.cover, st, static_cast<uint32_t*>(tws),
+                                          sckv::topk_hist_words(pl.topk), &zeroed);
+  if (e == hipSuccess) e = sckv::launch_topk(a, scores, pl.stride, pl.topk, tws, st, zeroed);
+  return e;
+}
+
 sckv_status csa_index_topk(const sckv_index_args* a, void* ws, size_t ws_bytes, void* stream) {
   IndexPlan pl;
   sckv_status s = check_index(a, &pl, true);
@@ -409,11 +421,7 @@ sckv_status csa_index_topk(const sckv_index_args* a, void* ws, size_t ws_bytes, 
                 ws ? ws_bytes : (size_t)0);
   if (!aligned16(ws)) return fail(SCKV_ERR_ALIGN, "csa_index_topk: workspace must be 16-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  float* scores = static_cast<float*>(ws);
-  hipError_t e = sckv::launch_index_score(*a, scores, pl.stride, pl.cover, st);
-  if (e == hipSuccess)
-    e = sckv::launch_topk(*a, scores, pl.stride, pl.topk, static_cast<char*>(ws) + pl.ws_scores, st);
-  return hip_status(e, "csa_index_topk");
+  return hip_status(index_then_topk(*a, pl, ws, st), "csa_index_topk");
 }
 
 sckv_status csa_index_topk_noalloc(const sckv_index_args* a, void* stream) {
@@ -439,11 +447,7 @@ sckv_status csa_index_topk_noalloc(const sckv_index_args* a, void* stream) {
   void* ws = nullptr;
   e = scratch_address(dev, &ws);
   if (e != hipSuccess) return hip_status(e, "csa_index_topk_noalloc (scratch address)");
-  float* scores = static_cast<float*>(ws);
-  e = sckv::launch_index_score(*a, scores, pl.stride, pl.cover, st);
-  if (e == hipSuccess)
-    e = sckv::launch_topk(*a, scores, pl.stride, pl.topk, static_cast<char*>(ws) + pl.ws_scores, st);
-  return hip_status(e, "csa_index_topk_noalloc");
+  return hip_status(index_then_topk(*a, pl, ws, st), "csa_index_topk_noalloc");
 }
 
 sckv_status csa_index_score(const sckv_index_args* a, float* scores, int64_t score_stride, void* stream) {

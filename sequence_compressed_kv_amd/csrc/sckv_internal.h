@@ -24,8 +24,12 @@ hipError_t launch_append(const sckv_append_stream& s, const sckv_append_stream* 
 // ---------------------------------------------------------------- indexer
 // Largest visible-entry count over the rows (the score matrix width needed).
 int64_t index_rows_cover(const sckv_index_args& a);
+// zero_hist (optional): per-row histograms [R][zero_words] that the decode scoring
+// kernel clears before it scores (the first block of each row); *zeroed tells
+// whether it did (other paths leave them to the top-k launch).
 hipError_t launch_index_score(const sckv_index_args& a, float* scores, int64_t stride,
-                              int64_t cover, hipStream_t stream);
+                              int64_t cover, hipStream_t stream, uint32_t* zero_hist = nullptr,
+                              int zero_words = 0, bool* zeroed = nullptr);
 
 // Top-k plan: one block per row when the visible count fits a block's registers;
 // for a few longer rows, many blocks per row (histogram, filter, final selection
@@ -43,8 +47,12 @@ struct TopkPlan {
   bool ok = false;
 };
 TopkPlan plan_topk(int64_t cover, int32_t k, int32_t R);
+// The many-block path's per-row histograms at the start of its workspace:
+// words per row (0 when the plan does not take that path).
+int topk_hist_words(const TopkPlan& p);
+// hist_zeroed: the histograms were already cleared on the stream (by the scoring kernel)
 hipError_t launch_topk(const sckv_index_args& a, const float* scores, int64_t stride,
-                       const TopkPlan& p, void* ws, hipStream_t stream);
+                       const TopkPlan& p, void* ws, hipStream_t stream, bool hist_zeroed = false);
 
 // ---------------------------------------------------------------- attention
 struct AttendPlan {

@@ -486,7 +486,7 @@ __device__ __forceinline__ void topk_row_final(const float* scores, int64_t stri
                                             int nb, const int32_t* cnt, const uint32_t* rkey, const int32_t* ridx,
                                             uint32_t b, uint32_t above, uint32_t n_valid, int32_t* out_idx,
                                             float* out_score, uint32_t* hist, uint32_t* scan_sh, uint32_t* ctl,
-                                            int32_t* pre, int32_t* flag) {
+                                            int32_t* pre, int32_t* flag, uint32_t* skey, int32_t* sidx) {
   constexpr int NI = kFinV / 4;
   const int w = wave_id(), l = lane_id();
   int32_t* oi = out_idx + (int64_t)r * k;
@@ -517,31 +517,33 @@ __device__ __forceinline__ void topk_row_final(const float* scores, int64_t stri
     return;
   }
   const int tot = pre[nb];
-  // survivor e (concatenation order) lives in region j, pre[j] <= e < pre[j+1]
+  // the survivors, region by region into LDS in concatenation (ascending index)
+  // order: wave w copies regions w, w + 16, ..., each with coalesced reads
+  for (int j = w; j < nb; j += kFinNT / kWave) {
+    const int c0 = pre[j], c = pre[j + 1] - c0;
+    const int64_t base = ((int64_t)r * nb + j) * kMbS;
+    for (int o = l; o < c; o += kWave) {
+      skey[c0 + o] = rkey[base + o];
+      sidx[c0 + o] = ridx[base + o];
+    }
+  }
+  __syncthreads();
   uint32_t key[kFinV];
   int32_t idx[kFinV];
   bool valid[kFinV];
 #pragma unroll
-  for (int i = 0; i < NI; ++i)
+  for (int i = 0; i < NI; ++i) {
+    const int e0 = w * 64 * kFinV + (i * 64 + l) * 4;
+    const u32x4 kv = e0 < tot ? *reinterpret_cast<const u32x4*>(&skey[e0]) : u32x4{0u, 0u, 0u, 0u};
+    const i32x4 iv = e0 < tot ? *reinterpret_cast<const i32x4*>(&sidx[e0]) : i32x4{-1, -1, -1, -1};
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const int v = 4 * i + jj;
-      const int e = w * 64 * kFinV + (i * 64 + l) * 4 + jj;
-      valid[v] = e < tot;
-      key[v] = 0u;
-      idx[v] = -1;
-      if (valid[v]) {
-        int lo = 0, hi = nb;                           // largest j with pre[j] <= e
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (pre[mid] <= e) lo = mid;
-          else hi = mid;
-        }
-        const int64_t at = ((int64_t)r * nb + lo) * kMbS + (e - pre[lo]);
-        key[v] = rkey[at];
-        idx[v] = ridx[at];
-      }
+      valid[v] = e0 + jj < tot;
+      key[v] = valid[v] ? kv[jj] : 0u;
+      idx[v] = valid[v] ? iv[jj] : -1;
     }
+  }
   select_ordered<kFinNT, kFinV>(key, idx, valid, (uint32_t)tot, kk, oi, os, k, hist, scan_sh, ctl, b + 1, above);
 }
 
@@ -610,11 +612,13 @@ __global__ __launch_bounds__(kFinNT) void topk_final(const float* __restrict__ s
   __shared__ uint32_t ctl[4];
   __shared__ int32_t pre[kMbMaxBlocks + 1];
   __shared__ int32_t flag;
+  __shared__ __attribute__((aligned(16))) uint32_t skey[kFinCap];
+  __shared__ __attribute__((aligned(16))) int32_t sidx[kFinCap];
   const int r = blockIdx.y;
   row_threshold_bin<kFinNT>(ghist + (int64_t)r * kBins, k, scan_sh, ctl);
   const uint32_t b = ctl[0], above = ctl[1], n_valid = ctl[3];
   topk_row_final(scores, stride, rows, r, k, nb, cnt, rkey, ridx, b, above, n_valid, out_idx, out_score, hist,
-                 scan_sh, ctl, pre, &flag);
+                 scan_sh, ctl, pre, &flag, skey, sidx);
 }
 
 static const int kCfg[][2] = {{256, 4}, {256, 16}, {256, 32}, {1024, 16}, {1024, 32}, {1024, 64}};
@@ -667,8 +671,10 @@ static void launch_cfg(int nt, int v, dim3 grid, const float* scores, int64_t st
 #undef SCKV_TK
 }
 
+int topk_hist_words(const TopkPlan& p) { return p.mb_blocks ? kBins : 0; }
+
 hipError_t launch_topk(const sckv_index_args& a, const float* scores, int64_t stride, const TopkPlan& p,
-                       void* ws, hipStream_t stream) {
+                       void* ws, hipStream_t stream, bool hist_zeroed) {
   TopkRows rr{a.rows.kind, a.rows.pos, a.rows.pos_max, a.rows.seq0, a.rows.pos0, a.m, a.W, a.E_cap};
   const int R = a.rows.R;
   if (p.mb_blocks) {
@@ -679,7 +685,8 @@ hipError_t launch_topk(const sckv_index_args& a, const float* scores, int64_t st
     uint32_t* rkey = reinterpret_cast<uint32_t*>(w + mb_cnt_offset(R) + align16((size_t)R * nb * 4));
     int32_t* ridx = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(rkey) + (size_t)R * nb * kMbS * 4);
     const int64_t nz = (int64_t)R * kBins;
-    hipLaunchKernelGGL(topk_zero_hist, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, stream, hist, nz);
+    if (!hist_zeroed)
+      hipLaunchKernelGGL(topk_zero_hist, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, stream, hist, nz);
     hipLaunchKernelGGL(topk_hist, dim3((unsigned)nb, R), dim3(kMbNT), 0, stream, scores, stride, rr, hist);
     hipLaunchKernelGGL(topk_filter, dim3((unsigned)nb, R), dim3(kMbNT), 0, stream, scores, stride, rr, a.k, nb, hist,
                        cnt, rkey, ridx);
