@@ -11,6 +11,7 @@
 // lowest-indexed ties.  Rows too long for one block are cut into slices whose
 // local top-k are merged by a second pass over the slices' candidates.
 #include <climits>
+#include <type_traits>
 
 #include "device_common.h"
 #include "sckv_internal.h"
@@ -487,7 +488,6 @@ __device__ __forceinline__ void topk_row_final(const float* scores, int64_t stri
                                             uint32_t b, uint32_t above, uint32_t n_valid, int32_t* out_idx,
                                             float* out_score, uint32_t* hist, uint32_t* scan_sh, uint32_t* ctl,
                                             int32_t* pre, int32_t* flag, uint32_t* skey, int32_t* sidx) {
-  constexpr int NI = kFinV / 4;
   const int w = wave_id(), l = lane_id();
   int32_t* oi = out_idx + (int64_t)r * k;
   float* os = out_score ? out_score + (int64_t)r * k : nullptr;
@@ -528,23 +528,31 @@ __device__ __forceinline__ void topk_row_final(const float* scores, int64_t stri
     }
   }
   __syncthreads();
-  uint32_t key[kFinV];
-  int32_t idx[kFinV];
-  bool valid[kFinV];
+  // V survivors per thread in element order (wave, group, lane, element); up to
+  // kFinNT * 4 of them (the common case) take the narrow form, whose passes touch
+  // a quarter of the slots
+  auto select = [&](auto vtag) __attribute__((always_inline)) {
+    constexpr int V = decltype(vtag)::value, NV = V / 4;
+    uint32_t key[V];
+    int32_t idx[V];
+    bool valid[V];
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int e0 = w * 64 * kFinV + (i * 64 + l) * 4;
-    const u32x4 kv = e0 < tot ? *reinterpret_cast<const u32x4*>(&skey[e0]) : u32x4{0u, 0u, 0u, 0u};
-    const i32x4 iv = e0 < tot ? *reinterpret_cast<const i32x4*>(&sidx[e0]) : i32x4{-1, -1, -1, -1};
+    for (int i = 0; i < NV; ++i) {
+      const int e0 = w * 64 * V + (i * 64 + l) * 4;
+      const u32x4 kv = e0 < tot ? *reinterpret_cast<const u32x4*>(&skey[e0]) : u32x4{0u, 0u, 0u, 0u};
+      const i32x4 iv = e0 < tot ? *reinterpret_cast<const i32x4*>(&sidx[e0]) : i32x4{-1, -1, -1, -1};
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int v = 4 * i + jj;
-      valid[v] = e0 + jj < tot;
-      key[v] = valid[v] ? kv[jj] : 0u;
-      idx[v] = valid[v] ? iv[jj] : -1;
+      for (int jj = 0; jj < 4; ++jj) {
+        const int v = 4 * i + jj;
+        valid[v] = e0 + jj < tot;
+        key[v] = valid[v] ? kv[jj] : 0u;
+        idx[v] = valid[v] ? iv[jj] : -1;
+      }
     }
-  }
-  select_ordered<kFinNT, kFinV>(key, idx, valid, (uint32_t)tot, kk, oi, os, k, hist, scan_sh, ctl, b + 1, above);
+    select_ordered<kFinNT, V>(key, idx, valid, (uint32_t)tot, kk, oi, os, k, hist, scan_sh, ctl, b + 1, above);
+  };
+  if (tot <= kFinNT * 4) select(std::integral_constant<int, 4>{});
+  else select(std::integral_constant<int, kFinV>{});
 }
 
 __global__ __launch_bounds__(kMbNT) void topk_filter(const float* __restrict__ scores, int64_t stride,
