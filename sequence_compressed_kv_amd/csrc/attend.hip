@@ -20,7 +20,7 @@
 
 namespace sckv {
 
-constexpr int kPlanChunk = 64;    // split boundaries fall on multiples of this many items
+constexpr int kPlanChunk = 64;    // split boundaries fall on multiples of this many items (32 in one case)
 constexpr int kMaxSplits = 256;   // splits per row: about one block per CU when a single row is decoded
 constexpr int kSegItems = 1024;   // item sources resolved per segment of a block's range
 
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma(AttendParams p) {
   const int col = l & 15, g = l >> 4;
   const int head = 16 * w + col;
 
-  const int64_t q_begin = (int64_t)split * p.per_split;     // per_split: items, a multiple of 64
+  const int64_t q_begin = (int64_t)split * p.per_split;     // per_split: items, a multiple of CH
   int64_t q_end = q_begin + p.per_split;
   q_end = q_end < ri.n_items ? q_end : ri.n_items;
 
@@ -836,7 +836,11 @@ AttendPlan plan_attend(const sckv_attend_args& a, bool csa) {
   int64_t ev = entries_visible(t, a.m, a.W);
   ev = ev < a.E_cap ? ev : a.E_cap;
   pl.items = (csa ? a.k : ev) + a.W;
-  pl.chunks = (pl.items + kPlanChunk - 1) / kPlanChunk;
+  // split granularity: 64 items, or for a few rows on the register-staged kernel
+  // at D = 512 (which stages 32 items at a time) single 32-item chunks
+  const bool dma = a.entry_dtype == SCKV_BF16 && a.D == 512 && a.H == 64;
+  const int64_t unit = (!dma && a.D == 512 && a.rows.R <= 16) ? 32 : kPlanChunk;
+  pl.chunks = (pl.items + unit - 1) / unit;
   pl.mfma = a.entry_dtype != SCKV_F32;
   if (!pl.mfma) {
     pl.nsplit = 1;
@@ -857,7 +861,7 @@ AttendPlan plan_attend(const sckv_attend_args& a, bool csa) {
   const int64_t min_per = a.rows.R <= 16 ? 1 : (pl.chunks < 2 ? pl.chunks : 2);
   per = per < min_per ? min_per : per;
   per = per < 1 ? 1 : per;
-  pl.per_split = per * kPlanChunk;       // in items
+  pl.per_split = per * unit;             // in items
   pl.nsplit = (int32_t)((pl.chunks + per - 1) / per);
   if (pl.nsplit < 1) pl.nsplit = 1;
   if (pl.nsplit > kMaxSplits) return pl;     // cannot happen: nsplit <= ns <= target_blocks

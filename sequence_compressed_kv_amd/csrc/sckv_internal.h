@@ -57,8 +57,8 @@ hipError_t launch_topk(const sckv_index_args& a, const float* scores, int64_t st
 // ---------------------------------------------------------------- attention
 struct AttendPlan {
   int64_t items = 0;        // widest row: listed/visible entries + window
-  int64_t chunks = 0;       // items / 64 rounded up
-  int64_t per_split = 0;    // items per split (a multiple of 64)
+  int64_t chunks = 0;       // items / split unit (64, or 32 for few rows at D = 512 off LDS-DMA) rounded up
+  int64_t per_split = 0;    // items per split (a multiple of the unit)
   int32_t nsplit = 1;
   int32_t hgroups = 1;      // blocks per (row, split), each taking H / hgroups heads
   bool mfma = false;
