@@ -32,6 +32,7 @@ STEP_COUNTERS = "pair_decode_128k_bf16.step_kernels.counters.txt"
 STEP_1M_COUNTERS = "pair_decode_1m_fp8.step_kernels.counters.txt"
 COMPRESS_COUNTERS = "compressors_128k_bf16_1m_fp8.counters.txt"
 PREFILL_COUNTERS = "csa_prefill_32k_bf16.kernels.counters.txt"
+FP4_COUNTERS = "pair_decode_128k_mxfp4_keys.step_kernels.counters.txt"
 
 
 def parse():
@@ -950,7 +951,8 @@ def decode_fp4_rate(dev, sk, torch, wl, c, h, qc, qh, steps: int = 50, replicas:
             "step_hbm_frac": step_gbps / PEAK_HBM_GBPS,
             "index_score": {"kernel": "index_score_decode (MXFP4 keys)", "launch_ms": score_ms,
                             "bytes_per_launch": score_by, "achieved_GBps": score_gbps,
-                            "frac": score_gbps / PEAK_HBM_GBPS}}
+                            "frac": score_gbps / PEAK_HBM_GBPS},
+            "kernel_traffic": kernel_counters(FP4_COUNTERS)}
 
 
 def algorithmic_bytes(wl):

@@ -38,7 +38,8 @@ def test_more_than_one_gpu_is_refused():
 def test_committed_counter_summaries_parse():
     """Every committed per-kernel counter summary names its kernels with calibrated
     bytes, algorithmic bytes and a source digest."""
-    for name in (bench.STEP_COUNTERS, bench.STEP_1M_COUNTERS, bench.COMPRESS_COUNTERS, bench.PREFILL_COUNTERS):
+    for name in (bench.STEP_COUNTERS, bench.STEP_1M_COUNTERS, bench.COMPRESS_COUNTERS, bench.PREFILL_COUNTERS,
+                 bench.FP4_COUNTERS):
         c = bench.kernel_counters(name)
         assert c, name
         for label, v in c.items():
