@@ -814,7 +814,7 @@ def decode_1m_rate(dev, sk, torch, gen, steps: int = 20, replicas: int = 4, fp4:
             "kernel_traffic": kernel_counters(STEP_1M_COUNTERS)}
 
 
-def compress_rates(dev, sk, torch, gen, iters: int = 5):
+def compress_rates(dev, sk, torch, gen, iters: int = 20):
     """The bulk compressors on one sequence's streams, as the caches are built: the
     128K pair's (CSA latent and indexer streams into bf16 entries and key tiles in
     one call, the HCA stream into bf16 entries) and the 1M pair's pre-population

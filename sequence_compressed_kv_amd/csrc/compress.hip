@@ -488,11 +488,15 @@ __device__ __forceinline__ void ov_block_sums(const RawBlock<IN>& rb, const floa
   }
 }
 
-// Overlapping 4:1 windows (m = o = 4) by the factored softmax: a slot of G = D/8
-// lanes pools a run of J consecutive entries, loading each token block once (the
-// next block's loads in flight while the current one is pooled) and carrying the
-// block's first-half sums into the next entry.  Channels whose bias rows spread
-// too far take the online path entry by entry.
+// Overlapping 4:1 windows (m = o = 4) by the factored softmax.  The S = 4 * 64/G
+// lane groups ("slots", G = D/8 lanes each) of a block take S consecutive entries
+// per step, J steps in turn, so a block pools a run of S * J consecutive entries.
+// Each slot loads and pools one 4-token block per step (the next step's block in
+// flight meanwhile) into its two half-window sums; an entry needs the first-half
+// sums of the block before its own, which the neighbouring slot computed in the
+// same step (slot 0: slot S-1 in the step before), passed through LDS.  Only the
+// block before the run is pooled twice.  Channels whose bias rows spread too far
+// take the online path entry by entry.
 template <int IN, int OUT, bool SCALED>
 __global__ __launch_bounds__(256) void compress_overlap_kernel(
     const void* __restrict__ val, const void* __restrict__ gate, const float* __restrict__ bpos,
@@ -500,12 +504,15 @@ __global__ __launch_bounds__(256) void compress_overlap_kernel(
     int64_t E_cap, int G, int key_tiles, int J) {
   const int lane = lane_id();
   const int epw = kWave / G;
-  const int slot = lane / G, sub = lane % G;
-  const int64_t first = ((int64_t)blockIdx.x * (4 * epw) + wave_id() * epw + slot) * J;   // first local entry
+  const int S = 4 * epw;
+  const int gs = wave_id() * epw + lane / G, sub = lane % G;    // slot in the block; threadIdx.x = gs * G + sub
+  const int64_t R0 = (int64_t)blockIdx.x * S * J;               // the block's first local entry
   const int64_t b = blockIdx.y;
   const int ch = sub * 8;
   // the bias factors of all D channels, [row][channel], shared by the block's slots
   __shared__ __attribute__((aligned(16))) float u_sh[2 * kOvM * kOvMaxD];
+  // first-half state (block max, sums) of each slot's block, two steps' worth
+  __shared__ float carry[2][3 * 8][256];
   bool ok = true;
   for (int c = threadIdx.x; c < D; c += blockDim.x) {
     float uc[2 * kOvM];
@@ -514,15 +521,17 @@ __global__ __launch_bounds__(256) void compress_overlap_kernel(
     for (int p = 0; p < 2 * kOvM; ++p) u_sh[p * D + c] = uc[p];
   }
   const bool fast = __syncthreads_and(ok ? 1 : 0) != 0;
-  if (first >= e_count) return;
+  if (R0 >= e_count) return;                                     // whole block
   if (!fast) {
     auto tok = [&](int64_t i, float (&g)[8], float (&v)[8]) __attribute__((always_inline)) {
       const int64_t row = (b * N + i) * D + ch;
       load8<IN>(gate, row, g);
       load8<IN>(val, row, v);
     };
-    for (int j = 0; j < J && first + j < e_count; ++j) {
-      const int64_t e = e_begin + first + j;
+    for (int j = 0; j < J; ++j) {
+      const int64_t el = R0 + (int64_t)j * S + gs;
+      if (el >= e_count) break;
+      const int64_t e = e_begin + el;
       const int64_t i0 = (int64_t)kOvM * e - kOvM, i1 = (int64_t)kOvM * e + kOvM;
       PoolState r;
       int64_t ia, ib;
@@ -532,31 +541,51 @@ __global__ __launch_bounds__(256) void compress_overlap_kernel(
     }
     return;
   }
-  const int64_t e0 = e_begin + first;
   const int64_t row_b = b * N * D + ch;            // token i's channels at row_b + i * D
-  float sp[8], lp[8], ap[8];                       // first-half state carried into the next entry
-  RawBlock<IN> rb;
-  if (e0 > 0) {
-    raw_block_load<IN>(gate, val, row_b + (e0 - 1) * kOvM * D, D, rb);
-    float la[8], aa[8];
-    ov_block_sums<IN>(rb, u_sh, D, ch, sp, la, aa, lp, ap);
-  } else {
+  const int64_t last = e_count - 1;                // loads of entries past the range re-read the last one
+  float sp[8], lp[8], ap[8];                       // slot 0: the state of the block before its entry
+  if (gs == 0) {
+    const int64_t e_prev = e_begin + R0 - 1;
+    if (e_prev >= 0) {
+      RawBlock<IN> pb;
+      raw_block_load<IN>(gate, val, row_b + e_prev * kOvM * D, D, pb);
+      float la[8], aa[8];
+      ov_block_sums<IN>(pb, u_sh, D, ch, sp, la, aa, lp, ap);
+    } else {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) { sp[c] = -INFINITY; lp[c] = 0.f; ap[c] = 0.f; }
+      for (int c = 0; c < 8; ++c) { sp[c] = -INFINITY; lp[c] = 0.f; ap[c] = 0.f; }
+    }
   }
-  raw_block_load<IN>(gate, val, row_b + e0 * kOvM * D, D, rb);
+  auto entry_of = [&](int j) { const int64_t el = R0 + (int64_t)j * S + gs; return el < last ? el : last; };
+  RawBlock<IN> rb;
+  raw_block_load<IN>(gate, val, row_b + (e_begin + entry_of(0)) * kOvM * D, D, rb);
   for (int j = 0; j < J; ++j) {
-    const int64_t el = first + j;
-    if (el >= e_count) break;
-    const int64_t e = e_begin + el;
+    if (R0 + (int64_t)j * S >= e_count) break;                  // uniform over the block
+    const int64_t el = R0 + (int64_t)j * S + gs;
+    const int64_t e = e_begin + (el < last ? el : last);
     RawBlock<IN> cur = rb;
-    if (j + 1 < J && el + 1 < e_count) raw_block_load<IN>(gate, val, row_b + (e + 1) * kOvM * D, D, rb);
+    if (j + 1 < J) raw_block_load<IN>(gate, val, row_b + (e_begin + entry_of(j + 1)) * kOvM * D, D, rb);
     float s[8], la[8], aa[8], lb[8], ab[8], cv[8];
     ov_block_sums<IN>(cur, u_sh, D, ch, s, la, aa, lb, ab);
-    ov_entry(sp, lp, ap, s, la, aa, cv);
-    store_values<OUT, SCALED>(cv, ch, G, true, sub, b, e, D, E_cap, key_tiles, out, out_scale);
+    float (&cw)[3 * 8][256] = carry[j & 1];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) { sp[c] = s[c]; lp[c] = lb[c]; ap[c] = ab[c]; }
+    for (int c = 0; c < 8; ++c) { cw[c][threadIdx.x] = s[c]; cw[8 + c][threadIdx.x] = lb[c]; cw[16 + c][threadIdx.x] = ab[c]; }
+    __syncthreads();
+    if (gs != 0) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        sp[c] = cw[c][threadIdx.x - G];
+        lp[c] = cw[8 + c][threadIdx.x - G];
+        ap[c] = cw[16 + c][threadIdx.x - G];
+      }
+    }
+    ov_entry(sp, lp, ap, s, la, aa, cv);
+    if (el < e_count) store_values<OUT, SCALED>(cv, ch, G, true, sub, b, e, D, E_cap, key_tiles, out, out_scale);
+    if (gs == 0) {                                               // slot S-1's block precedes slot 0's next entry
+      const int src = threadIdx.x + (S - 1) * G;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) { sp[c] = cw[c][src]; lp[c] = cw[8 + c][src]; ap[c] = cw[16 + c][src]; }
+    }
   }
 }
 
@@ -705,11 +734,11 @@ static hipError_t launch_in(const sckv_pool_stream& s, int32_t B, int64_t N, int
   const dim3 block(256);
   const int tiles = s.out_layout == SCKV_LAYOUT_KEY_TILES ? 1 : 0;
   const dim3 grid_parts((unsigned)((e_count + epw - 1) / epw), (unsigned)B);
-  // overlapping 4:1 windows: runs of J entries per slot (each run loads one block
-  // twice), J as large as keeps 2048 blocks in the grid
+  // overlapping 4:1 windows: a block pools 4 * epw * J consecutive entries (and the
+  // block before them), J as large as keeps 2048 blocks in the grid
   int J = 16;
   auto ov_blocks = [&](int j) { return ((e_count + (int64_t)j * 4 * epw - 1) / ((int64_t)j * 4 * epw)) * B; };
-  while (J > 2 && ov_blocks(J) < 2048) J /= 2;
+  while (J > 1 && ov_blocks(J) < 2048) J /= 2;
   const dim3 grid_ov((unsigned)((e_count + (int64_t)J * 4 * epw - 1) / ((int64_t)J * 4 * epw)), (unsigned)B);
 #define SCKV_LAUNCH(OUT, SC)                                                                                   \
   if (m == kOvM && o == kOvM)                                                                                  \
