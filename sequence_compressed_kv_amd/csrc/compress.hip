@@ -432,6 +432,14 @@ __global__ __launch_bounds__(256) void compress_kernel(
   store_entry<OUT, SCALED>(r, ch, G, active, sub, b, e, D, E_cap, key_tiles, out, out_scale);
 }
 
+// Bias-factor table in LDS: row p, channel c at [p][c mod 8 >= 4][c / 8][c mod 4],
+// so the 16-byte reads of a wave's lanes (channels 8 l .. 8 l + 3, then + 4 .. + 7)
+// are contiguous and free of bank conflicts.
+__device__ __forceinline__ int ov_u_index(int p, int c, int ch, int D) {
+  const int cc = ch + c;
+  return (2 * p + ((cc >> 2) & 1)) * (D >> 1) + (cc >> 3) * 4 + (cc & 3);
+}
+
 // Both half-window sums of one block straight from its loaded rows: the block
 // maximum first, then token by token the factor exp(g - s) and its two weighted
 // terms, with the bias factors of rows 4..7 (second half: la, aa) and rows 0..3
@@ -463,9 +471,10 @@ __device__ __forceinline__ void ov_block_sums(const RawBlock<IN>& rb, const floa
     raw_unpack<IN>(rb.g[t], g);
     raw_unpack<IN>(rb.v[t], v);
     {
-      const f32x4* qa = reinterpret_cast<const f32x4*>(&u_sh[(kOvM + t) * D + ch]);
-      const f32x4* qb = reinterpret_cast<const f32x4*>(&u_sh[t * D + ch]);
-      const f32x4 a0 = qa[0], a1 = qa[1], b0 = qb[0], b1 = qb[1];
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(&u_sh[ov_u_index(kOvM + t, 0, ch, D)]);
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(&u_sh[ov_u_index(kOvM + t, 4, ch, D)]);
+      const f32x4 b0 = *reinterpret_cast<const f32x4*>(&u_sh[ov_u_index(t, 0, ch, D)]);
+      const f32x4 b1 = *reinterpret_cast<const f32x4*>(&u_sh[ov_u_index(t, 4, ch, D)]);
 #pragma unroll
       for (int c = 0; c < 4; ++c) { ua[c] = a0[c]; ua[4 + c] = a1[c]; ub[c] = b0[c]; ub[4 + c] = b1[c]; }
     }
@@ -518,7 +527,7 @@ __global__ __launch_bounds__(256) void compress_overlap_kernel(
     float uc[2 * kOvM];
     ok = ov_bias_channel(bpos, D, c, uc) && ok;
 #pragma unroll
-    for (int p = 0; p < 2 * kOvM; ++p) u_sh[p * D + c] = uc[p];
+    for (int p = 0; p < 2 * kOvM; ++p) u_sh[ov_u_index(p, 0, c, D)] = uc[p];
   }
   const bool fast = __syncthreads_and(ok ? 1 : 0) != 0;
   if (R0 >= e_count) return;                                     // whole block
