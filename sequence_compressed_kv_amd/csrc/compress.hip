@@ -744,10 +744,10 @@ static hipError_t launch_in(const sckv_pool_stream& s, int32_t B, int64_t N, int
   const int tiles = s.out_layout == SCKV_LAYOUT_KEY_TILES ? 1 : 0;
   const dim3 grid_parts((unsigned)((e_count + epw - 1) / epw), (unsigned)B);
   // overlapping 4:1 windows: a block pools 4 * epw * J consecutive entries (and the
-  // block before them), J as large as keeps 2048 blocks in the grid
+  // block before them), J as large as keeps 1024 blocks in the grid
   int J = 16;
   auto ov_blocks = [&](int j) { return ((e_count + (int64_t)j * 4 * epw - 1) / ((int64_t)j * 4 * epw)) * B; };
-  while (J > 1 && ov_blocks(J) < 2048) J /= 2;
+  while (J > 1 && ov_blocks(J) < 1024) J /= 2;
   const dim3 grid_ov((unsigned)((e_count + (int64_t)J * 4 * epw - 1) / ((int64_t)J * 4 * epw)), (unsigned)B);
 #define SCKV_LAUNCH(OUT, SC)                                                                                   \
   if (m == kOvM && o == kOvM)                                                                                  \
