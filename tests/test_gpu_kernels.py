@@ -342,6 +342,49 @@ def test_overlap_windows_with_wide_bias_spread(D, outs, scaled):
             assert e4m3_flips(got, st["codes"], c / st["scale"][:, None], mag / st["scale"][:, None])[1] == 0
 
 
+@pytest.mark.parametrize("D,outs,e_begin,e_count", [(512, "bf16", 777, 9000), (128, "e4m3", 4099, 33000)])
+def test_overlap_range_equals_whole_sequence(D, outs, e_begin, e_count):
+    """A range of entries starting mid-sequence, long enough that every block of the
+    4:1 compressor pools a run of several steps (the first-half sums handed from
+    slot to slot and across steps): the entries equal those of one call over the
+    whole sequence bit for bit, the entries outside the range stay untouched, and
+    sampled entries follow the oracle in code space."""
+    print(f"overlap range D={D} {outs} e_begin={e_begin} e_count={e_count}", flush=True)
+    rng = np.random.default_rng(9 + D)
+    E = e_begin + e_count + 300
+    N = 4 * E
+    v = rng_store(rng, (1, N, D), "bf16")
+    g = rng_store(rng, (1, N, D), "bf16", 2.0)
+    bpos = rng.normal(0, 0.5, (8, D)).astype(np.float32)
+    vd, gd, bd = dev(v, "bf16"), dev(g, "bf16"), dev(bpos)
+    if outs == "e4m3":
+        whole = torch.zeros(1, E, D, device=DEV, dtype=torch.uint8).view(torch.float8_e4m3fn)
+        part = torch.full((1, E, D), 0x5A, device=DEV, dtype=torch.uint8).view(torch.float8_e4m3fn)
+    else:
+        whole = torch.zeros(1, E, D, device=DEV, dtype=torch.bfloat16)
+        part = torch.full((1, E, D), 7.0, device=DEV, dtype=torch.bfloat16)
+    sk.csa_compress(sk.Pool(vd, gd, bd, whole), m=4, o=4)
+    sk.csa_compress(sk.Pool(vd, gd, bd, part), m=4, o=4, e_begin=e_begin, e_count=e_count)
+    torch.cuda.synchronize()
+    raw = (lambda t: t.view(torch.uint8)) if outs == "e4m3" else (lambda t: t)
+    lo, hi = e_begin, e_begin + e_count
+    assert torch.equal(raw(part)[:, lo:hi], raw(whole)[:, lo:hi]), "a range differs from the whole-sequence call"
+    untouched = 0x5A if outs == "e4m3" else 7.0
+    assert bool((raw(part)[:, :lo] == untouched).all()) and bool((raw(part)[:, hi:] == untouched).all())
+    sample = np.unique(np.concatenate([np.arange(lo, lo + 70), rng.integers(lo, hi, 200), np.arange(hi - 70, hi)]))
+    t0, t1 = 4 * (int(sample.min()) - 1), 4 * int(sample.max()) + 4
+    c_all = method.compress(v[0, t0:t1], g[0, t0:t1], bpos, 4, 4)
+    m_all = method.compress(np.abs(v[0, t0:t1]), g[0, t0:t1], bpos, 4, 4)
+    off = t0 // 4
+    c, mag = c_all[sample - off], m_all[sample - off]
+    got = host(whole[0])[sample]
+    if outs == "bf16":
+        assert bf16_code_flips(got, c, method.store_entries(c, "bf16")["values"], magnitude=mag)[1] == 0
+    else:
+        st = method.store_keys(c, "e4m3")
+        assert e4m3_flips(got, st["codes"], c, mag)[1] == 0
+
+
 def test_compress_appends_only_requested_entries():
     rng = np.random.default_rng(5)
     B, N, D = 2, 256, 64
