@@ -4,12 +4,12 @@
 // DeepSeek-V4 KV-cache article, sections "CSA", "HCA" and "Ventana deslizante").
 //
 // MFMA path (bf16 queries; bf16 or e4m3 entries; bf16 window):
-//   block = (split, row); one wave per 16 heads.  Items are staged 32 at a time
-//   into LDS twice: row-major bf16 for Q.K^T and transposed fp16 for P.V.
+//   block = (split, row); one wave per 16 heads.  Items are staged 32 or 64 at
+//   a time into LDS twice, as bf16: row-major for Q.K^T and transposed for P.V.
 //   S^T = items x heads on v_mfma_f32_16x16x32_bf16 (items as M), so each lane
-//   holds one head column; the S accumulator registers are re-used directly as
-//   the A operand of P.V on v_mfma_f32_16x16x32_f16 (the K order of the item
-//   axis is chosen to match), with an online softmax between the two.
+//   holds one head column; the S accumulator registers become the A operand of
+//   P.V directly (the K order of the item axis is chosen to match), with an
+//   online softmax between the two.  P enters P.V as two bf16 parts (hi + lo).
 //   fp8 entries keep their exact codes in the MFMA operands; the per-entry scale
 //   multiplies the logit and the probability instead.
 //   Split-K over the item list writes (m, l, unnormalised o) partials that a
@@ -145,7 +145,7 @@ struct Lds {
   static constexpr int KR_STRIDE = D + 8;   // bf16 elements per item row
   static constexpr int CELLS = CH / 4;      // 4-item cells per dim row
   uint16_t kr[CH * KR_STRIDE];
-  u32x2 vt[D * CELLS];                      // [dim][cells of 4 items] fp16, cells XOR-swizzled
+  u32x2 vt[D * CELLS];                      // [dim][cells of 4 items] bf16, cells XOR-swizzled
   float isc[CH];
 };
 
@@ -183,15 +183,14 @@ __device__ __forceinline__ void stage_store(const Stage<ENT, D, NW, CH>& st, Lds
         }
         *reinterpret_cast<u32x4*>(&L.kr[(4 * a + i) * Lds<D, CH>::KR_STRIDE + part * 8]) = v[i];
       }
-      // fp16 copies, transposed: cell (dim 8 part + e, group a) = items 4a .. 4a+3 of that dim
+      // the same bf16 values transposed: cell (dim 8 part + e, group a) = items
+      // 4a .. 4a+3 of that dim
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float f[4];
+        uint32_t b[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) f[i] = bf16_to_f32((v[i][e >> 1] >> ((e & 1) * 16)) & 0xffffu);
-        const auto lo = __builtin_amdgcn_cvt_pkrtz(f[0], f[1]);
-        const auto hi = __builtin_amdgcn_cvt_pkrtz(f[2], f[3]);
-        L.vt[vt_cell<CH>(part * 8 + e, a)] = u32x2{bitcast<uint32_t>(lo), bitcast<uint32_t>(hi)};
+        for (int i = 0; i < 4; ++i) b[i] = (v[i][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+        L.vt[vt_cell<CH>(part * 8 + e, a)] = u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
       }
       if (part == 0) {
 #pragma unroll
@@ -294,14 +293,19 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma(AttendParams p) {
       const float alpha = grows ? (m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new)) : 1.f;
       m_run = m_new;
       // P as the A operand of P.V: k-step kk takes items 32kk + {4g..4g+3} (tile 2kk)
-      // and 32kk + 16 + {4g..4g+3} (tile 2kk+1), the order of the S^T registers
-      f16x8 pa[KK];
+      // and 32kk + 16 + {4g..4g+3} (tile 2kk+1), the order of the S^T registers.
+      // With fp8 entries the operand is p times the entry's scale.  It enters as
+      // the sum of two bf16 parts (about 16 significant bits together, fp32's
+      // exponent range): V stays in bf16, exact for decoded fp8 and bf16 values
       float psum = 0.f;
+      bf16x8 ph[KK], pl[KK];
 #pragma unroll
       for (int e = 0; e < 4 * MT; ++e) {
         const float pe = __builtin_amdgcn_exp2f(x[e] - m_use);
         psum += pe;
-        pa[e / 8][e % 8] = (_Float16)(ENT == SCKV_E4M3 ? pe * isc[e] : pe);
+        const float pv = ENT == SCKV_E4M3 ? pe * isc[e] : pe;
+        ph[e / 8][e % 8] = (__bf16)pv;
+        pl[e / 8][e % 8] = (__bf16)(pv - (float)ph[e / 8][e % 8]);
       }
       l_run = l_run * alpha + psum;
       // rescale the output rows (heads 4g + i of this wave) only when some maximum moved
@@ -321,8 +325,9 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma(AttendParams p) {
         for (int kk = 0; kk < KK; ++kk) {
           const u32x2 lo = L.vt[vt_cell<CH>(d, 8 * kk + g)];
           const u32x2 hi = L.vt[vt_cell<CH>(d, 8 * kk + 4 + g)];
-          const f16x8 bv = bitcast<f16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
-          o[nd] = mfma16_f16(pa[kk], bv, o[nd]);
+          const bf16x8 bv = bitcast<bf16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
+          o[nd] = mfma16_bf16(ph[kk], bv, o[nd]);
+          o[nd] = mfma16_bf16(pl[kk], bv, o[nd]);
         }
       }
     }

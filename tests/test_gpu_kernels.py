@@ -601,27 +601,28 @@ ATTEND_CASES = [
 ]
 
 
-@pytest.mark.parametrize("csa,ent,H,D,E_cap,positions,k,outs", ATTEND_CASES)
-def test_attend_decode(csa, ent, H, D, E_cap, positions, k, outs):
-    print(f"attend decode csa={csa} {ent} H={H} D={D} E_cap={E_cap} pos={positions} k={k} out={outs}", flush=True)
-    rng = np.random.default_rng(H * D + E_cap)
+def _attend_case(csa, ent, H, D, E_cap, positions, k, outs, mag=1.0, seed=None):
+    """Runs csa_attend / hca_attend on random decode rows (entries and window rows
+    of size mag, queries of size 0.3 / mag, so the logits stay of order one) and
+    returns the GPU outputs and log-sum-exps with the oracle's."""
+    rng = np.random.default_rng(H * D + E_cap if seed is None else seed)
     B = len(positions)
     qs = "f32" if ent == "f32" else "bf16"
-    q = rng_store(rng, (B, H, D), qs, 0.3)
+    q = rng_store(rng, (B, H, D), qs, 0.3 / mag)
     if ent == "e4m3":
-        st = method.store_entries(rng.normal(0, 1, (B * E_cap, D)), "e4m3")
+        st = method.store_entries(rng.normal(0, mag, (B * E_cap, D)), "e4m3")
         ev_vals = st["values"].reshape(B, E_cap, D)
         ent_dev = dev_codes(st["codes"].reshape(B, E_cap, D))
         esc = dev(st["scale"].reshape(B, E_cap))
     else:
-        ev_vals = rng_store(rng, (B, E_cap, D), ent).astype(np.float64)
+        ev_vals = rng_store(rng, (B, E_cap, D), ent, mag).astype(np.float64)
         ent_dev, esc = dev(ev_vals, ent), None
     R_w = 128
     win_vals = {}
     rings = np.zeros((B, R_w, D), np.float32)
     for b, t in enumerate(positions):
         wp = method.window_positions(t, 128)          # only the window tokens are ever read
-        win_vals[b] = rng_store(rng, (len(wp), D), qs)
+        win_vals[b] = rng_store(rng, (len(wp), D), qs, mag)
         rings[b][wp % R_w] = win_vals[b]
     idx = None
     idx_np = None
@@ -645,6 +646,7 @@ def test_attend_decode(csa, ent, H, D, E_cap, positions, k, outs):
         sk.hca_attend(rows, dev(q, qs), ent_dev, dev(rings, qs), out, **args)
     torch.cuda.synchronize()
     go, gl = host(out), host(lse)
+    want = []
     for b, t in enumerate(positions):
         if csa:
             sel = idx_np[b][idx_np[b] >= 0]
@@ -653,12 +655,46 @@ def test_attend_decode(csa, ent, H, D, E_cap, positions, k, outs):
             ev = min(method.entries_visible(t, 128, 128), E_cap)
             items = np.concatenate([ev_vals[b][:ev], win_vals[b]])
         o, lse_o, _ = method.attend(q[b], items, tau)
+        want.append((o, lse_o))
+    return go, gl, want
+
+
+@pytest.mark.parametrize("csa,ent,H,D,E_cap,positions,k,outs", ATTEND_CASES)
+def test_attend_decode(csa, ent, H, D, E_cap, positions, k, outs):
+    print(f"attend decode csa={csa} {ent} H={H} D={D} E_cap={E_cap} pos={positions} k={k} out={outs}", flush=True)
+    go, gl, want = _attend_case(csa, ent, H, D, E_cap, positions, k, outs)
+    for b, (o, lse_o) in enumerate(want):
         if ent == "f32":
             assert_close(go[b], o, rtol=1e-4, what=f"f32 out row {b}")
         else:
             err = assert_close(go[b], o, atol=2e-2, what=f"out row {b}")
             print(f"  row {b}: max abs err {err:.2e} (max |o| {np.abs(o).max():.2f})")
         np.testing.assert_allclose(gl[b], lse_o, rtol=1e-5, atol=1e-5)
+
+
+# entries, H, D, magnitude: the register-staged kernel (fp8 entries at D = 512 with
+# 64 heads, bf16 entries at other shapes) over values far from 1
+MAGNITUDE_CASES = [
+    ("e4m3", 64, 512, 1e-4),   # per-entry scales near 1e-6: p * scale far below fp16's normal range
+    ("e4m3", 64, 512, 1e7),    # per-entry scales near 1e5: p * scale past fp16's largest value
+    ("bf16", 16, 128, 1e5),    # values past fp16's largest value
+    ("bf16", 16, 128, 1e-6),   # values in fp16's subnormal range
+]
+
+
+@pytest.mark.parametrize("ent,H,D,mag", MAGNITUDE_CASES)
+def test_attend_entry_magnitudes(ent, H, D, mag):
+    """Entries and window rows of size mag, queries of size 1 / mag: the output
+    follows the oracle normwise to 1e-3 of max |o| (P.V takes probabilities, times
+    the fp8 scale, as two bf16 parts over bf16 values, with fp32's exponent range;
+    an fp16 operand would lose these cases to underflow or overflow)."""
+    print(f"attend magnitudes {ent} H={H} D={D} mag={mag:g}", flush=True)
+    go, gl, want = _attend_case(True, ent, H, D, 4096, [16511, 9000], 512, "f32", mag=mag,
+                                seed=H * D + int(round(math.log10(mag))) + 50)
+    for b, (o, lse_o) in enumerate(want):
+        err = assert_close(go[b], o, rtol=1e-3, what=f"out row {b}")
+        print(f"  row {b}: max err {err:.2e} (max |o| {np.abs(o).max():.3e})")
+        np.testing.assert_allclose(gl[b], lse_o, rtol=1e-4, atol=1e-4)
 
 
 def test_attend_causal_rows_and_determinism():
