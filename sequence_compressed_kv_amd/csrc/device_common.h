@@ -8,6 +8,7 @@
 namespace sckv {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) int32_t i32x4;
@@ -67,6 +68,9 @@ __device__ __forceinline__ float key_score(uint32_t k) {
 // elements of K-group l/16; D lane l holds column l%16, rows 4*(l/16) + i.
 __device__ __forceinline__ f32x4 mfma16_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16_f16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 // 16x16x4 fp32: A lane l holds row l%16, B lane l column l%16, each the K element
 // l/16; D as for 16x16x32.
