@@ -43,6 +43,43 @@ __device__ __forceinline__ int64_t row_visible(const TopkRows& rr, int r) {
   return e < rr.E_cap ? e : rr.E_cap;
 }
 
+// Elements wbase + (i*64 + l)*4 + j (i < V/4, j < 4) of a row of len 32-bit
+// values, for lane l of a wave; 0 past the end.  Every load is issued before any
+// is used, so the wave's part costs one memory round trip: a wave whose elements
+// all exist reads 16-byte vectors (wbase wave-uniform), a ragged wave reads each
+// element from an address clamped into the row and masks it afterwards.
+template <int V, typename T>
+__device__ __forceinline__ void load_part(const T* src, int64_t len, int64_t wbase, T (&s)[V]) {
+  static_assert(sizeof(T) == 4, "32-bit values");
+  constexpr int NI = V / 4;
+  typedef __attribute__((ext_vector_type(4))) T T4;
+  const int l = lane_id();
+  const bool vec = ((reinterpret_cast<uintptr_t>(src) & 15u) == 0);
+  if (vec && wbase + 64 * V <= len) {
+    T4 v[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) v[i] = *reinterpret_cast<const T4*>(src + wbase + ((int64_t)i * 64 + l) * 4);
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s[4 * i + j] = v[i][j];
+  } else if (len > 0) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int64_t e = wbase + ((int64_t)(v / 4) * 64 + l) * 4 + (v % 4);
+      s[v] = src[e < len ? e : len - 1];
+    }
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int64_t e = wbase + ((int64_t)(v / 4) * 64 + l) * 4 + (v % 4);
+      if (e >= len) s[v] = T(0);
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < V; ++v) s[v] = T(0);
+  }
+}
+
 // Bin of the kk_rem-th largest element of an LDS histogram (kBins bins, counted
 // from the top): ctl[0] = bin, ctl[1] = kk_rem minus the elements in higher bins.
 // Every thread must call it (block scan, barriers).
@@ -228,39 +265,19 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
   int32_t idx[V];
   bool valid[V];
   const float* src = MODE == TOPK_MERGE ? cand_s + (int64_t)r * cap : scores + (int64_t)r * stride + base;
-  const bool vec = ((reinterpret_cast<uintptr_t>(src) & 15u) == 0);
+  const int64_t wbase = (int64_t)w * 64 * V;
+  float sc[V];
+  int32_t ci[V];
+  load_part<V>(src, len, wbase, sc);
+  if (MODE == TOPK_MERGE) load_part<V>(cand_i + (int64_t)r * cap, len, wbase, ci);
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int64_t e0 = (int64_t)w * 64 * V + ((int64_t)i * 64 + l) * 4;
-    float s4[4] = {0.f, 0.f, 0.f, 0.f};
-    int32_t i4[4] = {-1, -1, -1, -1};
-    if (vec && e0 + 3 < len) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(src + e0);
-      s4[0] = v[0]; s4[1] = v[1]; s4[2] = v[2]; s4[3] = v[3];
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (e0 + j < len) s4[j] = src[e0 + j];
-    }
-    if (MODE == TOPK_MERGE) {
-      if (vec && e0 + 3 < len) {
-        const i32x4 v = *reinterpret_cast<const i32x4*>(cand_i + (int64_t)r * cap + e0);
-        i4[0] = v[0]; i4[1] = v[1]; i4[2] = v[2]; i4[3] = v[3];
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (e0 + j < len) i4[j] = cand_i[(int64_t)r * cap + e0 + j];
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t e = e0 + j;
-      bool ok = e < len;
-      if (MODE == TOPK_MERGE) ok = ok && i4[j] >= 0;           // unused candidate slots hold -1
-      valid[4 * i + j] = ok;
-      key[4 * i + j] = ok ? score_key(s4[j]) : 0u;
-      idx[4 * i + j] = MODE == TOPK_MERGE ? i4[j] : (int32_t)(base + e);
-    }
+  for (int v = 0; v < V; ++v) {
+    const int64_t e = wbase + ((int64_t)(v / 4) * 64 + l) * 4 + (v % 4);
+    bool ok = e < len;
+    if (MODE == TOPK_MERGE) ok = ok && ci[v] >= 0;             // unused candidate slots hold -1
+    valid[v] = ok;
+    key[v] = ok ? score_key(sc[v]) : 0u;
+    idx[v] = MODE == TOPK_MERGE ? ci[v] : (int32_t)(base + e);
   }
 
   // number of valid elements and how many to keep
@@ -314,28 +331,17 @@ constexpr int kMbMaxBlocks = 1024;                                  // blocks pe
 template <int NT, int V>
 __device__ __forceinline__ void load_row_part(const float* src, int64_t len, int64_t base, uint32_t (&key)[V],
                                               int32_t (&idx)[V], bool (&valid)[V]) {
-  constexpr int NI = V / 4;
   const int w = wave_id(), l = lane_id();
-  const bool vec = ((reinterpret_cast<uintptr_t>(src) & 15u) == 0);
+  const int64_t wbase = (int64_t)w * 64 * V;
+  float sc[V];
+  load_part<V>(src, len, wbase, sc);
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int64_t e0 = (int64_t)w * 64 * V + ((int64_t)i * 64 + l) * 4;
-    float s4[4] = {0.f, 0.f, 0.f, 0.f};
-    if (vec && e0 + 3 < len) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(src + e0);
-      s4[0] = v[0]; s4[1] = v[1]; s4[2] = v[2]; s4[3] = v[3];
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (e0 + j < len) s4[j] = src[e0 + j];
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bool ok = e0 + j < len;
-      valid[4 * i + j] = ok;
-      key[4 * i + j] = ok ? score_key(s4[j]) : 0u;
-      idx[4 * i + j] = (int32_t)(base + e0 + j);
-    }
+  for (int v = 0; v < V; ++v) {
+    const int64_t e = wbase + ((int64_t)(v / 4) * 64 + l) * 4 + (v % 4);
+    const bool ok = e < len;
+    valid[v] = ok;
+    key[v] = ok ? score_key(sc[v]) : 0u;
+    idx[v] = (int32_t)(base + e);
   }
 }
 
