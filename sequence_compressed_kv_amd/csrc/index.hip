@@ -220,20 +220,9 @@ __global__ __launch_bounds__(256) void index_score_decode(
   const RowRef rr = row_ref(SCKV_ROWS_DECODE, pos, pos_max, 0, 0, r);
   const int64_t e_vis = visible(rr.t, m, W, E_cap);
   if ((int64_t)blockIdx.x * 4 * KPW >= e_vis) return;           // whole block past the row
-  for (int i = threadIdx.x; i < HI * DI / 8; i += 256) {
-    const int h = i / (DI / 8), c = i % (DI / 8);
-    *reinterpret_cast<u32x4*>(&qs[h * QS + c * 8]) =
-        *reinterpret_cast<const u32x4*>(q + ((int64_t)r * HI + h) * DI + c * 8);
-  }
   const int l = lane_id(), n = l & 31, hh = l >> 5;
-  float wr[MT][16];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) wr[mt][i] = w[(int64_t)r * HI + 32 * mt + 8 * (i >> 2) + 4 * hh + (i & 3)];
-  __syncthreads();
+  // a wave past the row's last key re-reads its last tile and stores nothing
   const int64_t j_begin = ((int64_t)blockIdx.x * 4 + wave_id()) * KPW;
-  if (j_begin >= e_vis) return;
   const int64_t j_end = j_begin + KPW < e_vis ? j_begin + KPW : e_vis;
   const int64_t key_row0 = rr.seq * E_cap;
   float* srow = scores + (int64_t)r * stride;
@@ -245,6 +234,24 @@ __global__ __launch_bounds__(256) void index_score_decode(
     if constexpr (KEY == SCKV_MXFP4) load_fp4_tile<DI>(gkeys, (key_row0 + (key & ~(int64_t)31)) / 32 * (17 * DI), n, hh, b);
     else load_key_tile<KEY, DI>(gkeys, key_tile_elem<DI>(key_row0 * DI, key, hh * KS), b);
   };
+  // the first two tiles' loads go out before the query is staged, so the
+  // stream of keys starts one round trip earlier
+  bf16x8 buf[3][KS];
+  load(0, buf[0]);
+  if constexpr (NT > 1) load(1, buf[1]);
+  for (int i = threadIdx.x; i < HI * DI / 8; i += 256) {
+    const int h = i / (DI / 8), c = i % (DI / 8);
+    *reinterpret_cast<u32x4*>(&qs[h * QS + c * 8]) =
+        *reinterpret_cast<const u32x4*>(q + ((int64_t)r * HI + h) * DI + c * 8);
+  }
+  float wr[MT][16];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) wr[mt][i] = w[(int64_t)r * HI + 32 * mt + 8 * (i >> 2) + 4 * hh + (i & 3)];
+  __syncthreads();
+  if (j_begin >= e_vis) return;
+
   auto compute = [&](int t, const bf16x8 (&b)[KS]) {
     float part = 0.f;
 #pragma unroll
@@ -263,9 +270,6 @@ __global__ __launch_bounds__(256) void index_score_decode(
     if (hh == 0 && j < j_end) srow[j] = tot == 0.f ? 0.f : tot;
   };
 
-  bf16x8 buf[3][KS];
-  load(0, buf[0]);
-  if constexpr (NT > 1) load(1, buf[1]);
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     if (t + 2 < NT) load(t + 2, buf[(t + 2) % 3]);
