@@ -182,20 +182,30 @@ __device__ __forceinline__ void select_ordered(const uint32_t (&key)[V], const i
                                                uint32_t b1 = 0, uint32_t above = 0) {
   constexpr int NI = V / 4;
   uint32_t T = 0, need = UINT_MAX;
+  bool all_eq = true;                    // every key equal to T is kept (no tie to break)
   if (kk < n_valid) {
     if (b1) T = radix_threshold<NT, V>(key, valid, kk - above, hist, scan_sh, ctl, &need, (b1 - 1) << 20, 1);
     else T = radix_threshold<NT, V>(key, valid, kk, hist, scan_sh, ctl, &need);
+    // the last pass's histogram counts the keys equal to T (the same value in
+    // every thread, read after that pass's final barrier)
+    all_eq = hist[T & kDMask[2]] == need;
   }
 
-  // ordered compaction: keys above T, then the first `need` keys equal to T
+  // ordered compaction: keys above T, then the first `need` keys equal to T; the
+  // ranks among keys equal to T are only needed when some of them are left out
   uint32_t ceq[NI], eq_off[NI], tot;
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     ceq[i] = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) ceq[i] += (valid[4 * i + j] && key[4 * i + j] == T) ? 1u : 0u;
+    eq_off[i] = 0;
   }
-  ordered_scan<NT, NI>(ceq, eq_off, scan_sh, &tot);
+  if (!all_eq) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ceq[i] += (valid[4 * i + j] && key[4 * i + j] == T) ? 1u : 0u;
+    ordered_scan<NT, NI>(ceq, eq_off, scan_sh, &tot);
+  }
   bool sel[V];
   uint32_t csel[NI], sel_off[NI];
 #pragma unroll
@@ -206,7 +216,7 @@ __device__ __forceinline__ void select_ordered(const uint32_t (&key)[V], const i
     for (int j = 0; j < 4; ++j) {
       const int v = 4 * i + j;
       bool sv = valid[v] && key[v] > T;
-      if (valid[v] && key[v] == T) sv = eq_rank++ < need;
+      if (valid[v] && key[v] == T) sv = all_eq || eq_rank++ < need;
       sel[v] = sv;
       csel[i] += sv ? 1u : 0u;
     }
@@ -280,12 +290,17 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
     idx[v] = MODE == TOPK_MERGE ? ci[v] : (int32_t)(base + e);
   }
 
-  // number of valid elements and how many to keep
-  uint32_t nv = 0;
-#pragma unroll
-  for (int v = 0; v < V; ++v) nv += valid[v] ? 1u : 0u;
+  // number of valid elements (a row or slice: its length; the merge counts the
+  // used candidate slots) and how many to keep
   uint32_t n_valid;
-  (void)block_excl_scan<NT>(nv, scan_sh, &n_valid);
+  if (MODE == TOPK_MERGE) {
+    uint32_t nv = 0;
+#pragma unroll
+    for (int v = 0; v < V; ++v) nv += valid[v] ? 1u : 0u;
+    (void)block_excl_scan<NT>(nv, scan_sh, &n_valid);
+  } else {
+    n_valid = (uint32_t)(len < (int64_t)NT * V ? len : (int64_t)NT * V);
+  }
   const uint32_t kk = n_valid < (uint32_t)k ? n_valid : (uint32_t)k;
 
   int32_t* oi;
