@@ -497,6 +497,17 @@ __device__ __forceinline__ void ov_block_sums(const RawBlock<IN>& rb, const floa
   }
 }
 
+// Arguments of one stream of the overlapping-window compressor.
+struct OvArgs {
+  const void* val;
+  const void* gate;
+  const float* bpos;
+  void* out;
+  float* out_scale;
+  int64_t N, e_begin, e_count, E_cap;
+  int D, G, key_tiles, J;
+};
+
 // Overlapping 4:1 windows (m = o = 4) by the factored softmax.  The S = 4 * 64/G
 // lane groups ("slots", G = D/8 lanes each) of a block take S consecutive entries
 // per step, J steps in turn, so a block pools a run of S * J consecutive entries.
@@ -506,17 +517,23 @@ __device__ __forceinline__ void ov_block_sums(const RawBlock<IN>& rb, const floa
 // same step (slot 0: slot S-1 in the step before), passed through LDS.  Only the
 // block before the run is pooled twice.  Channels whose bias rows spread too far
 // take the online path entry by entry.
+// The block (bx, b) of one stream's grid (block-uniform: every barrier inside is
+// reached by the whole block).
 template <int IN, int OUT, bool SCALED>
-__global__ __launch_bounds__(256) void compress_overlap_kernel(
-    const void* __restrict__ val, const void* __restrict__ gate, const float* __restrict__ bpos,
-    void* __restrict__ out, float* __restrict__ out_scale, int64_t N, int D, int64_t e_begin, int64_t e_count,
-    int64_t E_cap, int G, int key_tiles, int J) {
+__device__ __forceinline__ void overlap_run(const OvArgs& a, int64_t bx, int64_t by) {
+  const void* __restrict__ val = a.val;
+  const void* __restrict__ gate = a.gate;
+  const float* __restrict__ bpos = a.bpos;
+  void* __restrict__ out = a.out;
+  float* __restrict__ out_scale = a.out_scale;
+  const int64_t N = a.N, e_begin = a.e_begin, e_count = a.e_count, E_cap = a.E_cap;
+  const int D = a.D, G = a.G, key_tiles = a.key_tiles, J = a.J;
   const int lane = lane_id();
   const int epw = kWave / G;
   const int S = 4 * epw;
   const int gs = wave_id() * epw + lane / G, sub = lane % G;    // slot in the block; threadIdx.x = gs * G + sub
-  const int64_t R0 = (int64_t)blockIdx.x * S * J;               // the block's first local entry
-  const int64_t b = blockIdx.y;
+  const int64_t R0 = bx * S * J;                                // the block's first local entry
+  const int64_t b = by;
   const int ch = sub * 8;
   // the bias factors of all D channels, [row][channel], shared by the block's slots
   __shared__ __attribute__((aligned(16))) float u_sh[2 * kOvM * kOvMaxD];
@@ -596,6 +613,21 @@ __global__ __launch_bounds__(256) void compress_overlap_kernel(
       for (int c = 0; c < 8; ++c) { sp[c] = cw[c][src]; lp[c] = cw[8 + c][src]; ap[c] = cw[16 + c][src]; }
     }
   }
+}
+
+template <int IN, int OUT, bool SCALED>
+__global__ __launch_bounds__(256) void compress_overlap_kernel(OvArgs a) {
+  overlap_run<IN, OUT, SCALED>(a, blockIdx.x, blockIdx.y);
+}
+
+// Two streams of the same types in one grid (the latent and the indexer keys of
+// a CSA layer): blocks 0 .. nb0 - 1 take the first, the rest the second, so the
+// second stream's blocks fill the first one's tail instead of a launch of
+// their own.
+template <int IN, int OUT, bool SCALED>
+__global__ __launch_bounds__(256) void compress_overlap_pair(OvArgs a0, OvArgs a1, unsigned nb0) {
+  if (blockIdx.x < nb0) overlap_run<IN, OUT, SCALED>(a0, blockIdx.x, blockIdx.y);
+  else overlap_run<IN, OUT, SCALED>(a1, blockIdx.x - nb0, blockIdx.y);
 }
 
 // Windows of 64 tokens or more (HCA): the 4 parts of each window on the 4 waves
@@ -734,6 +766,21 @@ __global__ __launch_bounds__(256) void append_kernel(AppendK s0, AppendK s1, int
   store_entry<OUT, SCALED>(st, ch, G, active, lane, b, e, D, s.E_cap, s.key_tiles, s.out, s.out_scale);
 }
 
+// Overlapping 4:1 windows: a block pools 4 * epw * J consecutive entries (and the
+// block before them), J as large as keeps 1024 blocks in the stream's grid
+// (*nbx blocks along x, B along y).
+static OvArgs ov_args(const sckv_pool_stream& s, int32_t B, int64_t N, int64_t e_begin, int64_t e_count,
+                      unsigned* nbx) {
+  const int G = s.D / 8;
+  const int epw = kWave / G;
+  int J = 16;
+  auto ov_blocks = [&](int j) { return ((e_count + (int64_t)j * 4 * epw - 1) / ((int64_t)j * 4 * epw)) * B; };
+  while (J > 1 && ov_blocks(J) < 1024) J /= 2;
+  *nbx = (unsigned)((e_count + (int64_t)J * 4 * epw - 1) / ((int64_t)J * 4 * epw));
+  const int tiles = s.out_layout == SCKV_LAYOUT_KEY_TILES ? 1 : 0;
+  return OvArgs{s.val, s.gate, s.bpos, s.out, s.out_scale, N, e_begin, e_count, s.E_cap, s.D, G, tiles, J};
+}
+
 template <int IN>
 static hipError_t launch_in(const sckv_pool_stream& s, int32_t B, int64_t N, int32_t m, int32_t o,
                             int64_t e_begin, int64_t e_count, hipStream_t stream) {
@@ -743,16 +790,12 @@ static hipError_t launch_in(const sckv_pool_stream& s, int32_t B, int64_t N, int
   const dim3 block(256);
   const int tiles = s.out_layout == SCKV_LAYOUT_KEY_TILES ? 1 : 0;
   const dim3 grid_parts((unsigned)((e_count + epw - 1) / epw), (unsigned)B);
-  // overlapping 4:1 windows: a block pools 4 * epw * J consecutive entries (and the
-  // block before them), J as large as keeps 1024 blocks in the grid
-  int J = 16;
-  auto ov_blocks = [&](int j) { return ((e_count + (int64_t)j * 4 * epw - 1) / ((int64_t)j * 4 * epw)) * B; };
-  while (J > 1 && ov_blocks(J) < 1024) J /= 2;
-  const dim3 grid_ov((unsigned)((e_count + (int64_t)J * 4 * epw - 1) / ((int64_t)J * 4 * epw)), (unsigned)B);
+  unsigned nb_ov;
+  const OvArgs ov = ov_args(s, B, N, e_begin, e_count, &nb_ov);
+  const dim3 grid_ov(nb_ov, (unsigned)B);
 #define SCKV_LAUNCH(OUT, SC)                                                                                   \
   if (m == kOvM && o == kOvM)                                                                                  \
-    hipLaunchKernelGGL((compress_overlap_kernel<IN, OUT, SC>), grid_ov, block, 0, stream, s.val, s.gate,       \
-                       s.bpos, s.out, s.out_scale, N, s.D, e_begin, e_count, s.E_cap, G, tiles, J);             \
+    hipLaunchKernelGGL((compress_overlap_kernel<IN, OUT, SC>), grid_ov, block, 0, stream, ov);                 \
   else if (m + o >= 64)                                                                                        \
     hipLaunchKernelGGL((compress_parts_kernel<IN, OUT, SC>), grid_parts, block, 0, stream, s.val, s.gate,      \
                        s.bpos, s.out, s.out_scale, N, s.D, m, o, e_begin, e_count, s.E_cap, G, tiles);          \
@@ -819,6 +862,43 @@ hipError_t launch_compress(const sckv_pool_stream& s, int32_t B, int64_t N, int3
   if (e_count == 0) return hipSuccess;
   if (s.in_dtype == SCKV_BF16) return launch_in<SCKV_BF16>(s, B, N, m, o, e_begin, e_count, stream);
   return launch_in<SCKV_F32>(s, B, N, m, o, e_begin, e_count, stream);
+}
+
+template <int IN>
+static hipError_t launch_pair_in(const sckv_pool_stream& s0, const sckv_pool_stream& s1, int32_t B, int64_t N,
+                                 int64_t e_begin, int64_t e_count, hipStream_t stream) {
+  unsigned nb0, nb1;
+  const OvArgs a0 = ov_args(s0, B, N, e_begin, e_count, &nb0);
+  const OvArgs a1 = ov_args(s1, B, N, e_begin, e_count, &nb1);
+  const dim3 grid(nb0 + nb1, (unsigned)B);
+#define SCKV_LAUNCH(OUT, SC) \
+  hipLaunchKernelGGL((compress_overlap_pair<IN, OUT, SC>), grid, dim3(256), 0, stream, a0, a1, nb0)
+  switch (s0.out_dtype) {
+    case SCKV_F32: SCKV_LAUNCH(SCKV_F32, false); break;
+    case SCKV_BF16: SCKV_LAUNCH(SCKV_BF16, false); break;
+    case SCKV_MXFP4: SCKV_LAUNCH(SCKV_MXFP4, false); break;
+    default:
+      if (s0.out_scale) SCKV_LAUNCH(SCKV_E4M3, true);
+      else SCKV_LAUNCH(SCKV_E4M3, false);
+  }
+#undef SCKV_LAUNCH
+  return hipGetLastError();
+}
+
+// A CSA layer's two streams: overlapping 4:1 windows of the same input and output
+// types share one launch; otherwise each stream takes its own.
+hipError_t launch_compress_pair(const sckv_pool_stream& s0, const sckv_pool_stream& s1, int32_t B, int64_t N,
+                                int32_t m, int32_t o, int64_t e_begin, int64_t e_count, hipStream_t stream) {
+  if (e_count == 0) return hipSuccess;
+  const bool pair = m == kOvM && o == kOvM && s0.in_dtype == s1.in_dtype && s0.out_dtype == s1.out_dtype &&
+                    (s0.out_dtype != SCKV_E4M3 || (s0.out_scale != nullptr) == (s1.out_scale != nullptr));
+  if (!pair) {
+    hipError_t e = launch_compress(s0, B, N, m, o, e_begin, e_count, stream);
+    if (e == hipSuccess) e = launch_compress(s1, B, N, m, o, e_begin, e_count, stream);
+    return e;
+  }
+  if (s0.in_dtype == SCKV_BF16) return launch_pair_in<SCKV_BF16>(s0, s1, B, N, e_begin, e_count, stream);
+  return launch_pair_in<SCKV_F32>(s0, s1, B, N, e_begin, e_count, stream);
 }
 
 }  // namespace sckv

@@ -358,8 +358,8 @@ sckv_status csa_compress(int32_t B, int64_t N, int32_t m, int32_t o, int64_t e_b
     if (s != SCKV_OK) return s;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = sckv::launch_compress(*kv, B, N, m, o, e_begin, e_count, st);
-  if (e == hipSuccess && index_keys) e = sckv::launch_compress(*index_keys, B, N, m, o, e_begin, e_count, st);
+  const hipError_t e = index_keys ? sckv::launch_compress_pair(*kv, *index_keys, B, N, m, o, e_begin, e_count, st)
+                                   : sckv::launch_compress(*kv, B, N, m, o, e_begin, e_count, st);
   return hip_status(e, "csa_compress");
 }
 
