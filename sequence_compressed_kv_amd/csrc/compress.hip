@@ -519,8 +519,16 @@ struct OvArgs {
 // take the online path entry by entry.
 // The block (bx, b) of one stream's grid (block-uniform: every barrier inside is
 // reached by the whole block).
+// LDS of an overlap block: the bias factors of all D channels ([row][channel],
+// shared by the block's slots) and the first-half state (block max, sums) of
+// each slot's block, two steps' worth.
+struct OvLds {
+  __attribute__((aligned(16))) float u_sh[2 * kOvM * kOvMaxD];
+  float carry[2][3 * 8][256];
+};
+
 template <int IN, int OUT, bool SCALED>
-__device__ __forceinline__ void overlap_run(const OvArgs& a, int64_t bx, int64_t by) {
+__device__ __forceinline__ void overlap_run(const OvArgs& a, int64_t bx, int64_t by, OvLds& L) {
   const void* __restrict__ val = a.val;
   const void* __restrict__ gate = a.gate;
   const float* __restrict__ bpos = a.bpos;
@@ -535,10 +543,8 @@ __device__ __forceinline__ void overlap_run(const OvArgs& a, int64_t bx, int64_t
   const int64_t R0 = bx * S * J;                                // the block's first local entry
   const int64_t b = by;
   const int ch = sub * 8;
-  // the bias factors of all D channels, [row][channel], shared by the block's slots
-  __shared__ __attribute__((aligned(16))) float u_sh[2 * kOvM * kOvMaxD];
-  // first-half state (block max, sums) of each slot's block, two steps' worth
-  __shared__ float carry[2][3 * 8][256];
+  float* u_sh = L.u_sh;
+  float (*carry)[3 * 8][256] = L.carry;
   bool ok = true;
   for (int c = threadIdx.x; c < D; c += blockDim.x) {
     float uc[2 * kOvM];
@@ -617,17 +623,19 @@ __device__ __forceinline__ void overlap_run(const OvArgs& a, int64_t bx, int64_t
 
 template <int IN, int OUT, bool SCALED>
 __global__ __launch_bounds__(256) void compress_overlap_kernel(OvArgs a) {
-  overlap_run<IN, OUT, SCALED>(a, blockIdx.x, blockIdx.y);
+  __shared__ OvLds L;
+  overlap_run<IN, OUT, SCALED>(a, blockIdx.x, blockIdx.y, L);
 }
 
-// Two streams of the same types in one grid (the latent and the indexer keys of
-// a CSA layer): blocks 0 .. nb0 - 1 take the first, the rest the second, so the
-// second stream's blocks fill the first one's tail instead of a launch of
-// their own.
-template <int IN, int OUT, bool SCALED>
+// Two streams of one input type in one grid (the latent and the indexer keys of
+// a CSA layer; each with its own output type): blocks 0 .. nb0 - 1 take the
+// first, the rest the second, so the second stream's blocks fill the first one's
+// tail instead of a launch of their own.
+template <int IN, int OUT0, bool SC0, int OUT1, bool SC1>
 __global__ __launch_bounds__(256) void compress_overlap_pair(OvArgs a0, OvArgs a1, unsigned nb0) {
-  if (blockIdx.x < nb0) overlap_run<IN, OUT, SCALED>(a0, blockIdx.x, blockIdx.y);
-  else overlap_run<IN, OUT, SCALED>(a1, blockIdx.x - nb0, blockIdx.y);
+  __shared__ OvLds L;
+  if (blockIdx.x < nb0) overlap_run<IN, OUT0, SC0>(a0, blockIdx.x, blockIdx.y, L);
+  else overlap_run<IN, OUT1, SC1>(a1, blockIdx.x - nb0, blockIdx.y, L);
 }
 
 // Windows of 64 tokens or more (HCA): the 4 parts of each window on the 4 waves
@@ -864,41 +872,47 @@ hipError_t launch_compress(const sckv_pool_stream& s, int32_t B, int64_t N, int3
   return launch_in<SCKV_F32>(s, B, N, m, o, e_begin, e_count, stream);
 }
 
-template <int IN>
-static hipError_t launch_pair_in(const sckv_pool_stream& s0, const sckv_pool_stream& s1, int32_t B, int64_t N,
-                                 int64_t e_begin, int64_t e_count, hipStream_t stream) {
-  unsigned nb0, nb1;
-  const OvArgs a0 = ov_args(s0, B, N, e_begin, e_count, &nb0);
-  const OvArgs a1 = ov_args(s1, B, N, e_begin, e_count, &nb1);
-  const dim3 grid(nb0 + nb1, (unsigned)B);
-#define SCKV_LAUNCH(OUT, SC) \
-  hipLaunchKernelGGL((compress_overlap_pair<IN, OUT, SC>), grid, dim3(256), 0, stream, a0, a1, nb0)
-  switch (s0.out_dtype) {
-    case SCKV_F32: SCKV_LAUNCH(SCKV_F32, false); break;
-    case SCKV_BF16: SCKV_LAUNCH(SCKV_BF16, false); break;
-    case SCKV_MXFP4: SCKV_LAUNCH(SCKV_MXFP4, false); break;
-    default:
-      if (s0.out_scale) SCKV_LAUNCH(SCKV_E4M3, true);
-      else SCKV_LAUNCH(SCKV_E4M3, false);
+// Output kinds of a pair launch: bf16 / e4m3 scaled / e4m3 / MXFP4 (one
+// template instance per supported combination).
+enum OvKind { OV_BF16, OV_E4M3_SCALED, OV_E4M3, OV_MXFP4, OV_OTHER };
+static OvKind ov_kind(const sckv_pool_stream& s) {
+  switch (s.out_dtype) {
+    case SCKV_BF16: return OV_BF16;
+    case SCKV_E4M3: return s.out_scale ? OV_E4M3_SCALED : OV_E4M3;
+    case SCKV_MXFP4: return OV_MXFP4;
+    default: return OV_OTHER;
   }
-#undef SCKV_LAUNCH
-  return hipGetLastError();
 }
 
-// A CSA layer's two streams: overlapping 4:1 windows of the same input and output
-// types share one launch; otherwise each stream takes its own.
+// A CSA layer's two streams: with bf16 input and overlapping 4:1 windows, the
+// combinations below share one launch (the latent in bf16 or scaled e4m3, the
+// indexer keys in the same type, unscaled e4m3 or MXFP4); otherwise each stream
+// takes its own.
 hipError_t launch_compress_pair(const sckv_pool_stream& s0, const sckv_pool_stream& s1, int32_t B, int64_t N,
                                 int32_t m, int32_t o, int64_t e_begin, int64_t e_count, hipStream_t stream) {
   if (e_count == 0) return hipSuccess;
-  const bool pair = m == kOvM && o == kOvM && s0.in_dtype == s1.in_dtype && s0.out_dtype == s1.out_dtype &&
-                    (s0.out_dtype != SCKV_E4M3 || (s0.out_scale != nullptr) == (s1.out_scale != nullptr));
-  if (!pair) {
-    hipError_t e = launch_compress(s0, B, N, m, o, e_begin, e_count, stream);
-    if (e == hipSuccess) e = launch_compress(s1, B, N, m, o, e_begin, e_count, stream);
-    return e;
+  const OvKind k0 = ov_kind(s0), k1 = ov_kind(s1);
+  const bool ov = m == kOvM && o == kOvM && s0.in_dtype == SCKV_BF16 && s1.in_dtype == SCKV_BF16;
+  unsigned nb0 = 0, nb1 = 0;
+  const OvArgs a0 = ov_args(s0, B, N, e_begin, e_count, &nb0);
+  const OvArgs a1 = ov_args(s1, B, N, e_begin, e_count, &nb1);
+  const dim3 grid(nb0 + nb1, (unsigned)B), block(256);
+#define SCKV_PAIR(O0, S0, O1, S1) \
+  hipLaunchKernelGGL((compress_overlap_pair<SCKV_BF16, O0, S0, O1, S1>), grid, block, 0, stream, a0, a1, nb0)
+  bool launched = ov;
+  if (ov) {
+    if (k0 == OV_BF16 && k1 == OV_BF16) SCKV_PAIR(SCKV_BF16, false, SCKV_BF16, false);
+    else if (k0 == OV_BF16 && k1 == OV_MXFP4) SCKV_PAIR(SCKV_BF16, false, SCKV_MXFP4, false);
+    else if (k0 == OV_E4M3_SCALED && k1 == OV_E4M3) SCKV_PAIR(SCKV_E4M3, true, SCKV_E4M3, false);
+    else if (k0 == OV_E4M3_SCALED && k1 == OV_E4M3_SCALED) SCKV_PAIR(SCKV_E4M3, true, SCKV_E4M3, true);
+    else if (k0 == OV_E4M3_SCALED && k1 == OV_MXFP4) SCKV_PAIR(SCKV_E4M3, true, SCKV_MXFP4, false);
+    else launched = false;
   }
-  if (s0.in_dtype == SCKV_BF16) return launch_pair_in<SCKV_BF16>(s0, s1, B, N, e_begin, e_count, stream);
-  return launch_pair_in<SCKV_F32>(s0, s1, B, N, e_begin, e_count, stream);
+#undef SCKV_PAIR
+  if (launched) return hipGetLastError();
+  hipError_t e = launch_compress(s0, B, N, m, o, e_begin, e_count, stream);
+  if (e == hipSuccess) e = launch_compress(s1, B, N, m, o, e_begin, e_count, stream);
+  return e;
 }
 
 }  // namespace sckv

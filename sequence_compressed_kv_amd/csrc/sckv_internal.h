@@ -18,7 +18,7 @@ inline int64_t entries_visible(int64_t t, int64_t m, int64_t W) {
 hipError_t launch_compress(const sckv_pool_stream& s, int32_t B, int64_t N, int32_t m, int32_t o,
                            int64_t e_begin, int64_t e_count, hipStream_t stream);
 // Both streams of a CSA layer: one launch when they pool overlapping 4:1 windows
-// with the same input and output types, else one launch each.
+// of bf16 input into a supported pair of output types, else one launch each.
 hipError_t launch_compress_pair(const sckv_pool_stream& s0, const sckv_pool_stream& s1, int32_t B, int64_t N,
                                 int32_t m, int32_t o, int64_t e_begin, int64_t e_count, hipStream_t stream);
 // Decode append of one stream, or of two streams (s2 non-NULL) over the same positions.

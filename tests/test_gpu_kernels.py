@@ -294,21 +294,41 @@ def test_csa_append_two_streams(kv_out, scaled):
         assert torch.equal(sa, sb)
 
 
-# ins, outs, scaled, latent dim, key dim, keys tiled, tokens, first entry, entries (None: the rest), latent bias spread
+# input, latent output ("e4m3s": scaled e4m3), key output, latent dim, key dim, keys tiled, tokens,
+# first entry, entries (None: the rest), a latent channel with a wide bias spread
 PAIR_CASES = [
-    ("bf16", "bf16", False, 512, 128, True, 40000, 0, None, False),     # the 128K layer's types, J > 1
-    ("bf16", "bf16", False, 512, 128, True, 20000, 1001, 3000, True),   # an entry range; wide-spread latent channel
-    ("f32", "f32", False, 256, 64, False, 6000, 0, None, False),
-    ("bf16", "e4m3", True, 512, 128, False, 9000, 7, 2000, False),
+    ("bf16", "bf16", "bf16", 512, 128, True, 40000, 0, None, False),      # the 128K layer's types, J > 1
+    ("bf16", "bf16", "bf16", 512, 128, True, 20000, 1001, 3000, True),    # an entry range, online-path channel
+    ("bf16", "e4m3s", "e4m3", 512, 128, True, 30000, 0, None, False),     # the 1M layer's types
+    ("bf16", "e4m3s", "e4m3s", 512, 128, False, 9000, 7, 2000, False),
+    ("bf16", "bf16", "mxfp4", 512, 128, True, 12000, 0, None, True),      # MXFP4 indexer keys
+    ("bf16", "e4m3s", "mxfp4", 256, 64, True, 8000, 33, 1500, False),
+    ("f32", "f32", "f32", 256, 64, False, 6000, 0, None, False),          # no pair instance: two launches
 ]
 
 
-@pytest.mark.parametrize("ins,outs,scaled,D,DI,tiled,N,e_begin,e_count,spread", PAIR_CASES)
-def test_csa_compress_pair_equals_single_streams(ins, outs, scaled, D, DI, tiled, N, e_begin, e_count, spread):
-    """csa_compress with both streams of matching types runs them in one grid; its
-    entries equal those of two single-stream calls bit for bit (so the single
-    stream's parity with the oracle carries over)."""
-    print(f"compress pair {ins}->{outs} scaled={scaled} D={D} DI={DI} N={N} range={e_begin}+{e_count} "
+def _pool_out(B, E, D, kind, tiled):
+    """(cache, scale or None, raw-bytes view) for one stream's output kind."""
+    if kind == "mxfp4":
+        keys = sk.Mxfp4Keys.empty(B, (E + 31) // 32 * 32, D, DEV)
+        keys.tiles.zero_()
+        return keys, None, lambda: keys.tiles
+    dt = {"bf16": torch.bfloat16, "f32": torch.float32, "e4m3": torch.uint8, "e4m3s": torch.uint8}[kind]
+    if tiled:
+        t = sk.key_tiles_empty(B, (E + 31) // 32 * 32, D, dt, DEV).zero_()
+    else:
+        t = torch.zeros(B, E, D, device=DEV, dtype=dt)
+    out = t.view(torch.float8_e4m3fn) if kind.startswith("e4m3") else t
+    sc = torch.zeros(B, E, device=DEV) if kind == "e4m3s" else None
+    return out, sc, lambda: t
+
+
+@pytest.mark.parametrize("ins,out0,out1,D,DI,tiled,N,e_begin,e_count,spread", PAIR_CASES)
+def test_csa_compress_pair_equals_single_streams(ins, out0, out1, D, DI, tiled, N, e_begin, e_count, spread):
+    """csa_compress with both streams runs them in one grid where a pair instance
+    exists for their types; its entries equal those of two single-stream calls
+    bit for bit (so the single stream's parity with the oracle carries over)."""
+    print(f"compress pair {ins} -> {out0} + {out1} D={D} DI={DI} N={N} range={e_begin}+{e_count} "
           f"spread={spread}", flush=True)
     rng = np.random.default_rng(N + D + e_begin)
     B, m, o = 2, 4, 4
@@ -319,34 +339,21 @@ def test_csa_compress_pair_equals_single_streams(ins, outs, scaled, D, DI, tiled
         bp[0, 5], bp[7, 5] = 35.0, -35.0                            # this channel takes the online path
     E = N // m
     n = E - e_begin if e_count is None else e_count
-    tdt = {"bf16": torch.bfloat16, "f32": torch.float32, "e4m3": torch.uint8}[outs]
-
-    def outputs():
-        ent = torch.zeros(B, E, D, device=DEV, dtype=tdt)
-        ent = ent.view(torch.float8_e4m3fn) if outs == "e4m3" else ent
-        if tiled:
-            keys = sk.key_tiles_empty(B, (E + 31) // 32 * 32, DI, tdt, DEV).zero_()
-        else:
-            keys = torch.zeros(B, E, DI, device=DEV, dtype=tdt)
-            keys = keys.view(torch.float8_e4m3fn) if outs == "e4m3" else keys
-        sc = (torch.zeros(B, E, device=DEV), torch.zeros(B, E, device=DEV)) if scaled else (None, None)
-        return ent, keys, sc
-
     vd, gd, vId, gId, bd, bId = dev(v, ins), dev(g, ins), dev(vI, ins), dev(gI, ins), dev(bp), dev(bpI)
-    lay = sk.LAYOUT_KEY_TILES if tiled else sk.LAYOUT_ROWS
-    ea, ka, (sa, saI) = outputs()
-    eb, kb, (sb, sbI) = outputs()
+    lay = sk.LAYOUT_KEY_TILES if tiled or out1 == "mxfp4" else sk.LAYOUT_ROWS
+    (ea, sa, ra), (ka, saI, rka) = _pool_out(B, E, D, out0, False), _pool_out(B, E, DI, out1, tiled)
+    (eb, sb, rb), (kb, sbI, rkb) = _pool_out(B, E, D, out0, False), _pool_out(B, E, DI, out1, tiled)
     args = dict(m=m, o=o, e_begin=e_begin, e_count=n)
     sk.csa_compress(sk.Pool(vd, gd, bd, ea, sa), sk.Pool(vId, gId, bId, ka, saI, layout=lay), **args)
     sk.csa_compress(sk.Pool(vd, gd, bd, eb, sb), **args)
     sk.csa_compress(sk.Pool(vId, gId, bId, kb, sbI, layout=lay), **args)
     torch.cuda.synchronize()
-    raw = (lambda x: x.view(torch.uint8)) if outs == "e4m3" else (lambda x: x)
-    assert torch.equal(raw(ea), raw(eb)), "latent entries of the paired launch differ"
-    assert torch.equal(raw(ka), raw(kb)), "indexer keys of the paired launch differ"
-    if scaled:
-        assert torch.equal(sa, sb) and torch.equal(saI, sbI)
-    assert raw(ea)[:, e_begin:e_begin + n].float().abs().sum() > 0       # the range was written
+    assert torch.equal(ra(), rb()), "latent entries of the paired launch differ"
+    assert torch.equal(rka(), rkb()), "indexer keys of the paired launch differ"
+    for x, y in ((sa, sb), (saI, sbI)):
+        if x is not None:
+            assert torch.equal(x, y)
+    assert ra()[:, e_begin:e_begin + n].float().abs().sum() > 0        # the range was written
 
 
 @pytest.mark.parametrize("D,outs,scaled", [(64, "bf16", False), (512, "e4m3", True)])
