@@ -914,6 +914,41 @@ def test_decode_step_replays_as_hip_graph(keys_s):
             assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("E,k", [(32735, 1024), (20000, 512)])
+def test_topk_select_one_block_threshold_bins(E, k):
+    """Selection from given scores on the one-block path: distinct scores, a group
+    of 40 equal scores straddling rank k (the lowest indices of the group are
+    kept), all-negative scores, all-equal scores, clustered scores (a few
+    first-digit bins hold the whole row), k/2 scores tied at the top, and a short
+    row."""
+    print(f"topk select one block E={E} k={k}", flush=True)
+    rng = np.random.default_rng(E + 3 * k)
+    pos = [4 * E + 127] * 6 + [4 * 600 + 128]
+    R = len(pos)
+    s = rng.normal(0, 3, (R, E)).astype(np.float32)
+    order = np.argsort(-s[1], kind="stable")
+    s[1, order[k - 20:k + 20]] = s[1, order[k]]              # 40 equal scores across rank k
+    s[2] = -np.abs(s[2]) - 1.0                               # all negative
+    s[3] = 1.5                                               # all equal: the bin holds the whole row
+    s[4] = (1000.0 + rng.normal(0, 1e-3, E)).astype(np.float32)   # clustered: a few first-digit bins
+    s[5, order[:k // 2]] = s[5, order[0]]                    # half of k tied at the top score
+    rows = sk.RowSpec.decode(dev_i32(pos), max(pos))
+    out_idx = torch.full((R, k), -7, device=DEV, dtype=torch.int32)
+    out_score = torch.zeros(R, k, device=DEV, dtype=torch.float32)
+    qI = torch.zeros(R, 64, 128, device=DEV, dtype=torch.bfloat16)
+    w = torch.zeros(R, 64, device=DEV)
+    keys = sk.key_tiles_empty(R, (E + 31) // 32 * 32, 128, torch.bfloat16, DEV)
+    sk.csa_topk_select(rows, dev(s), out_idx, keys_meta=(qI, w, keys), m=4, W=128, k=k, out_score=out_score)
+    torch.cuda.synchronize()
+    gi, gs = host(out_idx), host(out_score)
+    for r, t in enumerate(pos):
+        ev = min(method.entries_visible(t, 4, 128), E)
+        ora = method.topk(s[r, :ev], k)
+        np.testing.assert_array_equal(gi[r], ora, err_msg=f"row {r}")
+        sel = gi[r][gi[r] >= 0]
+        np.testing.assert_array_equal(gs[r, :len(sel)], s[r, sel])
+
+
 @pytest.mark.parametrize("E,k,tie", [(40000, 512, 7.0), (70016, 2048, 6.0)])
 def test_topk_select_many_blocks_and_ties(E, k, tie):
     """Selection from given scores on the many-blocks-per-row path (rows longer
