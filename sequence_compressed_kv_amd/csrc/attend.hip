@@ -669,14 +669,20 @@ __global__ __launch_bounds__(512) void attend_dma512(AttendParams p) {
 
 // Merge of split partials (maxima m_s in base-2 logit units):
 // o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
-// One block per (head, row, latent slice of `dslice` dims).  The splits' (m_s, l_s)
-// are read once, one thread per split, and reduced across the block; the weights
-// 2^(m_s - M) wait in LDS.  Each thread accumulates four consecutive dims over a
-// run of splits in split order, eight splits' loads in flight.  With SG = 1 one
-// thread takes all the splits (many rows: the grid alone fills the chip); with
-// SG > 1 (a few rows with many splits) SG thread groups take consecutive runs of
-// splits and their sums are added in run order through LDS.  The plan keeps the
-// number of splits at or below kMaxSplits.
+// One block per (head, row, latent slice of `dslice` dims); each thread takes
+// four consecutive dims.
+// - SG = 1 (many rows: the grid alone fills the chip): one thread per split
+//   reads (m_s, l_s) and the block reduces them; the weights 2^(m_s - M) wait in
+//   LDS, then each thread sums all the splits in split order, eight splits'
+//   loads in flight.
+// - SG > 1 (a few rows with many splits, about one block per CU): SG thread
+//   groups take consecutive runs of at most kMaxSplits / SG splits, and their
+//   sums are added in run order through LDS.  Nothing waits on the reductions
+//   but the weighting, so every load is issued first: a thread's partials and,
+//   one or two splits per thread, (m_s, l_s) as one 8-byte load.  The merge then
+//   costs one memory round trip instead of one per reduction and per batch of
+//   splits.
+// The plan keeps the number of splits at or below kMaxSplits.
 template <int SG>
 __global__ __launch_bounds__(256) void attend_combine(const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
                                                       void* __restrict__ out, float* __restrict__ lse, int H, int D,
@@ -688,64 +694,122 @@ __global__ __launch_bounds__(256) void attend_combine(const float* __restrict__ 
   const int nt = blockDim.x, nw = (nt + kWave - 1) / kWave;
   const int l = lane_id(), w = wave_id();
   const float* ml = ws_ml + ((int64_t)r * nsplit * H + h) * 2;           // split s at + s * 2 H
-  float mloc = -INFINITY;
-  for (int s = threadIdx.x; s < nsplit; s += nt) {
-    wgt[s] = ml[(int64_t)s * 2 * H];
-    mloc = fmaxf(mloc, wgt[s]);
-  }
-  for (int o = 32; o >= 1; o >>= 1) mloc = fmaxf(mloc, shfl_xor_f(mloc, o));
-  if (l == 0) red[0][w] = mloc;
-  __syncthreads();
-  float M = red[0][0];
-  for (int i = 1; i < nw; ++i) M = fmaxf(M, red[0][i]);
-  float lloc = 0.f;
-  for (int s = threadIdx.x; s < nsplit; s += nt) {
-    const float ms = wgt[s];
-    const float e = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-    lloc += e * ml[(int64_t)s * 2 * H + 1];
-    wgt[s] = e;
-  }
-  for (int o = 32; o >= 1; o >>= 1) lloc += shfl_xor_f(lloc, o);
-  if (l == 0) red[1][w] = lloc;
-  __syncthreads();
-  float L = red[1][0];
-  for (int i = 1; i < nw; ++i) L += red[1][i];
-  const float inv = 1.f / L;
-  const int td_n = nt / SG, td = threadIdx.x % td_n, sg = threadIdx.x / td_n;
-  const int per = (nsplit + SG - 1) / SG;
-  const int s_begin = sg * per, s_end = s_begin + per < nsplit ? s_begin + per : nsplit;
-  const int d_first = blockIdx.z * dslice;
-  // SG > 1: td_n == dslice / 4, so every thread makes exactly one pass (the barrier below)
-  for (int d4 = td; d4 < dslice / 4; d4 += td_n) {
-    const int dd = d_first + 4 * d4;
-    const float* src = ws_o + ((int64_t)r * nsplit * H + h) * D + dd;      // split s at + s H D
+  if constexpr (SG > 1) {
+    // dslice / 4 threads per group (dslice >= 64, so nt >= 2 * kWave and
+    // nsplit <= 2 nt); one pass over the slice
+    constexpr int MAXP = kMaxSplits / SG;
+    const int td_n = nt / SG, td = threadIdx.x % td_n, sg = threadIdx.x / td_n;
+    const int per = (nsplit + SG - 1) / SG;
+    const int s_begin = sg * per;
+    const int n = nsplit - s_begin < per ? nsplit - s_begin : per;         // may be <= 0 for the last groups
+    const int dd = blockIdx.z * dslice + 4 * td;
+    const float* src = ws_o + (((int64_t)r * nsplit + s_begin) * H + h) * D + dd;
+    f32x4 v[MAXP];
+#pragma unroll
+    for (int u = 0; u < MAXP; ++u)
+      if (u < n) v[u] = *reinterpret_cast<const f32x4*>(src + (int64_t)u * H * D);
+    u32x2 mlv[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int s = threadIdx.x + i * nt;
+      mlv[i] = s < nsplit ? *reinterpret_cast<const u32x2*>(ml + (int64_t)s * 2 * H)
+                          : u32x2{__float_as_uint(-INFINITY), 0u};
+    }
+    float mloc = fmaxf(__uint_as_float(mlv[0][0]), __uint_as_float(mlv[1][0]));
+    for (int o = 32; o >= 1; o >>= 1) mloc = fmaxf(mloc, shfl_xor_f(mloc, o));
+    if (l == 0) red[0][w] = mloc;
+    __syncthreads();
+    float M = red[0][0];
+    for (int i = 1; i < nw; ++i) M = fmaxf(M, red[0][i]);
+    float lloc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int s = threadIdx.x + i * nt;
+      if (s < nsplit) {
+        const float ms = __uint_as_float(mlv[i][0]);
+        const float e = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+        lloc += e * __uint_as_float(mlv[i][1]);
+        wgt[s] = e;
+      }
+    }
+    for (int o = 32; o >= 1; o >>= 1) lloc += shfl_xor_f(lloc, o);
+    if (l == 0) red[1][w] = lloc;
+    __syncthreads();
+    float L = red[1][0];
+    for (int i = 1; i < nw; ++i) L += red[1][i];
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    int s = s_begin;
-    for (; s + 8 <= s_end; s += 8) {
-      f32x4 v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const f32x4*>(src + (int64_t)(s + u) * H * D);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) acc += wgt[s + u] * v[u];
-    }
-    for (; s < s_end; ++s) acc += wgt[s] * *reinterpret_cast<const f32x4*>(src + (int64_t)s * H * D);
-    if (SG > 1) {
-      part[sg][td] = acc;
-      __syncthreads();
-      if (sg != 0) break;
+    for (int u = 0; u < MAXP; ++u)
+      if (u < n) acc += wgt[s_begin + u] * v[u];
+    part[sg][td] = acc;
+    __syncthreads();
+    if (sg == 0) {
       for (int g = 1; g < SG; ++g) acc += part[g][td];
+      const float inv = 1.f / L;
+      const int64_t off = ((int64_t)r * H + h) * D + dd;
+      if (out_dtype == SCKV_BF16) {
+        uint16_t* o = static_cast<uint16_t*>(out) + off;
+        const uint32_t lo = f32_to_bf16_rne(acc[0] * inv) | (f32_to_bf16_rne(acc[1] * inv) << 16);
+        const uint32_t hi = f32_to_bf16_rne(acc[2] * inv) | (f32_to_bf16_rne(acc[3] * inv) << 16);
+        *reinterpret_cast<u32x2*>(o) = u32x2{lo, hi};
+      } else {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(out) + off) = acc * inv;
+      }
     }
-    const int64_t off = ((int64_t)r * H + h) * D + dd;
-    if (out_dtype == SCKV_BF16) {
-      uint16_t* o = static_cast<uint16_t*>(out) + off;
-      const uint32_t lo = f32_to_bf16_rne(acc[0] * inv) | (f32_to_bf16_rne(acc[1] * inv) << 16);
-      const uint32_t hi = f32_to_bf16_rne(acc[2] * inv) | (f32_to_bf16_rne(acc[3] * inv) << 16);
-      *reinterpret_cast<u32x2*>(o) = u32x2{lo, hi};
-    } else {
-      *reinterpret_cast<f32x4*>(static_cast<float*>(out) + off) = acc * inv;
+    if (lse && threadIdx.x == 0 && blockIdx.z == 0) lse[(int64_t)r * H + h] = (M + log2f(L)) * 0.6931471805599453f;
+  } else {
+    float mloc = -INFINITY;
+    for (int s = threadIdx.x; s < nsplit; s += nt) {
+      wgt[s] = ml[(int64_t)s * 2 * H];
+      mloc = fmaxf(mloc, wgt[s]);
     }
+    for (int o = 32; o >= 1; o >>= 1) mloc = fmaxf(mloc, shfl_xor_f(mloc, o));
+    if (l == 0) red[0][w] = mloc;
+    __syncthreads();
+    float M = red[0][0];
+    for (int i = 1; i < nw; ++i) M = fmaxf(M, red[0][i]);
+    float lloc = 0.f;
+    for (int s = threadIdx.x; s < nsplit; s += nt) {
+      const float ms = wgt[s];
+      const float e = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+      lloc += e * ml[(int64_t)s * 2 * H + 1];
+      wgt[s] = e;
+    }
+    for (int o = 32; o >= 1; o >>= 1) lloc += shfl_xor_f(lloc, o);
+    if (l == 0) red[1][w] = lloc;
+    __syncthreads();
+    float L = red[1][0];
+    for (int i = 1; i < nw; ++i) L += red[1][i];
+    const float inv = 1.f / L;
+    const int td_n = nt / SG, td = threadIdx.x % td_n, sg = threadIdx.x / td_n;
+    const int per = (nsplit + SG - 1) / SG;
+    const int s_begin = sg * per, s_end = s_begin + per < nsplit ? s_begin + per : nsplit;
+    const int d_first = blockIdx.z * dslice;
+    for (int d4 = td; d4 < dslice / 4; d4 += td_n) {
+      const int dd = d_first + 4 * d4;
+      const float* src = ws_o + ((int64_t)r * nsplit * H + h) * D + dd;      // split s at + s H D
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      int s = s_begin;
+      for (; s + 8 <= s_end; s += 8) {
+        f32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const f32x4*>(src + (int64_t)(s + u) * H * D);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += wgt[s + u] * v[u];
+      }
+      for (; s < s_end; ++s) acc += wgt[s] * *reinterpret_cast<const f32x4*>(src + (int64_t)s * H * D);
+      const int64_t off = ((int64_t)r * H + h) * D + dd;
+      if (out_dtype == SCKV_BF16) {
+        uint16_t* o = static_cast<uint16_t*>(out) + off;
+        const uint32_t lo = f32_to_bf16_rne(acc[0] * inv) | (f32_to_bf16_rne(acc[1] * inv) << 16);
+        const uint32_t hi = f32_to_bf16_rne(acc[2] * inv) | (f32_to_bf16_rne(acc[3] * inv) << 16);
+        *reinterpret_cast<u32x2*>(o) = u32x2{lo, hi};
+      } else {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(out) + off) = acc * inv;
+      }
+    }
+    if (lse && threadIdx.x == 0 && blockIdx.z == 0) lse[(int64_t)r * H + h] = (M + log2f(L)) * 0.6931471805599453f;
   }
-  if (lse && threadIdx.x == 0 && blockIdx.z == 0) lse[(int64_t)r * H + h] = (M + log2f(L)) * 0.6931471805599453f;
 }
 
 // fp32 path: one block per row, items 64 at a time through LDS.

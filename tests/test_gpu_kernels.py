@@ -660,6 +660,7 @@ ATTEND_CASES = [
     (True, "bf16", 16, 256, 1000, [4127, 2000], 200, "bf16"),
     (True, "bf16", 48, 128, 2048, [8319, 5000, 129], 300, "f32"),      # three 16-head tiles
     (False, "e4m3", 112, 64, 1024, [131071, 70000], 0, "f32"),         # seven 16-head tiles
+    (False, "bf16", 16, 64, 16384, [16384 * 128 + 255], 0, "f32"),     # 129 splits: merge threads take 2 (m, l)
 ]
 
 
