@@ -343,13 +343,13 @@ constexpr int kMbMaxBlocks = 1024;                                  // blocks pe
 // Elements [base, base + NT*V) of a row (len of them exist) in element order
 // (wave, group, lane, element): wave w owns elements w*64*V .. ; its group i is one
 // coalesced 1 KB load, lane l taking elements (i*64 + l)*4 .. +3.
-template <int NT, int V>
-__device__ __forceinline__ void load_row_part(const float* src, int64_t len, int64_t base, uint32_t (&key)[V],
-                                              int32_t (&idx)[V], bool (&valid)[V]) {
-  const int w = wave_id(), l = lane_id();
-  const int64_t wbase = (int64_t)w * 64 * V;
-  float sc[V];
-  load_part<V>(src, len, wbase, sc);
+// Order-preserving keys, element indices and validity of a part loaded by
+// load_part (wave w's elements w*64*V + (i*64 + l)*4 + j of a row part of len).
+template <int V>
+__device__ __forceinline__ void part_keys(const float (&sc)[V], int64_t len, int64_t base, uint32_t (&key)[V],
+                                          int32_t (&idx)[V], bool (&valid)[V]) {
+  const int64_t wbase = (int64_t)wave_id() * 64 * V;
+  const int l = lane_id();
 #pragma unroll
   for (int v = 0; v < V; ++v) {
     const int64_t e = wbase + ((int64_t)(v / 4) * 64 + l) * 4 + (v % 4);
@@ -358,6 +358,14 @@ __device__ __forceinline__ void load_row_part(const float* src, int64_t len, int
     key[v] = ok ? score_key(sc[v]) : 0u;
     idx[v] = (int32_t)(base + e);
   }
+}
+
+template <int NT, int V>
+__device__ __forceinline__ void load_row_part(const float* src, int64_t len, int64_t base, uint32_t (&key)[V],
+                                              int32_t (&idx)[V], bool (&valid)[V]) {
+  float sc[V];
+  load_part<V>(src, len, (int64_t)wave_id() * 64 * V, sc);
+  part_keys<V>(sc, len, base, key, idx, valid);
 }
 
 __global__ __launch_bounds__(256) void topk_zero_hist(uint32_t* __restrict__ hist, int64_t n) {
@@ -373,12 +381,15 @@ __global__ __launch_bounds__(kMbNT) void topk_hist(const float* __restrict__ sco
   int64_t len = row_visible(rows, r) - base;
   if (len <= 0) return;
   len = len > kMbS ? kMbS : len;
+  // the scores are in flight while the LDS histogram is cleared
+  float sc[kMbV];
+  load_part<kMbV>(scores + (int64_t)r * stride + base, len, (int64_t)wave_id() * 64 * kMbV, sc);
   for (int i = threadIdx.x; i < kBins; i += kMbNT) h[i] = 0u;
   __syncthreads();
   uint32_t key[kMbV];
   int32_t idx[kMbV];
   bool valid[kMbV];
-  load_row_part<kMbNT, kMbV>(scores + (int64_t)r * stride + base, len, base, key, idx, valid);
+  part_keys<kMbV>(sc, len, base, key, idx, valid);
 #pragma unroll
   for (int v = 0; v < kMbV; ++v)
     if (valid[v]) atomicAdd(&h[key[v] >> 20], 1u);
@@ -508,24 +519,21 @@ __device__ __forceinline__ void topk_row_final(const float* scores, int64_t stri
                                             int nb, const int32_t* cnt, const uint32_t* rkey, const int32_t* ridx,
                                             uint32_t b, uint32_t above, uint32_t n_valid, int32_t* out_idx,
                                             float* out_score, uint32_t* hist, uint32_t* scan_sh, uint32_t* ctl,
-                                            int32_t* pre, int32_t* flag, uint32_t* skey, int32_t* sidx) {
+                                            int32_t* pre, int32_t* flag, uint32_t* skey, int32_t* sidx,
+                                            int32_t my) {
+  static_assert(kMbMaxBlocks <= kFinNT, "one filter block's survivor count per thread");
   const int w = wave_id(), l = lane_id();
   int32_t* oi = out_idx + (int64_t)r * k;
   float* os = out_score ? out_score + (int64_t)r * k : nullptr;
   const uint32_t kk = n_valid < (uint32_t)k ? n_valid : (uint32_t)k;
-  // survivors per block -> exclusive prefix in block order (nb <= kMbMaxBlocks)
+  // survivors per filter block (my: block threadIdx.x's count, loaded by the
+  // caller) -> exclusive prefix in block order
   if (threadIdx.x == 0) *flag = 0;
   __syncthreads();
-  uint32_t run = 0;
-  for (int j0 = 0; j0 < nb; j0 += kFinNT) {
-    const int j = j0 + threadIdx.x;
-    const int32_t my = j < nb ? cnt[(int64_t)r * nb + j] : 0;
-    if (my < 0) *flag = 1;
-    uint32_t t;
-    const uint32_t ex = block_excl_scan<kFinNT>(my < 0 ? 0u : (uint32_t)my, scan_sh, &t);
-    if (j < nb) pre[j] = (int32_t)(run + ex);
-    run += t;
-  }
+  if (my < 0) *flag = 1;
+  uint32_t run;
+  const uint32_t ex = block_excl_scan<kFinNT>(my < 0 ? 0u : (uint32_t)my, scan_sh, &run);
+  if (threadIdx.x < nb) pre[threadIdx.x] = (int32_t)ex;
   if (threadIdx.x == 0) pre[nb] = (int32_t)run;
   __syncthreads();
   if (*flag) {
@@ -539,13 +547,36 @@ __device__ __forceinline__ void topk_row_final(const float* scores, int64_t stri
   }
   const int tot = pre[nb];
   // the survivors, region by region into LDS in concatenation (ascending index)
-  // order: wave w copies regions w, w + 16, ..., each with coalesced reads
-  for (int j = w; j < nb; j += kFinNT / kWave) {
-    const int c0 = pre[j], c = pre[j + 1] - c0;
-    const int64_t base = ((int64_t)r * nb + j) * kMbS;
-    for (int o = l; o < c; o += kWave) {
-      skey[c0 + o] = rkey[base + o];
-      sidx[c0 + o] = ridx[base + o];
+  // order: wave w copies regions w, w + 16, ..., each with coalesced reads.  The
+  // first 64 survivors of four regions are loaded before any is stored (one
+  // memory round trip for the usual region sizes); longer regions finish in a loop
+  constexpr int NWF = kFinNT / kWave, RB = 4;
+  for (int j0 = w; j0 < nb; j0 += RB * NWF) {
+    int c0[RB], c[RB];
+    uint32_t kv[RB];
+    int32_t iv[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      const int j = j0 + i * NWF;
+      c0[i] = j < nb ? pre[j] : 0;
+      c[i] = j < nb ? pre[j + 1] - c0[i] : 0;
+      const int64_t base = ((int64_t)r * nb + j) * kMbS;
+      if (l < c[i]) {
+        kv[i] = rkey[base + l];
+        iv[i] = ridx[base + l];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      if (l < c[i]) {
+        skey[c0[i] + l] = kv[i];
+        sidx[c0[i] + l] = iv[i];
+      }
+      const int64_t base = ((int64_t)r * nb + j0 + i * NWF) * kMbS;
+      for (int o = kWave + l; o < c[i]; o += kWave) {
+        skey[c0[i] + o] = rkey[base + o];
+        sidx[c0[i] + o] = ridx[base + o];
+      }
     }
   }
   __syncthreads();
@@ -588,6 +619,10 @@ __global__ __launch_bounds__(kMbNT) void topk_filter(const float* __restrict__ s
   const int64_t slot = (int64_t)r * nb + blockIdx.x;
   int64_t len = row_visible(rows, r) - base;
   len = len < 0 ? 0 : (len > kMbS ? kMbS : len);
+  // the block's scores do not depend on the threshold bin: their loads and the
+  // histogram's are in flight together
+  float sc[kMbV];
+  if (len > 0) load_part<kMbV>(scores + (int64_t)r * stride + base, len, (int64_t)wave_id() * 64 * kMbV, sc);
   row_threshold_bin<kMbNT>(ghist + (int64_t)r * kBins, k, scan_sh, ctl);
   const uint32_t b = ctl[0], above = ctl[1];
   if (len == 0) {
@@ -598,7 +633,7 @@ __global__ __launch_bounds__(kMbNT) void topk_filter(const float* __restrict__ s
     uint32_t key[kMbV];
     int32_t idx[kMbV];
     bool valid[kMbV];
-    load_row_part<kMbNT, kMbV>(scores + (int64_t)r * stride + base, len, base, key, idx, valid);
+    part_keys<kMbV>(sc, len, base, key, idx, valid);
     bool keep[kMbV];
     uint32_t c[NI], off[NI], tot;
 #pragma unroll
@@ -644,10 +679,12 @@ __global__ __launch_bounds__(kFinNT) void topk_final(const float* __restrict__ s
   __shared__ __attribute__((aligned(16))) uint32_t skey[kFinCap];
   __shared__ __attribute__((aligned(16))) int32_t sidx[kFinCap];
   const int r = blockIdx.y;
+  // the filter blocks' survivor counts, in flight with the histogram's loads
+  const int32_t my = (int)threadIdx.x < nb ? cnt[(int64_t)r * nb + threadIdx.x] : 0;
   row_threshold_bin<kFinNT>(ghist + (int64_t)r * kBins, k, scan_sh, ctl);
   const uint32_t b = ctl[0], above = ctl[1], n_valid = ctl[3];
   topk_row_final(scores, stride, rows, r, k, nb, cnt, rkey, ridx, b, above, n_valid, out_idx, out_score, hist,
-                 scan_sh, ctl, pre, &flag, skey, sidx);
+                 scan_sh, ctl, pre, &flag, skey, sidx, my);
 }
 
 static const int kCfg[][2] = {{256, 4}, {256, 16}, {256, 32}, {1024, 16}, {1024, 32}, {1024, 64}};
