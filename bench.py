@@ -975,8 +975,9 @@ def hbm_read_reference(torch, dev, gib: int = 2, iters: int = 10):
     """Plain streaming references on the same GPU, timed with HIP events: the
     hand-written streaming read (libsckv_bench.so: every byte of `gib` GiB read once
     with 16-byte loads, 2048 blocks of 256 threads), torch's sum over the same bf16
-    tensor and a device copy of it (each byte read once and written once).  `GBps`
-    is the hand-written read's rate."""
+    tensor and a device copy of it (each byte read once and written once), and the
+    hand-written row gathers (`row_gather_1KB`: random 1 KB rows of the buffer).
+    `GBps` is the streaming read's rate."""
     import ctypes as C
     x = torch.ones(gib * (1 << 30) // 2, dtype=torch.bfloat16, device=dev)
     y = torch.empty_like(x)
@@ -1006,8 +1007,30 @@ def hbm_read_reference(torch, dev, gib: int = 2, iters: int = 10):
     kread = rate(kernel_read, nb)
     read = rate(lambda: x.sum(), nb)
     copy = rate(lambda: y.copy_(x), 2 * nb)
+
+    # random 1 KB rows of the same buffer, gathered 32 to a chunk by blocks of 8
+    # waves as decode attention gathers its items: through the asynchronous
+    # global -> LDS copies (three chunks in flight) and with loads into registers
+    # (one chunk in flight); the shapes of one 128K-context attention launch
+    # (192 blocks x 6 chunks) and of a long gather (256 blocks x 45 chunks)
+    blib.sckv_bench_gather_rows.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_void_p,
+                                            C.c_void_p]
+    blib.sckv_bench_gather_rows.restype = C.c_int
+    nrows = nb // 1024
+    g = torch.Generator(device=dev).manual_seed(11)
+    gather = {}
+    for blocks, nch in ((192, 6), (256, 45)):
+        rows = torch.randint(0, nrows, (blocks * nch * 32,), device=dev, generator=g, dtype=torch.int32)
+        for mode, name in ((1, "lds_copy"), (0, "registers")):
+            def run(mode=mode, rows=rows, blocks=blocks, nch=nch):
+                e = blib.sckv_bench_gather_rows(x.data_ptr(), rows.data_ptr(), blocks, nch, mode, sink.data_ptr(),
+                                                stream.cuda_stream)
+                if e != 0:
+                    raise RuntimeError(f"row-gather reference failed: hipError {e}")
+            gather[f"{name}_{blocks}x{nch}_GBps"] = rate(run, blocks * nch * 32 * 1024)
     del x, y
-    return {"stream_read_kernel_GBps": kread, "sum_read_GBps": read, "copy_GBps": copy, "bytes": nb, "GBps": kread}
+    return {"stream_read_kernel_GBps": kread, "sum_read_GBps": read, "copy_GBps": copy, "bytes": nb, "GBps": kread,
+            "row_gather_1KB": gather}
 
 
 def host_cpu():

@@ -60,3 +60,26 @@ def test_counter_summary_on_other_sources_reports_no_traffic(tmp_path, monkeypat
     c = bench.kernel_counters("s.txt")
     assert c["topk_kernel"]["stale"] and c["topk_kernel"]["traffic_B"] is None
     assert bench.kernel_counters("missing.txt") == {}
+
+
+def test_read_reference_library_rejects_bad_arguments():
+    """The benchmark's read references (libsckv_bench.so) export the streaming read
+    and the row gather, and refuse null pointers and empty shapes before any HIP
+    call (hipErrorInvalidValue = 1), so this runs without a GPU."""
+    import ctypes as C
+    lib_path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                            "sequence_compressed_kv_amd", "libsckv_bench.so")
+    if not os.path.exists(lib_path):
+        import pytest
+        pytest.skip("libsckv_bench.so not built")
+    lib = C.CDLL(lib_path)
+    lib.sckv_bench_stream_read.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int, C.c_void_p]
+    lib.sckv_bench_gather_rows.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_void_p,
+                                           C.c_void_p]
+    fake = C.c_void_p(16)                      # never dereferenced: the checks fail first
+    assert lib.sckv_bench_stream_read(None, 1024, fake, 1, None) == 1
+    assert lib.sckv_bench_stream_read(fake, 1000, fake, 1, None) == 1    # not a multiple of 16
+    assert lib.sckv_bench_gather_rows(None, fake, 1, 1, 1, fake, None) == 1
+    assert lib.sckv_bench_gather_rows(fake, None, 1, 1, 0, fake, None) == 1
+    assert lib.sckv_bench_gather_rows(fake, fake, 0, 1, 1, fake, None) == 1
+    assert lib.sckv_bench_gather_rows(fake, fake, 1, 0, 0, fake, None) == 1
