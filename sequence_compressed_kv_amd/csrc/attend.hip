@@ -403,18 +403,17 @@ __device__ __forceinline__ int chunk_swizzle(int r) {
 
 // bf16 entries and window with D = 512 (the MLA-style latent), 64 heads: items
 // travel global -> LDS by asynchronous copies (one 1 KB row per wavefront
-// instruction) into four 32-item stages, so three chunks are in flight while a
-// fourth is multiplied, without staging registers.  Waits are explicit: before
-// a chunk is used each wave waits until only the later chunks' copies are
-// outstanding, then one barrier publishes the chunk and frees the stage of the
-// chunk before it for the next copy.
+// instruction) into four 32-item stages, without staging registers.  Waits are
+// explicit: before a chunk is used each wave waits until only the next chunk's
+// copies are outstanding, then one barrier per chunk publishes it.
 //
-// Eight waves: wave w takes the 16 heads 16 (w % 4) .. and the latent half
-// h = w / 4 (dims 256 h .. 256 h + 255).  Q.K^T is split the same way: each
-// wave multiplies its half of the dims, the two halves of a head group meet
-// through LDS (both waves add the same two partial sums, so they hold the same
-// logits and take the same softmax), and each wave accumulates P.V for its own
-// half of the output.  Two waves per SIMD then hide each other's latencies.
+// Eight waves in two roles, one of each on every SIMD: wave w < 4 ("score
+// wave") takes the 16 heads 16 w .. over all 512 dims for Q.K^T and the online
+// softmax, and hands P (as two bf16 parts) and the rescale factors to wave w + 4
+// ("output wave") through LDS; the output wave accumulates P.V for the same 16
+// heads over all 512 dims.  Chunk i's scores and chunk i - 1's products run
+// between the same two barriers, so on every SIMD one wave's LDS reads and
+// softmax overlap the other's MFMAs, and no logits cross waves.
 //
 // Both products read the same staged rows.  Q.K^T takes row fragments (one item,
 // eight dims per lane).  P.V needs the transpose (one dim, eight items per lane):
@@ -422,12 +421,13 @@ __device__ __forceinline__ int chunk_swizzle(int r) {
 // group, lane 4r + c receives element c of the 8-byte words addressed by lanes
 // r, r + 4, r + 8 and r + 12 of the group.  So lane a of group g points at item
 // 4g + a/4, dims 4(a%4) .. +3, and lane n of the group comes back holding dim n
-// of items 4g .. 4g + 3, the k-group layout of the P operand.  That product
+// of items 4g .. 4g + 3, the k-group layout of the P operand, which is also the
+// layout in which a score wave's lane holds its probabilities.  That product
 // runs in bf16, so P enters as the sum of two bf16 parts (a second MFMA per dim
 // tile): a single bf16 P would cost up to 2^-9 of max |v| in the output.  The
 // normaliser (and the log-sum-exp) sums the unrounded fp32 probabilities.
 __global__ __launch_bounds__(512) void attend_dma512(AttendParams p) {
-  constexpr int NW = 8, D = 512, DH = D / 2, CH = 32, KSQ = DH / 32, ND = DH / 16;
+  constexpr int NW = 8, D = 512, CH = 32, KSQ = D / 32, ND = D / 16;
   constexpr int KRS = D;                     // LDS row (bf16 elements), 16-byte chunks swizzled per row
   constexpr int NT = NW * kWave;
   constexpr int RPW = CH / NW;               // rows copied per wave per chunk
@@ -435,7 +435,10 @@ __global__ __launch_bounds__(512) void attend_dma512(AttendParams p) {
   constexpr int STG = CH * KRS;              // stage size (bf16 elements)
   __shared__ __attribute__((aligned(16))) uint16_t stg[NSTG * STG];
   __shared__ int32_t srcs[kSegItems];
-  __shared__ f32x4 xs[NW][2][kWave];         // partial logits of each wave, exchanged per chunk
+  __shared__ u32x4 pb[2][4][2][kWave];       // P (hi, lo) of each score wave, two chunks
+  __shared__ __attribute__((aligned(16))) float al[2][4][16];   // rescale factor per head, two chunks
+  __shared__ int32_t resc[2][4];             // whether a chunk's factors differ from 1
+  __shared__ float xml[4][2][16];            // (m, l) per head at the end
 
   // one-dimensional grid; with rows in multiples of 8 the splits of a row share
   // an XCD (blocks are dealt to the 8 XCDs in turn), so its query and index
@@ -454,7 +457,8 @@ __global__ __launch_bounds__(512) void attend_dma512(AttendParams p) {
   }
   const RowItems ri = row_items(p, r);
   const int l = lane_id(), w = wave_id();
-  const int hg = w & 3, dh = w >> 2;         // head group, latent half
+  const bool scorer = w < 4;                 // wave-uniform role
+  const int hg = w & 3;                      // head group of both roles
   const int col = l & 15, g = l >> 4;
   const int head = 16 * hg + col;
 
@@ -463,19 +467,20 @@ __global__ __launch_bounds__(512) void attend_dma512(AttendParams p) {
   q_end = q_end < ri.n_items ? q_end : ri.n_items;
 
   const gbytes gent = opaque_global(p.entries), gwin = opaque_global(p.win);
-  // query fragments of this wave's latent half: loads issued here, waited for
-  // after the first source table
-  bf16x8 bq[KSQ];
-  {
-    const gbytes gq = opaque_global(p.q);
-    const int64_t e0 = ((int64_t)r * p.H + head) * D + DH * dh + g * (DH / 4);
-#pragma unroll
-    for (int ks = 0; ks < KSQ; ++ks) bq[ks] = bitcast<bf16x8>(gload<u32x4>(gq, (e0 + 8 * ks) * 2));
-  }
+  // One register array serves both roles: an output wave's sums of its 16 heads
+  // x 512 dims, a score wave's query fragments in its first KSQ entries (lane
+  // group g holds dims 128 g + 8 ks .. +7 of k-step ks; loads issued here,
+  // waited for after the first source table).
   f32x4 o[ND];
 #pragma unroll
   for (int nd = 0; nd < ND; ++nd) o[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  if (scorer) {
+    const gbytes gq = opaque_global(p.q);
+    const int64_t e0 = ((int64_t)r * p.H + head) * D + g * (D / 4);
+#pragma unroll
+    for (int ks = 0; ks < KSQ; ++ks) o[ks] = bitcast<f32x4>(gload<u32x4>(gq, (e0 + 8 * ks) * 2));
+  }
+  float m_run = -INFINITY, l_run = 0.f;      // score waves
   const float scale2 = p.scale * 1.4426950408889634f;
 
   const int wu = __builtin_amdgcn_readfirstlane(w);
@@ -488,16 +493,16 @@ __global__ __launch_bounds__(512) void attend_dma512(AttendParams p) {
   const int32_t t_slot = (int32_t)(ri.t % p.R_w);
 
   // Staged rows keep their 16-byte chunks permuted: logical chunk c of row r
-  // sits at chunk c ^ chunk_swizzle(r).  Eight consecutive rows then start in
-  // eight different bank groups (the Q.K^T reads, one chunk of 16 rows per
+  // sits at chunk c ^ chunk_swizzle(r).  Sixteen consecutive rows then start in
+  // sixteen different bank groups (the Q.K^T reads, one chunk of 16 rows per
   // instruction) and the four or eight rows of a transposing read group take
   // disjoint 32-byte bank spans (P.V, two chunks per row), with 32 or 64 banks.
   // Per-lane LDS byte offsets within a stage:
   const int fq = chunk_swizzle(col);                                        // Q.K^T: row col (+16)
-  const int qk_row = col * KRS * 2 + (32 * dh + 16 * (g >> 1) + (8 * (g & 1) ^ (fq & 8))) * 16;
+  const int qk_row = col * KRS * 2 + 16 * g * 16;
   const int pv_r = 4 * g + (col >> 2);                                      // P.V: item 4g + col/4 (+16)
   const int fv = chunk_swizzle(pv_r);
-  const int pv_row = pv_r * KRS * 2 + 32 * dh * 16 + 8 * (col & 1);
+  const int pv_row = pv_r * KRS * 2 + 8 * (col & 1);
   const int pv_h = (col >> 1) & 1;                                          // second chunk of the 32-byte span
   const lds_ptr lds0 = (lds_ptr)stg;
 
@@ -523,146 +528,169 @@ __global__ __launch_bounds__(512) void attend_dma512(AttendParams p) {
     __syncthreads();
     if (!q_ready) {
 #pragma unroll
-      for (int ks = 0; ks < KSQ; ++ks) pin(bq[ks]);
+      for (int ks = 0; ks < KSQ; ++ks) pin(o[ks]);
       q_ready = true;
     }
-    for (int c = 0; c < NSTG - 1 && c < nch; ++c) issue((int64_t)c * CH, c);
+    for (int c = 0; c < 2 && c < nch; ++c) issue((int64_t)c * CH, c);
 
-    for (int c = 0; c < nch; ++c) {
-      const int st = c & (NSTG - 1);
-      // validity of the chunk's 32 items: bit i set when item i has a source
-      const int32_t my_item = srcs[(int64_t)c * CH + (l & 31)];
+    // pass i: the score waves take chunk i, the output waves chunk i - 1
+    for (int i = 0; i <= nch; ++i) {
+      // validity of chunk i's 32 items: bit j set when item j has a source
+      const int32_t my_item = srcs[(int64_t)(i < nch ? i : 0) * CH + (l & 31)];
       const uint64_t valid = __ballot(l < 32 && my_item != -1);
-      if (c + 2 < nch) wait_vm_lgkm<2 * RPW, 0>();
-      else if (c + 1 < nch) wait_vm_lgkm<RPW, 0>();
+      if (i + 1 < nch) wait_vm_lgkm<RPW, 0>();
       else wait_vm_lgkm<0, 0>();
-      block_barrier();                                   // chunk c visible; stage of c-1 free
-      if (c + NSTG - 1 < nch) issue((int64_t)(c + NSTG - 1) * CH, (c + NSTG - 1) & (NSTG - 1));
-
-      // S^T = K Q^T over this wave's latent half, in four independent
-      // accumulators (2 item tiles x even/odd k-steps); fragments read in
-      // batches of 4 k-steps, one batch ahead
-      const uint8_t* sb = reinterpret_cast<const uint8_t*>(&stg[st * STG]) + qk_row;
-      f32x4 sacc[2][2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sacc[i >> 1][i & 1] = f32x4{0.f, 0.f, 0.f, 0.f};
-      constexpr int KB = 4, NB = KSQ / KB;
-      bf16x8 fa[2][2 * KB];
-      auto read_batch = [&](int b, bf16x8 (&f)[2 * KB]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int j = 0; j < KB; ++j)
-            f[mt * KB + j] = bitcast<bf16x8>(
-                *reinterpret_cast<const u32x4*>(sb + mt * 16 * KRS * 2 + (((KB * b + j) ^ (fq & 7)) << 4)));
-      };
-      read_batch(0, fa[0]);
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-#pragma unroll
-        for (int j = 0; j < 2 * KB; ++j) pin(fa[b & 1][j]);
-        if (b + 1 < NB) read_batch(b + 1, fa[(b + 1) & 1]);
-#pragma unroll
-        for (int j = 0; j < KB; ++j)
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
-            sacc[mt][j & 1] = mfma16_bf16(fa[b & 1][mt * KB + j], bq[KB * b + j], sacc[mt][j & 1]);
-      }
-      // the two halves of the head group meet: each wave adds its own and its
-      // partner's partial sums (the same two values, so the same logits)
-      f32x4 part[2];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) part[mt] = sacc[mt][0] + sacc[mt][1];
-      xs[w][0][l] = part[0];
-      xs[w][1][l] = part[1];
+      // chunk i visible, chunk i - 1's P visible; chunk i - 2's stage free
       block_barrier();
-      const f32x4 other0 = xs[w ^ 4][0][l], other1 = xs[w ^ 4][1][l];
-      float x[8];
+      if (i + 2 < nch) issue((int64_t)(i + 2) * CH, (i + 2) & (NSTG - 1));
+
+      if (scorer) {
+        if (i < nch) {
+          const int st = i & (NSTG - 1);
+          // S^T = K Q^T over all 512 dims: two item tiles x even/odd k-steps,
+          // fragments read in batches of 4 k-steps, one batch ahead
+          const uint8_t* sb = reinterpret_cast<const uint8_t*>(&stg[st * STG]) + qk_row;
+          f32x4 sacc[2][2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[i] = (part[0][i] + other0[i]) * scale2;
-        x[4 + i] = (part[1][i] + other1[i]) * scale2;
-      }
-      if ((uint32_t)valid != 0xffffffffu) {                // padding in this chunk
-        const uint32_t lo = (uint32_t)(valid >> (4 * g)), hi = (uint32_t)(valid >> (16 + 4 * g));
+          for (int j = 0; j < 4; ++j) sacc[j >> 1][j & 1] = f32x4{0.f, 0.f, 0.f, 0.f};
+          constexpr int KB = 2, NB = KSQ / KB;
+          bf16x8 fa[2][2 * KB];
+          auto read_batch = [&](int b, bf16x8 (&f)[2 * KB]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (!((lo >> i) & 1u)) x[i] = -INFINITY;
-          if (!((hi >> i) & 1u)) x[4 + i] = -INFINITY;
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+              for (int j = 0; j < KB; ++j)
+                f[mt * KB + j] = bitcast<bf16x8>(
+                    *reinterpret_cast<const u32x4*>(sb + mt * 16 * KRS * 2 + (((KB * b + j) ^ fq) << 4)));
+          };
+          read_batch(0, fa[0]);
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+#pragma unroll
+            for (int j = 0; j < 2 * KB; ++j) pin(fa[b & 1][j]);
+            if (b + 1 < NB) read_batch(b + 1, fa[(b + 1) & 1]);
+#pragma unroll
+            for (int j = 0; j < KB; ++j)
+#pragma unroll
+              for (int mt = 0; mt < 2; ++mt)
+                sacc[mt][j & 1] = mfma16_bf16(fa[b & 1][mt * KB + j], bitcast<bf16x8>(o[KB * b + j]), sacc[mt][j & 1]);
+          }
+          float x[8];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            x[j] = (sacc[0][0][j] + sacc[0][1][j]) * scale2;
+            x[4 + j] = (sacc[1][0][j] + sacc[1][1][j]) * scale2;
+          }
+          if ((uint32_t)valid != 0xffffffffu) {            // padding in this chunk
+            const uint32_t lo = (uint32_t)(valid >> (4 * g)), hi = (uint32_t)(valid >> (16 + 4 * g));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              if (!((lo >> j) & 1u)) x[j] = -INFINITY;
+              if (!((hi >> j) & 1u)) x[4 + j] = -INFINITY;
+            }
+          }
+          float cmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+          cmax = group_max4(cmax);
+          // the reference maximum moves only when a logit exceeds it by more
+          // than 2^8 (probabilities then stay below 256): rescales are rare
+          const bool grows = cmax > m_run + 8.f;
+          const bool had = m_run != -INFINITY;   // an earlier chunk contributed
+          const float m_new = grows ? cmax : m_run;
+          const float m_use = m_new == -INFINITY ? 0.f : m_new;
+          const float alpha = grows ? (had ? __builtin_amdgcn_exp2f(m_run - m_new) : 0.f) : 1.f;
+          m_run = m_new;
+          // P = hi + lo, both bf16 (about 16 significant bits together)
+          bf16x8 pa, pl;
+          float psum = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float pe = __builtin_amdgcn_exp2f(x[e] - m_use);
+            psum += pe;
+            pa[e] = (__bf16)pe;
+            pl[e] = (__bf16)(pe - (float)pa[e]);
+          }
+          l_run = l_run * alpha + psum;
+          pb[i & 1][hg][0][l] = bitcast<u32x4>(pa);
+          pb[i & 1][hg][1][l] = bitcast<u32x4>(pl);
+          if (g == 0) al[i & 1][hg][col] = alpha;
+          const bool any = __any(grows && had);
+          if (l == 0) resc[i & 1][hg] = any ? 1 : 0;
         }
-      }
-      float cmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-      cmax = group_max4(cmax);
-      // the reference maximum moves only when a logit exceeds it by more than
-      // 2^8 (probabilities then stay below 256): the output is rescaled rarely
-      const bool grows = cmax > m_run + 8.f;
-      const bool had = m_run != -INFINITY;       // an earlier chunk contributed
-      const float m_new = grows ? cmax : m_run;
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = grows ? (had ? __builtin_amdgcn_exp2f(m_run - m_new) : 0.f) : 1.f;
-      m_run = m_new;
-      // P = hi + lo, both bf16 (about 16 significant bits together)
-      bf16x8 pa, pl;
-      float psum = 0.f;
+      } else if (i >= 1) {
+        // O = O * alpha + P V for chunk i - 1, from the score wave's P
+        const int c = i - 1, st = c & (NSTG - 1);
+        const bf16x8 pa = bitcast<bf16x8>(pb[c & 1][hg][0][l]);
+        const bf16x8 pl = bitcast<bf16x8>(pb[c & 1][hg][1][l]);
+        if (resc[c & 1][hg]) {                   // nothing to rescale before the first contribution
+          const f32x4 a4 = *reinterpret_cast<const f32x4*>(&al[c & 1][hg][4 * g]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float pe = __builtin_amdgcn_exp2f(x[e] - m_use);
-        psum += pe;
-        pa[e] = (__bf16)pe;
-        pl[e] = (__bf16)(pe - (float)pa[e]);
-      }
-      l_run = l_run * alpha + psum;
-      if (__any(grows && had)) {                 // nothing to rescale before the first contribution
-        float al[4];
+          for (int nd = 0; nd < ND; ++nd)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i, kWave);
+            for (int j = 0; j < 4; ++j) o[nd][j] *= a4[j];
+        }
+        const int vb0 = st * STG * 2 + pv_row;
 #pragma unroll
-        for (int nd = 0; nd < ND; ++nd)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) o[nd][i] *= al[i];
-      }
-      // O += P V over this wave's latent half: B fragments by transposing reads
-      const int vb = st * STG * 2 + pv_row;
-#pragma unroll
-      for (int nd = 0; nd < ND; ++nd) {
-        const int off = vb + ((16 * (nd >> 3) + ((2 * (nd & 7) + pv_h) ^ fv)) << 4);
-        const u32x2 lo = lds_read_tr16(lds0, off);
-        const u32x2 hi = lds_read_tr16(lds0, off + 16 * KRS * 2);
-        const bf16x8 vb = bitcast<bf16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
-        o[nd] = mfma16_bf16(pa, vb, o[nd]);
-        o[nd] = mfma16_bf16(pl, vb, o[nd]);
+        for (int nd = 0; nd < ND; ++nd) {
+          const int off = vb0 + ((16 * (nd >> 3) + ((2 * (nd & 7) + pv_h) ^ fv)) << 4);
+          const u32x2 lo = lds_read_tr16(lds0, off);
+          const u32x2 hi = lds_read_tr16(lds0, off + 16 * KRS * 2);
+          const bf16x8 vb = bitcast<bf16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
+          o[nd] = mfma16_bf16(pa, vb, o[nd]);
+          o[nd] = mfma16_bf16(pl, vb, o[nd]);
+        }
       }
     }
   }
 
-  float l_tot = l_run;
-  l_tot += shfl_xor_f(l_tot, 16);
-  l_tot += shfl_xor_f(l_tot, 32);
+  // The score waves' (m, l) per head meet the output waves' sums, and each
+  // score wave takes over the upper latent half of its head group's sums
+  // (through the stage memory, free now) so that all eight waves store.
+  if (scorer) {
+    float l_tot = l_run;
+    l_tot += shfl_xor_f(l_tot, 16);
+    l_tot += shfl_xor_f(l_tot, 32);
+    if (g == 0) {
+      xml[hg][0][col] = m_run;
+      xml[hg][1][col] = l_tot;
+    }
+  }
+  f32x4* xo = reinterpret_cast<f32x4*>(stg);          // [head group][16 tiles][64 lanes]
+  __syncthreads();                                     // every stage read
+  if (!scorer) {
+#pragma unroll
+    for (int j = 0; j < ND / 2; ++j) xo[(hg * (ND / 2) + j) * kWave + l] = o[ND / 2 + j];
+  }
+  __syncthreads();
+  if (scorer) {
+#pragma unroll
+    for (int j = 0; j < ND / 2; ++j) o[j] = xo[(hg * (ND / 2) + j) * kWave + l];
+  }
+  const int hbase = 16 * hg + 4 * g;
+  const int dbase = (scorer ? D / 2 : 0) + col;        // this wave's latent half
   float lrow[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) lrow[i] = __shfl(l_tot, 4 * g + i, kWave);
-  const int hbase = 16 * hg + 4 * g;
-  const int dbase = DH * dh + col;
+  for (int j = 0; j < 4; ++j) lrow[j] = xml[hg][1][4 * g + j];
   if (p.nsplit == 1) {
 #pragma unroll
-    for (int nd = 0; nd < ND; ++nd)
+    for (int nd = 0; nd < ND / 2; ++nd)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float v = o[nd][i] / lrow[i];
-        const int64_t off = ((int64_t)r * p.H + hbase + i) * D + dbase + 16 * nd;
+      for (int j = 0; j < 4; ++j) {
+        const float v = o[nd][j] / lrow[j];
+        const int64_t off = ((int64_t)r * p.H + hbase + j) * D + dbase + 16 * nd;
         if (p.out_dtype == SCKV_BF16) static_cast<uint16_t*>(p.out)[off] = (uint16_t)f32_to_bf16_rne(v);
         else static_cast<float*>(p.out)[off] = v;
       }
-    if (p.lse && g == 0 && dh == 0) p.lse[(int64_t)r * p.H + head] = (m_run + log2f(l_tot)) * 0.6931471805599453f;
+    if (p.lse && g == 0 && !scorer)
+      p.lse[(int64_t)r * p.H + head] = (xml[hg][0][col] + log2f(xml[hg][1][col])) * 0.6931471805599453f;
   } else {
     const int64_t sbase = ((int64_t)r * p.nsplit + split) * p.H;
 #pragma unroll
-    for (int nd = 0; nd < ND; ++nd)
+    for (int nd = 0; nd < ND / 2; ++nd)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p.ws_o[(sbase + hbase + i) * D + dbase + 16 * nd] = o[nd][i];
-    if (g == 0 && dh == 0) {
-      p.ws_ml[(sbase + head) * 2] = m_run;
-      p.ws_ml[(sbase + head) * 2 + 1] = l_tot;
+      for (int j = 0; j < 4; ++j) p.ws_o[(sbase + hbase + j) * D + dbase + 16 * nd] = o[nd][j];
+    if (g == 0 && !scorer) {
+      p.ws_ml[(sbase + head) * 2] = xml[hg][0][col];
+      p.ws_ml[(sbase + head) * 2 + 1] = xml[hg][1][col];
     }
   }
 }

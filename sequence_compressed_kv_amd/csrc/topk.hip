@@ -82,20 +82,38 @@ __device__ __forceinline__ void load_part(const T* src, int64_t len, int64_t wba
 
 // Bin of the kk_rem-th largest element of an LDS histogram (kBins bins, counted
 // from the top): ctl[0] = bin, ctl[1] = kk_rem minus the elements in higher bins.
+// A histogram of NC copies keeps bin b's counts at words NC b .. NC b + NC - 1.
 // Every thread must call it (block scan, barriers).
-template <int NT>
+template <int NT, int NC = 1>
 __device__ __forceinline__ void find_bin(const uint32_t* hist, uint32_t kk_rem, uint32_t* scan_sh, uint32_t* ctl) {
+  static_assert(NC == 1 || NC % 4 == 0, "copies are read four at a time");
   constexpr int BPT = kBins / NT;
+  uint32_t hb[BPT];
   uint32_t tsum = 0;
 #pragma unroll
-  for (int i = 0; i < BPT; ++i) tsum += hist[threadIdx.x * BPT + i];
+  for (int i = 0; i < BPT; ++i) {
+    const int b = threadIdx.x * BPT + i;
+    uint32_t h = 0;
+    if constexpr (NC == 1) {
+      h = hist[b];
+    } else {
+#pragma unroll
+      for (int c = 0; c < NC; c += 4) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(hist + b * NC + c);
+        h += v[0] + v[1] + v[2] + v[3];
+      }
+    }
+    hb[i] = h;
+    tsum += h;
+  }
   uint32_t total;
   const uint32_t below = block_excl_scan<NT>(tsum, scan_sh, &total);
   const uint32_t above = total - below - tsum;      // elements in higher bins than this chunk
   if (above < kk_rem && kk_rem <= above + tsum) {
     uint32_t run = above;
+#pragma unroll
     for (int i = BPT - 1; i >= 0; --i) {
-      const uint32_t h = hist[threadIdx.x * BPT + i];
+      const uint32_t h = hb[i];
       if (run + h >= kk_rem) {
         ctl[0] = (uint32_t)(threadIdx.x * BPT + i);
         ctl[1] = kk_rem - run;
@@ -115,21 +133,38 @@ constexpr uint32_t kDMask[3] = {0xFFFu, 0xFFFu, 0xFFu};
 // many elements equal to T belong to the selection.  Every thread must call it.
 // A caller that already knows the first digit passes it as prefix (with kk
 // counted from that bin's top) and p0 = 1.
-template <int NT, int V>
+// The first digit's histogram has NC0 copies of each bin (kBins * NC0 words,
+// 16-byte aligned when NC0 > 1), lane l counting into copy l % NC0: scores
+// concentrate in a few dozen first-digit bins, and the atomics of a wave that
+// hit one LDS word are serialised, so spreading a bin over NC0 words cuts that
+// serialisation NC0-fold.  The later digits see only the keys of one bin,
+// spread over many bins, and keep one copy.
+template <int NT, int V, int NC0 = 1>
 __device__ __forceinline__ uint32_t radix_threshold(const uint32_t (&key)[V], const bool (&valid)[V],
                                                     uint32_t kk, uint32_t* hist, uint32_t* scan_sh,
                                                     uint32_t* ctl, uint32_t* need, uint32_t prefix = 0,
                                                     int p0 = 0) {
+  static_assert(NC0 == 1 || (NC0 % 4 == 0 && (NC0 & (NC0 - 1)) == 0), "copies: 1 or a power of two >= 4");
   uint32_t kk_rem = kk;
 #pragma unroll
-  for (int p = p0; p < 3; ++p) {
-    for (int i = threadIdx.x; i < kBins; i += NT) hist[i] = 0;
+  for (int p = 0; p < 3; ++p) {
+    if (p < p0) continue;
+    const int nc = p == 0 ? NC0 : 1;
+    if (nc > 1) {
+      for (int i = threadIdx.x * 4; i < kBins * nc; i += NT * 4)
+        *reinterpret_cast<u32x4*>(hist + i) = u32x4{0u, 0u, 0u, 0u};
+    } else {
+      for (int i = threadIdx.x; i < kBins; i += NT) hist[i] = 0;
+    }
     __syncthreads();
+    const uint32_t copy = p == 0 ? (uint32_t)(lane_id() & (NC0 - 1)) : 0u;
 #pragma unroll
     for (int v = 0; v < V; ++v)
-      if (valid[v] && (key[v] & kHMask[p]) == prefix) atomicAdd(&hist[(key[v] >> kShift[p]) & kDMask[p]], 1u);
+      if (valid[v] && (key[v] & kHMask[p]) == prefix)
+        atomicAdd(&hist[((key[v] >> kShift[p]) & kDMask[p]) * nc + copy], 1u);
     __syncthreads();
-    find_bin<NT>(hist, kk_rem, scan_sh, ctl);
+    if (p == 0) find_bin<NT, NC0>(hist, kk_rem, scan_sh, ctl);
+    else find_bin<NT>(hist, kk_rem, scan_sh, ctl);
     prefix |= ctl[0] << kShift[p];
     kk_rem = ctl[1];
     __syncthreads();
@@ -175,7 +210,7 @@ __device__ __forceinline__ void ordered_scan(const uint32_t (&c)[NI], uint32_t (
 // (wave, group, lane, element).  Every thread must call it.
 // A caller that knows the bin b of the first digit holding the kk-th key, and the
 // count `above` of elements in higher bins, passes b1 = b + 1 and above.
-template <int NT, int V>
+template <int NT, int V, int NC0 = 1>
 __device__ __forceinline__ void select_ordered(const uint32_t (&key)[V], const int32_t (&idx)[V],
                                                const bool (&valid)[V], uint32_t n_valid, uint32_t kk, int32_t* oi,
                                                float* os, int kpad, uint32_t* hist, uint32_t* scan_sh, uint32_t* ctl,
@@ -184,8 +219,8 @@ __device__ __forceinline__ void select_ordered(const uint32_t (&key)[V], const i
   uint32_t T = 0, need = UINT_MAX;
   bool all_eq = true;                    // every key equal to T is kept (no tie to break)
   if (kk < n_valid) {
-    if (b1) T = radix_threshold<NT, V>(key, valid, kk - above, hist, scan_sh, ctl, &need, (b1 - 1) << 20, 1);
-    else T = radix_threshold<NT, V>(key, valid, kk, hist, scan_sh, ctl, &need);
+    if (b1) T = radix_threshold<NT, V, NC0>(key, valid, kk - above, hist, scan_sh, ctl, &need, (b1 - 1) << 20, 1);
+    else T = radix_threshold<NT, V, NC0>(key, valid, kk, hist, scan_sh, ctl, &need);
     // the last pass's histogram counts the keys equal to T (the same value in
     // every thread, read after that pass's final barrier)
     all_eq = hist[T & kDMask[2]] == need;
@@ -253,7 +288,10 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
                                                   int32_t* __restrict__ cand_i,
                                                   int32_t* __restrict__ out_idx, float* __restrict__ out_score) {
   constexpr int NI = V / 4;
-  __shared__ uint32_t hist[kBins];
+  // one block per row of up to 32K scores: the first digit counted into four
+  // copies per bin (64 KB); smaller blocks, several to a CU, keep one copy
+  constexpr int NC0 = NT >= 1024 ? 4 : 1;
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kBins * NC0];
   __shared__ uint32_t scan_sh[NT / kWave + 1];
   __shared__ uint32_t ctl[2];
   const int r = blockIdx.y;
@@ -315,7 +353,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
     os = out_score ? out_score + (int64_t)r * k : nullptr;
     kpad = k;
   }
-  select_ordered<NT, V>(key, idx, valid, n_valid, kk, oi, os, kpad, hist, scan_sh, ctl);
+  select_ordered<NT, V, NC0>(key, idx, valid, n_valid, kk, oi, os, kpad, hist, scan_sh, ctl);
 }
 
 
