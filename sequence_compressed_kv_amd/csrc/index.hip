@@ -439,11 +439,15 @@ static void launch_mfma(const sckv_index_args& a, float* scores, int64_t stride,
     // per SIMD a long grid runs in rounds, and short waves keep the last round's
     // tail short: 32 rows of 1023 tiles take 49-51 us with 4, 52-53.5 with 8,
     // 53-54 with 16 and 58-61 with 2 (the block's query staging then weighs on
-    // too few keys).  Narrower keys spend more per tile on their conversion:
-    // the largest of 16/8/4 that still gives about 2048 waves (MXFP4 keys, same
-    // rows: 22.5 us with 8 against 25.5 with 4).
+    // too few keys).  MXFP4 keys (68 bytes a key) spend more per tile on their
+    // conversion and do best in one round of long waves: 16 tiles once that
+    // still gives 2048 waves (same rows: 20.1-20.2 us with 16, 21.4-22.5 with 8,
+    // 25.5 with 4).  e4m3 keys: the largest of 16/8/4 that still gives about
+    // 2048 waves.
     const int64_t tiles = (cover + 31) / 32 * a.rows.R;
-    const int nt = KEY == SCKV_BF16 ? 4 : (tiles >= 2048 * 16 ? 16 : (tiles >= 2048 * 8 ? 8 : 4));
+    const int nt = KEY == SCKV_BF16    ? 4
+                   : KEY == SCKV_MXFP4 ? (tiles >= 2048 * 8 ? 16 : 4)
+                                       : (tiles >= 2048 * 16 ? 16 : (tiles >= 2048 * 8 ? 8 : 4));
     const int64_t kpb = 4 * 32 * (int64_t)nt;
     const dim3 grid((unsigned)((cover + kpb - 1) / kpb), (unsigned)a.rows.R);
 #define SCKV_DEC(NTT)                                                                                          \
